@@ -1,0 +1,427 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Every check compares the oracle with something other than itself: values of
+the pages' worked examples evaluated by hand (tests/golden/), closed forms,
+the read-back invariant, orthonormal-key reduction to causal linear
+attention, brute-force transition products in fp64 and in exact rationals,
+the full-sequence triangular system, linearity, resume, varlen decomposition
+and the context-parallel composition. ``test_planted_mistakes_are_caught``
+compiles deliberately broken copies of the C oracle and checks that each one
+fails at least one of these pins.
+"""
+
+import json
+import os
+import shutil
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RTOL = 1e-12
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    scale = max(np.abs(b).max(), 1e-300)
+    return float(np.abs(a - b).max() / scale)
+
+
+def _unit_rows(rng, shape):
+    x = rng.standard_normal(shape)
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _inputs(rng, B=2, T=37, H=3, dk=8, dv=6, s0=True, beta_lo=0.0):
+    q = _unit_rows(rng, (B, T, H, dk))
+    k = _unit_rows(rng, (B, T, H, dk))
+    v = rng.standard_normal((B, T, H, dv))
+    beta = beta_lo + (1 - beta_lo) * rng.uniform(size=(B, T, H))
+    S0 = rng.standard_normal((B, H, dv, dk)) * 0.3 if s0 else None
+    return q, k, v, beta, S0
+
+
+def _frac_mat(rows):
+    return np.array([[float(Fraction(x)) for x in r] for r in rows])
+
+
+# ---------------------------------------------------------------------------
+# The pin battery, parameterised by the C library so planted mistakes can be
+# run through exactly the same checks.
+# ---------------------------------------------------------------------------
+
+def pin_golden_three_tokens(lib):
+    g = json.load(open(os.path.join(GOLDEN, "three_token_chunk.json")))
+    k = _frac_mat(g["inputs"]["k"])
+    v = _frac_mat(g["inputs"]["v"])
+    q = _frac_mat(g["inputs"]["q"])
+    beta = np.array([float(Fraction(x)) for x in g["inputs"]["beta"]])
+    o, Sf = oracle.deltanet_fwd(q[None, :, None], k[None, :, None], v[None, :, None],
+                                beta[None, :, None], lib=lib)
+    return (_rel(o[0, :, 0], _frac_mat(g["expected"]["o"])) < RTOL
+            and _rel(Sf[0, 0], _frac_mat(g["expected"]["S_final"])) < RTOL)
+
+
+def pin_golden_three_tokens_lambda(lib):
+    # With V = 0 and S0 = I (dk x dk) the state after the chunk is the ordered
+    # transition product, i.e. Lambda of the row convention, transposed.
+    g = json.load(open(os.path.join(GOLDEN, "three_token_chunk.json")))
+    k = _frac_mat(g["inputs"]["k"])
+    beta = np.array([float(Fraction(x)) for x in g["inputs"]["beta"]])
+    v = np.zeros((3, 2))
+    _, Sf = oracle.deltanet_fwd(k[None, :, None], k[None, :, None], v[None, :, None],
+                                beta[None, :, None], S0=np.eye(2)[None, None], lib=lib)
+    return _rel(Sf[0, 0], _frac_mat(g["expected"]["Lambda_row_convention"]).T) < RTOL
+
+
+def pin_golden_alice_bob(lib):
+    g = json.load(open(os.path.join(GOLDEN, "alice_bob.json")))
+    S0 = _frac_mat(g["S0"])
+    e2 = np.array([0.0, 1.0])
+    office = np.array([0.0, 0.0, 1.0])
+    ok = True
+    for case in g["cases"]:
+        b = float(Fraction(case["beta"]))
+        o, Sf = oracle.deltanet_fwd(e2[None, None, None], e2[None, None, None],
+                                    office[None, None, None], np.array([[[b]]]),
+                                    S0=S0[None, None], lib=lib)
+        ok &= _rel(o[0, 0, 0], [float(Fraction(x)) for x in case["o_bob"]]) < RTOL
+        ok &= _rel(Sf[0, 0], _frac_mat(case["S_final"])) < RTOL
+    return bool(ok)
+
+
+def pin_beta_zero(lib):
+    rng = np.random.default_rng(1)
+    q, k, v, beta, S0 = _inputs(rng)
+    beta[:] = 0.0
+    o, Sf = oracle.deltanet_fwd(q, k, v, beta, S0, lib=lib)
+    ref_o = np.einsum("bhij,bthj->bthi", S0, q)
+    return _rel(Sf, S0) < RTOL and _rel(o, ref_o) < RTOL
+
+
+def pin_single_token(lib):
+    rng = np.random.default_rng(2)
+    q, k, v, beta, _ = _inputs(rng, B=1, T=1, H=2, s0=False)
+    o, Sf = oracle.deltanet_fwd(q, k, v, beta, None, lib=lib)
+    ok = True
+    for h in range(2):
+        b, kk, vv, qq = beta[0, 0, h], k[0, 0, h], v[0, 0, h], q[0, 0, h]
+        ok &= _rel(Sf[0, h], b * np.outer(vv, kk)) < RTOL
+        ok &= _rel(o[0, 0, h], b * (kk @ qq) * vv) < RTOL
+    return bool(ok)
+
+
+def pin_read_back(lib):
+    # S_t k_t = (1 - b_t) S_{t-1} k_t + b_t v_t for unit keys; beta = 1 replaces.
+    rng = np.random.default_rng(3)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=12, H=1)
+    beta[0, 5, 0] = 1.0
+    ok = True
+    prev = S0[0, 0]
+    for t in range(12):
+        _, St = oracle.deltanet_fwd(q[:, :t + 1], k[:, :t + 1], v[:, :t + 1], beta[:, :t + 1],
+                                    S0, lib=lib)
+        kt, b = k[0, t, 0], beta[0, t, 0]
+        expect = (1 - b) * (prev @ kt) + b * v[0, t, 0]
+        ok &= _rel(St[0, 0] @ kt, expect) < 1e-11
+        prev = St[0, 0]
+    return bool(ok)
+
+
+def pin_orthonormal_keys(lib):
+    # Orthonormal keys and a zero start make every prediction zero, so the
+    # output is causal linear attention with values beta*v.
+    rng = np.random.default_rng(4)
+    dk, T = 16, 16
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[rng.permutation(dk)][:T][None, :, None]
+    q = _unit_rows(rng, (1, T, 1, dk))
+    v = rng.standard_normal((1, T, 1, 5))
+    beta = rng.uniform(0.1, 1.0, size=(1, T, 1))
+    o, Sf = oracle.deltanet_fwd(q, k, v, beta, None, lib=lib)
+    scores = np.tril(q[0, :, 0] @ k[0, :, 0].T)
+    ref = scores @ (beta[0, :, 0, None] * v[0, :, 0])
+    return _rel(o[0, :, 0], ref) < 1e-11
+
+
+def pin_householder_products(lib):
+    rng = np.random.default_rng(5)
+    q, k, v, beta, S0 = _inputs(rng, B=2, T=9, H=2, dk=5, dv=4)
+    o, Sf = oracle.deltanet_fwd(q, k, v, beta, S0, lib=lib)
+    ok = True
+    for b in range(2):
+        for h in range(2):
+            ro, rs = oracle.householder_unit(q[b, :, h], k[b, :, h], v[b, :, h], beta[b, :, h],
+                                             S0[b, h])
+            ok &= _rel(o[b, :, h], ro) < 1e-11 and _rel(Sf[b, h], rs) < 1e-11
+    return bool(ok)
+
+
+def pin_square_householder(lib):
+    # dk == dv, so an index transposed in the state still runs; the products catch it.
+    rng = np.random.default_rng(6)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=7, H=1, dk=4, dv=4)
+    o, Sf = oracle.deltanet_fwd(q, k, v, beta, S0, lib=lib)
+    ro, rs = oracle.householder_unit(q[0, :, 0], k[0, :, 0], v[0, :, 0], beta[0, :, 0], S0[0, 0])
+    return _rel(o[0, :, 0], ro) < 1e-11 and _rel(Sf[0, 0], rs) < 1e-11
+
+
+def pin_exact_rationals(lib):
+    kk = [[Fraction(1, 2), Fraction(-1, 3), Fraction(2, 3)],
+          [Fraction(1), Fraction(0), Fraction(-1, 4)],
+          [Fraction(-2, 5), Fraction(3, 5), Fraction(0)],
+          [Fraction(1, 3), Fraction(1, 3), Fraction(1, 3)],
+          [Fraction(0), Fraction(-1), Fraction(1, 2)]]
+    vv = [[Fraction(1), Fraction(-2)], [Fraction(3, 2), Fraction(1, 2)],
+          [Fraction(-1), Fraction(0)], [Fraction(2), Fraction(1, 3)],
+          [Fraction(0), Fraction(5, 4)]]
+    qq = [[Fraction(1), Fraction(0), Fraction(1)], [Fraction(0), Fraction(2), Fraction(-1)],
+          [Fraction(1, 2), Fraction(1, 2), Fraction(0)], [Fraction(-1), Fraction(1), Fraction(1)],
+          [Fraction(1, 4), Fraction(0), Fraction(3)]]
+    bb = [Fraction(1, 2), Fraction(1, 3), Fraction(3, 4), Fraction(1), Fraction(1, 5)]
+    S0 = [[Fraction(1, 7), Fraction(0), Fraction(-1, 2)], [Fraction(2), Fraction(1, 3), Fraction(0)]]
+    states = oracle.exact_states(kk, vv, bb, S0)
+    exact_o = [[sum((states[t][i][j] * qq[t][j] for j in range(3)), Fraction(0))
+                for i in range(2)] for t in range(5)]
+    f = lambda m: np.array([[float(x) for x in r] for r in m])
+    o, Sf = oracle.deltanet_fwd(f(qq)[None, :, None], f(kk)[None, :, None], f(vv)[None, :, None],
+                                np.array([float(x) for x in bb])[None, :, None],
+                                S0=f(S0)[None, None], lib=lib)
+    return _rel(o[0, :, 0], f(exact_o)) < RTOL and _rel(Sf[0, 0], f(states[-1])) < RTOL
+
+
+def pin_full_sequence(lib):
+    rng = np.random.default_rng(7)
+    q, k, v, beta, _ = _inputs(rng, B=2, T=40, H=2, s0=False)
+    o, Sf = oracle.deltanet_fwd(q, k, v, beta, None, lib=lib)
+    ro, rs = oracle.full_sequence_fwd(q, k, v, beta)
+    return _rel(o, ro) < 1e-10 and _rel(Sf, rs) < 1e-10
+
+
+def pin_linearity(lib):
+    rng = np.random.default_rng(8)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=20, H=2)
+    v2 = rng.standard_normal(v.shape)
+    S02 = rng.standard_normal(S0.shape)
+    a, c = 0.7, -1.3
+    o1, s1 = oracle.deltanet_fwd(q, k, v, beta, S0, lib=lib)
+    o2, s2 = oracle.deltanet_fwd(q, k, v2, beta, S02, lib=lib)
+    o3, s3 = oracle.deltanet_fwd(q, k, a * v + c * v2, beta, a * S0 + c * S02, lib=lib)
+    return _rel(o3, a * o1 + c * o2) < 1e-11 and _rel(s3, a * s1 + c * s2) < 1e-11
+
+
+def pin_resume(lib):
+    rng = np.random.default_rng(9)
+    q, k, v, beta, S0 = _inputs(rng, B=2, T=50, H=2)
+    o, Sf = oracle.deltanet_fwd(q, k, v, beta, S0, lib=lib)
+    t1 = 23
+    oa, Sa = oracle.deltanet_fwd(q[:, :t1], k[:, :t1], v[:, :t1], beta[:, :t1], S0, lib=lib)
+    ob, Sb = oracle.deltanet_fwd(q[:, t1:], k[:, t1:], v[:, t1:], beta[:, t1:], Sa, lib=lib)
+    return _rel(np.concatenate([oa, ob], axis=1), o) < RTOL and _rel(Sb, Sf) < RTOL
+
+
+def pin_varlen(lib):
+    rng = np.random.default_rng(10)
+    lens = [5, 0, 17, 1, 33]
+    T = sum(lens)
+    H, dk, dv = 2, 6, 5
+    q = _unit_rows(rng, (T, H, dk))
+    k = _unit_rows(rng, (T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    beta = rng.uniform(size=(T, H))
+    S0 = rng.standard_normal((len(lens), H, dv, dk))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    o, Sf = oracle.deltanet_fwd_varlen(q, k, v, beta, cu, S0, lib=lib)
+    ok = True
+    for n, L in enumerate(lens):
+        a = cu[n]
+        if L == 0:
+            ok &= _rel(Sf[n], S0[n]) < RTOL
+            continue
+        on, sn = oracle.deltanet_fwd(q[None, a:a + L], k[None, a:a + L], v[None, a:a + L],
+                                     beta[None, a:a + L], S0[n:n + 1], lib=lib)
+        for h in range(H):
+            hs, hs_ = oracle.householder_unit(q[a:a + L, h], k[a:a + L, h], v[a:a + L, h],
+                                              beta[a:a + L, h], S0[n, h])
+            ok &= _rel(o[a:a + L, h], hs) < 1e-11 and _rel(Sf[n, h], hs_) < 1e-11
+        ok &= _rel(o[a:a + L], on[0]) < RTOL and _rel(Sf[n], sn[0]) < RTOL
+    return bool(ok)
+
+
+def pin_chunked_agreement(lib):
+    rng = np.random.default_rng(11)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=45, H=2)
+    o, Sf = oracle.deltanet_fwd(q, k, v, beta, S0, lib=lib)
+    ok = True
+    for C in (1, 2, 16, 45):
+        co, cs = oracle.chunked_fwd(q, k, v, beta, S0, chunk=C)
+        ok &= _rel(co, o) < 1e-10 and _rel(cs, Sf) < 1e-10
+    return bool(ok)
+
+
+PINS = [pin_golden_three_tokens, pin_golden_three_tokens_lambda, pin_golden_alice_bob,
+        pin_beta_zero, pin_single_token, pin_read_back, pin_orthonormal_keys,
+        pin_householder_products, pin_square_householder, pin_exact_rationals,
+        pin_full_sequence, pin_linearity, pin_resume, pin_varlen, pin_chunked_agreement]
+
+
+def failed_pins(lib):
+    out = []
+    for pin in PINS:
+        try:
+            ok = pin(lib)
+        except Exception:
+            ok = False
+        if not ok:
+            out.append(pin.__name__)
+    return out
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    assert pin(oracle.load())
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each broken copy of the C oracle must fail some pin.
+# ---------------------------------------------------------------------------
+
+MUTANTS = {
+    "dropped_beta": ("const double ui = bt * (vt[i] - vhat[i]);",
+                     "const double ui = (vt[i] - vhat[i]);"),
+    "wrong_sign": ("const double ui = bt * (vt[i] - vhat[i]);",
+                   "const double ui = bt * (vt[i] + vhat[i]);"),
+    "dropped_prediction": ("const double ui = bt * (vt[i] - vhat[i]);",
+                           "const double ui = bt * vt[i];"),
+    "transposed_state": ("for (int j = 0; j < dk; ++j) acc += Si[j] * kt[j];",
+                         "for (int j = 0; j < dk; ++j) acc += S[(size_t)j * dk + i] * kt[j];"),
+    "write_at_query": ("for (int j = 0; j < dk; ++j) Si[j] += ui * kt[j];",
+                       "for (int j = 0; j < dk; ++j) Si[j] += ui * qt[j];"),
+    "ignored_S0": ("if (S0) memcpy(S, S0", "if (0) memcpy(S, S0"),
+    "dropped_last_token": ("for (int64_t t = 0; t < L; ++t) {",
+                           "for (int64_t t = 0; t + 1 < L; ++t) {"),
+    "beta_of_head0": ("beta + t0 * H + h,", "beta + t0 * H,"),
+    "read_before_write": ("        /* write: S += beta_t (v_t - vhat) k_t^T */",
+                          "        if (o) { double *ot = o + t * vo_stride;"
+                          " for (int i = 0; i < dv; ++i) { const double *Si = S + (size_t)i * dk;"
+                          " double acc = 0.0; for (int j = 0; j < dk; ++j) acc += Si[j] * qt[j];"
+                          " ot[i] = acc; } }\n        /* write */"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir():
+    d = tempfile.mkdtemp(prefix="oracle_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def test_real_oracle_passes_all_pins():
+    assert failed_pins(oracle.load()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistakes_are_caught(name, mutant_dir):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "deltanet_oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mutated = src.replace(old, new)
+    if name == "read_before_write":
+        # drop the original read-out so only the early one remains
+        tail_anchor = "        /* read-out after the write: o_t = S_t q_t */\n        if (o) {"
+        assert mutated.count(tail_anchor) == 1
+        mutated = mutated.replace(tail_anchor, "        if (0) {")
+    csrc = os.path.join(mutant_dir, f"{name}.c")
+    so = os.path.join(mutant_dir, f"lib{name}.so")
+    open(csrc, "w").write(mutated)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", csrc, "-o", so],
+                   check=True)
+    lib = oracle.load(so)
+    assert failed_pins(lib), f"planted mistake {name} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# The numpy forms: chunk factors, WY/UT identities, CP composition.
+# ---------------------------------------------------------------------------
+
+def test_chunk_factors_golden():
+    g = json.load(open(os.path.join(GOLDEN, "three_token_chunk.json")))
+    k = _frac_mat(g["inputs"]["k"])
+    v = _frac_mat(g["inputs"]["v"])
+    beta = np.array([float(Fraction(x)) for x in g["inputs"]["beta"]])
+    T, W, U = oracle.chunk_factors(k, v, beta)
+    assert _rel(T, _frac_mat(g["expected"]["T"])) < RTOL
+    assert _rel(W, _frac_mat(g["expected"]["W"])) < RTOL
+    assert _rel(U, _frac_mat(g["expected"]["U"])) < RTOL
+    Lam = np.eye(2) - k.T @ W
+    assert _rel(Lam, _frac_mat(g["expected"]["Lambda_row_convention"])) < RTOL
+
+
+@pytest.mark.parametrize("C", [1, 5, 16, 64])
+def test_wy_ut_identities(C):
+    rng = np.random.default_rng(20 + C)
+    dk, dv = 12, 7
+    K = _unit_rows(rng, (C, dk))
+    V = rng.standard_normal((C, dv))
+    b = rng.uniform(size=C)
+    T, W, U = oracle.chunk_factors(K, V, b)
+    # T is lower triangular with diag beta, and solves (I + B L) T = B
+    assert np.allclose(np.triu(T, 1), 0.0)
+    assert np.allclose(np.diag(T), b, rtol=0, atol=1e-15)
+    Lr = np.tril(K @ K.T, -1)
+    assert np.abs((np.eye(C) + b[:, None] * Lr) @ T - np.diag(b)).max() < 1e-13
+    # ordered product of the transitions equals I - W^T K (state transposed)
+    P = np.eye(dk)
+    for t in range(C):
+        P = P @ (np.eye(dk) - b[t] * np.outer(K[t], K[t]))
+    assert _rel(np.eye(dk) - W.T @ K, P) < 1e-12
+    # zero-start writes equal U^T K
+    _, Q = oracle.cp_group_transition(K, V, b)
+    assert _rel(U.T @ K, Q) < 1e-12
+
+
+def test_partial_chunk_equals_zero_padding():
+    # k = 0, beta = 0 tokens are identity transitions with no write
+    rng = np.random.default_rng(30)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=50, H=1)
+    o, Sf = oracle.chunked_fwd(q, k, v, beta, S0, chunk=16)
+    pad = 14
+    z = lambda a: np.concatenate([a, np.zeros((1, pad) + a.shape[2:])], axis=1)
+    op, Sp = oracle.chunked_fwd(z(q), z(k), z(v), z(beta), S0, chunk=16)
+    assert _rel(op[:, :50], o) < 1e-12 and _rel(Sp, Sf) < 1e-12
+
+
+@pytest.mark.parametrize("groups", [1, 2, 5])
+def test_cp_composition(groups):
+    rng = np.random.default_rng(40 + groups)
+    T, dk, dv = 64, 8, 6
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=T, H=1, dk=dk, dv=dv)
+    bounds = np.linspace(0, T, groups + 1).astype(int)
+    Ps, Qs = [], []
+    for g in range(groups):
+        a, b = bounds[g], bounds[g + 1]
+        P, Q = oracle.cp_group_transition(k[0, a:b, 0], v[0, a:b, 0], beta[0, a:b, 0])
+        Ps.append(P)
+        Qs.append(Q)
+    starts = oracle.cp_compose(S0[0, 0], Ps, Qs)
+    for g in range(groups + 1):
+        t = bounds[g]
+        if t == 0:
+            ref = S0[0, 0]
+        else:
+            _, St = oracle.deltanet_fwd(q[:, :t], k[:, :t], v[:, :t], beta[:, :t], S0)
+            ref = St[0, 0]
+        assert _rel(starts[g], ref) < 1e-11
+
+
+def test_oracle_threads_do_not_change_results():
+    rng = np.random.default_rng(50)
+    q, k, v, beta, S0 = _inputs(rng, B=3, T=33, H=5)
+    o1, s1 = oracle.deltanet_fwd(q, k, v, beta, S0, nthreads=1)
+    o4, s4 = oracle.deltanet_fwd(q, k, v, beta, S0, nthreads=4)
+    assert np.array_equal(o1, o4) and np.array_equal(s1, s4)
