@@ -1,0 +1,208 @@
+// C-ABI of the DeltaNet forward library: argument checks, context-parallel
+// planning and dispatch to the gfx950 kernels. Every check runs before the
+// first launch, so an error return means nothing was enqueued.
+#include "../../include/deltanet.h"
+#include "dn_internal.h"
+
+#include <mutex>
+#include <stdint.h>
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void *p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int check_shape(int dk, int dv, int chunk, int dtype) {
+    if (dtype != DN_F32 && dtype != DN_BF16) return DN_ERR_INVALID;
+    if (dk <= 0 || dv <= 0 || chunk <= 0) return DN_ERR_INVALID;
+    if (chunk != dn::kChunk) return DN_ERR_UNSUPPORTED;
+    if (dtype == DN_BF16) {
+        if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return DN_ERR_UNSUPPORTED;
+    } else {
+        if (dk != 64 || (dv != 64 && dv != 128)) return DN_ERR_UNSUPPORTED;
+    }
+    return DN_OK;
+}
+
+// Compute units of the current device, cached per device ordinal.
+int device_cus() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Choice of group count for cp_groups = 0. The serial pass keeps one
+// workgroup per (unit, 64-row tile) busy for the whole chunk chain. When
+// those workgroups fill at least half of the compute units, splitting only
+// adds the transition work. Otherwise the chain is cut into enough groups to
+// give every compute unit an output workgroup, keeping at least 8 chunks per
+// group so the per-group transition cost stays amortised.
+int pick_groups(int B, int H, int T, int dv) {
+    const int nc = (T + dn::kChunk - 1) / dn::kChunk;
+    const int serial_wgs = B * H * (dv / dn::kRows);
+    const int cus = device_cus();
+    if (serial_wgs * 2 >= cus || nc < 16) return 1;
+    int G = cus / serial_wgs;
+    if (G > nc / 8) G = nc / 8;
+    return G < 1 ? 1 : G;
+}
+
+// Resolve the requested group count into (G, chunks per group) with no empty group.
+void resolve_groups(int requested, int B, int H, int T, int dv, int &G, int &cpg) {
+    const int nc = (T + dn::kChunk - 1) / dn::kChunk;
+    G = requested == 0 ? pick_groups(B, H, T, dv) : requested;
+    if (G > nc) G = nc;
+    if (G < 1) G = 1;
+    cpg = nc > 0 ? (nc + G - 1) / G : 1;
+    G = nc > 0 ? (nc + cpg - 1) / cpg : 1;
+}
+
+size_t ws_bytes_for(int B, int H, int dk, int dv, int G) {
+    if (G <= 1) return 0;
+    return (size_t)B * H * G * ((size_t)dk * dk + 2 * (size_t)dv * dk) * sizeof(float);
+}
+
+} // namespace
+
+extern "C" {
+
+const char *deltanet_status_string(int status) {
+    switch (status) {
+    case DN_OK: return "ok";
+    case DN_ERR_INVALID: return "invalid argument";
+    case DN_ERR_UNSUPPORTED: return "unsupported shape or chunk size";
+    case DN_ERR_WORKSPACE: return "workspace missing or too small";
+    case DN_ERR_HIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+    }
+}
+
+int deltanet_pick_cp_groups(int B, int H, int T, int dk, int dv, int chunk) {
+    const int st = check_shape(dk, dv, chunk, DN_BF16);
+    if (st != DN_OK && check_shape(dk, dv, chunk, DN_F32) != DN_OK) return st;
+    if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
+    int G, cpg;
+    resolve_groups(0, B, H, T, dv, G, cpg);
+    return G;
+}
+
+size_t deltanet_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int cp_groups) {
+    if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return 0;
+    if (check_shape(dk, dv, chunk, DN_BF16) != DN_OK && check_shape(dk, dv, chunk, DN_F32) != DN_OK)
+        return 0;
+    int G, cpg;
+    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    return ws_bytes_for(B, H, dk, dv, G);
+}
+
+int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta, const float *S0,
+                 void *o, float *S_final, int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                 int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st = check_shape(dk, dv, chunk, dtype);
+    if (st != DN_OK) return st;
+    if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return DN_ERR_INVALID;
+    const size_t esz = dtype == DN_BF16 ? 2 : 4;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !o) return DN_ERR_INVALID;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return DN_ERR_INVALID;
+        if (!aligned_to(beta, esz)) return DN_ERR_INVALID;
+    }
+    if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return DN_ERR_INVALID;
+    if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
+
+    int G, cpg;
+    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    const size_t need = ws_bytes_for(B, H, dk, dv, G);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return DN_ERR_WORKSPACE;
+
+    dn::ChainArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.o = o;
+    a.S0 = S0;
+    a.S_final = S_final;
+    a.B = B;
+    a.H = H;
+    a.T = T;
+    hipError_t err;
+    if (G <= 1) {
+        a.kind = dn::kDense;
+        a.n_units = B * H;
+        a.n_tiles = dv / dn::kRows;
+        err = dn::launch_chain(dtype, dk, dv, true, a, stream);
+        return err == hipSuccess ? DN_OK : DN_ERR_HIP;
+    }
+    float *ws = static_cast<float *>(workspace);
+    const size_t per = (size_t)B * H * G;
+    a.ws_P = ws;
+    a.ws_Q = a.ws_P + per * dk * dk;
+    a.ws_S = a.ws_Q + per * dv * dk;
+    a.G = G;
+    a.chunks_per_group = cpg;
+    // (i) group transitions for groups 0..G-2
+    a.kind = dn::kCpTransition;
+    a.n_units = B * H * (G - 1);
+    a.n_tiles = dv / dn::kRows + dk / dn::kRows;
+    err = dn::launch_chain(dtype, dk, dv, false, a, stream);
+    if (err != hipSuccess) return DN_ERR_HIP;
+    // (ii) prefix composition of the maps -> start states of groups 1..G-1
+    err = dn::launch_compose(dk, dv, a, stream);
+    if (err != hipSuccess) return DN_ERR_HIP;
+    // (iii) every group from its start state, writing o (and S_final from the last group)
+    a.kind = dn::kCpOutput;
+    a.n_units = B * H * G;
+    a.n_tiles = dv / dn::kRows;
+    err = dn::launch_chain(dtype, dk, dv, true, a, stream);
+    return err == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
+int deltanet_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                        const float *S0, void *o, float *S_final, const int32_t *cu_seqlens,
+                        const int32_t *seq_order, int N, int total_T, int H, int dk, int dv,
+                        int chunk, int dtype, hipStream_t stream) {
+    int st = check_shape(dk, dv, chunk, dtype);
+    if (st != DN_OK) return st;
+    if (N <= 0 || H <= 0 || total_T < 0 || !cu_seqlens) return DN_ERR_INVALID;
+    const size_t esz = dtype == DN_BF16 ? 2 : 4;
+    if (total_T > 0) {
+        if (!q || !k || !v || !beta || !o) return DN_ERR_INVALID;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return DN_ERR_INVALID;
+        if (!aligned_to(beta, esz)) return DN_ERR_INVALID;
+    }
+    if (!aligned_to(cu_seqlens, 4) || (seq_order && !aligned_to(seq_order, 4))) return DN_ERR_INVALID;
+    if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return DN_ERR_INVALID;
+    if ((int64_t)N * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
+
+    dn::ChainArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.o = o;
+    a.S0 = S0;
+    a.S_final = S_final;
+    a.cu_seqlens = cu_seqlens;
+    a.seq_order = seq_order;
+    a.kind = dn::kVarlen;
+    a.B = N;
+    a.H = H;
+    a.T = total_T;
+    a.n_units = N * H;
+    a.n_tiles = dv / dn::kRows;
+    hipError_t err = dn::launch_chain(dtype, dk, dv, true, a, stream);
+    return err == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
+} // extern "C"

@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI layer (api.cpp) and the gfx950
+// kernels (kernels.hip). Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dn {
+
+constexpr int kChunk = 64;    // tokens per chunk (C)
+constexpr int kRows = 64;     // state rows per workgroup tile
+constexpr int kThreads = 256; // 4 waves of 64; each wave owns 16 state rows
+
+// How a workgroup finds its (unit, token range, state source/destination).
+enum WorkKind : int {
+    kDense = 0,        // one unit per (b, h); whole sequence; writes o
+    kVarlen = 1,       // one unit per (sequence, h); writes o
+    kCpTransition = 2, // one unit per (b, h, group < G-1); writes P_g^T, Q_g
+    kCpOutput = 3,     // one unit per (b, h, group); starts from the composed state; writes o
+};
+
+struct ChainArgs {
+    const void *q, *k, *v, *beta;
+    void *o;
+    const float *S0;
+    float *S_final;
+    const int32_t *cu_seqlens;
+    const int32_t *seq_order;
+    // Context-parallel workspace, per (b*H + h) and group g:
+    //   ws_P[((bh * G) + g) * dk * dk]  : P_g transposed (row = output column of S)
+    //   ws_Q[((bh * G) + g) * dv * dk]  : Q_g, the group's state from a zero start
+    //   ws_S[((bh * G) + g) * dv * dk]  : start state of group g (g >= 1)
+    float *ws_P, *ws_Q, *ws_S;
+    int kind;
+    int B;       // sequences (dense / cp) or N (varlen)
+    int H;
+    int T;       // tokens per sequence (dense / cp)
+    int G;       // groups (cp kinds)
+    int chunks_per_group;
+    int n_units; // units covered by the grid
+    int n_tiles; // 64-row state tiles per unit
+};
+
+// Enqueue the chunk-chain kernel for dtype (0 = fp32, 1 = bf16) and (dk, dv).
+// grid = n_units * n_tiles workgroups of kThreads threads.
+hipError_t launch_chain(int dtype, int dk, int dv, bool write_o, const ChainArgs &a,
+                        hipStream_t stream);
+
+// Enqueue the prefix composition S_{g+1} = S_g P_g + Q_g for g = 0..G-2,
+// writing start states of groups 1..G-1 into ws_S.
+hipError_t launch_compose(int dk, int dv, const ChainArgs &a, hipStream_t stream);
+
+} // namespace dn

@@ -1,0 +1,143 @@
+/*
+ * deltanet.h -- C-ABI of the MI355X (gfx950) DeltaNet chunkwise forward pass.
+ *
+ * What is computed. For every (sequence, head) unit the library runs the
+ * DeltaNet delta-rule recurrence, with the state S (dv x dk) acting on column
+ * vectors:
+ *     S_t = S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t
+ * ("Linear Attention, Visualized", Haoran Zhang: DeltaNet > "Recurrent form",
+ * with the state transposed as in "Context Parallelism for DeltaNet",
+ * yywangcs, section 2). It evaluates that recurrence with the chunkwise
+ * algorithm of the first page (DeltaNet > "Chunkwise algorithm" > "Complete
+ * per-chunk algorithm"), chunk C = 64: per chunk r
+ *     L = (K K^T) masked strictly lower,  (I + diag(beta) L) T = diag(beta),
+ *     W = T K,  U = T V,  Z = U - W S_r^T,
+ *     O_r = Q S_r^T + ((Q K^T) masked lower-inclusive) Z,
+ *     S_{r+1} = S_r + Z^T K.
+ * The readout is after the write (inclusive causal mask); q is not scaled;
+ * q and k are used exactly as given (no normalisation inside).
+ *
+ * Context parallelism (cp_groups > 1) splits each unit's chunk chain into
+ * groups. Each group first computes its affine map S_end = S_start P_g + Q_g
+ * (P_g the ordered product of (I - W^T K) over its chunks, Q_g its state from
+ * a zero start), a short pass composes these maps to fix every group's start
+ * state, and then all groups produce their outputs in parallel ("Context
+ * Parallelism for DeltaNet", sections 1-3; the chunk as an affine recurrence
+ * in "Linear Attention, Visualized", DeltaNet > "One chunk as an affine
+ * recurrence"). The result equals the serial one up to rounding.
+ *
+ * Layouts (row-major, contiguous, element strides fixed by the shape):
+ *   q, k : [B, T, H, dk]    v, o : [B, T, H, dv]    beta : [B, T, H]
+ *   S0, S_final : [B, H, dv, dk] float32 (S[b,h] is the dv x dk state)
+ *   varlen: q, k [T_total, H, dk], v, o [T_total, H, dv], beta [T_total, H],
+ *           S0/S_final [N, H, dv, dk]; sequence n owns tokens
+ *           [cu_seqlens[n], cu_seqlens[n+1]) and starts from S0[n] (or zero).
+ * q, k, v, beta and o share the element type `dtype`; S0 and S_final are
+ * always float32. All arithmetic accumulates in float32; with DN_BF16 the
+ * matrix-core operands are bfloat16 (intermediates W, T, Z and the state are
+ * rounded to bfloat16 where they enter a matrix product; the state itself is
+ * kept in float32).
+ *
+ * Supported shapes: chunk == 64; dk, dv in {64, 128} for DN_BF16; dk == 64,
+ * dv in {64, 128} for DN_F32. Any T >= 0 (a partial last chunk is masked).
+ *
+ * Ownership and threading. Every pointer is device memory owned by the
+ * caller. The library allocates nothing, frees nothing and never
+ * synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
+ * default stream) and completes asynchronously. The library keeps no state
+ * between calls except a per-device cache of the compute-unit count, and is
+ * safe to call from several threads. o and S_final must not overlap any input.
+ *
+ * Errors. Arguments are checked before anything is enqueued; on a non-zero
+ * return nothing was launched and no output was written. Launch failures
+ * return DN_ERR_HIP. Faults during execution surface at the caller's next
+ * synchronisation of `stream`. NaN/Inf inputs are not detected; they
+ * propagate.
+ */
+#ifndef DELTANET_H
+#define DELTANET_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, beta and o. */
+typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype_t;
+
+/* Status codes. */
+enum {
+    DN_OK = 0,
+    DN_ERR_INVALID = -1,     /* NULL/misaligned pointer, negative or zero size, bad enum */
+    DN_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (chunk, dk, dv) */
+    DN_ERR_WORKSPACE = -3,   /* workspace missing or smaller than deltanet_workspace_bytes */
+    DN_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+/*
+ * Forward pass over B sequences of T tokens each.
+ *   q, k, v, beta : inputs (see layouts above); required, 16-byte aligned.
+ *   S0            : initial states [B,H,dv,dk] fp32, or NULL for zero states.
+ *   o             : output [B,T,H,dv], required (may be NULL only when T == 0).
+ *   S_final       : final states [B,H,dv,dk] fp32, or NULL to skip writing them.
+ *   chunk         : must be 64.
+ *   dtype         : DN_F32 or DN_BF16.
+ *   cp_groups     : 1 = one serial chunk chain per unit; G > 1 = context
+ *                   parallelism with G groups (clamped to the chunk count);
+ *                   0 = let the library choose from the shape and the device's
+ *                   compute-unit count (deltanet_pick_cp_groups).
+ *   workspace, workspace_bytes : device scratch for cp_groups != 1; must hold
+ *                   deltanet_workspace_bytes(...) bytes (may be NULL/0 when the
+ *                   resolved group count is 1). Contents are scratch; they need
+ *                   no initialisation and are clobbered.
+ *   stream        : HIP stream to enqueue on.
+ * Returns DN_OK or a negative status.
+ */
+int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta,
+                 const float *S0, void *o, float *S_final, int B, int H, int T,
+                 int dk, int dv, int chunk, int dtype, int cp_groups,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Forward pass over N packed sequences of different lengths.
+ *   cu_seqlens : device int32 [N+1], cu_seqlens[0] = 0, non-decreasing,
+ *                cu_seqlens[N] = total_T. Not validated on the device: values
+ *                that break these rules give undefined results.
+ *   seq_order  : device int32 [N], a permutation of 0..N-1 giving the order in
+ *                which sequences are scheduled (longest first balances the
+ *                load), or NULL for 0..N-1. Results do not depend on it.
+ *   S0, S_final: [N,H,dv,dk] fp32 or NULL.
+ * Other arguments as in deltanet_fwd. No workspace is needed.
+ */
+int deltanet_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                        const float *S0, void *o, float *S_final,
+                        const int32_t *cu_seqlens, const int32_t *seq_order, int N,
+                        int total_T, int H, int dk, int dv, int chunk, int dtype,
+                        hipStream_t stream);
+
+/*
+ * Bytes of workspace deltanet_fwd needs for this shape and cp_groups (0 means
+ * the library's choice on the current device). Returns 0 when the resolved
+ * group count is 1, and also for invalid shapes.
+ */
+size_t deltanet_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                                int cp_groups);
+
+/*
+ * Group count deltanet_fwd uses when called with cp_groups = 0, for the
+ * current HIP device. Returns 1 (serial) when splitting does not pay, or a
+ * negative status for invalid shapes.
+ */
+int deltanet_pick_cp_groups(int B, int H, int T, int dk, int dv, int chunk);
+
+/* Static, human-readable text for a status code. */
+const char *deltanet_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTANET_H */

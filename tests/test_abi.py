@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: exports, status strings, workspace sizing and
+argument validation (every rejected call returns before anything touches the
+device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunkwise_delta_rule_amd as dn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "deltanet.h")
+
+DN_OK, DN_ERR_INVALID, DN_ERR_UNSUPPORTED, DN_ERR_WORKSPACE, DN_ERR_HIP = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(deltanet_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dn.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) >= {"deltanet_fwd", "deltanet_fwd_varlen", "deltanet_workspace_bytes",
+                          "deltanet_pick_cp_groups", "deltanet_status_string"}
+    raw = ctypes.CDLL(dn.library_path())
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in deltanet.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in (DN_OK, DN_ERR_INVALID, DN_ERR_UNSUPPORTED, DN_ERR_WORKSPACE, DN_ERR_HIP):
+        s = dn.deltanet_status_string(code)
+        assert s and s != "unknown status"
+    assert dn.deltanet_status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert dn.deltanet_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) == 0
+    # G = 4 groups over 64 chunks: per (b,h,g) P (dk^2) + Q and S (dv*dk each), fp32
+    assert dn.deltanet_workspace_bytes(2, 3, 4096, 128, 64, 64, 4) == 2 * 3 * 4 * (
+        128 * 128 + 2 * 64 * 128) * 4
+    # group count is clamped to the chunk count (3 chunks here)
+    assert dn.deltanet_workspace_bytes(1, 1, 150, 64, 64, 64, 10) == 3 * (64 * 64 + 2 * 64 * 64) * 4
+    # 5 chunks, 3 requested -> 2 chunks per group -> 3 groups
+    assert dn.deltanet_workspace_bytes(1, 1, 5 * 64, 64, 64, 64, 3) == 3 * (3 * 64 * 64) * 4
+    # 5 chunks, 4 requested -> 2 chunks per group -> 3 groups (no empty group)
+    assert dn.deltanet_workspace_bytes(1, 1, 5 * 64, 64, 64, 64, 4) == 3 * (3 * 64 * 64) * 4
+    assert dn.deltanet_workspace_bytes(1, 1, 64, 96, 64, 64, 2) == 0  # unsupported dk
+    assert dn.deltanet_workspace_bytes(0, 1, 64, 64, 64, 64, 2) == 0  # invalid B
+
+
+FAKE = 1 << 20  # an aligned non-NULL address; never dereferenced on these paths
+
+
+def call_fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, S0=None, o=FAKE, S_final=None, B=1, H=1, T=128,
+             dk=64, dv=64, chunk=64, dtype=1, cp_groups=1, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.deltanet_fwd(vp(a["q"]) if a["q"] else None, vp(a["k"]) if a["k"] else None,
+                            vp(a["v"]) if a["v"] else None, vp(a["beta"]) if a["beta"] else None,
+                            vp(a["S0"]) if a["S0"] else None, vp(a["o"]) if a["o"] else None,
+                            vp(a["S_final"]) if a["S_final"] else None, a["B"], a["H"], a["T"],
+                            a["dk"], a["dv"], a["chunk"], a["dtype"], a["cp_groups"],
+                            vp(a["ws"]) if a["ws"] else None, a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk=32), DN_ERR_UNSUPPORTED),
+    (dict(dk=96), DN_ERR_UNSUPPORTED),
+    (dict(dv=256), DN_ERR_UNSUPPORTED),
+    (dict(dtype=0, dk=128), DN_ERR_UNSUPPORTED),
+    (dict(dtype=7), DN_ERR_INVALID),
+    (dict(B=0), DN_ERR_INVALID),
+    (dict(H=-1), DN_ERR_INVALID),
+    (dict(T=-5), DN_ERR_INVALID),
+    (dict(dk=0), DN_ERR_INVALID),
+    (dict(q=None), DN_ERR_INVALID),
+    (dict(beta=None), DN_ERR_INVALID),
+    (dict(o=None), DN_ERR_INVALID),
+    (dict(k=FAKE + 8), DN_ERR_INVALID),
+    (dict(S0=FAKE + 4), DN_ERR_INVALID),
+    (dict(S_final=FAKE + 2), DN_ERR_INVALID),
+    (dict(beta=FAKE + 1), DN_ERR_INVALID),
+    (dict(cp_groups=-1), DN_ERR_INVALID),
+    (dict(cp_groups=2), DN_ERR_WORKSPACE),
+    (dict(cp_groups=2, ws=FAKE, ws_bytes=16), DN_ERR_WORKSPACE),
+    (dict(cp_groups=2, ws=FAKE + 8, ws_bytes=1 << 30), DN_ERR_WORKSPACE),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status):
+    assert call_fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), DN_ERR_INVALID),
+    (dict(cu=None), DN_ERR_INVALID),
+    (dict(chunk=16), DN_ERR_UNSUPPORTED),
+    (dict(order=FAKE + 2), DN_ERR_INVALID),
+    (dict(q=None), DN_ERR_INVALID),
+    (dict(dtype=0, dk=128), DN_ERR_UNSUPPORTED),
+])
+def test_varlen_rejects_bad_arguments(lib, kw, status):
+    a = dict(q=FAKE, cu=FAKE, order=None, N=2, total_T=100, dk=64, dv=64, chunk=64, dtype=1)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    st = lib.deltanet_fwd_varlen(vp(a["q"]) if a["q"] else None, vp(FAKE), vp(FAKE), vp(FAKE),
+                                 None, vp(FAKE), None, vp(a["cu"]) if a["cu"] else None,
+                                 vp(a["order"]) if a["order"] else None, a["N"], a["total_T"], 2,
+                                 a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+    assert st == status
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises((ValueError, TypeError)):
+        dn.deltanet_fwd(x, x, x, torch.zeros(1, 4, 1))
