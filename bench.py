@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the DeltaNet chunkwise forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cp-groups G]
+
+One step = one call of ``deltanet_fwd`` (every kernel of the forward pass) over
+one batch of synthetic inputs already resident in HBM. The default workload is
+B=8, H=16, T=4096, dk=dv=128, chunk 64, bf16 (the paper-scale layer). Prints
+one JSON line with the throughput (tokens/s), the fraction of the bf16
+matrix-core peak, a roofline object for the dominant kernel (timed with HIP
+events on the launch stream) and the fp64 CPU oracle's throughput on the
+host cores.
+
+Accounting (per head-token, chunk C, key/value widths dk/dv):
+  flops  F = 2C(3dk + 2dv) + 6 dk dv  -- the eight dense products of the
+         per-chunk algorithm (KK^T, TK, TV, WS^T, QK^T, QS^T, PZ, Z^T K) as
+         written, masked halves included; the T solve is not counted
+  bytes  read q, k, v, beta (+ S0 when given), write o and S_final: the
+         algorithmic minimum, each tensor touched once.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 matrix-core peak
+PEAK_FP32_FLOPS = 157.3e12  # MI355X dense fp32 matrix-core peak
+PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chain_layer_b8_h16_t4096.json")
+KERNEL_SRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc", "kernels.hip")
+
+
+def flops_per_head_token(C, dk, dv):
+    return 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w, esz, n_tokens, n_units, has_s0, has_sf):
+    per_tok = w.H * (2 * w.dk + 2 * w.dv + 1) * esz  # q, k, v, o, beta
+    state = n_units * w.dv * w.dk * 4
+    return n_tokens * per_tok + state * (int(has_s0) + int(has_sf))
+
+
+def load_traffic(workload_name, launch_bytes):
+    """HBM traffic from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source for this workload; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except Exception:
+        return None
+    if t.get("kernel_source_sha") != kernel_sha() or t.get("workload") != workload_name:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inputs, w, varlen, budget_s):
+    """Time the fp64 oracle on the host on a bounded sample of the workload."""
+    import numpy as np
+    import torch
+    import oracle
+
+    def f64(t):
+        return None if t is None else t.detach().to("cpu").to(torch.float64).numpy()
+
+    threads = oracle.max_threads()
+    if varlen:
+        q, k, v, beta, cu, S0, lengths = inputs
+        # sample: the first sequences (in index order) up to ~budget of work
+        est_rate = 2.0e9 * threads  # flop/s, conservative
+        n, work = 0, 0.0
+        while n < len(lengths) and (work + lengths[n] * w.H * 6 * w.dk * w.dv) / est_rate < budget_s:
+            work += lengths[n] * w.H * 6 * w.dk * w.dv
+            n += 1
+        n = max(n, 1)
+        end = int(cu[n].item())
+        args = [f64(x[:end]) for x in (q, k, v, beta)]
+        cu_s = cu[:n + 1].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.deltanet_fwd_varlen(*args, cu_s, None)
+        dt = time.perf_counter() - t0
+        toks = end
+        sample = f"first {n} of {len(lengths)} sequences ({toks} tokens x {w.H} heads)"
+        units = n * w.H
+    else:
+        q, k, v, beta, S0 = inputs
+        B = w.B
+        est_rate = 2.0e9 * threads
+        per_seq = w.T * w.H * 6 * w.dk * w.dv
+        nb = max(1, min(B, int(budget_s * est_rate // per_seq)))
+        args = [f64(x[:nb]) for x in (q, k, v, beta)]
+        s0 = None if S0 is None else f64(S0[:nb])
+        t0 = time.perf_counter()
+        oracle.deltanet_fwd(*args, s0)
+        dt = time.perf_counter() - t0
+        toks = nb * w.T
+        sample = f"{nb} of {B} sequences ({toks} tokens x {w.H} heads)"
+        units = nb * w.H
+    return {"value": toks / dt, "unit": "tokens/s", "cores": int(min(threads, units)),
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="layer_b8_h16_t4096")
+    ap.add_argument("--cp-groups", type=int, default=1,
+                    help="1 serial chunk chain, 0 library choice, G>1 forced")
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="target seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of 1 GiB (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is described in DESIGN.md, not implemented).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    esz = 2 if w.dtype == "bf16" else 4
+
+    print(f"[bench] workload {w.name}: generating inputs on {dev}", file=sys.stderr, flush=True)
+    inputs = workload_inputs(w, seed=args.seed, device=str(dev))
+    if w.varlen:
+        q, k, v, beta, cu, S0, lengths = inputs
+        n_tokens = int(sum(lengths))
+        n_units = w.N * w.H
+        order = dn.longest_first_order(cu)
+        o = torch.empty_like(v)
+        Sf = torch.empty((w.N, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+
+        def step():
+            dn.deltanet_fwd_varlen(q, k, v, beta, cu, S0, seq_order=order, o=o, S_final=Sf)
+        config = {"workload": w.name, "N": w.N, "H": w.H, "total_T": n_tokens, "dk": w.dk,
+                  "dv": w.dv, "chunk": w.chunk, "len_range": [w.len_lo, w.len_hi]}
+        groups = 1
+    else:
+        q, k, v, beta, S0 = inputs
+        n_tokens = w.B * w.T
+        n_units = w.B * w.H
+        o = torch.empty_like(v)
+        Sf = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+        need = dn.deltanet_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, args.cp_groups)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        groups = (args.cp_groups if args.cp_groups > 0 else
+                  dn.deltanet_pick_cp_groups(w.B, w.H, w.T, w.dk, w.dv, w.chunk))
+
+        def step():
+            dn.deltanet_fwd(q, k, v, beta, S0, o=o, S_final=Sf, cp_groups=args.cp_groups,
+                            workspace=ws)
+        config = {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                  "chunk": w.chunk, "cp_groups": groups}
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps between two synchronisations. Every launch goes on
+    # torch's current stream, so events recorded there bracket each step.
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = sum(per_step_ms) / len(per_step_ms)
+    if not bool(torch.isfinite(o).all()) or not bool(torch.isfinite(Sf).all()):
+        print("bench.py: non-finite output", file=sys.stderr)
+        sys.exit(3)
+
+    tokens_per_s = n_tokens / (ms_per_step / 1e3)
+    head_tokens = n_tokens * w.H
+    flops = head_tokens * flops_per_head_token(w.chunk, w.dk, w.dv)
+    peak_flops = PEAK_BF16_FLOPS if w.dtype == "bf16" else PEAK_FP32_FLOPS
+    nbytes = algorithmic_bytes(w, esz, n_tokens, n_units, S0 is not None, True)
+    mfma_frac = flops / (ms_per_step / 1e3) / peak_flops
+
+    # Dominant kernel: the serial path is one launch per step; with context
+    # parallelism the step holds three launches and the events cover all of
+    # them, so the figure is then a whole-step rate.
+    achieved_gbps = nbytes / (avg_launch_ms / 1e3) / 1e9
+    traffic = load_traffic(w.name, nbytes) if groups == 1 else None
+    roofline = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_BPS / 1e9,
+                "unit": "GB/s", "frac": round(achieved_gbps * 1e9 / PEAK_HBM_BPS, 4),
+                "traffic": traffic, "kernel": "chain_kernel<bf16,128,128,out>"
+                if w.dtype == "bf16" and w.dk == 128 and w.dv == 128 else "chain_kernel",
+                "algorithmic_bytes": nbytes, "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                "mfma_tflops": round(flops / (avg_launch_ms / 1e3) / 1e12, 1),
+                "mfma_frac": round(flops / (avg_launch_ms / 1e3) / peak_flops, 4)}
+
+    result = {
+        "metric": "forward tokens/sec + % bf16 MFMA peak, B=8 H=16 T=4096 d=128 chunk=64",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": config,
+        "mfma_frac_of_bf16_peak": round(mfma_frac, 4),
+        "flops_per_step": flops,
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inputs, w, w.varlen, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,17 +5,25 @@
 // "Linear Attention, Visualized" (Haoran Zhang), DeltaNet > "Complete
 // per-chunk algorithm", with the state transposed ("Context Parallelism for
 // DeltaNet", yywangcs, section 2: S is dv x dk):
-//   A  Gram G = K K^T and the masked scores P = (Q K^T) lower-inclusive
-//   B  diagonal 16x16 blocks of N = (I + diag(beta) L)^-1 by forward
-//      substitution, one wave per block ("Solving for U": unit lower
-//      triangular, row by row)
+//   A  Gram and masked scores: A = diag(beta) (K K^T) strictly lower (fp32,
+//      the matrix of the triangular solve) and P = (Q K^T) lower-inclusive
+//   B  diagonal 16x16 blocks of N = (I + A)^-1 by forward substitution, one
+//      column per lane, entries of A broadcast across the lane row with DPP
+//      ("Solving for U": unit lower triangular, solved row after row)
 //   C  off-diagonal blocks of N by block forward substitution on the matrix
 //      cores; T = N diag(beta) solves (I + diag(beta) L) T = diag(beta)
-//   D  W = T K (shared, to LDS as -W) and U = T V (per wave, kept in registers)
+//   D  W = T K (shared, stored as -W) and U = T V (per wave, in registers)
 //   E  the chain: Z = U - W S^T, O = Q S^T + P Z, S <- S + Z^T K
 // Rows of S are independent (row j of S, Z, U and O needs only row j and the
 // shared K, Q, W), so each wave owns 16 state rows and runs E on its own;
 // only A-D are shared through LDS.
+//
+// Two kernels use these phases. chain_kernel_pipe (bf16) is software
+// pipelined: iteration r runs E of chunk r in the same barrier intervals as
+// A-D of chunk r+1 (A with Z, B with O, C with the S update, D with the
+// staging of chunk r+2), so the VALU- and LDS-heavy preparation overlaps the
+// matrix-core chain. chain_kernel_serial (fp32, whose operands do not fit
+// two chunks in LDS) runs A-E one after the other.
 //
 // Matrix-core layout facts used throughout (16x16 tiles, wave64, lane
 // l = 16*g + c with g = l/16, c = l%16):
@@ -28,6 +36,15 @@
 // registers. A 16x16x32 bf16 product takes two k16 fragments (k blocks 2s and
 // 2s+1); since A and B use the same pairing of (lane, value) to k, any
 // consistent order of k inside the instruction is exact.
+//
+// Fragments are read from LDS in two ways. A "row" fragment (4 consecutive
+// elements of one row) is one 8-byte read. A "column" fragment (4 consecutive
+// rows of one column) of a row-major 16-bit matrix comes from the gfx950
+// transposing read ds_read_b64_tr_b16: inside each 16-lane group, lane i
+// receives element i%4 of the 8-byte chunks supplied by lanes i/4 + 4e
+// (e = 0..3), so lane p supplies row 4g + p/4, columns 4(p%4)..+3 and lane c
+// receives column c, rows 4g..4g+3. K and V therefore stay row-major in LDS,
+// and T is kept transposed so that every write of T is a vector store.
 #include "dn_internal.h"
 
 namespace dn {
@@ -37,6 +54,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <typename E> struct Tr;
 
@@ -45,7 +63,6 @@ template <> struct Tr<__bf16> {
     using F = bf16x4; // k16 fragment
     using V = bf16x8; // 16-byte vector
     static constexpr int kVec = 8;
-    static constexpr int kPad = 8; // LDS row padding, elements (16 bytes)
     __device__ static inline f32x4 mma16(f32x4 c, F a, F b) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                          __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
@@ -65,16 +82,20 @@ template <> struct Tr<__bf16> {
     }
     __device__ static inline float tof(__bf16 x) { return (float)x; }
     __device__ static inline __bf16 fromf(float x) { return (__bf16)x; }
+    // Y[k0 + 4g + e][n0 + c], e = 0..3, from a row-major LDS matrix (ld elements).
+    __device__ static inline F ldcol(const __bf16 *Y, int ld, int k0, int n0, int g, int c) {
+        const __bf16 *p = Y + (k0 + 4 * g + (c >> 2)) * ld + n0 + 4 * (c & 3);
+        return __builtin_bit_cast(F, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
+    }
 };
 
 // fp32 operands: four 16x16x4 products per k16 fragment. Product j takes
 // value j of every lane group, i.e. k = 4g + j, so the four together cover the
-// 16-deep block once.
+// 16-deep block once. Column fragments are four scalar reads.
 template <> struct Tr<float> {
     using F = f32x4;
     using V = f32x4;
     static constexpr int kVec = 4;
-    static constexpr int kPad = 4;
     __device__ static inline f32x4 mma16(f32x4 c, F a, F b) {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
@@ -88,36 +109,58 @@ template <> struct Tr<float> {
     __device__ static inline F cvt(f32x4 x) { return x; }
     __device__ static inline float tof(float x) { return x; }
     __device__ static inline float fromf(float x) { return x; }
+    __device__ static inline F ldcol(const float *Y, int ld, int k0, int n0, int g, int c) {
+        const float *p = Y + (k0 + 4 * g) * ld + n0 + c;
+        F r = {p[0], p[ld], p[2 * ld], p[3 * ld]};
+        return r;
+    }
 };
 
-// LDS carve-up of the chain kernel (byte offsets). Row strides are padded by
-// 16 bytes so that the 16 rows read by one fragment load fall on distinct banks.
-template <typename E, int DK> struct Smem {
-    static constexpr int LDK = DK + Tr<E>::kPad;     // Ks, Qs, Ws: [C][LDK]
-    static constexpr int LDC = kChunk + Tr<E>::kPad; // Kt: [DK][LDC]; Vt: [R][LDC]; Ts, Ps: [C][LDC]
-    static constexpr int LDG = kChunk + 4;           // Gs, Ns (fp32): [C][LDG]
-    static constexpr size_t oKs = 0;
-    static constexpr size_t oQs = oKs + sizeof(E) * kChunk * LDK;
-    static constexpr size_t oKt = oQs + sizeof(E) * kChunk * LDK;
-    static constexpr size_t oVt = oKt + sizeof(E) * DK * LDC;
-    static constexpr size_t oTs = oVt + sizeof(E) * kRows * LDC;
-    static constexpr size_t oPs = oTs + sizeof(E) * kChunk * LDC;
-    static constexpr size_t oGs = oPs + sizeof(E) * kChunk * LDC;
-    // Ws (-W, element type) shares space with Ns (fp32 diagonal inverses): Ns
-    // lives from phase B to C, Ws from D to E.
-    static constexpr size_t oWs = oGs + sizeof(float) * kChunk * LDG;
-    static constexpr size_t szWs = sizeof(E) * kChunk * LDK;
-    static constexpr size_t szNs = sizeof(float) * kChunk * LDG;
-    static constexpr size_t oBs = oWs + (szWs > szNs ? szWs : szNs);
-    static constexpr size_t total = oBs + sizeof(float) * kChunk;
-};
-
-template <typename E> __device__ inline typename Tr<E>::F ldf(const E *p) {
-    return *reinterpret_cast<const typename Tr<E>::F *>(p);
+template <typename E> __device__ inline typename Tr<E>::F ldrow(const E *Y, int ld, int row, int k0, int g) {
+    return *reinterpret_cast<const typename Tr<E>::F *>(Y + row * ld + k0 + 4 * g);
 }
 template <typename E> __device__ inline void stf(E *p, typename Tr<E>::F x) {
     *reinterpret_cast<typename Tr<E>::F *>(p) = x;
 }
+
+// Broadcast lane I of each 16-lane row to the whole row (DPP row_newbcast).
+template <int I> __device__ inline float row_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + I,
+                                                              0xF, 0xF, true));
+}
+
+// One column of (I + A)^-1 for a 16x16 strictly lower A held by rows (lane
+// c16 of each 16-lane row holds row c16 of A): right-looking substitution,
+// once x_J is final it is removed from every row below it.
+template <int J> __device__ inline void solve_step(float (&x)[16], const float (&arow)[16]) {
+    if constexpr (J < 15) {
+        const float nxj = -x[J];
+#define DN_UPD(I)                                                                                              \
+    if constexpr (I > J) x[I] = fmaf(row_bcast<I>(arow[J]), nxj, x[I]);
+        DN_UPD(1) DN_UPD(2) DN_UPD(3) DN_UPD(4) DN_UPD(5) DN_UPD(6) DN_UPD(7) DN_UPD(8)
+        DN_UPD(9) DN_UPD(10) DN_UPD(11) DN_UPD(12) DN_UPD(13) DN_UPD(14) DN_UPD(15)
+#undef DN_UPD
+        solve_step<J + 1>(x, arow);
+    }
+}
+
+// Row strides (elements), padded to 32 bytes beyond a multiple of 256 so that
+// the 16 rows touched by one fragment read (row or transposing) spread over
+// the LDS banks.
+template <typename E, int DK> struct Ld {
+    static constexpr int kPadE = 32 / sizeof(E);
+    static constexpr int K = DK + kPadE;     // K, Q, W: [C][K]
+    static constexpr int V = kRows + kPadE;  // V tile: [C][V]
+    static constexpr int T = kChunk + kPadE; // T^T, P: [C][T]
+    static constexpr int A = kChunk + 4;     // A (fp32): [C][A]
+    static constexpr int N = 16 + kPadE;     // N^T, 4 diagonal blocks: [64][N]
+    static constexpr size_t szK = sizeof(E) * kChunk * K;
+    static constexpr size_t szV = sizeof(E) * kChunk * V;
+    static constexpr size_t szT = sizeof(E) * kChunk * T;
+    static constexpr size_t szA = sizeof(float) * kChunk * A;
+    static constexpr size_t szN = sizeof(E) * 64 * N;
+    static constexpr size_t szWA = szA > szK ? szA : szK; // W and A share space
+};
 
 // Block index -> (unit, tile). Groups of 8 units are interleaved so that all
 // tiles of one unit get block indices congruent mod 8: the dispatcher deals
@@ -137,367 +180,800 @@ __device__ inline void map_block(int x, int n_units, int n_tiles, int &u, int &t
     }
 }
 
-// Off-diagonal blocks of column block b of N = (I + A)^-1, A = diag(beta) L:
-//   N_ab = -N_aa * sum_{c=b}^{a-1} A_ac N_cb,   a = b+1..3,
-// then T_ab = N_ab diag(beta_b). frag[c] holds N_cb as a k16 B fragment.
-template <typename E, int b>
-__device__ inline void offdiag_column(typename Tr<E>::F nbb, const float *Gs, const float *Ns,
-                                      const float *Bs, E *Ts, int g, int c16, int LDG, int LDC) {
-    using TR = Tr<E>;
-    using F = typename TR::F;
-    F frag[4];
-    frag[b] = nbb;
-    const float beta_col = Bs[16 * b + c16];
-#pragma unroll
-    for (int a = b + 1; a < 4; ++a) {
-        const float beta_row = Bs[16 * a + c16];
-        f32x4 R = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = b; c < a; ++c) {
-            f32x4 gr = *reinterpret_cast<const f32x4 *>(Gs + (16 * a + c16) * LDG + 16 * c + 4 * g);
-            R = TR::mma16(R, TR::cvt(gr * beta_row), frag[c]);
-        }
-        const f32x4 nr = *reinterpret_cast<const f32x4 *>(Ns + (16 * a + c16) * LDG + 16 * a + 4 * g);
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 nab = -TR::mma16(z, TR::cvt(nr), TR::cvt(R));
-        frag[a] = TR::cvt(nab);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            Ts[(16 * a + 4 * g + i) * LDC + 16 * b + c16] = TR::fromf(nab[i] * beta_col);
-    }
-}
+// What one workgroup works on: a token range of one (sequence, head), a
+// 64-row tile of the state, where the tile starts from and where it ends.
+struct Work {
+    int64_t tok0;
+    int len, h, row0;
+    const float *Sin; // initial rows, or nullptr (zero / identity)
+    float *Sout;      // final rows, or nullptr
+    bool identity, transposed_out, has_v;
+};
 
-template <typename E, int DK, int DV, bool WRITE_O>
-__global__ __launch_bounds__(kThreads) void chain_kernel(const ChainArgs a) {
-    using TR = Tr<E>;
-    using F = typename TR::F;
-    using V = typename TR::V;
-    using SM = Smem<E, DK>;
-    constexpr int NMT = DK / 16;                 // 16-wide dk tiles of the state
-    constexpr int NKB = DK / 32;                 // 32-deep k blocks over dk
-    constexpr int KQV = DK / TR::kVec;           // 16-byte vectors per K/Q row
-    constexpr int NKQ = kChunk * KQV / kThreads; // K (and Q) vectors per thread
-    constexpr int VV = kRows / TR::kVec;         // vectors per V-tile row
-    constexpr int NVV = kChunk * VV / kThreads;  // V vectors per thread
-    constexpr int LDK = SM::LDK, LDC = SM::LDC, LDG = SM::LDG;
-    static_assert(NKQ * kThreads == kChunk * KQV && NVV * kThreads == kChunk * VV, "tiling");
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SM::total];
-    E *Ks = reinterpret_cast<E *>(smem + SM::oKs);
-    E *Qs = reinterpret_cast<E *>(smem + SM::oQs);
-    E *Kt = reinterpret_cast<E *>(smem + SM::oKt);
-    E *Vt = reinterpret_cast<E *>(smem + SM::oVt);
-    E *Ts = reinterpret_cast<E *>(smem + SM::oTs);
-    E *Ps = reinterpret_cast<E *>(smem + SM::oPs);
-    float *Gs = reinterpret_cast<float *>(smem + SM::oGs);
-    float *Ns = reinterpret_cast<float *>(smem + SM::oWs);
-    E *Ws = reinterpret_cast<E *>(smem + SM::oWs);
-    float *Bs = reinterpret_cast<float *>(smem + SM::oBs);
-
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-
-    // ---------------- work decode ----------------
+template <int DK, int DV> __device__ inline Work decode_work(const ChainArgs &a) {
     int u, tau;
     map_block(blockIdx.x, a.n_units, a.n_tiles, u, tau);
     const int H = a.H;
-    int64_t tok0 = 0;
-    int len = 0, h = 0, row0 = tau * kRows;
-    const float *Sin = nullptr;
-    float *Sout = nullptr;
-    bool identity = false, transposed_out = false, has_v = true;
+    Work wk = {0, 0, 0, tau * kRows, nullptr, nullptr, false, false, true};
     if (a.kind == kDense) {
         const int b = u / H;
-        h = u - b * H;
-        tok0 = (int64_t)b * a.T;
-        len = a.T;
-        if (a.S0) Sin = a.S0 + ((int64_t)u * DV + row0) * DK;
-        if (a.S_final) Sout = a.S_final + ((int64_t)u * DV + row0) * DK;
+        wk.h = u - b * H;
+        wk.tok0 = (int64_t)b * a.T;
+        wk.len = a.T;
+        if (a.S0) wk.Sin = a.S0 + ((int64_t)u * DV + wk.row0) * DK;
+        if (a.S_final) wk.Sout = a.S_final + ((int64_t)u * DV + wk.row0) * DK;
     } else if (a.kind == kVarlen) {
         const int rank = u / H;
-        h = u - rank * H;
+        wk.h = u - rank * H;
         const int n = a.seq_order ? a.seq_order[rank] : rank;
-        tok0 = a.cu_seqlens[n];
-        len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
-        const int64_t su = (int64_t)n * H + h;
-        if (a.S0) Sin = a.S0 + (su * DV + row0) * DK;
-        if (a.S_final) Sout = a.S_final + (su * DV + row0) * DK;
+        wk.tok0 = a.cu_seqlens[n];
+        wk.len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+        const int64_t su = (int64_t)n * H + wk.h;
+        if (a.S0) wk.Sin = a.S0 + (su * DV + wk.row0) * DK;
+        if (a.S_final) wk.Sout = a.S_final + (su * DV + wk.row0) * DK;
     } else {
         const int groups = (a.kind == kCpOutput) ? a.G : a.G - 1;
         const int bh = u / groups;
         const int gi = u - bh * groups;
         const int b = bh / H;
-        h = bh - b * H;
+        wk.h = bh - b * H;
         const int t_begin = gi * a.chunks_per_group * kChunk;
         const int t_end = min(a.T, (gi + 1) * a.chunks_per_group * kChunk);
-        tok0 = (int64_t)b * a.T + t_begin;
-        len = t_end - t_begin;
+        wk.tok0 = (int64_t)b * a.T + t_begin;
+        wk.len = t_end - t_begin;
         const int64_t slot = (int64_t)bh * a.G + gi;
         if (a.kind == kCpOutput) {
             if (gi == 0) {
-                if (a.S0) Sin = a.S0 + ((int64_t)bh * DV + row0) * DK;
+                if (a.S0) wk.Sin = a.S0 + ((int64_t)bh * DV + wk.row0) * DK;
             } else {
-                Sin = a.ws_S + (slot * DV + row0) * DK;
+                wk.Sin = a.ws_S + (slot * DV + wk.row0) * DK;
             }
-            if (gi == a.G - 1 && a.S_final) Sout = a.S_final + ((int64_t)bh * DV + row0) * DK;
+            if (gi == a.G - 1 && a.S_final) wk.Sout = a.S_final + ((int64_t)bh * DV + wk.row0) * DK;
         } else if (tau < DV / kRows) {
-            Sout = a.ws_Q + (slot * DV + row0) * DK; // Q_g rows, from a zero start
+            wk.Sout = a.ws_Q + (slot * DV + wk.row0) * DK; // Q_g rows, from a zero start
         } else {
-            row0 = (tau - DV / kRows) * kRows; // rows of P_g (dk index), from identity
-            identity = true;
-            has_v = false;
-            transposed_out = true;
-            Sout = a.ws_P + slot * DK * DK;
+            wk.row0 = (tau - DV / kRows) * kRows; // rows of P_g (dk index), from identity
+            wk.identity = true;
+            wk.has_v = false;
+            wk.transposed_out = true;
+            wk.Sout = a.ws_P + slot * DK * DK;
         }
     }
+    return wk;
+}
 
-    // ---------------- state init ----------------
-    // Sacc[m][i] = S[row0 + 16w + c16][16m + 4g + i]
-    const int srow = row0 + 16 * w + c16;
-    f32x4 Sacc[NMT];
-#pragma unroll
-    for (int m = 0; m < NMT; ++m) {
-        if (Sin) {
-            Sacc[m] = *reinterpret_cast<const f32x4 *>(Sin + (16 * w + c16) * DK + 16 * m + 4 * g);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                Sacc[m][i] = (identity && (16 * m + 4 * g + i) == srow) ? 1.f : 0.f;
-        }
-    }
+// The per-chunk phases, shared by both kernels. Each is executed by every
+// wave (w = wave, g = lane group, c16 = lane in group) on LDS operands.
+//
+// Every phase is split into a fetch (all LDS operand fragments of the phase
+// into registers) and a compute step. The kernels put a scheduling fence
+// between the fetches and the computes of a barrier interval: all reads of
+// the interval are in flight before the first matrix product needs one, so
+// LDS latency is paid once per interval instead of once per product (with one
+// wave per SIMD nothing else would hide it).
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-    const int NC = (len + kChunk - 1) / kChunk;
-    const int64_t sqk = (int64_t)H * DK, sv = (int64_t)H * DV;
-    const E *qg = reinterpret_cast<const E *>(a.q) + tok0 * sqk + (int64_t)h * DK;
-    const E *kg = reinterpret_cast<const E *>(a.k) + tok0 * sqk + (int64_t)h * DK;
-    const E *vg = reinterpret_cast<const E *>(a.v) + tok0 * sv + (int64_t)h * DV + row0;
-    const E *bg = reinterpret_cast<const E *>(a.beta) + tok0 * H + h;
-    E *og = WRITE_O ? reinterpret_cast<E *>(a.o) + tok0 * sv + (int64_t)h * DV + row0 : nullptr;
+template <typename E, int DK> struct Phases {
+    using TR = Tr<E>;
+    using F = typename TR::F;
+    using L = Ld<E, DK>;
+    static constexpr int NMT = DK / 16; // 16-wide dk tiles
+    static constexpr int NKB = DK / 32; // 32-deep k blocks over dk
 
-    // ---------------- chunk staging (global -> registers -> LDS) ----------------
-    V rk[NKQ], rq[NKQ], rv[NVV];
-    float rb = 0.f;
-    auto gload = [&](int c) {
-        const int nval = min(kChunk, len - c * kChunk);
-        const int64_t base = (int64_t)c * kChunk;
-        const V zero = {};
-#pragma unroll
-        for (int p = 0; p < NKQ; ++p) {
-            const int vi = p * kThreads + tid, row = vi / KQV, cv = vi - row * KQV;
-            if (row < nval) {
-                rk[p] = *reinterpret_cast<const V *>(kg + (base + row) * sqk + cv * TR::kVec);
-                rq[p] = *reinterpret_cast<const V *>(qg + (base + row) * sqk + cv * TR::kVec);
-            } else {
-                rk[p] = zero;
-                rq[p] = zero;
-            }
-        }
-        if (has_v) {
-#pragma unroll
-            for (int p = 0; p < NVV; ++p) {
-                const int vi = p * kThreads + tid, row = vi / VV, cv = vi - row * VV;
-                rv[p] = (row < nval)
-                            ? *reinterpret_cast<const V *>(vg + (base + row) * sv + cv * TR::kVec)
-                            : zero;
-            }
-        }
-        if (tid < kChunk) rb = (tid < nval) ? TR::tof(bg[(base + tid) * H]) : 0.f;
+    // ---- A: Gram (as the solve's A = beta_i k_i.k_j, j < i, fp32) and masked
+    // scores P. Wave roles: 0 Gram rows {0,3}, 1 scores rows {0,3}, 2 Gram
+    // rows {1,2}, 3 scores rows {1,2}; tile (a, c <= a) = K_c X_a^T with X = K
+    // (Gram) or Q (scores). The role is a template argument so each wave's code
+    // is free of branches.
+    template <int W> struct GramFrags {
+        static constexpr int A1 = (W < 2) ? 0 : 1, A2 = (W < 2) ? 3 : 2;
+        F xb[2][NKB][2]; // X rows of blocks A1, A2
+        F kc[A2 + 1][NKB][2]; // K rows of blocks 0..A2
     };
-    auto lstore = [&]() {
+    template <int W>
+    __device__ static inline void gram_fetch(GramFrags<W> &f, const E *Ks, const E *Qs, int g, int c16) {
+        using G = GramFrags<W>;
+        const E *X = (W & 1) ? Qs : Ks;
 #pragma unroll
-        for (int p = 0; p < NKQ; ++p) {
-            const int vi = p * kThreads + tid, row = vi / KQV, cv = vi - row * KQV;
-            *reinterpret_cast<V *>(Ks + row * LDK + cv * TR::kVec) = rk[p];
-            *reinterpret_cast<V *>(Qs + row * LDK + cv * TR::kVec) = rq[p];
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int e = 0; e < TR::kVec; ++e) Kt[(cv * TR::kVec + e) * LDC + row] = rk[p][e];
-        }
-        if (has_v) {
+            for (int h2 = 0; h2 < 2; ++h2) {
+                f.xb[0][kb][h2] = ldrow(X, L::K, 16 * G::A1 + c16, 32 * kb + 16 * h2, g);
+                f.xb[1][kb][h2] = ldrow(X, L::K, 16 * G::A2 + c16, 32 * kb + 16 * h2, g);
 #pragma unroll
-            for (int p = 0; p < NVV; ++p) {
-                const int vi = p * kThreads + tid, row = vi / VV, cv = vi - row * VV;
-#pragma unroll
-                for (int e = 0; e < TR::kVec; ++e) Vt[(cv * TR::kVec + e) * LDC + row] = rv[p][e];
+                for (int cb = 0; cb <= G::A2; ++cb)
+                    f.kc[cb][kb][h2] = ldrow(Ks, L::K, 16 * cb + c16, 32 * kb + 16 * h2, g);
             }
-        }
-        if (tid < kChunk) Bs[tid] = rb;
-    };
-
-    if (NC > 0) gload(0);
-    // T and P are lower triangular: their upper blocks are never written, so
-    // zero both once.
-    for (int i = tid; i < kChunk * LDC; i += kThreads) {
-        Ts[i] = TR::fromf(0.f);
-        Ps[i] = TR::fromf(0.f);
     }
-    if (NC > 0) lstore();
-    __syncthreads();
-
-    f32x4 Zacc[4];
-    for (int c = 0; c < NC; ++c) {
-        const int nval = min(kChunk, len - c * kChunk);
-        if (c + 1 < NC) gload(c + 1);
-
-        // ---- A: Gram and masked scores, lower block pairs (ab >= cb) ----
-        // Product p = 2*pair + isP; wave w takes p = w, w+4, ... (waves 0,2: G; 1,3: P).
-        {
-            const int isP = w & 1;
+    template <int W>
+    __device__ static inline void gram_compute(const GramFrags<W> &f, const float *Bs, float *As, E *Ps, int g,
+                                               int c16) {
+        using G = GramFrags<W>;
+        constexpr bool isP = W & 1;
 #pragma unroll
-            for (int p = w; p < 20; p += 4) {
-                const int pair = p >> 1;
-                const int ab = pair >= 6 ? 3 : pair >= 3 ? 2 : pair >= 1 ? 1 : 0;
-                const int cb = pair - (ab * (ab + 1)) / 2;
-                const E *Ar = Ks + (16 * cb + c16) * LDK;
-                const E *Br = (isP ? Qs : Ks) + (16 * ab + c16) * LDK;
+        for (int which = 0; which < 2; ++which) {
+            const int ab = which ? G::A2 : G::A1;
+#pragma unroll
+            for (int cb = 0; cb <= G::A2; ++cb) {
+                if (cb > ab) continue;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
-                    acc = TR::mma32(acc, ldf(Ar + 32 * kb + 4 * g), ldf(Ar + 32 * kb + 16 + 4 * g),
-                                    ldf(Br + 32 * kb + 4 * g), ldf(Br + 32 * kb + 16 + 4 * g));
-                // acc[i] = k_{16cb+4g+i} . x_{16ab+c16}, x = k (Gram) or q (scores)
+                    acc = TR::mma32(acc, f.kc[cb][kb][0], f.kc[cb][kb][1], f.xb[which][kb][0], f.xb[which][kb][1]);
+                // acc[e] = k_{16cb+4g+e} . x_{16ab+c16}
                 const int row = 16 * ab + c16, col = 16 * cb + 4 * g;
-                if (!isP) {
-                    *reinterpret_cast<f32x4 *>(Gs + row * LDG + col) = acc;
+                if constexpr (!isP) {
+                    const float br = Bs[row];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = (col + e < row) ? acc[e] * br : 0.f;
+                    *reinterpret_cast<f32x4 *>(As + row * L::A + col) = acc;
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (col + i > row) acc[i] = 0.f;
-                    stf(Ps + row * LDC + col, TR::cvt(acc));
+                    for (int e = 0; e < 4; ++e) acc[e] = (col + e > row) ? 0.f : acc[e];
+                    stf(Ps + row * L::T + col, TR::cvt(acc));
                 }
             }
         }
-        __syncthreads();
+    }
 
-        // ---- B: diagonal blocks N_ww = (I + A_ww)^-1, column c16 per lane ----
-        F nfrag;
-        {
-            const int o = 16 * w;
-            float x[16];
+    // ---- B: N_ww = (I + A_ww)^-1 for the diagonal block w, column c16 per
+    // lane (all four lane groups compute the same column). Writes N_ww^T and
+    // the diagonal block of T^T; returns N_ww as a k16 B fragment.
+    struct DiagFrags {
+        float arow[16]; // A[16w + c16][16w + j]
+        float bc;       // beta_{16w + c16}
+    };
+    __device__ static inline void diag_fetch(DiagFrags &f, const float *As, const float *Bs, int w, int c16) {
+        const int o = 16 * w;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < i; ++j) s = fmaf(Gs[(o + i) * LDG + o + j], x[j], s);
-                x[i] = (i == c16 ? 1.f : 0.f) - Bs[o + i] * s;
-            }
-            if (g == 0) {
-                const float bc = Bs[o + c16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    Ns[(o + i) * LDG + o + c16] = x[i];
-                    Ts[(o + i) * LDC + o + c16] = TR::fromf(x[i] * bc);
-                }
-            }
-            f32x4 xf;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xf[i] = g == 0 ? x[i] : g == 1 ? x[4 + i] : g == 2 ? x[8 + i] : x[12 + i];
-            nfrag = TR::cvt(xf);
+        for (int j4 = 0; j4 < 4; ++j4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(As + (o + c16) * L::A + o + 4 * j4);
+            f.arow[4 * j4 + 0] = t[0];
+            f.arow[4 * j4 + 1] = t[1];
+            f.arow[4 * j4 + 2] = t[2];
+            f.arow[4 * j4 + 3] = t[3];
         }
-        __syncthreads();
+        f.bc = Bs[o + c16];
+    }
+    __device__ static inline F diag_compute(const DiagFrags &f, E *NsT, E *TsT, int w, int g, int c16) {
+        const int o = 16 * w;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == c16) ? 1.f : 0.f;
+        solve_step<0>(x, f.arow);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 xv = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
+            // every lane group writes the same values: no branch needed
+            stf(NsT + (o + c16) * L::N + 4 * i4, TR::cvt(xv));
+            stf(TsT + (o + c16) * L::T + o + 4 * i4, TR::cvt(xv * f.bc));
+        }
+        f32x4 xf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            xf[i] = g == 0 ? x[i] : g == 1 ? x[4 + i] : g == 2 ? x[8 + i] : x[12 + i];
+        return TR::cvt(xf);
+    }
 
-        // ---- C: off-diagonal blocks of N, column block w ----
-        if (w == 0) offdiag_column<E, 0>(nfrag, Gs, Ns, Bs, Ts, g, c16, LDG, LDC);
-        else if (w == 1) offdiag_column<E, 1>(nfrag, Gs, Ns, Bs, Ts, g, c16, LDG, LDC);
-        else if (w == 2) offdiag_column<E, 2>(nfrag, Gs, Ns, Bs, Ts, g, c16, LDG, LDC);
-        __syncthreads();
+    // ---- C: off-diagonal blocks of column block b of N:
+    //   N_ab = -N_aa * sum_{c=b}^{a-1} A_ac N_cb,  a = b+1..3,  T_ab = N_ab diag(beta_b).
+    template <int b> struct OffFrags {
+        F arow[4][4]; // A_ac rows (a > b, b <= c < a)
+        F nrow[4];    // rows of N_aa (a > b)
+        float beta_col;
+    };
+    template <int b>
+    __device__ static inline void off_fetch(OffFrags<b> &f, const float *As, const E *NsT, const float *Bs, int g,
+                                            int c16) {
+        f.beta_col = Bs[16 * b + c16];
+#pragma unroll
+        for (int a = b + 1; a < 4; ++a) {
+#pragma unroll
+            for (int c = b; c < a; ++c)
+                f.arow[a][c] =
+                    TR::cvt(*reinterpret_cast<const f32x4 *>(As + (16 * a + c16) * L::A + 16 * c + 4 * g));
+            f.nrow[a] = TR::ldcol(NsT + a * 16 * L::N, L::N, 0, 0, g, c16); // row c16 of N_aa
+        }
+    }
+    template <int b>
+    __device__ static inline void off_compute(const OffFrags<b> &f, F nbb, E *TsT, int g, int c16) {
+        F frag[4];
+        frag[b] = nbb;
+#pragma unroll
+        for (int a = b + 1; a < 4; ++a) {
+            f32x4 R = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = b; c < a; ++c) R = TR::mma16(R, f.arow[a][c], frag[c]);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 nab = -TR::mma16(z, f.nrow[a], TR::cvt(R));
+            frag[a] = TR::cvt(nab);
+            // nab[e] = N[16a + 4g + e][16b + c16] -> T^T row 16b + c16, columns 16a + 4g..
+            stf(TsT + (16 * b + c16) * L::T + 16 * a + 4 * g, TR::cvt(nab * f.beta_col));
+        }
+    }
 
-        // ---- D: -W = -(T K) to LDS (shared), U = T V for this wave's rows ----
+    // ---- D: -W = -(T K) for this wave's dk tiles to LDS; U = T V for this
+    // wave's 16 value rows (zero when there is no V).
+    struct WUFrags {
+        F trow[4][4];        // T[16n + c16][16kk + 4g..] (kk <= n | 1)
+        F kcol[NMT / 4][4];  // K[16kk + 4g..][16m + c16] for this wave's dk tiles m
+        F vcol[4];           // V[16kk + 4g..][16w + c16]
+    };
+    __device__ static inline void wu_fetch(WUFrags &f, const E *Ks, const E *Vs, const E *TsT, bool has_v, int w,
+                                           int g, int c16) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                if (kk <= (n | 1)) f.trow[n][kk] = TR::ldcol(TsT, L::T, 16 * kk, 16 * n, g, c16);
+#pragma unroll
+        for (int mm = 0; mm < NMT / 4; ++mm)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                f.kcol[mm][kk] = TR::ldcol(Ks, L::K, 16 * kk, 16 * (w * (NMT / 4) + mm), g, c16);
+        if (has_v) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) f.vcol[kk] = TR::ldcol(Vs, L::V, 16 * kk, 16 * w, g, c16);
+        }
+    }
+    __device__ static inline void wu_compute(const WUFrags &f, E *Ws, bool has_v, f32x4 (&Zacc)[4], int w, int g,
+                                             int c16) {
 #pragma unroll
         for (int mm = 0; mm < NMT / 4; ++mm) {
             const int m = w * (NMT / 4) + mm;
-            const E *Ar = Kt + (16 * m + c16) * LDC;
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
-                const E *Br = Ts + (16 * n + c16) * LDC;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s <= n / 2; ++s)
-                    acc = TR::mma32(acc, ldf(Ar + 32 * s + 4 * g), ldf(Ar + 32 * s + 16 + 4 * g),
-                                    ldf(Br + 32 * s + 4 * g), ldf(Br + 32 * s + 16 + 4 * g));
-                // acc[i] = W[16n + c16][16m + 4g + i]
-                stf(Ws + (16 * n + c16) * LDK + 16 * m + 4 * g, TR::cvt(-acc));
+                    acc = TR::mma32(acc, f.kcol[mm][2 * s], f.kcol[mm][2 * s + 1], f.trow[n][2 * s],
+                                    f.trow[n][2 * s + 1]);
+                // acc[e] = W[16n + c16][16m + 4g + e]
+                stf(Ws + (16 * n + c16) * L::K + 16 * m + 4 * g, TR::cvt(-acc));
             }
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (has_v) {
-                const E *Ar = Ts + (16 * t + c16) * LDC;
-                const E *Br = Vt + (16 * w + c16) * LDC;
 #pragma unroll
                 for (int s = 0; s <= t / 2; ++s)
-                    acc = TR::mma32(acc, ldf(Ar + 32 * s + 4 * g), ldf(Ar + 32 * s + 16 + 4 * g),
-                                    ldf(Br + 32 * s + 4 * g), ldf(Br + 32 * s + 16 + 4 * g));
+                    acc = TR::mma32(acc, f.trow[t][2 * s], f.trow[t][2 * s + 1], f.vcol[2 * s], f.vcol[2 * s + 1]);
             }
-            Zacc[t] = acc; // U[16t + 4g + i][row 16w + c16]
+            Zacc[t] = acc; // U[16t + 4g + e][row 16w + c16]
+        }
+    }
+
+    // ---- E1: Z = U - W S^T (Ws holds -W); result as k16 fragments over tokens.
+    struct ZFrags {
+        F wr[4][NKB][2]; // -W rows 16t + c16
+    };
+    __device__ static inline void z_fetch(ZFrags &f, const E *Ws, int g, int c16) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                f.wr[t][kb][0] = ldrow(Ws, L::K, 16 * t + c16, 32 * kb, g);
+                f.wr[t][kb][1] = ldrow(Ws, L::K, 16 * t + c16, 32 * kb + 16, g);
+            }
+    }
+    __device__ static inline void z_compute(const ZFrags &f, const F (&SB)[NMT], const f32x4 (&Zacc)[4], F (&ZB)[4]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 z = Zacc[t];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) z = TR::mma32(z, f.wr[t][kb][0], f.wr[t][kb][1], SB[2 * kb], SB[2 * kb + 1]);
+            ZB[t] = TR::cvt(z); // Z[16t + 4g + e][row 16w + c16]
+        }
+    }
+
+    // ---- E2: O^T tiles = S Q^T + Z^T P^T (with the pre-update S);
+    // Oacc[t][e] = O[16t + c16][16w + 4g + e].
+    struct OFrags {
+        F qr[4][NKB][2]; // Q rows 16t + c16
+        F pr[4][2][2];   // P rows 16t + c16, k blocks s <= t/2
+    };
+    __device__ static inline void o_fetch(OFrags &f, const E *Qs, const E *Ps, int g, int c16) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                f.qr[t][kb][0] = ldrow(Qs, L::K, 16 * t + c16, 32 * kb, g);
+                f.qr[t][kb][1] = ldrow(Qs, L::K, 16 * t + c16, 32 * kb + 16, g);
+            }
+#pragma unroll
+            for (int s = 0; s <= t / 2; ++s) {
+                f.pr[t][s][0] = ldrow(Ps, L::T, 16 * t + c16, 32 * s, g);
+                f.pr[t][s][1] = ldrow(Ps, L::T, 16 * t + c16, 32 * s + 16, g);
+            }
+        }
+    }
+    __device__ static inline void o_compute(const OFrags &f, const F (&SB)[NMT], const F (&ZB)[4], f32x4 (&Oacc)[4]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) acc = TR::mma32(acc, SB[2 * kb], SB[2 * kb + 1], f.qr[t][kb][0], f.qr[t][kb][1]);
+#pragma unroll
+            for (int s = 0; s <= t / 2; ++s) acc = TR::mma32(acc, ZB[2 * s], ZB[2 * s + 1], f.pr[t][s][0], f.pr[t][s][1]);
+            Oacc[t] = acc;
+        }
+    }
+
+    // ---- E3: S^T += K^T Z.
+    struct SFrags {
+        F kc[NMT][4]; // K[16kk + 4g..][16m + c16]
+    };
+    __device__ static inline void s_fetch(SFrags &f, const E *Ks, int g, int c16) {
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) f.kc[m][kk] = TR::ldcol(Ks, L::K, 16 * kk, 16 * m, g, c16);
+    }
+    __device__ static inline void s_compute(const SFrags &f, const F (&ZB)[4], f32x4 (&Sacc)[NMT]) {
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) {
+            Sacc[m] = TR::mma32(Sacc[m], f.kc[m][0], f.kc[m][1], ZB[0], ZB[1]);
+            Sacc[m] = TR::mma32(Sacc[m], f.kc[m][2], f.kc[m][3], ZB[2], ZB[3]);
+        }
+    }
+};
+
+// Global -> register -> LDS staging of one chunk (K, Q, V tile, beta).
+// Loads are unconditional: rows past the end of the sequence re-read the last
+// valid row (always in bounds) and become zeros when written to LDS, so no
+// load sits behind a branch; beta stays raw until it is written.
+template <typename E, int DK> struct Stager {
+    using TR = Tr<E>;
+    using V = typename TR::V;
+    using L = Ld<E, DK>;
+    static constexpr int KQV = DK / TR::kVec;           // vectors per K/Q row
+    static constexpr int NKQ = kChunk * KQV / kThreads; // K (and Q) vectors per thread
+    static constexpr int VV = kRows / TR::kVec;         // vectors per V-tile row
+    static constexpr int NVV = kChunk * VV / kThreads;  // V vectors per thread
+    static_assert(NKQ * kThreads == kChunk * KQV && NVV * kThreads == kChunk * VV, "tiling");
+
+    const E *kg, *qg, *vg, *bg;
+    int64_t sqk, sv;
+    int H, len, tid;
+    bool has_v;
+    V rk[NKQ], rq[NKQ], rv[NVV];
+    E rbeta;
+    int nval;
+
+    __device__ inline void load(int c) {
+        nval = min(kChunk, len - c * kChunk);
+        const int last = nval - 1;
+        const int64_t base = (int64_t)c * kChunk;
+#pragma unroll
+        for (int p = 0; p < NKQ; ++p) {
+            const int vi = p * kThreads + tid, row = min(vi / KQV, last), cv = vi % KQV;
+            rk[p] = *reinterpret_cast<const V *>(kg + (base + row) * sqk + cv * TR::kVec);
+            rq[p] = *reinterpret_cast<const V *>(qg + (base + row) * sqk + cv * TR::kVec);
+        }
+        if (has_v) {
+#pragma unroll
+            for (int p = 0; p < NVV; ++p) {
+                const int vi = p * kThreads + tid, row = min(vi / VV, last), cv = vi % VV;
+                rv[p] = *reinterpret_cast<const V *>(vg + (base + row) * sv + cv * TR::kVec);
+            }
+        }
+        rbeta = bg[(base + min(tid & (kChunk - 1), last)) * H]; // every wave holds all 64
+    }
+    __device__ inline void store_kqb(E *Ks, E *Qs, float *Bs) const {
+        const V zero = {};
+#pragma unroll
+        for (int p = 0; p < NKQ; ++p) {
+            const int vi = p * kThreads + tid, row = vi / KQV, cv = vi % KQV;
+            const bool ok = row < nval;
+            *reinterpret_cast<V *>(Ks + row * L::K + cv * TR::kVec) = ok ? rk[p] : zero;
+            *reinterpret_cast<V *>(Qs + row * L::K + cv * TR::kVec) = ok ? rq[p] : zero;
+        }
+        // the four waves write identical values: no branch needed
+        Bs[tid & (kChunk - 1)] = (tid & (kChunk - 1)) < nval ? TR::tof(rbeta) : 0.f;
+    }
+    __device__ inline void store_v(E *Vs) const {
+        if (!has_v) return;
+        const V zero = {};
+#pragma unroll
+        for (int p = 0; p < NVV; ++p) {
+            const int vi = p * kThreads + tid, row = vi / VV, cv = vi % VV;
+            *reinterpret_cast<V *>(Vs + row * L::V + cv * TR::kVec) = row < nval ? rv[p] : zero;
+        }
+    }
+};
+
+template <typename E, int DK, int DV, bool WRITE_O>
+__device__ inline Stager<E, DK> make_stager(const ChainArgs &a, const Work &wk, int tid) {
+    Stager<E, DK> sg;
+    sg.sqk = (int64_t)a.H * DK;
+    sg.sv = (int64_t)a.H * DV;
+    sg.kg = reinterpret_cast<const E *>(a.k) + wk.tok0 * sg.sqk + (int64_t)wk.h * DK;
+    sg.qg = reinterpret_cast<const E *>(a.q) + wk.tok0 * sg.sqk + (int64_t)wk.h * DK;
+    sg.vg = reinterpret_cast<const E *>(a.v) + wk.tok0 * sg.sv + (int64_t)wk.h * DV + wk.row0;
+    sg.bg = reinterpret_cast<const E *>(a.beta) + wk.tok0 * a.H + wk.h;
+    sg.H = a.H;
+    sg.len = wk.len;
+    sg.tid = tid;
+    sg.has_v = WRITE_O || wk.has_v; // outputs are only written by tiles that have V
+    sg.rbeta = Tr<E>::fromf(0.f);
+    sg.nval = 0;
+    return sg;
+}
+
+// Sacc[m][i] = S[row0 + 16w + c16][16m + 4g + i]
+template <int DK>
+__device__ inline void state_in(f32x4 (&Sacc)[DK / 16], const Work &wk, int w, int g, int c16) {
+    const int srow = wk.row0 + 16 * w + c16;
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m) {
+        if (wk.Sin) {
+            Sacc[m] = *reinterpret_cast<const f32x4 *>(wk.Sin + (16 * w + c16) * DK + 16 * m + 4 * g);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Sacc[m][i] = (wk.identity && (16 * m + 4 * g + i) == srow) ? 1.f : 0.f;
+        }
+    }
+}
+template <int DK>
+__device__ inline void state_out(const f32x4 (&Sacc)[DK / 16], const Work &wk, int w, int g, int c16) {
+    if (!wk.Sout) return;
+    if (!wk.transposed_out) {
+#pragma unroll
+        for (int m = 0; m < DK / 16; ++m)
+            *reinterpret_cast<f32x4 *>(wk.Sout + (16 * w + c16) * DK + 16 * m + 4 * g) = Sacc[m];
+    } else {
+        const int srow = wk.row0 + 16 * w + c16;
+#pragma unroll
+        for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wk.Sout[(int64_t)(16 * m + 4 * g + i) * DK + srow] = Sacc[m][i];
+    }
+}
+
+// O store: Oacc[t][e] = O[16t + c16][16w + 4g + e] of chunk c.
+template <typename E>
+__device__ inline void store_o(E *og, int64_t sv, int c, int nval, const f32x4 (&Oacc)[4], int w, int g,
+                               int c16) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int tok = 16 * t + c16;
+        if (tok < nval) stf(og + ((int64_t)c * kChunk + tok) * sv + 16 * w + 4 * g, Tr<E>::cvt(Oacc[t]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Serial kernel: A, B, C, D, E one after the other, one staging buffer.
+// ---------------------------------------------------------------------------
+template <typename E, int DK> struct SmemSerial {
+    using L = Ld<E, DK>;
+    static constexpr size_t oKs = 0;
+    static constexpr size_t oQs = oKs + L::szK;
+    static constexpr size_t oVs = oQs + L::szK;
+    static constexpr size_t oBs = oVs + L::szV;
+    static constexpr size_t oTs = oBs + sizeof(float) * kChunk;
+    static constexpr size_t oPs = oTs + L::szT;
+    static constexpr size_t oNs = oPs + L::szT;
+    static constexpr size_t oWA = oNs + L::szN;
+    static constexpr size_t total = oWA + L::szWA;
+};
+
+template <typename E, int DK, int DV, bool WRITE_O>
+__global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs a) {
+    using TR = Tr<E>;
+    using F = typename TR::F;
+    using PH = Phases<E, DK>;
+    using SM = SmemSerial<E, DK>;
+    using L = Ld<E, DK>;
+    constexpr int NMT = DK / 16;
+    static_assert(SM::total <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SM::total];
+    E *Ks = reinterpret_cast<E *>(smem + SM::oKs);
+    E *Qs = reinterpret_cast<E *>(smem + SM::oQs);
+    E *Vs = reinterpret_cast<E *>(smem + SM::oVs);
+    float *Bs = reinterpret_cast<float *>(smem + SM::oBs);
+    E *TsT = reinterpret_cast<E *>(smem + SM::oTs);
+    E *Ps = reinterpret_cast<E *>(smem + SM::oPs);
+    E *NsT = reinterpret_cast<E *>(smem + SM::oNs);
+    float *As = reinterpret_cast<float *>(smem + SM::oWA);
+    E *Ws = reinterpret_cast<E *>(smem + SM::oWA);
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const Work wk = decode_work<DK, DV>(a);
+    f32x4 Sacc[NMT];
+    state_in<DK>(Sacc, wk, w, g, c16);
+    const int NC = (wk.len + kChunk - 1) / kChunk;
+    auto sg = make_stager<E, DK, DV, WRITE_O>(a, wk, tid);
+    const bool has_v = WRITE_O || wk.has_v;
+    const int64_t sv = (int64_t)a.H * DV;
+    E *og = WRITE_O ? reinterpret_cast<E *>(a.o) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 : nullptr;
+
+    // T and P are lower triangular and only their lower blocks are written:
+    // zero both once so the blocks above the diagonal stay zero.
+    for (int i = tid; i < kChunk * L::T; i += kThreads) {
+        TsT[i] = TR::fromf(0.f);
+        Ps[i] = TR::fromf(0.f);
+    }
+    if (NC > 0) {
+        sg.load(0);
+        sg.store_kqb(Ks, Qs, Bs);
+        sg.store_v(Vs);
+    }
+    __syncthreads();
+
+    f32x4 Zacc[4], Oacc[4];
+    for (int c = 0; c < NC; ++c) {
+        const int nval = min(kChunk, wk.len - c * kChunk);
+        sg.load(min(c + 1, NC - 1)); // next chunk (the last iteration re-reads its own)
+        // A
+        switch (w) {
+#define DN_A(W)                                                                                                \
+    case W: {                                                                                                  \
+        typename PH::template GramFrags<W> f;                                                                  \
+        PH::template gram_fetch<W>(f, Ks, Qs, g, c16);                                                         \
+        sched_fence();                                                                                         \
+        if (WRITE_O || !(W & 1)) PH::template gram_compute<W>(f, Bs, As, Ps, g, c16);                          \
+    } break;
+            DN_A(0) DN_A(1) DN_A(2) DN_A(3)
+#undef DN_A
+        }
+        __syncthreads();
+        // B
+        F nfrag;
+        {
+            typename PH::DiagFrags df;
+            PH::diag_fetch(df, As, Bs, w, c16);
+            sched_fence();
+            nfrag = PH::diag_compute(df, NsT, TsT, w, g, c16);
+        }
+        __syncthreads();
+        // C
+        switch (w) {
+#define DN_C(B)                                                                                                \
+    case B: {                                                                                                  \
+        typename PH::template OffFrags<B> f;                                                                   \
+        PH::template off_fetch<B>(f, As, NsT, Bs, g, c16);                                                     \
+        sched_fence();                                                                                         \
+        PH::template off_compute<B>(f, nfrag, TsT, g, c16);                                                    \
+    } break;
+            DN_C(0) DN_C(1) DN_C(2)
+#undef DN_C
+        default: break;
+        }
+        __syncthreads();
+        // D
+        {
+            typename PH::WUFrags f;
+            PH::wu_fetch(f, Ks, Vs, TsT, has_v, w, g, c16);
+            sched_fence();
+            PH::wu_compute(f, Ws, has_v, Zacc, w, g, c16);
+        }
+        __syncthreads();
+        // E
+        F SB[NMT], ZB[4];
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) SB[m] = TR::cvt(Sacc[m]);
+        {
+            typename PH::ZFrags f;
+            PH::z_fetch(f, Ws, g, c16);
+            sched_fence();
+            PH::z_compute(f, SB, Zacc, ZB);
+        }
+        if constexpr (WRITE_O) {
+            typename PH::OFrags f;
+            PH::o_fetch(f, Qs, Ps, g, c16);
+            sched_fence();
+            PH::o_compute(f, SB, ZB, Oacc);
+            store_o(og, sv, c, nval, Oacc, w, g, c16);
+        }
+        {
+            typename PH::SFrags f;
+            PH::s_fetch(f, Ks, g, c16);
+            sched_fence();
+            PH::s_compute(f, ZB, Sacc);
+        }
+        __syncthreads();
+        sg.store_kqb(Ks, Qs, Bs);
+        sg.store_v(Vs);
+        __syncthreads();
+    }
+    state_out<DK>(Sacc, wk, w, g, c16);
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel (bf16): iteration r = E of chunk r + A-D of chunk r+1.
+// LDS: K, Q, beta, P and W (which shares space with the solve's A) in two
+// sets, the chunk's parity selects the set; one V tile, one T^T and one N^T.
+// ---------------------------------------------------------------------------
+template <typename E, int DK> struct SmemPipe {
+    using L = Ld<E, DK>;
+    static constexpr size_t oKs = 0;                 // 2 sets
+    static constexpr size_t oQs = oKs + 2 * L::szK;  // 2 sets
+    static constexpr size_t oPs = oQs + 2 * L::szK;  // 2 sets
+    static constexpr size_t oWA = oPs + 2 * L::szT;  // 2 sets
+    static constexpr size_t oBs = oWA + 2 * L::szWA; // 2 sets of 64 fp32
+    static constexpr size_t oVs = oBs + 2 * sizeof(float) * kChunk;
+    static constexpr size_t oTs = oVs + L::szV;
+    static constexpr size_t oNs = oTs + L::szT;
+    static constexpr size_t total = oNs + L::szN;
+};
+
+template <typename E, int DK, int DV, bool WRITE_O>
+__global__ __launch_bounds__(kThreads) void chain_kernel_pipe(const ChainArgs a) {
+    using TR = Tr<E>;
+    using F = typename TR::F;
+    using PH = Phases<E, DK>;
+    using SM = SmemPipe<E, DK>;
+    using L = Ld<E, DK>;
+    constexpr int NMT = DK / 16;
+    static_assert(SM::total <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SM::total];
+    // Set s of the double-buffered regions (pointer arithmetic on the parity,
+    // so that no array of LDS pointers is materialised).
+    auto KsAt = [&](int s) { return reinterpret_cast<E *>(smem + SM::oKs + s * L::szK); };
+    auto QsAt = [&](int s) { return reinterpret_cast<E *>(smem + SM::oQs + s * L::szK); };
+    auto PsAt = [&](int s) { return reinterpret_cast<E *>(smem + SM::oPs + s * L::szT); };
+    auto WsAt = [&](int s) { return reinterpret_cast<E *>(smem + SM::oWA + s * L::szWA); };
+    auto AsAt = [&](int s) { return reinterpret_cast<float *>(smem + SM::oWA + s * L::szWA); };
+    auto BsAt = [&](int s) { return reinterpret_cast<float *>(smem + SM::oBs) + s * kChunk; };
+    E *Vs = reinterpret_cast<E *>(smem + SM::oVs);
+    E *TsT = reinterpret_cast<E *>(smem + SM::oTs);
+    E *NsT = reinterpret_cast<E *>(smem + SM::oNs);
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const Work wk = decode_work<DK, DV>(a);
+    f32x4 Sacc[NMT];
+    state_in<DK>(Sacc, wk, w, g, c16);
+    const int NC = (wk.len + kChunk - 1) / kChunk;
+    auto sg = make_stager<E, DK, DV, WRITE_O>(a, wk, tid);
+    const bool has_v = WRITE_O || wk.has_v;
+    const int64_t sv = (int64_t)a.H * DV;
+    E *og = WRITE_O ? reinterpret_cast<E *>(a.o) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 : nullptr;
+
+    // T and P are lower triangular and only their lower blocks are written:
+    // zero them once so the blocks above the diagonal stay zero.
+    for (int i = tid; i < kChunk * L::T; i += kThreads) {
+        TsT[i] = TR::fromf(0.f);
+        PsAt(0)[i] = TR::fromf(0.f);
+        PsAt(1)[i] = TR::fromf(0.f);
+    }
+    f32x4 Zacc[4];
+    if (NC > 0) {
+        // prologue: stage chunk 0, prepare it (A-D), stage K/Q/beta of chunk 1
+        sg.load(0);
+        sg.store_kqb(KsAt(0), QsAt(0), BsAt(0));
+        sg.store_v(Vs);
+        __syncthreads();
+        sg.load(min(1, NC - 1));
+        switch (w) {
+#define DN_A(W)                                                                                                \
+    case W: {                                                                                                  \
+        typename PH::template GramFrags<W> f;                                                                  \
+        PH::template gram_fetch<W>(f, KsAt(0), QsAt(0), g, c16);                                               \
+        sched_fence();                                                                                         \
+        if (WRITE_O || !(W & 1)) PH::template gram_compute<W>(f, BsAt(0), AsAt(0), PsAt(0), g, c16);           \
+    } break;
+            DN_A(0) DN_A(1) DN_A(2) DN_A(3)
+#undef DN_A
+        }
+        __syncthreads();
+        F nfrag;
+        {
+            typename PH::DiagFrags df;
+            PH::diag_fetch(df, AsAt(0), BsAt(0), w, c16);
+            sched_fence();
+            nfrag = PH::diag_compute(df, NsT, TsT, w, g, c16);
+        }
+        __syncthreads();
+        switch (w) {
+#define DN_C(B)                                                                                                \
+    case B: {                                                                                                  \
+        typename PH::template OffFrags<B> f;                                                                   \
+        PH::template off_fetch<B>(f, AsAt(0), NsT, BsAt(0), g, c16);                                           \
+        sched_fence();                                                                                         \
+        PH::template off_compute<B>(f, nfrag, TsT, g, c16);                                                    \
+    } break;
+            DN_C(0) DN_C(1) DN_C(2)
+#undef DN_C
+        default: break;
+        }
+        __syncthreads();
+        {
+            typename PH::WUFrags f;
+            PH::wu_fetch(f, KsAt(0), Vs, TsT, has_v, w, g, c16);
+            sched_fence();
+            PH::wu_compute(f, WsAt(0), has_v, Zacc, w, g, c16);
+        }
+        sg.store_kqb(KsAt(1), QsAt(1), BsAt(1));
+        __syncthreads();
+    }
+
+    // The preparation of chunk r+1 runs in every iteration, also the last one,
+    // where it works on a repeated copy of the last chunk and its results are
+    // never used: keeping it unconditional leaves each wave's work inside an
+    // interval in one basic block, which lets the scheduler interleave the
+    // two independent streams.
+    for (int r = 0; r < NC; ++r) {
+        const int cur = r & 1, nxt = cur ^ 1;
+        const int nval = min(kChunk, wk.len - r * kChunk);
+        // V of chunk r+1 (fetched one iteration ago) into the V tile, then fetch chunk r+2
+        sg.store_v(Vs);
+        sg.load(min(r + 2, NC - 1));
+
+        F SB[NMT], ZB[4];
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) SB[m] = TR::cvt(Sacc[m]);
+
+        // I1: A of chunk r+1 | Z of chunk r
+        switch (w) {
+#define DN_I1(W)                                                                                               \
+    case W: {                                                                                                  \
+        typename PH::template GramFrags<W> gf;                                                                 \
+        typename PH::ZFrags zf;                                                                                \
+        PH::z_fetch(zf, WsAt(cur), g, c16);                                                                    \
+        PH::template gram_fetch<W>(gf, KsAt(nxt), QsAt(nxt), g, c16);                                          \
+        sched_fence();                                                                                         \
+        PH::z_compute(zf, SB, Zacc, ZB);                                                                       \
+        if (WRITE_O || !(W & 1)) PH::template gram_compute<W>(gf, BsAt(nxt), AsAt(nxt), PsAt(nxt), g, c16);    \
+    } break;
+            DN_I1(0) DN_I1(1) DN_I1(2) DN_I1(3)
+#undef DN_I1
         }
         __syncthreads();
 
-        // ---- E: the chain, per wave ----
-        F SB[NMT];
-#pragma unroll
-        for (int m = 0; m < NMT; ++m) SB[m] = TR::cvt(Sacc[m]);
-        F ZB[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const E *Ar = Ws + (16 * t + c16) * LDK;
-            f32x4 z = Zacc[t];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-                z = TR::mma32(z, ldf(Ar + 32 * kb + 4 * g), ldf(Ar + 32 * kb + 16 + 4 * g),
-                              SB[2 * kb], SB[2 * kb + 1]);
-            ZB[t] = TR::cvt(z); // Z[16t + 4g + i][row 16w + c16]
-        }
-        if constexpr (WRITE_O) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const E *Qr = Qs + (16 * t + c16) * LDK;
-                const E *Pr = Ps + (16 * t + c16) * LDC;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-                    acc = TR::mma32(acc, SB[2 * kb], SB[2 * kb + 1], ldf(Qr + 32 * kb + 4 * g),
-                                    ldf(Qr + 32 * kb + 16 + 4 * g));
-#pragma unroll
-                for (int s = 0; s <= t / 2; ++s)
-                    acc = TR::mma32(acc, ZB[2 * s], ZB[2 * s + 1], ldf(Pr + 32 * s + 4 * g),
-                                    ldf(Pr + 32 * s + 16 + 4 * g));
-                // acc[i] = O[token 16t + c16][row 16w + 4g + i]
-                const int tok = 16 * t + c16;
-                if (tok < nval)
-                    stf(og + ((int64_t)c * kChunk + tok) * sv + 16 * w + 4 * g, TR::cvt(acc));
+        // I2: B of chunk r+1 | O of chunk r
+        F nfrag;
+        {
+            typename PH::DiagFrags df;
+            typename PH::OFrags of;
+            PH::diag_fetch(df, AsAt(nxt), BsAt(nxt), w, c16);
+            if constexpr (WRITE_O) PH::o_fetch(of, QsAt(cur), PsAt(cur), g, c16);
+            sched_fence();
+            nfrag = PH::diag_compute(df, NsT, TsT, w, g, c16);
+            if constexpr (WRITE_O) {
+                f32x4 Oacc[4];
+                PH::o_compute(of, SB, ZB, Oacc);
+                store_o(og, sv, r, nval, Oacc, w, g, c16);
             }
         }
-#pragma unroll
-        for (int m = 0; m < NMT; ++m) {
-            const E *Ar = Kt + (16 * m + c16) * LDC;
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                Sacc[m] = TR::mma32(Sacc[m], ldf(Ar + 32 * s + 4 * g), ldf(Ar + 32 * s + 16 + 4 * g),
-                                    ZB[2 * s], ZB[2 * s + 1]);
-        }
+        __syncthreads();
 
-        if (c + 1 < NC) {
-            __syncthreads();
-            lstore();
-            __syncthreads();
+        // I3: C of chunk r+1 | S update of chunk r
+        switch (w) {
+#define DN_I3(B)                                                                                               \
+    case B: {                                                                                                  \
+        typename PH::template OffFrags<B> ff;                                                                  \
+        typename PH::SFrags sf;                                                                                \
+        PH::template off_fetch<B>(ff, AsAt(nxt), NsT, BsAt(nxt), g, c16);                                      \
+        PH::s_fetch(sf, KsAt(cur), g, c16);                                                                    \
+        sched_fence();                                                                                         \
+        PH::template off_compute<B>(ff, nfrag, TsT, g, c16);                                                   \
+        PH::s_compute(sf, ZB, Sacc);                                                                           \
+    } break;
+            DN_I3(0) DN_I3(1) DN_I3(2)
+#undef DN_I3
+        default: {
+            typename PH::SFrags sf;
+            PH::s_fetch(sf, KsAt(cur), g, c16);
+            sched_fence();
+            PH::s_compute(sf, ZB, Sacc);
+        } break;
         }
-    }
+        __syncthreads();
 
-    // ---------------- state out ----------------
-    if (Sout) {
-        if (!transposed_out) {
-#pragma unroll
-            for (int m = 0; m < NMT; ++m)
-                *reinterpret_cast<f32x4 *>(Sout + (16 * w + c16) * DK + 16 * m + 4 * g) = Sacc[m];
-        } else {
-#pragma unroll
-            for (int m = 0; m < NMT; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Sout[(int64_t)(16 * m + 4 * g + i) * DK + srow] = Sacc[m][i];
+        // I4: D of chunk r+1 | stage K/Q/beta of chunk r+2 into this chunk's set
+        {
+            typename PH::WUFrags f;
+            PH::wu_fetch(f, KsAt(nxt), Vs, TsT, has_v, w, g, c16);
+            sched_fence();
+            PH::wu_compute(f, WsAt(nxt), has_v, Zacc, w, g, c16);
         }
+        sg.store_kqb(KsAt(cur), QsAt(cur), BsAt(cur));
+        __syncthreads();
     }
+    state_out<DK>(Sacc, wk, w, g, c16);
 }
 
 // Prefix composition of the group maps for one (b, h) and 16 state rows:
@@ -552,7 +1028,10 @@ template <typename E, int DK, int DV, bool WO>
 hipError_t launch_one(const ChainArgs &a, hipStream_t s) {
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((chain_kernel<E, DK, DV, WO>), dim3(grid), dim3(kThreads), 0, s, a);
+    if constexpr (sizeof(E) == 2)
+        hipLaunchKernelGGL((chain_kernel_pipe<E, DK, DV, WO>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((chain_kernel_serial<E, DK, DV, WO>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
