@@ -16,8 +16,10 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libdeltanet.so")
-SOURCES = [os.path.join(PKG, "csrc", "kernels.hip"), os.path.join(PKG, "csrc", "api.cpp")]
-HEADERS = [os.path.join(PKG, "csrc", "dn_internal.h"), os.path.join(ROOT, "include", "deltanet.h")]
+SOURCES = [os.path.join(PKG, "csrc", "kernels.hip"), os.path.join(PKG, "csrc", "chain_bf16.hip"),
+           os.path.join(PKG, "csrc", "api.cpp")]
+HEADERS = [os.path.join(PKG, "csrc", "dn_internal.h"), os.path.join(PKG, "csrc", "dn_work.h"),
+           os.path.join(ROOT, "include", "deltanet.h")]
 ARCH = "gfx950"
 
 

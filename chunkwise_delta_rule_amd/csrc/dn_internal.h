@@ -47,6 +47,10 @@ struct ChainArgs {
 hipError_t launch_chain(int dtype, int dk, int dv, bool write_o, const ChainArgs &a,
                         hipStream_t stream);
 
+// The bf16 chain kernel with specialised waves (chain_bf16.hip); same
+// contract as launch_chain, 512 threads per workgroup.
+hipError_t launch_chain_bf16(int dk, int dv, bool write_o, const ChainArgs &a, hipStream_t stream);
+
 // Enqueue the prefix composition S_{g+1} = S_g P_g + Q_g for g = 0..G-2,
 // writing start states of groups 1..G-1 into ws_S.
 hipError_t launch_compose(int dk, int dv, const ChainArgs &a, hipStream_t stream);

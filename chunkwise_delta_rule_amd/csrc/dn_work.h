@@ -1,0 +1,89 @@
+// Device-side work decoding shared by the chain kernels: which unit, token
+// range, 64-row state tile and state source/destination a workgroup owns.
+#pragma once
+
+#include "dn_internal.h"
+
+namespace dn {
+
+// Block index -> (unit, tile). Groups of 8 units are interleaved so that all
+// tiles of one unit get block indices congruent mod 8: the dispatcher deals
+// workgroups round-robin over the 8 XCDs, so the tiles of a unit (which read
+// the same K and Q chunks) land on one XCD and share its L2.
+__device__ inline void map_block(int x, int n_units, int n_tiles, int &u, int &tau) {
+    const int per = 8 * n_tiles;
+    const int full = n_units >> 3;
+    if (x < full * per) {
+        const int grp = x / per, r = x - grp * per;
+        u = grp * 8 + (r & 7);
+        tau = r >> 3;
+    } else {
+        const int rem = x - full * per;
+        u = full * 8 + rem / n_tiles;
+        tau = rem - (rem / n_tiles) * n_tiles;
+    }
+}
+
+// What one workgroup works on: a token range of one (sequence, head), a
+// 64-row tile of the state, where the tile starts from and where it ends.
+struct Work {
+    int64_t tok0;
+    int len, h, row0;
+    const float *Sin; // initial rows, or nullptr (zero / identity)
+    float *Sout;      // final rows, or nullptr
+    bool identity, transposed_out, has_v;
+};
+
+template <int DK, int DV> __device__ inline Work decode_work(const ChainArgs &a) {
+    int u, tau;
+    map_block(blockIdx.x, a.n_units, a.n_tiles, u, tau);
+    const int H = a.H;
+    Work wk = {0, 0, 0, tau * kRows, nullptr, nullptr, false, false, true};
+    if (a.kind == kDense) {
+        const int b = u / H;
+        wk.h = u - b * H;
+        wk.tok0 = (int64_t)b * a.T;
+        wk.len = a.T;
+        if (a.S0) wk.Sin = a.S0 + ((int64_t)u * DV + wk.row0) * DK;
+        if (a.S_final) wk.Sout = a.S_final + ((int64_t)u * DV + wk.row0) * DK;
+    } else if (a.kind == kVarlen) {
+        const int rank = u / H;
+        wk.h = u - rank * H;
+        const int n = a.seq_order ? a.seq_order[rank] : rank;
+        wk.tok0 = a.cu_seqlens[n];
+        wk.len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+        const int64_t su = (int64_t)n * H + wk.h;
+        if (a.S0) wk.Sin = a.S0 + (su * DV + wk.row0) * DK;
+        if (a.S_final) wk.Sout = a.S_final + (su * DV + wk.row0) * DK;
+    } else {
+        const int groups = (a.kind == kCpOutput) ? a.G : a.G - 1;
+        const int bh = u / groups;
+        const int gi = u - bh * groups;
+        const int b = bh / H;
+        wk.h = bh - b * H;
+        const int t_begin = gi * a.chunks_per_group * kChunk;
+        const int t_end = min(a.T, (gi + 1) * a.chunks_per_group * kChunk);
+        wk.tok0 = (int64_t)b * a.T + t_begin;
+        wk.len = t_end - t_begin;
+        const int64_t slot = (int64_t)bh * a.G + gi;
+        if (a.kind == kCpOutput) {
+            if (gi == 0) {
+                if (a.S0) wk.Sin = a.S0 + ((int64_t)bh * DV + wk.row0) * DK;
+            } else {
+                wk.Sin = a.ws_S + (slot * DV + wk.row0) * DK;
+            }
+            if (gi == a.G - 1 && a.S_final) wk.Sout = a.S_final + ((int64_t)bh * DV + wk.row0) * DK;
+        } else if (tau < DV / kRows) {
+            wk.Sout = a.ws_Q + (slot * DV + wk.row0) * DK; // Q_g rows, from a zero start
+        } else {
+            wk.row0 = (tau - DV / kRows) * kRows; // rows of P_g (dk index), from identity
+            wk.identity = true;
+            wk.has_v = false;
+            wk.transposed_out = true;
+            wk.Sout = a.ws_P + slot * DK * DK;
+        }
+    }
+    return wk;
+}
+
+} // namespace dn
