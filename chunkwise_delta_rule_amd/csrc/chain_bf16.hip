@@ -34,13 +34,20 @@
 // one row and receiver lane i gets element i % 4 of the chunks of providers
 // i / 4 + 4e, e = 0..3, so each provider picks its row and 4-column group):
 //   * dk index of the state accumulator tile m, lane group g, register i:
-//       delta(m, g, i) = 32 (m / 2) + 8 g + 4 (m % 2) + i
+//       delta(m, g, i) = 32 (m / 2) + 8 g + 4 ((m + g) % 2) + i
 //     so a pair of state tiles (2s, 2s+1) gives lane group g the 8
-//     consecutive dk values 32 s + 8 g .. +7: W and Q rows are read as one
-//     16-byte piece each, straight from their natural row-major layout;
+//     consecutive dk values 32 s + 8 g .. +7 (in one order or the other): W
+//     and Q rows are read as one 16-byte piece each from their natural
+//     row-major layout, and the transposing reads of K for the state update
+//     alternate the two 8-byte halves of each 16-byte unit;
 //   * tokens keep their natural order in Z; consecutive Z tiles (2s, 2s+1)
 //     give lane group g tokens 32 s + 4 g + e and 32 s + 16 + 4 g + e, so the
 //     columns of P are stored in the matching interleaved order.
+// LDS rows are unpadded; the 16-byte units of each row are permuted by an XOR
+// of a few row bits so that all of the fragment reads above, the 8-byte
+// writes of W and T^T and the staging writes are free of bank conflicts
+// (64 banks of 4 bytes; 16 lanes per pass for 16-byte accesses, 32 lanes per
+// pass for 8-byte ones).
 #include "dn_internal.h"
 #include "dn_work.h"
 
@@ -81,6 +88,7 @@ __device__ inline void st8(__bf16 *p, bf16x8 x) { *reinterpret_cast<bf16x8 *>(p)
 __device__ inline bf16x4 tr4(const __bf16 *p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
 }
+__device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Broadcast lane I of each 16-lane row to the whole row (DPP row_newbcast).
 template <int I> __device__ inline float row_bcast(float v) {
@@ -101,96 +109,37 @@ template <int J> __device__ inline void fwd_subst(float (&x)[16], const float (&
     }
 }
 
-// LDS layout. Row strides in elements, padded by 16 bytes.
+// Element offsets inside the LDS buffers. K, Q, W: [64][DK]; T^T, P, V tile:
+// [64][64]. The 8-element (16-byte) unit u of row r is stored at unit
+// u ^ swz(r).
+template <int DK> __device__ inline int kswz(int r) {
+    if constexpr (DK == 128) // row bits 0,1,2,3 -> unit bits 0,2,3,1
+        return (r & 1) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 1);
+    else // 8 units per row: row bits 1,2,3 -> unit bits 0,2,1
+        return ((r >> 1) & 1) | (((r >> 2) & 1) << 2) | (((r >> 3) & 1) << 1);
+}
+template <int DK> __device__ inline int koff(int r, int c) { return r * DK + (((c >> 3) ^ kswz<DK>(r)) << 3) + (c & 7); }
+__device__ inline int s64swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+__device__ inline int s64off(int r, int c) { return r * 64 + (((c >> 3) ^ s64swz(r)) << 3) + (c & 7); }
+// First dk of the 4-run held by lane group g of state tile m (delta above).
+__device__ inline int dk_of(int m, int g) { return 32 * (m >> 1) + 8 * g + 4 * ((m + g) & 1); }
+
+// LDS layout (bytes).
 template <int DK> struct WsLds {
-    static constexpr int LK = DK + 8;  // K, Q, W: [64][LK] bf16
-    static constexpr int L64 = 64 + 8; // T^T, P, V tile: [64][L64] bf16
-    static constexpr int LN = 16 + 8;  // N^T of the four diagonal blocks: [64][LN] bf16
-    static constexpr int LX = 16 + 4;  // diagonal Gram tiles for the row exchange: [64][LX] fp32
-    static constexpr size_t szK = sizeof(__bf16) * 64 * LK;
-    static constexpr size_t sz64 = sizeof(__bf16) * 64 * L64;
-    static constexpr size_t oK = 0;              // 3 buffers, chunk c in buffer c % 3
-    static constexpr size_t oQ = oK + 3 * szK;   // 2 buffers, c % 2
-    static constexpr size_t oW = oQ + 2 * szK;   // -W
-    static constexpr size_t oT = oW + szK;       // T^T, 2 buffers, c % 2
-    static constexpr size_t oP = oT + 2 * sz64;  // P, columns interleaved
-    static constexpr size_t oV = oP + sz64;      // V: this workgroup's 64 value columns
+    static constexpr int LX = 16 + 4; // diagonal Gram tiles for the row exchange: [64][LX] fp32
+    static constexpr int LN = 16 + 8; // N^T of the four diagonal blocks: [64][LN] bf16
+    static constexpr size_t szK = sizeof(__bf16) * 64 * DK;
+    static constexpr size_t sz64 = sizeof(__bf16) * 64 * 64;
+    static constexpr size_t oK = 0;             // 3 buffers, chunk c in buffer c % 3
+    static constexpr size_t oQ = oK + 3 * szK;  // 2 buffers, c % 2
+    static constexpr size_t oW = oQ + 2 * szK;  // -W
+    static constexpr size_t oT = oW + szK;      // T^T, 2 buffers, c % 2
+    static constexpr size_t oP = oT + 2 * sz64; // P, columns interleaved
+    static constexpr size_t oV = oP + sz64;     // V: this workgroup's 64 value columns
     static constexpr size_t oN = oV + sz64;
     static constexpr size_t oX = oN + sizeof(__bf16) * 64 * LN;
     static constexpr size_t oB = oX + sizeof(float) * 64 * LX; // beta ring, 4 x 64 fp32, c % 4
     static constexpr size_t total = oB + sizeof(float) * 4 * 64;
-};
-
-// Global -> register -> LDS staging of one chunk, shared by the 256 threads of
-// waves 4-7 (pt = 0..255). Loads are unconditional within the chunk: rows past
-// the end of the sequence re-read the last valid row and are written as zeros.
-template <int DK> struct WsStager {
-    static constexpr int KV = DK / 8;          // 16-byte vectors per K / Q row
-    static constexpr int NK = 64 * KV / 256;   // K (and Q) vectors per thread
-    static constexpr int NV = 64 * 8 / 256;    // vectors per thread of the 64x64 V tile
-    static_assert(NK * 256 == 64 * KV, "tiling");
-    const __bf16 *kg, *qg, *vg, *bg;
-    int64_t sqk, sv;
-    int H, len, pt;
-    bf16x8 rk[NK], rq[NK], rv[NV];
-    __bf16 rb;
-    int nk, nq, nv;
-
-    __device__ inline int rows_of(int c) const { return min(kChunk, len - c * kChunk); }
-    __device__ inline void load_k(int c) {
-        nk = rows_of(c);
-        const int64_t base = (int64_t)c * kChunk;
-#pragma unroll
-        for (int p = 0; p < NK; ++p) {
-            const int v = p * 256 + pt, row = min(v / KV, nk - 1), cv = v % KV;
-            rk[p] = ld8g(kg + (base + row) * sqk + 8 * cv);
-        }
-        if (pt < 64) rb = bg[(base + min(pt, nk - 1)) * H];
-    }
-    __device__ inline void load_q(int c) {
-        nq = rows_of(c);
-        const int64_t base = (int64_t)c * kChunk;
-#pragma unroll
-        for (int p = 0; p < NK; ++p) {
-            const int v = p * 256 + pt, row = min(v / KV, nq - 1), cv = v % KV;
-            rq[p] = ld8g(qg + (base + row) * sqk + 8 * cv);
-        }
-    }
-    __device__ inline void load_v(int c) {
-        nv = rows_of(c);
-        const int64_t base = (int64_t)c * kChunk;
-#pragma unroll
-        for (int p = 0; p < NV; ++p) {
-            const int v = p * 256 + pt, row = min(v / 8, nv - 1), cv = v % 8;
-            rv[p] = ld8g(vg + (base + row) * sv + 8 * cv);
-        }
-    }
-    __device__ inline void write_k(__bf16 *Ks, float *Bs) const {
-        const bf16x8 z = {};
-#pragma unroll
-        for (int p = 0; p < NK; ++p) {
-            const int v = p * 256 + pt, row = v / KV, cv = v % KV;
-            st8(Ks + row * WsLds<DK>::LK + 8 * cv, row < nk ? rk[p] : z);
-        }
-        if (pt < 64) Bs[pt] = pt < nk ? (float)rb : 0.f;
-    }
-    __device__ inline void write_q(__bf16 *Qs) const {
-        const bf16x8 z = {};
-#pragma unroll
-        for (int p = 0; p < NK; ++p) {
-            const int v = p * 256 + pt, row = v / KV, cv = v % KV;
-            st8(Qs + row * WsLds<DK>::LK + 8 * cv, row < nq ? rq[p] : z);
-        }
-    }
-    __device__ inline void write_v(__bf16 *Vs) const {
-        const bf16x8 z = {};
-#pragma unroll
-        for (int p = 0; p < NV; ++p) {
-            const int v = p * 256 + pt, row = v / 8, cv = v % 8;
-            st8(Vs + row * WsLds<DK>::L64 + 8 * cv, row < nv ? rv[p] : z);
-        }
-    }
-    __device__ static inline bf16x8 ld8g(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 };
 
 // Shared LDS pointers of one workgroup.
@@ -207,15 +156,98 @@ template <int DK> struct WsBufs {
     __device__ inline float *B(int c) const { return (float *)(base + WsLds<DK>::oB) + (c & 3) * 64; }
 };
 
-// State rows in and out. Sacc[m][i] = S[row][delta(m, g, i)] for the lane's
-// state row (column index c of the accumulator).
-template <int DK> __device__ inline int dk_of(int m, int g) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1); }
+// Global -> register -> LDS staging of one chunk, shared by the 256 threads of
+// waves 4-7 (pt = 0..255). Thread pt owns the same 16-byte column piece of
+// rows RPS * p + pt / KV (p = 0..NK-1) of every chunk, so its addresses are a
+// fixed per-thread pointer plus a per-chunk offset, and (RPS being a multiple
+// of 16) its swizzled LDS offsets are fixed too. A partial last chunk re-reads
+// its last valid row for the missing rows and writes them as zeros.
+template <int DK> struct WsStager {
+    static constexpr int KV = DK / 8;        // 16-byte vectors per K / Q row
+    static constexpr int NK = 64 * KV / 256; // K (and Q) vectors per thread
+    static constexpr int RPS = 256 / KV;     // rows between a thread's K / Q vectors
+    static constexpr int NV = 2;             // vectors per thread of the 64x64 V tile
+    static_assert(NK * 256 == 64 * KV && RPS % 16 == 0, "tiling");
+    const __bf16 *kt, *qt, *vt, *bg; // per-thread pointers into chunk 0
+    int64_t sqk, sv;
+    int H, len, pt, rk0, rv0; // first row of this thread's K / Q and V vectors
+    int lk, lv;               // LDS element offsets of the first vector
+    bf16x8 rk[NK], rq[NK], rv[NV];
+    __bf16 rb;
+    int nk, nq, nv;
 
+    __device__ inline void init(const __bf16 *kg, const __bf16 *qg, const __bf16 *vg, const __bf16 *bg_, int64_t sqk_,
+                                int64_t sv_, int H_, int len_, int pt_) {
+        sqk = sqk_;
+        sv = sv_;
+        H = H_;
+        len = len_;
+        pt = pt_;
+        rk0 = pt / KV;
+        rv0 = pt / 8;
+        kt = kg + rk0 * sqk + 8 * (pt % KV);
+        qt = qg + rk0 * sqk + 8 * (pt % KV);
+        vt = vg + rv0 * sv + 8 * (pt % 8);
+        bg = bg_;
+        lk = koff<DK>(rk0, 8 * (pt % KV));
+        lv = s64off(rv0, 8 * (pt % 8));
+        nk = nq = nv = 0;
+    }
+    __device__ inline int rows_of(int c) const { return min(kChunk, len - c * kChunk); }
+    // rows STEP * p + r0 of chunk c from per-thread pointer t (row stride ld)
+    template <int N, int STEP>
+    __device__ static inline void fetch(bf16x8 (&r)[N], const __bf16 *t, int64_t ld, int c, int n, int r0) {
+        const __bf16 *b = t + (int64_t)c * kChunk * ld;
+        if (n == kChunk) {
+#pragma unroll
+            for (int p = 0; p < N; ++p) r[p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(STEP * p) * ld);
+        } else {
+#pragma unroll
+            for (int p = 0; p < N; ++p) {
+                const int row = min(STEP * p + r0, n - 1);
+                r[p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(row - r0) * ld);
+            }
+        }
+    }
+    template <int N, int STEP, int LD>
+    __device__ static inline void put(__bf16 *dst, const bf16x8 (&r)[N], int n, int r0) {
+        if (n == kChunk) {
+#pragma unroll
+            for (int p = 0; p < N; ++p) st8(dst + STEP * p * LD, r[p]);
+        } else {
+            const bf16x8 z = {};
+#pragma unroll
+            for (int p = 0; p < N; ++p) st8(dst + STEP * p * LD, STEP * p + r0 < n ? r[p] : z);
+        }
+    }
+    __device__ inline void load_k(int c) {
+        nk = rows_of(c);
+        fetch<NK, RPS>(rk, kt, sqk, c, nk, rk0);
+        if (pt < 64) rb = bg[((int64_t)c * kChunk + min(pt, nk - 1)) * H];
+    }
+    __device__ inline void load_q(int c) {
+        nq = rows_of(c);
+        fetch<NK, RPS>(rq, qt, sqk, c, nq, rk0);
+    }
+    __device__ inline void load_v(int c) {
+        nv = rows_of(c);
+        fetch<NV, 32>(rv, vt, sv, c, nv, rv0);
+    }
+    __device__ inline void write_k(__bf16 *Ks, float *Bs) const {
+        put<NK, RPS, DK>(Ks + lk, rk, nk, rk0);
+        if (pt < 64) Bs[pt] = pt < nk ? (float)rb : 0.f;
+    }
+    __device__ inline void write_q(__bf16 *Qs) const { put<NK, RPS, DK>(Qs + lk, rq, nq, rk0); }
+    __device__ inline void write_v(__bf16 *Vs) const { put<NV, 32, 64>(Vs + lv, rv, nv, rv0); }
+};
+
+// State rows in and out: Sacc[m][i] = S[row][delta(m, g, i)] for the lane's
+// state row (column index c of the accumulator).
 template <int DK> __device__ inline void ws_state_in(f32x4 (&Sacc)[DK / 16], const Work &wk, int cw, int g, int c16) {
     const int lrow = 16 * cw + c16, srow = wk.row0 + lrow;
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m) {
-        const int d0 = dk_of<DK>(m, g);
+        const int d0 = dk_of(m, g);
         if (wk.Sin) {
             Sacc[m] = *reinterpret_cast<const f32x4 *>(wk.Sin + lrow * DK + d0);
         } else {
@@ -230,7 +262,7 @@ __device__ inline void ws_state_out(const f32x4 (&Sacc)[DK / 16], const Work &wk
     const int lrow = 16 * cw + c16, srow = wk.row0 + lrow;
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m) {
-        const int d0 = dk_of<DK>(m, g);
+        const int d0 = dk_of(m, g);
         if (!wk.transposed_out) {
             *reinterpret_cast<f32x4 *>(wk.Sout + lrow * DK + d0) = Sacc[m];
         } else {
@@ -240,98 +272,180 @@ __device__ inline void ws_state_out(const f32x4 (&Sacc)[DK / 16], const Work &wk
     }
 }
 
+// Transposing read of the K^T fragment for state tile m (dk delta(m, .)) over
+// the 32 tokens 32 s + {4g + e, 16 + 4g + e}; slots in the order of ZB_s.
+template <int DK> __device__ inline bf16x8 k_trfrag(const __bf16 *Kb, int m, int s, int g, int c16) {
+    const int q = c16 & 3, col = 32 * (m >> 1) + 8 * q + 4 * ((m + q) & 1);
+    const int row = 32 * s + 4 * g + (c16 >> 2);
+    return cat8(tr4(Kb + koff<DK>(row, col)), tr4(Kb + koff<DK>(row + 16, col)));
+}
+
 // ---------------------------------------------------------------------------
 // Consumers (waves 0-3).
 // ---------------------------------------------------------------------------
+// The consumer's work on one chunk as a list of matrix products, each with one
+// LDS operand fragment (the other operand is in registers):
+//   Z  (t, s):   Z_t += (-W)_{t,s} SB_s                 4 * DK/32 steps
+//   Op (t, s):   O_t += ZB_s P_{t,s}^T, s <= t/2        6 steps (with output)
+//   S  (m, s):   S^T_m += K^T_{m,s} ZB_s                2 * DK/16 steps
+// The other half of the output, O_t = SB_s Q_{t,s}^T, needs only the state
+// before the chunk, so it runs in the previous iteration's second phase
+// (consumer_oq). Fragments are fetched `depth` steps ahead into a rotating
+// register buffer and scheduling fences keep that order, so LDS latency hides
+// behind the matrix products of the steps in between.
+template <int DK, bool WO> struct ChainSteps {
+    static constexpr int NKB = DK / 32, NMT = DK / 16;
+    static constexpr int nZ = 4 * NKB, nOq = 0, nOp = WO ? 6 : 0, nS = 2 * NMT;
+    static constexpr int n = nZ + nOq + nOp + nS;
+    static constexpr int kind(int i) { return i < nZ ? 0 : i < nZ + nOq ? 1 : i < nZ + nOq + nOp ? 2 : 3; }
+    static constexpr int idx(int i) {
+        return kind(i) == 0 ? i : kind(i) == 1 ? i - nZ : kind(i) == 2 ? i - nZ - nOq : i - nZ - nOq - nOp;
+    }
+    static constexpr int opT(int j) { return j < 2 ? j : j < 4 ? 2 : 3; }
+    static constexpr int opS(int j) { return (j == 3 || j == 5) ? 1 : 0; }
+    // step at which Z is converted to the bf16 operand ZB
+    static constexpr int zb_at = nZ;
+    static constexpr int depth = 8;
+};
+
+template <int DK, bool WO>
+__device__ inline bf16x8 chain_fetch(int i, const __bf16 *Wb, const __bf16 *Qb, const __bf16 *Pb, const __bf16 *Kb,
+                                     int g, int c16) {
+    using CS = ChainSteps<DK, WO>;
+    const int k = CS::kind(i), j = CS::idx(i);
+    if (k == 0) return ld8(Wb + koff<DK>(16 * (j / CS::NKB) + c16, 32 * (j % CS::NKB) + 8 * g));
+    if (k == 1) return ld8(Qb + koff<DK>(16 * (j / CS::NKB) + c16, 32 * (j % CS::NKB) + 8 * g));
+    if (k == 2) return ld8(Pb + s64off(16 * CS::opT(j) + c16, 32 * CS::opS(j) + 8 * g));
+    return k_trfrag<DK>(Kb, j / 2, j % 2, g, c16);
+}
+
+template <int DK, bool WO>
+__device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)[DK / 16], const f32x4 (&Zacc)[4],
+                                      f32x4 (&O)[4], __bf16 *og, int64_t sv, int nval, int g, int c16) {
+    using CS = ChainSteps<DK, WO>;
+    constexpr int D = CS::depth;
+    const __bf16 *Wb = bf.W(), *Kb = bf.K(r);
+    const __bf16 *Qb = WO ? bf.Q(r) : nullptr, *Pb = bf.P();
+    bf16x8 SB[CS::NKB], ZB[2], buf[D];
+    f32x4 Z[4];
+#pragma unroll
+    for (int i = 0; i < D; ++i) buf[i] = chain_fetch<DK, WO>(i, Wb, Qb, Pb, Kb, g, c16);
+    // SB_s slots = dk 32 s + 8 g + 0..7: tiles (2s, 2s+1) hold the low / high
+    // half for even g and the other way round for odd g.
+    const bool odd = g & 1;
+#pragma unroll
+    for (int s = 0; s < CS::NKB; ++s) {
+        const bf16x4 lo = cvt4(Sacc[2 * s]), hi = cvt4(Sacc[2 * s + 1]);
+        SB[s] = odd ? cat8(hi, lo) : cat8(lo, hi);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) Z[t] = Zacc[t];
+    fence();
+#pragma unroll
+    for (int i = 0; i < CS::n; ++i) {
+        const bf16x8 f = buf[i % D];
+        if (i + D < CS::n) buf[i % D] = chain_fetch<DK, WO>(i + D, Wb, Qb, Pb, Kb, g, c16);
+        if (i == CS::zb_at) {
+            ZB[0] = cvt8(Z[0], Z[1]);
+            ZB[1] = cvt8(Z[2], Z[3]);
+        }
+        fence();
+        const int k = CS::kind(i), j = CS::idx(i);
+        if (k == 0) Z[j / CS::NKB] = mfma32(f, SB[j % CS::NKB], Z[j / CS::NKB]);
+        if (k == 1) O[j / CS::NKB] = mfma32(SB[j % CS::NKB], f, O[j / CS::NKB]);
+        if (k == 2) O[CS::opT(j)] = mfma32(ZB[CS::opS(j)], f, O[CS::opT(j)]);
+        if (k == 3) Sacc[j / 2] = mfma32(f, ZB[j % 2], Sacc[j / 2]);
+        fence();
+    }
+    if constexpr (WO) {
+        // O[t][i] = O[16t + c][row 4g + i] (rows relative to this wave's 16)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int tok = 16 * t + c16;
+            if (tok < nval) st4(og + (int64_t)tok * sv, cvt4(O[t]));
+        }
+    }
+}
+
+// O_t = S Q_t^T for the 4 token tiles of chunk c with the state before chunk c
+// (16 products, Q row fragments fetched 8 ahead).
+template <int DK>
+__device__ inline void consumer_oq(const WsBufs<DK> &bf, int c, const f32x4 (&Sacc)[DK / 16], f32x4 (&O)[4], int g,
+                                   int c16) {
+    constexpr int NKB = DK / 32, n = 4 * NKB, D = 8;
+    const __bf16 *Qb = bf.Q(c);
+    bf16x8 SB[NKB], buf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) buf[i] = ld8(Qb + koff<DK>(16 * (i / NKB) + c16, 32 * (i % NKB) + 8 * g));
+    const bool odd = g & 1;
+#pragma unroll
+    for (int s = 0; s < NKB; ++s) {
+        const bf16x4 lo = cvt4(Sacc[2 * s]), hi = cvt4(Sacc[2 * s + 1]);
+        SB[s] = odd ? cat8(hi, lo) : cat8(lo, hi);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    fence();
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+        const bf16x8 f = buf[i % D];
+        if (i + D < n) buf[i % D] = ld8(Qb + koff<DK>(16 * ((i + D) / NKB) + c16, 32 * ((i + D) % NKB) + 8 * g));
+        fence();
+        O[i / NKB] = mfma32(SB[i % NKB], f, O[i / NKB]);
+        fence();
+    }
+}
+
 template <int DK, int DV, bool WO>
 __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int cw, int g,
                               int c16) {
-    using LY = WsLds<DK>;
-    constexpr int NMT = DK / 16, NKB = DK / 32;
+    constexpr int NMT = DK / 16;
     const bool has_v = WO || wk.has_v;
-    f32x4 Sacc[NMT], Zacc[4];
+    f32x4 Sacc[NMT], Zacc[4], O[4];
     ws_state_in<DK>(Sacc, wk, cw, g, c16);
 #pragma unroll
     for (int t = 0; t < 4; ++t) Zacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t sv = (int64_t)a.H * DV;
     __bf16 *og = WO ? reinterpret_cast<__bf16 *>(a.o) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 + 16 * cw + 4 * g
-                    : nullptr;
+                    : nullptr; // only dereferenced with output
     const int kq = c16 >> 2, kr = c16 & 3; // transposing-read provider coordinates
 
     __syncthreads(); // K(0) staged
     for (int r = -2; r < NC; ++r) {
         // ---------------- phase 1: chain of chunk r
-        if (r >= 0) {
-            const __bf16 *Wb = bf.W(), *Kb = bf.K(r);
-            bf16x8 SB[NKB];
+        if (r >= 0)
+            consumer_chain<DK, WO>(bf, r, Sacc, Zacc, O, WO ? og + (int64_t)r * kChunk * sv : nullptr, sv,
+                                   min(kChunk, wk.len - r * kChunk), g, c16);
+        __syncthreads();
+        // ---------------- phase 2: U of chunk r+1 (T^T and V of r+1 are in LDS)
+        if (r + 1 >= 0 && r + 1 < NC && has_v) {
+            const __bf16 *Tb = bf.Tt(r + 1), *Vb = bf.V();
+            bf16x8 vf[2], tf[6];
 #pragma unroll
-            for (int s = 0; s < NKB; ++s) SB[s] = cvt8(Sacc[2 * s], Sacc[2 * s + 1]);
-            // Z = U - W S^T  (the W buffer holds -W); Z[t][i] = Z[16t + 4g + i][row c]
-            f32x4 Z[4];
+            for (int s = 0; s < 2; ++s) {
+                const int row = 32 * s + 4 * g + kq;
+                vf[s] = cat8(tr4(Vb + s64off(row, 16 * cw + 4 * kr)), tr4(Vb + s64off(row + 16, 16 * cw + 4 * kr)));
+            }
+            int i = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int s = 0; s <= t / 2; ++s, ++i) {
+                    const int row = 32 * s + 4 * g + kq;
+                    tf[i] = cat8(tr4(Tb + s64off(row, 16 * t + 4 * kr)), tr4(Tb + s64off(row + 16, 16 * t + 4 * kr)));
+                }
+            i = 0;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                f32x4 z = Zacc[t];
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < NKB; ++s) z = mfma32(ld8(Wb + (16 * t + c16) * LY::LK + 32 * s + 8 * g), SB[s], z);
-                Z[t] = z;
-            }
-            bf16x8 ZB[2];
-            ZB[0] = cvt8(Z[0], Z[1]);
-            ZB[1] = cvt8(Z[2], Z[3]);
-            f32x4 O[4];
-            if constexpr (WO) {
-                // O^T = S Q^T + Z^T P^T with the pre-update S; O[t][i] = O[16t + c][row 4g + i]
-                const __bf16 *Qb = bf.Q(r), *Pb = bf.P();
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < NKB; ++s) o = mfma32(SB[s], ld8(Qb + (16 * t + c16) * LY::LK + 32 * s + 8 * g), o);
-#pragma unroll
-                    for (int s = 0; s <= t / 2; ++s)
-                        o = mfma32(ZB[s], ld8(Pb + (16 * t + c16) * LY::L64 + 32 * s + 8 * g), o);
-                    O[t] = o;
-                }
-            }
-            // S^T += K^T Z over the tokens of the chunk
-#pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                const int col = 32 * (m >> 1) + 8 * kr + 4 * (m & 1);
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const bf16x4 k0 = tr4(Kb + (32 * s + 4 * g + kq) * LY::LK + col);
-                    const bf16x4 k1 = tr4(Kb + (32 * s + 16 + 4 * g + kq) * LY::LK + col);
-                    Sacc[m] = mfma32(cat8(k0, k1), ZB[s], Sacc[m]);
-                }
-            }
-            if constexpr (WO) {
-                const int nval = min(kChunk, wk.len - r * kChunk);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int tok = 16 * t + c16;
-                    if (tok < nval) st4(og + ((int64_t)r * kChunk + tok) * sv, cvt4(O[t]));
-                }
+                for (int s = 0; s <= t / 2; ++s, ++i) u = mfma32(tf[i], vf[s], u);
+                Zacc[t] = u; // U[16t + 4g + i][row c]
             }
         }
-        __syncthreads();
-        // ---------------- phase 2: U of chunk r+1 (T of r+1 and V of r+1 are in LDS)
-        if (r + 1 >= 0 && r + 1 < NC) {
-            if (has_v) {
-                const __bf16 *Tb = bf.Tt(r + 1), *Vb = bf.V();
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s <= t / 2; ++s) {
-                        const bf16x4 t0 = tr4(Tb + (32 * s + 4 * g + kq) * LY::L64 + 16 * t + 4 * kr);
-                        const bf16x4 t1 = tr4(Tb + (32 * s + 16 + 4 * g + kq) * LY::L64 + 16 * t + 4 * kr);
-                        const bf16x4 v0 = tr4(Vb + (32 * s + 4 * g + kq) * LY::L64 + 16 * cw + 4 * kr);
-                        const bf16x4 v1 = tr4(Vb + (32 * s + 16 + 4 * g + kq) * LY::L64 + 16 * cw + 4 * kr);
-                        u = mfma32(cat8(t0, t1), cat8(v0, v1), u);
-                    }
-                    Zacc[t] = u; // U[16t + 4g + i][row c]
-                }
-            }
+        // Q S^T part of the output of chunk r+1 (Q of r+1 is in LDS, S is final for r+1)
+        if constexpr (WO) {
+            if (r + 1 >= 0 && r + 1 < NC) consumer_oq<DK>(bf, r + 1, Sacc, O, g, c16);
         }
         __syncthreads();
     }
@@ -342,27 +456,37 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
 // Producers (waves 4-7). ROLE 0: diagonal solve; 1: off-diagonal Gram and
 // block substitution; 2, 3: W and P (halves).
 // ---------------------------------------------------------------------------
-template <int DK> struct DiagState {};
+
+// Row fragments of the four 16-row blocks of K (slots = dk 32 kb + 8 g ..).
+template <int DK> struct KRows {
+    bf16x8 f[4][DK / 32];
+};
+template <int DK> __device__ inline void k_rows(KRows<DK> &k, const __bf16 *Kb, int g, int c16) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) k.f[b][kb] = ld8(Kb + koff<DK>(16 * b + c16, 32 * kb + 8 * g));
+}
+// acc[i] = x_{4g + i} . y_{c}, x and y row fragments of two 16-row blocks
+template <int DK> __device__ inline f32x4 dot_tile(const bf16x8 (&x)[DK / 32], const bf16x8 (&y)[DK / 32]) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) acc = mfma32(x[kb], y[kb], acc);
+    return acc;
+}
 
 // Wave 4, phase 1: diagonal Gram tiles G_bb of chunk c, lane group b solves
 // block b: lane (b, j) computes column j of N_bb = (I + A_bb)^-1; writes
 // N_bb^T (for wave 5) and the diagonal blocks of T^T.
-template <int DK>
-__device__ inline void diag_solve(const WsBufs<DK> &bf, int c, int g, int c16) {
+template <int DK> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c, int g, int c16) {
     using LY = WsLds<DK>;
-    constexpr int NKB = DK / 32;
-    const __bf16 *Kb = bf.K(c);
     float *X = bf.X();
+    KRows<DK> k;
+    k_rows<DK>(k, bf.K(c), g, c16);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const bf16x8 kf = ld8(Kb + (16 * b + c16) * LY::LK + 32 * kb + 8 * g);
-            acc = mfma32(kf, kf, acc);
-        }
-        // acc[i] = k_{16b+4g+i} . k_{16b+c} = G_bb[c][4g + i]
-        *reinterpret_cast<f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g) = acc;
+        // G_bb[c][4g + i] (symmetric) -> X row 16b + c
+        *reinterpret_cast<f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g) = dot_tile<DK>(k.f[b], k.f[b]);
     }
     const float br = bf.B(c)[16 * g + c16];
     float arow[16];
@@ -378,13 +502,14 @@ __device__ inline void diag_solve(const WsBufs<DK> &bf, int c, int g, int c16) {
     fwd_subst<0>(x, arow);
     // x[i] = N_gg[i][c]; N^T row 16g + c; T^T row 16g + c, columns 16g..16g+15
     __bf16 *Nr = bf.N() + (16 * g + c16) * LY::LN;
-    __bf16 *Tr = bf.Tt(c) + (16 * g + c16) * LY::L64 + 16 * g;
+    __bf16 *Tt = bf.Tt(c);
+    const int trow = 16 * g + c16;
     const f32x4 x0 = {x[0], x[1], x[2], x[3]}, x1 = {x[4], x[5], x[6], x[7]};
     const f32x4 x2 = {x[8], x[9], x[10], x[11]}, x3 = {x[12], x[13], x[14], x[15]};
     st8(Nr, cvt8(x0, x1));
     st8(Nr + 8, cvt8(x2, x3));
-    st8(Tr, cvt8(x0 * br, x1 * br));
-    st8(Tr + 8, cvt8(x2 * br, x3 * br));
+    st8(Tt + s64off(trow, 16 * g), cvt8(x0 * br, x1 * br));
+    st8(Tt + s64off(trow, 16 * g + 8), cvt8(x2 * br, x3 * br));
 }
 
 // Wave 5, phase 1: off-diagonal Gram tiles of chunk c as bf16 k16 operands,
@@ -392,26 +517,19 @@ __device__ inline void diag_solve(const WsBufs<DK> &bf, int c, int g, int c16) {
 struct OffGram {
     bf16x4 A10, A20, A21, A30, A31, A32;
 };
-template <int DK> __device__ inline f32x4 gram_tile(const __bf16 *Kb, int a, int cb, int g, int c16) {
-    using LY = WsLds<DK>;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb)
-        acc = mfma32(ld8(Kb + (16 * cb + c16) * LY::LK + 32 * kb + 8 * g),
-                     ld8(Kb + (16 * a + c16) * LY::LK + 32 * kb + 8 * g), acc);
-    return acc; // acc[i] = k_{16cb+4g+i} . k_{16a+c} = G[16a + c][16cb + 4g + i]
-}
 template <int DK> __device__ inline OffGram off_gram(const WsBufs<DK> &bf, int c, int g, int c16) {
-    const __bf16 *Kb = bf.K(c);
+    KRows<DK> k;
+    k_rows<DK>(k, bf.K(c), g, c16);
     const float *Bs = bf.B(c);
     const float b1 = Bs[16 + c16], b2 = Bs[32 + c16], b3 = Bs[48 + c16];
     OffGram o;
-    o.A10 = cvt4(gram_tile<DK>(Kb, 1, 0, g, c16) * b1);
-    o.A20 = cvt4(gram_tile<DK>(Kb, 2, 0, g, c16) * b2);
-    o.A21 = cvt4(gram_tile<DK>(Kb, 2, 1, g, c16) * b2);
-    o.A30 = cvt4(gram_tile<DK>(Kb, 3, 0, g, c16) * b3);
-    o.A31 = cvt4(gram_tile<DK>(Kb, 3, 1, g, c16) * b3);
-    o.A32 = cvt4(gram_tile<DK>(Kb, 3, 2, g, c16) * b3);
+    // dot_tile(K_c, K_a)[i] = k_{16c+4g+i} . k_{16a+j} = G[16a + j][16c + 4g + i]
+    o.A10 = cvt4(dot_tile<DK>(k.f[0], k.f[1]) * b1);
+    o.A20 = cvt4(dot_tile<DK>(k.f[0], k.f[2]) * b2);
+    o.A21 = cvt4(dot_tile<DK>(k.f[1], k.f[2]) * b2);
+    o.A30 = cvt4(dot_tile<DK>(k.f[0], k.f[3]) * b3);
+    o.A31 = cvt4(dot_tile<DK>(k.f[1], k.f[3]) * b3);
+    o.A32 = cvt4(dot_tile<DK>(k.f[2], k.f[3]) * b3);
     return o;
 }
 
@@ -433,7 +551,9 @@ template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, const O
     const bf16x4 r33 = tr4(Ns + (48 + 4 * g + kq) * LY::LN + 4 * kr);
     const float be0 = Bs[c16], be1 = Bs[16 + c16], be2 = Bs[32 + c16];
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    auto put = [&](int b, int a, f32x4 nab, float be) { st4(Tt + (16 * b + c16) * LY::L64 + 16 * a + 4 * g, cvt4(nab * be)); };
+    auto put = [&](int b, int a, f32x4 nab, float be) {
+        st4(Tt + s64off(16 * b + c16, 16 * a + 4 * g), cvt4(nab * be));
+    };
     // column block 0
     const f32x4 n10 = -mfma16(r11, cvt4(mfma16(o.A10, n00, z)), z);
     const bf16x4 f10 = cvt4(n10);
@@ -455,10 +575,12 @@ template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, const O
 }
 
 // Waves 6-7: W = T K for half of the dk tiles and half of the score tiles of
-// chunk c, kept in registers during phase 1 and written in phase 2.
+// chunk c, kept in registers during phase 1 and written in phase 2. W tile mt
+// uses the dk labels of state tile mt, so its K^T fragments are the
+// conflict-free transposing reads of the state update.
 template <int DK> struct WPRegs {
     static constexpr int MT = DK / 32; // dk tiles per wave
-    bf16x4 w[MT][4];                   // -W[16nt + c][16mt + 4g ..]
+    bf16x4 w[MT][4];                   // -W[16nt + c][delta(mt, g, 0..3)]
     bf16x4 p[5];                       // score tiles
 };
 
@@ -468,7 +590,6 @@ __device__ constexpr int kPC[2][5] = {{0, 0, 1, 2, 3}, {0, 1, 0, 1, 2}};
 
 template <int DK, bool WO>
 __device__ inline void wp_compute(WPRegs<DK> &R, const WsBufs<DK> &bf, int c, int half, int g, int c16) {
-    using LY = WsLds<DK>;
     constexpr int MT = WPRegs<DK>::MT;
     const __bf16 *Kb = bf.K(c), *Tb = bf.Tt(c);
     const int kq = c16 >> 2, kr = c16 & 3;
@@ -477,37 +598,42 @@ __device__ inline void wp_compute(WPRegs<DK> &R, const WsBufs<DK> &bf, int c, in
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int s = 0; s <= nt / 2; ++s)
-            tf[nt][s] = cat8(tr4(Tb + (32 * s + 4 * g + kq) * LY::L64 + 16 * nt + 4 * kr),
-                             tr4(Tb + (32 * s + 16 + 4 * g + kq) * LY::L64 + 16 * nt + 4 * kr));
+        for (int s = 0; s <= nt / 2; ++s) {
+            const int row = 32 * s + 4 * g + kq;
+            tf[nt][s] = cat8(tr4(Tb + s64off(row, 16 * nt + 4 * kr)), tr4(Tb + s64off(row + 16, 16 * nt + 4 * kr)));
+        }
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) {
         const int mt = half * MT + mm;
         bf16x8 kf[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            kf[s] = cat8(tr4(Kb + (32 * s + 4 * g + kq) * LY::LK + 16 * mt + 4 * kr),
-                         tr4(Kb + (32 * s + 16 + 4 * g + kq) * LY::LK + 16 * mt + 4 * kr));
+        for (int s = 0; s < 2; ++s) kf[s] = k_trfrag<DK>(Kb, mt, s, g, c16);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s <= nt / 2; ++s) acc = mfma32(kf[s], tf[nt][s], acc);
-            // acc[i] = W[16nt + c][16mt + 4g + i]
+            // acc[i] = W[16nt + c][delta(mt, g, i)]
             R.w[mm][nt] = cvt4(-acc);
         }
     }
     if constexpr (WO) {
         const __bf16 *Qb = bf.Q(c);
+        // K row blocks 0..3 and this wave's two Q row blocks ({0, 3} or {1, 2})
+        KRows<DK> k;
+        k_rows<DK>(k, Kb, g, c16);
+        bf16x8 qf[2][DK / 32];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb)
+                qf[i][kb] = ld8(Qb + koff<DK>(16 * (half ? 1 + i : 3 * i) + c16, 32 * kb + 8 * g));
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const int pa = kPA[half][i], pc = kPC[half][i];
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb)
-                acc = mfma32(ld8(Kb + (16 * pc + c16) * LY::LK + 32 * kb + 8 * g),
-                             ld8(Qb + (16 * pa + c16) * LY::LK + 32 * kb + 8 * g), acc);
-            // acc[e] = q_{16pa+c} . k_{16pc+4g+e} = P[16pa + c][16pc + 4g + e]
+            const int qi = half ? pa - 1 : (pa == 3 ? 1 : 0);
+            // acc[e] = k_{16pc+4g+e} . q_{16pa+c} = P[16pa + c][16pc + 4g + e]
+            f32x4 acc = dot_tile<DK>(k.f[pc], qf[qi]);
             if (pa == pc) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e > c16) ? 0.f : acc[e];
@@ -518,20 +644,19 @@ __device__ inline void wp_compute(WPRegs<DK> &R, const WsBufs<DK> &bf, int c, in
 }
 template <int DK, bool WO>
 __device__ inline void wp_write(const WPRegs<DK> &R, const WsBufs<DK> &bf, int half, int g, int c16) {
-    using LY = WsLds<DK>;
     constexpr int MT = WPRegs<DK>::MT;
     __bf16 *Wb = bf.W();
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) st4(Wb + (16 * nt + c16) * LY::LK + 16 * (half * MT + mm) + 4 * g, R.w[mm][nt]);
+        for (int nt = 0; nt < 4; ++nt) st4(Wb + koff<DK>(16 * nt + c16, dk_of(half * MT + mm, g)), R.w[mm][nt]);
     if constexpr (WO) {
         __bf16 *Pb = bf.P();
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const int pa = kPA[half][i], pc = kPC[half][i];
             // token 16pc + 4g + e sits at column 32 (pc / 2) + 8g + 4 (pc % 2) + e
-            st4(Pb + (16 * pa + c16) * LY::L64 + 32 * (pc >> 1) + 8 * g + 4 * (pc & 1), R.p[i]);
+            st4(Pb + s64off(16 * pa + c16, 32 * (pc >> 1) + 8 * g + 4 * (pc & 1)), R.p[i]);
         }
     }
 }
@@ -540,32 +665,43 @@ template <int DK, int DV, bool WO, int ROLE>
 __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int pt, int g,
                               int c16) {
     const bool has_v = WO || wk.has_v;
+    // the solve waves are on the critical path: let their instructions issue
+    // ahead of the consumer sharing their SIMD
+    if constexpr (ROLE < 2) __builtin_amdgcn_s_setprio(2);
     WsStager<DK> st;
-    st.sqk = (int64_t)a.H * DK;
-    st.sv = (int64_t)a.H * DV;
-    st.kg = reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * st.sqk + (int64_t)wk.h * DK;
-    st.qg = reinterpret_cast<const __bf16 *>(a.q) + wk.tok0 * st.sqk + (int64_t)wk.h * DK;
-    st.vg = reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * st.sv + (int64_t)wk.h * DV + wk.row0;
-    st.bg = reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h;
-    st.H = a.H;
-    st.len = wk.len;
-    st.pt = pt;
-    st.nk = st.nq = st.nv = 0;
+    {
+        const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
+        st.init(reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * sqk + (int64_t)wk.h * DK,
+                reinterpret_cast<const __bf16 *>(a.q) + wk.tok0 * sqk + (int64_t)wk.h * DK,
+                reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0,
+                reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h, sqk, sv, a.H, wk.len, pt);
+    }
     // prologue: K(0) into LDS; K(1) and Q(0) in flight
     if (NC > 0) {
         st.load_k(0);
         st.write_k(bf.K(0), bf.B(0));
+        st.load_k(min(1, NC - 1));
+        if (WO) st.load_q(0);
     }
-    if (1 < NC) st.load_k(1);
-    if (WO && 0 < NC) st.load_q(0);
     __syncthreads();
+    if (NC == 0) { // no chunks: the same barriers as the consumers' two iterations
+#pragma unroll
+        for (int i = 0; i < 4; ++i) __syncthreads();
+        return;
+    }
 
+    // Staging is unconditional (chunk indices clamped to the last chunk): the
+    // copies past the end land in ring slots that are never read again, and
+    // straight-line loads let every wait count only the loads it needs.
     OffGram og;
     WPRegs<DK> wr;
+    const int last = NC - 1;
     for (int r = -2; r < NC; ++r) {
         // ---------------- phase 1
-        if (has_v && r + 1 >= 0 && r + 1 < NC) st.write_v(bf.V());
-        if (has_v && r + 2 < NC) st.load_v(r + 2);
+        if (has_v) {
+            st.write_v(bf.V());              // V(r+1)
+            st.load_v(min(max(r + 2, 0), last)); // V(r+2)
+        }
         if constexpr (ROLE == 0) {
             if (r + 2 < NC) diag_solve<DK>(bf, r + 2, g, c16);
         } else if constexpr (ROLE == 1) {
@@ -580,10 +716,10 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
         } else if constexpr (ROLE >= 2) {
             if (r + 1 >= 0 && r + 1 < NC) wp_write<DK, WO>(wr, bf, ROLE - 2, g, c16);
         }
-        if (r + 3 < NC) st.write_k(bf.K(r + 3), bf.B(r + 3));
-        if (WO && r + 2 < NC) st.write_q(bf.Q(r + 2));
-        if (r + 4 < NC) st.load_k(r + 4);
-        if (WO && r + 3 < NC) st.load_q(r + 3);
+        st.write_k(bf.K(r + 3), bf.B(r + 3)); // K(r+3)
+        if (WO) st.write_q(bf.Q(r + 2));      // Q(r+2)
+        st.load_k(min(r + 4, last));
+        if (WO) st.load_q(min(r + 3, last));
         __syncthreads();
     }
 }
