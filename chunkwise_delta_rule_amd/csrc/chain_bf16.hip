@@ -12,17 +12,19 @@
 // Wave roles (two waves per SIMD; wave w and w+4 share a SIMD):
 //   waves 0-3  consumers: each holds 16 rows of S in fp32 registers and runs
 //              Z, O and the state update of chunk r, then U of chunk r+1
-//   wave 4     diagonal 16x16 Gram tiles of chunk r+2 and their inverses by
-//              forward substitution ("Solving for U": one column per lane,
-//              entries of A broadcast along the 16-lane row with DPP)
-//   wave 5     off-diagonal Gram tiles of chunk r+2, then the off-diagonal
-//              blocks of N by block substitution on the matrix cores
-//   waves 6-7  W and P of chunk r+1
+//   wave 4     diagonal 16x16 Gram tiles of chunk r+3 (phase 2) and their
+//              inverses for chunk r+2 by forward substitution (phase 1;
+//              "Solving for U": one column per lane, entries of A broadcast
+//              along the 16-lane row with DPP)
+//   wave 5     off-diagonal Gram tiles of chunk r+3 (phase 2) and the
+//              off-diagonal blocks of N of chunk r+1 by block substitution on
+//              the matrix cores (phase 1)
+//   waves 6-7  P (phase 1) and W (phase 2) of chunk r+1
 //   waves 4-7  also stage K, Q, V and beta from HBM, one iteration ahead
-// Each iteration has two barrier-separated phases; the producers run two
-// chunks (solve) and one chunk (W, P) ahead of the consumers. LDS rings:
-// K x3, Q x2, T^T x2, and one each of W, P, V, so every buffer written in a
-// phase is read by nobody in that phase.
+// Each iteration has two barrier-separated phases, and every producer has
+// work in both. LDS rings: K x4, Q x2, T^T x2, N x2, off-diagonal operands
+// x2, beta x4, and one each of W, P, V; every buffer written in a phase is
+// read by nobody in that phase.
 //
 // Matrix-core layout (16x16x32 bf16, wave64, lane l = 16 g + c, g = l / 16):
 // lane l holds row (or column) c of an operand and the 8 contraction slots
@@ -90,23 +92,34 @@ __device__ inline bf16x4 tr4(const __bf16 *p) {
 }
 __device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Broadcast lane I of each 16-lane row to the whole row (DPP row_newbcast).
-template <int I> __device__ inline float row_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + I, 0xF, 0xF, true));
+// acc + a_I * b, where a_I is the value of a in lane I of this lane's 16-lane
+// row: one v_fmac_f32 whose first operand is read through DPP row_newbcast.
+template <int I> __device__ inline float fmac_bcast(float acc, float a, float b) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(a), "v"(b), "i"(I));
+    return acc;
 }
 // Column c of (I + A)^-1 for a 16x16 strictly lower A whose row c sits in
 // lane c of the 16-lane row: once x_J is final it is removed from every later
 // row (right-looking forward substitution).
-template <int J> __device__ inline void fwd_subst(float (&x)[16], const float (&arow)[16]) {
+template <int J> __device__ inline void fwd_subst_step(float (&x)[16], const float (&arow)[16]) {
     if constexpr (J < 15) {
         const float nxj = -x[J];
 #define DN_UPD(I)                                                                                              \
-    if constexpr (I > J) x[I] = fmaf(row_bcast<I>(arow[J]), nxj, x[I]);
+    if constexpr (I > J) x[I] = fmac_bcast<I>(x[I], arow[J], nxj);
         DN_UPD(1) DN_UPD(2) DN_UPD(3) DN_UPD(4) DN_UPD(5) DN_UPD(6) DN_UPD(7) DN_UPD(8)
         DN_UPD(9) DN_UPD(10) DN_UPD(11) DN_UPD(12) DN_UPD(13) DN_UPD(14) DN_UPD(15)
 #undef DN_UPD
-        fwd_subst<J + 1>(x, arow);
+        fwd_subst_step<J + 1>(x, arow);
     }
+}
+__device__ inline void fwd_subst(float (&x)[16], float (&arow)[16]) {
+    // DPP reads of a register need two wait states after a VALU write of it:
+    // settle all of arow first, then wait once.
+    asm volatile("" : "+v"(arow[0]), "+v"(arow[1]), "+v"(arow[2]), "+v"(arow[3]), "+v"(arow[4]), "+v"(arow[5]),
+                 "+v"(arow[6]), "+v"(arow[7]), "+v"(arow[8]), "+v"(arow[9]), "+v"(arow[10]), "+v"(arow[11]),
+                 "+v"(arow[12]), "+v"(arow[13]), "+v"(arow[14]), "+v"(arow[15]));
+    asm volatile("s_nop 1");
+    fwd_subst_step<0>(x, arow);
 }
 
 // Element offsets inside the LDS buffers. K, Q, W: [64][DK]; T^T, P, V tile:
@@ -126,32 +139,36 @@ __device__ inline int dk_of(int m, int g) { return 32 * (m >> 1) + 8 * g + 4 * (
 
 // LDS layout (bytes).
 template <int DK> struct WsLds {
-    static constexpr int LX = 16 + 4; // diagonal Gram tiles for the row exchange: [64][LX] fp32
-    static constexpr int LN = 16 + 8; // N^T of the four diagonal blocks: [64][LN] bf16
+    static constexpr int LX = 16; // diagonal Gram tiles for the row exchange: [64][LX] fp32
+    static constexpr int LN = 16; // N^T of the four diagonal blocks: [64][LN] bf16
     static constexpr size_t szK = sizeof(__bf16) * 64 * DK;
     static constexpr size_t sz64 = sizeof(__bf16) * 64 * 64;
-    static constexpr size_t oK = 0;             // 3 buffers, chunk c in buffer c % 3
-    static constexpr size_t oQ = oK + 3 * szK;  // 2 buffers, c % 2
+    static constexpr size_t oK = 0;             // 4 buffers, chunk c in buffer c % 4
+    static constexpr size_t oQ = oK + 4 * szK;  // 2 buffers, c % 2
     static constexpr size_t oW = oQ + 2 * szK;  // -W
     static constexpr size_t oT = oW + szK;      // T^T, 2 buffers, c % 2
     static constexpr size_t oP = oT + 2 * sz64; // P, columns interleaved
     static constexpr size_t oV = oP + sz64;     // V: this workgroup's 64 value columns
-    static constexpr size_t oN = oV + sz64;
-    static constexpr size_t oX = oN + sizeof(__bf16) * 64 * LN;
-    static constexpr size_t oB = oX + sizeof(float) * 64 * LX; // beta ring, 4 x 64 fp32, c % 4
+    static constexpr size_t szN = sizeof(__bf16) * 64 * LN;
+    static constexpr size_t szA = 6 * 64 * 8;
+    static constexpr size_t oN = oV + sz64;                     // 2 buffers, c % 2
+    static constexpr size_t oX = oN + 2 * szN;
+    static constexpr size_t oA = oX + sizeof(float) * 64 * LX;  // off-diagonal Gram operands, 2 buffers, c % 2
+    static constexpr size_t oB = oA + 2 * szA;                  // beta ring, 4 x 64 fp32, c % 4
     static constexpr size_t total = oB + sizeof(float) * 4 * 64;
 };
 
 // Shared LDS pointers of one workgroup.
 template <int DK> struct WsBufs {
     unsigned char *base;
-    __device__ inline __bf16 *K(int c) const { return (__bf16 *)(base + WsLds<DK>::oK + (c % 3) * WsLds<DK>::szK); }
+    __device__ inline __bf16 *K(int c) const { return (__bf16 *)(base + WsLds<DK>::oK + (c & 3) * WsLds<DK>::szK); }
     __device__ inline __bf16 *Q(int c) const { return (__bf16 *)(base + WsLds<DK>::oQ + (c & 1) * WsLds<DK>::szK); }
     __device__ inline __bf16 *W() const { return (__bf16 *)(base + WsLds<DK>::oW); }
     __device__ inline __bf16 *Tt(int c) const { return (__bf16 *)(base + WsLds<DK>::oT + (c & 1) * WsLds<DK>::sz64); }
     __device__ inline __bf16 *P() const { return (__bf16 *)(base + WsLds<DK>::oP); }
     __device__ inline __bf16 *V() const { return (__bf16 *)(base + WsLds<DK>::oV); }
-    __device__ inline __bf16 *N() const { return (__bf16 *)(base + WsLds<DK>::oN); }
+    __device__ inline __bf16 *N(int c) const { return (__bf16 *)(base + WsLds<DK>::oN + (c & 1) * WsLds<DK>::szN); }
+    __device__ inline __bf16 *A(int c) const { return (__bf16 *)(base + WsLds<DK>::oA + (c & 1) * WsLds<DK>::szA); }
     __device__ inline float *X() const { return (float *)(base + WsLds<DK>::oX); }
     __device__ inline float *B(int c) const { return (float *)(base + WsLds<DK>::oB) + (c & 3) * 64; }
 };
@@ -410,8 +427,8 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
                     : nullptr; // only dereferenced with output
     const int kq = c16 >> 2, kr = c16 & 3; // transposing-read provider coordinates
 
-    __syncthreads(); // K(0) staged
-    for (int r = -2; r < NC; ++r) {
+    __syncthreads(); // matches the producers' prologue
+    for (int r = -3; r < NC; ++r) {
         // ---------------- phase 1: chain of chunk r
         if (r >= 0)
             consumer_chain<DK, WO>(bf, r, Sacc, Zacc, O, WO ? og + (int64_t)r * kChunk * sv : nullptr, sv,
@@ -453,11 +470,11 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
 }
 
 // ---------------------------------------------------------------------------
-// Producers (waves 4-7). ROLE 0: diagonal solve; 1: off-diagonal Gram and
-// block substitution; 2, 3: W and P (halves).
+// Producers (waves 4-7). ROLE 0: diagonal Gram tiles and solve; 1:
+// off-diagonal Gram tiles and block substitution; 2, 3: P and W (halves).
 // ---------------------------------------------------------------------------
 
-// Row fragments of the four 16-row blocks of K (slots = dk 32 kb + 8 g ..).
+// Row fragments of the four 16-row blocks of a K / Q buffer (slots = dk 32 kb + 8 g ..).
 template <int DK> struct KRows {
     bf16x8 f[4][DK / 32];
 };
@@ -475,19 +492,27 @@ template <int DK> __device__ inline f32x4 dot_tile(const bf16x8 (&x)[DK / 32], c
     return acc;
 }
 
-// Wave 4, phase 1: diagonal Gram tiles G_bb of chunk c, lane group b solves
-// block b: lane (b, j) computes column j of N_bb = (I + A_bb)^-1; writes
+// Wave 4, phase 2: the four diagonal Gram tiles G_bb of chunk c into the row
+// exchange buffer X (row 16b + j holds G_bb[j][0..15]; G_bb is symmetric).
+template <int DK> __device__ inline void gram_diag(const WsBufs<DK> &bf, int c, int g, int c16) {
+    using LY = WsLds<DK>;
+    float *X = bf.X();
+    const __bf16 *Kb = bf.K(c);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        bf16x8 kf[DK / 32];
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) kf[kb] = ld8(Kb + koff<DK>(16 * b + c16, 32 * kb + 8 * g));
+        *reinterpret_cast<f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g) = dot_tile<DK>(kf, kf);
+    }
+}
+
+// Wave 4, phase 1: lane group b solves diagonal block b of chunk c: lane
+// (b, j) computes column j of N_bb = (I + A_bb)^-1 from row j of G_bb; writes
 // N_bb^T (for wave 5) and the diagonal blocks of T^T.
 template <int DK> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c, int g, int c16) {
     using LY = WsLds<DK>;
-    float *X = bf.X();
-    KRows<DK> k;
-    k_rows<DK>(k, bf.K(c), g, c16);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        // G_bb[c][4g + i] (symmetric) -> X row 16b + c
-        *reinterpret_cast<f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g) = dot_tile<DK>(k.f[b], k.f[b]);
-    }
+    const float *X = bf.X();
     const float br = bf.B(c)[16 * g + c16];
     float arow[16];
 #pragma unroll
@@ -499,9 +524,9 @@ template <int DK> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c,
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == c16) ? 1.f : 0.f;
-    fwd_subst<0>(x, arow);
+    fwd_subst(x, arow);
     // x[i] = N_gg[i][c]; N^T row 16g + c; T^T row 16g + c, columns 16g..16g+15
-    __bf16 *Nr = bf.N() + (16 * g + c16) * LY::LN;
+    __bf16 *Nr = bf.N(c) + (16 * g + c16) * LY::LN;
     __bf16 *Tt = bf.Tt(c);
     const int trow = 16 * g + c16;
     const f32x4 x0 = {x[0], x[1], x[2], x[3]}, x1 = {x[4], x[5], x[6], x[7]};
@@ -512,34 +537,33 @@ template <int DK> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c,
     st8(Tt + s64off(trow, 16 * g + 8), cvt8(x2 * br, x3 * br));
 }
 
-// Wave 5, phase 1: off-diagonal Gram tiles of chunk c as bf16 k16 operands,
-// A_ac (a > c): lane (g, j) holds A[16a + j][16c + 4g .. +3].
-struct OffGram {
-    bf16x4 A10, A20, A21, A30, A31, A32;
-};
-template <int DK> __device__ inline OffGram off_gram(const WsBufs<DK> &bf, int c, int g, int c16) {
+// Wave 5, phase 2: off-diagonal Gram tiles of chunk c as bf16 k16 operands,
+// A_ac (a > c): lane (g, j) holds A[16a + j][16c + 4g .. +3]; stored per lane
+// in the order A10, A20, A21, A30, A31, A32.
+template <int DK> __device__ inline void off_gram(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
     KRows<DK> k;
     k_rows<DK>(k, bf.K(c), g, c16);
     const float *Bs = bf.B(c);
     const float b1 = Bs[16 + c16], b2 = Bs[32 + c16], b3 = Bs[48 + c16];
-    OffGram o;
+    __bf16 *As = bf.A(c) + 4 * lane;
     // dot_tile(K_c, K_a)[i] = k_{16c+4g+i} . k_{16a+j} = G[16a + j][16c + 4g + i]
-    o.A10 = cvt4(dot_tile<DK>(k.f[0], k.f[1]) * b1);
-    o.A20 = cvt4(dot_tile<DK>(k.f[0], k.f[2]) * b2);
-    o.A21 = cvt4(dot_tile<DK>(k.f[1], k.f[2]) * b2);
-    o.A30 = cvt4(dot_tile<DK>(k.f[0], k.f[3]) * b3);
-    o.A31 = cvt4(dot_tile<DK>(k.f[1], k.f[3]) * b3);
-    o.A32 = cvt4(dot_tile<DK>(k.f[2], k.f[3]) * b3);
-    return o;
+    st4(As + 0 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[1]) * b1));
+    st4(As + 1 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[2]) * b2));
+    st4(As + 2 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[2]) * b2));
+    st4(As + 3 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[3]) * b3));
+    st4(As + 4 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[3]) * b3));
+    st4(As + 5 * 256, cvt4(dot_tile<DK>(k.f[2], k.f[3]) * b3));
 }
 
-// Wave 5, phase 2: N_ab = -N_aa sum_{c=b}^{a-1} A_ac N_cb for a > b, and
+// Wave 5, phase 1: N_ab = -N_aa sum_{c=b}^{a-1} A_ac N_cb for a > b, and
 // T_ab = N_ab diag(beta_b) into T^T (row 16b + j, columns 16a + 4g ..).
-template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, const OffGram &o, int c, int g, int c16) {
+template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
     using LY = WsLds<DK>;
-    const __bf16 *Ns = bf.N();
+    const __bf16 *Ns = bf.N(c), *As = bf.A(c) + 4 * lane;
     const float *Bs = bf.B(c);
     __bf16 *Tt = bf.Tt(c);
+    const bf16x4 A10 = ld4(As + 0 * 256), A20 = ld4(As + 1 * 256), A21 = ld4(As + 2 * 256);
+    const bf16x4 A30 = ld4(As + 3 * 256), A31 = ld4(As + 4 * 256), A32 = ld4(As + 5 * 256);
     // B fragments of the diagonal blocks: N_bb[4g + e][c16] = N^T[16b + c16][4g + e]
     const bf16x4 n00 = ld4(Ns + (c16)*LY::LN + 4 * g);
     const bf16x4 n11 = ld4(Ns + (16 + c16) * LY::LN + 4 * g);
@@ -555,17 +579,17 @@ template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, const O
         st4(Tt + s64off(16 * b + c16, 16 * a + 4 * g), cvt4(nab * be));
     };
     // column block 0
-    const f32x4 n10 = -mfma16(r11, cvt4(mfma16(o.A10, n00, z)), z);
+    const f32x4 n10 = -mfma16(r11, cvt4(mfma16(A10, n00, z)), z);
     const bf16x4 f10 = cvt4(n10);
-    const f32x4 n20 = -mfma16(r22, cvt4(mfma16(o.A21, f10, mfma16(o.A20, n00, z))), z);
+    const f32x4 n20 = -mfma16(r22, cvt4(mfma16(A21, f10, mfma16(A20, n00, z))), z);
     const bf16x4 f20 = cvt4(n20);
-    const f32x4 n30 = -mfma16(r33, cvt4(mfma16(o.A32, f20, mfma16(o.A31, f10, mfma16(o.A30, n00, z)))), z);
+    const f32x4 n30 = -mfma16(r33, cvt4(mfma16(A32, f20, mfma16(A31, f10, mfma16(A30, n00, z)))), z);
     // column block 1
-    const f32x4 n21 = -mfma16(r22, cvt4(mfma16(o.A21, n11, z)), z);
+    const f32x4 n21 = -mfma16(r22, cvt4(mfma16(A21, n11, z)), z);
     const bf16x4 f21 = cvt4(n21);
-    const f32x4 n31 = -mfma16(r33, cvt4(mfma16(o.A32, f21, mfma16(o.A31, n11, z))), z);
+    const f32x4 n31 = -mfma16(r33, cvt4(mfma16(A32, f21, mfma16(A31, n11, z))), z);
     // column block 2
-    const f32x4 n32 = -mfma16(r33, cvt4(mfma16(o.A32, n22, z)), z);
+    const f32x4 n32 = -mfma16(r33, cvt4(mfma16(A32, n22, z)), z);
     put(0, 1, n10, be0);
     put(0, 2, n20, be0);
     put(0, 3, n30, be0);
@@ -574,24 +598,13 @@ template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, const O
     put(2, 3, n32, be2);
 }
 
-// Waves 6-7: W = T K for half of the dk tiles and half of the score tiles of
-// chunk c, kept in registers during phase 1 and written in phase 2. W tile mt
-// uses the dk labels of state tile mt, so its K^T fragments are the
-// conflict-free transposing reads of the state update.
-template <int DK> struct WPRegs {
-    static constexpr int MT = DK / 32; // dk tiles per wave
-    bf16x4 w[MT][4];                   // -W[16nt + c][delta(mt, g, 0..3)]
-    bf16x4 p[5];                       // score tiles
-};
-
-// Score tiles: wave 6 rows blocks {0, 3}, wave 7 blocks {1, 2}.
-__device__ constexpr int kPA[2][5] = {{0, 3, 3, 3, 3}, {1, 1, 2, 2, 2}};
-__device__ constexpr int kPC[2][5] = {{0, 0, 1, 2, 3}, {0, 1, 0, 1, 2}};
-
-template <int DK, bool WO>
-__device__ inline void wp_compute(WPRegs<DK> &R, const WsBufs<DK> &bf, int c, int half, int g, int c16) {
-    constexpr int MT = WPRegs<DK>::MT;
+// Waves 6-7, phase 2: W = T K for half of the dk tiles of chunk c, written as
+// -W. W tile mt uses the dk labels of state tile mt, so its K^T fragments are
+// the conflict-free transposing reads of the state update.
+template <int DK> __device__ inline void w_tiles(const WsBufs<DK> &bf, int c, int half, int g, int c16) {
+    constexpr int MT = DK / 32; // dk tiles per wave
     const __bf16 *Kb = bf.K(c), *Tb = bf.Tt(c);
+    __bf16 *Wb = bf.W();
     const int kq = c16 >> 2, kr = c16 & 3;
     // T^T column fragments: lane (g, j) slots = tokens 32s + 16h + 4g + e of column 16nt + j
     bf16x8 tf[4][2];
@@ -614,50 +627,48 @@ __device__ inline void wp_compute(WPRegs<DK> &R, const WsBufs<DK> &bf, int c, in
 #pragma unroll
             for (int s = 0; s <= nt / 2; ++s) acc = mfma32(kf[s], tf[nt][s], acc);
             // acc[i] = W[16nt + c][delta(mt, g, i)]
-            R.w[mm][nt] = cvt4(-acc);
-        }
-    }
-    if constexpr (WO) {
-        const __bf16 *Qb = bf.Q(c);
-        // K row blocks 0..3 and this wave's two Q row blocks ({0, 3} or {1, 2})
-        KRows<DK> k;
-        k_rows<DK>(k, Kb, g, c16);
-        bf16x8 qf[2][DK / 32];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb)
-                qf[i][kb] = ld8(Qb + koff<DK>(16 * (half ? 1 + i : 3 * i) + c16, 32 * kb + 8 * g));
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const int pa = kPA[half][i], pc = kPC[half][i];
-            const int qi = half ? pa - 1 : (pa == 3 ? 1 : 0);
-            // acc[e] = k_{16pc+4g+e} . q_{16pa+c} = P[16pa + c][16pc + 4g + e]
-            f32x4 acc = dot_tile<DK>(k.f[pc], qf[qi]);
-            if (pa == pc) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e > c16) ? 0.f : acc[e];
-            }
-            R.p[i] = cvt4(acc);
+            st4(Wb + koff<DK>(16 * nt + c16, dk_of(mt, g)), cvt4(-acc));
         }
     }
 }
-template <int DK, bool WO>
-__device__ inline void wp_write(const WPRegs<DK> &R, const WsBufs<DK> &bf, int half, int g, int c16) {
-    constexpr int MT = WPRegs<DK>::MT;
-    __bf16 *Wb = bf.W();
+
+// Waves 6-7: the score tiles of chunk c, wave 6 rows blocks {0, 3}, wave 7
+// blocks {1, 2}; computed in phase 1, written in phase 2.
+__device__ constexpr int kPA[2][5] = {{0, 3, 3, 3, 3}, {1, 1, 2, 2, 2}};
+__device__ constexpr int kPC[2][5] = {{0, 0, 1, 2, 3}, {0, 1, 0, 1, 2}};
+struct PRegs {
+    bf16x4 p[5];
+};
+template <int DK> __device__ inline void p_compute(PRegs &R, const WsBufs<DK> &bf, int c, int half, int g, int c16) {
+    const __bf16 *Kb = bf.K(c), *Qb = bf.Q(c);
+    KRows<DK> k;
+    k_rows<DK>(k, Kb, g, c16);
+    bf16x8 qf[2][DK / 32];
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) st4(Wb + koff<DK>(16 * nt + c16, dk_of(half * MT + mm, g)), R.w[mm][nt]);
-    if constexpr (WO) {
-        __bf16 *Pb = bf.P();
+        for (int kb = 0; kb < DK / 32; ++kb)
+            qf[i][kb] = ld8(Qb + koff<DK>(16 * (half ? 1 + i : 3 * i) + c16, 32 * kb + 8 * g));
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const int pa = kPA[half][i], pc = kPC[half][i];
-            // token 16pc + 4g + e sits at column 32 (pc / 2) + 8g + 4 (pc % 2) + e
-            st4(Pb + s64off(16 * pa + c16, 32 * (pc >> 1) + 8 * g + 4 * (pc & 1)), R.p[i]);
+    for (int i = 0; i < 5; ++i) {
+        const int pa = kPA[half][i], pc = kPC[half][i];
+        const int qi = half ? pa - 1 : (pa == 3 ? 1 : 0);
+        // acc[e] = k_{16pc+4g+e} . q_{16pa+c} = P[16pa + c][16pc + 4g + e]
+        f32x4 acc = dot_tile<DK>(k.f[pc], qf[qi]);
+        if (pa == pc) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e > c16) ? 0.f : acc[e];
         }
+        R.p[i] = cvt4(acc);
+    }
+}
+template <int DK> __device__ inline void p_write(const PRegs &R, const WsBufs<DK> &bf, int half, int g, int c16) {
+    __bf16 *Pb = bf.P();
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int pa = kPA[half][i], pc = kPC[half][i];
+        // token 16pc + 4g + e sits at column 32 (pc / 2) + 8g + 4 (pc % 2) + e
+        st4(Pb + s64off(16 * pa + c16, 32 * (pc >> 1) + 8 * g + 4 * (pc & 1)), R.p[i]);
     }
 }
 
@@ -665,6 +676,7 @@ template <int DK, int DV, bool WO, int ROLE>
 __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int pt, int g,
                               int c16) {
     const bool has_v = WO || wk.has_v;
+    const int lane = 16 * g + c16;
     // the solve waves are on the critical path: let their instructions issue
     // ahead of the consumer sharing their SIMD
     if constexpr (ROLE < 2) __builtin_amdgcn_s_setprio(2);
@@ -676,50 +688,55 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
                 reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0,
                 reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h, sqk, sv, a.H, wk.len, pt);
     }
-    // prologue: K(0) into LDS; K(1) and Q(0) in flight
-    if (NC > 0) {
-        st.load_k(0);
-        st.write_k(bf.K(0), bf.B(0));
-        st.load_k(min(1, NC - 1));
-        if (WO) st.load_q(0);
-    }
+    if (NC > 0) st.load_k(0); // K(0) is written in the first iteration
     __syncthreads();
-    if (NC == 0) { // no chunks: the same barriers as the consumers' two iterations
+    if (NC == 0) { // no chunks: the same barriers as the consumers' three iterations
 #pragma unroll
-        for (int i = 0; i < 4; ++i) __syncthreads();
+        for (int i = 0; i < 6; ++i) __syncthreads();
         return;
     }
 
-    // Staging is unconditional (chunk indices clamped to the last chunk): the
-    // copies past the end land in ring slots that are never read again, and
+    // Per iteration r (chunk indices; staging of chunk c happens before its
+    // first reader: K(c) in phase 1 of r = c-3, V(c) in phase 1 of c-1, Q(c)
+    // in phase 2 of c-2):
+    //   phase 1: diagonal solve (r+2) | off-diagonal solve (r+1) | P (r+1)
+    //   phase 2: diagonal Gram (r+3)  | off-diagonal Gram (r+3)  | W (r+1), P written
+    // Staging is unconditional (chunk indices clamped to the sequence): the
+    // copies outside it land in ring slots that are never read, and
     // straight-line loads let every wait count only the loads it needs.
-    OffGram og;
-    WPRegs<DK> wr;
+    PRegs pr;
     const int last = NC - 1;
-    for (int r = -2; r < NC; ++r) {
+    for (int r = -3; r < NC; ++r) {
         // ---------------- phase 1
+        st.write_k(bf.K(r + 3), bf.B(r + 3)); // K(r+3)
+        st.load_k(min(r + 4, last));
         if (has_v) {
-            st.write_v(bf.V());              // V(r+1)
+            st.write_v(bf.V());                   // V(r+1)
             st.load_v(min(max(r + 2, 0), last)); // V(r+2)
         }
         if constexpr (ROLE == 0) {
-            if (r + 2 < NC) diag_solve<DK>(bf, r + 2, g, c16);
+            if (r + 2 >= 0 && r + 2 < NC) diag_solve<DK>(bf, r + 2, g, c16);
         } else if constexpr (ROLE == 1) {
-            if (r + 2 < NC) og = off_gram<DK>(bf, r + 2, g, c16);
-        } else {
-            if (r + 1 >= 0 && r + 1 < NC) wp_compute<DK, WO>(wr, bf, r + 1, ROLE - 2, g, c16);
+            if (r + 1 >= 0 && r + 1 < NC) off_solve<DK>(bf, r + 1, lane, g, c16);
+        } else if constexpr (WO) {
+            if (r + 1 >= 0 && r + 1 < NC) p_compute<DK>(pr, bf, r + 1, ROLE - 2, g, c16);
         }
         __syncthreads();
         // ---------------- phase 2
-        if constexpr (ROLE == 1) {
-            if (r + 2 < NC) off_solve<DK>(bf, og, r + 2, g, c16);
-        } else if constexpr (ROLE >= 2) {
-            if (r + 1 >= 0 && r + 1 < NC) wp_write<DK, WO>(wr, bf, ROLE - 2, g, c16);
+        if constexpr (ROLE == 0) {
+            if (r + 3 < NC) gram_diag<DK>(bf, r + 3, g, c16);
+        } else if constexpr (ROLE == 1) {
+            if (r + 3 < NC) off_gram<DK>(bf, r + 3, lane, g, c16);
+        } else {
+            if (r + 1 >= 0 && r + 1 < NC) {
+                w_tiles<DK>(bf, r + 1, ROLE - 2, g, c16);
+                if constexpr (WO) p_write<DK>(pr, bf, ROLE - 2, g, c16);
+            }
         }
-        st.write_k(bf.K(r + 3), bf.B(r + 3)); // K(r+3)
-        if (WO) st.write_q(bf.Q(r + 2));      // Q(r+2)
-        st.load_k(min(r + 4, last));
-        if (WO) st.load_q(min(r + 3, last));
+        if (WO) {
+            st.write_q(bf.Q(r + 2)); // Q(r+2)
+            st.load_q(min(max(r + 3, 0), last));
+        }
         __syncthreads();
     }
 }
