@@ -5,26 +5,29 @@
 // order, evaluating per chunk the algorithm of "Linear Attention, Visualized"
 // (Haoran Zhang), DeltaNet > "Complete per-chunk algorithm", with S transposed
 // as in "Context Parallelism for DeltaNet" (yywangcs), section 2:
-//   A  = diag(beta) (K K^T), strictly lower      N = (I + A)^-1,  T = N diag(beta)
-//   W  = T K,  U = T V,  P = (Q K^T) lower-inclusive
-//   Z  = U - W S^T,  O = Q S^T + P Z,  S <- S + Z^T K.
+//   A = diag(beta) (K K^T), strictly lower      N = (I + A)^-1,  T = N diag(beta)
+//   P = (Q K^T) lower-inclusive
+//   Y = V - K S^T,  Z = T Y,  O = Q S^T + P Z,  S <- S + Z^T K.
+// Z is the page's U - W S^T (W = T K, U = T V) with T taken out on the left,
+// so neither W nor U is formed: everything that depends on the state is one
+// chain of products per 16 state rows, and everything else (Gram tiles, the
+// inverse, P) depends only on the chunk and runs ahead of that chain.
 //
-// Wave roles (two waves per SIMD; wave w and w+4 share a SIMD):
+// Wave roles (two waves per SIMD; wave w and w+4 share a SIMD), iteration r:
 //   waves 0-3  consumers: each holds 16 rows of S in fp32 registers and runs
-//              Z, O and the state update of chunk r, then U of chunk r+1
-//   wave 4     diagonal 16x16 Gram tiles of chunk r+3 (phase 2) and their
-//              inverses for chunk r+2 by forward substitution (phase 1;
-//              "Solving for U": one column per lane, entries of A broadcast
-//              along the 16-lane row with DPP)
-//   wave 5     off-diagonal Gram tiles of chunk r+3 (phase 2) and the
-//              off-diagonal blocks of N of chunk r+1 by block substitution on
-//              the matrix cores (phase 1)
-//   waves 6-7  P (phase 1) and W (phase 2) of chunk r+1
-//   waves 4-7  also stage K, Q, V and beta from HBM, one iteration ahead
-// Each iteration has two barrier-separated phases, and every producer has
-// work in both. LDS rings: K x4, Q x2, T^T x2, N x2, off-diagonal operands
-// x2, beta x4, and one each of W, P, V; every buffer written in a phase is
-// read by nobody in that phase.
+//              Y, Z, O and the state update of chunk r
+//   wave 4     diagonal 16x16 Gram tiles of chunk r+2 and their inverses by
+//              forward substitution ("Solving for U": one column per lane,
+//              entries of A broadcast along the 16-lane row with DPP)
+//   wave 5     T of chunk r+1 (off-diagonal blocks by block substitution on
+//              the matrix cores, diagonal blocks from wave 4's columns), then
+//              the off-diagonal Gram tiles of chunk r+2
+//   waves 6-7  P of chunk r+1, half of the row blocks each; Q goes from HBM
+//              straight into their operand registers and on to the Q ring
+//   waves 4-7  also stage K, V and beta from HBM
+// One barrier per chunk; a buffer written in an iteration is read by nobody
+// in that iteration. LDS rings: K x4, Q x2, T^T x2, P x2, V x2, N x2, X x2,
+// off-diagonal operands x2, beta x4.
 //
 // Matrix-core layout (16x16x32 bf16, wave64, lane l = 16 g + c, g = l / 16):
 // lane l holds row (or column) c of an operand and the 8 contraction slots
@@ -38,18 +41,19 @@
 //   * dk index of the state accumulator tile m, lane group g, register i:
 //       delta(m, g, i) = 32 (m / 2) + 8 g + 4 ((m + g) % 2) + i
 //     so a pair of state tiles (2s, 2s+1) gives lane group g the 8
-//     consecutive dk values 32 s + 8 g .. +7 (in one order or the other): W
+//     consecutive dk values 32 s + 8 g .. +7 (in one order or the other): K
 //     and Q rows are read as one 16-byte piece each from their natural
 //     row-major layout, and the transposing reads of K for the state update
 //     alternate the two 8-byte halves of each 16-byte unit;
-//   * tokens keep their natural order in Z; consecutive Z tiles (2s, 2s+1)
-//     give lane group g tokens 32 s + 4 g + e and 32 s + 16 + 4 g + e, so the
-//     columns of P are stored in the matching interleaved order.
+//   * tokens keep their natural order in Y and Z; consecutive tiles (2s,
+//     2s+1) give lane group g tokens 32 s + 4 g + e and 32 s + 16 + 4 g + e,
+//     so T is read as columns of T^T by transposing reads and P is stored as
+//     ready-made operand fragments in that token order.
 // LDS rows are unpadded; the 16-byte units of each row are permuted by an XOR
 // of a few row bits so that all of the fragment reads above, the 8-byte
-// writes of W and T^T and the staging writes are free of bank conflicts
-// (64 banks of 4 bytes; 16 lanes per pass for 16-byte accesses, 32 lanes per
-// pass for 8-byte ones).
+// writes of T^T and the staging writes are free of bank conflicts (64 banks
+// of 4 bytes; 16 lanes per pass for 16-byte accesses, 32 lanes per pass for
+// 8-byte ones).
 #include "dn_internal.h"
 #include "dn_work.h"
 
@@ -92,6 +96,19 @@ __device__ inline bf16x4 tr4(const __bf16 *p) {
 }
 __device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Compile-time loop: f(Int<I>{}) for I = B..E-1. Long unrolled step lists go
+// through this rather than #pragma unroll, whose size limit would otherwise
+// leave the step index (and every register array indexed by it) dynamic.
+template <int I> struct Int {
+    static constexpr int value = I;
+};
+template <int B, int E, typename F> __device__ inline void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(Int<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // acc + a_I * b, where a_I is the value of a in lane I of this lane's 16-lane
 // row: one v_fmac_f32 whose first operand is read through DPP row_newbcast.
 template <int I> __device__ inline float fmac_bcast(float acc, float a, float b) {
@@ -122,7 +139,7 @@ __device__ inline void fwd_subst(float (&x)[16], float (&arow)[16]) {
     fwd_subst_step<0>(x, arow);
 }
 
-// Element offsets inside the LDS buffers. K, Q, W: [64][DK]; T^T, P, V tile:
+// Element offsets inside the LDS buffers. K, Q: [64][DK]; T^T, V tile:
 // [64][64]. The 8-element (16-byte) unit u of row r is stored at unit
 // u ^ swz(r).
 template <int DK> __device__ inline int kswz(int r) {
@@ -136,65 +153,69 @@ __device__ inline int s64swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) &
 __device__ inline int s64off(int r, int c) { return r * 64 + (((c >> 3) ^ s64swz(r)) << 3) + (c & 7); }
 // First dk of the 4-run held by lane group g of state tile m (delta above).
 __device__ inline int dk_of(int m, int g) { return 32 * (m >> 1) + 8 * g + 4 * ((m + g) & 1); }
+// P operand fragment of token tile t and 32-token block s <= t / 2 (0..5).
+__device__ constexpr int pfrag(int t, int s) { return t < 2 ? t : 2 * t - 2 + s; }
 
 // LDS layout (bytes).
 template <int DK> struct WsLds {
-    static constexpr int LX = 16; // diagonal Gram tiles for the row exchange: [64][LX] fp32
+    static constexpr int LX = 16; // diagonal blocks, one row per lane: [64][LX] fp32
     static constexpr int LN = 16; // N^T of the four diagonal blocks: [64][LN] bf16
     static constexpr size_t szK = sizeof(__bf16) * 64 * DK;
     static constexpr size_t sz64 = sizeof(__bf16) * 64 * 64;
-    static constexpr size_t oK = 0;             // 4 buffers, chunk c in buffer c % 4
-    static constexpr size_t oQ = oK + 4 * szK;  // 2 buffers, c % 2
-    static constexpr size_t oW = oQ + 2 * szK;  // -W
-    static constexpr size_t oT = oW + szK;      // T^T, 2 buffers, c % 2
-    static constexpr size_t oP = oT + 2 * sz64; // P, columns interleaved
-    static constexpr size_t oV = oP + sz64;     // V: this workgroup's 64 value columns
+    static constexpr size_t szP = sizeof(__bf16) * 6 * 64 * 8; // six 16x32 operand fragments
     static constexpr size_t szN = sizeof(__bf16) * 64 * LN;
+    static constexpr size_t szX = sizeof(float) * 64 * LX;
     static constexpr size_t szA = 6 * 64 * 8;
-    static constexpr size_t oN = oV + sz64;                     // 2 buffers, c % 2
-    static constexpr size_t oX = oN + 2 * szN;
-    static constexpr size_t oA = oX + sizeof(float) * 64 * LX;  // off-diagonal Gram operands, 2 buffers, c % 2
-    static constexpr size_t oB = oA + 2 * szA;                  // beta ring, 4 x 64 fp32, c % 4
+    static constexpr size_t oK = 0;            // 4 buffers, chunk c in buffer c % 4
+    static constexpr size_t oQ = oK + 4 * szK; // 2 buffers, c % 2 (and so on)
+    static constexpr size_t oT = oQ + 2 * szK; // T^T
+    static constexpr size_t oP = oT + 2 * sz64; // -P as fragments
+    static constexpr size_t oV = oP + 2 * szP; // V: this workgroup's 64 value columns
+    static constexpr size_t oN = oV + 2 * sz64;
+    static constexpr size_t oX = oN + 2 * szN; // Gram rows, then columns of T
+    static constexpr size_t oA = oX + 2 * szX; // off-diagonal Gram operands
+    static constexpr size_t oB = oA + 2 * szA; // beta ring, 4 x 64 fp32, c % 4
     static constexpr size_t total = oB + sizeof(float) * 4 * 64;
 };
 
 // Shared LDS pointers of one workgroup.
 template <int DK> struct WsBufs {
+    using LY = WsLds<DK>;
     unsigned char *base;
-    __device__ inline __bf16 *K(int c) const { return (__bf16 *)(base + WsLds<DK>::oK + (c & 3) * WsLds<DK>::szK); }
-    __device__ inline __bf16 *Q(int c) const { return (__bf16 *)(base + WsLds<DK>::oQ + (c & 1) * WsLds<DK>::szK); }
-    __device__ inline __bf16 *W() const { return (__bf16 *)(base + WsLds<DK>::oW); }
-    __device__ inline __bf16 *Tt(int c) const { return (__bf16 *)(base + WsLds<DK>::oT + (c & 1) * WsLds<DK>::sz64); }
-    __device__ inline __bf16 *P() const { return (__bf16 *)(base + WsLds<DK>::oP); }
-    __device__ inline __bf16 *V() const { return (__bf16 *)(base + WsLds<DK>::oV); }
-    __device__ inline __bf16 *N(int c) const { return (__bf16 *)(base + WsLds<DK>::oN + (c & 1) * WsLds<DK>::szN); }
-    __device__ inline __bf16 *A(int c) const { return (__bf16 *)(base + WsLds<DK>::oA + (c & 1) * WsLds<DK>::szA); }
-    __device__ inline float *X() const { return (float *)(base + WsLds<DK>::oX); }
-    __device__ inline float *B(int c) const { return (float *)(base + WsLds<DK>::oB) + (c & 3) * 64; }
+    __device__ inline __bf16 *K(int c) const { return (__bf16 *)(base + LY::oK + (c & 3) * LY::szK); }
+    __device__ inline __bf16 *Q(int c) const { return (__bf16 *)(base + LY::oQ + (c & 1) * LY::szK); }
+    __device__ inline __bf16 *Tt(int c) const { return (__bf16 *)(base + LY::oT + (c & 1) * LY::sz64); }
+    __device__ inline __bf16 *P(int c) const { return (__bf16 *)(base + LY::oP + (c & 1) * LY::szP); }
+    __device__ inline __bf16 *V(int c) const { return (__bf16 *)(base + LY::oV + (c & 1) * LY::sz64); }
+    __device__ inline __bf16 *N(int c) const { return (__bf16 *)(base + LY::oN + (c & 1) * LY::szN); }
+    __device__ inline float *X(int c) const { return (float *)(base + LY::oX + (c & 1) * LY::szX); }
+    __device__ inline __bf16 *A(int c) const { return (__bf16 *)(base + LY::oA + (c & 1) * LY::szA); }
+    __device__ inline float *B(int c) const { return (float *)(base + LY::oB) + (c & 3) * 64; }
 };
 
-// Global -> register -> LDS staging of one chunk, shared by the 256 threads of
-// waves 4-7 (pt = 0..255). Thread pt owns the same 16-byte column piece of
-// rows RPS * p + pt / KV (p = 0..NK-1) of every chunk, so its addresses are a
-// fixed per-thread pointer plus a per-chunk offset, and (RPS being a multiple
-// of 16) its swizzled LDS offsets are fixed too. A partial last chunk re-reads
-// its last valid row for the missing rows and writes them as zeros.
+// Global -> register -> LDS staging of K, V and beta, shared by the 256
+// threads of waves 4-7 (pt = 0..255). Thread pt owns the same 16-byte column
+// piece of rows RPS * p + pt / KV (p = 0..NK-1) of every chunk, so its
+// addresses are a fixed per-thread pointer plus a per-chunk offset, and (RPS
+// being a multiple of 16) its swizzled LDS offsets are fixed too. A partial
+// last chunk re-reads its last valid row for the missing rows and writes
+// them as zeros.
 template <int DK> struct WsStager {
-    static constexpr int KV = DK / 8;        // 16-byte vectors per K / Q row
-    static constexpr int NK = 64 * KV / 256; // K (and Q) vectors per thread
-    static constexpr int RPS = 256 / KV;     // rows between a thread's K / Q vectors
+    static constexpr int KV = DK / 8;        // 16-byte vectors per K row
+    static constexpr int NK = 64 * KV / 256; // K vectors per thread
+    static constexpr int RPS = 256 / KV;     // rows between a thread's K vectors
     static constexpr int NV = 2;             // vectors per thread of the 64x64 V tile
     static_assert(NK * 256 == 64 * KV && RPS % 16 == 0, "tiling");
-    const __bf16 *kt, *qt, *vt, *bg; // per-thread pointers into chunk 0
+    const __bf16 *kt, *vt, *bg; // per-thread pointers into chunk 0
     int64_t sqk, sv;
-    int H, len, pt, rk0, rv0; // first row of this thread's K / Q and V vectors
+    int H, len, pt, rk0, rv0; // first row of this thread's K and V vectors
     int lk, lv;               // LDS element offsets of the first vector
-    bf16x8 rk[NK], rq[NK], rv[NV];
+    bf16x8 rk[NK], rv[NV];
     __bf16 rb;
-    int nk, nq, nv;
+    int nk, nv;
 
-    __device__ inline void init(const __bf16 *kg, const __bf16 *qg, const __bf16 *vg, const __bf16 *bg_, int64_t sqk_,
-                                int64_t sv_, int H_, int len_, int pt_) {
+    __device__ inline void init(const __bf16 *kg, const __bf16 *vg, const __bf16 *bg_, int64_t sqk_, int64_t sv_,
+                                int H_, int len_, int pt_) {
         sqk = sqk_;
         sv = sv_;
         H = H_;
@@ -203,12 +224,11 @@ template <int DK> struct WsStager {
         rk0 = pt / KV;
         rv0 = pt / 8;
         kt = kg + rk0 * sqk + 8 * (pt % KV);
-        qt = qg + rk0 * sqk + 8 * (pt % KV);
         vt = vg + rv0 * sv + 8 * (pt % 8);
         bg = bg_;
         lk = koff<DK>(rk0, 8 * (pt % KV));
         lv = s64off(rv0, 8 * (pt % 8));
-        nk = nq = nv = 0;
+        nk = nv = 0;
     }
     __device__ inline int rows_of(int c) const { return min(kChunk, len - c * kChunk); }
     // rows STEP * p + r0 of chunk c from per-thread pointer t (row stride ld)
@@ -242,10 +262,6 @@ template <int DK> struct WsStager {
         fetch<NK, RPS>(rk, kt, sqk, c, nk, rk0);
         if (pt < 64) rb = bg[((int64_t)c * kChunk + min(pt, nk - 1)) * H];
     }
-    __device__ inline void load_q(int c) {
-        nq = rows_of(c);
-        fetch<NK, RPS>(rq, qt, sqk, c, nq, rk0);
-    }
     __device__ inline void load_v(int c) {
         nv = rows_of(c);
         fetch<NV, 32>(rv, vt, sv, c, nv, rv0);
@@ -254,8 +270,46 @@ template <int DK> struct WsStager {
         put<NK, RPS, DK>(Ks + lk, rk, nk, rk0);
         if (pt < 64) Bs[pt] = pt < nk ? (float)rb : 0.f;
     }
-    __device__ inline void write_q(__bf16 *Qs) const { put<NK, RPS, DK>(Qs + lk, rq, nq, rk0); }
     __device__ inline void write_v(__bf16 *Vs) const { put<NV, 32, 64>(Vs + lv, rv, nv, rv0); }
+};
+
+// Waves 6-7: the Q rows of two 16-row blocks (wave 6: blocks 0 and 3, wave
+// 7: blocks 1 and 2) go from HBM straight into the row fragments of P's
+// products (lane (g, j): row 16 b + j, dk 32 kb + 8 g .. +7) and from there
+// into the Q ring for the consumers. Rows past the end of the sequence repeat
+// its last row; the outputs they feed are never stored.
+template <int DK> struct QStage {
+    static constexpr int NKB = DK / 32;
+    const __bf16 *qt[2]; // row[i] of chunk 0, dk 8 g
+    int64_t sqk;
+    int len, row[2];
+    bf16x8 f[2][NKB];
+    __device__ static constexpr int block(int half, int i) { return half ? 1 + i : 3 * i; }
+    __device__ inline void init(const __bf16 *qg, int64_t sqk_, int len_, int half, int g, int c16) {
+        sqk = sqk_;
+        len = len_;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            row[i] = 16 * block(half, i) + c16;
+            qt[i] = qg + row[i] * sqk + 8 * g;
+        }
+    }
+    __device__ inline void load(int c) {
+        const int n = min(kChunk, len - c * kChunk);
+        const int64_t off = (int64_t)c * kChunk * sqk;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const __bf16 *b = qt[i] + off + (int64_t)(min(row[i], n - 1) - row[i]) * sqk;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) f[i][kb] = *reinterpret_cast<const bf16x8 *>(b + 32 * kb);
+        }
+    }
+    __device__ inline void write(__bf16 *Qs, int g) const {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) st8(Qs + koff<DK>(row[i], 32 * kb + 8 * g), f[i][kb]);
+    }
 };
 
 // State rows in and out: Sacc[m][i] = S[row][delta(m, g, i)] for the lane's
@@ -301,180 +355,155 @@ template <int DK> __device__ inline bf16x8 k_trfrag(const __bf16 *Kb, int m, int
 // Consumers (waves 0-3).
 // ---------------------------------------------------------------------------
 // The consumer's work on one chunk as a list of matrix products, each with one
-// LDS operand fragment (the other operand is in registers):
-//   Z  (t, s):   Z_t += (-W)_{t,s} SB_s                 4 * DK/32 steps
-//   Op (t, s):   O_t += ZB_s P_{t,s}^T, s <= t/2        6 steps (with output)
-//   S  (m, s):   S^T_m += K^T_{m,s} ZB_s                2 * DK/16 steps
-// The other half of the output, O_t = SB_s Q_{t,s}^T, needs only the state
-// before the chunk, so it runs in the previous iteration's second phase
-// (consumer_oq). Fragments are fetched `depth` steps ahead into a rotating
-// register buffer and scheduling fences keep that order, so LDS latency hides
-// behind the matrix products of the steps in between.
+// LDS operand fragment (the other operand is in registers; SB = bf16(-S)):
+//   Y  (t, kb):  Y_t += K_{t,kb} SB_kb          4 * DK/32 steps (Y_t starts at V_t)
+//   Oq (t, kb):  O_t += SB_kb Q_{t,kb}^T         4 * DK/32 steps (with output)
+//   Z  (t, s):   Z_t += T_{t,s} YB_s, s <= t/2   6 steps
+//   Op (t, s):   O_t += ZB_s (-P)_{t,s}^T        6 steps (with output)
+//   S  (m, s):   S^T_m += K^T_{m,s} ZB_s         2 * DK/16 steps
+// O accumulates -O. Half of the Oq steps sit between Y and Z and the other
+// half between Z and Op, so the conversions YB = bf16(Y) and ZB = bf16(Z)
+// never wait for a product still in flight. Fragments are fetched `depth`
+// steps ahead into a rotating register buffer and scheduling fences keep that
+// order, so LDS latency hides behind the matrix products in between.
 template <int DK, bool WO> struct ChainSteps {
     static constexpr int NKB = DK / 32, NMT = DK / 16;
-    static constexpr int nZ = 4 * NKB, nOq = 0, nOp = WO ? 6 : 0, nS = 2 * NMT;
-    static constexpr int n = nZ + nOq + nOp + nS;
-    static constexpr int kind(int i) { return i < nZ ? 0 : i < nZ + nOq ? 1 : i < nZ + nOq + nOp ? 2 : 3; }
-    static constexpr int idx(int i) {
-        return kind(i) == 0 ? i : kind(i) == 1 ? i - nZ : kind(i) == 2 ? i - nZ - nOq : i - nZ - nOq - nOp;
-    }
-    static constexpr int opT(int j) { return j < 2 ? j : j < 4 ? 2 : 3; }
-    static constexpr int opS(int j) { return (j == 3 || j == 5) ? 1 : 0; }
-    // step at which Z is converted to the bf16 operand ZB
-    static constexpr int zb_at = nZ;
+    static constexpr int nY = 4 * NKB, nOq = WO ? 4 * NKB : 0, nZ = 6, nOp = WO ? 6 : 0, nS = 2 * NMT;
+    static constexpr int bOq1 = nY, bZ = bOq1 + nOq / 2, bOq2 = bZ + nZ, bOp = bOq2 + nOq - nOq / 2, bS = bOp + nOp;
+    static constexpr int n = bS + nS;
     static constexpr int depth = 8;
+    enum { kY, kOq, kZ, kOp, kS };
+    static constexpr int kind(int i) {
+        return i < bOq1 ? kY : i < bZ ? kOq : i < bOq2 ? kZ : i < bOp ? kOq : i < bS ? kOp : kS;
+    }
+    static constexpr int idx(int i) {
+        return i < bOq1 ? i
+               : i < bZ ? i - bOq1
+               : i < bOq2 ? i - bZ
+               : i < bOp ? i - bOq2 + nOq / 2
+               : i < bS ? i - bOp
+                        : i - bS;
+    }
+    // Z / Op step j -> token tile t and 32-token block s (pfrag(tT(j), tS(j)) == j)
+    static constexpr int tT(int j) { return j < 2 ? j : j < 4 ? 2 : 3; }
+    static constexpr int tS(int j) { return (j == 3 || j == 5) ? 1 : 0; }
+};
+
+template <int DK, bool WO> struct ChainSrc {
+    const __bf16 *K, *Q, *T, *P;
 };
 
 template <int DK, bool WO>
-__device__ inline bf16x8 chain_fetch(int i, const __bf16 *Wb, const __bf16 *Qb, const __bf16 *Pb, const __bf16 *Kb,
-                                     int g, int c16) {
+__device__ inline bf16x8 chain_fetch(int i, const ChainSrc<DK, WO> &src, int lane, int g, int c16) {
     using CS = ChainSteps<DK, WO>;
     const int k = CS::kind(i), j = CS::idx(i);
-    if (k == 0) return ld8(Wb + koff<DK>(16 * (j / CS::NKB) + c16, 32 * (j % CS::NKB) + 8 * g));
-    if (k == 1) return ld8(Qb + koff<DK>(16 * (j / CS::NKB) + c16, 32 * (j % CS::NKB) + 8 * g));
-    if (k == 2) return ld8(Pb + s64off(16 * CS::opT(j) + c16, 32 * CS::opS(j) + 8 * g));
-    return k_trfrag<DK>(Kb, j / 2, j % 2, g, c16);
+    if (k == CS::kY) return ld8(src.K + koff<DK>(16 * (j / CS::NKB) + c16, 32 * (j % CS::NKB) + 8 * g));
+    if (k == CS::kOq) return ld8(src.Q + koff<DK>(16 * (j / CS::NKB) + c16, 32 * (j % CS::NKB) + 8 * g));
+    if (k == CS::kZ) {
+        // T row 16t + c16 = column of T^T, over tokens 32s + {4g + e, 16 + 4g + e}
+        const int t = CS::tT(j), row = 32 * CS::tS(j) + 4 * g + (c16 >> 2), col = 16 * t + 4 * (c16 & 3);
+        return cat8(tr4(src.T + s64off(row, col)), tr4(src.T + s64off(row + 16, col)));
+    }
+    if (k == CS::kOp) return ld8(src.P + 512 * j + 8 * lane);
+    return k_trfrag<DK>(src.K, j / 2, j % 2, g, c16);
 }
 
+__device__ inline f32x4 widen4(bf16x4 v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
+
 template <int DK, bool WO>
-__device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)[DK / 16], const f32x4 (&Zacc)[4],
-                                      f32x4 (&O)[4], __bf16 *og, int64_t sv, int nval, int g, int c16) {
+__device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)[DK / 16], __bf16 *og, int64_t sv,
+                                      int nval, bool has_v, int cw, int lane, int g, int c16) {
     using CS = ChainSteps<DK, WO>;
     constexpr int D = CS::depth;
-    const __bf16 *Wb = bf.W(), *Kb = bf.K(r);
-    const __bf16 *Qb = WO ? bf.Q(r) : nullptr, *Pb = bf.P();
-    bf16x8 SB[CS::NKB], ZB[2], buf[D];
-    f32x4 Z[4];
+    const ChainSrc<DK, WO> src{bf.K(r), WO ? bf.Q(r) : nullptr, bf.Tt(r), WO ? bf.P(r) : nullptr};
+    bf16x8 SB[CS::NKB], YB[2], ZB[2], buf[D];
+    f32x4 Y[4], Z[4], O[4];
+    // V_t in the accumulator layout: lane (g, c) gets V[16t + 4g + e][16cw + c]
+    bf16x4 vf[4];
+    if (has_v) {
+        const __bf16 *Vb = bf.V(r);
 #pragma unroll
-    for (int i = 0; i < D; ++i) buf[i] = chain_fetch<DK, WO>(i, Wb, Qb, Pb, Kb, g, c16);
+        for (int s = 0; s < 2; ++s) {
+            const int row = 32 * s + 4 * g + (c16 >> 2), col = 16 * cw + 4 * (c16 & 3);
+            vf[2 * s] = tr4(Vb + s64off(row, col));
+            vf[2 * s + 1] = tr4(Vb + s64off(row + 16, col));
+        }
+    }
+    static_for<0, D>([&](auto ic) { buf[ic.value] = chain_fetch<DK, WO>(ic.value, src, lane, g, c16); });
     // SB_s slots = dk 32 s + 8 g + 0..7: tiles (2s, 2s+1) hold the low / high
     // half for even g and the other way round for odd g.
     const bool odd = g & 1;
 #pragma unroll
     for (int s = 0; s < CS::NKB; ++s) {
-        const bf16x4 lo = cvt4(Sacc[2 * s]), hi = cvt4(Sacc[2 * s + 1]);
+        const bf16x4 lo = cvt4(-Sacc[2 * s]), hi = cvt4(-Sacc[2 * s + 1]);
         SB[s] = odd ? cat8(hi, lo) : cat8(lo, hi);
     }
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) Z[t] = Zacc[t];
+    for (int t = 0; t < 4; ++t) {
+        Y[t] = has_v ? widen4(vf[t]) : zero;
+        Z[t] = zero;
+        O[t] = zero;
+    }
     fence();
-#pragma unroll
-    for (int i = 0; i < CS::n; ++i) {
+    static_for<0, CS::n>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
         const bf16x8 f = buf[i % D];
-        if (i + D < CS::n) buf[i % D] = chain_fetch<DK, WO>(i + D, Wb, Qb, Pb, Kb, g, c16);
-        if (i == CS::zb_at) {
+        if constexpr (i + D < CS::n) buf[i % D] = chain_fetch<DK, WO>(i + D, src, lane, g, c16);
+        if constexpr (i == CS::bZ) {
+            YB[0] = cvt8(Y[0], Y[1]);
+            YB[1] = cvt8(Y[2], Y[3]);
+        }
+        if constexpr (i == CS::bOp) {
             ZB[0] = cvt8(Z[0], Z[1]);
             ZB[1] = cvt8(Z[2], Z[3]);
         }
         fence();
-        const int k = CS::kind(i), j = CS::idx(i);
-        if (k == 0) Z[j / CS::NKB] = mfma32(f, SB[j % CS::NKB], Z[j / CS::NKB]);
-        if (k == 1) O[j / CS::NKB] = mfma32(SB[j % CS::NKB], f, O[j / CS::NKB]);
-        if (k == 2) O[CS::opT(j)] = mfma32(ZB[CS::opS(j)], f, O[CS::opT(j)]);
-        if (k == 3) Sacc[j / 2] = mfma32(f, ZB[j % 2], Sacc[j / 2]);
+        constexpr int k = CS::kind(i), j = CS::idx(i);
+        if constexpr (k == CS::kY) Y[j / CS::NKB] = mfma32(f, SB[j % CS::NKB], Y[j / CS::NKB]);
+        if constexpr (k == CS::kOq) O[j / CS::NKB] = mfma32(SB[j % CS::NKB], f, O[j / CS::NKB]);
+        if constexpr (k == CS::kZ) Z[CS::tT(j)] = mfma32(f, YB[CS::tS(j)], Z[CS::tT(j)]);
+        if constexpr (k == CS::kOp) O[CS::tT(j)] = mfma32(ZB[CS::tS(j)], f, O[CS::tT(j)]);
+        if constexpr (k == CS::kS) Sacc[j / 2] = mfma32(f, ZB[j % 2], Sacc[j / 2]);
         fence();
-    }
+    });
     if constexpr (WO) {
-        // O[t][i] = O[16t + c][row 4g + i] (rows relative to this wave's 16)
+        // O[t][i] = -O[16t + c][row 4g + i] (rows relative to this wave's 16)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int tok = 16 * t + c16;
-            if (tok < nval) st4(og + (int64_t)tok * sv, cvt4(O[t]));
+            if (tok < nval) st4(og + (int64_t)tok * sv, cvt4(-O[t]));
         }
-    }
-}
-
-// O_t = S Q_t^T for the 4 token tiles of chunk c with the state before chunk c
-// (16 products, Q row fragments fetched 8 ahead).
-template <int DK>
-__device__ inline void consumer_oq(const WsBufs<DK> &bf, int c, const f32x4 (&Sacc)[DK / 16], f32x4 (&O)[4], int g,
-                                   int c16) {
-    constexpr int NKB = DK / 32, n = 4 * NKB, D = 8;
-    const __bf16 *Qb = bf.Q(c);
-    bf16x8 SB[NKB], buf[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) buf[i] = ld8(Qb + koff<DK>(16 * (i / NKB) + c16, 32 * (i % NKB) + 8 * g));
-    const bool odd = g & 1;
-#pragma unroll
-    for (int s = 0; s < NKB; ++s) {
-        const bf16x4 lo = cvt4(Sacc[2 * s]), hi = cvt4(Sacc[2 * s + 1]);
-        SB[s] = odd ? cat8(hi, lo) : cat8(lo, hi);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    fence();
-#pragma unroll
-    for (int i = 0; i < n; ++i) {
-        const bf16x8 f = buf[i % D];
-        if (i + D < n) buf[i % D] = ld8(Qb + koff<DK>(16 * ((i + D) / NKB) + c16, 32 * ((i + D) % NKB) + 8 * g));
-        fence();
-        O[i / NKB] = mfma32(SB[i % NKB], f, O[i / NKB]);
-        fence();
     }
 }
 
 template <int DK, int DV, bool WO>
-__device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int cw, int g,
-                              int c16) {
+__device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int cw, int lane,
+                              int g, int c16) {
     constexpr int NMT = DK / 16;
     const bool has_v = WO || wk.has_v;
-    f32x4 Sacc[NMT], Zacc[4], O[4];
+    f32x4 Sacc[NMT];
     ws_state_in<DK>(Sacc, wk, cw, g, c16);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) Zacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t sv = (int64_t)a.H * DV;
     __bf16 *og = WO ? reinterpret_cast<__bf16 *>(a.o) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 + 16 * cw + 4 * g
                     : nullptr; // only dereferenced with output
-    const int kq = c16 >> 2, kr = c16 & 3; // transposing-read provider coordinates
 
     __syncthreads(); // matches the producers' prologue
     for (int r = -3; r < NC; ++r) {
-        // ---------------- phase 1: chain of chunk r
         if (r >= 0)
-            consumer_chain<DK, WO>(bf, r, Sacc, Zacc, O, WO ? og + (int64_t)r * kChunk * sv : nullptr, sv,
-                                   min(kChunk, wk.len - r * kChunk), g, c16);
-        __syncthreads();
-        // ---------------- phase 2: U of chunk r+1 (T^T and V of r+1 are in LDS)
-        if (r + 1 >= 0 && r + 1 < NC && has_v) {
-            const __bf16 *Tb = bf.Tt(r + 1), *Vb = bf.V();
-            bf16x8 vf[2], tf[6];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int row = 32 * s + 4 * g + kq;
-                vf[s] = cat8(tr4(Vb + s64off(row, 16 * cw + 4 * kr)), tr4(Vb + s64off(row + 16, 16 * cw + 4 * kr)));
-            }
-            int i = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int s = 0; s <= t / 2; ++s, ++i) {
-                    const int row = 32 * s + 4 * g + kq;
-                    tf[i] = cat8(tr4(Tb + s64off(row, 16 * t + 4 * kr)), tr4(Tb + s64off(row + 16, 16 * t + 4 * kr)));
-                }
-            i = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s <= t / 2; ++s, ++i) u = mfma32(tf[i], vf[s], u);
-                Zacc[t] = u; // U[16t + 4g + i][row c]
-            }
-        }
-        // Q S^T part of the output of chunk r+1 (Q of r+1 is in LDS, S is final for r+1)
-        if constexpr (WO) {
-            if (r + 1 >= 0 && r + 1 < NC) consumer_oq<DK>(bf, r + 1, Sacc, O, g, c16);
-        }
+            consumer_chain<DK, WO>(bf, r, Sacc, WO ? og + (int64_t)r * kChunk * sv : nullptr, sv,
+                                   min(kChunk, wk.len - r * kChunk), has_v, cw, lane, g, c16);
         __syncthreads();
     }
     ws_state_out<DK>(Sacc, wk, cw, g, c16);
 }
 
 // ---------------------------------------------------------------------------
-// Producers (waves 4-7). ROLE 0: diagonal Gram tiles and solve; 1:
-// off-diagonal Gram tiles and block substitution; 2, 3: P and W (halves).
+// Producers (waves 4-7). ROLE 0: diagonal Gram tiles and solve; 1: T and the
+// off-diagonal Gram tiles; 2, 3: P (halves).
 // ---------------------------------------------------------------------------
 
-// Row fragments of the four 16-row blocks of a K / Q buffer (slots = dk 32 kb + 8 g ..).
+// Row fragments of the four 16-row blocks of a K buffer (slots = dk 32 kb + 8 g ..).
 template <int DK> struct KRows {
     bf16x8 f[4][DK / 32];
 };
@@ -492,11 +521,11 @@ template <int DK> __device__ inline f32x4 dot_tile(const bf16x8 (&x)[DK / 32], c
     return acc;
 }
 
-// Wave 4, phase 2: the four diagonal Gram tiles G_bb of chunk c into the row
-// exchange buffer X (row 16b + j holds G_bb[j][0..15]; G_bb is symmetric).
+// Wave 4: the four diagonal Gram tiles G_bb of chunk c into X(c) (row 16b + j
+// holds G_bb[j][0..15]; G_bb is symmetric).
 template <int DK> __device__ inline void gram_diag(const WsBufs<DK> &bf, int c, int g, int c16) {
     using LY = WsLds<DK>;
-    float *X = bf.X();
+    float *X = bf.X(c);
     const __bf16 *Kb = bf.K(c);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -507,17 +536,18 @@ template <int DK> __device__ inline void gram_diag(const WsBufs<DK> &bf, int c, 
     }
 }
 
-// Wave 4, phase 1: lane group b solves diagonal block b of chunk c: lane
-// (b, j) computes column j of N_bb = (I + A_bb)^-1 from row j of G_bb; writes
-// N_bb^T (for wave 5) and the diagonal blocks of T^T.
+// Wave 4, after gram_diag on the same chunk: lane group b solves diagonal
+// block b: lane (b, j) computes column j of N_bb = (I + A_bb)^-1 from row j
+// of G_bb (its own row of X); writes N_bb^T (bf16, for wave 5's products)
+// and replaces its row of X with column j of T_bb = N_bb beta_j in fp32.
 template <int DK> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c, int g, int c16) {
     using LY = WsLds<DK>;
-    const float *X = bf.X();
+    float *Xr = bf.X(c) + (16 * g + c16) * LY::LX;
     const float br = bf.B(c)[16 * g + c16];
     float arow[16];
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
-        const f32x4 t = *reinterpret_cast<const f32x4 *>(X + (16 * g + c16) * LY::LX + 4 * j4);
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(Xr + 4 * j4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) arow[4 * j4 + e] = (4 * j4 + e < c16) ? t[e] * br : 0.f;
     }
@@ -525,21 +555,21 @@ template <int DK> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c,
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == c16) ? 1.f : 0.f;
     fwd_subst(x, arow);
-    // x[i] = N_gg[i][c]; N^T row 16g + c; T^T row 16g + c, columns 16g..16g+15
+    // x[i] = N_gg[i][c]
     __bf16 *Nr = bf.N(c) + (16 * g + c16) * LY::LN;
-    __bf16 *Tt = bf.Tt(c);
-    const int trow = 16 * g + c16;
     const f32x4 x0 = {x[0], x[1], x[2], x[3]}, x1 = {x[4], x[5], x[6], x[7]};
     const f32x4 x2 = {x[8], x[9], x[10], x[11]}, x3 = {x[12], x[13], x[14], x[15]};
     st8(Nr, cvt8(x0, x1));
     st8(Nr + 8, cvt8(x2, x3));
-    st8(Tt + s64off(trow, 16 * g), cvt8(x0 * br, x1 * br));
-    st8(Tt + s64off(trow, 16 * g + 8), cvt8(x2 * br, x3 * br));
+    *reinterpret_cast<f32x4 *>(Xr + 0) = x0 * br;
+    *reinterpret_cast<f32x4 *>(Xr + 4) = x1 * br;
+    *reinterpret_cast<f32x4 *>(Xr + 8) = x2 * br;
+    *reinterpret_cast<f32x4 *>(Xr + 12) = x3 * br;
 }
 
-// Wave 5, phase 2: off-diagonal Gram tiles of chunk c as bf16 k16 operands,
-// A_ac (a > c): lane (g, j) holds A[16a + j][16c + 4g .. +3]; stored per lane
-// in the order A10, A20, A21, A30, A31, A32.
+// Wave 5: off-diagonal Gram tiles of chunk c as bf16 k16 operands, A_ac
+// (a > c): lane (g, j) holds A[16a + j][16c + 4g .. +3]; stored per lane in
+// the order A10, A20, A21, A30, A31, A32.
 template <int DK> __device__ inline void off_gram(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
     KRows<DK> k;
     k_rows<DK>(k, bf.K(c), g, c16);
@@ -555,12 +585,13 @@ template <int DK> __device__ inline void off_gram(const WsBufs<DK> &bf, int c, i
     st4(As + 5 * 256, cvt4(dot_tile<DK>(k.f[2], k.f[3]) * b3));
 }
 
-// Wave 5, phase 1: N_ab = -N_aa sum_{c=b}^{a-1} A_ac N_cb for a > b, and
-// T_ab = N_ab diag(beta_b) into T^T (row 16b + j, columns 16a + 4g ..).
+// Wave 5: T^T of chunk c. Off-diagonal blocks N_ab = -N_aa sum_{c=b}^{a-1}
+// A_ac N_cb for a > b on the matrix cores, T_ab = N_ab diag(beta_b) into T^T
+// (row 16b + j, columns 16a + 4g ..); diagonal blocks T_bb from X(c).
 template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
     using LY = WsLds<DK>;
     const __bf16 *Ns = bf.N(c), *As = bf.A(c) + 4 * lane;
-    const float *Bs = bf.B(c);
+    const float *Bs = bf.B(c), *X = bf.X(c);
     __bf16 *Tt = bf.Tt(c);
     const bf16x4 A10 = ld4(As + 0 * 256), A20 = ld4(As + 1 * 256), A21 = ld4(As + 2 * 256);
     const bf16x4 A30 = ld4(As + 3 * 256), A31 = ld4(As + 4 * 256), A32 = ld4(As + 5 * 256);
@@ -574,10 +605,12 @@ template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, int c, 
     const bf16x4 r22 = tr4(Ns + (32 + 4 * g + kq) * LY::LN + 4 * kr);
     const bf16x4 r33 = tr4(Ns + (48 + 4 * g + kq) * LY::LN + 4 * kr);
     const float be0 = Bs[c16], be1 = Bs[16 + c16], be2 = Bs[32 + c16];
+    // T^T[16b + c16][16b + 4g + e] = T_bb[4g + e][c16], from row 16b + c16 of X
+    f32x4 td[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) td[b] = *reinterpret_cast<const f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g);
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    auto put = [&](int b, int a, f32x4 nab, float be) {
-        st4(Tt + s64off(16 * b + c16, 16 * a + 4 * g), cvt4(nab * be));
-    };
+    auto put = [&](int b, int a, f32x4 tab) { st4(Tt + s64off(16 * b + c16, 16 * a + 4 * g), cvt4(tab)); };
     // column block 0
     const f32x4 n10 = -mfma16(r11, cvt4(mfma16(A10, n00, z)), z);
     const bf16x4 f10 = cvt4(n10);
@@ -590,85 +623,44 @@ template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, int c, 
     const f32x4 n31 = -mfma16(r33, cvt4(mfma16(A32, f21, mfma16(A31, n11, z))), z);
     // column block 2
     const f32x4 n32 = -mfma16(r33, cvt4(mfma16(A32, n22, z)), z);
-    put(0, 1, n10, be0);
-    put(0, 2, n20, be0);
-    put(0, 3, n30, be0);
-    put(1, 2, n21, be1);
-    put(1, 3, n31, be1);
-    put(2, 3, n32, be2);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) put(b, b, td[b]);
+    put(0, 1, n10 * be0);
+    put(0, 2, n20 * be0);
+    put(0, 3, n30 * be0);
+    put(1, 2, n21 * be1);
+    put(1, 3, n31 * be1);
+    put(2, 3, n32 * be2);
 }
 
-// Waves 6-7, phase 2: W = T K for half of the dk tiles of chunk c, written as
-// -W. W tile mt uses the dk labels of state tile mt, so its K^T fragments are
-// the conflict-free transposing reads of the state update.
-template <int DK> __device__ inline void w_tiles(const WsBufs<DK> &bf, int c, int half, int g, int c16) {
-    constexpr int MT = DK / 32; // dk tiles per wave
-    const __bf16 *Kb = bf.K(c), *Tb = bf.Tt(c);
-    __bf16 *Wb = bf.W();
-    const int kq = c16 >> 2, kr = c16 & 3;
-    // T^T column fragments: lane (g, j) slots = tokens 32s + 16h + 4g + e of column 16nt + j
-    bf16x8 tf[4][2];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int s = 0; s <= nt / 2; ++s) {
-            const int row = 32 * s + 4 * g + kq;
-            tf[nt][s] = cat8(tr4(Tb + s64off(row, 16 * nt + 4 * kr)), tr4(Tb + s64off(row + 16, 16 * nt + 4 * kr)));
-        }
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm) {
-        const int mt = half * MT + mm;
-        bf16x8 kf[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) kf[s] = k_trfrag<DK>(Kb, mt, s, g, c16);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s <= nt / 2; ++s) acc = mfma32(kf[s], tf[nt][s], acc);
-            // acc[i] = W[16nt + c][delta(mt, g, i)]
-            st4(Wb + koff<DK>(16 * nt + c16, dk_of(mt, g)), cvt4(-acc));
-        }
-    }
-}
-
-// Waves 6-7: the score tiles of chunk c, wave 6 rows blocks {0, 3}, wave 7
-// blocks {1, 2}; computed in phase 1, written in phase 2.
+// Waves 6-7: the score tiles of chunk c, wave 6 row blocks {0, 3}, wave 7
+// blocks {1, 2}, written as -P operand fragments.
 __device__ constexpr int kPA[2][5] = {{0, 3, 3, 3, 3}, {1, 1, 2, 2, 2}};
 __device__ constexpr int kPC[2][5] = {{0, 0, 1, 2, 3}, {0, 1, 0, 1, 2}};
-struct PRegs {
-    bf16x4 p[5];
-};
-template <int DK> __device__ inline void p_compute(PRegs &R, const WsBufs<DK> &bf, int c, int half, int g, int c16) {
-    const __bf16 *Kb = bf.K(c), *Qb = bf.Q(c);
+template <int DK>
+__device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c, int half, int lane, int g, int c16) {
+    const __bf16 *Kb = bf.K(c);
+    __bf16 *Pb = bf.P(c) + 8 * lane;
     KRows<DK> k;
     k_rows<DK>(k, Kb, g, c16);
-    bf16x8 qf[2][DK / 32];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb)
-            qf[i][kb] = ld8(Qb + koff<DK>(16 * (half ? 1 + i : 3 * i) + c16, 32 * kb + 8 * g));
+    bf16x4 p[5];
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
         const int pa = kPA[half][i], pc = kPC[half][i];
         const int qi = half ? pa - 1 : (pa == 3 ? 1 : 0);
         // acc[e] = k_{16pc+4g+e} . q_{16pa+c} = P[16pa + c][16pc + 4g + e]
-        f32x4 acc = dot_tile<DK>(k.f[pc], qf[qi]);
+        f32x4 acc = dot_tile<DK>(k.f[pc], q.f[qi]);
         if (pa == pc) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e > c16) ? 0.f : acc[e];
         }
-        R.p[i] = cvt4(acc);
+        p[i] = cvt4(-acc);
     }
-}
-template <int DK> __device__ inline void p_write(const PRegs &R, const WsBufs<DK> &bf, int half, int g, int c16) {
-    __bf16 *Pb = bf.P();
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
         const int pa = kPA[half][i], pc = kPC[half][i];
-        // token 16pc + 4g + e sits at column 32 (pc / 2) + 8g + 4 (pc % 2) + e
-        st4(Pb + s64off(16 * pa + c16, 32 * (pc >> 1) + 8 * g + 4 * (pc & 1)), R.p[i]);
+        // token 16pc + 4g + e is slot 4 (pc % 2) + e of fragment (pa, pc / 2), lane 16g + c
+        st4(Pb + 512 * pfrag(pa, pc >> 1) + 4 * (pc & 1), p[i]);
     }
 }
 
@@ -677,65 +669,58 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
                               int c16) {
     const bool has_v = WO || wk.has_v;
     const int lane = 16 * g + c16;
-    // the solve waves are on the critical path: let their instructions issue
-    // ahead of the consumer sharing their SIMD
-    if constexpr (ROLE < 2) __builtin_amdgcn_s_setprio(2);
     WsStager<DK> st;
+    QStage<DK> q;
     {
         const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
         st.init(reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * sqk + (int64_t)wk.h * DK,
-                reinterpret_cast<const __bf16 *>(a.q) + wk.tok0 * sqk + (int64_t)wk.h * DK,
                 reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0,
                 reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h, sqk, sv, a.H, wk.len, pt);
+        if constexpr (WO && ROLE >= 2)
+            q.init(reinterpret_cast<const __bf16 *>(a.q) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len, ROLE - 2,
+                   g, c16);
     }
-    if (NC > 0) st.load_k(0); // K(0) is written in the first iteration
+    if (NC > 0) {
+        st.load_k(0); // K(0) is written in the first iteration
+        if (has_v) st.load_v(0);
+    }
     __syncthreads();
     if (NC == 0) { // no chunks: the same barriers as the consumers' three iterations
 #pragma unroll
-        for (int i = 0; i < 6; ++i) __syncthreads();
+        for (int i = 0; i < 3; ++i) __syncthreads();
         return;
     }
 
-    // Per iteration r (chunk indices; staging of chunk c happens before its
-    // first reader: K(c) in phase 1 of r = c-3, V(c) in phase 1 of c-1, Q(c)
-    // in phase 2 of c-2):
-    //   phase 1: diagonal solve (r+2) | off-diagonal solve (r+1) | P (r+1)
-    //   phase 2: diagonal Gram (r+3)  | off-diagonal Gram (r+3)  | W (r+1), P written
+    // Per iteration r: K(r+3) and beta(r+3) and V(r+1) into LDS from the
+    // registers loaded one iteration before, then
+    //   wave 4: Gram diagonal tiles and their inverses of chunk r+2
+    //   wave 5: T of chunk r+1, off-diagonal Gram tiles of chunk r+2
+    //   waves 6-7: Q of chunk r+1 into LDS, P of chunk r+1
     // Staging is unconditional (chunk indices clamped to the sequence): the
     // copies outside it land in ring slots that are never read, and
     // straight-line loads let every wait count only the loads it needs.
-    PRegs pr;
     const int last = NC - 1;
     for (int r = -3; r < NC; ++r) {
-        // ---------------- phase 1
-        st.write_k(bf.K(r + 3), bf.B(r + 3)); // K(r+3)
+        st.write_k(bf.K(r + 3), bf.B(r + 3));
         st.load_k(min(r + 4, last));
         if (has_v) {
-            st.write_v(bf.V());                   // V(r+1)
-            st.load_v(min(max(r + 2, 0), last)); // V(r+2)
+            st.write_v(bf.V(r + 1));
+            st.load_v(min(max(r + 2, 0), last));
         }
         if constexpr (ROLE == 0) {
-            if (r + 2 >= 0 && r + 2 < NC) diag_solve<DK>(bf, r + 2, g, c16);
+            if (r + 2 >= 0 && r + 2 < NC) {
+                gram_diag<DK>(bf, r + 2, g, c16);
+                diag_solve<DK>(bf, r + 2, g, c16);
+            }
         } else if constexpr (ROLE == 1) {
             if (r + 1 >= 0 && r + 1 < NC) off_solve<DK>(bf, r + 1, lane, g, c16);
+            if (r + 2 >= 0 && r + 2 < NC) off_gram<DK>(bf, r + 2, lane, g, c16);
         } else if constexpr (WO) {
-            if (r + 1 >= 0 && r + 1 < NC) p_compute<DK>(pr, bf, r + 1, ROLE - 2, g, c16);
-        }
-        __syncthreads();
-        // ---------------- phase 2
-        if constexpr (ROLE == 0) {
-            if (r + 3 < NC) gram_diag<DK>(bf, r + 3, g, c16);
-        } else if constexpr (ROLE == 1) {
-            if (r + 3 < NC) off_gram<DK>(bf, r + 3, lane, g, c16);
-        } else {
             if (r + 1 >= 0 && r + 1 < NC) {
-                w_tiles<DK>(bf, r + 1, ROLE - 2, g, c16);
-                if constexpr (WO) p_write<DK>(pr, bf, ROLE - 2, g, c16);
+                q.write(bf.Q(r + 1), g);
+                p_tiles<DK>(bf, q, r + 1, ROLE - 2, lane, g, c16);
             }
-        }
-        if (WO) {
-            st.write_q(bf.Q(r + 2)); // Q(r+2)
-            st.load_q(min(max(r + 3, 0), last));
+            q.load(min(max(r + 2, 0), last));
         }
         __syncthreads();
     }
@@ -753,18 +738,18 @@ __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a)
     const int NC = (wk.len + kChunk - 1) / kChunk;
     const WsBufs<DK> bf{smem};
 
-    // T^T and P: only their lower (P) / upper (T^T) blocks are ever written, so
-    // zero both rings once.
+    // T^T and P: only the blocks of T's lower triangle and P's lower-inclusive
+    // triangle are ever written, so zero both rings once.
     {
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 *zt = reinterpret_cast<f32x4 *>(smem + LY::oT);
-        constexpr int nvec = (int)((2 * LY::sz64 + LY::sz64) / 16); // T^T x2 and P are contiguous
+        constexpr int nvec = (int)((2 * LY::sz64 + 2 * LY::szP) / 16); // T^T x2 and P x2 are contiguous
         for (int i = tid; i < nvec; i += kWsThreads) zt[i] = zero;
     }
     __syncthreads();
 
     if (wave < 4) {
-        consumer_loop<DK, DV, WO>(a, wk, bf, NC, wave, g, c16);
+        consumer_loop<DK, DV, WO>(a, wk, bf, NC, wave, lane, g, c16);
     } else if (wave == 4) {
         producer_loop<DK, DV, WO, 0>(a, wk, bf, NC, tid - 256, g, c16);
     } else if (wave == 5) {
