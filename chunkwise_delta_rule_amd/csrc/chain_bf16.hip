@@ -16,15 +16,16 @@
 // Wave roles (two waves per SIMD; wave w and w+4 share a SIMD), iteration r:
 //   waves 0-3  consumers: each holds 16 rows of S in fp32 registers and runs
 //              Y, Z, O and the state update of chunk r
-//   wave 4     diagonal 16x16 Gram tiles of chunk r+2 and their inverses by
-//              forward substitution ("Solving for U": one column per lane,
-//              entries of A broadcast along the 16-lane row with DPP)
+//   wave 4     all Gram tiles of chunk r+2 from one set of K fragments, and
+//              the inverses of the diagonal 16x16 blocks by forward
+//              substitution ("Solving for U": one column per lane, entries of
+//              A broadcast along the 16-lane row with DPP)
 //   wave 5     T of chunk r+1 (off-diagonal blocks by block substitution on
-//              the matrix cores, diagonal blocks from wave 4's columns), then
-//              the off-diagonal Gram tiles of chunk r+2
+//              the matrix cores, diagonal blocks from wave 4's columns);
+//              stages V and beta from HBM
 //   waves 6-7  P of chunk r+1, half of the row blocks each; Q goes from HBM
-//              straight into their operand registers and on to the Q ring
-//   waves 4-7  also stage K, V and beta from HBM
+//              straight into their operand registers and on to the Q ring;
+//              stage K from HBM
 // One barrier per chunk; a buffer written in an iteration is read by nobody
 // in that iteration. LDS rings: K x4, Q x2, T^T x2, P x2, V x2, N x2, X x2,
 // off-diagonal operands x2, beta x4.
@@ -193,97 +194,122 @@ template <int DK> struct WsBufs {
     __device__ inline float *B(int c) const { return (float *)(base + LY::oB) + (c & 3) * 64; }
 };
 
-// Global -> register -> LDS staging of K, V and beta, shared by the 256
-// threads of waves 4-7 (pt = 0..255). Thread pt owns the same 16-byte column
-// piece of rows RPS * p + pt / KV (p = 0..NK-1) of every chunk, so its
-// addresses are a fixed per-thread pointer plus a per-chunk offset, and (RPS
-// being a multiple of 16) its swizzled LDS offsets are fixed too. A partial
-// last chunk re-reads its last valid row for the missing rows and writes
-// them as zeros.
-template <int DK> struct WsStager {
-    static constexpr int KV = DK / 8;        // 16-byte vectors per K row
-    static constexpr int NK = 64 * KV / 256; // K vectors per thread
-    static constexpr int RPS = 256 / KV;     // rows between a thread's K vectors
-    static constexpr int NV = 2;             // vectors per thread of the 64x64 V tile
-    static_assert(NK * 256 == 64 * KV && RPS % 16 == 0, "tiling");
-    const __bf16 *kt, *vt, *bg; // per-thread pointers into chunk 0
-    int64_t sqk, sv;
-    int H, len, pt, rk0, rv0; // first row of this thread's K and V vectors
-    int lk, lv;               // LDS element offsets of the first vector
-    bf16x8 rk[NK], rv[NV];
-    __bf16 rb;
-    int nk, nv;
+// Global -> register -> LDS staging. A partial last chunk re-reads its last
+// valid row for the missing rows and writes them as zeros. Two register sets
+// (chunk parity) keep two chunks in flight.
+__device__ inline int rows_of(int len, int c) { return min(kChunk, len - c * kChunk); }
 
-    __device__ inline void init(const __bf16 *kg, const __bf16 *vg, const __bf16 *bg_, int64_t sqk_, int64_t sv_,
-                                int H_, int len_, int pt_) {
+// K by the 128 threads of waves 6-7 (pt = 0..127): thread pt owns the 16-byte
+// column piece 8 (pt % KV) of rows pt / KV + RPS p, p = 0..NK-1.
+template <int DK> struct KStager {
+    static constexpr int KV = DK / 8, NT = 128;
+    static constexpr int NK = 64 * KV / NT, RPS = NT / KV;
+    static_assert(NK * NT == 64 * KV, "tiling");
+    const __bf16 *kt; // row rk0 of chunk 0, column col
+    int64_t sqk;
+    int len, rk0, col;
+    bf16x8 r[2][NK];
+    int n[2];
+    __device__ inline void init(const __bf16 *kg, int64_t sqk_, int len_, int pt) {
         sqk = sqk_;
-        sv = sv_;
-        H = H_;
         len = len_;
-        pt = pt_;
         rk0 = pt / KV;
-        rv0 = pt / 8;
-        kt = kg + rk0 * sqk + 8 * (pt % KV);
-        vt = vg + rv0 * sv + 8 * (pt % 8);
-        bg = bg_;
-        lk = koff<DK>(rk0, 8 * (pt % KV));
-        lv = s64off(rv0, 8 * (pt % 8));
-        nk = nv = 0;
+        col = 8 * (pt % KV);
+        kt = kg + rk0 * sqk + col;
+        n[0] = n[1] = 0;
     }
-    __device__ inline int rows_of(int c) const { return min(kChunk, len - c * kChunk); }
-    // rows STEP * p + r0 of chunk c from per-thread pointer t (row stride ld)
-    template <int N, int STEP>
-    __device__ static inline void fetch(bf16x8 (&r)[N], const __bf16 *t, int64_t ld, int c, int n, int r0) {
-        const __bf16 *b = t + (int64_t)c * kChunk * ld;
-        if (n == kChunk) {
+    template <int B> __device__ inline void load(int c) {
+        n[B] = rows_of(len, c);
+        const __bf16 *b = kt + (int64_t)c * kChunk * sqk;
+        if (n[B] == kChunk) {
 #pragma unroll
-            for (int p = 0; p < N; ++p) r[p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(STEP * p) * ld);
+            for (int p = 0; p < NK; ++p) r[B][p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(RPS * p) * sqk);
         } else {
 #pragma unroll
-            for (int p = 0; p < N; ++p) {
-                const int row = min(STEP * p + r0, n - 1);
-                r[p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(row - r0) * ld);
+            for (int p = 0; p < NK; ++p) {
+                const int row = min(rk0 + RPS * p, n[B] - 1);
+                r[B][p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(row - rk0) * sqk);
             }
         }
     }
-    template <int N, int STEP, int LD>
-    __device__ static inline void put(__bf16 *dst, const bf16x8 (&r)[N], int n, int r0) {
-        if (n == kChunk) {
+    template <int B> __device__ inline void write(__bf16 *Ks) const {
+        const bf16x8 z = {};
 #pragma unroll
-            for (int p = 0; p < N; ++p) st8(dst + STEP * p * LD, r[p]);
-        } else {
-            const bf16x8 z = {};
-#pragma unroll
-            for (int p = 0; p < N; ++p) st8(dst + STEP * p * LD, STEP * p + r0 < n ? r[p] : z);
+        for (int p = 0; p < NK; ++p) {
+            const int row = rk0 + RPS * p;
+            st8(Ks + koff<DK>(row, col), (n[B] == kChunk || row < n[B]) ? r[B][p] : z);
         }
     }
-    __device__ inline void load_k(int c) {
-        nk = rows_of(c);
-        fetch<NK, RPS>(rk, kt, sqk, c, nk, rk0);
-        if (pt < 64) rb = bg[((int64_t)c * kChunk + min(pt, nk - 1)) * H];
+};
+
+// V tile (64 x 64) and beta by the 64 lanes of wave 5: lane l owns the
+// 16-byte piece 8 (l % 8) of rows l / 8 + 8 p, p = 0..7, and beta of row l.
+struct VStager {
+    static constexpr int NV = 8;
+    const __bf16 *vt, *bt;
+    int64_t sv;
+    int H, len, lane, rv0, col;
+    bf16x8 r[2][NV];
+    __bf16 rb[2];
+    int n[2], nb[2];
+    __device__ inline void init(const __bf16 *vg, const __bf16 *bg, int64_t sv_, int H_, int len_, int lane_) {
+        sv = sv_;
+        H = H_;
+        len = len_;
+        lane = lane_;
+        rv0 = lane / 8;
+        col = 8 * (lane % 8);
+        vt = vg + rv0 * sv + col;
+        bt = bg;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            n[b] = nb[b] = 0;
+            rb[b] = (__bf16)0.f;
+#pragma unroll
+            for (int p = 0; p < NV; ++p) r[b][p] = bf16x8{};
+        }
     }
-    __device__ inline void load_v(int c) {
-        nv = rows_of(c);
-        fetch<NV, 32>(rv, vt, sv, c, nv, rv0);
+    template <int B> __device__ inline void load_v(int c) {
+        n[B] = rows_of(len, c);
+        const __bf16 *b = vt + (int64_t)c * kChunk * sv;
+        if (n[B] == kChunk) {
+#pragma unroll
+            for (int p = 0; p < NV; ++p) r[B][p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(8 * p) * sv);
+        } else {
+#pragma unroll
+            for (int p = 0; p < NV; ++p) {
+                const int row = min(rv0 + 8 * p, n[B] - 1);
+                r[B][p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(row - rv0) * sv);
+            }
+        }
     }
-    __device__ inline void write_k(__bf16 *Ks, float *Bs) const {
-        put<NK, RPS, DK>(Ks + lk, rk, nk, rk0);
-        if (pt < 64) Bs[pt] = pt < nk ? (float)rb : 0.f;
+    template <int B> __device__ inline void load_beta(int c) {
+        nb[B] = rows_of(len, c);
+        rb[B] = bt[((int64_t)c * kChunk + min(lane, nb[B] - 1)) * H];
     }
-    __device__ inline void write_v(__bf16 *Vs) const { put<NV, 32, 64>(Vs + lv, rv, nv, rv0); }
+    template <int B> __device__ inline void write_v(__bf16 *Vs) const {
+        const bf16x8 z = {};
+#pragma unroll
+        for (int p = 0; p < NV; ++p) {
+            const int row = rv0 + 8 * p;
+            st8(Vs + s64off(row, col), (n[B] == kChunk || row < n[B]) ? r[B][p] : z);
+        }
+    }
+    template <int B> __device__ inline void write_beta(float *Bs) const { Bs[lane] = lane < nb[B] ? (float)rb[B] : 0.f; }
 };
 
 // Waves 6-7: the Q rows of two 16-row blocks (wave 6: blocks 0 and 3, wave
 // 7: blocks 1 and 2) go from HBM straight into the row fragments of P's
 // products (lane (g, j): row 16 b + j, dk 32 kb + 8 g .. +7) and from there
 // into the Q ring for the consumers. Rows past the end of the sequence repeat
-// its last row; the outputs they feed are never stored.
+// its last row; the outputs they feed are never stored. Two register sets
+// (chunk parity) keep two chunks in flight.
 template <int DK> struct QStage {
     static constexpr int NKB = DK / 32;
     const __bf16 *qt[2]; // row[i] of chunk 0, dk 8 g
     int64_t sqk;
     int len, row[2];
-    bf16x8 f[2][NKB];
+    bf16x8 f[2][2][NKB]; // [set][block][kb]
     __device__ static constexpr int block(int half, int i) { return half ? 1 + i : 3 * i; }
     __device__ inline void init(const __bf16 *qg, int64_t sqk_, int len_, int half, int g, int c16) {
         sqk = sqk_;
@@ -294,21 +320,21 @@ template <int DK> struct QStage {
             qt[i] = qg + row[i] * sqk + 8 * g;
         }
     }
-    __device__ inline void load(int c) {
+    template <int B> __device__ inline void load(int c) {
         const int n = min(kChunk, len - c * kChunk);
         const int64_t off = (int64_t)c * kChunk * sqk;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const __bf16 *b = qt[i] + off + (int64_t)(min(row[i], n - 1) - row[i]) * sqk;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) f[i][kb] = *reinterpret_cast<const bf16x8 *>(b + 32 * kb);
+            for (int kb = 0; kb < NKB; ++kb) f[B][i][kb] = *reinterpret_cast<const bf16x8 *>(b + 32 * kb);
         }
     }
-    __device__ inline void write(__bf16 *Qs, int g) const {
+    template <int B> __device__ inline void write(__bf16 *Qs, int g) const {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) st8(Qs + koff<DK>(row[i], 32 * kb + 8 * g), f[i][kb]);
+            for (int kb = 0; kb < NKB; ++kb) st8(Qs + koff<DK>(row[i], 32 * kb + 8 * g), f[B][i][kb]);
     }
 };
 
@@ -507,9 +533,9 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
 template <int DK> struct KRows {
     bf16x8 f[4][DK / 32];
 };
-template <int DK> __device__ inline void k_rows(KRows<DK> &k, const __bf16 *Kb, int g, int c16) {
+template <int DK, int NB = 4> __device__ inline void k_rows(KRows<DK> &k, const __bf16 *Kb, int g, int c16) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) k.f[b][kb] = ld8(Kb + koff<DK>(16 * b + c16, 32 * kb + 8 * g));
 }
@@ -521,22 +547,33 @@ template <int DK> __device__ inline f32x4 dot_tile(const bf16x8 (&x)[DK / 32], c
     return acc;
 }
 
-// Wave 4: the four diagonal Gram tiles G_bb of chunk c into X(c) (row 16b + j
-// holds G_bb[j][0..15]; G_bb is symmetric).
-template <int DK> __device__ inline void gram_diag(const WsBufs<DK> &bf, int c, int g, int c16) {
+// Wave 4: the Gram tiles of chunk c from one set of K row fragments. The four
+// diagonal tiles G_bb go to X(c) (row 16b + j holds G_bb[j][0..15]; G_bb is
+// symmetric), then the off-diagonal tiles A_ac = diag(beta_a) G_ac (a > c)
+// go to A(c) as bf16 k16 operands: lane (g, j) holds A[16a + j][16c + 4g ..
+// +3], per lane in the order A10, A20, A21, A30, A31, A32. The off-diagonal
+// products cover the LDS round trip of X before the solve reads it back.
+template <int DK> __device__ inline void gram_tiles(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
     using LY = WsLds<DK>;
+    KRows<DK> k;
+    k_rows<DK>(k, bf.K(c), g, c16);
     float *X = bf.X(c);
-    const __bf16 *Kb = bf.K(c);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        bf16x8 kf[DK / 32];
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) kf[kb] = ld8(Kb + koff<DK>(16 * b + c16, 32 * kb + 8 * g));
-        *reinterpret_cast<f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g) = dot_tile<DK>(kf, kf);
-    }
+    for (int b = 0; b < 4; ++b)
+        *reinterpret_cast<f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g) = dot_tile<DK>(k.f[b], k.f[b]);
+    const float *Bs = bf.B(c);
+    const float b1 = Bs[16 + c16], b2 = Bs[32 + c16], b3 = Bs[48 + c16];
+    __bf16 *As = bf.A(c) + 4 * lane;
+    // dot_tile(K_c, K_a)[i] = k_{16c+4g+i} . k_{16a+j} = G[16a + j][16c + 4g + i]
+    st4(As + 0 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[1]) * b1));
+    st4(As + 1 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[2]) * b2));
+    st4(As + 2 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[2]) * b2));
+    st4(As + 3 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[3]) * b3));
+    st4(As + 4 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[3]) * b3));
+    st4(As + 5 * 256, cvt4(dot_tile<DK>(k.f[2], k.f[3]) * b3));
 }
 
-// Wave 4, after gram_diag on the same chunk: lane group b solves diagonal
+// Wave 4, after gram_tiles on the same chunk: lane group b solves diagonal
 // block b: lane (b, j) computes column j of N_bb = (I + A_bb)^-1 from row j
 // of G_bb (its own row of X); writes N_bb^T (bf16, for wave 5's products)
 // and replaces its row of X with column j of T_bb = N_bb beta_j in fp32.
@@ -565,24 +602,6 @@ template <int DK> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c,
     *reinterpret_cast<f32x4 *>(Xr + 4) = x1 * br;
     *reinterpret_cast<f32x4 *>(Xr + 8) = x2 * br;
     *reinterpret_cast<f32x4 *>(Xr + 12) = x3 * br;
-}
-
-// Wave 5: off-diagonal Gram tiles of chunk c as bf16 k16 operands, A_ac
-// (a > c): lane (g, j) holds A[16a + j][16c + 4g .. +3]; stored per lane in
-// the order A10, A20, A21, A30, A31, A32.
-template <int DK> __device__ inline void off_gram(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
-    KRows<DK> k;
-    k_rows<DK>(k, bf.K(c), g, c16);
-    const float *Bs = bf.B(c);
-    const float b1 = Bs[16 + c16], b2 = Bs[32 + c16], b3 = Bs[48 + c16];
-    __bf16 *As = bf.A(c) + 4 * lane;
-    // dot_tile(K_c, K_a)[i] = k_{16c+4g+i} . k_{16a+j} = G[16a + j][16c + 4g + i]
-    st4(As + 0 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[1]) * b1));
-    st4(As + 1 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[2]) * b2));
-    st4(As + 2 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[2]) * b2));
-    st4(As + 3 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[3]) * b3));
-    st4(As + 4 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[3]) * b3));
-    st4(As + 5 * 256, cvt4(dot_tile<DK>(k.f[2], k.f[3]) * b3));
 }
 
 // Wave 5: T^T of chunk c. Off-diagonal blocks N_ab = -N_aa sum_{c=b}^{a-1}
@@ -637,7 +656,7 @@ template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, int c, 
 // blocks {1, 2}, written as -P operand fragments.
 __device__ constexpr int kPA[2][5] = {{0, 3, 3, 3, 3}, {1, 1, 2, 2, 2}};
 __device__ constexpr int kPC[2][5] = {{0, 0, 1, 2, 3}, {0, 1, 0, 1, 2}};
-template <int DK>
+template <int DK, int B>
 __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c, int half, int lane, int g, int c16) {
     const __bf16 *Kb = bf.K(c);
     __bf16 *Pb = bf.P(c) + 8 * lane;
@@ -649,7 +668,7 @@ __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c,
         const int pa = kPA[half][i], pc = kPC[half][i];
         const int qi = half ? pa - 1 : (pa == 3 ? 1 : 0);
         // acc[e] = k_{16pc+4g+e} . q_{16pa+c} = P[16pa + c][16pc + 4g + e]
-        f32x4 acc = dot_tile<DK>(k.f[pc], q.f[qi]);
+        f32x4 acc = dot_tile<DK>(k.f[pc], q.f[B][qi]);
         if (pa == pc) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e > c16) ? 0.f : acc[e];
@@ -665,24 +684,32 @@ __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c,
 }
 
 template <int DK, int DV, bool WO, int ROLE>
-__device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int pt, int g,
-                              int c16) {
+__device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int g, int c16) {
     const bool has_v = WO || wk.has_v;
     const int lane = 16 * g + c16;
-    WsStager<DK> st;
+    const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
+    KStager<DK> ks;
+    VStager vs;
     QStage<DK> q;
-    {
-        const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
-        st.init(reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * sqk + (int64_t)wk.h * DK,
-                reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0,
-                reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h, sqk, sv, a.H, wk.len, pt);
-        if constexpr (WO && ROLE >= 2)
+    if constexpr (ROLE == 1)
+        vs.init(reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0,
+                reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h, sv, a.H, wk.len, lane);
+    if constexpr (ROLE >= 2) {
+        ks.init(reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len,
+                64 * (ROLE - 2) + lane);
+        if constexpr (WO)
             q.init(reinterpret_cast<const __bf16 *>(a.q) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len, ROLE - 2,
                    g, c16);
     }
-    if (NC > 0) {
-        st.load_k(0); // K(0) is written in the first iteration
-        if (has_v) st.load_v(0);
+    if (NC > 0) { // K(0), K(1), beta(0), beta(1) are written in the first two iterations
+        if constexpr (ROLE >= 2) {
+            ks.template load<0>(0);
+            ks.template load<1>(min(1, NC - 1));
+        }
+        if constexpr (ROLE == 1) {
+            vs.template load_beta<0>(0);
+            vs.template load_beta<1>(min(1, NC - 1));
+        }
     }
     __syncthreads();
     if (NC == 0) { // no chunks: the same barriers as the consumers' three iterations
@@ -691,38 +718,47 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
         return;
     }
 
-    // Per iteration r: K(r+3) and beta(r+3) and V(r+1) into LDS from the
-    // registers loaded one iteration before, then
-    //   wave 4: Gram diagonal tiles and their inverses of chunk r+2
-    //   wave 5: T of chunk r+1, off-diagonal Gram tiles of chunk r+2
-    //   waves 6-7: Q of chunk r+1 into LDS, P of chunk r+1
-    // Staging is unconditional (chunk indices clamped to the sequence): the
-    // copies outside it land in ring slots that are never read, and
-    // straight-line loads let every wait count only the loads it needs.
+    // Iteration r:
+    //   wave 4:    Gram tiles of chunk r+2, inverses of its diagonal blocks
+    //   wave 5:    V(r+1) and beta(r+3) into LDS; T of chunk r+1
+    //   waves 6-7: K(r+3) into LDS; Q and P of chunk r+1
+    // Every staging copy comes from registers loaded two iterations before
+    // (register set = chunk parity; R = r & 1 is a template argument, so the
+    // loop runs two iterations per trip) and is replaced by the loads of the
+    // chunk two further on. Staging is unconditional (chunk indices clamped
+    // to the sequence): copies outside it land in ring slots that are never
+    // read, and straight-line loads let every wait count only the loads it
+    // needs.
     const int last = NC - 1;
-    for (int r = -3; r < NC; ++r) {
-        st.write_k(bf.K(r + 3), bf.B(r + 3));
-        st.load_k(min(r + 4, last));
-        if (has_v) {
-            st.write_v(bf.V(r + 1));
-            st.load_v(min(max(r + 2, 0), last));
-        }
+    auto iteration = [&](int r, auto rpar) {
+        constexpr int S = 1 - decltype(rpar)::value; // set of chunks r+1, r+3, r+5
         if constexpr (ROLE == 0) {
             if (r + 2 >= 0 && r + 2 < NC) {
-                gram_diag<DK>(bf, r + 2, g, c16);
+                gram_tiles<DK>(bf, r + 2, lane, g, c16);
                 diag_solve<DK>(bf, r + 2, g, c16);
             }
         } else if constexpr (ROLE == 1) {
+            if (has_v) vs.template write_v<S>(bf.V(r + 1));
+            vs.template write_beta<S>(bf.B(r + 3));
+            if (has_v) vs.template load_v<S>(min(max(r + 3, 0), last));
+            vs.template load_beta<S>(min(r + 5, last));
             if (r + 1 >= 0 && r + 1 < NC) off_solve<DK>(bf, r + 1, lane, g, c16);
-            if (r + 2 >= 0 && r + 2 < NC) off_gram<DK>(bf, r + 2, lane, g, c16);
-        } else if constexpr (WO) {
-            if (r + 1 >= 0 && r + 1 < NC) {
-                q.write(bf.Q(r + 1), g);
-                p_tiles<DK>(bf, q, r + 1, ROLE - 2, lane, g, c16);
+        } else {
+            ks.template write<S>(bf.K(r + 3));
+            ks.template load<S>(min(r + 5, last));
+            if constexpr (WO) {
+                if (r + 1 >= 0 && r + 1 < NC) {
+                    q.template write<S>(bf.Q(r + 1), g);
+                    p_tiles<DK, S>(bf, q, r + 1, ROLE - 2, lane, g, c16);
+                }
             }
-            q.load(min(max(r + 2, 0), last));
+            if constexpr (WO) q.template load<S>(min(max(r + 3, 0), last));
         }
         __syncthreads();
+    };
+    for (int r = -3; r < NC; r += 2) { // r odd
+        iteration(r, Int<1>{});
+        if (r + 1 < NC) iteration(r + 1, Int<0>{});
     }
 }
 
@@ -751,13 +787,13 @@ __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a)
     if (wave < 4) {
         consumer_loop<DK, DV, WO>(a, wk, bf, NC, wave, lane, g, c16);
     } else if (wave == 4) {
-        producer_loop<DK, DV, WO, 0>(a, wk, bf, NC, tid - 256, g, c16);
+        producer_loop<DK, DV, WO, 0>(a, wk, bf, NC, g, c16);
     } else if (wave == 5) {
-        producer_loop<DK, DV, WO, 1>(a, wk, bf, NC, tid - 256, g, c16);
+        producer_loop<DK, DV, WO, 1>(a, wk, bf, NC, g, c16);
     } else if (wave == 6) {
-        producer_loop<DK, DV, WO, 2>(a, wk, bf, NC, tid - 256, g, c16);
+        producer_loop<DK, DV, WO, 2>(a, wk, bf, NC, g, c16);
     } else {
-        producer_loop<DK, DV, WO, 3>(a, wk, bf, NC, tid - 256, g, c16);
+        producer_loop<DK, DV, WO, 3>(a, wk, bf, NC, g, c16);
     }
 }
 
