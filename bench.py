@@ -35,7 +35,8 @@ PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 matrix-core peak
 PEAK_FP32_FLOPS = 157.3e12  # MI355X dense fp32 matrix-core peak
 PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chain_layer_b8_h16_t4096.json")
-KERNEL_SRC = os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc", "kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc", f)
+               for f in ("kernels.hip", "chain_bf16.hip", "dn_work.h")]
 
 
 def flops_per_head_token(C, dk, dv):
@@ -43,7 +44,12 @@ def flops_per_head_token(C, dk, dv):
 
 
 def kernel_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the device sources; the committed counter summary is used only
+    while it matches."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(w, esz, n_tokens, n_units, has_s0, has_sf):
@@ -228,7 +234,7 @@ def main():
     traffic = load_traffic(w.name, nbytes) if groups == 1 else None
     roofline = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_BPS / 1e9,
                 "unit": "GB/s", "frac": round(achieved_gbps * 1e9 / PEAK_HBM_BPS, 4),
-                "traffic": traffic, "kernel": "chain_kernel<bf16,128,128,out>"
+                "traffic": traffic, "kernel": "chain_kernel_ws<128,128,out>"
                 if w.dtype == "bf16" and w.dk == 128 and w.dv == 128 else "chain_kernel",
                 "algorithmic_bytes": nbytes, "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                 "mfma_tflops": round(flops / (avg_launch_ms / 1e3) / 1e12, 1),
