@@ -36,7 +36,7 @@ PEAK_FP32_FLOPS = 157.3e12  # MI355X dense fp32 matrix-core peak
 PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chain_layer_b8_h16_t4096.json")
 KERNEL_SRCS = [os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc", f)
-               for f in ("kernels.hip", "chain_bf16.hip", "dn_work.h")]
+               for f in ("chain_bf16.hip", "dn_work.h", "dn_internal.h")]
 
 
 def flops_per_head_token(C, dk, dv):
@@ -44,8 +44,8 @@ def flops_per_head_token(C, dk, dv):
 
 
 def kernel_sha():
-    """Hash of the device sources; the committed counter summary is used only
-    while it matches."""
+    """Hash of the sources of the dominant kernel (chain_kernel_ws); the
+    committed counter summary is used only while it matches."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
         h.update(open(path, "rb").read())

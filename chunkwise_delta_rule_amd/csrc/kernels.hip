@@ -18,11 +18,10 @@
 // shared K, Q, W), so each wave owns 16 state rows and runs E on its own;
 // only A-D are shared through LDS.
 //
-// Two kernels use these phases. chain_kernel_pc (bf16) has eight waves, two
-// per SIMD: four consumers run E of chunk r while four producers run A-C of
-// chunk r+1, so the VALU- and LDS-heavy preparation overlaps the matrix-core
-// chain. chain_kernel_serial (fp32, whose operands do not fit two chunks in
-// LDS) has four waves and runs A-E one after the other.
+// This file holds the fp32 path: chain_kernel_serial (four waves, A-E one
+// after the other; fp32 operands do not fit two chunks in LDS) and the
+// context-parallel prefix composition. The bf16 path, with specialised waves
+// and a different order of products, is chain_bf16.hip.
 //
 // Matrix-core layout facts used throughout (16x16 tiles, wave64, lane
 // l = 16*g + c with g = l/16, c = l%16):
@@ -701,316 +700,6 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
     state_out<DK>(Sacc, wk, w, g, c16);
 }
 
-// ---------------------------------------------------------------------------
-// Producer/consumer kernel (bf16): 8 waves, two per SIMD. Waves 0-3
-// (consumers) own 16 state rows each and run the chain of chunk r; waves 4-7
-// (producers) prepare chunk r+1 meanwhile: Gram tiles, each producer's own
-// diagonal 16x16 inverse (it holds that Gram tile, so no barrier is needed
-// before solving it), then the off-diagonal blocks. Consumers also compute
-// the masked scores P of chunk r+1, and all eight waves compute W of chunk
-// r+1 (one 16-wide dk tile each) while the consumers compute their U. With
-// two waves per SIMD, one wave's LDS waits and VALU-heavy solve overlap the
-// other's matrix products.
-//
-// Per iteration r (three barriers):
-//   I1  producers: Gram(r+1) -> A, own diagonal inverse -> N^T, T^T
-//       consumers: Z(r), O(r) (stored), P(r+1)
-//   I2  producers: off-diagonal blocks of N(r+1) -> T^T;  consumers: S += K^T Z (r)
-//   I3  all: W(r+1) -> LDS;  consumers: U(r+1) -> registers;  all: stage chunk r+2
-// LDS: K, Q, P, W (sharing space with A) and beta in two sets selected by
-// chunk parity; one V tile, one T^T, one N^T.
-// ---------------------------------------------------------------------------
-constexpr int kThreadsPC = 512;
-
-// Gram / score tiles (a, c), a >= c, split 3-3-2-2 over four waves; for the
-// producers the first tile of wave b is the diagonal tile (b, b).
-__device__ constexpr int kTileA[4][3] = {{0, 3, 3}, {1, 1, 3}, {2, 2, -1}, {3, 2, -1}};
-__device__ constexpr int kTileC[4][3] = {{0, 0, 1}, {1, 0, 2}, {2, 0, -1}, {3, 1, -1}};
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-// Row fragment for a product whose two operands both come from LDS: lane
-// group g takes the 8 consecutive k values 8g..8g+7 of a 32-deep block (any
-// order common to both operands is exact), one 16-byte read.
-__device__ inline bf16x8_t ldrow8(const __bf16 *Y, int ld, int row, int k0, int g) {
-    return *reinterpret_cast<const bf16x8_t *>(Y + row * ld + k0 + 8 * g);
-}
-
-template <int DK> struct SmemPC {
-    using L = Ld<__bf16, DK>;
-    static constexpr size_t szB = sizeof(float) * kChunk;
-    static constexpr size_t szSet = 2 * L::szK + L::szWA + L::szT + szB; // K, Q, W|A, P, beta
-    static constexpr size_t oSet = 0;
-    static constexpr size_t oK = 0, oQ = L::szK, oWA = 2 * L::szK, oP = oWA + L::szWA, oB = oP + L::szT;
-    static constexpr size_t oVs = 2 * szSet;
-    static constexpr size_t oTs = oVs + L::szV;
-    static constexpr size_t oNs = oTs + L::szT;
-    static constexpr size_t total = oNs + L::szN;
-};
-
-// One Gram (IS_P = false: A = beta_i k_i.k_j, j < i, fp32) or score
-// (IS_P = true: P = q_i.k_j, j <= i) tile (a, c): rows of block a, columns of
-// block c; tile = K_c X_a^T with X = K or Q.
-template <int DK, bool IS_P>
-__device__ inline void score_tile(int a, int c, const __bf16 *Ks, const __bf16 *X, const float *Bs, float *As,
-                                  __bf16 *Ps, int g, int c16) {
-    using L = Ld<__bf16, DK>;
-    constexpr int NKB = DK / 32;
-    bf16x8_t ka[NKB], xa[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        ka[kb] = ldrow8(Ks, L::K, 16 * c + c16, 32 * kb, g);
-        xa[kb] = ldrow8(X, L::K, 16 * a + c16, 32 * kb, g);
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], xa[kb], acc, 0, 0, 0);
-    // acc[e] = k_{16c+4g+e} . x_{16a+c16}
-    const int row = 16 * a + c16, col = 16 * c + 4 * g;
-    if constexpr (!IS_P) {
-        const float br = Bs[row];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = (col + e < row) ? acc[e] * br : 0.f;
-        *reinterpret_cast<f32x4 *>(As + row * L::A + col) = acc;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = (col + e > row) ? 0.f : acc[e];
-        stf(Ps + row * L::T + col, Tr<__bf16>::cvt(acc));
-    }
-}
-
-template <int DK, bool IS_P, int W>
-__device__ inline void score_tiles(const __bf16 *Ks, const __bf16 *X, const float *Bs, float *As, __bf16 *Ps, int g,
-                                   int c16) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-        if (kTileA[W][i] >= 0) score_tile<DK, IS_P>(kTileA[W][i], kTileC[W][i], Ks, X, Bs, As, Ps, g, c16);
-}
-
-// W tile m (16 dk columns) of W = T K for all 4 token blocks -> -W in LDS.
-template <int DK>
-__device__ inline void w_tile(int m, const __bf16 *Ks, const __bf16 *TsT, __bf16 *Ws, int g, int c16) {
-    using TR = Tr<__bf16>;
-    using F = TR::F;
-    using L = Ld<__bf16, DK>;
-    F kcol[4], trow[4][4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kcol[kk] = TR::ldcol(Ks, L::K, 16 * kk, 16 * m, g, c16);
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            if (kk <= (n | 1)) trow[n][kk] = TR::ldcol(TsT, L::T, 16 * kk, 16 * n, g, c16);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s <= n / 2; ++s)
-            acc = TR::mma32(acc, kcol[2 * s], kcol[2 * s + 1], trow[n][2 * s], trow[n][2 * s + 1]);
-        // acc[e] = W[16n + c16][16m + 4g + e]
-        stf(Ws + (16 * n + c16) * L::K + 16 * m + 4 * g, TR::cvt(-acc));
-    }
-}
-
-// U = T V for the value rows 16cw..16cw+15 into Zacc (U[16t + 4g + e][16cw + c16]).
-template <int DK>
-__device__ inline void u_tiles(int cw, const __bf16 *Vs, const __bf16 *TsT, f32x4 (&Zacc)[4], int g, int c16) {
-    using TR = Tr<__bf16>;
-    using F = TR::F;
-    using L = Ld<__bf16, DK>;
-    F vcol[4], trow[4][4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) vcol[kk] = TR::ldcol(Vs, L::V, 16 * kk, 16 * cw, g, c16);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            if (kk <= (t | 1)) trow[t][kk] = TR::ldcol(TsT, L::T, 16 * kk, 16 * t, g, c16);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s <= t / 2; ++s)
-            acc = TR::mma32(acc, trow[t][2 * s], trow[t][2 * s + 1], vcol[2 * s], vcol[2 * s + 1]);
-        Zacc[t] = acc;
-    }
-}
-
-// Producer wave b: Gram tiles of chunk (set) -> A, then the inverse of its
-// own diagonal block -> N^T, T^T; returns that block as a k16 B fragment.
-template <int DK, int B>
-__device__ inline Tr<__bf16>::F produce_gram_diag(const __bf16 *Ks, const float *Bs, float *As, __bf16 *NsT,
-                                                  __bf16 *TsT, int g, int c16) {
-    using PH = Phases<__bf16, DK>;
-    score_tiles<DK, false, B>(Ks, Ks, Bs, As, nullptr, g, c16);
-    typename PH::DiagFrags df;
-    PH::diag_fetch(df, As, Bs, B, c16); // this wave's own rows: LDS keeps one wave's accesses in order
-    return PH::diag_compute(df, NsT, TsT, B, g, c16);
-}
-
-template <int DK, int B>
-__device__ inline void produce_offdiag(Tr<__bf16>::F nfrag, const float *As, const __bf16 *NsT, const float *Bs,
-                                       __bf16 *TsT, int g, int c16) {
-    using PH = Phases<__bf16, DK>;
-    if constexpr (B < 3) {
-        typename PH::template OffFrags<B> f;
-        PH::template off_fetch<B>(f, As, NsT, Bs, g, c16);
-        PH::template off_compute<B>(f, nfrag, TsT, g, c16);
-    }
-}
-
-template <int DK, int DV, bool WRITE_O>
-__global__ __launch_bounds__(kThreadsPC) void chain_kernel_pc(const ChainArgs a) {
-    using E = __bf16;
-    using TR = Tr<E>;
-    using F = typename TR::F;
-    using PH = Phases<E, DK>;
-    using SM = SmemPC<DK>;
-    using L = Ld<E, DK>;
-    constexpr int NMT = DK / 16;
-    static_assert(SM::total <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SM::total];
-    auto KsAt = [&](int s) { return reinterpret_cast<E *>(smem + s * SM::szSet + SM::oK); };
-    auto QsAt = [&](int s) { return reinterpret_cast<E *>(smem + s * SM::szSet + SM::oQ); };
-    auto WsAt = [&](int s) { return reinterpret_cast<E *>(smem + s * SM::szSet + SM::oWA); };
-    auto AsAt = [&](int s) { return reinterpret_cast<float *>(smem + s * SM::szSet + SM::oWA); };
-    auto PsAt = [&](int s) { return reinterpret_cast<E *>(smem + s * SM::szSet + SM::oP); };
-    auto BsAt = [&](int s) { return reinterpret_cast<float *>(smem + s * SM::szSet + SM::oB); };
-    E *Vs = reinterpret_cast<E *>(smem + SM::oVs);
-    E *TsT = reinterpret_cast<E *>(smem + SM::oTs);
-    E *NsT = reinterpret_cast<E *>(smem + SM::oNs);
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    const bool consumer = wave < 4;
-    const int cw = wave & 3; // consumer: value-row slice; producer: diagonal block
-    const Work wk = decode_work<DK, DV>(a);
-    const bool has_v = WRITE_O || wk.has_v;
-    f32x4 Sacc[NMT];
-    state_in<DK>(Sacc, wk, cw, g, c16);
-    const int NC = (wk.len + kChunk - 1) / kChunk;
-    auto sg = make_stager<E, DK, DV, WRITE_O, kThreadsPC>(a, wk, tid);
-    const int64_t sv = (int64_t)a.H * DV;
-    E *og = WRITE_O ? reinterpret_cast<E *>(a.o) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 : nullptr;
-
-    // T and P are lower triangular and only their lower blocks are written:
-    // zero them once so the blocks above the diagonal stay zero.
-    for (int i = tid; i < kChunk * L::T; i += kThreadsPC) {
-        TsT[i] = TR::fromf(0.f);
-        PsAt(0)[i] = TR::fromf(0.f);
-        PsAt(1)[i] = TR::fromf(0.f);
-    }
-    f32x4 Zacc[4];
-    F nfrag = {};
-
-    // producer I1 / I2 work on chunk data in set s
-    auto produce_i1 = [&](int s) {
-        switch (cw) {
-        case 0: nfrag = produce_gram_diag<DK, 0>(KsAt(s), BsAt(s), AsAt(s), NsT, TsT, g, c16); break;
-        case 1: nfrag = produce_gram_diag<DK, 1>(KsAt(s), BsAt(s), AsAt(s), NsT, TsT, g, c16); break;
-        case 2: nfrag = produce_gram_diag<DK, 2>(KsAt(s), BsAt(s), AsAt(s), NsT, TsT, g, c16); break;
-        default: nfrag = produce_gram_diag<DK, 3>(KsAt(s), BsAt(s), AsAt(s), NsT, TsT, g, c16); break;
-        }
-    };
-    auto produce_i2 = [&](int s) {
-        switch (cw) {
-        case 0: produce_offdiag<DK, 0>(nfrag, AsAt(s), NsT, BsAt(s), TsT, g, c16); break;
-        case 1: produce_offdiag<DK, 1>(nfrag, AsAt(s), NsT, BsAt(s), TsT, g, c16); break;
-        case 2: produce_offdiag<DK, 2>(nfrag, AsAt(s), NsT, BsAt(s), TsT, g, c16); break;
-        default: break;
-        }
-    };
-    auto scores = [&](int s) {
-        if constexpr (WRITE_O) {
-            switch (cw) {
-            case 0: score_tiles<DK, true, 0>(KsAt(s), QsAt(s), nullptr, nullptr, PsAt(s), g, c16); break;
-            case 1: score_tiles<DK, true, 1>(KsAt(s), QsAt(s), nullptr, nullptr, PsAt(s), g, c16); break;
-            case 2: score_tiles<DK, true, 2>(KsAt(s), QsAt(s), nullptr, nullptr, PsAt(s), g, c16); break;
-            default: score_tiles<DK, true, 3>(KsAt(s), QsAt(s), nullptr, nullptr, PsAt(s), g, c16); break;
-            }
-        }
-    };
-    // I3 work: W tile(s) of this wave, and U for consumers
-    auto w_and_u = [&](int s) {
-        if (wave < NMT) w_tile<DK>(wave, KsAt(s), TsT, WsAt(s), g, c16);
-        if (consumer) {
-            if (has_v) u_tiles<DK>(cw, Vs, TsT, Zacc, g, c16);
-            else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) Zacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-    };
-
-    if (NC > 0) {
-        // prologue: stage chunk 0, prepare it, stage K/Q/beta of chunk 1
-        sg.load(0);
-        sg.store_kqb(KsAt(0), QsAt(0), BsAt(0));
-        sg.store_v(Vs);
-        __syncthreads();
-        sg.load(min(1, NC - 1));
-        if (consumer) scores(0);
-        else produce_i1(0);
-        __syncthreads();
-        if (!consumer) produce_i2(0);
-        __syncthreads();
-        w_and_u(0);
-        sg.store_kqb(KsAt(1), QsAt(1), BsAt(1));
-        __syncthreads();
-    }
-
-    // The preparation of chunk r+1 runs in every iteration, also the last
-    // one, where it works on a repeated copy of the last chunk and its results
-    // are never used; this keeps the barrier pattern uniform.
-    for (int r = 0; r < NC; ++r) {
-        const int cur = r & 1, nxt = cur ^ 1;
-        const int nval = min(kChunk, wk.len - r * kChunk);
-        // V of chunk r+1 (fetched one iteration ago) into the V tile, then fetch chunk r+2
-        sg.store_v(Vs);
-        sg.load(min(r + 2, NC - 1));
-
-        F ZB[4];
-        if (consumer) {
-            // I1 (consumers): Z and O of chunk r, scores of chunk r+1
-            F SB[NMT];
-#pragma unroll
-            for (int m = 0; m < NMT; ++m) SB[m] = TR::cvt(Sacc[m]);
-            {
-                typename PH::ZFrags f;
-                PH::z_fetch(f, WsAt(cur), g, c16);
-                PH::z_compute(f, SB, Zacc, ZB);
-            }
-            if constexpr (WRITE_O) {
-                typename PH::OFrags f;
-                PH::o_fetch(f, QsAt(cur), PsAt(cur), g, c16);
-                f32x4 Oacc[4];
-                PH::o_compute(f, SB, ZB, Oacc);
-                store_o(og, sv, r, nval, Oacc, cw, g, c16);
-            }
-            scores(nxt);
-        } else {
-            produce_i1(nxt);
-        }
-        __syncthreads();
-
-        // I2: S update of chunk r | off-diagonal blocks of chunk r+1
-        if (consumer) {
-            typename PH::SFrags f;
-            PH::s_fetch(f, KsAt(cur), g, c16);
-            PH::s_compute(f, ZB, Sacc);
-        } else {
-            produce_i2(nxt);
-        }
-        __syncthreads();
-
-        // I3: W and U of chunk r+1; stage K/Q/beta of chunk r+2 into this chunk's set
-        w_and_u(nxt);
-        sg.store_kqb(KsAt(cur), QsAt(cur), BsAt(cur));
-        __syncthreads();
-    }
-    if (consumer) state_out<DK>(Sacc, wk, cw, g, c16);
-}
-
 // Prefix composition of the group maps for one (b, h) and 16 state rows:
 //   S_{g+1} = S_g P_g + Q_g,  g = 0..G-2,  S_0 = S0 (or zero);
 // writes S_1..S_{G-1} to ws_S. fp32 throughout (fp32 matrix cores). Each
@@ -1059,27 +748,16 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(const ChainArgs a) {
     }
 }
 
-template <typename E, int DK, int DV, bool WO>
-hipError_t launch_one(const ChainArgs &a, hipStream_t s) {
+template <int DK, int DV, bool WO> hipError_t launch_one(const ChainArgs &a, hipStream_t s) {
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
-    if constexpr (sizeof(E) == 2)
-        hipLaunchKernelGGL((chain_kernel_pc<DK, DV, WO>), dim3(grid), dim3(kThreadsPC), 0, s, a);
-    else
-        hipLaunchKernelGGL((chain_kernel_serial<E, DK, DV, WO>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((chain_kernel_serial<float, DK, DV, WO>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename E, bool WO> hipError_t launch_dims(int dk, int dv, const ChainArgs &a, hipStream_t s) {
-    if constexpr (sizeof(E) == 2) {
-        if (dk == 128 && dv == 128) return launch_one<E, 128, 128, WO>(a, s);
-        if (dk == 128 && dv == 64) return launch_one<E, 128, 64, WO>(a, s);
-        if (dk == 64 && dv == 128) return launch_one<E, 64, 128, WO>(a, s);
-        if (dk == 64 && dv == 64) return launch_one<E, 64, 64, WO>(a, s);
-    } else {
-        if (dk == 64 && dv == 128) return launch_one<E, 64, 128, WO>(a, s);
-        if (dk == 64 && dv == 64) return launch_one<E, 64, 64, WO>(a, s);
-    }
+template <bool WO> hipError_t launch_dims_f32(int dk, int dv, const ChainArgs &a, hipStream_t s) {
+    if (dk == 64 && dv == 128) return launch_one<64, 128, WO>(a, s);
+    if (dk == 64 && dv == 64) return launch_one<64, 64, WO>(a, s);
     return hipErrorInvalidValue;
 }
 
@@ -1088,8 +766,7 @@ template <typename E, bool WO> hipError_t launch_dims(int dk, int dv, const Chai
 hipError_t launch_chain(int dtype, int dk, int dv, bool write_o, const ChainArgs &a,
                         hipStream_t stream) {
     if (dtype == 1) return launch_chain_bf16(dk, dv, write_o, a, stream);
-    return write_o ? launch_dims<float, true>(dk, dv, a, stream)
-                   : launch_dims<float, false>(dk, dv, a, stream);
+    return write_o ? launch_dims_f32<true>(dk, dv, a, stream) : launch_dims_f32<false>(dk, dv, a, stream);
 }
 
 hipError_t launch_compose(int dk, int dv, const ChainArgs &a, hipStream_t stream) {
