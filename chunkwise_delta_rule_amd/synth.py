@@ -16,6 +16,10 @@ size 2048 = 16 heads x 128):
 * v ~ N(0, 1), rounded to the input dtype.
 * beta = sigmoid(N(0, 1)) in fp32, rounded to the input dtype.
 * S0: zero, or N(0, std) in fp32 when requested.
+* g (Gated DeltaNet, log decay per token and head, always fp32):
+  g = log sigmoid(x), x ~ N(mu, 1) with mu = 2 by default, so a = exp(g)
+  has mean about 0.85 and a chunk of 64 tokens decays by about e^-10 end to
+  end; drawn from its own generator seeded with ``seed + 104729``.
 * varlen lengths: integers uniform on the inclusive range [lo, hi].
 
 Draw order: varlen lengths come from a CPU ``torch.Generator`` seeded with
@@ -109,6 +113,13 @@ def make_inputs(B: int, H: int, T: int, dk: int, dv: int, dtype: str = "bf16", s
     else:
         S0 = torch.zeros((B, H, dv, dk), device=device, dtype=torch.float32)
     return q, k, v, beta, S0
+
+
+def make_gates(shape, seed: int = 0, device: str = "cpu", mu: float = 2.0):
+    """Log decays g = log sigmoid(N(mu, 1)), fp32, of the given shape ([B,T,H] or [T,H])."""
+    g = _gen(device, seed + 104729)
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32) + mu
+    return torch.nn.functional.logsigmoid(x)
 
 
 def make_varlen_inputs(lengths, H: int, dk: int, dv: int, dtype: str = "bf16", seed: int = 0,

@@ -27,13 +27,19 @@ by Haoran Zhang, "p1" is "Context Parallelism for DeltaNet" by yywangcs):
 * ``cp_group_transition`` / ``cp_compose`` -- the affine map of a group of
   chunks and its composition (p3 "One chunk as an affine recurrence"; p1
   sections 2-3, context parallelism).
+* ``gated_deltanet_fwd`` / ``gated_deltanet_fwd_varlen`` -- the Gated
+  DeltaNet definition: p3 "Gated DeltaNet (GDN)" token recurrence, in C
+  (the decay a_t = exp(g_t) multiplies the previous state before the
+  correction); ``gated_chunked_fwd`` -- that section's "Complete per-chunk
+  algorithm"; ``householder_states``, ``exact_states`` and
+  ``cp_group_transition`` take the decays as an optional argument.
 
 Convention (p1 section 2): the state S is dv x dk and acts on column vectors:
 S_t = S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t. The
 formulas of p3, written for a dk x dv state acting on row vectors, map onto it
 by transposing S.
 
-Layouts: q, k [B, T, H, dk]; v, o [B, T, H, dv]; beta [B, T, H];
+Layouts: q, k [B, T, H, dk]; v, o [B, T, H, dv]; beta, g [B, T, H];
 S0, S_final [B, H, dv, dk]. Every function takes and returns float64 numpy
 arrays (exact_states works on ``fractions.Fraction``).
 
@@ -61,7 +67,7 @@ _lib = None
 def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
     """Compile the C oracle with gcc (fp64, OpenMP, no fast-math)."""
     if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", src, "-o", out]
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", src, "-o", out, "-lm"]
         subprocess.run(cmd, check=True)
     return out
 
@@ -83,6 +89,15 @@ def load(path: str = _LIB_PATH):
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int]
     lib.oracle_deltanet_fwd_varlen.restype = ctypes.c_int
+    lib.oracle_gated_deltanet_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int]
+    lib.oracle_gated_deltanet_fwd.restype = ctypes.c_int
+    lib.oracle_gated_deltanet_fwd_varlen.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                                     ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+                                                     ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                     ctypes.c_int]
+    lib.oracle_gated_deltanet_fwd_varlen.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     if path == _LIB_PATH:
@@ -157,6 +172,56 @@ def deltanet_fwd_varlen(q, k, v, beta, cu_seqlens, S0=None, nthreads: int = 0, l
     return o, Sf
 
 
+def gated_deltanet_fwd(q, k, v, beta, g, S0=None, nthreads: int = 0, lib=None):
+    """Token-serial fp64 Gated DeltaNet forward. Returns (o, S_final).
+
+    p3 "Gated DeltaNet (GDN)", token recurrence (transposed state):
+    S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t,
+    with a_t = exp(g_t); g has the layout of beta, [B, T, H].
+    """
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    assert q.shape == k.shape and v.shape[:3] == (B, T, H)
+    assert beta.shape == (B, T, H) and g.shape == (B, T, H)
+    S0 = None if S0 is None else _f64(S0)
+    if S0 is not None:
+        assert S0.shape == (B, H, dv, dk)
+    o = np.empty((B, T, H, dv))
+    Sf = np.empty((B, H, dv, dk))
+    lib = lib or load()
+    rc = lib.oracle_gated_deltanet_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0),
+                                       _ptr(o), _ptr(Sf), B, H, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gated_deltanet_fwd failed with {rc}")
+    return o, Sf
+
+
+def gated_deltanet_fwd_varlen(q, k, v, beta, g, cu_seqlens, S0=None, nthreads: int = 0,
+                              lib=None):
+    """Token-serial fp64 Gated DeltaNet over packed sequences (g: [T, H])."""
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    if k.ndim == 4:
+        q, k, v, beta, g = q[0], k[0], v[0], beta[0], g[0]
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    assert g.shape == (T, H)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    N = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == T
+    S0 = None if S0 is None else _f64(S0)
+    o = np.empty((T, H, dv))
+    Sf = np.empty((N, H, dv, dk))
+    lib = lib or load()
+    rc = lib.oracle_gated_deltanet_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                              _ptr(S0), _ptr(o), _ptr(Sf),
+                                              cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                              N, H, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gated_deltanet_fwd_varlen failed with {rc}")
+    return o, Sf
+
+
 # ---------------------------------------------------------------------------
 # Chunked form (numpy, fp64): p3 "Complete per-chunk algorithm"
 # ---------------------------------------------------------------------------
@@ -222,6 +287,61 @@ def chunked_fwd(q, k, v, beta, S0=None, chunk: int = 64):
     return o, Sf
 
 
+def gated_chunked_unit(q, k, v, beta, a, S, C):
+    """One unit of Gated DeltaNet, chunk size C, the last chunk may be partial.
+
+    p3 "Gated DeltaNet (GDN)" > "Complete per-chunk algorithm", in the page's
+    order and notation, with the state transposed. Within a chunk (1-based
+    positions l, i):
+        lambda[i:j] = a_i a_{i+1} ... a_j  (1 when i > j)
+        Gamma[l, i] = lambda[i+1:l] for i <= l, else 0
+        <-q_l = lambda[1:l] q_l,  <-k_l = lambda[1:l] k_l,  ->k_l = lambda[l+1:C] k_l
+        L = (K K^T . Gamma) strictly lower,  (I + B L) T = B
+        U = T V,  <-W = T <-K,  Z = U - <-W S^T
+        O = <-Q S^T + (Q K^T . Gamma) Z,  S <- lambda[1:C] S + Z^T ->K
+    a: [L] decays (not logarithms). C of a partial last chunk is its length.
+    """
+    Ltot = k.shape[0]
+    o = np.zeros((Ltot, v.shape[1]))
+    S = np.array(S, dtype=np.float64, copy=True)
+    for c0 in range(0, Ltot, C):
+        Kr, Qr, Vr, br, ar = k[c0:c0 + C], q[c0:c0 + C], v[c0:c0 + C], beta[c0:c0 + C], a[c0:c0 + C]
+        n = Kr.shape[0]
+
+        def lam(i, j):  # 1-based inclusive product a_i ... a_j
+            return float(np.prod(ar[i - 1:j])) if i <= j else 1.0
+
+        Gam = np.zeros((n, n))
+        for l in range(1, n + 1):
+            for i in range(1, l + 1):
+                Gam[l - 1, i - 1] = lam(i + 1, l)
+        left = np.array([lam(1, l) for l in range(1, n + 1)])
+        right = np.array([lam(l + 1, n) for l in range(1, n + 1)])
+        Lr = np.tril(Kr @ Kr.T * Gam, -1)
+        T = forward_substitution_T(Lr, br)
+        U = T @ Vr
+        W_left = T @ (left[:, None] * Kr)
+        Z = U - W_left @ S.T
+        o[c0:c0 + C] = (left[:, None] * Qr) @ S.T + (Qr @ Kr.T * Gam) @ Z
+        S = lam(1, n) * S + Z.T @ (right[:, None] * Kr)
+    return o, S
+
+
+def gated_chunked_fwd(q, k, v, beta, g, S0=None, chunk: int = 64):
+    """Chunked fp64 Gated DeltaNet over [B,T,H,*] inputs (g = log a). Returns (o, S_final)."""
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    Sf = np.zeros((B, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dv, dk)) if S0 is None else _f64(S0)[b, h]
+            o[b, :, h], Sf[b, h] = gated_chunked_unit(q[b, :, h], k[b, :, h], v[b, :, h],
+                                                      beta[b, :, h], np.exp(g[b, :, h]), S, chunk)
+    return o, Sf
+
+
 # ---------------------------------------------------------------------------
 # Full-sequence triangular system (zero initial state)
 # ---------------------------------------------------------------------------
@@ -258,18 +378,20 @@ def full_sequence_fwd(q, k, v, beta):
 # Explicit transition products (brute force)
 # ---------------------------------------------------------------------------
 
-def householder_states(k, v, beta, S0):
+def householder_states(k, v, beta, S0, a=None):
     """All states S_1..S_L of one unit from explicit d x d transition products.
 
     p3 "One chunk as an affine recurrence": each token applies the affine map
     S -> S A_t + X_t with A_t = I - beta_t k_t k_t^T and X_t = beta_t v_t k_t^T
     (state transposed). Unrolled:
         S_t = S0 A_1 ... A_t + sum_{i<=t} X_i A_{i+1} ... A_t.
+    With decays a (p3 "Gated DeltaNet (GDN)"), A_t = a_t (I - beta_t k_t k_t^T).
     Each S_t is rebuilt from scratch from these products (O(t^2) matrix
     products per state), so no state is carried from one t to the next.
     """
     L, dk = k.shape
-    A = [np.eye(dk) - beta[t] * np.outer(k[t], k[t]) for t in range(L)]
+    av = np.ones(L) if a is None else np.asarray(a, dtype=np.float64)
+    A = [av[t] * (np.eye(dk) - beta[t] * np.outer(k[t], k[t])) for t in range(L)]
     X = [beta[t] * np.outer(v[t], k[t]) for t in range(L)]
     states = []
     for t in range(L):
@@ -286,9 +408,9 @@ def householder_states(k, v, beta, S0):
     return states
 
 
-def householder_unit(q, k, v, beta, S0):
+def householder_unit(q, k, v, beta, S0, a=None):
     """(o, S_final) of one unit from ``householder_states``; o_t = S_t q_t."""
-    states = householder_states(k, v, beta, S0)
+    states = householder_states(k, v, beta, S0, a)
     o = np.stack([states[t] @ q[t] for t in range(len(states))]) if states else \
         np.zeros((0, v.shape[1]))
     return o, (states[-1] if states else np.array(S0, dtype=np.float64))
@@ -308,13 +430,15 @@ def _fadd(A, Bm):
     return [[a + b for a, b in zip(ra, rb)] for ra, rb in zip(A, Bm)]
 
 
-def exact_states(k, v, beta, S0):
+def exact_states(k, v, beta, S0, a=None):
     """``householder_states`` in exact rational arithmetic (fractions.Fraction).
 
     k: L lists of dk Fractions; v: L lists of dv; beta: L Fractions;
-    S0: dv x dk nested lists. Returns the list of exact states S_1..S_L.
+    S0: dv x dk nested lists; a: L Fractions (decays) or None.
+    Returns the list of exact states S_1..S_L.
     """
     L, dk = len(k), len(k[0])
+    av = [Fraction(1)] * L if a is None else list(a)
     dv = len(v[0])
     A, X = [], []
     for t in range(L):
@@ -322,7 +446,7 @@ def exact_states(k, v, beta, S0):
         Xt = _fmat(dv, dk)
         for i in range(dk):
             for j in range(dk):
-                At[i][j] = (Fraction(1) if i == j else Fraction(0)) - beta[t] * k[t][i] * k[t][j]
+                At[i][j] = av[t] * ((Fraction(1) if i == j else Fraction(0)) - beta[t] * k[t][i] * k[t][j])
         for i in range(dv):
             for j in range(dk):
                 Xt[i][j] = beta[t] * v[t][i] * k[t][j]
@@ -348,7 +472,7 @@ def exact_states(k, v, beta, S0):
 # Context parallelism: affine group transitions and their composition
 # ---------------------------------------------------------------------------
 
-def cp_group_transition(k, v, beta):
+def cp_group_transition(k, v, beta, a=None):
     """Affine map of a token range of one unit: S_end = S_start P + Q.
 
     P = A_1 A_2 ... A_L (ordered products of the transitions, dk x dk) and
@@ -356,14 +480,16 @@ def cp_group_transition(k, v, beta):
     Both are built as explicit d x d matrix products, composing the per-token
     affine maps (A_t, X_t) one after another: (P, Q) <- (P A_t, Q A_t + X_t)
     (p3 "One chunk as an affine recurrence"; p1 section 3 splits the chunk
-    chain into groups that are processed independently).
+    chain into groups that are processed independently). With decays a,
+    A_t = a_t (I - beta_t k_t k_t^T) (p3 "Gated DeltaNet (GDN)").
     """
     L, dk = k.shape
     dv = v.shape[1]
+    av = np.ones(L) if a is None else np.asarray(a, dtype=np.float64)
     P = np.eye(dk)
     Q = np.zeros((dv, dk))
     for t in range(L):
-        At = np.eye(dk) - beta[t] * np.outer(k[t], k[t])
+        At = av[t] * (np.eye(dk) - beta[t] * np.outer(k[t], k[t]))
         P = P @ At
         Q = Q @ At + beta[t] * np.outer(v[t], k[t])
     return P, Q

@@ -17,8 +17,16 @@
  *   (yywangcs), section 2, chunk-state update equation. The rank-one form equals
  *   S_t = S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
  *
+ * Gated DeltaNet (same page, section "Gated DeltaNet (GDN)", token recurrence
+ * in the first display): the previous state is first multiplied by the
+ * token's scalar decay a_t, then corrected as above:
+ *       S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *   i.e. Sd = a_t S_{t-1}; vhat_t = Sd k_t; S_t = Sd + beta_t (v_t - vhat_t) k_t^T.
+ *   The decay is passed as its natural logarithm g_t (a_t = exp(g_t), in
+ *   fp64 here); a NULL gate array means a_t = 1 (plain DeltaNet).
+ *
  * Layouts (all fp64, row-major, contiguous):
- *   q, k : [B, T, H, dk]     v, o : [B, T, H, dv]     beta : [B, T, H]
+ *   q, k : [B, T, H, dk]     v, o : [B, T, H, dv]     beta, g : [B, T, H]
  *   S0, S_final : [B, H, dv, dk]   (S0 may be NULL: zero initial state)
  * Varlen: B = 1, T = cu_seqlens[N]; sequence n owns tokens
  *   [cu_seqlens[n], cu_seqlens[n+1]); S0/S_final are [N, H, dv, dk]; the state
@@ -31,14 +39,16 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <math.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
 
 /* One (sequence, head) unit. Row r of q/k lives at q + r*qk_stride, of v/o at
- * v + r*vo_stride, beta_r at beta[r*beta_stride]. S is dv x dk, updated in place. */
+ * v + r*vo_stride, beta_r at beta[r*beta_stride] and g_r (log decay, or NULL)
+ * at g[r*beta_stride]. S is dv x dk, updated in place. */
 static void unit_forward(const double *q, const double *k, const double *v,
-                         const double *beta, double *o, ptrdiff_t qk_stride,
+                         const double *beta, const double *g, double *o, ptrdiff_t qk_stride,
                          ptrdiff_t vo_stride, ptrdiff_t beta_stride, int64_t L,
                          int dk, int dv, double *S, double *vhat)
 {
@@ -47,6 +57,11 @@ static void unit_forward(const double *q, const double *k, const double *v,
         const double *qt = q + t * qk_stride;
         const double *vt = v + t * vo_stride;
         const double bt = beta[t * beta_stride];
+        /* decay of the previous state: S <- a_t S */
+        if (g) {
+            const double at = exp(g[t * beta_stride]);
+            for (size_t e = 0; e < (size_t)dv * dk; ++e) S[e] *= at;
+        }
         /* prediction: vhat = S k_t */
         for (int i = 0; i < dv; ++i) {
             const double *Si = S + (size_t)i * dk;
@@ -74,7 +89,7 @@ static void unit_forward(const double *q, const double *k, const double *v,
 }
 
 static int run_units(const double *q, const double *k, const double *v,
-                     const double *beta, const double *S0, double *o,
+                     const double *beta, const double *g, const double *S0, double *o,
                      double *S_final, int64_t n_units, int H, int dk, int dv,
                      const int64_t *starts, const int64_t *lens, int nthreads)
 {
@@ -106,6 +121,7 @@ static int run_units(const double *q, const double *k, const double *v,
                              k + t0 * qk_stride + (ptrdiff_t)h * dk,
                              v + t0 * vo_stride + (ptrdiff_t)h * dv,
                              beta + t0 * H + h,
+                             g ? g + t0 * H + h : NULL,
                              o ? o + t0 * vo_stride + (ptrdiff_t)h * dv : NULL,
                              qk_stride, vo_stride, H, lens[seq], dk, dv, S, vhat);
                 if (S_final) memcpy(S_final + (size_t)u * sz, S, sizeof(double) * sz);
@@ -116,10 +132,10 @@ static int run_units(const double *q, const double *k, const double *v,
     return failed ? -2 : 0;
 }
 
-int oracle_deltanet_fwd(const double *q, const double *k, const double *v,
-                        const double *beta, const double *S0, double *o,
-                        double *S_final, int B, int H, int64_t T, int dk, int dv,
-                        int nthreads)
+static int dense_fwd(const double *q, const double *k, const double *v,
+                     const double *beta, const double *g, const double *S0, double *o,
+                     double *S_final, int B, int H, int64_t T, int dk, int dv,
+                     int nthreads)
 {
     if (!q || !k || !v || !beta || B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
         return -1;
@@ -127,16 +143,16 @@ int oracle_deltanet_fwd(const double *q, const double *k, const double *v,
     if (!starts) return -2;
     int64_t *lens = starts + B;
     for (int b = 0; b < B; ++b) { starts[b] = (int64_t)b * T; lens[b] = T; }
-    int rc = run_units(q, k, v, beta, S0, o, S_final, (int64_t)B * H, H, dk, dv,
+    int rc = run_units(q, k, v, beta, g, S0, o, S_final, (int64_t)B * H, H, dk, dv,
                        starts, lens, nthreads);
     free(starts);
     return rc;
 }
 
-int oracle_deltanet_fwd_varlen(const double *q, const double *k, const double *v,
-                               const double *beta, const double *S0, double *o,
-                               double *S_final, const int64_t *cu_seqlens, int N,
-                               int H, int dk, int dv, int nthreads)
+static int varlen_fwd(const double *q, const double *k, const double *v,
+                      const double *beta, const double *g, const double *S0, double *o,
+                      double *S_final, const int64_t *cu_seqlens, int N,
+                      int H, int dk, int dv, int nthreads)
 {
     if (!q || !k || !v || !beta || !cu_seqlens || N <= 0 || H <= 0 || dk <= 0 || dv <= 0)
         return -1;
@@ -149,10 +165,46 @@ int oracle_deltanet_fwd_varlen(const double *q, const double *k, const double *v
         starts[n] = cu_seqlens[n];
         lens[n] = cu_seqlens[n + 1] - cu_seqlens[n];
     }
-    int rc = run_units(q, k, v, beta, S0, o, S_final, (int64_t)N * H, H, dk, dv,
+    int rc = run_units(q, k, v, beta, g, S0, o, S_final, (int64_t)N * H, H, dk, dv,
                        starts, lens, nthreads);
     free(starts);
     return rc;
+}
+
+/* DeltaNet (no decay). */
+int oracle_deltanet_fwd(const double *q, const double *k, const double *v,
+                        const double *beta, const double *S0, double *o,
+                        double *S_final, int B, int H, int64_t T, int dk, int dv,
+                        int nthreads)
+{
+    return dense_fwd(q, k, v, beta, NULL, S0, o, S_final, B, H, T, dk, dv, nthreads);
+}
+
+int oracle_deltanet_fwd_varlen(const double *q, const double *k, const double *v,
+                               const double *beta, const double *S0, double *o,
+                               double *S_final, const int64_t *cu_seqlens, int N,
+                               int H, int dk, int dv, int nthreads)
+{
+    return varlen_fwd(q, k, v, beta, NULL, S0, o, S_final, cu_seqlens, N, H, dk, dv, nthreads);
+}
+
+/* Gated DeltaNet: g holds log a_t, same layout as beta (required). */
+int oracle_gated_deltanet_fwd(const double *q, const double *k, const double *v,
+                              const double *beta, const double *g, const double *S0,
+                              double *o, double *S_final, int B, int H, int64_t T, int dk,
+                              int dv, int nthreads)
+{
+    if (!g) return -1;
+    return dense_fwd(q, k, v, beta, g, S0, o, S_final, B, H, T, dk, dv, nthreads);
+}
+
+int oracle_gated_deltanet_fwd_varlen(const double *q, const double *k, const double *v,
+                                     const double *beta, const double *g, const double *S0,
+                                     double *o, double *S_final, const int64_t *cu_seqlens,
+                                     int N, int H, int dk, int dv, int nthreads)
+{
+    if (!g) return -1;
+    return varlen_fwd(q, k, v, beta, g, S0, o, S_final, cu_seqlens, N, H, dk, dv, nthreads);
 }
 
 int oracle_max_threads(void)

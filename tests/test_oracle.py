@@ -264,10 +264,185 @@ def pin_chunked_agreement(lib):
     return bool(ok)
 
 
+# ---- Gated DeltaNet (p3 "Gated DeltaNet (GDN)"): S_t = a_t S_{t-1}(I - b k k^T) + b v k^T
+
+def _gates(rng, shape, lo=0.3):
+    """log a with a uniform on [lo, 1)."""
+    return np.log(rng.uniform(lo, 1.0, size=shape))
+
+
+def pin_gated_no_decay_is_deltanet(lib):
+    rng = np.random.default_rng(21)
+    q, k, v, beta, S0 = _inputs(rng, B=2, T=19, H=2)
+    o, Sf = oracle.gated_deltanet_fwd(q, k, v, beta, np.zeros(beta.shape), S0, lib=lib)
+    ro, rs = oracle.deltanet_fwd(q, k, v, beta, S0, lib=lib)
+    return _rel(o, ro) < RTOL and _rel(Sf, rs) < RTOL
+
+
+def pin_gated_beta_zero(lib):
+    # No writes: the state only decays, S_t = (a_1 ... a_t) S0.
+    rng = np.random.default_rng(22)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=23, H=2)
+    beta[:] = 0.0
+    g = _gates(rng, beta.shape)
+    o, Sf = oracle.gated_deltanet_fwd(q, k, v, beta, g, S0, lib=lib)
+    lam = np.exp(np.cumsum(g, axis=1))  # [B, T, H]
+    ref_o = lam[..., None] * np.einsum("bhij,bthj->bthi", S0, q)
+    ref_s = lam[:, -1, :, None, None] * S0
+    return _rel(o, ref_o) < RTOL and _rel(Sf, ref_s) < RTOL
+
+
+def pin_gated_single_token(lib):
+    rng = np.random.default_rng(23)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=1, H=2)
+    g = _gates(rng, beta.shape)
+    o, Sf = oracle.gated_deltanet_fwd(q, k, v, beta, g, S0, lib=lib)
+    ok = True
+    for h in range(2):
+        b, a = beta[0, 0, h], np.exp(g[0, 0, h])
+        kk, vv, qq = k[0, 0, h], v[0, 0, h], q[0, 0, h]
+        S1 = a * S0[0, h] @ (np.eye(len(kk)) - b * np.outer(kk, kk)) + b * np.outer(vv, kk)
+        ok &= _rel(Sf[0, h], S1) < RTOL and _rel(o[0, 0, h], S1 @ qq) < RTOL
+    return bool(ok)
+
+
+def pin_gated_read_back(lib):
+    # Unit keys: S_t k_t = a_t (1 - b_t) S_{t-1} k_t + b_t v_t.
+    rng = np.random.default_rng(24)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=10, H=1)
+    g = _gates(rng, beta.shape)
+    ok = True
+    prev = S0[0, 0]
+    for t in range(10):
+        _, St = oracle.gated_deltanet_fwd(q[:, :t + 1], k[:, :t + 1], v[:, :t + 1],
+                                          beta[:, :t + 1], g[:, :t + 1], S0, lib=lib)
+        kt, b, a = k[0, t, 0], beta[0, t, 0], np.exp(g[0, t, 0])
+        ok &= _rel(St[0, 0] @ kt, a * (1 - b) * (prev @ kt) + b * v[0, t, 0]) < 1e-11
+        prev = St[0, 0]
+    return bool(ok)
+
+
+def pin_gated_orthonormal_keys(lib):
+    # Orthonormal keys from a zero start: no prediction ever fires, and the
+    # output is causal linear attention with scalar decay,
+    # o_t = sum_{i<=t} b_i (a_{i+1} ... a_t) (k_i . q_t) v_i.
+    rng = np.random.default_rng(25)
+    dk, T = 12, 12
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[rng.permutation(dk)][:T][None, :, None]
+    q = _unit_rows(rng, (1, T, 1, dk))
+    v = rng.standard_normal((1, T, 1, 4))
+    beta = rng.uniform(0.1, 1.0, size=(1, T, 1))
+    a = rng.uniform(0.2, 1.0, size=T)
+    o, _ = oracle.gated_deltanet_fwd(q, k, v, beta, np.log(a)[None, :, None], None, lib=lib)
+    ref = np.zeros((T, 4))
+    for t in range(T):
+        for i in range(t + 1):
+            ref[t] += beta[0, i, 0] * np.prod(a[i + 1:t + 1]) * (k[0, i, 0] @ q[0, t, 0]) * v[0, i, 0]
+    return _rel(o[0, :, 0], ref) < 1e-11
+
+
+def pin_gated_reset(lib):
+    # a_t = 0 forgets everything before t: the state after t is b_t v_t k_t^T,
+    # so the rest of the sequence equals a fresh run started at t.
+    rng = np.random.default_rng(26)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=20, H=2)
+    g = _gates(rng, beta.shape)
+    t0 = 8
+    g[:, t0] = -np.inf
+    o, Sf = oracle.gated_deltanet_fwd(q, k, v, beta, g, S0, lib=lib)
+    g_fresh = g[:, t0:].copy()
+    g_fresh[:, 0] = 0.0
+    ro, rs = oracle.gated_deltanet_fwd(q[:, t0:], k[:, t0:], v[:, t0:], beta[:, t0:], g_fresh,
+                                       None, lib=lib)
+    return _rel(o[:, t0:], ro) < RTOL and _rel(Sf, rs) < RTOL
+
+
+def pin_gated_householder(lib):
+    rng = np.random.default_rng(27)
+    q, k, v, beta, S0 = _inputs(rng, B=2, T=8, H=2, dk=5, dv=5)
+    g = _gates(rng, beta.shape, lo=0.1)
+    o, Sf = oracle.gated_deltanet_fwd(q, k, v, beta, g, S0, lib=lib)
+    ok = True
+    for b in range(2):
+        for h in range(2):
+            ro, rs = oracle.householder_unit(q[b, :, h], k[b, :, h], v[b, :, h], beta[b, :, h],
+                                             S0[b, h], a=np.exp(g[b, :, h]))
+            ok &= _rel(o[b, :, h], ro) < 1e-11 and _rel(Sf[b, h], rs) < 1e-11
+    return bool(ok)
+
+
+def pin_gated_exact_rationals(lib):
+    kk = [[Fraction(1, 2), Fraction(-1, 3)], [Fraction(1), Fraction(1, 4)],
+          [Fraction(-2, 5), Fraction(3, 5)], [Fraction(1, 3), Fraction(2, 3)]]
+    vv = [[Fraction(1), Fraction(-2), Fraction(1, 2)], [Fraction(3, 2), Fraction(1, 2), Fraction(0)],
+          [Fraction(-1), Fraction(0), Fraction(2)], [Fraction(2), Fraction(1, 3), Fraction(-1)]]
+    qq = [[Fraction(1), Fraction(1)], [Fraction(0), Fraction(2)], [Fraction(1, 2), Fraction(-1)],
+          [Fraction(-1), Fraction(1, 3)]]
+    bb = [Fraction(1, 2), Fraction(1), Fraction(3, 4), Fraction(1, 5)]
+    aa = [Fraction(3, 4), Fraction(1, 2), Fraction(1), Fraction(2, 5)]
+    S0 = [[Fraction(1, 7), Fraction(-1, 2)], [Fraction(2), Fraction(0)], [Fraction(0), Fraction(1, 3)]]
+    states = oracle.exact_states(kk, vv, bb, S0, a=aa)
+    exact_o = [[sum((states[t][i][j] * qq[t][j] for j in range(2)), Fraction(0)) for i in range(3)]
+               for t in range(4)]
+    f = lambda m: np.array([[float(x) for x in r] for r in m])
+    g = np.log(np.array([float(x) for x in aa]))[None, :, None]
+    o, Sf = oracle.gated_deltanet_fwd(f(qq)[None, :, None], f(kk)[None, :, None],
+                                      f(vv)[None, :, None],
+                                      np.array([float(x) for x in bb])[None, :, None], g,
+                                      S0=f(S0)[None, None], lib=lib)
+    return _rel(o[0, :, 0], f(exact_o)) < 1e-14 and _rel(Sf[0, 0], f(states[-1])) < 1e-14
+
+
+def pin_gated_chunked_agreement(lib):
+    rng = np.random.default_rng(28)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=45, H=2)
+    g = _gates(rng, beta.shape, lo=0.05)
+    o, Sf = oracle.gated_deltanet_fwd(q, k, v, beta, g, S0, lib=lib)
+    ok = True
+    for C in (1, 2, 16, 45):
+        co, cs = oracle.gated_chunked_fwd(q, k, v, beta, g, S0, chunk=C)
+        ok &= _rel(co, o) < 1e-10 and _rel(cs, Sf) < 1e-10
+    return bool(ok)
+
+
+def pin_gated_resume_and_varlen(lib):
+    rng = np.random.default_rng(29)
+    lens = [7, 0, 30, 1]
+    T = sum(lens)
+    H, dk, dv = 2, 6, 5
+    q = _unit_rows(rng, (T, H, dk))
+    k = _unit_rows(rng, (T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    beta = rng.uniform(size=(T, H))
+    g = _gates(rng, (T, H))
+    S0 = rng.standard_normal((len(lens), H, dv, dk))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    o, Sf = oracle.gated_deltanet_fwd_varlen(q, k, v, beta, g, cu, S0, lib=lib)
+    ok = True
+    for n, L in enumerate(lens):
+        a0 = cu[n]
+        if L == 0:
+            ok &= _rel(Sf[n], S0[n]) < RTOL
+            continue
+        t1 = L // 2
+        sl = lambda x, i, j: x[None, a0 + i:a0 + j]
+        oa, Sa = oracle.gated_deltanet_fwd(sl(q, 0, t1), sl(k, 0, t1), sl(v, 0, t1), sl(beta, 0, t1),
+                                           sl(g, 0, t1), S0[n:n + 1], lib=lib)
+        ob, Sb = oracle.gated_deltanet_fwd(sl(q, t1, L), sl(k, t1, L), sl(v, t1, L), sl(beta, t1, L),
+                                           sl(g, t1, L), Sa, lib=lib)
+        ok &= _rel(o[a0:a0 + L], np.concatenate([oa[0], ob[0]])) < RTOL and _rel(Sf[n], Sb[0]) < RTOL
+    return bool(ok)
+
+
 PINS = [pin_golden_three_tokens, pin_golden_three_tokens_lambda, pin_golden_alice_bob,
         pin_beta_zero, pin_single_token, pin_read_back, pin_orthonormal_keys,
         pin_householder_products, pin_square_householder, pin_exact_rationals,
-        pin_full_sequence, pin_linearity, pin_resume, pin_varlen, pin_chunked_agreement]
+        pin_full_sequence, pin_linearity, pin_resume, pin_varlen, pin_chunked_agreement,
+        pin_gated_no_decay_is_deltanet, pin_gated_beta_zero, pin_gated_single_token,
+        pin_gated_read_back, pin_gated_orthonormal_keys, pin_gated_reset,
+        pin_gated_householder, pin_gated_exact_rationals, pin_gated_chunked_agreement,
+        pin_gated_resume_and_varlen]
 
 
 def failed_pins(lib):
@@ -306,6 +481,13 @@ MUTANTS = {
     "dropped_last_token": ("for (int64_t t = 0; t < L; ++t) {",
                            "for (int64_t t = 0; t + 1 < L; ++t) {"),
     "beta_of_head0": ("beta + t0 * H + h,", "beta + t0 * H,"),
+    "gate_after_write": ("        /* decay of the previous state: S <- a_t S */\n        if (g) {",
+                         "        if (0) {"),
+    "gate_not_exponentiated": ("const double at = exp(g[t * beta_stride]);",
+                               "const double at = 1.0 + g[t * beta_stride];"),
+    "gate_of_previous_token": ("const double at = exp(g[t * beta_stride]);",
+                               "const double at = exp(g[(t > 0 ? t - 1 : 0) * beta_stride]);"),
+    "gate_of_head0": ("g ? g + t0 * H + h : NULL,", "g ? g + t0 * H : NULL,"),
     "read_before_write": ("        /* write: S += beta_t (v_t - vhat) k_t^T */",
                           "        if (o) { double *ot = o + t * vo_stride;"
                           " for (int i = 0; i < dv; ++i) { const double *Si = S + (size_t)i * dk;"
@@ -331,6 +513,13 @@ def test_planted_mistakes_are_caught(name, mutant_dir):
     old, new = MUTANTS[name]
     assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
     mutated = src.replace(old, new)
+    if name == "gate_after_write":
+        # re-apply the decay after the correction instead of before it
+        anchor = "        /* read-out after the write: o_t = S_t q_t */"
+        assert mutated.count(anchor) == 1
+        mutated = mutated.replace(anchor, "        if (g) { const double at = exp(g[t * beta_stride]);"
+                                  " for (size_t e = 0; e < (size_t)dv * dk; ++e) S[e] *= at; }\n"
+                                  + anchor)
     if name == "read_before_write":
         # drop the original read-out so only the early one remains
         tail_anchor = "        /* read-out after the write: o_t = S_t q_t */\n        if (o) {"
@@ -339,7 +528,7 @@ def test_planted_mistakes_are_caught(name, mutant_dir):
     csrc = os.path.join(mutant_dir, f"{name}.c")
     so = os.path.join(mutant_dir, f"lib{name}.so")
     open(csrc, "w").write(mutated)
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", csrc, "-o", so],
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", csrc, "-o", so, "-lm"],
                    check=True)
     lib = oracle.load(so)
     assert failed_pins(lib), f"planted mistake {name} passed every pin"
@@ -417,6 +606,40 @@ def test_cp_composition(groups):
             _, St = oracle.deltanet_fwd(q[:, :t], k[:, :t], v[:, :t], beta[:, :t], S0)
             ref = St[0, 0]
         assert _rel(starts[g], ref) < 1e-11
+
+
+def test_gated_partial_chunk_equals_zero_padding():
+    # padded tokens with k = 0, beta = 0 and no decay (g = 0) change nothing
+    rng = np.random.default_rng(31)
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=50, H=1)
+    g = _gates(rng, beta.shape)
+    o, Sf = oracle.gated_chunked_fwd(q, k, v, beta, g, S0, chunk=16)
+    pad = 14
+    z = lambda a: np.concatenate([a, np.zeros((1, pad) + a.shape[2:])], axis=1)
+    op, Sp = oracle.gated_chunked_fwd(z(q), z(k), z(v), z(beta), z(g), S0, chunk=16)
+    assert _rel(op[:, :50], o) < 1e-12 and _rel(Sp, Sf) < 1e-12
+
+
+@pytest.mark.parametrize("groups", [1, 3])
+def test_gated_cp_composition(groups):
+    # the gated chunk chain is still affine in the state: S_end = S_start P + Q
+    rng = np.random.default_rng(45 + groups)
+    T, dk, dv = 48, 8, 6
+    q, k, v, beta, S0 = _inputs(rng, B=1, T=T, H=1, dk=dk, dv=dv)
+    gl = _gates(rng, beta.shape, lo=0.2)
+    bounds = np.linspace(0, T, groups + 1).astype(int)
+    Ps, Qs = [], []
+    for gi in range(groups):
+        a, b = bounds[gi], bounds[gi + 1]
+        P, Q = oracle.cp_group_transition(k[0, a:b, 0], v[0, a:b, 0], beta[0, a:b, 0],
+                                          a=np.exp(gl[0, a:b, 0]))
+        Ps.append(P)
+        Qs.append(Q)
+    starts = oracle.cp_compose(S0[0, 0], Ps, Qs)
+    for gi in range(1, groups + 1):
+        t = bounds[gi]
+        _, St = oracle.gated_deltanet_fwd(q[:, :t], k[:, :t], v[:, :t], beta[:, :t], gl[:, :t], S0)
+        assert _rel(starts[gi], St[0, 0]) < 1e-11
 
 
 def test_oracle_threads_do_not_change_results():
