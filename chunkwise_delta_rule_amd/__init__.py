@@ -12,6 +12,9 @@ The method (the state S is dv x dk, read after the write):
 evaluated chunkwise with chunk 64 ("Linear Attention, Visualized", Haoran
 Zhang, DeltaNet > "Complete per-chunk algorithm"), optionally with
 context parallelism over chunk groups ("Context Parallelism for DeltaNet").
+The gated variant (same page, "Gated DeltaNet (GDN)") multiplies the
+previous state by a per-token decay a_t = exp(g_t) first:
+    S_t = a_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
 """
 
 from __future__ import annotations
@@ -21,7 +24,8 @@ import os
 
 import torch
 
-__all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_workspace_bytes",
+__all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
+           "deltanet_workspace_bytes",
            "deltanet_pick_cp_groups", "deltanet_status_string", "longest_first_order",
            "library_path", "load_library", "DeltaNetError", "DN_F32", "DN_BF16"]
 
@@ -60,6 +64,10 @@ def load_library(path: str | None = None):
     lib.deltanet_fwd.restype = i
     lib.deltanet_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.deltanet_fwd_varlen.restype = i
+    lib.deltanet_gated_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.deltanet_gated_fwd.restype = i
+    lib.deltanet_gated_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.deltanet_gated_fwd_varlen.restype = i
     lib.deltanet_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.deltanet_workspace_bytes.restype = sz
     lib.deltanet_pick_cp_groups.argtypes = [i, i, i, i, i, i]
@@ -108,17 +116,7 @@ def _check(t, name, dtype, device, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
-def deltanet_fwd(q, k, v, beta, S0=None, *, chunk: int = 64, cp_groups: int = 1, o=None,
-                 S_final=None, output_final_state: bool = True, workspace=None, stream=None):
-    """Forward pass over [B, T, H, d] inputs (C-ABI ``deltanet_fwd``).
-
-    q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H] (same dtype, fp32 or bf16);
-    S0: [B,H,dv,dk] fp32 or None. Returns (o, S_final); S_final is None when
-    ``output_final_state`` is False. ``cp_groups``: 1 serial, 0 library's
-    choice, G > 1 forced. Preallocated ``o``/``S_final``/``workspace`` are used
-    when given (workspace: a uint8 CUDA tensor of at least
-    ``deltanet_workspace_bytes`` bytes).
-    """
+def _fwd(q, k, v, beta, g, S0, chunk, cp_groups, o, S_final, output_final_state, workspace, stream):
     lib = load_library()
     if k.dim() != 4:
         raise ValueError("k must be [B, T, H, dk]")
@@ -131,6 +129,8 @@ def deltanet_fwd(q, k, v, beta, S0=None, *, chunk: int = 64, cp_groups: int = 1,
     _check(k, "k", dt, dev, (B, T, H, dk))
     _check(v, "v", dt, dev, (B, T, H, dv))
     _check(beta, "beta", dt, dev, (B, T, H))
+    if g is not None:
+        _check(g, "g", torch.float32, dev, (B, T, H))
     if S0 is not None:
         _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
     if o is None:
@@ -145,12 +145,46 @@ def deltanet_fwd(q, k, v, beta, S0=None, *, chunk: int = 64, cp_groups: int = 1,
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
-        st = lib.deltanet_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o),
-                              _ptr(S_final), B, H, T, dk, dv, chunk, _DTYPE_CODE[dt], cp_groups,
-                              _ptr(workspace), ws_bytes, _stream_handle(stream))
+        if g is None:
+            st = lib.deltanet_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o),
+                                  _ptr(S_final), B, H, T, dk, dv, chunk, _DTYPE_CODE[dt], cp_groups,
+                                  _ptr(workspace), ws_bytes, _stream_handle(stream))
+        else:
+            st = lib.deltanet_gated_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0),
+                                        _ptr(o), _ptr(S_final), B, H, T, dk, dv, chunk,
+                                        _DTYPE_CODE[dt], cp_groups, _ptr(workspace), ws_bytes,
+                                        _stream_handle(stream))
     if st != 0:
-        raise DeltaNetError(st, "deltanet_fwd")
+        raise DeltaNetError(st, "deltanet_fwd" if g is None else "deltanet_gated_fwd")
     return o, S_final
+
+
+def deltanet_fwd(q, k, v, beta, S0=None, *, chunk: int = 64, cp_groups: int = 1, o=None,
+                 S_final=None, output_final_state: bool = True, workspace=None, stream=None):
+    """Forward pass over [B, T, H, d] inputs (C-ABI ``deltanet_fwd``).
+
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H] (same dtype, fp32 or bf16);
+    S0: [B,H,dv,dk] fp32 or None. Returns (o, S_final); S_final is None when
+    ``output_final_state`` is False. ``cp_groups``: 1 serial, 0 library's
+    choice, G > 1 forced. Preallocated ``o``/``S_final``/``workspace`` are used
+    when given (workspace: a uint8 CUDA tensor of at least
+    ``deltanet_workspace_bytes`` bytes).
+    """
+    return _fwd(q, k, v, beta, None, S0, chunk, cp_groups, o, S_final, output_final_state,
+                workspace, stream)
+
+
+def deltanet_gated_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64, cp_groups: int = 1, o=None,
+                       S_final=None, output_final_state: bool = True, workspace=None, stream=None):
+    """Gated DeltaNet forward (C-ABI ``deltanet_gated_fwd``).
+
+    As ``deltanet_fwd``, plus g: [B,T,H] float32, the natural logarithm of
+    each token's decay a_t.
+    """
+    if g is None:
+        raise ValueError("g is required")
+    return _fwd(q, k, v, beta, g, S0, chunk, cp_groups, o, S_final, output_final_state,
+                workspace, stream)
 
 
 def longest_first_order(cu_seqlens) -> torch.Tensor:
@@ -165,14 +199,8 @@ def longest_first_order(cu_seqlens) -> torch.Tensor:
     return torch.tensor(order, dtype=torch.int32, device=cu_seqlens.device)
 
 
-def deltanet_fwd_varlen(q, k, v, beta, cu_seqlens, S0=None, *, seq_order=None, chunk: int = 64,
-                        o=None, S_final=None, output_final_state: bool = True, stream=None):
-    """Forward pass over packed sequences (C-ABI ``deltanet_fwd_varlen``).
-
-    q, k: [T,H,dk]; v: [T,H,dv]; beta: [T,H]; cu_seqlens: int32 [N+1] on the
-    device; S0: [N,H,dv,dk] fp32 or None; seq_order: int32 [N] device
-    permutation (scheduling order only) or None.
-    """
+def _fwd_varlen(q, k, v, beta, g, cu_seqlens, S0, seq_order, chunk, o, S_final,
+                output_final_state, stream):
     lib = load_library()
     if k.dim() != 3:
         raise ValueError("k must be [T, H, dk]")
@@ -186,6 +214,8 @@ def deltanet_fwd_varlen(q, k, v, beta, cu_seqlens, S0=None, *, seq_order=None, c
     _check(k, "k", dt, dev, (T, H, dk))
     _check(v, "v", dt, dev, (T, H, dv))
     _check(beta, "beta", dt, dev, (T, H))
+    if g is not None:
+        _check(g, "g", torch.float32, dev, (T, H))
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev, (N + 1,))
     if seq_order is not None:
         _check(seq_order, "seq_order", torch.int32, dev, (N,))
@@ -199,9 +229,40 @@ def deltanet_fwd_varlen(q, k, v, beta, cu_seqlens, S0=None, *, seq_order=None, c
     if S_final is not None:
         _check(S_final, "S_final", torch.float32, dev, (N, H, dv, dk))
     with torch.cuda.device(dev):
-        st = lib.deltanet_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o),
-                                     _ptr(S_final), _ptr(cu_seqlens), _ptr(seq_order), N, T, H, dk,
-                                     dv, chunk, _DTYPE_CODE[dt], _stream_handle(stream))
+        if g is None:
+            st = lib.deltanet_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o),
+                                         _ptr(S_final), _ptr(cu_seqlens), _ptr(seq_order), N, T, H,
+                                         dk, dv, chunk, _DTYPE_CODE[dt], _stream_handle(stream))
+        else:
+            st = lib.deltanet_gated_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                               _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens),
+                                               _ptr(seq_order), N, T, H, dk, dv, chunk,
+                                               _DTYPE_CODE[dt], _stream_handle(stream))
     if st != 0:
-        raise DeltaNetError(st, "deltanet_fwd_varlen")
+        raise DeltaNetError(st, "deltanet_fwd_varlen" if g is None else "deltanet_gated_fwd_varlen")
     return o, S_final
+
+
+def deltanet_fwd_varlen(q, k, v, beta, cu_seqlens, S0=None, *, seq_order=None, chunk: int = 64,
+                        o=None, S_final=None, output_final_state: bool = True, stream=None):
+    """Forward pass over packed sequences (C-ABI ``deltanet_fwd_varlen``).
+
+    q, k: [T,H,dk]; v: [T,H,dv]; beta: [T,H]; cu_seqlens: int32 [N+1] on the
+    device; S0: [N,H,dv,dk] fp32 or None; seq_order: int32 [N] device
+    permutation (scheduling order only) or None.
+    """
+    return _fwd_varlen(q, k, v, beta, None, cu_seqlens, S0, seq_order, chunk, o, S_final,
+                       output_final_state, stream)
+
+
+def deltanet_gated_fwd_varlen(q, k, v, beta, g, cu_seqlens, S0=None, *, seq_order=None,
+                              chunk: int = 64, o=None, S_final=None,
+                              output_final_state: bool = True, stream=None):
+    """Gated DeltaNet over packed sequences (C-ABI ``deltanet_gated_fwd_varlen``).
+
+    As ``deltanet_fwd_varlen``, plus g: [T,H] float32 log decays.
+    """
+    if g is None:
+        raise ValueError("g is required")
+    return _fwd_varlen(q, k, v, beta, g, cu_seqlens, S0, seq_order, chunk, o, S_final,
+                       output_final_state, stream)

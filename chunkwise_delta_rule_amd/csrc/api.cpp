@@ -71,42 +71,10 @@ size_t ws_bytes_for(int B, int H, int dk, int dv, int G) {
     return (size_t)B * H * G * ((size_t)dk * dk + 2 * (size_t)dv * dk) * sizeof(float);
 }
 
-} // namespace
-
-extern "C" {
-
-const char *deltanet_status_string(int status) {
-    switch (status) {
-    case DN_OK: return "ok";
-    case DN_ERR_INVALID: return "invalid argument";
-    case DN_ERR_UNSUPPORTED: return "unsupported shape or chunk size";
-    case DN_ERR_WORKSPACE: return "workspace missing or too small";
-    case DN_ERR_HIP: return "HIP runtime or launch failure";
-    default: return "unknown status";
-    }
-}
-
-int deltanet_pick_cp_groups(int B, int H, int T, int dk, int dv, int chunk) {
-    const int st = check_shape(dk, dv, chunk, DN_BF16);
-    if (st != DN_OK && check_shape(dk, dv, chunk, DN_F32) != DN_OK) return st;
-    if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
-    int G, cpg;
-    resolve_groups(0, B, H, T, dv, G, cpg);
-    return G;
-}
-
-size_t deltanet_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int cp_groups) {
-    if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return 0;
-    if (check_shape(dk, dv, chunk, DN_BF16) != DN_OK && check_shape(dk, dv, chunk, DN_F32) != DN_OK)
-        return 0;
-    int G, cpg;
-    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
-    return ws_bytes_for(B, H, dk, dv, G);
-}
-
-int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta, const float *S0,
-                 void *o, float *S_final, int B, int H, int T, int dk, int dv, int chunk, int dtype,
-                 int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+// Dense forward, with (g != nullptr) or without the per-token decay.
+int fwd_dense(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
+              void *o, float *S_final, int B, int H, int T, int dk, int dv, int chunk, int dtype, int cp_groups,
+              void *workspace, size_t workspace_bytes, hipStream_t stream) {
     int st = check_shape(dk, dv, chunk, dtype);
     if (st != DN_OK) return st;
     if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return DN_ERR_INVALID;
@@ -115,6 +83,7 @@ int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta, 
         if (!q || !k || !v || !beta || !o) return DN_ERR_INVALID;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return DN_ERR_INVALID;
         if (!aligned_to(beta, esz)) return DN_ERR_INVALID;
+        if (g && !aligned_to(g, 4)) return DN_ERR_INVALID;
     }
     if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return DN_ERR_INVALID;
     if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
@@ -130,6 +99,7 @@ int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta, 
     a.k = k;
     a.v = v;
     a.beta = beta;
+    a.g = g;
     a.o = o;
     a.S0 = S0;
     a.S_final = S_final;
@@ -168,10 +138,9 @@ int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta, 
     return err == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 
-int deltanet_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
-                        const float *S0, void *o, float *S_final, const int32_t *cu_seqlens,
-                        const int32_t *seq_order, int N, int total_T, int H, int dk, int dv,
-                        int chunk, int dtype, hipStream_t stream) {
+int fwd_varlen(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
+               void *o, float *S_final, const int32_t *cu_seqlens, const int32_t *seq_order, int N, int total_T,
+               int H, int dk, int dv, int chunk, int dtype, hipStream_t stream) {
     int st = check_shape(dk, dv, chunk, dtype);
     if (st != DN_OK) return st;
     if (N <= 0 || H <= 0 || total_T < 0 || !cu_seqlens) return DN_ERR_INVALID;
@@ -180,6 +149,7 @@ int deltanet_fwd_varlen(const void *q, const void *k, const void *v, const void 
         if (!q || !k || !v || !beta || !o) return DN_ERR_INVALID;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return DN_ERR_INVALID;
         if (!aligned_to(beta, esz)) return DN_ERR_INVALID;
+        if (g && !aligned_to(g, 4)) return DN_ERR_INVALID;
     }
     if (!aligned_to(cu_seqlens, 4) || (seq_order && !aligned_to(seq_order, 4))) return DN_ERR_INVALID;
     if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return DN_ERR_INVALID;
@@ -190,6 +160,7 @@ int deltanet_fwd_varlen(const void *q, const void *k, const void *v, const void 
     a.k = k;
     a.v = v;
     a.beta = beta;
+    a.g = g;
     a.o = o;
     a.S0 = S0;
     a.S_final = S_final;
@@ -203,6 +174,72 @@ int deltanet_fwd_varlen(const void *q, const void *k, const void *v, const void 
     a.n_tiles = dv / dn::kRows;
     hipError_t err = dn::launch_chain(dtype, dk, dv, true, a, stream);
     return err == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *deltanet_status_string(int status) {
+    switch (status) {
+    case DN_OK: return "ok";
+    case DN_ERR_INVALID: return "invalid argument";
+    case DN_ERR_UNSUPPORTED: return "unsupported shape or chunk size";
+    case DN_ERR_WORKSPACE: return "workspace missing or too small";
+    case DN_ERR_HIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+    }
+}
+
+int deltanet_pick_cp_groups(int B, int H, int T, int dk, int dv, int chunk) {
+    const int st = check_shape(dk, dv, chunk, DN_BF16);
+    if (st != DN_OK && check_shape(dk, dv, chunk, DN_F32) != DN_OK) return st;
+    if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
+    int G, cpg;
+    resolve_groups(0, B, H, T, dv, G, cpg);
+    return G;
+}
+
+size_t deltanet_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int cp_groups) {
+    if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return 0;
+    if (check_shape(dk, dv, chunk, DN_BF16) != DN_OK && check_shape(dk, dv, chunk, DN_F32) != DN_OK)
+        return 0;
+    int G, cpg;
+    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    return ws_bytes_for(B, H, dk, dv, G);
+}
+
+int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta, const float *S0,
+                 void *o, float *S_final, int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                 int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return fwd_dense(q, k, v, beta, nullptr, S0, o, S_final, B, H, T, dk, dv, chunk, dtype, cp_groups, workspace,
+                     workspace_bytes, stream);
+}
+
+int deltanet_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                        const float *S0, void *o, float *S_final, const int32_t *cu_seqlens,
+                        const int32_t *seq_order, int N, int total_T, int H, int dk, int dv,
+                        int chunk, int dtype, hipStream_t stream) {
+    return fwd_varlen(q, k, v, beta, nullptr, S0, o, S_final, cu_seqlens, seq_order, N, total_T, H, dk, dv, chunk,
+                      dtype, stream);
+}
+
+int deltanet_gated_fwd(const void *q, const void *k, const void *v, const void *beta, const float *g,
+                       const float *S0, void *o, float *S_final, int B, int H, int T, int dk, int dv,
+                       int chunk, int dtype, int cp_groups, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    if (T > 0 && !g) return DN_ERR_INVALID;
+    return fwd_dense(q, k, v, beta, g, S0, o, S_final, B, H, T, dk, dv, chunk, dtype, cp_groups, workspace,
+                     workspace_bytes, stream);
+}
+
+int deltanet_gated_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                              const float *g, const float *S0, void *o, float *S_final,
+                              const int32_t *cu_seqlens, const int32_t *seq_order, int N, int total_T,
+                              int H, int dk, int dv, int chunk, int dtype, hipStream_t stream) {
+    if (total_T > 0 && !g) return DN_ERR_INVALID;
+    return fwd_varlen(q, k, v, beta, g, S0, o, S_final, cu_seqlens, seq_order, N, total_T, H, dk, dv, chunk, dtype,
+                      stream);
 }
 
 } // extern "C"

@@ -28,7 +28,17 @@
 //              stage K from HBM
 // One barrier per chunk; a buffer written in an iteration is read by nobody
 // in that iteration. LDS rings: K x4, Q x2, T^T x2, P x2, V x2, N x2, X x2,
-// off-diagonal operands x2, beta x4.
+// off-diagonal operands x2, beta x4 (and decay prefix sums x4 when gated).
+//
+// Gated DeltaNet (same page, "Gated DeltaNet (GDN)" > "Complete per-chunk
+// algorithm"). Wave 5 also stages the decay logarithms and turns them into
+// in-chunk prefix sums gamma_l (base-2 units, one token per lane). Then
+//   A and P take the factor exp(gamma_l - gamma_i) on every unmasked entry,
+//   Y = V - diag(exp(gamma)) K S^T, O = diag(exp(gamma)) Q S^T + P Z and
+//   S <- exp(gamma_C) S + Z^T diag(exp(gamma_C - gamma)) K.
+// The consumers apply the row factors to their accumulators (Y, the Q S^T
+// part of O, the state) and to Z before the update; every factor is a
+// difference of prefix sums with the later one first, so it lies in (0, 1].
 //
 // Matrix-core layout (16x16x32 bf16, wave64, lane l = 16 g + c, g = l / 16):
 // lane l holds row (or column) c of an operand and the 8 contraction slots
@@ -96,6 +106,10 @@ __device__ inline bf16x4 tr4(const __bf16 *p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
 }
 __device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
+__device__ inline f32x4 exp2v(f32x4 x) {
+    return f32x4{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]), __builtin_amdgcn_exp2f(x[2]),
+                 __builtin_amdgcn_exp2f(x[3])};
+}
 
 // Compile-time loop: f(Int<I>{}) for I = B..E-1. Long unrolled step lists go
 // through this rather than #pragma unroll, whose size limit would otherwise
@@ -177,6 +191,8 @@ template <int DK> struct WsLds {
     static constexpr size_t oA = oX + 2 * szX; // off-diagonal Gram operands
     static constexpr size_t oB = oA + 2 * szA; // beta ring, 4 x 64 fp32, c % 4
     static constexpr size_t total = oB + sizeof(float) * 4 * 64;
+    static constexpr size_t oG = total; // gated: decay prefix sums, 4 x 64 fp32, c % 4
+    static constexpr size_t total_gated = oG + sizeof(float) * 4 * 64;
 };
 
 // Shared LDS pointers of one workgroup.
@@ -192,6 +208,7 @@ template <int DK> struct WsBufs {
     __device__ inline float *X(int c) const { return (float *)(base + LY::oX + (c & 1) * LY::szX); }
     __device__ inline __bf16 *A(int c) const { return (__bf16 *)(base + LY::oA + (c & 1) * LY::szA); }
     __device__ inline float *B(int c) const { return (float *)(base + LY::oB) + (c & 3) * 64; }
+    __device__ inline float *G(int c) const { return (float *)(base + LY::oG) + (c & 3) * 64; }
 };
 
 // Global -> register -> LDS staging. A partial last chunk re-reads its last
@@ -243,16 +260,20 @@ template <int DK> struct KStager {
 };
 
 // V tile (64 x 64) and beta by the 64 lanes of wave 5: lane l owns the
-// 16-byte piece 8 (l % 8) of rows l / 8 + 8 p, p = 0..7, and beta of row l.
+// 16-byte piece 8 (l % 8) of rows l / 8 + 8 p, p = 0..7, and beta (and the
+// decay logarithm, when gated) of row l.
 struct VStager {
     static constexpr int NV = 8;
     const __bf16 *vt, *bt;
+    const float *gt; // log decays, or nullptr
     int64_t sv;
     int H, len, lane, rv0, col;
     bf16x8 r[2][NV];
     __bf16 rb[2];
+    float rg[2];
     int n[2], nb[2];
-    __device__ inline void init(const __bf16 *vg, const __bf16 *bg, int64_t sv_, int H_, int len_, int lane_) {
+    __device__ inline void init(const __bf16 *vg, const __bf16 *bg, const float *gg, int64_t sv_, int H_, int len_,
+                                int lane_) {
         sv = sv_;
         H = H_;
         len = len_;
@@ -261,10 +282,12 @@ struct VStager {
         col = 8 * (lane % 8);
         vt = vg + rv0 * sv + col;
         bt = bg;
+        gt = gg;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             n[b] = nb[b] = 0;
             rb[b] = (__bf16)0.f;
+            rg[b] = 0.f;
 #pragma unroll
             for (int p = 0; p < NV; ++p) r[b][p] = bf16x8{};
         }
@@ -286,6 +309,7 @@ struct VStager {
     template <int B> __device__ inline void load_beta(int c) {
         nb[B] = rows_of(len, c);
         rb[B] = bt[((int64_t)c * kChunk + min(lane, nb[B] - 1)) * H];
+        if (gt) rg[B] = gt[((int64_t)c * kChunk + min(lane, nb[B] - 1)) * H];
     }
     template <int B> __device__ inline void write_v(__bf16 *Vs) const {
         const bf16x8 z = {};
@@ -296,6 +320,17 @@ struct VStager {
         }
     }
     template <int B> __device__ inline void write_beta(float *Bs) const { Bs[lane] = lane < nb[B] ? (float)rb[B] : 0.f; }
+    // Inclusive prefix sum of the chunk's decay logarithms over the lanes
+    // (token l in lane l), in base-2 units; tokens past the end add nothing.
+    template <int B> __device__ inline void write_gate(float *Gs) const {
+        float x = lane < nb[B] ? rg[B] * 1.44269504088896340736f : 0.f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        Gs[lane] = x;
+    }
 };
 
 // Waves 6-7: the Q rows of two 16-row blocks (wave 6: blocks 0 and 3, wave
@@ -436,13 +471,13 @@ __device__ inline bf16x8 chain_fetch(int i, const ChainSrc<DK, WO> &src, int lan
 
 __device__ inline f32x4 widen4(bf16x4 v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
 
-template <int DK, bool WO>
+template <int DK, bool WO, bool GATED>
 __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)[DK / 16], __bf16 *og, int64_t sv,
                                       int nval, bool has_v, int cw, int lane, int g, int c16) {
     using CS = ChainSteps<DK, WO>;
     constexpr int D = CS::depth;
     const ChainSrc<DK, WO> src{bf.K(r), WO ? bf.Q(r) : nullptr, bf.Tt(r), WO ? bf.P(r) : nullptr};
-    bf16x8 SB[CS::NKB], YB[2], ZB[2], buf[D];
+    bf16x8 SB[CS::NKB], YB[2], ZB[2], ZS[2], buf[D];
     f32x4 Y[4], Z[4], O[4];
     // V_t in the accumulator layout: lane (g, c) gets V[16t + 4g + e][16cw + c]
     bf16x4 vf[4];
@@ -454,6 +489,23 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
             vf[2 * s] = tr4(Vb + s64off(row, col));
             vf[2 * s + 1] = tr4(Vb + s64off(row + 16, col));
         }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vf[t] = bf16x4{};
+    }
+    // Gated: prefix sums of the tokens this lane's accumulators touch:
+    // gv[t][e] of token 16t + 4g + e (rows of Y and Z), gq[t] of token
+    // 16t + c (columns of O), gC of the chunk's last token.
+    f32x4 gv[4];
+    float gq[4], gC = 0.f;
+    if constexpr (GATED) {
+        const float *Gs = bf.G(r);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            gv[t] = *reinterpret_cast<const f32x4 *>(Gs + 16 * t + 4 * g);
+            gq[t] = Gs[16 * t + c16];
+        }
+        gC = Gs[kChunk - 1];
     }
     static_for<0, D>([&](auto ic) { buf[ic.value] = chain_fetch<DK, WO>(ic.value, src, lane, g, c16); });
     // SB_s slots = dk 32 s + 8 g + 0..7: tiles (2s, 2s+1) hold the low / high
@@ -464,10 +516,15 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
         const bf16x4 lo = cvt4(-Sacc[2 * s]), hi = cvt4(-Sacc[2 * s + 1]);
         SB[s] = odd ? cat8(hi, lo) : cat8(lo, hi);
     }
+    if constexpr (GATED) { // the decayed state the update adds to
+        const float eC = __builtin_amdgcn_exp2f(gC);
+#pragma unroll
+        for (int m = 0; m < CS::NMT; ++m) Sacc[m] *= eC;
+    }
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        Y[t] = has_v ? widen4(vf[t]) : zero;
+        Y[t] = GATED ? zero : widen4(vf[t]); // gated: -K S^T first, V added with the row factors
         Z[t] = zero;
         O[t] = zero;
     }
@@ -477,20 +534,34 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
         const bf16x8 f = buf[i % D];
         if constexpr (i + D < CS::n) buf[i % D] = chain_fetch<DK, WO>(i + D, src, lane, g, c16);
         if constexpr (i == CS::bZ) {
+            if constexpr (GATED) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) Y[t] = widen4(vf[t]) + exp2v(gv[t]) * Y[t];
+            }
             YB[0] = cvt8(Y[0], Y[1]);
             YB[1] = cvt8(Y[2], Y[3]);
         }
         if constexpr (i == CS::bOp) {
             ZB[0] = cvt8(Z[0], Z[1]);
             ZB[1] = cvt8(Z[2], Z[3]);
+            if constexpr (GATED) { // rows of Z scaled by exp(gamma_C - gamma_l) for the update
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    ZS[s] = cvt8(Z[2 * s] * exp2v(gC - gv[2 * s]), Z[2 * s + 1] * exp2v(gC - gv[2 * s + 1]));
+            }
         }
         fence();
         constexpr int k = CS::kind(i), j = CS::idx(i);
         if constexpr (k == CS::kY) Y[j / CS::NKB] = mfma32(f, SB[j % CS::NKB], Y[j / CS::NKB]);
         if constexpr (k == CS::kOq) O[j / CS::NKB] = mfma32(SB[j % CS::NKB], f, O[j / CS::NKB]);
         if constexpr (k == CS::kZ) Z[CS::tT(j)] = mfma32(f, YB[CS::tS(j)], Z[CS::tT(j)]);
-        if constexpr (k == CS::kOp) O[CS::tT(j)] = mfma32(ZB[CS::tS(j)], f, O[CS::tT(j)]);
-        if constexpr (k == CS::kS) Sacc[j / 2] = mfma32(f, ZB[j % 2], Sacc[j / 2]);
+        if constexpr (k == CS::kOp) {
+            // gated: the Q S^T part of O tile t is complete; scale its token
+            // columns before the first P Z product of the tile
+            if constexpr (GATED && CS::tS(j) == 0) O[CS::tT(j)] *= __builtin_amdgcn_exp2f(gq[CS::tT(j)]);
+            O[CS::tT(j)] = mfma32(ZB[CS::tS(j)], f, O[CS::tT(j)]);
+        }
+        if constexpr (k == CS::kS) Sacc[j / 2] = mfma32(f, GATED ? ZS[j % 2] : ZB[j % 2], Sacc[j / 2]);
         fence();
     });
     if constexpr (WO) {
@@ -503,7 +574,7 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
     }
 }
 
-template <int DK, int DV, bool WO>
+template <int DK, int DV, bool WO, bool GATED>
 __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int cw, int lane,
                               int g, int c16) {
     constexpr int NMT = DK / 16;
@@ -517,7 +588,7 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     __syncthreads(); // matches the producers' prologue
     for (int r = -3; r < NC; ++r) {
         if (r >= 0)
-            consumer_chain<DK, WO>(bf, r, Sacc, WO ? og + (int64_t)r * kChunk * sv : nullptr, sv,
+            consumer_chain<DK, WO, GATED>(bf, r, Sacc, WO ? og + (int64_t)r * kChunk * sv : nullptr, sv,
                                    min(kChunk, wk.len - r * kChunk), has_v, cw, lane, g, c16);
         __syncthreads();
     }
@@ -553,7 +624,8 @@ template <int DK> __device__ inline f32x4 dot_tile(const bf16x8 (&x)[DK / 32], c
 // go to A(c) as bf16 k16 operands: lane (g, j) holds A[16a + j][16c + 4g ..
 // +3], per lane in the order A10, A20, A21, A30, A31, A32. The off-diagonal
 // products cover the LDS round trip of X before the solve reads it back.
-template <int DK> __device__ inline void gram_tiles(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
+// Gated: entry (l, i) of A_ac also takes the decay exp(gamma_l - gamma_i).
+template <int DK, bool GATED> __device__ inline void gram_tiles(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
     using LY = WsLds<DK>;
     KRows<DK> k;
     k_rows<DK>(k, bf.K(c), g, c16);
@@ -563,28 +635,48 @@ template <int DK> __device__ inline void gram_tiles(const WsBufs<DK> &bf, int c,
         *reinterpret_cast<f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g) = dot_tile<DK>(k.f[b], k.f[b]);
     const float *Bs = bf.B(c);
     const float b1 = Bs[16 + c16], b2 = Bs[32 + c16], b3 = Bs[48 + c16];
+    // row factors of A_ac: beta of row token 16a + j, times the decay when gated
+    f32x4 s10 = {b1, b1, b1, b1}, s20 = {b2, b2, b2, b2}, s21 = s20, s30 = {b3, b3, b3, b3}, s31 = s30, s32 = s30;
+    if constexpr (GATED) {
+        const float *Gs = bf.G(c);
+        const float g1 = Gs[16 + c16], g2 = Gs[32 + c16], g3 = Gs[48 + c16];
+        const f32x4 h0 = *reinterpret_cast<const f32x4 *>(Gs + 4 * g);
+        const f32x4 h1 = *reinterpret_cast<const f32x4 *>(Gs + 16 + 4 * g);
+        const f32x4 h2 = *reinterpret_cast<const f32x4 *>(Gs + 32 + 4 * g);
+        s10 *= exp2v(g1 - h0);
+        s20 *= exp2v(g2 - h0);
+        s21 *= exp2v(g2 - h1);
+        s30 *= exp2v(g3 - h0);
+        s31 *= exp2v(g3 - h1);
+        s32 *= exp2v(g3 - h2);
+    }
     __bf16 *As = bf.A(c) + 4 * lane;
     // dot_tile(K_c, K_a)[i] = k_{16c+4g+i} . k_{16a+j} = G[16a + j][16c + 4g + i]
-    st4(As + 0 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[1]) * b1));
-    st4(As + 1 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[2]) * b2));
-    st4(As + 2 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[2]) * b2));
-    st4(As + 3 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[3]) * b3));
-    st4(As + 4 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[3]) * b3));
-    st4(As + 5 * 256, cvt4(dot_tile<DK>(k.f[2], k.f[3]) * b3));
+    st4(As + 0 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[1]) * s10));
+    st4(As + 1 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[2]) * s20));
+    st4(As + 2 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[2]) * s21));
+    st4(As + 3 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[3]) * s30));
+    st4(As + 4 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[3]) * s31));
+    st4(As + 5 * 256, cvt4(dot_tile<DK>(k.f[2], k.f[3]) * s32));
 }
 
 // Wave 4, after gram_tiles on the same chunk: lane group b solves diagonal
 // block b: lane (b, j) computes column j of N_bb = (I + A_bb)^-1 from row j
 // of G_bb (its own row of X); writes N_bb^T (bf16, for wave 5's products)
 // and replaces its row of X with column j of T_bb = N_bb beta_j in fp32.
-template <int DK> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c, int g, int c16) {
+// Gated: entry (j, i) of A_bb also takes the decay exp(gamma_j - gamma_i).
+template <int DK, bool GATED> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c, int g, int c16) {
     using LY = WsLds<DK>;
     float *Xr = bf.X(c) + (16 * g + c16) * LY::LX;
     const float br = bf.B(c)[16 * g + c16];
     float arow[16];
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
-        const f32x4 t = *reinterpret_cast<const f32x4 *>(Xr + 4 * j4);
+        f32x4 t = *reinterpret_cast<const f32x4 *>(Xr + 4 * j4);
+        if constexpr (GATED) {
+            const float *Gs = bf.G(c) + 16 * g;
+            t *= exp2v(Gs[c16] - *reinterpret_cast<const f32x4 *>(Gs + 4 * j4)); // masked entries unused
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) arow[4 * j4 + e] = (4 * j4 + e < c16) ? t[e] * br : 0.f;
     }
@@ -653,15 +745,17 @@ template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, int c, 
 }
 
 // Waves 6-7: the score tiles of chunk c, wave 6 row blocks {0, 3}, wave 7
-// blocks {1, 2}, written as -P operand fragments.
+// blocks {1, 2}, written as -P operand fragments. Gated: entry (l, i) also
+// takes the decay exp(gamma_l - gamma_i).
 __device__ constexpr int kPA[2][5] = {{0, 3, 3, 3, 3}, {1, 1, 2, 2, 2}};
 __device__ constexpr int kPC[2][5] = {{0, 0, 1, 2, 3}, {0, 1, 0, 1, 2}};
-template <int DK, int B>
+template <int DK, int B, bool GATED>
 __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c, int half, int lane, int g, int c16) {
     const __bf16 *Kb = bf.K(c);
     __bf16 *Pb = bf.P(c) + 8 * lane;
     KRows<DK> k;
     k_rows<DK>(k, Kb, g, c16);
+    const float *Gs = bf.G(c);
     bf16x4 p[5];
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
@@ -669,6 +763,8 @@ __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c,
         const int qi = half ? pa - 1 : (pa == 3 ? 1 : 0);
         // acc[e] = k_{16pc+4g+e} . q_{16pa+c} = P[16pa + c][16pc + 4g + e]
         f32x4 acc = dot_tile<DK>(k.f[pc], q.f[B][qi]);
+        if constexpr (GATED) // masked entries (diagonal tiles) are replaced below
+            acc *= exp2v(Gs[16 * pa + c16] - *reinterpret_cast<const f32x4 *>(Gs + 16 * pc + 4 * g));
         if (pa == pc) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e > c16) ? 0.f : acc[e];
@@ -683,7 +779,7 @@ __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c,
     }
 }
 
-template <int DK, int DV, bool WO, int ROLE>
+template <int DK, int DV, bool WO, bool GATED, int ROLE>
 __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int g, int c16) {
     const bool has_v = WO || wk.has_v;
     const int lane = 16 * g + c16;
@@ -693,7 +789,8 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     QStage<DK> q;
     if constexpr (ROLE == 1)
         vs.init(reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0,
-                reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h, sv, a.H, wk.len, lane);
+                reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h,
+                GATED ? a.g + wk.tok0 * a.H + wk.h : nullptr, sv, a.H, wk.len, lane);
     if constexpr (ROLE >= 2) {
         ks.init(reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len,
                 64 * (ROLE - 2) + lane);
@@ -734,12 +831,13 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
         constexpr int S = 1 - decltype(rpar)::value; // set of chunks r+1, r+3, r+5
         if constexpr (ROLE == 0) {
             if (r + 2 >= 0 && r + 2 < NC) {
-                gram_tiles<DK>(bf, r + 2, lane, g, c16);
-                diag_solve<DK>(bf, r + 2, g, c16);
+                gram_tiles<DK, GATED>(bf, r + 2, lane, g, c16);
+                diag_solve<DK, GATED>(bf, r + 2, g, c16);
             }
         } else if constexpr (ROLE == 1) {
             if (has_v) vs.template write_v<S>(bf.V(r + 1));
             vs.template write_beta<S>(bf.B(r + 3));
+            if constexpr (GATED) vs.template write_gate<S>(bf.G(r + 3));
             if (has_v) vs.template load_v<S>(min(max(r + 3, 0), last));
             vs.template load_beta<S>(min(r + 5, last));
             if (r + 1 >= 0 && r + 1 < NC) off_solve<DK>(bf, r + 1, lane, g, c16);
@@ -749,7 +847,7 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
             if constexpr (WO) {
                 if (r + 1 >= 0 && r + 1 < NC) {
                     q.template write<S>(bf.Q(r + 1), g);
-                    p_tiles<DK, S>(bf, q, r + 1, ROLE - 2, lane, g, c16);
+                    p_tiles<DK, S, GATED>(bf, q, r + 1, ROLE - 2, lane, g, c16);
                 }
             }
             if constexpr (WO) q.template load<S>(min(max(r + 3, 0), last));
@@ -762,11 +860,12 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     }
 }
 
-template <int DK, int DV, bool WO>
+template <int DK, int DV, bool WO, bool GATED>
 __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a) {
     using LY = WsLds<DK>;
-    static_assert(LY::total <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
+    constexpr size_t kLds = GATED ? LY::total_gated : LY::total;
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -785,22 +884,25 @@ __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a)
     __syncthreads();
 
     if (wave < 4) {
-        consumer_loop<DK, DV, WO>(a, wk, bf, NC, wave, lane, g, c16);
+        consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
     } else if (wave == 4) {
-        producer_loop<DK, DV, WO, 0>(a, wk, bf, NC, g, c16);
+        producer_loop<DK, DV, WO, GATED, 0>(a, wk, bf, NC, g, c16);
     } else if (wave == 5) {
-        producer_loop<DK, DV, WO, 1>(a, wk, bf, NC, g, c16);
+        producer_loop<DK, DV, WO, GATED, 1>(a, wk, bf, NC, g, c16);
     } else if (wave == 6) {
-        producer_loop<DK, DV, WO, 2>(a, wk, bf, NC, g, c16);
+        producer_loop<DK, DV, WO, GATED, 2>(a, wk, bf, NC, g, c16);
     } else {
-        producer_loop<DK, DV, WO, 3>(a, wk, bf, NC, g, c16);
+        producer_loop<DK, DV, WO, GATED, 3>(a, wk, bf, NC, g, c16);
     }
 }
 
 template <int DK, int DV, bool WO> hipError_t launch_ws(const ChainArgs &a, hipStream_t s) {
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO>), dim3(grid), dim3(kWsThreads), 0, s, a);
+    if (a.g)
+        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, true>), dim3(grid), dim3(kWsThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, false>), dim3(grid), dim3(kWsThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ enum WorkKind : int {
 
 struct ChainArgs {
     const void *q, *k, *v, *beta;
+    const float *g; // log decay per token, layout of beta; nullptr: no decay (DeltaNet)
     void *o;
     const float *S0;
     float *S_final;

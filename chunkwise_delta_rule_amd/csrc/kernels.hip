@@ -18,6 +18,16 @@
 // shared K, Q, W), so each wave owns 16 state rows and runs E on its own;
 // only A-D are shared through LDS.
 //
+// Gated DeltaNet (same page, "Gated DeltaNet (GDN)" > "Complete per-chunk
+// algorithm"): with gamma_l the decay logarithms summed over the chunk up to
+// token l, the masks of A and P take the factor exp(gamma_l - gamma_i), W is
+// built from K with rows scaled by exp(gamma_l), the Q S^T part of O is
+// scaled by exp(gamma_l) per token, and the update becomes
+// S <- exp(gamma_C) S + Z^T (K with rows scaled by exp(gamma_C - gamma_l)).
+// Every factor is a difference of two prefix sums with the later one first,
+// so it lies in (0, 1]; pairs outside a mask are never multiplied in. The
+// prefix sums are kept in LDS in base-2 units (times log2 e).
+//
 // This file holds the fp32 path: chain_kernel_serial (four waves, A-E one
 // after the other; fp32 operands do not fit two chunks in LDS) and the
 // context-parallel prefix composition. The bf16 path, with specialised waves
@@ -81,6 +91,10 @@ template <> struct Tr<__bf16> {
     }
     __device__ static inline float tof(__bf16 x) { return (float)x; }
     __device__ static inline __bf16 fromf(float x) { return (__bf16)x; }
+    __device__ static inline F scale(F x, f32x4 s) {
+        const f32x4 w = {(float)x[0] * s[0], (float)x[1] * s[1], (float)x[2] * s[2], (float)x[3] * s[3]};
+        return cvt(w);
+    }
     // Y[k0 + 4g + e][n0 + c], e = 0..3, from a row-major LDS matrix (ld elements).
     __device__ static inline F ldcol(const __bf16 *Y, int ld, int k0, int n0, int g, int c) {
         const __bf16 *p = Y + (k0 + 4 * g + (c >> 2)) * ld + n0 + 4 * (c & 3);
@@ -108,6 +122,7 @@ template <> struct Tr<float> {
     __device__ static inline F cvt(f32x4 x) { return x; }
     __device__ static inline float tof(float x) { return x; }
     __device__ static inline float fromf(float x) { return x; }
+    __device__ static inline F scale(F x, f32x4 s) { return x * s; }
     __device__ static inline F ldcol(const float *Y, int ld, int k0, int n0, int g, int c) {
         const float *p = Y + (k0 + 4 * g) * ld + n0 + c;
         F r = {p[0], p[ld], p[2 * ld], p[3 * ld]};
@@ -126,6 +141,12 @@ template <typename E> __device__ inline void stf(E *p, typename Tr<E>::F x) {
 template <int I> __device__ inline float row_bcast(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + I,
                                                               0xF, 0xF, true));
+}
+
+// exp2 of each element (decay factors from base-2 prefix sums).
+__device__ inline f32x4 exp2v(f32x4 x) {
+    return f32x4{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]), __builtin_amdgcn_exp2f(x[2]),
+                 __builtin_amdgcn_exp2f(x[3])};
 }
 
 // One column of (I + A)^-1 for a 16x16 strictly lower A held by rows (lane
@@ -204,9 +225,9 @@ template <typename E, int DK> struct Phases {
                     f.kc[cb][kb][h2] = ldrow(Ks, L::K, 16 * cb + c16, 32 * kb + 16 * h2, g);
             }
     }
-    template <int W>
-    __device__ static inline void gram_compute(const GramFrags<W> &f, const float *Bs, float *As, E *Ps, int g,
-                                               int c16) {
+    template <int W, bool GATED>
+    __device__ static inline void gram_compute(const GramFrags<W> &f, const float *Bs, const float *Gs, float *As,
+                                               E *Ps, int g, int c16) {
         using G = GramFrags<W>;
         constexpr bool isP = W & 1;
 #pragma unroll
@@ -221,6 +242,11 @@ template <typename E, int DK> struct Phases {
                     acc = TR::mma32(acc, f.kc[cb][kb][0], f.kc[cb][kb][1], f.xb[which][kb][0], f.xb[which][kb][1]);
                 // acc[e] = k_{16cb+4g+e} . x_{16ab+c16}
                 const int row = 16 * ab + c16, col = 16 * cb + 4 * g;
+                if constexpr (GATED) {
+                    // decay between column token col + e and row token row (masked pairs unused)
+                    const f32x4 gc = *reinterpret_cast<const f32x4 *>(Gs + col);
+                    acc *= exp2v(Gs[row] - gc);
+                }
                 if constexpr (!isP) {
                     const float br = Bs[row];
 #pragma unroll
@@ -318,8 +344,9 @@ template <typename E, int DK> struct Phases {
         F kcol[NMT / 4][4];  // K[16kk + 4g..][16m + c16] for this wave's dk tiles m
         F vcol[4];           // V[16kk + 4g..][16w + c16]
     };
-    __device__ static inline void wu_fetch(WUFrags &f, const E *Ks, const E *Vs, const E *TsT, bool has_v, int w,
-                                           int g, int c16) {
+    template <bool GATED>
+    __device__ static inline void wu_fetch(WUFrags &f, const E *Ks, const E *Vs, const E *TsT, const float *Gs,
+                                           bool has_v, int w, int g, int c16) {
 #pragma unroll
         for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -328,8 +355,13 @@ template <typename E, int DK> struct Phases {
 #pragma unroll
         for (int mm = 0; mm < NMT / 4; ++mm)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+            for (int kk = 0; kk < 4; ++kk) {
                 f.kcol[mm][kk] = TR::ldcol(Ks, L::K, 16 * kk, 16 * (w * (NMT / 4) + mm), g, c16);
+                // W = T (K with token rows scaled by exp(gamma_l))
+                if constexpr (GATED)
+                    f.kcol[mm][kk] =
+                        TR::scale(f.kcol[mm][kk], exp2v(*reinterpret_cast<const f32x4 *>(Gs + 16 * kk + 4 * g)));
+            }
         if (has_v) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) f.vcol[kk] = TR::ldcol(Vs, L::V, 16 * kk, 16 * w, g, c16);
@@ -391,8 +423,10 @@ template <typename E, int DK> struct Phases {
     struct OFrags {
         F qr[4][NKB][2]; // Q rows 16t + c16
         F pr[4][2][2];   // P rows 16t + c16, k blocks s <= t/2
+        float eq[4];     // exp(gamma) of token 16t + c16 (gated)
     };
-    __device__ static inline void o_fetch(OFrags &f, const E *Qs, const E *Ps, int g, int c16) {
+    template <bool GATED>
+    __device__ static inline void o_fetch(OFrags &f, const E *Qs, const E *Ps, const float *Gs, int g, int c16) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -405,33 +439,50 @@ template <typename E, int DK> struct Phases {
                 f.pr[t][s][0] = ldrow(Ps, L::T, 16 * t + c16, 32 * s, g);
                 f.pr[t][s][1] = ldrow(Ps, L::T, 16 * t + c16, 32 * s + 16, g);
             }
+            if constexpr (GATED) f.eq[t] = __builtin_amdgcn_exp2f(Gs[16 * t + c16]);
         }
     }
+    template <bool GATED>
     __device__ static inline void o_compute(const OFrags &f, const F (&SB)[NMT], const F (&ZB)[4], f32x4 (&Oacc)[4]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) acc = TR::mma32(acc, SB[2 * kb], SB[2 * kb + 1], f.qr[t][kb][0], f.qr[t][kb][1]);
+            if constexpr (GATED) acc *= f.eq[t]; // Q rows scaled by exp(gamma_l)
 #pragma unroll
             for (int s = 0; s <= t / 2; ++s) acc = TR::mma32(acc, ZB[2 * s], ZB[2 * s + 1], f.pr[t][s][0], f.pr[t][s][1]);
             Oacc[t] = acc;
         }
     }
 
-    // ---- E3: S^T += K^T Z.
+    // ---- E3: S^T += K^T Z (gated: S^T <- exp(gamma_C) S^T + (K rows scaled by
+    // exp(gamma_C - gamma_l))^T Z).
     struct SFrags {
         F kc[NMT][4]; // K[16kk + 4g..][16m + c16]
+        float ec;     // exp(gamma_C) (gated)
     };
-    __device__ static inline void s_fetch(SFrags &f, const E *Ks, int g, int c16) {
+    template <bool GATED> __device__ static inline void s_fetch(SFrags &f, const E *Ks, const float *Gs, int g, int c16) {
+        f32x4 er[4];
+        if constexpr (GATED) {
+            const float gC = Gs[kChunk - 1];
+            f.ec = __builtin_amdgcn_exp2f(gC);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) er[kk] = exp2v(gC - *reinterpret_cast<const f32x4 *>(Gs + 16 * kk + 4 * g));
+        }
 #pragma unroll
         for (int m = 0; m < NMT; ++m)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) f.kc[m][kk] = TR::ldcol(Ks, L::K, 16 * kk, 16 * m, g, c16);
+            for (int kk = 0; kk < 4; ++kk) {
+                f.kc[m][kk] = TR::ldcol(Ks, L::K, 16 * kk, 16 * m, g, c16);
+                if constexpr (GATED) f.kc[m][kk] = TR::scale(f.kc[m][kk], er[kk]);
+            }
     }
+    template <bool GATED>
     __device__ static inline void s_compute(const SFrags &f, const F (&ZB)[4], f32x4 (&Sacc)[NMT]) {
 #pragma unroll
         for (int m = 0; m < NMT; ++m) {
+            if constexpr (GATED) Sacc[m] *= f.ec;
             Sacc[m] = TR::mma32(Sacc[m], f.kc[m][0], f.kc[m][1], ZB[0], ZB[1]);
             Sacc[m] = TR::mma32(Sacc[m], f.kc[m][2], f.kc[m][3], ZB[2], ZB[3]);
         }
@@ -453,11 +504,13 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
     static_assert(NKQ * NT == kChunk * KQV && NVV * NT == kChunk * VV, "tiling");
 
     const E *kg, *qg, *vg, *bg;
+    const float *gg; // log decays, or nullptr
     int64_t sqk, sv;
     int H, len, tid;
     bool has_v;
     V rk[NKQ], rq[NKQ], rv[NVV];
     E rbeta;
+    float rg;
     int nval;
 
     __device__ inline void load(int c) {
@@ -478,8 +531,9 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
             }
         }
         rbeta = bg[(base + min(tid & (kChunk - 1), last)) * H]; // every wave holds all 64
+        if (gg) rg = gg[(base + min(tid & (kChunk - 1), last)) * H];
     }
-    __device__ inline void store_kqb(E *Ks, E *Qs, float *Bs) const {
+    __device__ inline void store_kqb(E *Ks, E *Qs, float *Bs, float *Gs) const {
         const V zero = {};
 #pragma unroll
         for (int p = 0; p < NKQ; ++p) {
@@ -489,7 +543,19 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
             *reinterpret_cast<V *>(Qs + row * L::K + cv * TR::kVec) = ok ? rq[p] : zero;
         }
         // the four waves write identical values: no branch needed
-        Bs[tid & (kChunk - 1)] = (tid & (kChunk - 1)) < nval ? TR::tof(rbeta) : 0.f;
+        const int l = tid & (kChunk - 1);
+        Bs[l] = l < nval ? TR::tof(rbeta) : 0.f;
+        if (gg) {
+            // inclusive prefix sum over the chunk's tokens (lane l = token l), in
+            // base-2 units; tokens past the end add nothing
+            float x = l < nval ? rg * 1.44269504088896340736f : 0.f;
+#pragma unroll
+            for (int d = 1; d < kChunk; d <<= 1) {
+                const float y = __shfl_up(x, d, kChunk);
+                if (l >= d) x += y;
+            }
+            Gs[l] = x;
+        }
     }
     __device__ inline void store_v(E *Vs) const {
         if (!has_v) return;
@@ -511,6 +577,8 @@ __device__ inline Stager<E, DK, NT> make_stager(const ChainArgs &a, const Work &
     sg.qg = reinterpret_cast<const E *>(a.q) + wk.tok0 * sg.sqk + (int64_t)wk.h * DK;
     sg.vg = reinterpret_cast<const E *>(a.v) + wk.tok0 * sg.sv + (int64_t)wk.h * DV + wk.row0;
     sg.bg = reinterpret_cast<const E *>(a.beta) + wk.tok0 * a.H + wk.h;
+    sg.gg = a.g ? a.g + wk.tok0 * a.H + wk.h : nullptr;
+    sg.rg = 0.f;
     sg.H = a.H;
     sg.len = wk.len;
     sg.tid = tid;
@@ -570,14 +638,15 @@ template <typename E, int DK> struct SmemSerial {
     static constexpr size_t oQs = oKs + L::szK;
     static constexpr size_t oVs = oQs + L::szK;
     static constexpr size_t oBs = oVs + L::szV;
-    static constexpr size_t oTs = oBs + sizeof(float) * kChunk;
+    static constexpr size_t oGs = oBs + sizeof(float) * kChunk; // decay prefix sums
+    static constexpr size_t oTs = oGs + sizeof(float) * kChunk;
     static constexpr size_t oPs = oTs + L::szT;
     static constexpr size_t oNs = oPs + L::szT;
     static constexpr size_t oWA = oNs + L::szN;
     static constexpr size_t total = oWA + L::szWA;
 };
 
-template <typename E, int DK, int DV, bool WRITE_O>
+template <typename E, int DK, int DV, bool WRITE_O, bool GATED>
 __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs a) {
     using TR = Tr<E>;
     using F = typename TR::F;
@@ -591,6 +660,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
     E *Qs = reinterpret_cast<E *>(smem + SM::oQs);
     E *Vs = reinterpret_cast<E *>(smem + SM::oVs);
     float *Bs = reinterpret_cast<float *>(smem + SM::oBs);
+    float *Gs = reinterpret_cast<float *>(smem + SM::oGs);
     E *TsT = reinterpret_cast<E *>(smem + SM::oTs);
     E *Ps = reinterpret_cast<E *>(smem + SM::oPs);
     E *NsT = reinterpret_cast<E *>(smem + SM::oNs);
@@ -616,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
     }
     if (NC > 0) {
         sg.load(0);
-        sg.store_kqb(Ks, Qs, Bs);
+        sg.store_kqb(Ks, Qs, Bs, Gs);
         sg.store_v(Vs);
     }
     __syncthreads();
@@ -632,7 +702,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
         typename PH::template GramFrags<W> f;                                                                  \
         PH::template gram_fetch<W>(f, Ks, Qs, g, c16);                                                         \
         sched_fence();                                                                                         \
-        if (WRITE_O || !(W & 1)) PH::template gram_compute<W>(f, Bs, As, Ps, g, c16);                          \
+        if (WRITE_O || !(W & 1)) PH::template gram_compute<W, GATED>(f, Bs, Gs, As, Ps, g, c16);               \
     } break;
             DN_A(0) DN_A(1) DN_A(2) DN_A(3)
 #undef DN_A
@@ -664,7 +734,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
         // D
         {
             typename PH::WUFrags f;
-            PH::wu_fetch(f, Ks, Vs, TsT, has_v, w, g, c16);
+            PH::template wu_fetch<GATED>(f, Ks, Vs, TsT, Gs, has_v, w, g, c16);
             sched_fence();
             PH::wu_compute(f, Ws, has_v, Zacc, w, g, c16);
         }
@@ -681,19 +751,19 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
         }
         if constexpr (WRITE_O) {
             typename PH::OFrags f;
-            PH::o_fetch(f, Qs, Ps, g, c16);
+            PH::template o_fetch<GATED>(f, Qs, Ps, Gs, g, c16);
             sched_fence();
-            PH::o_compute(f, SB, ZB, Oacc);
+            PH::template o_compute<GATED>(f, SB, ZB, Oacc);
             store_o(og, sv, c, nval, Oacc, w, g, c16);
         }
         {
             typename PH::SFrags f;
-            PH::s_fetch(f, Ks, g, c16);
+            PH::template s_fetch<GATED>(f, Ks, Gs, g, c16);
             sched_fence();
-            PH::s_compute(f, ZB, Sacc);
+            PH::template s_compute<GATED>(f, ZB, Sacc);
         }
         __syncthreads();
-        sg.store_kqb(Ks, Qs, Bs);
+        sg.store_kqb(Ks, Qs, Bs, Gs);
         sg.store_v(Vs);
         __syncthreads();
     }
@@ -751,7 +821,10 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(const ChainArgs a) {
 template <int DK, int DV, bool WO> hipError_t launch_one(const ChainArgs &a, hipStream_t s) {
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((chain_kernel_serial<float, DK, DV, WO>), dim3(grid), dim3(kThreads), 0, s, a);
+    if (a.g)
+        hipLaunchKernelGGL((chain_kernel_serial<float, DK, DV, WO, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((chain_kernel_serial<float, DK, DV, WO, false>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -17,6 +17,20 @@
  * The readout is after the write (inclusive causal mask); q is not scaled;
  * q and k are used exactly as given (no normalisation inside).
  *
+ * Gated DeltaNet (deltanet_gated_fwd*): the same page, section "Gated
+ * DeltaNet (GDN)", adds a per-token scalar decay a_t of the previous state:
+ *     S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t,
+ * evaluated with that section's "Complete per-chunk algorithm": with
+ * lambda[i:j] the product of a over chunk positions i..j, the masks of L and
+ * of Q K^T take the factor lambda[i+1:l] at (l, i), K enters W with rows
+ * scaled by lambda[1:l], Q enters the Q S^T part of O scaled by lambda[1:l],
+ * and S_{r+1} = lambda[1:C] S_r + Z^T (K with rows scaled by lambda[l+1:C]).
+ * The decay is passed as g_t = ln a_t (float32, the layout of beta); a_t = 1
+ * (g_t = 0) gives DeltaNet. The kernels form prefix sums of g within each
+ * chunk and only ever exponentiate differences with the later token first,
+ * so every factor lies in (0, 1] for g <= 0. g must be finite; g > 0 (growth)
+ * is accepted but may overflow.
+ *
  * Context parallelism (cp_groups > 1) splits each unit's chunk chain into
  * groups. Each group first computes its affine map S_end = S_start P_g + Q_g
  * (P_g the ordered product of (I - W^T K) over its chunks, Q_g its state from
@@ -27,13 +41,13 @@
  * recurrence"). The result equals the serial one up to rounding.
  *
  * Layouts (row-major, contiguous, element strides fixed by the shape):
- *   q, k : [B, T, H, dk]    v, o : [B, T, H, dv]    beta : [B, T, H]
+ *   q, k : [B, T, H, dk]    v, o : [B, T, H, dv]    beta, g : [B, T, H]
  *   S0, S_final : [B, H, dv, dk] float32 (S[b,h] is the dv x dk state)
- *   varlen: q, k [T_total, H, dk], v, o [T_total, H, dv], beta [T_total, H],
+ *   varlen: q, k [T_total, H, dk], v, o [T_total, H, dv], beta, g [T_total, H],
  *           S0/S_final [N, H, dv, dk]; sequence n owns tokens
  *           [cu_seqlens[n], cu_seqlens[n+1]) and starts from S0[n] (or zero).
- * q, k, v, beta and o share the element type `dtype`; S0 and S_final are
- * always float32. All arithmetic accumulates in float32; with DN_BF16 the
+ * q, k, v, beta and o share the element type `dtype`; g, S0 and S_final
+ * are always float32. All arithmetic accumulates in float32; with DN_BF16 the
  * matrix-core operands are bfloat16 (intermediates W, T, Z and the state are
  * rounded to bfloat16 where they enter a matrix product; the state itself is
  * kept in float32).
@@ -119,9 +133,34 @@ int deltanet_fwd_varlen(const void *q, const void *k, const void *v, const void 
                         hipStream_t stream);
 
 /*
- * Bytes of workspace deltanet_fwd needs for this shape and cp_groups (0 means
- * the library's choice on the current device). Returns 0 when the resolved
- * group count is 1, and also for invalid shapes.
+ * Gated DeltaNet forward pass over B sequences of T tokens each
+ * ("Gated DeltaNet (GDN)" > "Complete per-chunk algorithm", see above).
+ *   g : log decays ln a_t, float32 [B,T,H], 4-byte aligned; required when T > 0.
+ * Every other argument, the workspace (same size as deltanet_fwd's for the
+ * same shape and cp_groups) and the error behaviour are as in deltanet_fwd.
+ * Context parallelism applies unchanged: a group's chunks still map its
+ * start state affinely to its end state.
+ */
+int deltanet_gated_fwd(const void *q, const void *k, const void *v, const void *beta,
+                       const float *g, const float *S0, void *o, float *S_final, int B, int H,
+                       int T, int dk, int dv, int chunk, int dtype, int cp_groups,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Gated DeltaNet forward pass over N packed sequences.
+ *   g : log decays, float32 [T_total, H]; required when total_T > 0.
+ * Other arguments as in deltanet_fwd_varlen.
+ */
+int deltanet_gated_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                              const float *g, const float *S0, void *o, float *S_final,
+                              const int32_t *cu_seqlens, const int32_t *seq_order, int N,
+                              int total_T, int H, int dk, int dv, int chunk, int dtype,
+                              hipStream_t stream);
+
+/*
+ * Bytes of workspace deltanet_fwd (or deltanet_gated_fwd) needs for this
+ * shape and cp_groups (0 means the library's choice on the current device).
+ * Returns 0 when the resolved group count is 1, and also for invalid shapes.
  */
 size_t deltanet_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
                                 int cp_groups);

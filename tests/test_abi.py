@@ -29,7 +29,8 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = declared_functions()
-    assert set(names) >= {"deltanet_fwd", "deltanet_fwd_varlen", "deltanet_workspace_bytes",
+    assert set(names) >= {"deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd",
+                          "deltanet_gated_fwd_varlen", "deltanet_workspace_bytes",
                           "deltanet_pick_cp_groups", "deltanet_status_string"}
     raw = ctypes.CDLL(dn.library_path())
     for n in names:
@@ -116,6 +117,45 @@ def test_varlen_rejects_bad_arguments(lib, kw, status):
                                  None, vp(FAKE), None, vp(a["cu"]) if a["cu"] else None,
                                  vp(a["order"]) if a["order"] else None, a["N"], a["total_T"], 2,
                                  a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+    assert st == status
+
+
+def call_gated(lib, g=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, S0=None, o=FAKE, S_final=None, B=1, H=1, T=128,
+             dk=64, dv=64, chunk=64, dtype=1, cp_groups=1, ws=None, ws_bytes=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.deltanet_gated_fwd(vp(a["q"]) if a["q"] else None, vp(a["k"]), vp(a["v"]), vp(a["beta"]),
+                                  vp(g) if g else None, None, vp(a["o"]) if a["o"] else None, None,
+                                  a["B"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"],
+                                  a["cp_groups"], vp(a["ws"]) if a["ws"] else None, a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None), DN_ERR_INVALID),
+    (dict(g=FAKE + 2), DN_ERR_INVALID),
+    (dict(q=None), DN_ERR_INVALID),
+    (dict(chunk=32), DN_ERR_UNSUPPORTED),
+    (dict(dtype=0, dk=128), DN_ERR_UNSUPPORTED),
+    (dict(cp_groups=2), DN_ERR_WORKSPACE),
+])
+def test_gated_fwd_rejects_bad_arguments(lib, kw, status):
+    assert call_gated(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None), DN_ERR_INVALID),
+    (dict(g=FAKE + 1), DN_ERR_INVALID),
+    (dict(N=0), DN_ERR_INVALID),
+    (dict(chunk=16), DN_ERR_UNSUPPORTED),
+])
+def test_gated_varlen_rejects_bad_arguments(lib, kw, status):
+    a = dict(g=FAKE, N=2, chunk=64)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    st = lib.deltanet_gated_fwd_varlen(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                       vp(a["g"]) if a["g"] else None, None, vp(FAKE), None,
+                                       vp(FAKE), None, a["N"], 100, 2, 64, 64, a["chunk"], 1, None)
     assert st == status
 
 

@@ -52,8 +52,8 @@ def kernels(asm_text):
 
 
 def test_instances_present(asm):
-    # dk, dv in {64, 128}, with and without output
-    assert len(kernels(asm)) == 8
+    # dk, dv in {64, 128}, with and without output, with and without decay
+    assert len(kernels(asm)) == 16
 
 
 def test_no_scratch_and_register_budget(asm):
