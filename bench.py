@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the DeltaNet chunkwise forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cp-groups G]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cp-groups G] [--gated]
 
 One step = one call of ``deltanet_fwd`` (every kernel of the forward pass) over
 one batch of synthetic inputs already resident in HBM. The default workload is
@@ -9,14 +9,16 @@ B=8, H=16, T=4096, dk=dv=128, chunk 64, bf16 (the paper-scale layer). Prints
 one JSON line with the throughput (tokens/s), the fraction of the bf16
 matrix-core peak, a roofline object for the dominant kernel (timed with HIP
 events on the launch stream) and the fp64 CPU oracle's throughput on the
-host cores.
+host cores. ``--gated`` measures Gated DeltaNet (``deltanet_gated_fwd``, with
+per-token log decays) instead; without it, a short gated run of the same
+workload is reported under ``variants.gated`` next to the headline figures.
 
 Accounting (per head-token, chunk C, key/value widths dk/dv):
   flops  F = 2C(3dk + 2dv) + 6 dk dv  -- the eight dense products of the
          per-chunk algorithm (KK^T, TK, TV, WS^T, QK^T, QS^T, PZ, Z^T K) as
          written, masked halves included; the T solve is not counted
   bytes  read q, k, v, beta (+ S0 when given), write o and S_final: the
-         algorithmic minimum, each tensor touched once.
+         algorithmic minimum, each tensor touched once (gated: + g, fp32).
 """
 
 from __future__ import annotations
@@ -52,10 +54,36 @@ def kernel_sha():
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, esz, n_tokens, n_units, has_s0, has_sf):
+def algorithmic_bytes(w, esz, n_tokens, n_units, has_s0, has_sf, gated=False):
     per_tok = w.H * (2 * w.dk + 2 * w.dv + 1) * esz  # q, k, v, o, beta
+    if gated:
+        per_tok += w.H * 4  # g, fp32
     state = n_units * w.dv * w.dk * 4
     return n_tokens * per_tok + state * (int(has_s0) + int(has_sf))
+
+
+def time_steps(step, warmup, steps):
+    """Run ``warmup`` untimed steps, then ``steps`` timed ones bracketed by
+    synchronisations. Every launch goes on torch's current stream, so events
+    recorded there bracket each step. Returns (ms per step over the whole
+    region, mean of the per-step event times, wall seconds)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    return starts[0].elapsed_time(ends[-1]) / steps, sum(per_step_ms) / len(per_step_ms), wall
 
 
 def load_traffic(workload_name, launch_bytes):
@@ -72,8 +100,9 @@ def load_traffic(workload_name, launch_bytes):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inputs, w, varlen, budget_s):
-    """Time the fp64 oracle on the host on a bounded sample of the workload."""
+def cpu_baseline(inputs, w, varlen, budget_s, g=None):
+    """Time the fp64 oracle on the host on a bounded sample of the workload
+    (the gated oracle when log decays ``g`` are given)."""
     import numpy as np
     import torch
     import oracle
@@ -95,7 +124,10 @@ def cpu_baseline(inputs, w, varlen, budget_s):
         args = [f64(x[:end]) for x in (q, k, v, beta)]
         cu_s = cu[:n + 1].cpu().numpy()
         t0 = time.perf_counter()
-        oracle.deltanet_fwd_varlen(*args, cu_s, None)
+        if g is None:
+            oracle.deltanet_fwd_varlen(*args, cu_s, None)
+        else:
+            oracle.gated_deltanet_fwd_varlen(*args, f64(g[:end]), cu_s, None)
         dt = time.perf_counter() - t0
         toks = end
         sample = f"first {n} of {len(lengths)} sequences ({toks} tokens x {w.H} heads)"
@@ -109,7 +141,10 @@ def cpu_baseline(inputs, w, varlen, budget_s):
         args = [f64(x[:nb]) for x in (q, k, v, beta)]
         s0 = None if S0 is None else f64(S0[:nb])
         t0 = time.perf_counter()
-        oracle.deltanet_fwd(*args, s0)
+        if g is None:
+            oracle.deltanet_fwd(*args, s0)
+        else:
+            oracle.gated_deltanet_fwd(*args, f64(g[:nb]), s0)
         dt = time.perf_counter() - t0
         toks = nb * w.T
         sample = f"{nb} of {B} sequences ({toks} tokens x {w.H} heads)"
@@ -130,6 +165,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="target seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--gated", action="store_true",
+                    help="measure Gated DeltaNet (per-token log decays) instead of DeltaNet")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the short gated run reported under variants.gated")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 1 GiB (for counter calibration)")
     args = ap.parse_args()
@@ -141,7 +180,7 @@ def main():
 
     import torch
     import chunkwise_delta_rule_amd as dn
-    from chunkwise_delta_rule_amd.synth import WORKLOADS, workload_inputs
+    from chunkwise_delta_rule_amd.synth import WORKLOADS, make_gates, workload_inputs
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -161,9 +200,14 @@ def main():
         order = dn.longest_first_order(cu)
         o = torch.empty_like(v)
         Sf = torch.empty((w.N, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+        g = make_gates((n_tokens, w.H), seed=args.seed, device=str(dev))
 
-        def step():
-            dn.deltanet_fwd_varlen(q, k, v, beta, cu, S0, seq_order=order, o=o, S_final=Sf)
+        def step(gated=args.gated):
+            if gated:
+                dn.deltanet_gated_fwd_varlen(q, k, v, beta, g, cu, S0, seq_order=order, o=o,
+                                             S_final=Sf)
+            else:
+                dn.deltanet_fwd_varlen(q, k, v, beta, cu, S0, seq_order=order, o=o, S_final=Sf)
         config = {"workload": w.name, "N": w.N, "H": w.H, "total_T": n_tokens, "dk": w.dk,
                   "dv": w.dv, "chunk": w.chunk, "len_range": [w.len_lo, w.len_hi]}
         groups = 1
@@ -178,9 +222,15 @@ def main():
         groups = (args.cp_groups if args.cp_groups > 0 else
                   dn.deltanet_pick_cp_groups(w.B, w.H, w.T, w.dk, w.dv, w.chunk))
 
-        def step():
-            dn.deltanet_fwd(q, k, v, beta, S0, o=o, S_final=Sf, cp_groups=args.cp_groups,
-                            workspace=ws)
+        g = make_gates((w.B, w.T, w.H), seed=args.seed, device=str(dev))
+
+        def step(gated=args.gated):
+            if gated:
+                dn.deltanet_gated_fwd(q, k, v, beta, g, S0, o=o, S_final=Sf,
+                                      cp_groups=args.cp_groups, workspace=ws)
+            else:
+                dn.deltanet_fwd(q, k, v, beta, S0, o=o, S_final=Sf, cp_groups=args.cp_groups,
+                                workspace=ws)
         config = {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                   "chunk": w.chunk, "cp_groups": groups}
     torch.cuda.synchronize()
@@ -193,29 +243,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: K steps between two synchronisations. Every launch goes on
-    # torch's current stream, so events recorded there bracket each step.
-    stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    total_ms = starts[0].elapsed_time(ends[-1])
-    ms_per_step = total_ms / args.steps
-    avg_launch_ms = sum(per_step_ms) / len(per_step_ms)
+    print(f"[bench] warmup {args.warmup}, timing {args.steps} steps"
+          f"{' (gated)' if args.gated else ''}", file=sys.stderr, flush=True)
+    ms_per_step, avg_launch_ms, wall = time_steps(step, args.warmup, args.steps)
     if not bool(torch.isfinite(o).all()) or not bool(torch.isfinite(Sf).all()):
         print("bench.py: non-finite output", file=sys.stderr)
         sys.exit(3)
@@ -224,24 +254,26 @@ def main():
     head_tokens = n_tokens * w.H
     flops = head_tokens * flops_per_head_token(w.chunk, w.dk, w.dv)
     peak_flops = PEAK_BF16_FLOPS if w.dtype == "bf16" else PEAK_FP32_FLOPS
-    nbytes = algorithmic_bytes(w, esz, n_tokens, n_units, S0 is not None, True)
+    nbytes = algorithmic_bytes(w, esz, n_tokens, n_units, S0 is not None, True, args.gated)
     mfma_frac = flops / (ms_per_step / 1e3) / peak_flops
 
     # Dominant kernel: the serial path is one launch per step; with context
     # parallelism the step holds three launches and the events cover all of
     # them, so the figure is then a whole-step rate.
     achieved_gbps = nbytes / (avg_launch_ms / 1e3) / 1e9
-    traffic = load_traffic(w.name, nbytes) if groups == 1 else None
+    traffic = load_traffic(w.name, nbytes) if groups == 1 and not args.gated else None
+    kname = ("chain_kernel_ws<128,128,out,gated>" if args.gated else "chain_kernel_ws<128,128,out>") \
+        if w.dtype == "bf16" and w.dk == 128 and w.dv == 128 else "chain_kernel"
     roofline = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_BPS / 1e9,
                 "unit": "GB/s", "frac": round(achieved_gbps * 1e9 / PEAK_HBM_BPS, 4),
-                "traffic": traffic, "kernel": "chain_kernel_ws<128,128,out>"
-                if w.dtype == "bf16" and w.dk == 128 and w.dv == 128 else "chain_kernel",
+                "traffic": traffic, "kernel": kname,
                 "algorithmic_bytes": nbytes, "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                 "mfma_tflops": round(flops / (avg_launch_ms / 1e3) / 1e12, 1),
                 "mfma_frac": round(flops / (avg_launch_ms / 1e3) / peak_flops, 4)}
 
+    metric = "forward tokens/sec + % bf16 MFMA peak, B=8 H=16 T=4096 d=128 chunk=64"
     result = {
-        "metric": "forward tokens/sec + % bf16 MFMA peak, B=8 H=16 T=4096 d=128 chunk=64",
+        "metric": ("Gated DeltaNet " + metric) if args.gated else metric,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -259,9 +291,22 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
     }
+    if not args.gated and not args.no_variants:
+        # the same workload through deltanet_gated_fwd (log decays drawn as in synth.make_gates)
+        print("[bench] gated variant: warmup 5, timing 20 steps", file=sys.stderr, flush=True)
+        g_ms, g_launch_ms, _ = time_steps(lambda: step(gated=True), 5, 20)
+        g_bytes = algorithmic_bytes(w, esz, n_tokens, n_units, S0 is not None, True, True)
+        result["variants"] = {"gated": {
+            "call": "deltanet_gated_fwd", "steps": 20, "warmup": 5,
+            "ms_per_step": round(g_ms, 5), "tokens_per_s": round(n_tokens / (g_ms / 1e3), 1),
+            "avg_launch_us": round(g_launch_ms * 1e3, 2), "algorithmic_bytes": g_bytes,
+            "hbm_frac": round(g_bytes / (g_launch_ms / 1e3) / PEAK_HBM_BPS, 4),
+            "mfma_frac": round(flops / (g_launch_ms / 1e3) / peak_flops, 4),
+            "vs_ungated_time": round(g_launch_ms / avg_launch_ms, 4)}}
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(inputs, w, w.varlen, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(inputs, w, w.varlen, args.cpu_budget,
+                                              g if args.gated else None)
     print(json.dumps(result), flush=True)
 
 

@@ -106,6 +106,16 @@ __device__ inline bf16x4 tr4(const __bf16 *p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
 }
 __device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
+// Lane I of each group of four lanes, broadcast to the four (DPP quad_perm).
+template <int I> __device__ inline float quad_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x55 * I, 0xF, 0xF, true));
+}
+// Lane group g needs a value of the four tokens base + 4g + i (i = 0..3) in
+// every lane: lane (g, c) computes the one of token base + 4g + c % 4 and the
+// quad spreads them, so each needs one transcendental instead of four.
+__device__ inline f32x4 quad_spread(float x) {
+    return f32x4{quad_bcast<0>(x), quad_bcast<1>(x), quad_bcast<2>(x), quad_bcast<3>(x)};
+}
 __device__ inline f32x4 exp2v(f32x4 x) {
     return f32x4{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]), __builtin_amdgcn_exp2f(x[2]),
                  __builtin_amdgcn_exp2f(x[3])};
@@ -323,13 +333,7 @@ struct VStager {
     // Inclusive prefix sum of the chunk's decay logarithms over the lanes
     // (token l in lane l), in base-2 units; tokens past the end add nothing.
     template <int B> __device__ inline void write_gate(float *Gs) const {
-        float x = lane < nb[B] ? rg[B] * 1.44269504088896340736f : 0.f;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float y = __shfl_up(x, d, 64);
-            if (lane >= d) x += y;
-        }
-        Gs[lane] = x;
+        Gs[lane] = wave_inclusive_sum(lane < nb[B] ? rg[B] * 1.44269504088896340736f : 0.f, lane);
     }
 };
 
@@ -493,19 +497,24 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
 #pragma unroll
         for (int t = 0; t < 4; ++t) vf[t] = bf16x4{};
     }
-    // Gated: prefix sums of the tokens this lane's accumulators touch:
-    // gv[t][e] of token 16t + 4g + e (rows of Y and Z), gq[t] of token
-    // 16t + c (columns of O), gC of the chunk's last token.
-    f32x4 gv[4];
-    float gq[4], gC = 0.f;
+    // Gated: decay factors of the tokens this lane's accumulators touch,
+    // formed before the chain so that none of them waits on a product:
+    // eg[t][e] = exp(gamma) and ez[t][e] = exp(gamma_C - gamma) of token
+    // 16t + 4g + e (rows of Y and Z), eq[t] = exp(gamma) of token 16t + c
+    // (columns of O), eC = exp(gamma_C).
+    f32x4 eg[4], ez[4];
+    float eq[4], eC = 1.f;
     if constexpr (GATED) {
         const float *Gs = bf.G(r);
+        const float gC = Gs[kChunk - 1];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            gv[t] = *reinterpret_cast<const f32x4 *>(Gs + 16 * t + 4 * g);
-            gq[t] = Gs[16 * t + c16];
+            const float gq = Gs[16 * t + 4 * g + (c16 & 3)];
+            eg[t] = quad_spread(__builtin_amdgcn_exp2f(gq));
+            ez[t] = quad_spread(__builtin_amdgcn_exp2f(gC - gq));
+            eq[t] = __builtin_amdgcn_exp2f(Gs[16 * t + c16]);
         }
-        gC = Gs[kChunk - 1];
+        eC = __builtin_amdgcn_exp2f(gC);
     }
     static_for<0, D>([&](auto ic) { buf[ic.value] = chain_fetch<DK, WO>(ic.value, src, lane, g, c16); });
     // SB_s slots = dk 32 s + 8 g + 0..7: tiles (2s, 2s+1) hold the low / high
@@ -517,7 +526,6 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
         SB[s] = odd ? cat8(hi, lo) : cat8(lo, hi);
     }
     if constexpr (GATED) { // the decayed state the update adds to
-        const float eC = __builtin_amdgcn_exp2f(gC);
 #pragma unroll
         for (int m = 0; m < CS::NMT; ++m) Sacc[m] *= eC;
     }
@@ -536,7 +544,7 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
         if constexpr (i == CS::bZ) {
             if constexpr (GATED) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) Y[t] = widen4(vf[t]) + exp2v(gv[t]) * Y[t];
+                for (int t = 0; t < 4; ++t) Y[t] = widen4(vf[t]) + eg[t] * Y[t];
             }
             YB[0] = cvt8(Y[0], Y[1]);
             YB[1] = cvt8(Y[2], Y[3]);
@@ -547,7 +555,7 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
             if constexpr (GATED) { // rows of Z scaled by exp(gamma_C - gamma_l) for the update
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    ZS[s] = cvt8(Z[2 * s] * exp2v(gC - gv[2 * s]), Z[2 * s + 1] * exp2v(gC - gv[2 * s + 1]));
+                    ZS[s] = cvt8(Z[2 * s] * ez[2 * s], Z[2 * s + 1] * ez[2 * s + 1]);
             }
         }
         fence();
@@ -558,7 +566,7 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
         if constexpr (k == CS::kOp) {
             // gated: the Q S^T part of O tile t is complete; scale its token
             // columns before the first P Z product of the tile
-            if constexpr (GATED && CS::tS(j) == 0) O[CS::tT(j)] *= __builtin_amdgcn_exp2f(gq[CS::tT(j)]);
+            if constexpr (GATED && CS::tS(j) == 0) O[CS::tT(j)] *= eq[CS::tT(j)];
             O[CS::tT(j)] = mfma32(ZB[CS::tS(j)], f, O[CS::tT(j)]);
         }
         if constexpr (k == CS::kS) Sacc[j / 2] = mfma32(f, GATED ? ZS[j % 2] : ZB[j % 2], Sacc[j / 2]);
@@ -638,17 +646,22 @@ template <int DK, bool GATED> __device__ inline void gram_tiles(const WsBufs<DK>
     // row factors of A_ac: beta of row token 16a + j, times the decay when gated
     f32x4 s10 = {b1, b1, b1, b1}, s20 = {b2, b2, b2, b2}, s21 = s20, s30 = {b3, b3, b3, b3}, s31 = s30, s32 = s30;
     if constexpr (GATED) {
+        // exp(gamma_l - gamma_i) = exp(gamma_l - E_c) exp(E_c - gamma_i), with E_c
+        // the prefix sum at the end of column block c: row token l lies after
+        // it and column token i in it, so both factors lie in (0, 1]
         const float *Gs = bf.G(c);
         const float g1 = Gs[16 + c16], g2 = Gs[32 + c16], g3 = Gs[48 + c16];
-        const f32x4 h0 = *reinterpret_cast<const f32x4 *>(Gs + 4 * g);
-        const f32x4 h1 = *reinterpret_cast<const f32x4 *>(Gs + 16 + 4 * g);
-        const f32x4 h2 = *reinterpret_cast<const f32x4 *>(Gs + 32 + 4 * g);
-        s10 *= exp2v(g1 - h0);
-        s20 *= exp2v(g2 - h0);
-        s21 *= exp2v(g2 - h1);
-        s30 *= exp2v(g3 - h0);
-        s31 *= exp2v(g3 - h1);
-        s32 *= exp2v(g3 - h2);
+        const float E0 = Gs[15], E1 = Gs[31], E2 = Gs[47];
+        const int q = 4 * g + (c16 & 3);
+        const f32x4 h0 = quad_spread(__builtin_amdgcn_exp2f(E0 - Gs[q]));
+        const f32x4 h1 = quad_spread(__builtin_amdgcn_exp2f(E1 - Gs[16 + q]));
+        const f32x4 h2 = quad_spread(__builtin_amdgcn_exp2f(E2 - Gs[32 + q]));
+        s10 *= __builtin_amdgcn_exp2f(g1 - E0) * h0;
+        s20 *= __builtin_amdgcn_exp2f(g2 - E0) * h0;
+        s21 *= __builtin_amdgcn_exp2f(g2 - E1) * h1;
+        s30 *= __builtin_amdgcn_exp2f(g3 - E0) * h0;
+        s31 *= __builtin_amdgcn_exp2f(g3 - E1) * h1;
+        s32 *= __builtin_amdgcn_exp2f(g3 - E2) * h2;
     }
     __bf16 *As = bf.A(c) + 4 * lane;
     // dot_tile(K_c, K_a)[i] = k_{16c+4g+i} . k_{16a+j} = G[16a + j][16c + 4g + i]
@@ -763,8 +776,16 @@ __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c,
         const int qi = half ? pa - 1 : (pa == 3 ? 1 : 0);
         // acc[e] = k_{16pc+4g+e} . q_{16pa+c} = P[16pa + c][16pc + 4g + e]
         f32x4 acc = dot_tile<DK>(k.f[pc], q.f[B][qi]);
-        if constexpr (GATED) // masked entries (diagonal tiles) are replaced below
-            acc *= exp2v(Gs[16 * pa + c16] - *reinterpret_cast<const f32x4 *>(Gs + 16 * pc + 4 * g));
+        if constexpr (GATED) {
+            const float gl = Gs[16 * pa + c16];
+            if (pa == pc) { // masked entries are replaced below
+                acc *= exp2v(gl - *reinterpret_cast<const f32x4 *>(Gs + 16 * pc + 4 * g));
+            } else { // split at the end of column block pc, as for the Gram tiles
+                const float E = Gs[16 * pc + 15];
+                acc *= __builtin_amdgcn_exp2f(gl - E) *
+                       quad_spread(__builtin_amdgcn_exp2f(E - Gs[16 * pc + 4 * g + (c16 & 3)]));
+            }
+        }
         if (pa == pc) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e > c16) ? 0.f : acc[e];

@@ -86,4 +86,25 @@ template <int DK, int DV> __device__ inline Work decode_work(const ChainArgs &a)
     return wk;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (lane l gets the sum of
+// lanes 0..l): a scan inside each 16-lane row with DPP row shifts (lanes
+// shifted in from outside the row read 0), then the totals of the rows below
+// added from lanes 15, 31 and 47. Every lane of the wave must be active.
+__device__ inline float wave_inclusive_sum(float x, int lane) {
+    const int zero = 0;
+#define DN_ROW_SHR(N)                                                                                          \
+    x += __builtin_bit_cast(                                                                                   \
+        float, __builtin_amdgcn_update_dpp(zero, __builtin_bit_cast(int, x), 0x110 + (N), 0xF, 0xF, false))
+    DN_ROW_SHR(1);
+    DN_ROW_SHR(2);
+    DN_ROW_SHR(4);
+    DN_ROW_SHR(8);
+#undef DN_ROW_SHR
+    const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+    const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+    const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+    const int row = lane >> 4;
+    return x + (row == 0 ? 0.f : row == 1 ? t0 : row == 2 ? t0 + t1 : t0 + t1 + t2);
+}
+
 } // namespace dn

@@ -548,13 +548,7 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
         if (gg) {
             // inclusive prefix sum over the chunk's tokens (lane l = token l), in
             // base-2 units; tokens past the end add nothing
-            float x = l < nval ? rg * 1.44269504088896340736f : 0.f;
-#pragma unroll
-            for (int d = 1; d < kChunk; d <<= 1) {
-                const float y = __shfl_up(x, d, kChunk);
-                if (l >= d) x += y;
-            }
-            Gs[l] = x;
+            Gs[l] = wave_inclusive_sum(l < nval ? rg * 1.44269504088896340736f : 0.f, l);
         }
     }
     __device__ inline void store_v(E *Vs) const {
