@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 matrix-core peak
 PEAK_FP32_FLOPS = 157.3e12  # MI355X dense fp32 matrix-core peak
 PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chain_layer_b8_h16_t4096.json")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRCS = [os.path.join(ROOT, "chunkwise_delta_rule_amd", "csrc", f)
                for f in ("chain_bf16.hip", "dn_work.h", "dn_internal.h")]
 
@@ -86,13 +86,14 @@ def time_steps(step, warmup, steps):
     return starts[0].elapsed_time(ends[-1]) / steps, sum(per_step_ms) / len(per_step_ms), wall
 
 
-def load_traffic(workload_name, launch_bytes):
+def load_traffic(workload_name, gated=False):
     """HBM traffic from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source for this workload; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = os.path.join(PROFILES, f"traffic_chain{'_gated' if gated else ''}_{workload_name}.json")
+    if not os.path.exists(path):
         return None
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(path))
     except Exception:
         return None
     if t.get("kernel_source_sha") != kernel_sha() or t.get("workload") != workload_name:
@@ -261,7 +262,7 @@ def main():
     # parallelism the step holds three launches and the events cover all of
     # them, so the figure is then a whole-step rate.
     achieved_gbps = nbytes / (avg_launch_ms / 1e3) / 1e9
-    traffic = load_traffic(w.name, nbytes) if groups == 1 and not args.gated else None
+    traffic = load_traffic(w.name, args.gated) if groups == 1 else None
     kname = ("chain_kernel_ws<128,128,out,gated>" if args.gated else "chain_kernel_ws<128,128,out>") \
         if w.dtype == "bf16" and w.dk == 128 and w.dv == 128 else "chain_kernel"
     roofline = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_BPS / 1e9,
