@@ -12,6 +12,8 @@ events on the launch stream) and the fp64 CPU oracle's throughput on the
 host cores. ``--gated`` measures Gated DeltaNet (``deltanet_gated_fwd``, with
 per-token log decays) instead; without it, a short gated run of the same
 workload is reported under ``variants.gated`` next to the headline figures.
+``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
+head, state updated in place) on B=256 H=16 d=128 bf16, a 256 MiB state.
 
 Accounting (per head-token, chunk C, key/value widths dk/dv):
   flops  F = 2C(3dk + 2dv) + 6 dk dv  -- the eight dense products of the
@@ -154,6 +156,34 @@ def cpu_baseline(inputs, w, varlen, budget_s, g=None):
             "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
 
 
+def decode_variant(dev, B=256, H=16, d=128, steps=50, warmup=10):
+    """Time deltanet_decode_step (with and without decay) on a B x H state of
+    d x d fp32 in place; bytes = the state read and written plus the token's
+    vectors (q, k, v, o, beta, g)."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import make_gates, make_inputs
+
+    print(f"[bench] decode variant B={B} H={H} d={d}", file=sys.stderr, flush=True)
+    q, k, v, beta, S = make_inputs(B, H, 1, d, d, seed=5, device=str(dev), s0_std=0.1)
+    q, k, v, beta = (x[:, 0].contiguous() for x in (q, k, v, beta))
+    g = make_gates((B, H), seed=5, device=str(dev))
+    o = torch.empty_like(v)
+    out = {"call": "deltanet_decode_step", "config": {"B": B, "H": H, "dk": d, "dv": d, "dtype": "bf16"},
+           "steps": steps, "warmup": warmup}
+    for name, gg in (("plain", None), ("gated", g)):
+        ms, launch_ms, _ = time_steps(lambda: dn.deltanet_decode_step(q, k, v, beta, S, gg, o=o), warmup, steps)
+        nbytes = B * H * (2 * d * d * 4 + 2 * (2 * d + 2 * d + 1) + (4 if gg is not None else 0))
+        out[name] = {"ms_per_step": round(ms, 5), "avg_launch_us": round(launch_ms * 1e3, 2),
+                     "tokens_per_s": round(B / (ms / 1e3), 1), "algorithmic_bytes": nbytes,
+                     "achieved_GBps": round(nbytes / (launch_ms / 1e3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4)}
+    if not bool(torch.isfinite(S).all()):
+        print("bench.py: non-finite decode state", file=sys.stderr)
+        sys.exit(3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,7 +199,7 @@ def main():
     ap.add_argument("--gated", action="store_true",
                     help="measure Gated DeltaNet (per-token log decays) instead of DeltaNet")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the short gated run reported under variants.gated")
+                    help="skip the short gated and decode runs reported under variants")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 1 GiB (for counter calibration)")
     args = ap.parse_args()
@@ -304,6 +334,8 @@ def main():
             "hbm_frac": round(g_bytes / (g_launch_ms / 1e3) / PEAK_HBM_BPS, 4),
             "mfma_frac": round(flops / (g_launch_ms / 1e3) / peak_flops, 4),
             "vs_ungated_time": round(g_launch_ms / avg_launch_ms, 4)}}
+    if not args.gated and not args.no_variants:
+        result.setdefault("variants", {})["decode"] = decode_variant(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inputs, w, w.varlen, args.cpu_budget,

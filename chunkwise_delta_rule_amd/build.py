@@ -3,7 +3,8 @@
     python -m chunkwise_delta_rule_amd.build
 
 The library is the C-ABI declared in ``include/deltanet.h``: the host layer
-(``csrc/api.cpp``) and the kernels (``csrc/kernels.hip``), compiled for gfx950
+(``csrc/api.cpp``) and the kernels (``csrc/kernels.hip``, ``csrc/chain_bf16.hip``,
+``csrc/decode.hip``), compiled for gfx950
 only. Packed-fp32 VALU instructions are switched off for all device code.
 """
 
@@ -17,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libdeltanet.so")
 SOURCES = [os.path.join(PKG, "csrc", "kernels.hip"), os.path.join(PKG, "csrc", "chain_bf16.hip"),
-           os.path.join(PKG, "csrc", "api.cpp")]
+           os.path.join(PKG, "csrc", "decode.hip"), os.path.join(PKG, "csrc", "api.cpp")]
 HEADERS = [os.path.join(PKG, "csrc", "dn_internal.h"), os.path.join(PKG, "csrc", "dn_work.h"),
            os.path.join(ROOT, "include", "deltanet.h")]
 ARCH = "gfx950"

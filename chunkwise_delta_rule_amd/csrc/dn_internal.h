@@ -43,6 +43,21 @@ struct ChainArgs {
     int n_tiles; // 64-row state tiles per unit
 };
 
+// One decode step: a single token per unit applied to the state in place.
+// q, k: [n_units, dk]; v, o: [n_units, dv]; beta, g: [n_units]; S: [n_units, dv, dk].
+struct DecodeArgs {
+    const void *q, *k, *v, *beta;
+    const float *g; // log decays, or nullptr (no decay)
+    float *S;
+    void *o;
+    int n_units;
+    int dv;
+};
+
+// Enqueue the decode kernel for dtype (0 = fp32, 1 = bf16) and dk (dv is in
+// the arguments; dk, dv in {64, 128}). grid = n_units * dv / 64 workgroups.
+hipError_t launch_decode(int dtype, int dk, const DecodeArgs &a, hipStream_t stream);
+
 // Enqueue the chunk-chain kernel for dtype (0 = fp32, 1 = bf16) and (dk, dv).
 // grid = n_units * n_tiles workgroups of kThreads threads.
 hipError_t launch_chain(int dtype, int dk, int dv, bool write_o, const ChainArgs &a,

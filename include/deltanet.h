@@ -158,6 +158,24 @@ int deltanet_gated_fwd_varlen(const void *q, const void *k, const void *v, const
                               hipStream_t stream);
 
 /*
+ * One decode step: one new token per (sequence, head) applied to a state held
+ * in HBM, in place ("Linear Attention, Visualized": DeltaNet > "Recurrent
+ * form", one step of the recurrence above; with g, one step of "Gated
+ * DeltaNet (GDN)"). For each unit u = (b, h):
+ *     S[u] <- a S[u] (I - beta k k^T) + beta v k^T,   o = S[u] q   (a = exp(g); 1 if g is NULL)
+ *   q, k : [B, H, dk]   v, o : [B, H, dv]   beta : [B, H]   (element type dtype)
+ *   g    : [B, H] float32 log decays, or NULL for DeltaNet
+ *   S    : [B, H, dv, dk] float32, read and overwritten (e.g. the S_final of a
+ *          forward pass, which continues exactly from there)
+ * dk, dv in {64, 128} for both dtypes. Alignment: q and k to 4 elements, S to
+ * 16 bytes, the others to their element size. o must not overlap S or the
+ * inputs. Errors as in deltanet_fwd. No workspace.
+ */
+int deltanet_decode_step(const void *q, const void *k, const void *v, const void *beta,
+                         const float *g, float *S, void *o, int B, int H, int dk, int dv,
+                         int dtype, hipStream_t stream);
+
+/*
  * Bytes of workspace deltanet_fwd (or deltanet_gated_fwd) needs for this
  * shape and cp_groups (0 means the library's choice on the current device).
  * Returns 0 when the resolved group count is 1, and also for invalid shapes.

@@ -30,7 +30,8 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd",
-                          "deltanet_gated_fwd_varlen", "deltanet_workspace_bytes",
+                          "deltanet_gated_fwd_varlen", "deltanet_decode_step",
+                          "deltanet_workspace_bytes",
                           "deltanet_pick_cp_groups", "deltanet_status_string"}
     raw = ctypes.CDLL(dn.library_path())
     for n in names:
@@ -156,6 +157,27 @@ def test_gated_varlen_rejects_bad_arguments(lib, kw, status):
     st = lib.deltanet_gated_fwd_varlen(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
                                        vp(a["g"]) if a["g"] else None, None, vp(FAKE), None,
                                        vp(FAKE), None, a["N"], 100, 2, 64, 64, a["chunk"], 1, None)
+    assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), DN_ERR_INVALID),
+    (dict(dk=96), DN_ERR_UNSUPPORTED),
+    (dict(dv=32), DN_ERR_UNSUPPORTED),
+    (dict(dtype=3), DN_ERR_INVALID),
+    (dict(S=None), DN_ERR_INVALID),
+    (dict(S=FAKE + 8), DN_ERR_INVALID),
+    (dict(q=FAKE + 2), DN_ERR_INVALID),
+    (dict(g=FAKE + 2), DN_ERR_INVALID),
+    (dict(o=None), DN_ERR_INVALID),
+])
+def test_decode_step_rejects_bad_arguments(lib, kw, status):
+    a = dict(q=FAKE, g=None, S=FAKE, o=FAKE, B=2, H=2, dk=128, dv=128, dtype=1)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    st = lib.deltanet_decode_step(vp(a["q"]), vp(FAKE), vp(FAKE), vp(FAKE), vp(a["g"]) if a["g"] else None,
+                                  vp(a["S"]) if a["S"] else None, vp(a["o"]) if a["o"] else None,
+                                  a["B"], a["H"], a["dk"], a["dv"], a["dtype"], None)
     assert st == status
 
 

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import chunkwise_delta_rule_amd as dn
-from chunkwise_delta_rule_amd.synth import WORKLOADS, workload_inputs
+from chunkwise_delta_rule_amd.synth import WORKLOADS, make_gates, workload_inputs
 from helpers import TOL, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -131,4 +131,40 @@ def test_varlen_n64_h32_sampled():
     es = rel_err(np.stack(gs), np.stack(rs))
     print(f"  varlen: sampled units {list(zip(seqs, heads))} lengths {[int(lens[n]) for n in seqs]} "
           f"err o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_gated_layer_b8_h16_t4096_sampled():
+    # Gated DeltaNet at the benchmark's full shape and launch configuration
+    w = WORKLOADS["layer_b8_h16_t4096"]
+    print(f"[case] {w.name} full size, gated", flush=True)
+    q, k, v, beta, S0 = workload_inputs(w, seed=2, device=DEV)
+    g = make_gates((w.B, w.T, w.H), seed=2, device=DEV)
+    o, Sf = dn.deltanet_gated_fwd(q, k, v, beta, g, S0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(Sf).all())
+    units = [(0, 0), (2, 9), (6, 15)]
+    sel = lambda x, b, h: f64(x[b:b + 1, :, h:h + 1])
+    cat = lambda xs: np.concatenate(xs, axis=0)
+    ro, rs = oracle.gated_deltanet_fwd(*(cat([sel(x, b, h) for b, h in units]) for x in (q, k, v, beta, g)))
+    eo = rel_err(np.stack([f64(o[b, :, h]) for b, h in units]), ro[:, :, 0])
+    es = rel_err(np.stack([f64(Sf[b, h]) for b, h in units]), rs[:, 0])
+    print(f"  gated {w.name}: sampled {len(units)} units, err o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= TOL[q.dtype] and es <= TOL[q.dtype]
+
+
+def test_gated_long_context_parallel_sampled():
+    w = WORKLOADS["long_b1_h16_t131072"]
+    print(f"[case] {w.name} full size, gated, cp auto", flush=True)
+    q, k, v, beta, S0 = workload_inputs(w, seed=4, device=DEV)
+    g = make_gates((w.B, w.T, w.H), seed=4, device=DEV)
+    o, Sf = dn.deltanet_gated_fwd(q, k, v, beta, g, S0, cp_groups=0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(Sf).all())
+    h = 6
+    sel = lambda x: f64(x[:, :, h:h + 1])
+    ro, rs = oracle.gated_deltanet_fwd(sel(q), sel(k), sel(v), sel(beta), sel(g))
+    eo = rel_err(f64(o[0, :, h]), ro[0, :, 0])
+    es = rel_err(f64(Sf[0, h]), rs[0, 0])
+    print(f"  gated {w.name} head {h}: err o={eo:.3e} S={es:.3e}", flush=True)
     assert eo <= 2e-2 and es <= 2e-2
