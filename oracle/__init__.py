@@ -33,6 +33,9 @@ by Haoran Zhang, "p1" is "Context Parallelism for DeltaNet" by yywangcs):
   correction); ``gated_chunked_fwd`` -- that section's "Complete per-chunk
   algorithm"; ``householder_states``, ``exact_states`` and
   ``cp_group_transition`` take the decays as an optional argument.
+* ``gdp_fwd`` -- Gated Delta Product token by token with its substeps (p3
+  "Gated Delta Product (GDP)"); ``gdp_virtual_sequence`` -- the mapping of p3
+  "GDP as GDN over a virtual sequence".
 
 Convention (p1 section 2): the state S is dv x dk and acts on column vectors:
 S_t = S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t. The
@@ -220,6 +223,60 @@ def gated_deltanet_fwd_varlen(q, k, v, beta, g, cu_seqlens, S0=None, nthreads: i
     if rc != 0:
         raise RuntimeError(f"oracle_gated_deltanet_fwd_varlen failed with {rc}")
     return o, Sf
+
+
+def gdp_fwd(q, k, v, beta, g, n_h, S0=None):
+    """Gated Delta Product forward, fp64, token by token (numpy; small cases).
+
+    p3 "Gated Delta Product (GDP)": for each real token t, the previous state
+    decays once, S_{t,0} = a_t S_{t-1} (a_t = exp(g_t)); then n_h generalized
+    Householder substeps follow in order, S_{t,j} = S_{t,j-1}(I - b_{t,j}
+    k_{t,j} k_{t,j}^T) + b_{t,j} v_{t,j} k_{t,j}^T (state transposed, p1
+    section 2); the query reads the state after the last substep,
+    o_t = S_{t,n_h} q_t.
+
+    q: [B,T,H,dk]; k: [B,T,n_h,H,dk]; v: [B,T,n_h,H,dv]; beta: [B,T,n_h,H];
+    g: [B,T,H]; S0: [B,H,dv,dk] or None. Returns (o [B,T,H,dv], S_final).
+    """
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, T, n_h, H, dk) and v.shape == (B, T, n_h, H, dv)
+    assert beta.shape == (B, T, n_h, H) and g.shape == (B, T, H)
+    o = np.zeros((B, T, H, dv))
+    Sf = np.zeros((B, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dv, dk)) if S0 is None else _f64(S0)[b, h].copy()
+            for t in range(T):
+                S = np.exp(g[b, t, h]) * S
+                for j in range(n_h):
+                    kk, vv, bb = k[b, t, j, h], v[b, t, j, h], beta[b, t, j, h]
+                    S = S - bb * np.outer(S @ kk, kk) + bb * np.outer(vv, kk)
+                o[b, t, h] = S @ q[b, t, h]
+            Sf[b, h] = S
+    return o, Sf
+
+
+def gdp_virtual_sequence(q, k, v, beta, g, n_h):
+    """The virtual sequence of p3 "GDP as GDN over a virtual sequence".
+
+    Real token t and substep j become virtual step m = n_h t + j (0-based):
+    k, v, beta move over unchanged; the decay sits on the first substep
+    (g = g_t for j = 0, else 0, i.e. a = 1); the query sits on the last
+    (q_t for j = n_h - 1, else zero). Returns q, k, v, beta, g of shapes
+    [B, T n_h, H, *].
+    """
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    qv = np.zeros((B, T, n_h, H, dk))
+    qv[:, :, n_h - 1] = q
+    gv = np.zeros((B, T, n_h, H))
+    gv[:, :, 0] = g
+    Tv = T * n_h
+    return (qv.reshape(B, Tv, H, dk), k.reshape(B, Tv, H, dk), v.reshape(B, Tv, H, dv),
+            beta.reshape(B, Tv, H), gv.reshape(B, Tv, H))
 
 
 # ---------------------------------------------------------------------------

@@ -642,6 +642,61 @@ def test_gated_cp_composition(groups):
         assert _rel(starts[gi], St[0, 0]) < 1e-11
 
 
+# ---- Gated Delta Product (p3 "Gated Delta Product (GDP)")
+
+def _gdp_inputs(rng, B=2, T=7, H=2, n_h=3, dk=5, dv=4):
+    q = _unit_rows(rng, (B, T, H, dk))
+    k = _unit_rows(rng, (B, T, n_h, H, dk))
+    v = rng.standard_normal((B, T, n_h, H, dv))
+    beta = rng.uniform(size=(B, T, n_h, H))
+    g = _gates(rng, (B, T, H))
+    S0 = rng.standard_normal((B, H, dv, dk)) * 0.3
+    return q, k, v, beta, g, S0
+
+
+def test_gdp_with_one_substep_is_gated_deltanet():
+    rng = np.random.default_rng(60)
+    q, k, v, beta, g, S0 = _gdp_inputs(rng, n_h=1)
+    o, Sf = oracle.gdp_fwd(q, k, v, beta, g, 1, S0)
+    ro, rs = oracle.gated_deltanet_fwd(q, k[:, :, 0], v[:, :, 0], beta[:, :, 0], g, S0)
+    assert _rel(o, ro) < RTOL and _rel(Sf, rs) < RTOL
+
+
+def test_gdp_single_token_closed_form():
+    # one token, two substeps: S1 = A2 (A1 (a S0) ...) written out with the transitions
+    rng = np.random.default_rng(61)
+    q, k, v, beta, g, S0 = _gdp_inputs(rng, B=1, T=1, H=1, n_h=2)
+    o, Sf = oracle.gdp_fwd(q, k, v, beta, g, 2, S0)
+    a = np.exp(g[0, 0, 0])
+    A = [np.eye(5) - beta[0, 0, j, 0] * np.outer(k[0, 0, j, 0], k[0, 0, j, 0]) for j in range(2)]
+    X = [beta[0, 0, j, 0] * np.outer(v[0, 0, j, 0], k[0, 0, j, 0]) for j in range(2)]
+    S = (a * S0[0, 0] @ A[0] + X[0]) @ A[1] + X[1]
+    assert _rel(Sf[0, 0], S) < RTOL and _rel(o[0, 0, 0], S @ q[0, 0, 0]) < RTOL
+
+
+def test_gdp_decay_applies_once_per_token():
+    # beta = 0: only the decay acts, once per real token whatever n_h is
+    rng = np.random.default_rng(62)
+    q, k, v, beta, g, S0 = _gdp_inputs(rng, T=6, n_h=3)
+    beta[:] = 0
+    o, Sf = oracle.gdp_fwd(q, k, v, beta, g, 3, S0)
+    lam = np.exp(np.cumsum(g, axis=1))
+    assert _rel(Sf, lam[:, -1, :, None, None] * S0) < RTOL
+    assert _rel(o, lam[..., None] * np.einsum("bhij,bthj->bthi", S0, q)) < RTOL
+
+
+@pytest.mark.parametrize("n_h", [2, 3])
+def test_gdp_equals_gated_deltanet_over_the_virtual_sequence(n_h):
+    # p3 "GDP as GDN over a virtual sequence": the substep definition and the
+    # token-serial gated oracle over the virtual sequence agree
+    rng = np.random.default_rng(63 + n_h)
+    q, k, v, beta, g, S0 = _gdp_inputs(rng, T=9, n_h=n_h)
+    o, Sf = oracle.gdp_fwd(q, k, v, beta, g, n_h, S0)
+    vq, vk, vv, vb, vg = oracle.gdp_virtual_sequence(q, k, v, beta, g, n_h)
+    ov, sv = oracle.gated_deltanet_fwd(vq, vk, vv, vb, vg, S0)
+    assert _rel(ov[:, n_h - 1::n_h], o) < 1e-12 and _rel(sv, Sf) < 1e-12
+
+
 def test_oracle_threads_do_not_change_results():
     rng = np.random.default_rng(50)
     q, k, v, beta, S0 = _inputs(rng, B=3, T=33, H=5)
