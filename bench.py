@@ -12,7 +12,8 @@ events on the launch stream) and the fp64 CPU oracle's throughput on the
 host cores. ``--gated`` measures Gated DeltaNet (``deltanet_gated_fwd``, with
 per-token log decays) instead; without it, a short gated run of the same
 workload is reported under ``variants.gated`` next to the headline figures.
-``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
+``variants.gdp`` times ``deltanet_gdp_fwd`` (Gated Delta Product, n_h = 2 substeps
+per token) on the same B, H, T and widths. ``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
 head, state updated in place) on B=256 H=16 d=128 bf16, a 256 MiB state.
 
 Accounting (per head-token, chunk C, key/value widths dk/dv):
@@ -154,6 +155,34 @@ def cpu_baseline(inputs, w, varlen, budget_s, g=None):
         units = nb * w.H
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(min(threads, units)),
             "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+
+
+def gdp_variant(dev, w, flops_per_head_step, peak_flops, nh=2, steps=20, warmup=5):
+    """Time deltanet_gdp_fwd with nh substeps per token on the workload's B, H,
+    T (real tokens) and widths: the chunkwise path runs over T nh virtual
+    steps. Bytes: q, g, o per real token; k, v, beta per substep."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import make_gates, make_inputs
+
+    print(f"[bench] gdp variant n_h={nh}", file=sys.stderr, flush=True)
+    B, H, T = w.B, w.H, w.T
+    q, _, _, _, _ = make_inputs(B, H, T, w.dk, w.dv, seed=6, device=str(dev))
+    _, k, v, beta, _ = make_inputs(B, H, T * nh, w.dk, w.dv, seed=7, device=str(dev))
+    k, v, beta = k.view(B, T, nh, H, w.dk), v.view(B, T, nh, H, w.dv), beta.view(B, T, nh, H)
+    g = make_gates((B, T, H), seed=6, device=str(dev))
+    o = torch.empty((B, T, H, w.dv), dtype=q.dtype, device=dev)
+    Sf = torch.empty((B, H, w.dv, w.dk), dtype=torch.float32, device=dev)
+    ms, launch_ms, _ = time_steps(lambda: dn.deltanet_gdp_fwd(q, k, v, beta, g, None, o=o, S_final=Sf),
+                                  warmup, steps)
+    nbytes = B * T * H * (2 * (w.dk + w.dv) + 4 + nh * 2 * (w.dk + w.dv + 1)) + B * H * w.dv * w.dk * 4
+    flops = B * T * nh * H * flops_per_head_step
+    return {"call": "deltanet_gdp_fwd", "n_h": nh, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(B * T / (ms / 1e3), 1),
+            "virtual_steps_per_s": round(B * T * nh / (ms / 1e3), 1),
+            "avg_launch_us": round(launch_ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            "hbm_frac": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4),
+            "mfma_frac": round(flops / (launch_ms / 1e3) / peak_flops, 4)}
 
 
 def decode_variant(dev, B=256, H=16, d=128, steps=50, warmup=10):
@@ -334,6 +363,8 @@ def main():
             "hbm_frac": round(g_bytes / (g_launch_ms / 1e3) / PEAK_HBM_BPS, 4),
             "mfma_frac": round(flops / (g_launch_ms / 1e3) / peak_flops, 4),
             "vs_ungated_time": round(g_launch_ms / avg_launch_ms, 4)}}
+    if not args.gated and not args.no_variants and not w.varlen and w.dtype == "bf16":
+        result.setdefault("variants", {})["gdp"] = gdp_variant(dev, w, flops / n_tokens / w.H, peak_flops)
     if not args.gated and not args.no_variants:
         result.setdefault("variants", {})["decode"] = decode_variant(dev)
     if not args.no_cpu_baseline:

@@ -25,7 +25,7 @@ import os
 import torch
 
 __all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
-           "deltanet_decode_step", "deltanet_workspace_bytes",
+           "deltanet_gdp_fwd", "deltanet_decode_step", "deltanet_workspace_bytes",
            "deltanet_pick_cp_groups", "deltanet_status_string", "longest_first_order",
            "library_path", "load_library", "DeltaNetError", "DN_F32", "DN_BF16"]
 
@@ -68,6 +68,8 @@ def load_library(path: str | None = None):
     lib.deltanet_gated_fwd.restype = i
     lib.deltanet_gated_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.deltanet_gated_fwd_varlen.restype = i
+    lib.deltanet_gdp_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.deltanet_gdp_fwd.restype = i
     lib.deltanet_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.deltanet_decode_step.restype = i
     lib.deltanet_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
@@ -199,6 +201,49 @@ def longest_first_order(cu_seqlens) -> torch.Tensor:
     lens = cu[1:] - cu[:-1]
     order = sorted(range(lens.numel()), key=lambda n: (-int(lens[n]), n))
     return torch.tensor(order, dtype=torch.int32, device=cu_seqlens.device)
+
+
+def deltanet_gdp_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64, cp_groups: int = 1, o=None,
+                     S_final=None, output_final_state: bool = True, workspace=None, stream=None):
+    """Gated Delta Product forward (C-ABI ``deltanet_gdp_fwd``).
+
+    q: [B,T,H,dk]; k: [B,T,n_h,H,dk]; v: [B,T,n_h,H,dv]; beta: [B,T,n_h,H];
+    g: [B,T,H] float32 log decays; S0: [B,H,dv,dk] fp32 or None. Returns
+    (o [B,T,H,dv], S_final).
+    """
+    lib = load_library()
+    if k.dim() != 5:
+        raise ValueError("k must be [B, T, n_h, H, dk]")
+    B, T, nh, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check(q, "q", dt, dev, (B, T, H, dk))
+    _check(k, "k", dt, dev, (B, T, nh, H, dk))
+    _check(v, "v", dt, dev, (B, T, nh, H, dv))
+    _check(beta, "beta", dt, dev, (B, T, nh, H))
+    _check(g, "g", torch.float32, dev, (B, T, H))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(o, "o", dt, dev, (B, T, H, dv))
+    if output_final_state and S_final is None:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _check(S_final, "S_final", torch.float32, dev, (B, H, dv, dk))
+    need = int(lib.deltanet_workspace_bytes(B, H, T * nh, dk, dv, chunk, cp_groups))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.deltanet_gdp_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o),
+                                  _ptr(S_final), B, H, T, nh, dk, dv, chunk, _DTYPE_CODE[dt],
+                                  cp_groups, _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if st != 0:
+        raise DeltaNetError(st, "deltanet_gdp_fwd")
+    return o, S_final
 
 
 def _fwd_varlen(q, k, v, beta, g, cu_seqlens, S0, seq_order, chunk, o, S_final,

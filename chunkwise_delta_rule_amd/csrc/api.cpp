@@ -71,10 +71,12 @@ size_t ws_bytes_for(int B, int H, int dk, int dv, int G) {
     return (size_t)B * H * G * ((size_t)dk * dk + 2 * (size_t)dv * dk) * sizeof(float);
 }
 
-// Dense forward, with (g != nullptr) or without the per-token decay.
+// Dense forward, with (g != nullptr) or without the per-token decay. T counts
+// virtual steps: nh substeps per real token (Gated Delta Product; nh = 1
+// otherwise), so q, g and o hold T / nh real tokens per sequence.
 int fwd_dense(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
-              void *o, float *S_final, int B, int H, int T, int dk, int dv, int chunk, int dtype, int cp_groups,
-              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+              void *o, float *S_final, int B, int H, int T, int nh, int dk, int dv, int chunk, int dtype,
+              int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     int st = check_shape(dk, dv, chunk, dtype);
     if (st != DN_OK) return st;
     if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return DN_ERR_INVALID;
@@ -106,6 +108,7 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
     a.B = B;
     a.H = H;
     a.T = T;
+    a.nh = nh;
     hipError_t err;
     if (G <= 1) {
         a.kind = dn::kDense;
@@ -167,6 +170,7 @@ int fwd_varlen(const void *q, const void *k, const void *v, const void *beta, co
     a.cu_seqlens = cu_seqlens;
     a.seq_order = seq_order;
     a.kind = dn::kVarlen;
+    a.nh = 1;
     a.B = N;
     a.H = H;
     a.T = total_T;
@@ -212,7 +216,7 @@ size_t deltanet_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, 
 int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta, const float *S0,
                  void *o, float *S_final, int B, int H, int T, int dk, int dv, int chunk, int dtype,
                  int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return fwd_dense(q, k, v, beta, nullptr, S0, o, S_final, B, H, T, dk, dv, chunk, dtype, cp_groups, workspace,
+    return fwd_dense(q, k, v, beta, nullptr, S0, o, S_final, B, H, T, 1, dk, dv, chunk, dtype, cp_groups, workspace,
                      workspace_bytes, stream);
 }
 
@@ -229,8 +233,19 @@ int deltanet_gated_fwd(const void *q, const void *k, const void *v, const void *
                        int chunk, int dtype, int cp_groups, void *workspace, size_t workspace_bytes,
                        hipStream_t stream) {
     if (T > 0 && !g) return DN_ERR_INVALID;
-    return fwd_dense(q, k, v, beta, g, S0, o, S_final, B, H, T, dk, dv, chunk, dtype, cp_groups, workspace,
+    return fwd_dense(q, k, v, beta, g, S0, o, S_final, B, H, T, 1, dk, dv, chunk, dtype, cp_groups, workspace,
                      workspace_bytes, stream);
+}
+
+int deltanet_gdp_fwd(const void *q, const void *k, const void *v, const void *beta, const float *g,
+                     const float *S0, void *o, float *S_final, int B, int H, int T, int n_h, int dk,
+                     int dv, int chunk, int dtype, int cp_groups, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    if (n_h <= 0 || T < 0) return DN_ERR_INVALID;
+    if ((int64_t)T * n_h > INT32_MAX / 2) return DN_ERR_UNSUPPORTED;
+    if (T > 0 && !g) return DN_ERR_INVALID;
+    return fwd_dense(q, k, v, beta, g, S0, o, S_final, B, H, T * n_h, n_h, dk, dv, chunk, dtype, cp_groups,
+                     workspace, workspace_bytes, stream);
 }
 
 int deltanet_gated_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,

@@ -275,7 +275,8 @@ template <int DK> struct KStager {
 struct VStager {
     static constexpr int NV = 8;
     const __bf16 *vt, *bt;
-    const float *gt; // log decays, or nullptr
+    const float *gt; // this head's log decays at real token 0, or nullptr
+    SubstepBase sb;  // split of the work's first virtual step
     int64_t sv;
     int H, len, lane, rv0, col;
     bf16x8 r[2][NV];
@@ -319,7 +320,11 @@ struct VStager {
     template <int B> __device__ inline void load_beta(int c) {
         nb[B] = rows_of(len, c);
         rb[B] = bt[((int64_t)c * kChunk + min(lane, nb[B] - 1)) * H];
-        if (gt) rg[B] = gt[((int64_t)c * kChunk + min(lane, nb[B] - 1)) * H];
+        if (gt) { // the decay sits on the first substep of its real token
+            const Substep st = substep_at(sb, (uint32_t)(c * kChunk + min(lane, nb[B] - 1)));
+            const float x = gt[st.t * H];
+            rg[B] = st.j == 0 ? x : 0.f;
+        }
     }
     template <int B> __device__ inline void write_v(__bf16 *Vs) const {
         const bf16x8 z = {};
@@ -374,6 +379,25 @@ template <int DK> struct QStage {
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) st8(Qs + koff<DK>(row[i], 32 * kb + 8 * g), f[B][i][kb]);
+    }
+    // Gated kernels: virtual row M = tok0 + 64 c + row carries the query of
+    // its real token on the last substep and zero on the others (qh: this
+    // head's query at real token 0, dk 8 g).
+    const __bf16 *qh;
+    SubstepBase sb; // split of the work's first virtual step
+    template <int B> __device__ inline void load_virtual(int c) {
+        const int n = min(kChunk, len - c * kChunk);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const Substep st = substep_at(sb, (uint32_t)(c * kChunk + min(row[i], n - 1)));
+            const __bf16 *b = qh + st.t * sqk;
+            const bool keep = st.j == (int)sb.nh - 1;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(b + 32 * kb);
+                f[B][i][kb] = keep ? x : bf16x8{};
+            }
+        }
     }
 };
 
@@ -477,7 +501,8 @@ __device__ inline f32x4 widen4(bf16x4 v) { return f32x4{(float)v[0], (float)v[1]
 
 template <int DK, bool WO, bool GATED>
 __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)[DK / 16], __bf16 *og, int64_t sv,
-                                      int nval, bool has_v, int cw, int lane, int g, int c16) {
+                                      int nval, const SubstepBase &sb, bool has_v, int cw, int lane, int g,
+                                      int c16) {
     using CS = ChainSteps<DK, WO>;
     constexpr int D = CS::depth;
     const ChainSrc<DK, WO> src{bf.K(r), WO ? bf.Q(r) : nullptr, bf.Tt(r), WO ? bf.P(r) : nullptr};
@@ -573,11 +598,19 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
         fence();
     });
     if constexpr (WO) {
-        // O[t][i] = -O[16t + c][row 4g + i] (rows relative to this wave's 16)
+        // O[t][i] = -O[16t + c][row 4g + i] (rows relative to this wave's 16).
+        // Gated kernels: og is the output at real token 0; virtual row
+        // 64 r + tok of the work is stored at its real token on the last
+        // substep only.
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int tok = 16 * t + c16;
-            if (tok < nval) st4(og + (int64_t)tok * sv, cvt4(-O[t]));
+            if constexpr (GATED) {
+                const Substep st = substep_at(sb, (uint32_t)(r * kChunk + tok));
+                if (tok < nval && st.j == (int)sb.nh - 1) st4(og + st.t * sv, cvt4(-O[t]));
+            } else {
+                if (tok < nval) st4(og + (int64_t)tok * sv, cvt4(-O[t]));
+            }
         }
     }
 }
@@ -590,14 +623,17 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     f32x4 Sacc[NMT];
     ws_state_in<DK>(Sacc, wk, cw, g, c16);
     const int64_t sv = (int64_t)a.H * DV;
-    __bf16 *og = WO ? reinterpret_cast<__bf16 *>(a.o) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 + 16 * cw + 4 * g
-                    : nullptr; // only dereferenced with output
+    // only dereferenced with output; gated kernels address real tokens from token 0
+    __bf16 *og = WO ? reinterpret_cast<__bf16 *>(a.o) + (GATED ? 0 : wk.tok0 * sv) + (int64_t)wk.h * DV + wk.row0 +
+                          16 * cw + 4 * g
+                    : nullptr;
 
+    const SubstepBase sb = GATED ? substep_base(wk.tok0, a.nh) : SubstepBase{0, 0u, 1u};
     __syncthreads(); // matches the producers' prologue
     for (int r = -3; r < NC; ++r) {
         if (r >= 0)
-            consumer_chain<DK, WO, GATED>(bf, r, Sacc, WO ? og + (int64_t)r * kChunk * sv : nullptr, sv,
-                                   min(kChunk, wk.len - r * kChunk), has_v, cw, lane, g, c16);
+            consumer_chain<DK, WO, GATED>(bf, r, Sacc, WO ? og + (GATED ? 0 : (int64_t)r * kChunk * sv) : nullptr,
+                                          sv, min(kChunk, wk.len - r * kChunk), sb, has_v, cw, lane, g, c16);
         __syncthreads();
     }
     ws_state_out<DK>(Sacc, wk, cw, g, c16);
@@ -808,16 +844,22 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     KStager<DK> ks;
     VStager vs;
     QStage<DK> q;
-    if constexpr (ROLE == 1)
+    if constexpr (ROLE == 1) {
         vs.init(reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0,
                 reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h,
-                GATED ? a.g + wk.tok0 * a.H + wk.h : nullptr, sv, a.H, wk.len, lane);
+                GATED ? a.g + wk.h : nullptr, sv, a.H, wk.len, lane);
+        if constexpr (GATED) vs.sb = substep_base(wk.tok0, a.nh);
+    }
     if constexpr (ROLE >= 2) {
         ks.init(reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len,
                 64 * (ROLE - 2) + lane);
         if constexpr (WO)
             q.init(reinterpret_cast<const __bf16 *>(a.q) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len, ROLE - 2,
                    g, c16);
+        if constexpr (WO && GATED) {
+            q.qh = reinterpret_cast<const __bf16 *>(a.q) + (int64_t)wk.h * DK + 8 * g;
+            q.sb = substep_base(wk.tok0, a.nh);
+        }
     }
     if (NC > 0) { // K(0), K(1), beta(0), beta(1) are written in the first two iterations
         if constexpr (ROLE >= 2) {
@@ -871,7 +913,12 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
                     p_tiles<DK, S, GATED>(bf, q, r + 1, ROLE - 2, lane, g, c16);
                 }
             }
-            if constexpr (WO) q.template load<S>(min(max(r + 3, 0), last));
+            if constexpr (WO) {
+                if constexpr (GATED)
+                    q.template load_virtual<S>(min(max(r + 3, 0), last));
+                else
+                    q.template load<S>(min(max(r + 3, 0), last));
+            }
         }
         __syncthreads();
     };

@@ -39,6 +39,7 @@ struct ChainArgs {
     int T;       // tokens per sequence (dense / cp)
     int G;       // groups (cp kinds)
     int chunks_per_group;
+    int nh;      // substeps per real token (Gated Delta Product; 1 otherwise, gated kernels only)
     int n_units; // units covered by the grid
     int n_tiles; // 64-row state tiles per unit
 };

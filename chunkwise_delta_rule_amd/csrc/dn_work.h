@@ -86,6 +86,34 @@ template <int DK, int DV> __device__ inline Work decode_work(const ChainArgs &a)
     return wk;
 }
 
+// Gated Delta Product runs as Gated DeltaNet over a virtual sequence of nh
+// substeps per real token ("Linear Attention, Visualized", "GDP as GDN over a
+// virtual sequence"): virtual step M is substep M % nh of real token M / nh.
+// Queries and outputs live at the real tokens (used on the last substep),
+// the decay at the real token (applied on the first substep); keys, values
+// and beta are stored per substep, i.e. already in virtual order.
+// A work item splits its first virtual step once (64-bit) and then locates
+// step first + x with a 32-bit division (x < 2^31 within one sequence).
+struct Substep {
+    int64_t t;
+    int j;
+};
+struct SubstepBase {
+    int64_t t0;  // real token of the first virtual step
+    uint32_t j0; // its substep
+    uint32_t nh;
+};
+__device__ inline SubstepBase substep_base(int64_t first, int nh) {
+    if (nh == 1) return {first, 0u, 1u};
+    const int64_t t = first / nh;
+    return {t, (uint32_t)(first - t * nh), (uint32_t)nh};
+}
+__device__ inline Substep substep_at(const SubstepBase &b, uint32_t x) {
+    if (b.nh == 1) return {b.t0 + x, 0};
+    const uint32_t y = b.j0 + x, d = y / b.nh;
+    return {b.t0 + d, (int)(y - d * b.nh)};
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (lane l gets the sum of
 // lanes 0..l): a scan inside each 16-lane row with DPP row shifts (lanes
 // shifted in from outside the row read 0), then the totals of the rows below

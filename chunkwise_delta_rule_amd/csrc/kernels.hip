@@ -505,6 +505,12 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
 
     const E *kg, *qg, *vg, *bg;
     const float *gg; // log decays, or nullptr
+    // Gated path: queries and decays are addressed by real token (virtual
+    // step tok0 + row is substep (.) % nh of real token (.) / nh); qh and gh
+    // point at this head's real token 0.
+    const E *qh;
+    const float *gh;
+    SubstepBase sb;
     int64_t sqk, sv;
     int H, len, tid;
     bool has_v;
@@ -521,7 +527,13 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
         for (int p = 0; p < NKQ; ++p) {
             const int vi = p * NT + tid, row = min(vi / KQV, last), cv = vi % KQV;
             rk[p] = *reinterpret_cast<const V *>(kg + (base + row) * sqk + cv * TR::kVec);
-            rq[p] = *reinterpret_cast<const V *>(qg + (base + row) * sqk + cv * TR::kVec);
+            if (gg) { // the query of the real token, on its last substep only
+                const Substep st = substep_at(sb, (uint32_t)(base + row));
+                const V x = *reinterpret_cast<const V *>(qh + st.t * sqk + cv * TR::kVec);
+                rq[p] = st.j == (int)sb.nh - 1 ? x : V{};
+            } else {
+                rq[p] = *reinterpret_cast<const V *>(qg + (base + row) * sqk + cv * TR::kVec);
+            }
         }
         if (has_v) {
 #pragma unroll
@@ -531,7 +543,11 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
             }
         }
         rbeta = bg[(base + min(tid & (kChunk - 1), last)) * H]; // every wave holds all 64
-        if (gg) rg = gg[(base + min(tid & (kChunk - 1), last)) * H];
+        if (gg) { // the decay of the real token, on its first substep only
+            const Substep st = substep_at(sb, (uint32_t)(base + min(tid & (kChunk - 1), last)));
+            const float x = gh[st.t * H];
+            rg = st.j == 0 ? x : 0.f;
+        }
     }
     __device__ inline void store_kqb(E *Ks, E *Qs, float *Bs, float *Gs) const {
         const V zero = {};
@@ -572,6 +588,9 @@ __device__ inline Stager<E, DK, NT> make_stager(const ChainArgs &a, const Work &
     sg.vg = reinterpret_cast<const E *>(a.v) + wk.tok0 * sg.sv + (int64_t)wk.h * DV + wk.row0;
     sg.bg = reinterpret_cast<const E *>(a.beta) + wk.tok0 * a.H + wk.h;
     sg.gg = a.g ? a.g + wk.tok0 * a.H + wk.h : nullptr;
+    sg.qh = reinterpret_cast<const E *>(a.q) + (int64_t)wk.h * DK;
+    sg.gh = a.g ? a.g + wk.h : nullptr;
+    sg.sb = a.g ? substep_base(wk.tok0, a.nh) : SubstepBase{0, 0u, 1u};
     sg.rg = 0.f;
     sg.H = a.H;
     sg.len = wk.len;
@@ -612,14 +631,21 @@ __device__ inline void state_out(const f32x4 (&Sacc)[DK / 16], const Work &wk, i
     }
 }
 
-// O store: Oacc[t][e] = O[16t + c16][16w + 4g + e] of chunk c.
-template <typename E>
-__device__ inline void store_o(E *og, int64_t sv, int c, int nval, const f32x4 (&Oacc)[4], int w, int g,
-                               int c16) {
+// O store: Oacc[t][e] = O[16t + c16][16w + 4g + e] of chunk c. Gated path:
+// og is the output at real token 0 and virtual row 64 c + tok of the work is
+// stored at its real token on the last substep only.
+template <typename E, bool GATED>
+__device__ inline void store_o(E *og, int64_t sv, int c, int nval, const SubstepBase &sb, const f32x4 (&Oacc)[4],
+                               int w, int g, int c16) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int tok = 16 * t + c16;
-        if (tok < nval) stf(og + ((int64_t)c * kChunk + tok) * sv + 16 * w + 4 * g, Tr<E>::cvt(Oacc[t]));
+        if constexpr (GATED) {
+            const Substep st = substep_at(sb, (uint32_t)(c * kChunk + tok));
+            if (tok < nval && st.j == (int)sb.nh - 1) stf(og + st.t * sv + 16 * w + 4 * g, Tr<E>::cvt(Oacc[t]));
+        } else {
+            if (tok < nval) stf(og + ((int64_t)c * kChunk + tok) * sv + 16 * w + 4 * g, Tr<E>::cvt(Oacc[t]));
+        }
     }
 }
 
@@ -670,7 +696,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
     auto sg = make_stager<E, DK, DV, WRITE_O>(a, wk, tid);
     const bool has_v = WRITE_O || wk.has_v;
     const int64_t sv = (int64_t)a.H * DV;
-    E *og = WRITE_O ? reinterpret_cast<E *>(a.o) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 : nullptr;
+    E *og = WRITE_O ? reinterpret_cast<E *>(a.o) + (GATED ? 0 : wk.tok0 * sv) + (int64_t)wk.h * DV + wk.row0
+                    : nullptr;
 
     // T and P are lower triangular and only their lower blocks are written:
     // zero both once so the blocks above the diagonal stay zero.
@@ -748,7 +775,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
             PH::template o_fetch<GATED>(f, Qs, Ps, Gs, g, c16);
             sched_fence();
             PH::template o_compute<GATED>(f, SB, ZB, Oacc);
-            store_o(og, sv, c, nval, Oacc, w, g, c16);
+            store_o<E, GATED>(og, sv, c, nval, sg.sb, Oacc, w, g, c16);
         }
         {
             typename PH::SFrags f;

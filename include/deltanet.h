@@ -147,6 +147,28 @@ int deltanet_gated_fwd(const void *q, const void *k, const void *v, const void *
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Gated Delta Product forward pass ("Linear Attention, Visualized", "Gated
+ * Delta Product (GDP)"): each real token t carries n_h (key, value, beta)
+ * substeps applied in order after one decay of the previous state,
+ *     S_{t,0} = a_t S_{t-1},  S_{t,j} = S_{t,j-1}(I - b_{t,j} k_{t,j} k_{t,j}^T) + b_{t,j} v_{t,j} k_{t,j}^T,
+ *     S_t = S_{t,n_h},  o_t = S_t q_t,
+ * evaluated as Gated DeltaNet over the virtual sequence of T n_h steps of
+ * that page's "GDP as GDN over a virtual sequence" (decay on the first
+ * substep, query on the last). The kernels index real tokens directly; no
+ * virtual copy of q, g or o is made.
+ *   q    : [B, T, H, dk]          k : [B, T, n_h, H, dk]     v : [B, T, n_h, H, dv]
+ *   beta : [B, T, n_h, H]         g : [B, T, H] float32 (required when T > 0)
+ *   o    : [B, T, H, dv]          S0, S_final : [B, H, dv, dk] float32
+ * k, v and beta in this layout are already in virtual order. n_h >= 1
+ * (n_h = 1 is deltanet_gated_fwd). Workspace: deltanet_workspace_bytes with
+ * T n_h in place of T. Other arguments and errors as in deltanet_gated_fwd.
+ */
+int deltanet_gdp_fwd(const void *q, const void *k, const void *v, const void *beta,
+                     const float *g, const float *S0, void *o, float *S_final, int B, int H,
+                     int T, int n_h, int dk, int dv, int chunk, int dtype, int cp_groups,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Gated DeltaNet forward pass over N packed sequences.
  *   g : log decays, float32 [T_total, H]; required when total_T > 0.
  * Other arguments as in deltanet_fwd_varlen.

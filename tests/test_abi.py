@@ -30,7 +30,7 @@ def lib():
 def test_library_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd",
-                          "deltanet_gated_fwd_varlen", "deltanet_decode_step",
+                          "deltanet_gated_fwd_varlen", "deltanet_gdp_fwd", "deltanet_decode_step",
                           "deltanet_workspace_bytes",
                           "deltanet_pick_cp_groups", "deltanet_status_string"}
     raw = ctypes.CDLL(dn.library_path())
@@ -178,6 +178,23 @@ def test_decode_step_rejects_bad_arguments(lib, kw, status):
     st = lib.deltanet_decode_step(vp(a["q"]), vp(FAKE), vp(FAKE), vp(FAKE), vp(a["g"]) if a["g"] else None,
                                   vp(a["S"]) if a["S"] else None, vp(a["o"]) if a["o"] else None,
                                   a["B"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+    assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nh=0), DN_ERR_INVALID),
+    (dict(g=None), DN_ERR_INVALID),
+    (dict(T=1 << 28, nh=8), DN_ERR_UNSUPPORTED),
+    (dict(chunk=32), DN_ERR_UNSUPPORTED),
+    (dict(cp_groups=2), DN_ERR_WORKSPACE),
+])
+def test_gdp_rejects_bad_arguments(lib, kw, status):
+    a = dict(g=FAKE, T=100, nh=2, chunk=64, cp_groups=1)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    st = lib.deltanet_gdp_fwd(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(a["g"]) if a["g"] else None,
+                              None, vp(FAKE), None, 1, 2, a["T"], a["nh"], 64, 64, a["chunk"], 1,
+                              a["cp_groups"], None, 0, None)
     assert st == status
 
 
