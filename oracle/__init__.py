@@ -33,6 +33,8 @@ by Haoran Zhang, "p1" is "Context Parallelism for DeltaNet" by yywangcs):
   correction); ``gated_chunked_fwd`` -- that section's "Complete per-chunk
   algorithm"; ``householder_states``, ``exact_states`` and
   ``cp_group_transition`` take the decays as an optional argument.
+* ``deltanet_bwd`` -- the backward pass: reverse mode of the token-serial
+  recurrence in fp64 (C), with the states recomputed from checkpoints.
 * ``gdp_fwd`` -- Gated Delta Product token by token with its substeps (p3
   "Gated Delta Product (GDP)"); ``gdp_virtual_sequence`` -- the mapping of p3
   "GDP as GDN over a virtual sequence".
@@ -101,6 +103,9 @@ def load(path: str = _LIB_PATH):
                                                      ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                      ctypes.c_int]
     lib.oracle_gated_deltanet_fwd_varlen.restype = ctypes.c_int
+    lib.oracle_deltanet_bwd.argtypes = [dp] * 12 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                                    ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_deltanet_bwd.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     if path == _LIB_PATH:
@@ -223,6 +228,31 @@ def gated_deltanet_fwd_varlen(q, k, v, beta, g, cu_seqlens, S0=None, nthreads: i
     if rc != 0:
         raise RuntimeError(f"oracle_gated_deltanet_fwd_varlen failed with {rc}")
     return o, Sf
+
+
+def deltanet_bwd(q, k, v, beta, dO, S0=None, dS_final=None, nthreads: int = 0, lib=None):
+    """Token-serial fp64 backward of DeltaNet (reverse mode of the recurrence).
+
+    Upstream gradients dO [B,T,H,dv] of o and dS_final [B,H,dv,dk] of the final
+    state (None: zero). Returns (dq, dk, dv, dbeta, dS0). The pages give no
+    backward pass; this is the chain rule on p3 DeltaNet > "Recurrent form"
+    (transposed state), written out in ``deltanet_oracle.c``.
+    """
+    q, k, v, beta, dO = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(dO)
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    S0 = None if S0 is None else _f64(S0)
+    dS_final = None if dS_final is None else _f64(dS_final)
+    dq, dkk, dvv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    db = np.empty_like(beta)
+    dS0 = np.empty((B, H, dv, dk))
+    lib = lib or load()
+    rc = lib.oracle_deltanet_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(dO),
+                                 _ptr(dS_final), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dS0),
+                                 B, H, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_deltanet_bwd failed with {rc}")
+    return dq, dkk, dvv, db, dS0
 
 
 def gdp_fwd(q, k, v, beta, g, n_h, S0=None):

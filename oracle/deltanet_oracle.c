@@ -207,6 +207,149 @@ int oracle_gated_deltanet_fwd_varlen(const double *q, const double *k, const dou
     return varlen_fwd(q, k, v, beta, g, S0, o, S_final, cu_seqlens, N, H, dk, dv, nthreads);
 }
 
+/*
+ * Backward pass of the DeltaNet recurrence (reverse mode of the token-serial
+ * definition above, in fp64). For a loss with upstream gradients dO_t of the
+ * outputs and dS_T of the final state, reading the recurrence backwards:
+ *   G  <- dS_T                                   (gradient of S_T)
+ *   for t = T .. 1:
+ *     G  += dO_t q_t^T ;      dq_t = S_t^T dO_t          (o_t = S_t q_t)
+ *     r_t = v_t - S_{t-1} k_t                    (the residual of the write)
+ *     du  = G k_t                                (S_t = S_{t-1} + beta_t r_t k_t^T)
+ *     dk_t = beta_t G^T r_t - beta_t S_{t-1}^T du
+ *     dv_t = beta_t du ;      dbeta_t = du . r_t
+ *     G  <- G - beta_t du k_t^T                  (gradient of S_{t-1})
+ *   dS_0 = G.
+ * The pages derive no backward pass; this is the chain rule applied to the
+ * recurrence of "Linear Attention, Visualized", DeltaNet > "Recurrent form".
+ * States S_{t-1} are recomputed forward from checkpoints every kSeg tokens.
+ */
+enum { kSeg = 64 };
+
+static void unit_backward(const double *q, const double *k, const double *v, const double *beta,
+                          const double *dO, double *dq, double *dk, double *dv, double *dbeta,
+                          ptrdiff_t qk_stride, ptrdiff_t vo_stride, ptrdiff_t beta_stride, int64_t L,
+                          int dk_, int dv_, double *S, double *G, double *seg, double *tmp)
+{
+    /* S holds S0 on entry; G holds dS_T. seg: (kSeg + 1) states; tmp: dv + dk + dv */
+    const size_t sz = (size_t)dv_ * dk_;
+    const int64_t nseg = (L + kSeg - 1) / kSeg;
+    double *ck = (double *)malloc(sizeof(double) * sz * (size_t)(nseg > 0 ? nseg : 1));
+    if (!ck) return;
+    /* forward: checkpoint the state at each segment start */
+    for (int64_t sgi = 0; sgi < nseg; ++sgi) {
+        memcpy(ck + (size_t)sgi * sz, S, sizeof(double) * sz);
+        const int64_t t1 = (sgi + 1) * kSeg < L ? (sgi + 1) * kSeg : L;
+        unit_forward(q + sgi * kSeg * qk_stride, k + sgi * kSeg * qk_stride, v + sgi * kSeg * vo_stride,
+                     beta + sgi * kSeg * beta_stride, NULL, NULL, qk_stride, vo_stride, beta_stride,
+                     t1 - sgi * kSeg, dk_, dv_, S, tmp);
+    }
+    double *r = tmp, *du = tmp + dv_, *vh = tmp + 2 * dv_;
+    for (int64_t sgi = nseg - 1; sgi >= 0; --sgi) {
+        const int64_t t0 = sgi * kSeg, t1 = (sgi + 1) * kSeg < L ? (sgi + 1) * kSeg : L;
+        /* seg[j] = state before token t0 + j, j = 0 .. t1 - t0 */
+        memcpy(seg, ck + (size_t)sgi * sz, sizeof(double) * sz);
+        for (int64_t t = t0; t < t1; ++t) {
+            double *Sn = seg + (size_t)(t - t0 + 1) * sz;
+            memcpy(Sn, seg + (size_t)(t - t0) * sz, sizeof(double) * sz);
+            unit_forward(q + t * qk_stride, k + t * qk_stride, v + t * vo_stride, beta + t * beta_stride,
+                         NULL, NULL, qk_stride, vo_stride, beta_stride, 1, dk_, dv_, Sn, vh);
+        }
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+            const double *St = seg + (size_t)(t - t0 + 1) * sz, *Sp = seg + (size_t)(t - t0) * sz;
+            const double *kt = k + t * qk_stride, *qt = q + t * qk_stride, *vt = v + t * vo_stride;
+            const double *dot = dO + t * vo_stride;
+            const double bt = beta[t * beta_stride];
+            /* readout: G += dO q^T ; dq = S_t^T dO */
+            for (int j = 0; j < dk_; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dv_; ++i) acc += St[(size_t)i * dk_ + j] * dot[i];
+                dq[t * qk_stride + j] = acc;
+            }
+            for (int i = 0; i < dv_; ++i)
+                for (int j = 0; j < dk_; ++j) G[(size_t)i * dk_ + j] += dot[i] * qt[j];
+            /* residual r = v - S_{t-1} k ; du = G k */
+            for (int i = 0; i < dv_; ++i) {
+                double a = 0.0, b = 0.0;
+                for (int j = 0; j < dk_; ++j) {
+                    a += Sp[(size_t)i * dk_ + j] * kt[j];
+                    b += G[(size_t)i * dk_ + j] * kt[j];
+                }
+                r[i] = vt[i] - a;
+                du[i] = b;
+            }
+            double db = 0.0;
+            for (int i = 0; i < dv_; ++i) db += du[i] * r[i];
+            dbeta[t * beta_stride] = db;
+            for (int i = 0; i < dv_; ++i) dv[t * vo_stride + i] = bt * du[i];
+            for (int j = 0; j < dk_; ++j) {
+                double a = 0.0, b = 0.0;
+                for (int i = 0; i < dv_; ++i) {
+                    a += G[(size_t)i * dk_ + j] * r[i];
+                    b += Sp[(size_t)i * dk_ + j] * du[i];
+                }
+                dk[t * qk_stride + j] = bt * a - bt * b;
+            }
+            /* G <- G - beta du k^T */
+            for (int i = 0; i < dv_; ++i)
+                for (int j = 0; j < dk_; ++j) G[(size_t)i * dk_ + j] -= bt * du[i] * kt[j];
+        }
+    }
+    free(ck);
+}
+
+/*
+ * dq, dk [B,T,H,dk], dv [B,T,H,dv], dbeta [B,T,H], dS0 [B,H,dv,dk] (may be
+ * NULL) for upstream gradients dO [B,T,H,dv] and dS_final [B,H,dv,dk] (NULL:
+ * zero). S0 may be NULL (zero). Returns 0, -1 on bad arguments, -2 on
+ * allocation failure.
+ */
+int oracle_deltanet_bwd(const double *q, const double *k, const double *v, const double *beta,
+                        const double *S0, const double *dO, const double *dS_final, double *dq,
+                        double *dk, double *dv, double *dbeta, double *dS0, int B, int H, int64_t T,
+                        int dk_, int dv_, int nthreads)
+{
+    if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta || B <= 0 || H <= 0 || T < 0 ||
+        dk_ <= 0 || dv_ <= 0)
+        return -1;
+    const ptrdiff_t qk_stride = (ptrdiff_t)H * dk_, vo_stride = (ptrdiff_t)H * dv_;
+    const size_t sz = (size_t)dv_ * dk_;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *buf = (double *)malloc(sizeof(double) * (sz * (kSeg + 3) + 3 * (size_t)(dv_ + dk_)));
+        if (!buf) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            double *S = buf, *G = buf + sz, *seg = buf + 2 * sz, *tmp = seg + sz * (kSeg + 1);
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < (int64_t)B * H; ++u) {
+                const int64_t b = u / H;
+                const int h = (int)(u % H);
+                const int64_t t0 = b * T;
+                if (S0) memcpy(S, S0 + (size_t)u * sz, sizeof(double) * sz);
+                else memset(S, 0, sizeof(double) * sz);
+                if (dS_final) memcpy(G, dS_final + (size_t)u * sz, sizeof(double) * sz);
+                else memset(G, 0, sizeof(double) * sz);
+                unit_backward(q + t0 * qk_stride + (ptrdiff_t)h * dk_, k + t0 * qk_stride + (ptrdiff_t)h * dk_,
+                              v + t0 * vo_stride + (ptrdiff_t)h * dv_, beta + t0 * H + h,
+                              dO + t0 * vo_stride + (ptrdiff_t)h * dv_, dq + t0 * qk_stride + (ptrdiff_t)h * dk_,
+                              dk + t0 * qk_stride + (ptrdiff_t)h * dk_, dv + t0 * vo_stride + (ptrdiff_t)h * dv_,
+                              dbeta + t0 * H + h, qk_stride, vo_stride, H, T, dk_, dv_, S, G, seg, tmp);
+                if (dS0) memcpy(dS0 + (size_t)u * sz, G, sizeof(double) * sz);
+            }
+            free(buf);
+        }
+    }
+    return failed ? -2 : 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

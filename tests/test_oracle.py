@@ -435,6 +435,81 @@ def pin_gated_resume_and_varlen(lib):
     return bool(ok)
 
 
+# ---- Backward pass (chain rule on the recurrence): pinned by finite differences
+
+def _bwd_case(seed, B=1, T=70, H=2, dk=4, dv=3):
+    rng = np.random.default_rng(seed)
+    q, k, v, beta, S0 = _inputs(rng, B=B, T=T, H=H, dk=dk, dv=dv)
+    dO = rng.standard_normal(v.shape)
+    dSf = rng.standard_normal(S0.shape)
+    return rng, (q, k, v, beta, S0), dO, dSf
+
+
+def _loss(lib, args, dO, dSf):
+    o, S = oracle.deltanet_fwd(*args, lib=lib)
+    return float((o * dO).sum() + (S * dSf).sum())
+
+
+def pin_bwd_finite_differences(lib):
+    # central differences of L = <dO, o> + <dS_final, S_T> for sampled entries of
+    # every input; T = 70 crosses the oracle's 64-token checkpoint segment
+    rng, args, dO, dSf = _bwd_case(70)
+    grads = oracle.deltanet_bwd(*args[:4], dO, args[4], dSf, lib=lib)
+    grads = (grads[0], grads[1], grads[2], grads[3], grads[4])
+    ok = True
+    for ai in range(5):
+        a = args[ai]
+        for _ in range(12):
+            idx = tuple(int(rng.integers(0, n)) for n in a.shape)
+            h = 1e-5
+            ap = [x.copy() for x in args]
+            am = [x.copy() for x in args]
+            ap[ai][idx] += h
+            am[ai][idx] -= h
+            fd = (_loss(lib, ap, dO, dSf) - _loss(lib, am, dO, dSf)) / (2 * h)
+            ok &= abs(fd - grads[ai][idx]) <= 1e-6 * max(1.0, abs(fd))
+    return bool(ok)
+
+
+def pin_bwd_linear_inputs_exact(lib):
+    # L is linear in v and in S0 (the recurrence is affine in them), so a unit
+    # step gives the exact directional derivative: <dv, E> = L(v + E) - L(v)
+    rng, args, dO, dSf = _bwd_case(71, T=33)
+    dq, dk, dv, db, dS0 = oracle.deltanet_bwd(*args[:4], dO, args[4], dSf, lib=lib)
+    base = _loss(lib, args, dO, dSf)
+    Ev = rng.standard_normal(args[2].shape)
+    Es = rng.standard_normal(args[4].shape)
+    lv = _loss(lib, [args[0], args[1], args[2] + Ev, args[3], args[4]], dO, dSf) - base
+    ls = _loss(lib, [args[0], args[1], args[2], args[3], args[4] + Es], dO, dSf) - base
+    return (abs(lv - (dv * Ev).sum()) <= 1e-10 * max(1.0, abs(lv))
+            and abs(ls - (dS0 * Es).sum()) <= 1e-10 * max(1.0, abs(ls)))
+
+
+def pin_bwd_zero_upstream_and_empty(lib):
+    rng, args, dO, dSf = _bwd_case(72, T=20)
+    g = oracle.deltanet_bwd(*args[:4], np.zeros_like(dO), args[4], None, lib=lib)
+    ok = all(np.abs(x).max() == 0 for x in g)
+    # T = 0: the final state is S0, so dS0 = dS_final
+    e = lambda x: x[:, :0]
+    g0 = oracle.deltanet_bwd(e(args[0]), e(args[1]), e(args[2]), e(args[3]), e(dO), args[4], dSf, lib=lib)
+    return bool(ok and np.array_equal(g0[4], dSf))
+
+
+def pin_bwd_state_gradient_closed_form(lib):
+    # dS0 = dS_T P^T + sum_t dO_t q_t^T (A_1..A_t)^T with A_t = I - b_t k_t k_t^T,
+    # because S_t = S0 A_1..A_t + (terms without S0)
+    rng, args, dO, dSf = _bwd_case(73, T=9, H=1)
+    q, k, v, beta, S0 = args
+    _, _, _, _, dS0 = oracle.deltanet_bwd(q, k, v, beta, dO, S0, dSf, lib=lib)
+    P = np.eye(4)
+    ref = np.zeros((3, 4))
+    for t in range(9):
+        P = P @ (np.eye(4) - beta[0, t, 0] * np.outer(k[0, t, 0], k[0, t, 0]))
+        ref += np.outer(dO[0, t, 0], q[0, t, 0]) @ P.T
+    ref += dSf[0, 0] @ P.T
+    return _rel(dS0[0, 0], ref) < 1e-12
+
+
 PINS = [pin_golden_three_tokens, pin_golden_three_tokens_lambda, pin_golden_alice_bob,
         pin_beta_zero, pin_single_token, pin_read_back, pin_orthonormal_keys,
         pin_householder_products, pin_square_householder, pin_exact_rationals,
@@ -442,7 +517,8 @@ PINS = [pin_golden_three_tokens, pin_golden_three_tokens_lambda, pin_golden_alic
         pin_gated_no_decay_is_deltanet, pin_gated_beta_zero, pin_gated_single_token,
         pin_gated_read_back, pin_gated_orthonormal_keys, pin_gated_reset,
         pin_gated_householder, pin_gated_exact_rationals, pin_gated_chunked_agreement,
-        pin_gated_resume_and_varlen]
+        pin_gated_resume_and_varlen, pin_bwd_finite_differences, pin_bwd_linear_inputs_exact,
+        pin_bwd_zero_upstream_and_empty, pin_bwd_state_gradient_closed_form]
 
 
 def failed_pins(lib):
@@ -477,10 +553,12 @@ MUTANTS = {
                          "for (int j = 0; j < dk; ++j) acc += S[(size_t)j * dk + i] * kt[j];"),
     "write_at_query": ("for (int j = 0; j < dk; ++j) Si[j] += ui * kt[j];",
                        "for (int j = 0; j < dk; ++j) Si[j] += ui * qt[j];"),
-    "ignored_S0": ("if (S0) memcpy(S, S0", "if (0) memcpy(S, S0"),
+    "ignored_S0": ("if (S0) memcpy(S, S0 + (size_t)u * sz, sizeof(double) * sz);\n                else memset(S, 0, sizeof(double) * sz);\n                unit_forward(",
+                   "if (0) memcpy(S, S0 + (size_t)u * sz, sizeof(double) * sz);\n                else memset(S, 0, sizeof(double) * sz);\n                unit_forward("),
     "dropped_last_token": ("for (int64_t t = 0; t < L; ++t) {",
                            "for (int64_t t = 0; t + 1 < L; ++t) {"),
-    "beta_of_head0": ("beta + t0 * H + h,", "beta + t0 * H,"),
+    "beta_of_head0": ("beta + t0 * H + h,\n                             g ? g",
+                      "beta + t0 * H,\n                             g ? g"),
     "gate_after_write": ("        /* decay of the previous state: S <- a_t S */\n        if (g) {",
                          "        if (0) {"),
     "gate_not_exponentiated": ("const double at = exp(g[t * beta_stride]);",
@@ -488,6 +566,15 @@ MUTANTS = {
     "gate_of_previous_token": ("const double at = exp(g[t * beta_stride]);",
                                "const double at = exp(g[(t > 0 ? t - 1 : 0) * beta_stride]);"),
     "gate_of_head0": ("g ? g + t0 * H + h : NULL,", "g ? g + t0 * H : NULL,"),
+    "bwd_dq_from_previous_state": ("for (int i = 0; i < dv_; ++i) acc += St[(size_t)i * dk_ + j] * dot[i];",
+                                   "for (int i = 0; i < dv_; ++i) acc += Sp[(size_t)i * dk_ + j] * dot[i];"),
+    "bwd_residual_of_new_state": ("a += Sp[(size_t)i * dk_ + j] * kt[j];",
+                                  "a += St[(size_t)i * dk_ + j] * kt[j];"),
+    "bwd_dropped_prediction_term": ("dk[t * qk_stride + j] = bt * a - bt * b;",
+                                    "dk[t * qk_stride + j] = bt * a;"),
+    "bwd_state_gradient_sign": ("G[(size_t)i * dk_ + j] -= bt * du[i] * kt[j];",
+                                "G[(size_t)i * dk_ + j] += bt * du[i] * kt[j];"),
+    "bwd_beta_gradient_scaled": ("dbeta[t * beta_stride] = db;", "dbeta[t * beta_stride] = bt * db;"),
     "read_before_write": ("        /* write: S += beta_t (v_t - vhat) k_t^T */",
                           "        if (o) { double *ot = o + t * vo_stride;"
                           " for (int i = 0; i < dv; ++i) { const double *Si = S + (size_t)i * dk;"
