@@ -12,7 +12,9 @@ events on the launch stream) and the fp64 CPU oracle's throughput on the
 host cores. ``--gated`` measures Gated DeltaNet (``deltanet_gated_fwd``, with
 per-token log decays) instead; without it, a short gated run of the same
 workload is reported under ``variants.gated`` next to the headline figures.
-``variants.gdp`` times ``deltanet_gdp_fwd`` (Gated Delta Product, n_h = 2 substeps
+``variants.bwd`` times ``deltanet_bwd`` (the backward pass: forward chain with
+per-chunk states, reverse state-gradient chain, chunk-parallel finish) on the
+same workload. ``variants.gdp`` times ``deltanet_gdp_fwd`` (Gated Delta Product, n_h = 2 substeps
 per token) on the same B, H, T and widths. ``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
 head, state updated in place) on B=256 H=16 d=128 bf16, a 256 MiB state.
 
@@ -155,6 +157,29 @@ def cpu_baseline(inputs, w, varlen, budget_s, g=None):
         units = nb * w.H
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(min(threads, units)),
             "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+
+
+def bwd_variant(dev, w, inputs, fwd_ms, steps=10, warmup=3):
+    """Time deltanet_bwd on the workload (dO ~ N(0, 1) in bf16, no final-state
+    gradient). Bytes: the algorithmic minimum of reading q, k, v, beta, dO and
+    writing dq, dk, dv, dbeta; the per-chunk states and partial sums the
+    three passes exchange through HBM are reported separately."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+
+    print("[bench] backward variant", file=sys.stderr, flush=True)
+    q, k, v, beta, S0 = inputs
+    g = torch.Generator(device=dev).manual_seed(9)
+    dO = torch.randn(v.shape, generator=g, device=dev, dtype=torch.float32).to(v.dtype)
+    need = dn.deltanet_bwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ms, launch_ms, _ = time_steps(lambda: dn.deltanet_bwd(q, k, v, beta, dO, S0, workspace=ws), warmup, steps)
+    esz = 2
+    nbytes = w.B * w.T * w.H * (2 * (2 * w.dk + 2 * w.dv + 1)) * esz
+    return {"call": "deltanet_bwd", "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1), "avg_launch_us": round(launch_ms * 1e3, 2),
+            "vs_forward_time": round(launch_ms / fwd_ms, 3), "algorithmic_bytes": nbytes,
+            "workspace_bytes": need, "hbm_frac_algorithmic": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4)}
 
 
 def gdp_variant(dev, w, flops_per_head_step, peak_flops, nh=2, steps=20, warmup=5):
@@ -364,7 +389,8 @@ def main():
             "mfma_frac": round(flops / (g_launch_ms / 1e3) / peak_flops, 4),
             "vs_ungated_time": round(g_launch_ms / avg_launch_ms, 4)}}
     if not args.gated and not args.no_variants and not w.varlen and w.dtype == "bf16":
-        result.setdefault("variants", {})["gdp"] = gdp_variant(dev, w, flops / n_tokens / w.H, peak_flops)
+        result.setdefault("variants", {})["bwd"] = bwd_variant(dev, w, inputs, avg_launch_ms)
+        result["variants"]["gdp"] = gdp_variant(dev, w, flops / n_tokens / w.H, peak_flops)
     if not args.gated and not args.no_variants:
         result.setdefault("variants", {})["decode"] = decode_variant(dev)
     if not args.no_cpu_baseline:

@@ -25,7 +25,8 @@ import os
 import torch
 
 __all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
-           "deltanet_gdp_fwd", "deltanet_decode_step", "deltanet_workspace_bytes",
+           "deltanet_gdp_fwd", "deltanet_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
+           "deltanet_workspace_bytes",
            "deltanet_pick_cp_groups", "deltanet_status_string", "longest_first_order",
            "library_path", "load_library", "DeltaNetError", "DN_F32", "DN_BF16"]
 
@@ -70,6 +71,10 @@ def load_library(path: str | None = None):
     lib.deltanet_gated_fwd_varlen.restype = i
     lib.deltanet_gdp_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.deltanet_gdp_fwd.restype = i
+    lib.deltanet_bwd.argtypes = [vp] * 12 + [i, i, i, i, i, i, i, vp, sz, vp]
+    lib.deltanet_bwd.restype = i
+    lib.deltanet_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.deltanet_bwd_workspace_bytes.restype = sz
     lib.deltanet_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.deltanet_decode_step.restype = i
     lib.deltanet_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
@@ -347,3 +352,46 @@ def deltanet_decode_step(q, k, v, beta, S, g=None, *, o=None, stream=None):
     if st != 0:
         raise DeltaNetError(st, "deltanet_decode_step")
     return o
+
+
+def deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk=64) -> int:
+    return int(load_library().deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def deltanet_bwd(q, k, v, beta, dO, S0=None, dS_final=None, *, chunk: int = 64, workspace=None,
+                 want_dS0: bool = True, stream=None):
+    """Backward of ``deltanet_fwd`` (C-ABI ``deltanet_bwd``, bf16 only).
+
+    q, k: [B,T,H,dk]; v, dO: [B,T,H,dv]; beta: [B,T,H] (bf16); S0, dS_final:
+    [B,H,dv,dk] fp32 or None. Returns (dq, dk, dv, dbeta, dS0 or None).
+    """
+    lib = load_library()
+    if k.dim() != 4:
+        raise ValueError("k must be [B, T, H, dk]")
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    if dt != torch.bfloat16:
+        raise TypeError("deltanet_bwd supports bfloat16 inputs only")
+    _check(q, "q", dt, dev, (B, T, H, dk))
+    _check(k, "k", dt, dev, (B, T, H, dk))
+    _check(v, "v", dt, dev, (B, T, H, dv))
+    _check(beta, "beta", dt, dev, (B, T, H))
+    _check(dO, "dO", dt, dev, (B, T, H, dv))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if dS_final is not None:
+        _check(dS_final, "dS_final", torch.float32, dev, (B, H, dv, dk))
+    dq, dkk, dvv, db = (torch.empty_like(x) for x in (q, k, v, beta))
+    dS0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None
+    need = int(lib.deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.deltanet_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_final),
+                              _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dS0), B, H, T, dk, dv, chunk,
+                              DN_BF16, _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if st != 0:
+        raise DeltaNetError(st, "deltanet_bwd")
+    return dq, dkk, dvv, db, dS0

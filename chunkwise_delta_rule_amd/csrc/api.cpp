@@ -257,6 +257,80 @@ int deltanet_gated_fwd_varlen(const void *q, const void *k, const void *v, const
                       stream);
 }
 
+size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    if (B <= 0 || H <= 0 || T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
+    const size_t units = (size_t)B * H, nc = (size_t)(T + dn::kChunk - 1) / dn::kChunk;
+    return units * nc * ((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_floats(dk)) * sizeof(float);
+}
+
+int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, const float *S0, const void *dO,
+                 const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dS0, int B, int H, int T,
+                 int dk, int dv, int chunk, int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st = check_shape(dk, dv, chunk, dtype);
+    if (st != DN_OK) return st;
+    if (dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
+    if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
+    if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !dO || !dq || !dk_ || !dv_ || !dbeta) return DN_ERR_INVALID;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned_to(beta, 2) ||
+            !aligned_to(dq, 2) || !aligned_to(dk_, 2) || !aligned_to(dv_, 2) || !aligned_to(dbeta, 2))
+            return DN_ERR_INVALID;
+    }
+    if ((S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
+        return DN_ERR_INVALID;
+    const size_t need = deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return DN_ERR_WORKSPACE;
+    const int NC = (T + dn::kChunk - 1) / dn::kChunk;
+    float *Sck = static_cast<float *>(workspace);
+    if (NC == 0) { // no tokens: the gradient of S0 is the gradient of the final state
+        if (dS0) {
+            const size_t n = (size_t)B * H * dv * dk * sizeof(float);
+            const hipError_t e = dS_final ? hipMemcpyAsync(dS0, dS_final, n, hipMemcpyDeviceToDevice, stream)
+                                          : dn::launch_fill(dS0, n / sizeof(float), 0.f, stream);
+            if (e != hipSuccess) return DN_ERR_HIP;
+        }
+        return DN_OK;
+    }
+    // pass 1: the forward chain, keeping the state that enters every chunk
+    dn::ChainArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.S0 = S0;
+    a.S_chunks = Sck;
+    a.B = B;
+    a.H = H;
+    a.T = T;
+    a.nh = 1;
+    a.kind = dn::kDense;
+    a.n_units = B * H;
+    a.n_tiles = dv / dn::kRows;
+    if (dn::launch_chain(dtype, dk, dv, false, a, stream) != hipSuccess) return DN_ERR_HIP;
+    // passes 2 and 3
+    dn::BwdArgs b = {};
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.beta = beta;
+    b.dO = dO;
+    b.dS_final = dS_final;
+    b.S_chunks = Sck;
+    b.part = Sck + (size_t)B * H * NC * dv * dk;
+    b.dS0 = dS0;
+    b.dq = dq;
+    b.dk = dk_;
+    b.dv = dv_;
+    b.dbeta = dbeta;
+    b.B = B;
+    b.H = H;
+    b.T = T;
+    b.NC = NC;
+    b.n_tiles = dv / dn::kRows;
+    return dn::launch_bwd(dk, dv, b, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
 int deltanet_decode_step(const void *q, const void *k, const void *v, const void *beta, const float *g,
                          float *S, void *o, int B, int H, int dk, int dv, int dtype, hipStream_t stream) {
     if (dtype != DN_F32 && dtype != DN_BF16) return DN_ERR_INVALID;

@@ -631,6 +631,12 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     const SubstepBase sb = GATED ? substep_base(wk.tok0, a.nh) : SubstepBase{0, 0u, 1u};
     __syncthreads(); // matches the producers' prologue
     for (int r = -3; r < NC; ++r) {
+        if (!WO && r >= 0 && wk.Schunks) { // the state entering chunk r, for the backward pass
+            Work ck = wk;
+            ck.Sout = wk.Schunks + (int64_t)r * DV * DK;
+            ck.transposed_out = false;
+            ws_state_out<DK>(Sacc, ck, cw, g, c16);
+        }
         if (r >= 0)
             consumer_chain<DK, WO, GATED>(bf, r, Sacc, WO ? og + (GATED ? 0 : (int64_t)r * kChunk * sv) : nullptr,
                                           sv, min(kChunk, wk.len - r * kChunk), sb, has_v, cw, lane, g, c16);

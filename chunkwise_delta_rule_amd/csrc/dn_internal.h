@@ -26,6 +26,8 @@ struct ChainArgs {
     void *o;
     const float *S0;
     float *S_final;
+    float *S_chunks; // dense kind only, or nullptr: the state entering every chunk,
+                     // [B*H][chunks][dv][dk] fp32 (kept for the backward pass)
     const int32_t *cu_seqlens;
     const int32_t *seq_order;
     // Context-parallel workspace, per (b*H + h) and group g:
@@ -54,6 +56,23 @@ struct DecodeArgs {
     int n_units;
     int dv;
 };
+
+// Backward pass (bf16): gradients of q, k, v, beta and S0 for upstream dO and
+// dS_final, from the per-chunk states S_chunks of a forward pass.
+struct BwdArgs {
+    const void *q, *k, *v, *beta, *dO;
+    const float *dS_final; // [B*H][dv][dk] or nullptr (zero)
+    const float *S_chunks; // [B*H][NC][dv][dk]: the state entering each chunk
+    float *part;           // [n_tiles][B*H][NC] blocks of per-tile partial sums
+    float *dS0;            // [B*H][dv][dk] or nullptr
+    void *dq, *dk, *dv, *dbeta;
+    int B, H, T, NC, n_tiles;
+};
+// Floats of one partial block: dP, dT (64 x 64 each), dQ, dK (64 x dk each).
+constexpr size_t bwd_part_floats(int dk) { return 2 * 64 * 64 + 2 * 64 * (size_t)dk; }
+hipError_t launch_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream);
+// Fill n floats with value (a kernel, not a memset, so it can sit in a captured graph).
+hipError_t launch_fill(float *p, size_t n, float value, hipStream_t stream);
 
 // Enqueue the decode kernel for dtype (0 = fp32, 1 = bf16) and dk (dv is in
 // the arguments; dk, dv in {64, 128}). grid = n_units * dv / 64 workgroups.

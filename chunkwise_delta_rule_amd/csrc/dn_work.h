@@ -29,6 +29,8 @@ __device__ inline void map_block(int x, int n_units, int n_tiles, int &u, int &t
 struct Work {
     int64_t tok0;
     int len, h, row0;
+    int unit;         // index of the (sequence, head) unit
+    float *Schunks;   // rows of the state entering chunk 0 of this unit (dense kind), or nullptr
     const float *Sin; // initial rows, or nullptr (zero / identity)
     float *Sout;      // final rows, or nullptr
     bool identity, transposed_out, has_v;
@@ -38,12 +40,14 @@ template <int DK, int DV> __device__ inline Work decode_work(const ChainArgs &a)
     int u, tau;
     map_block(blockIdx.x, a.n_units, a.n_tiles, u, tau);
     const int H = a.H;
-    Work wk = {0, 0, 0, tau * kRows, nullptr, nullptr, false, false, true};
+    Work wk = {0, 0, 0, tau * kRows, u, nullptr, nullptr, nullptr, false, false, true};
     if (a.kind == kDense) {
         const int b = u / H;
         wk.h = u - b * H;
         wk.tok0 = (int64_t)b * a.T;
         wk.len = a.T;
+        if (a.S_chunks)
+            wk.Schunks = a.S_chunks + ((int64_t)u * ((a.T + kChunk - 1) / kChunk) * DV + wk.row0) * DK;
         if (a.S0) wk.Sin = a.S0 + ((int64_t)u * DV + wk.row0) * DK;
         if (a.S_final) wk.Sout = a.S_final + ((int64_t)u * DV + wk.row0) * DK;
     } else if (a.kind == kVarlen) {

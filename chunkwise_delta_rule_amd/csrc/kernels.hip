@@ -855,12 +855,478 @@ template <bool WO> hipError_t launch_dims_f32(int dk, int dv, const ChainArgs &a
     return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass (bf16 operands, fp32 accumulation).
+//
+// The pages give no backward pass; these kernels apply the chain rule to the
+// per-chunk algorithm of "Linear Attention, Visualized", DeltaNet > "Complete
+// per-chunk algorithm", in the form the forward kernels use (state S,
+// dv x dk; P = (Q K^T) lower-inclusive; T = (I + A)^-1 diag(beta) with
+// A = diag(beta) (K K^T) strictly lower):
+//   Y = V - K S^T,  Z = T Y,  O = Q S^T + P Z,  S' = S + Z^T K.
+// For upstream dO (chunk) and dS' (state after the chunk):
+//   dZ = P^T dO + K dS'^T,  dY = T^T dZ,  dV = dY,
+//   dS = dS' + dO^T Q - dY^T K                        (the reverse chain)
+//   dP = dO Z^T (lower-inclusive),  dT = dZ Y^T (lower-inclusive),
+//   dQ = dO S + dP K,  dK = dP^T Q + Z dS' - dY S + (dL + dL^T) K,
+// and through T = N diag(beta), N = (I + A)^-1, A = diag(beta) L:
+//   X = N^T dT,  dbeta_i = X_ii + sum_j dA_ij L_ij,  dA = -(X diag(beta)) N^T
+//   (strictly lower),  dL = diag(beta) dA.
+// Pass 1 is the forward chain kernel without output, keeping the state that
+// enters every chunk. Pass 2 (bwd_chain_kernel) walks the chunks backwards
+// per (unit, 64 value rows), carrying dS in registers; it writes dV and,
+// per chunk, the sums over its 64 value rows of dP, dT, dO S and Z dS' - dY S.
+// Pass 3 (bwd_finish_kernel, one workgroup per chunk) adds those partial
+// sums over the value tiles and finishes dQ, dK and dbeta.
+// ---------------------------------------------------------------------------
+__device__ inline f32x4 widen_bf16(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
+
+// T^T (and, WITH_P, the masked scores P) of the staged chunk by the forward's
+// phases. ONES_AFTER_A: beta is replaced by ones after the Gram phase, so the
+// solve yields N^T instead of T^T.
+template <int DK, bool WITH_P, bool ONES_AFTER_A>
+__device__ inline void bwd_solve(const __bf16 *Ks, const __bf16 *Qs, float *Bs, float *As, __bf16 *Ps, __bf16 *TsT,
+                                 __bf16 *NsT, int w, int lane, int g, int c16) {
+    using PH = Phases<__bf16, DK>;
+    using F = typename Tr<__bf16>::F;
+    switch (w) {
+#define DN_BA(W)                                                                                               \
+    case W: {                                                                                                  \
+        typename PH::template GramFrags<W> f;                                                                  \
+        PH::template gram_fetch<W>(f, Ks, Qs, g, c16);                                                         \
+        sched_fence();                                                                                         \
+        if constexpr (WITH_P || !(W & 1)) PH::template gram_compute<W, false>(f, Bs, nullptr, As, Ps, g, c16); \
+    } break;
+        DN_BA(0) DN_BA(1) DN_BA(2) DN_BA(3)
+#undef DN_BA
+    }
+    __syncthreads();
+    if constexpr (ONES_AFTER_A) {
+        if (w == 0) Bs[lane] = 1.f;
+        __syncthreads();
+    }
+    F nfrag;
+    {
+        typename PH::DiagFrags df;
+        PH::diag_fetch(df, As, Bs, w, c16);
+        sched_fence();
+        nfrag = PH::diag_compute(df, NsT, TsT, w, g, c16);
+    }
+    __syncthreads();
+    switch (w) {
+#define DN_BC(B)                                                                                               \
+    case B: {                                                                                                  \
+        typename PH::template OffFrags<B> f;                                                                   \
+        PH::template off_fetch<B>(f, As, NsT, Bs, g, c16);                                                     \
+        sched_fence();                                                                                         \
+        PH::template off_compute<B>(f, nfrag, TsT, g, c16);                                                    \
+    } break;
+        DN_BC(0) DN_BC(1) DN_BC(2)
+#undef DN_BC
+    default: break;
+    }
+    __syncthreads();
+}
+
+template <int DK> struct BwdLds {
+    using L = Ld<__bf16, DK>;
+    static constexpr int LT = L::T; // stride of the 64-wide bf16 tiles
+    static constexpr size_t oK = 0, oQ = oK + L::szK, oV = oQ + L::szK, oD = oV + L::szV, oB = oD + L::szV;
+    static constexpr size_t oT = oB + 256, oP = oT + L::szT, oN = oP + L::szT;
+    static constexpr size_t oX = oN + L::szN; // Y, Z, dZ, dY tiles; the Gram rows (fp32) alias them
+    static constexpr size_t oS = oX + 4 * L::szT, oR = oS + L::szK, total = oR + L::szK;
+    static_assert(L::szA <= 4 * L::szT, "Gram rows fit in the tile region");
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
+    using E = __bf16;
+    using TR = Tr<E>;
+    using F = typename TR::F;
+    using L = Ld<E, DK>;
+    using LY = BwdLds<DK>;
+    constexpr int NMT = DK / 16, LT = LY::LT;
+    static_assert(LY::total <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
+    E *Ks = reinterpret_cast<E *>(smem + LY::oK), *Qs = reinterpret_cast<E *>(smem + LY::oQ);
+    E *Vs = reinterpret_cast<E *>(smem + LY::oV), *Ds = reinterpret_cast<E *>(smem + LY::oD);
+    float *Bs = reinterpret_cast<float *>(smem + LY::oB);
+    E *TsT = reinterpret_cast<E *>(smem + LY::oT), *Ps = reinterpret_cast<E *>(smem + LY::oP);
+    E *NsT = reinterpret_cast<E *>(smem + LY::oN);
+    float *As = reinterpret_cast<float *>(smem + LY::oX);
+    E *Ys = reinterpret_cast<E *>(smem + LY::oX), *Zs = Ys + 64 * LT, *dZs = Zs + 64 * LT, *dYs = dZs + 64 * LT;
+    E *Ss = reinterpret_cast<E *>(smem + LY::oS), *Rs = reinterpret_cast<E *>(smem + LY::oR);
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int u = blockIdx.x / a.n_tiles, tau = blockIdx.x - u * a.n_tiles;
+    const int b = u / a.H, h = u - b * a.H, row0 = 64 * tau;
+    const int64_t tok0 = (int64_t)b * a.T, sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
+    const int units = a.B * a.H;
+
+    Stager<E, DK> sg;
+    sg.sqk = sqk;
+    sg.sv = sv;
+    sg.kg = reinterpret_cast<const E *>(a.k) + tok0 * sqk + (int64_t)h * DK;
+    sg.qg = reinterpret_cast<const E *>(a.q) + tok0 * sqk + (int64_t)h * DK;
+    sg.vg = reinterpret_cast<const E *>(a.v) + tok0 * sv + (int64_t)h * DV + row0;
+    sg.bg = reinterpret_cast<const E *>(a.beta) + tok0 * a.H + h;
+    sg.gg = nullptr;
+    sg.qh = nullptr;
+    sg.gh = nullptr;
+    sg.sb = SubstepBase{0, 0u, 1u};
+    sg.H = a.H;
+    sg.len = a.T;
+    sg.tid = tid;
+    sg.has_v = true;
+    sg.rbeta = TR::fromf(0.f);
+    sg.rg = 0.f;
+    sg.nval = 0;
+    const E *dOg = reinterpret_cast<const E *>(a.dO) + tok0 * sv + (int64_t)h * DV + row0;
+    E *dVg = reinterpret_cast<E *>(a.dv) + tok0 * sv + (int64_t)h * DV + row0;
+
+    // dS rows 16w + c16 of this tile: dSacc[m][i] = dS[row0 + 16w + c16][16m + 4g + i]
+    f32x4 dSacc[NMT], Sacc[NMT];
+#pragma unroll
+    for (int m = 0; m < NMT; ++m)
+        dSacc[m] = a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + ((int64_t)u * DV + row0 + 16 * w + c16) *
+                                                                                  DK + 16 * m + 4 * g)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = tid; i < kChunk * LT; i += kThreads) {
+        TsT[i] = TR::fromf(0.f);
+        Ps[i] = TR::fromf(0.f);
+    }
+
+    for (int r = a.NC - 1; r >= 0; --r) {
+        const int nval = min(kChunk, a.T - r * kChunk);
+        sg.load(r);
+        typename TR::V dov[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
+            dov[p] = *reinterpret_cast<const typename TR::V *>(dOg + ((int64_t)r * kChunk + min(row, nval - 1)) * sv +
+                                                               8 * cv);
+        }
+        const float *Sr = a.S_chunks + (((int64_t)u * a.NC + r) * DV + row0 + 16 * w + c16) * DK + 4 * g;
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) Sacc[m] = *reinterpret_cast<const f32x4 *>(Sr + 16 * m);
+        __syncthreads(); // the previous chunk's reads of the staging buffers are done
+        sg.store_kqb(Ks, Qs, Bs, nullptr);
+        sg.store_v(Vs);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
+            *reinterpret_cast<typename TR::V *>(Ds + row * L::V + 8 * cv) = row < nval ? dov[p] : typename TR::V{};
+        }
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) {
+            stf(Ss + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(Sacc[m]));
+            stf(Rs + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(dSacc[m])); // dS after the chunk
+        }
+        __syncthreads();
+        bwd_solve<DK, true, false>(Ks, Qs, Bs, As, Ps, TsT, NsT, w, lane, g, c16);
+
+        // This wave's 16 value rows (column c16 of the accumulators).
+        F SBn[NMT], dSB[NMT], YB[4], dZB[4], dYBn[4];
+        f32x4 acc[4];
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) {
+            SBn[m] = TR::cvt(-Sacc[m]);
+            dSB[m] = TR::cvt(dSacc[m]);
+        }
+        // Y = V - K S^T
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            acc[t] = widen_bf16(TR::ldcol(Vs, L::V, 16 * t, 16 * w, g, c16));
+#pragma unroll
+            for (int kb = 0; kb < NMT / 2; ++kb)
+                acc[t] = TR::mma32(acc[t], ldrow(Ks, L::K, 16 * t + c16, 32 * kb, g),
+                                   ldrow(Ks, L::K, 16 * t + c16, 32 * kb + 16, g), SBn[2 * kb], SBn[2 * kb + 1]);
+            YB[t] = TR::cvt(acc[t]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ys[(16 * t + 4 * g + i) * LT + 16 * w + c16] = YB[t][i];
+        }
+        // Z = T Y
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 <= t; ++s2) z = TR::mma16(z, TR::ldcol(TsT, L::T, 16 * s2, 16 * t, g, c16), YB[s2]);
+            const F zb = TR::cvt(z);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Zs[(16 * t + 4 * g + i) * LT + 16 * w + c16] = zb[i];
+        }
+        // dZ = P^T dO + K dS'^T
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = t; s2 < 4; ++s2)
+                z = TR::mma16(z, TR::ldcol(Ps, L::T, 16 * s2, 16 * t, g, c16), TR::ldcol(Ds, L::V, 16 * s2, 16 * w, g, c16));
+#pragma unroll
+            for (int m = 0; m < NMT; ++m) z = TR::mma16(z, ldrow(Ks, L::K, 16 * t + c16, 16 * m, g), dSB[m]);
+            dZB[t] = TR::cvt(z);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dZs[(16 * t + 4 * g + i) * LT + 16 * w + c16] = dZB[t][i];
+        }
+        // dY = T^T dZ; dV = dY
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = t; s2 < 4; ++s2) z = TR::mma16(z, ldrow(TsT, L::T, 16 * t + c16, 16 * s2, g), dZB[s2]);
+            dYBn[t] = TR::cvt(-z);
+            const F yb = TR::cvt(z);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = 16 * t + 4 * g + i;
+                dYs[tok * LT + 16 * w + c16] = yb[i];
+                if (tok < nval) dVg[((int64_t)r * kChunk + tok) * sv + 16 * w + c16] = yb[i];
+            }
+        }
+        // dS <- dS' + dO^T Q - dY^T K
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                dSacc[m] = TR::mma16(dSacc[m], TR::ldcol(Qs, L::K, 16 * s2, 16 * m, g, c16),
+                                     TR::ldcol(Ds, L::V, 16 * s2, 16 * w, g, c16));
+                dSacc[m] = TR::mma16(dSacc[m], TR::ldcol(Ks, L::K, 16 * s2, 16 * m, g, c16), dYBn[s2]);
+            }
+        __syncthreads(); // Y, Z, dZ, dY tiles complete
+
+        // Sums over this tile's 64 value rows, token rows 16w .. 16w + 15 per wave.
+        float *pb = a.part + (((int64_t)tau * units + u) * a.NC + r) * bwd_part_floats(DK);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kv = 0; kv < 4; ++kv) {
+                dp = TR::mma16(dp, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), ldrow(Zs, LT, 16 * s2 + c16, 16 * kv, g));
+                dt = TR::mma16(dt, ldrow(dZs, LT, 16 * w + c16, 16 * kv, g), ldrow(Ys, LT, 16 * s2 + c16, 16 * kv, g));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pb[(16 * w + 4 * g + i) * 64 + 16 * s2 + c16] = dp[i];
+                pb[4096 + (16 * w + 4 * g + i) * 64 + 16 * s2 + c16] = dt[i];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) {
+            f32x4 dq = {0.f, 0.f, 0.f, 0.f}, dk1 = {0.f, 0.f, 0.f, 0.f}, dk2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kv = 0; kv < 4; ++kv) {
+                dq = TR::mma16(dq, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16));
+                dk1 = TR::mma16(dk1, ldrow(Zs, LT, 16 * w + c16, 16 * kv, g), TR::ldcol(Rs, L::K, 16 * kv, 16 * m, g, c16));
+                dk2 = TR::mma16(dk2, ldrow(dYs, LT, 16 * w + c16, 16 * kv, g), TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pb[8192 + (16 * w + 4 * g + i) * DK + 16 * m + c16] = dq[i];
+                pb[8192 + 64 * DK + (16 * w + 4 * g + i) * DK + 16 * m + c16] = dk1[i] - dk2[i];
+            }
+        }
+    }
+    if (a.dS0) {
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+            *reinterpret_cast<f32x4 *>(a.dS0 + ((int64_t)u * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g) = dSacc[m];
+    }
+}
+
+template <int DK> struct FinLds {
+    using L = Ld<__bf16, DK>;
+    static constexpr int LT = L::T;
+    static constexpr size_t szX = sizeof(__bf16) * 64 * LT;
+    static constexpr size_t oK = 0, oQ = oK + L::szK, oB = oQ + L::szK, oBt = oB + 256, oDa = oBt + 256;
+    static constexpr size_t oA = oDa + 256, oT = oA + L::szA, oN = oT + L::szT, oP = oN + L::szN;
+    static constexpr size_t oDT = oP + szX, oXs = oDT + szX, oL = oXs + szX, total = oL + szX;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
+    using E = __bf16;
+    using TR = Tr<E>;
+    using F = typename TR::F;
+    using L = Ld<E, DK>;
+    using LY = FinLds<DK>;
+    constexpr int NMT = DK / 16, LT = LY::LT;
+    static_assert(LY::total <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
+    E *Ks = reinterpret_cast<E *>(smem + LY::oK), *Qs = reinterpret_cast<E *>(smem + LY::oQ);
+    float *Bs = reinterpret_cast<float *>(smem + LY::oB), *Bt = reinterpret_cast<float *>(smem + LY::oBt);
+    float *dba = reinterpret_cast<float *>(smem + LY::oDa), *As = reinterpret_cast<float *>(smem + LY::oA);
+    E *TsT = reinterpret_cast<E *>(smem + LY::oT), *NsT = reinterpret_cast<E *>(smem + LY::oN);
+    E *dPs = reinterpret_cast<E *>(smem + LY::oP), *dTs = reinterpret_cast<E *>(smem + LY::oDT);
+    E *Xs = reinterpret_cast<E *>(smem + LY::oXs), *dLs = reinterpret_cast<E *>(smem + LY::oL);
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int u = blockIdx.x / a.NC, r = blockIdx.x - u * a.NC;
+    const int b = u / a.H, h = u - b * a.H;
+    const int64_t tok0 = (int64_t)b * a.T, sqk = (int64_t)a.H * DK;
+    const int units = a.B * a.H, nval = min(kChunk, a.T - r * kChunk);
+
+    Stager<E, DK> sg;
+    sg.sqk = sqk;
+    sg.sv = 0;
+    sg.kg = reinterpret_cast<const E *>(a.k) + tok0 * sqk + (int64_t)h * DK;
+    sg.qg = reinterpret_cast<const E *>(a.q) + tok0 * sqk + (int64_t)h * DK;
+    sg.vg = nullptr;
+    sg.bg = reinterpret_cast<const E *>(a.beta) + tok0 * a.H + h;
+    sg.gg = nullptr;
+    sg.qh = nullptr;
+    sg.gh = nullptr;
+    sg.sb = SubstepBase{0, 0u, 1u};
+    sg.H = a.H;
+    sg.len = a.T;
+    sg.tid = tid;
+    sg.has_v = false;
+    sg.rbeta = TR::fromf(0.f);
+    sg.rg = 0.f;
+    sg.nval = 0;
+    sg.load(r);
+    for (int i = tid; i < kChunk * LT; i += kThreads) TsT[i] = TR::fromf(0.f);
+    sg.store_kqb(Ks, Qs, Bs, nullptr);
+    if (w == 0) Bt[lane] = lane < nval ? TR::tof(sg.rbeta) : 0.f;
+
+    // Partial sums over the value tiles: dP, dT (lower-inclusive, to LDS) and
+    // dQ, dK (this wave's token rows, in registers).
+    const size_t PB = bwd_part_floats(DK);
+    for (int idx = tid; idx < 64 * 64; idx += kThreads) {
+        const int row = idx >> 6, col = idx & 63;
+        float p = 0.f, t = 0.f;
+        for (int tau = 0; tau < a.n_tiles; ++tau) {
+            const float *pb = a.part + (((int64_t)tau * units + u) * a.NC + r) * PB;
+            p += pb[idx];
+            t += pb[4096 + idx];
+        }
+        dPs[row * LT + col] = TR::fromf(col <= row ? p : 0.f);
+        dTs[row * LT + col] = TR::fromf(col <= row ? t : 0.f);
+    }
+    f32x4 dQa[NMT], dKa[NMT];
+#pragma unroll
+    for (int m = 0; m < NMT; ++m) {
+        dQa[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dKa[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int tau = 0; tau < a.n_tiles; ++tau) {
+        const float *pb = a.part + (((int64_t)tau * units + u) * a.NC + r) * PB + 8192;
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dQa[m][i] += pb[(16 * w + 4 * g + i) * DK + 16 * m + c16];
+                dKa[m][i] += pb[64 * DK + (16 * w + 4 * g + i) * DK + 16 * m + c16];
+            }
+    }
+    __syncthreads();
+    // As = diag(beta) L (Gram phase), then N^T into TsT (solve with beta = 1)
+    bwd_solve<DK, false, true>(Ks, Qs, Bs, As, nullptr, TsT, NsT, w, lane, g, c16);
+
+    // This wave's token rows t = 16w + 4g + i:
+    //   X = N^T dT -> dbeta_a = diag X, Xs = X diag(beta)
+    //   G = K K^T (Gram, unscaled)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            x = TR::mma16(x, ldrow(TsT, L::T, 16 * w + c16, 16 * rb, g), TR::ldcol(dTs, LT, 16 * rb, 16 * j, g, c16));
+        const float bc = Bt[16 * j + c16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (j == w && c16 == 4 * g + i) dba[16 * w + 4 * g + i] = x[i];
+            Xs[(16 * w + 4 * g + i) * LT + 16 * j + c16] = TR::fromf(x[i] * bc);
+        }
+    }
+    __syncthreads();
+    // dA = -(X diag(beta)) N^T, strictly lower; dbeta_b = sum_j dA_tj G_tj; dL = diag(beta) dA
+    float dbb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f32x4 da = {0.f, 0.f, 0.f, 0.f}, gm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            da = TR::mma16(da, ldrow(Xs, LT, 16 * w + c16, 16 * rb, g), TR::ldcol(TsT, L::T, 16 * rb, 16 * j, g, c16));
+#pragma unroll
+        for (int kd = 0; kd < NMT; ++kd)
+            gm = TR::mma16(gm, ldrow(Ks, L::K, 16 * w + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
+            const float dai = col < t ? -da[i] : 0.f;
+            dbb[i] += dai * gm[i];
+            dLs[t * LT + col] = TR::fromf(Bt[t] * dai);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) // sum over the 16 lanes of the row group
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) dbb[i] += __shfl_xor(dbb[i], o, 16);
+    __syncthreads();
+    // dQ += dP K;  dK += dP^T Q + (dL + dL^T) K
+#pragma unroll
+    for (int m = 0; m < NMT; ++m)
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            const F kc = TR::ldcol(Ks, L::K, 16 * sb, 16 * m, g, c16);
+            dQa[m] = TR::mma16(dQa[m], ldrow(dPs, LT, 16 * w + c16, 16 * sb, g), kc);
+            dKa[m] = TR::mma16(dKa[m], TR::ldcol(dPs, LT, 16 * sb, 16 * w, g, c16), TR::ldcol(Qs, L::K, 16 * sb, 16 * m, g, c16));
+            dKa[m] = TR::mma16(dKa[m], ldrow(dLs, LT, 16 * w + c16, 16 * sb, g), kc);
+            dKa[m] = TR::mma16(dKa[m], TR::ldcol(dLs, LT, 16 * sb, 16 * w, g, c16), kc);
+        }
+    E *dqg = reinterpret_cast<E *>(a.dq) + (tok0 + (int64_t)r * kChunk) * sqk + (int64_t)h * DK;
+    E *dkg = reinterpret_cast<E *>(a.dk) + (tok0 + (int64_t)r * kChunk) * sqk + (int64_t)h * DK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 16 * w + 4 * g + i;
+        if (t < nval) {
+#pragma unroll
+            for (int m = 0; m < NMT; ++m) {
+                dqg[(int64_t)t * sqk + 16 * m + c16] = TR::fromf(dQa[m][i]);
+                dkg[(int64_t)t * sqk + 16 * m + c16] = TR::fromf(dKa[m][i]);
+            }
+            if (c16 == 0)
+                reinterpret_cast<E *>(a.dbeta)[(tok0 + (int64_t)r * kChunk + t) * a.H + h] = TR::fromf(dba[t] + dbb[i]);
+        }
+    }
+}
+
+__global__ void fill_kernel(float *p, size_t n, float value) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+template <int DK, int DV> hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t s) {
+    const int units = a.B * a.H;
+    if (units <= 0 || a.NC <= 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_chain_kernel<DK, DV>), dim3(units * a.n_tiles), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_finish_kernel<DK, DV>), dim3(units * a.NC), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 } // namespace
 
 hipError_t launch_chain(int dtype, int dk, int dv, bool write_o, const ChainArgs &a,
                         hipStream_t stream) {
     if (dtype == 1) return launch_chain_bf16(dk, dv, write_o, a, stream);
     return write_o ? launch_dims_f32<true>(dk, dv, a, stream) : launch_dims_f32<false>(dk, dv, a, stream);
+}
+
+hipError_t launch_fill(float *p, size_t n, float value, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream) {
+    if (dk == 128 && dv == 128) return launch_bwd_dims<128, 128>(a, stream);
+    if (dk == 128 && dv == 64) return launch_bwd_dims<128, 64>(a, stream);
+    if (dk == 64 && dv == 128) return launch_bwd_dims<64, 128>(a, stream);
+    if (dk == 64 && dv == 64) return launch_bwd_dims<64, 64>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_compose(int dk, int dv, const ChainArgs &a, hipStream_t stream) {

@@ -198,6 +198,31 @@ int deltanet_decode_step(const void *q, const void *k, const void *v, const void
                          int dtype, hipStream_t stream);
 
 /*
+ * Backward pass of deltanet_fwd (DN_BF16 only): gradients for upstream dO of
+ * the output and dS_final of the final state. The pages give no backward
+ * pass; this is the chain rule applied to the per-chunk algorithm above (see
+ * the kernels' notes), exact up to rounding, with bf16 matrix-core operands
+ * and fp32 accumulation.
+ *   q, k, v, beta, S0 : the forward inputs (S0 NULL: zero)
+ *   dO      : [B,T,H,dv] (dtype);  dS_final : [B,H,dv,dk] fp32 or NULL (zero)
+ *   dq, dk, dv, dbeta : outputs, layouts of q, k, v, beta (dtype)
+ *   dS0     : [B,H,dv,dk] fp32 output, or NULL to skip
+ *   workspace : at least deltanet_bwd_workspace_bytes(...) bytes, 16-byte
+ *             aligned: the state entering each chunk and per-chunk partial sums
+ * Three launches: the forward chain keeping the per-chunk states, the reverse
+ * chain of the state gradient, and a chunk-parallel pass for dq, dk, dbeta.
+ * Errors as in deltanet_fwd (DN_ERR_UNSUPPORTED for DN_F32).
+ */
+int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta,
+                 const float *S0, const void *dO, const float *dS_final, void *dq, void *dk,
+                 void *dv, void *dbeta, float *dS0, int B, int H, int T, int dk_, int dv_,
+                 int chunk, int dtype, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Bytes of workspace deltanet_bwd needs (0 for invalid shapes). */
+size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+
+/*
  * Bytes of workspace deltanet_fwd (or deltanet_gated_fwd) needs for this
  * shape and cp_groups (0 means the library's choice on the current device).
  * Returns 0 when the resolved group count is 1, and also for invalid shapes.

@@ -168,3 +168,27 @@ def test_gated_long_context_parallel_sampled():
     es = rel_err(f64(Sf[0, h]), rs[0, 0])
     print(f"  gated {w.name} head {h}: err o={eo:.3e} S={es:.3e}", flush=True)
     assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_bwd_layer_b8_h16_t4096_sampled():
+    # the backward pass at the benchmark's full shape, sampled units against the oracle
+    w = WORKLOADS["layer_b8_h16_t4096"]
+    print(f"[case] {w.name} full size, backward", flush=True)
+    q, k, v, beta, S0 = workload_inputs(w, seed=2, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(9)
+    dO = torch.randn(v.shape, generator=g, device=DEV, dtype=torch.float32).to(v.dtype)
+    out = dn.deltanet_bwd(q, k, v, beta, dO, S0)
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(x).all()) for x in out)
+    units = [(0, 0), (5, 11)]
+    sel = lambda x, b, h: f64(x[b:b + 1, :, h:h + 1])
+    cat = lambda xs: np.concatenate(xs, axis=0)
+    ref = oracle.deltanet_bwd(*(cat([sel(x, b, h) for b, h in units]) for x in (q, k, v, beta, dO)))
+    for name, i, gi in (("dq", 0, out[0]), ("dk", 1, out[1]), ("dv", 2, out[2])):
+        e = rel_err(np.stack([f64(gi[b, :, h]) for b, h in units]), ref[i][:, :, 0])
+        print(f"  {name} err {e:.3e}", flush=True)
+        assert e <= 2e-2
+    eb = rel_err(np.stack([f64(out[3][b, :, h]) for b, h in units]), ref[3][:, :, 0])
+    es = rel_err(np.stack([f64(out[4][b, h]) for b, h in units]), ref[4][:, 0])
+    print(f"  dbeta err {eb:.3e} dS0 err {es:.3e}", flush=True)
+    assert eb <= 2e-2 and es <= 2e-2
