@@ -122,6 +122,14 @@ def make_gates(shape, seed: int = 0, device: str = "cpu", mu: float = 2.0):
     return torch.nn.functional.logsigmoid(x)
 
 
+def make_channel_gates(shape, seed: int = 0, device: str = "cpu", mu: float = 2.0):
+    """Per-channel log decays for KDA, g = log sigmoid(N(mu, 1)) per element,
+    fp32, shape [B, T, H, dk]; own generator seeded with ``seed + 130363``."""
+    g = _gen(device, seed + 130363)
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32) + mu
+    return torch.nn.functional.logsigmoid(x)
+
+
 def make_varlen_inputs(lengths, H: int, dk: int, dv: int, dtype: str = "bf16", seed: int = 0,
                        device: str = "cpu", s0_std: float = 0.0):
     """Packed inputs for sequences of the given lengths.

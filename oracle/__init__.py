@@ -33,6 +33,9 @@ by Haoran Zhang, "p1" is "Context Parallelism for DeltaNet" by yywangcs):
   correction); ``gated_chunked_fwd`` -- that section's "Complete per-chunk
   algorithm"; ``householder_states``, ``exact_states`` and
   ``cp_group_transition`` take the decays as an optional argument.
+* ``kda_fwd`` -- Kimi Delta Attention token by token (p3 "Kimi Delta
+  Attention (KDA)": decay per key channel, then the delta rule), in C;
+  ``kda_chunked_fwd`` -- that section's complete per-chunk algorithm.
 * ``deltanet_bwd`` -- the backward pass: reverse mode of the token-serial
   recurrence in fp64 (C), with the states recomputed from checkpoints.
 * ``gdp_fwd`` -- Gated Delta Product token by token with its substeps (p3
@@ -106,6 +109,9 @@ def load(path: str = _LIB_PATH):
     lib.oracle_deltanet_bwd.argtypes = [dp] * 12 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                                     ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.oracle_deltanet_bwd.restype = ctypes.c_int
+    lib.oracle_kda_fwd.argtypes = [dp] * 8 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int]
+    lib.oracle_kda_fwd.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     if path == _LIB_PATH:
@@ -227,6 +233,86 @@ def gated_deltanet_fwd_varlen(q, k, v, beta, g, cu_seqlens, S0=None, nthreads: i
                                               N, H, dk, dv, int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_gated_deltanet_fwd_varlen failed with {rc}")
+    return o, Sf
+
+
+def kda_fwd(q, k, v, beta, g, S0=None, nthreads: int = 0, lib=None):
+    """Token-serial fp64 Kimi Delta Attention (KDA) forward.
+
+    p3 "Kimi Delta Attention (KDA)" (transposed state): the state decays per
+    key channel, S <- S Diag(exp(g_t)), then the delta-rule correction
+    applies; g: [B,T,H,dk]. Returns (o [B,T,H,dv], S_final [B,H,dv,dk]).
+    """
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    assert g.shape == k.shape and beta.shape == (B, T, H)
+    S0 = None if S0 is None else _f64(S0)
+    o = np.empty((B, T, H, dv))
+    Sf = np.empty((B, H, dv, dk))
+    lib = lib or load()
+    rc = lib.oracle_kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o), _ptr(Sf),
+                            B, H, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_kda_fwd failed with {rc}")
+    return o, Sf
+
+
+def kda_chunked_unit(q, k, v, beta, a, S, C):
+    """One unit of KDA, chunk size C, in the page's order and notation.
+
+    p3 "Kimi Delta Attention (KDA)" > "Complete per-chunk algorithm" (state
+    transposed): per chunk, with lambda[i:j] the elementwise product of the
+    decay vectors a_i .. a_j (ones when i > j),
+        <-q_l = lambda[1:l] * q_l, <-k_l = lambda[1:l] * k_l, ->k_l = lambda[l+1:C] * k_l,
+        A[l, m] = q_l . (lambda[m+1:l] * k_m) for m <= l,
+        L[l, m] = k_l . (lambda[m+1:l] * k_m) for m < l,
+        (I + B L) T = B,  U = T V,  <-W = T <-K,  Z = U - <-W S^T,
+        O = <-Q S^T + A Z,  S <- S Diag(lambda[1:C]) + Z^T ->K.
+    a: [L, dk] decays (not logarithms).
+    """
+    Ltot, dk = k.shape
+    o = np.zeros((Ltot, v.shape[1]))
+    S = np.array(S, dtype=np.float64, copy=True)
+    for c0 in range(0, Ltot, C):
+        Kr, Qr, Vr, br, ar = k[c0:c0 + C], q[c0:c0 + C], v[c0:c0 + C], beta[c0:c0 + C], a[c0:c0 + C]
+        n = Kr.shape[0]
+
+        def lam(i, j):  # 1-based inclusive elementwise product a_i ... a_j
+            return np.prod(ar[i - 1:j], axis=0) if i <= j else np.ones(dk)
+
+        Qb = np.stack([lam(1, l) * Qr[l - 1] for l in range(1, n + 1)])
+        Kb = np.stack([lam(1, l) * Kr[l - 1] for l in range(1, n + 1)])
+        Kf = np.stack([lam(l + 1, n) * Kr[l - 1] for l in range(1, n + 1)])
+        Am = np.zeros((n, n))
+        Lm = np.zeros((n, n))
+        for l in range(1, n + 1):
+            for m in range(1, l + 1):
+                wk = lam(m + 1, l) * Kr[m - 1]
+                Am[l - 1, m - 1] = Qr[l - 1] @ wk
+                if m < l:
+                    Lm[l - 1, m - 1] = Kr[l - 1] @ wk
+        T = forward_substitution_T(Lm, br)
+        U = T @ Vr
+        Wb = T @ Kb
+        Z = U - Wb @ S.T
+        o[c0:c0 + C] = Qb @ S.T + Am @ Z
+        S = S * lam(1, n)[None, :] + Z.T @ Kf
+    return o, S
+
+
+def kda_chunked_fwd(q, k, v, beta, g, S0=None, chunk: int = 64):
+    """Chunked fp64 KDA over [B,T,H,*] inputs (g: [B,T,H,dk] log decays)."""
+    q, k, v, beta, g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g)
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    Sf = np.zeros((B, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dv, dk)) if S0 is None else _f64(S0)[b, h]
+            o[b, :, h], Sf[b, h] = kda_chunked_unit(q[b, :, h], k[b, :, h], v[b, :, h], beta[b, :, h],
+                                                    np.exp(g[b, :, h]), S, chunk)
     return o, Sf
 
 

@@ -208,6 +208,85 @@ int oracle_gated_deltanet_fwd_varlen(const double *q, const double *k, const dou
 }
 
 /*
+ * Kimi Delta Attention (KDA), "Linear Attention, Visualized", section "Kimi
+ * Delta Attention (KDA)": the previous state first decays channel by channel
+ * (one decay a_{t,j} = exp(g_{t,j}) per key channel j), then the delta-rule
+ * correction applies. In the column convention (S is dv x dk, key channels
+ * are columns):
+ *     Sd = S_{t-1} Diag(a_t);  vhat = Sd k_t;  S_t = Sd + beta_t (v_t - vhat) k_t^T;  o_t = S_t q_t.
+ * g: [B, T, H, dk] (log decays per channel).
+ */
+static void unit_forward_kda(const double *q, const double *k, const double *v, const double *beta,
+                             const double *g, double *o, ptrdiff_t qk_stride, ptrdiff_t vo_stride,
+                             ptrdiff_t beta_stride, int64_t L, int dk, int dv, double *S, double *vhat)
+{
+    for (int64_t t = 0; t != L; ++t) {
+        const double *kt = k + t * qk_stride, *qt = q + t * qk_stride, *vt = v + t * vo_stride;
+        const double *gt = g + t * qk_stride;
+        const double bt = beta[t * beta_stride];
+        for (int i = 0; i < dv; ++i)
+            for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= exp(gt[j]);
+        for (int i = 0; i < dv; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * kt[j];
+            vhat[i] = acc;
+        }
+        for (int i = 0; i < dv; ++i) {
+            const double corr = bt * (vt[i] - vhat[i]);
+            for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] += corr * kt[j];
+        }
+        if (o) {
+            double *ot = o + t * vo_stride;
+            for (int i = 0; i < dv; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * qt[j];
+                ot[i] = acc;
+            }
+        }
+    }
+}
+
+int oracle_kda_fwd(const double *q, const double *k, const double *v, const double *beta, const double *g,
+                   const double *S0, double *o, double *S_final, int B, int H, int64_t T, int dk, int dv,
+                   int nthreads)
+{
+    if (!q || !k || !v || !beta || !g || B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
+    const ptrdiff_t qk_stride = (ptrdiff_t)H * dk, vo_stride = (ptrdiff_t)H * dv;
+    const size_t sz = (size_t)dv * dk;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * (sz + (size_t)dv));
+        if (!S) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < (int64_t)B * H; ++u) {
+                const int64_t b = u / H;
+                const int h = (int)(u % H);
+                const int64_t t0 = b * T;
+                if (S0) memcpy(S, S0 + (size_t)u * sz, sizeof(double) * sz);
+                else memset(S, 0, sizeof(double) * sz);
+                unit_forward_kda(q + t0 * qk_stride + (ptrdiff_t)h * dk, k + t0 * qk_stride + (ptrdiff_t)h * dk,
+                                 v + t0 * vo_stride + (ptrdiff_t)h * dv, beta + t0 * H + h,
+                                 g + t0 * qk_stride + (ptrdiff_t)h * dk,
+                                 o ? o + t0 * vo_stride + (ptrdiff_t)h * dv : NULL, qk_stride, vo_stride, H, T, dk,
+                                 dv, S, S + sz);
+                if (S_final) memcpy(S_final + (size_t)u * sz, S, sizeof(double) * sz);
+            }
+            free(S);
+        }
+    }
+    return failed ? -2 : 0;
+}
+
+/*
  * Backward pass of the DeltaNet recurrence (reverse mode of the token-serial
  * definition above, in fp64). For a loss with upstream gradients dO_t of the
  * outputs and dS_T of the final state, reading the recurrence backwards:

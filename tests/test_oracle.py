@@ -510,6 +510,90 @@ def pin_bwd_state_gradient_closed_form(lib):
     return _rel(dS0[0, 0], ref) < 1e-12
 
 
+# ---- Kimi Delta Attention (p3 "Kimi Delta Attention (KDA)"): per-channel decay
+
+def _kda_case(seed, B=1, T=23, H=2, dk=6, dv=4):
+    rng = np.random.default_rng(seed)
+    q, k, v, beta, S0 = _inputs(rng, B=B, T=T, H=H, dk=dk, dv=dv)
+    g = _gates(rng, (B, T, H, dk), lo=0.2)
+    return rng, q, k, v, beta, g, S0
+
+
+def pin_kda_scalar_decay_is_gdn(lib):
+    rng, q, k, v, beta, g, S0 = _kda_case(80)
+    gs = np.repeat(g[..., :1], g.shape[-1], axis=-1)
+    o, Sf = oracle.kda_fwd(q, k, v, beta, gs, S0, lib=lib)
+    ro, rs = oracle.gated_deltanet_fwd(q, k, v, beta, gs[..., 0], S0, lib=lib)
+    return _rel(o, ro) < RTOL and _rel(Sf, rs) < RTOL
+
+
+def pin_kda_beta_zero(lib):
+    # no writes: each key channel (column of S) decays on its own
+    rng, q, k, v, beta, g, S0 = _kda_case(81)
+    beta[:] = 0
+    o, Sf = oracle.kda_fwd(q, k, v, beta, g, S0, lib=lib)
+    lam = np.exp(np.cumsum(g, axis=1))  # [B, T, H, dk]
+    ref_o = np.einsum("bhij,bthj->bthi", S0, lam * q)
+    ref_s = S0 * lam[:, -1][:, :, None, :]
+    return _rel(o, ref_o) < RTOL and _rel(Sf, ref_s) < RTOL
+
+
+def pin_kda_single_token(lib):
+    rng, q, k, v, beta, g, S0 = _kda_case(82, T=1)
+    o, Sf = oracle.kda_fwd(q, k, v, beta, g, S0, lib=lib)
+    ok = True
+    for h in range(2):
+        b, a = beta[0, 0, h], np.exp(g[0, 0, h])
+        kk, vv, qq = k[0, 0, h], v[0, 0, h], q[0, 0, h]
+        S1 = S0[0, h] @ np.diag(a) @ (np.eye(len(kk)) - b * np.outer(kk, kk)) + b * np.outer(vv, kk)
+        ok &= _rel(Sf[0, h], S1) < RTOL and _rel(o[0, 0, h], S1 @ qq) < RTOL
+    return bool(ok)
+
+
+def pin_kda_one_hot_keys(lib):
+    # keys on distinct standard basis vectors from a zero start: no prediction
+    # fires, and o_t = sum_{i<=t} b_i v_i q_t[j_i] prod_{s=i+1..t} a_{s, j_i}
+    rng = np.random.default_rng(83)
+    dk, T = 8, 8
+    perm = rng.permutation(dk)
+    k = np.eye(dk)[perm][None, :, None]
+    q = _unit_rows(rng, (1, T, 1, dk))
+    v = rng.standard_normal((1, T, 1, 3))
+    beta = rng.uniform(0.1, 1.0, size=(1, T, 1))
+    a = rng.uniform(0.2, 1.0, size=(T, dk))
+    o, _ = oracle.kda_fwd(q, k, v, beta, np.log(a)[None, :, None], None, lib=lib)
+    ref = np.zeros((T, 3))
+    for t in range(T):
+        for i in range(t + 1):
+            j = perm[i]
+            ref[t] += beta[0, i, 0] * np.prod(a[i + 1:t + 1, j]) * q[0, t, 0, j] * v[0, i, 0]
+    return _rel(o[0, :, 0], ref) < 1e-12
+
+
+def pin_kda_read_back(lib):
+    # unit keys: S_t k_t = (1 - b_t) S_{t-1} Diag(a_t) k_t + b_t v_t
+    rng, q, k, v, beta, g, S0 = _kda_case(84, T=8, H=1)
+    ok = True
+    prev = S0[0, 0]
+    for t in range(8):
+        _, St = oracle.kda_fwd(q[:, :t + 1], k[:, :t + 1], v[:, :t + 1], beta[:, :t + 1], g[:, :t + 1], S0,
+                               lib=lib)
+        kt, b, a = k[0, t, 0], beta[0, t, 0], np.exp(g[0, t, 0])
+        ok &= _rel(St[0, 0] @ kt, (1 - b) * (prev @ (a * kt)) + b * v[0, t, 0]) < 1e-11
+        prev = St[0, 0]
+    return bool(ok)
+
+
+def pin_kda_chunked_agreement(lib):
+    rng, q, k, v, beta, g, S0 = _kda_case(85, T=45)
+    o, Sf = oracle.kda_fwd(q, k, v, beta, g, S0, lib=lib)
+    ok = True
+    for C in (1, 2, 16, 45):
+        co, cs = oracle.kda_chunked_fwd(q, k, v, beta, g, S0, chunk=C)
+        ok &= _rel(co, o) < 1e-10 and _rel(cs, Sf) < 1e-10
+    return bool(ok)
+
+
 PINS = [pin_golden_three_tokens, pin_golden_three_tokens_lambda, pin_golden_alice_bob,
         pin_beta_zero, pin_single_token, pin_read_back, pin_orthonormal_keys,
         pin_householder_products, pin_square_householder, pin_exact_rationals,
@@ -518,7 +602,9 @@ PINS = [pin_golden_three_tokens, pin_golden_three_tokens_lambda, pin_golden_alic
         pin_gated_read_back, pin_gated_orthonormal_keys, pin_gated_reset,
         pin_gated_householder, pin_gated_exact_rationals, pin_gated_chunked_agreement,
         pin_gated_resume_and_varlen, pin_bwd_finite_differences, pin_bwd_linear_inputs_exact,
-        pin_bwd_zero_upstream_and_empty, pin_bwd_state_gradient_closed_form]
+        pin_bwd_zero_upstream_and_empty, pin_bwd_state_gradient_closed_form,
+        pin_kda_scalar_decay_is_gdn, pin_kda_beta_zero, pin_kda_single_token, pin_kda_one_hot_keys,
+        pin_kda_read_back, pin_kda_chunked_agreement]
 
 
 def failed_pins(lib):
@@ -575,6 +661,12 @@ MUTANTS = {
     "bwd_state_gradient_sign": ("G[(size_t)i * dk_ + j] -= bt * du[i] * kt[j];",
                                 "G[(size_t)i * dk_ + j] += bt * du[i] * kt[j];"),
     "bwd_beta_gradient_scaled": ("dbeta[t * beta_stride] = db;", "dbeta[t * beta_stride] = bt * db;"),
+    "kda_decay_of_channel0": ("for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= exp(gt[j]);",
+                              "for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= exp(gt[0]);"),
+    "kda_decay_by_value_row": ("for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= exp(gt[j]);",
+                               "for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= exp(gt[i % dk]);"),
+    "kda_dropped_decay": ("for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= exp(gt[j]);",
+                          "for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= 1.0;"),
     "read_before_write": ("        /* write: S += beta_t (v_t - vhat) k_t^T */",
                           "        if (o) { double *ot = o + t * vo_stride;"
                           " for (int i = 0; i < dv; ++i) { const double *Si = S + (size_t)i * dk;"
