@@ -14,7 +14,8 @@ per-token log decays) instead; without it, a short gated run of the same
 workload is reported under ``variants.gated`` next to the headline figures.
 ``variants.bwd`` times ``deltanet_bwd`` (the backward pass: forward chain with
 per-chunk states, reverse state-gradient chain, chunk-parallel finish) on the
-same workload. ``variants.gdp`` times ``deltanet_gdp_fwd`` (Gated Delta Product, n_h = 2 substeps
+same workload. ``variants.kda`` times ``deltanet_kda_fwd`` (per-channel decay) on the same
+workload. ``variants.gdp`` times ``deltanet_gdp_fwd`` (Gated Delta Product, n_h = 2 substeps
 per token) on the same B, H, T and widths. ``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
 head, state updated in place) on B=256 H=16 d=128 bf16, a 256 MiB state.
 
@@ -180,6 +181,27 @@ def bwd_variant(dev, w, inputs, fwd_ms, steps=10, warmup=3):
             "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1), "avg_launch_us": round(launch_ms * 1e3, 2),
             "vs_forward_time": round(launch_ms / fwd_ms, 3), "algorithmic_bytes": nbytes,
             "workspace_bytes": need, "hbm_frac_algorithmic": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4)}
+
+
+def kda_variant(dev, w, inputs, fwd_ms, steps=20, warmup=5):
+    """Time deltanet_kda_fwd on the workload with per-channel log decays
+    (synth.make_channel_gates). Bytes: q, k, v, beta, o plus g (fp32, dk per
+    head-token)."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import make_channel_gates
+
+    print("[bench] kda variant", file=sys.stderr, flush=True)
+    q, k, v, beta, S0 = inputs
+    g = make_channel_gates((w.B, w.T, w.H, w.dk), seed=8, device=str(dev))
+    o = torch.empty_like(v)
+    Sf = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+    ms, launch_ms, _ = time_steps(lambda: dn.deltanet_kda_fwd(q, k, v, beta, g, S0, o=o, S_final=Sf), warmup, steps)
+    nbytes = w.B * w.T * w.H * (2 * (2 * w.dk + 2 * w.dv + 1) + 4 * w.dk) + w.B * w.H * w.dv * w.dk * 4
+    return {"call": "deltanet_kda_fwd", "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1), "avg_launch_us": round(launch_ms * 1e3, 2),
+            "vs_deltanet_time": round(launch_ms / fwd_ms, 3), "algorithmic_bytes": nbytes,
+            "hbm_frac": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4)}
 
 
 def gdp_variant(dev, w, flops_per_head_step, peak_flops, nh=2, steps=20, warmup=5):
@@ -391,6 +413,7 @@ def main():
     if not args.gated and not args.no_variants and not w.varlen and w.dtype == "bf16":
         result.setdefault("variants", {})["bwd"] = bwd_variant(dev, w, inputs, avg_launch_ms)
         result["variants"]["gdp"] = gdp_variant(dev, w, flops / n_tokens / w.H, peak_flops)
+        result["variants"]["kda"] = kda_variant(dev, w, inputs, avg_launch_ms)
     if not args.gated and not args.no_variants:
         result.setdefault("variants", {})["decode"] = decode_variant(dev)
     if not args.no_cpu_baseline:

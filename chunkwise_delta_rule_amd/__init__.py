@@ -25,7 +25,7 @@ import os
 import torch
 
 __all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
-           "deltanet_gdp_fwd", "deltanet_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
+           "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
            "deltanet_workspace_bytes",
            "deltanet_pick_cp_groups", "deltanet_status_string", "longest_first_order",
            "library_path", "load_library", "DeltaNetError", "DN_F32", "DN_BF16"]
@@ -71,6 +71,8 @@ def load_library(path: str | None = None):
     lib.deltanet_gated_fwd_varlen.restype = i
     lib.deltanet_gdp_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.deltanet_gdp_fwd.restype = i
+    lib.deltanet_kda_fwd.argtypes = [vp] * 8 + [i, i, i, i, i, i, i, vp]
+    lib.deltanet_kda_fwd.restype = i
     lib.deltanet_bwd.argtypes = [vp] * 12 + [i, i, i, i, i, i, i, vp, sz, vp]
     lib.deltanet_bwd.restype = i
     lib.deltanet_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -395,3 +397,40 @@ def deltanet_bwd(q, k, v, beta, dO, S0=None, dS_final=None, *, chunk: int = 64, 
     if st != 0:
         raise DeltaNetError(st, "deltanet_bwd")
     return dq, dkk, dvv, db, dS0
+
+
+def deltanet_kda_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64, o=None, S_final=None,
+                     output_final_state: bool = True, stream=None):
+    """Kimi Delta Attention forward (C-ABI ``deltanet_kda_fwd``, bf16 only).
+
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H]; g: [B,T,H,dk] float32
+    per-channel log decays; S0: [B,H,dv,dk] fp32 or None. Returns (o, S_final).
+    """
+    lib = load_library()
+    if k.dim() != 4:
+        raise ValueError("k must be [B, T, H, dk]")
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    if dt != torch.bfloat16:
+        raise TypeError("deltanet_kda_fwd supports bfloat16 inputs only")
+    _check(q, "q", dt, dev, (B, T, H, dk))
+    _check(k, "k", dt, dev, (B, T, H, dk))
+    _check(v, "v", dt, dev, (B, T, H, dv))
+    _check(beta, "beta", dt, dev, (B, T, H))
+    _check(g, "g", torch.float32, dev, (B, T, H, dk))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(o, "o", dt, dev, (B, T, H, dv))
+    if output_final_state and S_final is None:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _check(S_final, "S_final", torch.float32, dev, (B, H, dv, dk))
+    with torch.cuda.device(dev):
+        st = lib.deltanet_kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o),
+                                  _ptr(S_final), B, H, T, dk, dv, chunk, DN_BF16, _stream_handle(stream))
+    if st != 0:
+        raise DeltaNetError(st, "deltanet_kda_fwd")
+    return o, S_final

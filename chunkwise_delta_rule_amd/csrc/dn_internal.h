@@ -57,6 +57,17 @@ struct DecodeArgs {
     int dv;
 };
 
+// Kimi Delta Attention forward (bf16): per-channel log decays g [B,T,H,dk] fp32.
+struct KdaArgs {
+    const void *q, *k, *v, *beta;
+    const float *g;
+    const float *S0;
+    void *o;
+    float *S_final;
+    int B, H, T;
+};
+hipError_t launch_kda(int dk, int dv, const KdaArgs &a, hipStream_t stream);
+
 // Backward pass (bf16): gradients of q, k, v, beta and S0 for upstream dO and
 // dS_final, from the per-chunk states S_chunks of a forward pass.
 struct BwdArgs {

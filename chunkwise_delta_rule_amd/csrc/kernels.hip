@@ -885,7 +885,7 @@ __device__ inline f32x4 widen_bf16(bf16x4 x) { return f32x4{(float)x[0], (float)
 // phases. ONES_AFTER_A: beta is replaced by ones after the Gram phase, so the
 // solve yields N^T instead of T^T.
 template <int DK, bool WITH_P, bool ONES_AFTER_A>
-__device__ inline void bwd_solve(const __bf16 *Ks, const __bf16 *Qs, float *Bs, float *As, __bf16 *Ps, __bf16 *TsT,
+__device__ __attribute__((always_inline)) inline void bwd_solve(const __bf16 *Ks, const __bf16 *Qs, float *Bs, float *As, __bf16 *Ps, __bf16 *TsT,
                                  __bf16 *NsT, int w, int lane, int g, int c16) {
     using PH = Phases<__bf16, DK>;
     using F = typename Tr<__bf16>::F;
@@ -1291,6 +1291,206 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Kimi Delta Attention (KDA) forward, bf16 operands.
+//
+// "Linear Attention, Visualized", "Kimi Delta Attention (KDA)": the state
+// (dv x dk here) first decays per key channel, S <- S Diag(a_t), then the
+// delta-rule correction applies. The page's "Complete per-chunk algorithm"
+// needs, inside a chunk, products k_l . (lambda[m+1:l] * k_m) whose decay
+// differs per channel, so no single row or column scaling of K K^T gives
+// them. The kernel therefore runs that algorithm on sub-chunks of 16 tokens
+// (the page's exactness holds for every chunk size): with gamma the
+// per-channel prefix sums of ln a inside a sub-chunk,
+//   Kl = K * exp(gamma),  Ql = Q * exp(gamma)          (<-K, <-Q; factors <= 1)
+//   Kr = K * exp(-gamma)                               (factors >= 1, bounded
+//                                                        by 16 tokens of decay)
+//   Kf = K * exp(gamma_16 - gamma)                     (->K; factors <= 1)
+//   L = Kl Kr^T (strictly lower),  A = Ql Kr^T (lower-inclusive),
+//   T = (I + diag(beta) L)^-1 diag(beta)               (the DPP diagonal solve)
+//   Y = V - Kl S^T,  Z = T Y,  O = Ql S^T + A Z,  S <- S Diag(exp(gamma_16)) + Z^T Kf.
+// Staging still moves 64-token chunks. Four waves; each wave holds 16 state
+// rows, computes the Gram/score tiles and the solve of one sub-chunk, then
+// runs the four sub-chunks' products for its rows in order.
+// Limit: exp(-gamma) must stay finite, i.e. every sum of 16 consecutive
+// log decays of one channel must exceed about -87 (g >= -5.4 suffices).
+// ---------------------------------------------------------------------------
+template <int DK> struct KdaLds {
+    using L = Ld<__bf16, DK>;
+    static constexpr size_t oK = 0, oQ = oK + L::szK, oKr = oQ + L::szK, oKf = oKr + L::szK;
+    static constexpr size_t oG = oKf + L::szK;                       // g tile, fp32 [64][DK]
+    static constexpr size_t oE = oG + sizeof(float) * 64 * DK;       // exp(gamma_16), fp32 [4][DK]
+    static constexpr size_t oV = oE + sizeof(float) * 4 * DK, oB = oV + L::szV, oA = oB + 256;
+    static constexpr size_t oT = oA + L::szA, oN = oT + L::szT, oP = oN + L::szN, total = oP + L::szT;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
+    using E = __bf16;
+    using TR = Tr<E>;
+    using F = typename TR::F;
+    using L = Ld<E, DK>;
+    using LY = KdaLds<DK>;
+    using PH = Phases<E, DK>;
+    constexpr int NMT = DK / 16;
+    static_assert(LY::total <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
+    E *Ks = reinterpret_cast<E *>(smem + LY::oK), *Qs = reinterpret_cast<E *>(smem + LY::oQ);
+    E *Kr = reinterpret_cast<E *>(smem + LY::oKr), *Kf = reinterpret_cast<E *>(smem + LY::oKf);
+    float *Gt = reinterpret_cast<float *>(smem + LY::oG), *E16 = reinterpret_cast<float *>(smem + LY::oE);
+    E *Vs = reinterpret_cast<E *>(smem + LY::oV);
+    float *Bs = reinterpret_cast<float *>(smem + LY::oB), *As = reinterpret_cast<float *>(smem + LY::oA);
+    E *TsT = reinterpret_cast<E *>(smem + LY::oT), *NsT = reinterpret_cast<E *>(smem + LY::oN);
+    E *Ps = reinterpret_cast<E *>(smem + LY::oP);
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int ntile = DV / 64;
+    const int u = blockIdx.x / ntile, tau = blockIdx.x - u * ntile;
+    const int b = u / a.H, h = u - b * a.H, row0 = 64 * tau;
+    const int64_t tok0 = (int64_t)b * a.T, sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
+    const int NC = (a.T + kChunk - 1) / kChunk;
+
+    Stager<E, DK> sg;
+    sg.sqk = sqk;
+    sg.sv = sv;
+    sg.kg = reinterpret_cast<const E *>(a.k) + tok0 * sqk + (int64_t)h * DK;
+    sg.qg = reinterpret_cast<const E *>(a.q) + tok0 * sqk + (int64_t)h * DK;
+    sg.vg = reinterpret_cast<const E *>(a.v) + tok0 * sv + (int64_t)h * DV + row0;
+    sg.bg = reinterpret_cast<const E *>(a.beta) + tok0 * a.H + h;
+    sg.gg = nullptr;
+    sg.qh = nullptr;
+    sg.gh = nullptr;
+    sg.sb = SubstepBase{0, 0u, 1u};
+    sg.H = a.H;
+    sg.len = a.T;
+    sg.tid = tid;
+    sg.has_v = true;
+    sg.rbeta = TR::fromf(0.f);
+    sg.rg = 0.f;
+    sg.nval = 0;
+    const float *gg = a.g + tok0 * sqk + (int64_t)h * DK;
+    E *og = reinterpret_cast<E *>(a.o) + tok0 * sv + (int64_t)h * DV + row0;
+
+    // state rows 16w + c16 of this tile: Sacc[m][i] = S[row0 + 16w + c16][16m + 4g + i]
+    f32x4 Sacc[NMT];
+#pragma unroll
+    for (int m = 0; m < NMT; ++m)
+        Sacc[m] = a.S0 ? *reinterpret_cast<const f32x4 *>(a.S0 + ((int64_t)u * DV + row0 + 16 * w + c16) * DK +
+                                                           16 * m + 4 * g)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int NG = 64 * DK / 4 / kThreads; // f32x4 pieces of the g tile per thread
+
+    for (int r = 0; r < NC; ++r) {
+        const int nval = min(kChunk, a.T - r * kChunk);
+        sg.load(r);
+        f32x4 gv[NG];
+#pragma unroll
+        for (int p = 0; p < NG; ++p) {
+            const int vi = p * kThreads + tid, row = vi / (DK / 4), c4 = vi % (DK / 4);
+            gv[p] = *reinterpret_cast<const f32x4 *>(gg + ((int64_t)r * kChunk + min(row, nval - 1)) * sqk + 4 * c4);
+        }
+        __syncthreads(); // the previous chunk's reads are done
+        sg.store_kqb(Ks, Qs, Bs, nullptr);
+        sg.store_v(Vs);
+#pragma unroll
+        for (int p = 0; p < NG; ++p) {
+            const int vi = p * kThreads + tid, row = vi / (DK / 4), c4 = vi % (DK / 4);
+            *reinterpret_cast<f32x4 *>(Gt + row * DK + 4 * c4) = row < nval ? gv[p] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+        // Per-channel prefix sums inside each sub-chunk (base 2) and the scaled
+        // operands; thread (channel d, sub-chunks j) walks its 16 tokens.
+        {
+            constexpr int PER = 4 * DK / kThreads; // sub-chunks per thread
+            const int d = tid % DK;
+#pragma unroll
+            for (int s2 = 0; s2 < PER; ++s2) {
+                const int j = (tid / DK) * PER + s2;
+                float gam[16], kraw[16], gsum = 0.f;
+#pragma unroll
+                for (int l = 0; l < 16; ++l) {
+                    const int row = 16 * j + l;
+                    gsum += Gt[row * DK + d] * 1.44269504088896340736f;
+                    gam[l] = gsum;
+                    const float kv = TR::tof(Ks[row * L::K + d]), qv = TR::tof(Qs[row * L::K + d]);
+                    kraw[l] = kv;
+                    const float el = __builtin_amdgcn_exp2f(gsum);
+                    Ks[row * L::K + d] = TR::fromf(kv * el);
+                    Qs[row * L::K + d] = TR::fromf(qv * el);
+                    Kr[row * L::K + d] = TR::fromf(kv * __builtin_amdgcn_exp2f(-gsum));
+                }
+                E16[j * DK + d] = __builtin_amdgcn_exp2f(gsum);
+#pragma unroll
+                for (int l = 0; l < 16; ++l) {
+                    const int row = 16 * j + l;
+                    Kf[row * L::K + d] = TR::fromf(kraw[l] * __builtin_amdgcn_exp2f(gsum - gam[l]));
+                }
+            }
+        }
+        __syncthreads();
+        // Sub-chunk w: L = Kl Kr^T (strictly lower, times beta of the row) and A = Ql Kr^T.
+        {
+            f32x4 lt = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NMT; ++m) {
+                const F kr = ldrow(Kr, L::K, 16 * w + c16, 16 * m, g);
+                lt = TR::mma16(lt, ldrow(Ks, L::K, 16 * w + c16, 16 * m, g), kr);
+                at = TR::mma16(at, ldrow(Qs, L::K, 16 * w + c16, 16 * m, g), kr);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * w + 4 * g + i;
+                As[row * L::A + 16 * w + c16] = c16 < 4 * g + i ? Bs[row] * lt[i] : 0.f;
+                Ps[row * L::T + 16 * w + c16] = TR::fromf(c16 <= 4 * g + i ? at[i] : 0.f);
+            }
+        }
+        __syncthreads();
+        {
+            typename PH::DiagFrags df;
+            PH::diag_fetch(df, As, Bs, w, c16);
+            sched_fence();
+            (void)PH::diag_compute(df, NsT, TsT, w, g, c16);
+        }
+        __syncthreads();
+        // The four sub-chunks in order, for this wave's 16 state rows.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            F SB[NMT], SBn[NMT];
+#pragma unroll
+            for (int m = 0; m < NMT; ++m) {
+                SB[m] = TR::cvt(Sacc[m]);
+                SBn[m] = TR::cvt(-Sacc[m]);
+            }
+            f32x4 y = widen_bf16(TR::ldcol(Vs, L::V, 16 * j, 16 * w, g, c16));
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NMT; ++m) {
+                y = TR::mma16(y, ldrow(Ks, L::K, 16 * j + c16, 16 * m, g), SBn[m]);
+                o = TR::mma16(o, ldrow(Qs, L::K, 16 * j + c16, 16 * m, g), SB[m]);
+            }
+            const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+            const F zb = TR::cvt(TR::mma16(z0, TR::ldcol(TsT, L::T, 16 * j, 16 * j, g, c16), TR::cvt(y)));
+            o = TR::mma16(o, ldrow(Ps, L::T, 16 * j + c16, 16 * j, g), zb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = 16 * j + 4 * g + i;
+                if (tok < nval) og[((int64_t)r * kChunk + tok) * sv + 16 * w + c16] = TR::fromf(o[i]);
+            }
+#pragma unroll
+            for (int m = 0; m < NMT; ++m) {
+                Sacc[m] *= *reinterpret_cast<const f32x4 *>(E16 + j * DK + 16 * m + 4 * g);
+                Sacc[m] = TR::mma16(Sacc[m], TR::ldcol(Kf, L::K, 16 * j, 16 * m, g, c16), zb);
+            }
+        }
+    }
+    if (a.S_final) {
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+            *reinterpret_cast<f32x4 *>(a.S_final + ((int64_t)u * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g) =
+                Sacc[m];
+    }
+}
+
 __global__ void fill_kernel(float *p, size_t n, float value) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = value;
@@ -1319,6 +1519,21 @@ hipError_t launch_fill(float *p, size_t n, float value, hipStream_t stream) {
     const size_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n, value);
     return hipGetLastError();
+}
+
+template <int DK, int DV> hipError_t launch_kda_dims(const KdaArgs &a, hipStream_t s) {
+    const int grid = a.B * a.H * (DV / 64);
+    if (grid <= 0 || a.T <= 0) return hipSuccess;
+    hipLaunchKernelGGL((kda_chain_kernel<DK, DV>), dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_kda(int dk, int dv, const KdaArgs &a, hipStream_t stream) {
+    if (dk == 128 && dv == 128) return launch_kda_dims<128, 128>(a, stream);
+    if (dk == 128 && dv == 64) return launch_kda_dims<128, 64>(a, stream);
+    if (dk == 64 && dv == 128) return launch_kda_dims<64, 128>(a, stream);
+    if (dk == 64 && dv == 64) return launch_kda_dims<64, 64>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream) {

@@ -198,6 +198,23 @@ int deltanet_decode_step(const void *q, const void *k, const void *v, const void
                          int dtype, hipStream_t stream);
 
 /*
+ * Kimi Delta Attention forward ("Linear Attention, Visualized", "Kimi Delta
+ * Attention (KDA)"), DN_BF16 only: the previous state decays per key
+ * channel, then the delta correction applies:
+ *     S_t = S_{t-1} Diag(a_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t,
+ * with a_t = exp(g_t) elementwise (state transposed as above).
+ *   g : [B, T, H, dk] float32 log decays, 16-byte aligned, required when T > 0.
+ * Evaluated with that section's complete per-chunk algorithm on sub-chunks of
+ * 16 tokens (exact for any chunk size); the in-sub-chunk growth factor
+ * exp(-sum of g over up to 16 tokens) must stay finite in fp32, which holds
+ * for g >= -5.4. Other arguments as in deltanet_fwd (serial chain only, no
+ * workspace).
+ */
+int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *beta,
+                     const float *g, const float *S0, void *o, float *S_final, int B, int H,
+                     int T, int dk, int dv, int chunk, int dtype, hipStream_t stream);
+
+/*
  * Backward pass of deltanet_fwd (DN_BF16 only): gradients for upstream dO of
  * the output and dS_final of the final state. The pages give no backward
  * pass; this is the chain rule applied to the per-chunk algorithm above (see

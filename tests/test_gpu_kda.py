@@ -1,0 +1,63 @@
+"""Kimi Delta Attention forward through the C-ABI vs the fp64 oracle.
+
+The oracle runs the KDA token recurrence of "Linear Attention, Visualized"
+("Kimi Delta Attention (KDA)": per-channel decay, then the delta rule) token
+by token; the library runs that section's per-chunk algorithm on 16-token
+sub-chunks. Cases: every (dk, dv), ragged lengths around chunk and sub-chunk
+boundaries, initial state, weak, strong and absent decay, and decay equal
+across channels against the Gated DeltaNet kernel. Bar: max|gpu - oracle| /
+max|oracle| within 2e-2 (bf16 operands), for o and for the final state.
+"""
+
+import pytest
+import torch
+
+import oracle
+from chunkwise_delta_rule_amd import deltanet_gated_fwd, deltanet_kda_fwd
+from chunkwise_delta_rule_amd.synth import make_channel_gates, make_inputs
+from helpers import TOL, f64, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_kda(B, H, T, dk, dv, seed, s0_std=0.3, mu=2.0):
+    print(f"[case] kda B={B} H={H} T={T} dk={dk} dv={dv} mu={mu}", flush=True)
+    q, k, v, beta, S0 = make_inputs(B, H, T, dk, dv, seed=seed, s0_std=s0_std)
+    g = make_channel_gates((B, T, H, dk), seed=seed, mu=mu)
+    d = [x.to(DEV) for x in (q, k, v, beta, g)]
+    o, Sf = deltanet_kda_fwd(*d, None if S0 is None else S0.to(DEV))
+    torch.cuda.synchronize()
+    ro, rs = oracle.kda_fwd(f64(q), f64(k), f64(v), f64(beta), f64(g), f64(S0))
+    eo, es = rel_err(f64(o), ro), rel_err(f64(Sf), rs)
+    print(f"  err o={eo:.3e} S={es:.3e}", flush=True)
+    return eo, es
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_kda_shapes_ragged(dk, dv):
+    eo, es = run_kda(2, 2, 200, dk, dv, seed=500 + dk + dv)
+    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 64, 65, 130])
+def test_kda_lengths(T):
+    eo, es = run_kda(1, 2, T, 128, 128, seed=510 + T)
+    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("mu", [-1.0, 6.0])
+def test_kda_strong_and_weak_decay(mu):
+    eo, es = run_kda(1, 2, 150, 128, 128, seed=520, mu=mu)
+    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+
+
+def test_kda_equal_channels_matches_gated_deltanet():
+    B, H, T = 1, 2, 140
+    q, k, v, beta, S0 = make_inputs(B, H, T, 128, 128, seed=530, s0_std=0.3)
+    gs = make_channel_gates((B, T, H, 1), seed=530).expand(B, T, H, 128).contiguous()
+    d = [x.to(DEV) for x in (q, k, v, beta)]
+    o1, s1 = deltanet_kda_fwd(*d, gs.to(DEV), S0.to(DEV))
+    o2, s2 = deltanet_gated_fwd(*d, gs[..., 0].contiguous().to(DEV), S0.to(DEV))
+    torch.cuda.synchronize()
+    assert rel_err(f64(o1), f64(o2)) < 2e-2 and rel_err(f64(s1), f64(s2)) < 2e-2

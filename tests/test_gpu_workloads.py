@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import chunkwise_delta_rule_amd as dn
-from chunkwise_delta_rule_amd.synth import WORKLOADS, make_gates, workload_inputs
+from chunkwise_delta_rule_amd.synth import WORKLOADS, make_channel_gates, make_gates, workload_inputs
 from helpers import TOL, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -192,3 +192,22 @@ def test_bwd_layer_b8_h16_t4096_sampled():
     es = rel_err(np.stack([f64(out[4][b, h]) for b, h in units]), ref[4][:, 0])
     print(f"  dbeta err {eb:.3e} dS0 err {es:.3e}", flush=True)
     assert eb <= 2e-2 and es <= 2e-2
+
+
+def test_kda_layer_b8_h16_t4096_sampled():
+    # KDA at the benchmark's full shape, sampled units against the oracle
+    w = WORKLOADS["layer_b8_h16_t4096"]
+    print(f"[case] {w.name} full size, kda", flush=True)
+    q, k, v, beta, S0 = workload_inputs(w, seed=2, device=DEV)
+    g = make_channel_gates((w.B, w.T, w.H, w.dk), seed=2, device=DEV)
+    o, Sf = dn.deltanet_kda_fwd(q, k, v, beta, g, S0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(Sf).all())
+    units = [(1, 1), (6, 14)]
+    sel = lambda x, b, h: f64(x[b:b + 1, :, h:h + 1])
+    cat = lambda xs: np.concatenate(xs, axis=0)
+    ro, rs = oracle.kda_fwd(*(cat([sel(x, b, h) for b, h in units]) for x in (q, k, v, beta, g)))
+    eo = rel_err(np.stack([f64(o[b, :, h]) for b, h in units]), ro[:, :, 0])
+    es = rel_err(np.stack([f64(Sf[b, h]) for b, h in units]), rs[:, 0])
+    print(f"  kda {w.name}: err o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= 2e-2 and es <= 2e-2
