@@ -1380,15 +1380,21 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
                        : f32x4{0.f, 0.f, 0.f, 0.f};
     constexpr int NG = 64 * DK / 4 / kThreads; // f32x4 pieces of the g tile per thread
 
-    for (int r = 0; r < NC; ++r) {
-        const int nval = min(kChunk, a.T - r * kChunk);
-        sg.load(r);
-        f32x4 gv[NG];
+    // Loads of chunk c into registers; issued one chunk ahead so that they
+    // overlap the previous chunk's products.
+    f32x4 gv[NG];
+    auto load_chunk = [&](int c) {
+        sg.load(c);
+        const int n = min(kChunk, a.T - c * kChunk);
 #pragma unroll
         for (int p = 0; p < NG; ++p) {
             const int vi = p * kThreads + tid, row = vi / (DK / 4), c4 = vi % (DK / 4);
-            gv[p] = *reinterpret_cast<const f32x4 *>(gg + ((int64_t)r * kChunk + min(row, nval - 1)) * sqk + 4 * c4);
+            gv[p] = *reinterpret_cast<const f32x4 *>(gg + ((int64_t)c * kChunk + min(row, n - 1)) * sqk + 4 * c4);
         }
+    };
+    if (NC > 0) load_chunk(0);
+    for (int r = 0; r < NC; ++r) {
+        const int nval = min(kChunk, a.T - r * kChunk);
         __syncthreads(); // the previous chunk's reads are done
         sg.store_kqb(Ks, Qs, Bs, nullptr);
         sg.store_v(Vs);
@@ -1398,6 +1404,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
             *reinterpret_cast<f32x4 *>(Gt + row * DK + 4 * c4) = row < nval ? gv[p] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         __syncthreads();
+        if (r + 1 < NC) load_chunk(r + 1);
         // Per-channel prefix sums inside each sub-chunk (base 2) and the scaled
         // operands; thread (channel d, sub-chunks j) walks its 16 tokens.
         {
