@@ -1392,10 +1392,27 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
             gv[p] = *reinterpret_cast<const f32x4 *>(gg + ((int64_t)c * kChunk + min(row, n - 1)) * sqk + 4 * c4);
         }
     };
+    // The output tile of a chunk ([64 tokens][64 values], bf16) is assembled in
+    // LDS over the Gram rows (free once the solve is done) and written as
+    // whole 128-byte rows after the next barrier.
+    E *Os = reinterpret_cast<E *>(As);
+    constexpr int LO = 64 + 8;
+    static_assert(sizeof(E) * 64 * LO <= L::szA, "output tile fits over the Gram rows");
+    auto flush_o = [&](int c) {
+        const int n = min(kChunk, a.T - c * kChunk);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
+            if (row < n)
+                *reinterpret_cast<typename TR::V *>(og + ((int64_t)c * kChunk + row) * sv + 8 * cv) =
+                    *reinterpret_cast<const typename TR::V *>(Os + row * LO + 8 * cv);
+        }
+    };
     if (NC > 0) load_chunk(0);
     for (int r = 0; r < NC; ++r) {
         const int nval = min(kChunk, a.T - r * kChunk);
         __syncthreads(); // the previous chunk's reads are done
+        if (r > 0) flush_o(r - 1);
         sg.store_kqb(Ks, Qs, Bs, nullptr);
         sg.store_v(Vs);
 #pragma unroll
@@ -1406,32 +1423,44 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
         __syncthreads();
         if (r + 1 < NC) load_chunk(r + 1);
         // Per-channel prefix sums inside each sub-chunk (base 2) and the scaled
-        // operands; thread (channel d, sub-chunks j) walks its 16 tokens.
+        // operands. Thread (channel pair, sub-chunk j) reads its 16 tokens'
+        // decays, keys and queries at once, then walks them.
         {
-            constexpr int PER = 4 * DK / kThreads; // sub-chunks per thread
-            const int d = tid % DK;
-#pragma unroll
-            for (int s2 = 0; s2 < PER; ++s2) {
-                const int j = (tid / DK) * PER + s2;
-                float gam[16], kraw[16], gsum = 0.f;
-#pragma unroll
-                for (int l = 0; l < 16; ++l) {
-                    const int row = 16 * j + l;
-                    gsum += Gt[row * DK + d] * 1.44269504088896340736f;
-                    gam[l] = gsum;
-                    const float kv = TR::tof(Ks[row * L::K + d]), qv = TR::tof(Qs[row * L::K + d]);
-                    kraw[l] = kv;
-                    const float el = __builtin_amdgcn_exp2f(gsum);
-                    Ks[row * L::K + d] = TR::fromf(kv * el);
-                    Qs[row * L::K + d] = TR::fromf(qv * el);
-                    Kr[row * L::K + d] = TR::fromf(kv * __builtin_amdgcn_exp2f(-gsum));
-                }
-                E16[j * DK + d] = __builtin_amdgcn_exp2f(gsum);
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            constexpr int NP = DK / 2; // channel pairs
+            for (int item = tid; item < 4 * NP; item += kThreads) {
+                const int j = item / NP, d = 2 * (item % NP);
+                f32x2 gl[16];
+                bf16x2 kl[16], ql[16];
 #pragma unroll
                 for (int l = 0; l < 16; ++l) {
                     const int row = 16 * j + l;
-                    Kf[row * L::K + d] = TR::fromf(kraw[l] * __builtin_amdgcn_exp2f(gsum - gam[l]));
+                    gl[l] = *reinterpret_cast<const f32x2 *>(Gt + row * DK + d);
+                    kl[l] = *reinterpret_cast<const bf16x2 *>(Ks + row * L::K + d);
+                    ql[l] = *reinterpret_cast<const bf16x2 *>(Qs + row * L::K + d);
                 }
+                f32x2 gam[16], acc = {0.f, 0.f};
+#pragma unroll
+                for (int l = 0; l < 16; ++l) {
+                    acc += gl[l] * 1.44269504088896340736f;
+                    gam[l] = acc;
+                }
+#pragma unroll
+                for (int l = 0; l < 16; ++l) {
+                    const int row = 16 * j + l;
+                    const f32x2 kv = {(float)kl[l][0], (float)kl[l][1]}, qv = {(float)ql[l][0], (float)ql[l][1]};
+                    const f32x2 el = {__builtin_amdgcn_exp2f(gam[l][0]), __builtin_amdgcn_exp2f(gam[l][1])};
+                    const f32x2 er = {__builtin_amdgcn_exp2f(-gam[l][0]), __builtin_amdgcn_exp2f(-gam[l][1])};
+                    const f32x2 ef = {__builtin_amdgcn_exp2f(acc[0] - gam[l][0]), __builtin_amdgcn_exp2f(acc[1] - gam[l][1])};
+                    const f32x2 a1 = kv * el, a2 = qv * el, a3 = kv * er, a4 = kv * ef;
+                    *reinterpret_cast<bf16x2 *>(Ks + row * L::K + d) = bf16x2{(__bf16)a1[0], (__bf16)a1[1]};
+                    *reinterpret_cast<bf16x2 *>(Qs + row * L::K + d) = bf16x2{(__bf16)a2[0], (__bf16)a2[1]};
+                    *reinterpret_cast<bf16x2 *>(Kr + row * L::K + d) = bf16x2{(__bf16)a3[0], (__bf16)a3[1]};
+                    *reinterpret_cast<bf16x2 *>(Kf + row * L::K + d) = bf16x2{(__bf16)a4[0], (__bf16)a4[1]};
+                }
+                *reinterpret_cast<f32x2 *>(E16 + j * DK + d) =
+                    f32x2{__builtin_amdgcn_exp2f(acc[0]), __builtin_amdgcn_exp2f(acc[1])};
             }
         }
         __syncthreads();
@@ -1462,33 +1491,45 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
         // The four sub-chunks in order, for this wave's 16 state rows.
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            // every LDS operand of the sub-chunk first, so their latency is paid once
+            F kl[NMT], ql[NMT], kf[NMT];
+            f32x4 ef[NMT];
+#pragma unroll
+            for (int m = 0; m < NMT; ++m) {
+                kl[m] = ldrow(Ks, L::K, 16 * j + c16, 16 * m, g);
+                ql[m] = ldrow(Qs, L::K, 16 * j + c16, 16 * m, g);
+                kf[m] = TR::ldcol(Kf, L::K, 16 * j, 16 * m, g, c16);
+                ef[m] = *reinterpret_cast<const f32x4 *>(E16 + j * DK + 16 * m + 4 * g);
+            }
+            const F vf = TR::ldcol(Vs, L::V, 16 * j, 16 * w, g, c16);
+            const F tf = TR::ldcol(TsT, L::T, 16 * j, 16 * j, g, c16);
+            const F pf = ldrow(Ps, L::T, 16 * j + c16, 16 * j, g);
+            sched_fence();
             F SB[NMT], SBn[NMT];
 #pragma unroll
             for (int m = 0; m < NMT; ++m) {
                 SB[m] = TR::cvt(Sacc[m]);
                 SBn[m] = TR::cvt(-Sacc[m]);
             }
-            f32x4 y = widen_bf16(TR::ldcol(Vs, L::V, 16 * j, 16 * w, g, c16));
+            f32x4 y = widen_bf16(vf);
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NMT; ++m) {
-                y = TR::mma16(y, ldrow(Ks, L::K, 16 * j + c16, 16 * m, g), SBn[m]);
-                o = TR::mma16(o, ldrow(Qs, L::K, 16 * j + c16, 16 * m, g), SB[m]);
+                y = TR::mma16(y, kl[m], SBn[m]);
+                o = TR::mma16(o, ql[m], SB[m]);
             }
             const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
-            const F zb = TR::cvt(TR::mma16(z0, TR::ldcol(TsT, L::T, 16 * j, 16 * j, g, c16), TR::cvt(y)));
-            o = TR::mma16(o, ldrow(Ps, L::T, 16 * j + c16, 16 * j, g), zb);
+            const F zb = TR::cvt(TR::mma16(z0, tf, TR::cvt(y)));
+            o = TR::mma16(o, pf, zb);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 16 * j + 4 * g + i;
-                if (tok < nval) og[((int64_t)r * kChunk + tok) * sv + 16 * w + c16] = TR::fromf(o[i]);
-            }
+            for (int i = 0; i < 4; ++i) Os[(16 * j + 4 * g + i) * LO + 16 * w + c16] = TR::fromf(o[i]);
 #pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                Sacc[m] *= *reinterpret_cast<const f32x4 *>(E16 + j * DK + 16 * m + 4 * g);
-                Sacc[m] = TR::mma16(Sacc[m], TR::ldcol(Kf, L::K, 16 * j, 16 * m, g, c16), zb);
-            }
+            for (int m = 0; m < NMT; ++m) Sacc[m] = TR::mma16(Sacc[m] * ef[m], kf[m], zb);
         }
+    }
+    if (NC > 0) {
+        __syncthreads();
+        flush_o(NC - 1);
     }
     if (a.S_final) {
 #pragma unroll
