@@ -958,7 +958,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     E *Ss = reinterpret_cast<E *>(smem + LY::oS), *Rs = reinterpret_cast<E *>(smem + LY::oR);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    const int u = blockIdx.x / a.n_tiles, tau = blockIdx.x - u * a.n_tiles;
+    int u, tau;
+    map_block(blockIdx.x, a.B * a.H, a.n_tiles, u, tau); // the tiles of a unit share an XCD
     const int b = u / a.H, h = u - b * a.H, row0 = 64 * tau;
     const int64_t tok0 = (int64_t)b * a.T, sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
     const int units = a.B * a.H;
@@ -1345,7 +1346,8 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     const int ntile = DV / 64;
-    const int u = blockIdx.x / ntile, tau = blockIdx.x - u * ntile;
+    int u, tau;
+    map_block(blockIdx.x, a.B * a.H, ntile, u, tau); // the tiles of a unit share an XCD
     const int b = u / a.H, h = u - b * a.H, row0 = 64 * tau;
     const int64_t tok0 = (int64_t)b * a.T, sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
     const int NC = (a.T + kChunk - 1) / kChunk;
