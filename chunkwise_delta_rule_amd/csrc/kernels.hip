@@ -997,19 +997,26 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         Ps[i] = TR::fromf(0.f);
     }
 
-    for (int r = a.NC - 1; r >= 0; --r) {
-        const int nval = min(kChunk, a.T - r * kChunk);
-        sg.load(r);
-        typename TR::V dov[2];
+    // HBM loads of chunk c (K, Q, V, beta, dO and the state entering it) into
+    // registers; issued one chunk ahead so their latency hides under the
+    // previous chunk's products.
+    typename TR::V dov[2];
+    auto load_chunk = [&](int c) {
+        const int n = min(kChunk, a.T - c * kChunk);
+        sg.load(c);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
-            dov[p] = *reinterpret_cast<const typename TR::V *>(dOg + ((int64_t)r * kChunk + min(row, nval - 1)) * sv +
+            dov[p] = *reinterpret_cast<const typename TR::V *>(dOg + ((int64_t)c * kChunk + min(row, n - 1)) * sv +
                                                                8 * cv);
         }
-        const float *Sr = a.S_chunks + (((int64_t)u * a.NC + r) * DV + row0 + 16 * w + c16) * DK + 4 * g;
+        const float *Sr = a.S_chunks + (((int64_t)u * a.NC + c) * DV + row0 + 16 * w + c16) * DK + 4 * g;
 #pragma unroll
         for (int m = 0; m < NMT; ++m) Sacc[m] = *reinterpret_cast<const f32x4 *>(Sr + 16 * m);
+    };
+    if (a.NC > 0) load_chunk(a.NC - 1);
+    for (int r = a.NC - 1; r >= 0; --r) {
+        const int nval = min(kChunk, a.T - r * kChunk);
         __syncthreads(); // the previous chunk's reads of the staging buffers are done
         sg.store_kqb(Ks, Qs, Bs, nullptr);
         sg.store_v(Vs);
@@ -1018,22 +1025,19 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
             const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
             *reinterpret_cast<typename TR::V *>(Ds + row * L::V + 8 * cv) = row < nval ? dov[p] : typename TR::V{};
         }
-#pragma unroll
-        for (int m = 0; m < NMT; ++m) {
-            stf(Ss + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(Sacc[m]));
-            stf(Rs + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(dSacc[m])); // dS after the chunk
-        }
-        __syncthreads();
-        bwd_solve<DK, true, false>(Ks, Qs, Bs, As, Ps, TsT, NsT, w, lane, g, c16);
-
         // This wave's 16 value rows (column c16 of the accumulators).
         F SBn[NMT], dSB[NMT], YB[4], dZB[4], dYBn[4];
         f32x4 acc[4];
 #pragma unroll
         for (int m = 0; m < NMT; ++m) {
+            stf(Ss + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(Sacc[m]));
+            stf(Rs + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(dSacc[m])); // dS after the chunk
             SBn[m] = TR::cvt(-Sacc[m]);
             dSB[m] = TR::cvt(dSacc[m]);
         }
+        __syncthreads();
+        if (r > 0) load_chunk(r - 1);
+        bwd_solve<DK, true, false>(Ks, Qs, Bs, As, Ps, TsT, NsT, w, lane, g, c16);
         // Y = V - K S^T
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -1095,7 +1099,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
             }
         __syncthreads(); // Y, Z, dZ, dY tiles complete
 
-        // Sums over this tile's 64 value rows, token rows 16w .. 16w + 15 per wave.
+        // Sums over this tile's 64 value rows, token rows 16w .. 16w + 15 per wave,
+        // stored in accumulator order: one 16-byte piece per (wave, column
+        // block, lane), so every store (and the finishing kernel's load) of a
+        // wave moves 1 KB of contiguous memory.
         float *pb = a.part + (((int64_t)tau * units + u) * a.NC + r) * bwd_part_floats(DK);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
@@ -1105,11 +1112,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
                 dp = TR::mma16(dp, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), ldrow(Zs, LT, 16 * s2 + c16, 16 * kv, g));
                 dt = TR::mma16(dt, ldrow(dZs, LT, 16 * w + c16, 16 * kv, g), ldrow(Ys, LT, 16 * s2 + c16, 16 * kv, g));
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pb[(16 * w + 4 * g + i) * 64 + 16 * s2 + c16] = dp[i];
-                pb[4096 + (16 * w + 4 * g + i) * 64 + 16 * s2 + c16] = dt[i];
-            }
+            *reinterpret_cast<f32x4 *>(pb + ((w * 4 + s2) * 64 + lane) * 4) = dp;
+            *reinterpret_cast<f32x4 *>(pb + 4096 + ((w * 4 + s2) * 64 + lane) * 4) = dt;
         }
 #pragma unroll
         for (int m = 0; m < NMT; ++m) {
@@ -1120,11 +1124,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
                 dk1 = TR::mma16(dk1, ldrow(Zs, LT, 16 * w + c16, 16 * kv, g), TR::ldcol(Rs, L::K, 16 * kv, 16 * m, g, c16));
                 dk2 = TR::mma16(dk2, ldrow(dYs, LT, 16 * w + c16, 16 * kv, g), TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16));
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pb[8192 + (16 * w + 4 * g + i) * DK + 16 * m + c16] = dq[i];
-                pb[8192 + 64 * DK + (16 * w + 4 * g + i) * DK + 16 * m + c16] = dk1[i] - dk2[i];
-            }
+            *reinterpret_cast<f32x4 *>(pb + 8192 + ((w * NMT + m) * 64 + lane) * 4) = dq;
+            *reinterpret_cast<f32x4 *>(pb + 8192 + 64 * DK + ((w * NMT + m) * 64 + lane) * 4) = dk1 - dk2;
         }
     }
     if (a.dS0) {
@@ -1185,40 +1186,50 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     sg.rg = 0.f;
     sg.nval = 0;
     sg.load(r);
+    // Partial sums over the value tiles (the chain kernel's accumulator
+    // order): dP, dT (lower-inclusive, to LDS) and dQ, dK (this wave's token
+    // rows, in registers). Every load is issued before the first use.
+    constexpr int NT = DV / 64;
+    const size_t PB = bwd_part_floats(DK);
+    const float *pbt[NT];
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) pbt[tau] = a.part + (((int64_t)tau * units + u) * a.NC + r) * PB;
+    auto ld4 = [&](int tau, int off) { return *reinterpret_cast<const f32x4 *>(pbt[tau] + off + lane * 4); };
+    f32x4 pp[4], tt[4], dQa[NMT], dKa[NMT];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+        pp[s2] = ld4(0, (w * 4 + s2) * 256);
+        tt[s2] = ld4(0, 4096 + (w * 4 + s2) * 256);
+    }
+#pragma unroll
+    for (int m = 0; m < NMT; ++m) {
+        dQa[m] = ld4(0, 8192 + (w * NMT + m) * 256);
+        dKa[m] = ld4(0, 8192 + 64 * DK + (w * NMT + m) * 256);
+    }
+#pragma unroll
+    for (int tau = 1; tau < NT; ++tau) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            pp[s2] += ld4(tau, (w * 4 + s2) * 256);
+            tt[s2] += ld4(tau, 4096 + (w * 4 + s2) * 256);
+        }
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) {
+            dQa[m] += ld4(tau, 8192 + (w * NMT + m) * 256);
+            dKa[m] += ld4(tau, 8192 + 64 * DK + (w * NMT + m) * 256);
+        }
+    }
     for (int i = tid; i < kChunk * LT; i += kThreads) TsT[i] = TR::fromf(0.f);
     sg.store_kqb(Ks, Qs, Bs, nullptr);
     if (w == 0) Bt[lane] = lane < nval ? TR::tof(sg.rbeta) : 0.f;
-
-    // Partial sums over the value tiles: dP, dT (lower-inclusive, to LDS) and
-    // dQ, dK (this wave's token rows, in registers).
-    const size_t PB = bwd_part_floats(DK);
-    for (int idx = tid; idx < 64 * 64; idx += kThreads) {
-        const int row = idx >> 6, col = idx & 63;
-        float p = 0.f, t = 0.f;
-        for (int tau = 0; tau < a.n_tiles; ++tau) {
-            const float *pb = a.part + (((int64_t)tau * units + u) * a.NC + r) * PB;
-            p += pb[idx];
-            t += pb[4096 + idx];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * s2 + c16;
+            dPs[row * LT + col] = TR::fromf(col <= row ? pp[s2][i] : 0.f);
+            dTs[row * LT + col] = TR::fromf(col <= row ? tt[s2][i] : 0.f);
         }
-        dPs[row * LT + col] = TR::fromf(col <= row ? p : 0.f);
-        dTs[row * LT + col] = TR::fromf(col <= row ? t : 0.f);
-    }
-    f32x4 dQa[NMT], dKa[NMT];
-#pragma unroll
-    for (int m = 0; m < NMT; ++m) {
-        dQa[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dKa[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int tau = 0; tau < a.n_tiles; ++tau) {
-        const float *pb = a.part + (((int64_t)tau * units + u) * a.NC + r) * PB + 8192;
-#pragma unroll
-        for (int m = 0; m < NMT; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dQa[m][i] += pb[(16 * w + 4 * g + i) * DK + 16 * m + c16];
-                dKa[m][i] += pb[64 * DK + (16 * w + 4 * g + i) * DK + 16 * m + c16];
-            }
-    }
     __syncthreads();
     // As = diag(beta) L (Gram phase), then N^T into TsT (solve with beta = 1)
     bwd_solve<DK, false, true>(Ks, Qs, Bs, As, nullptr, TsT, NsT, w, lane, g, c16);
