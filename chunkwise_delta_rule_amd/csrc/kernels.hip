@@ -62,6 +62,8 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -81,13 +83,15 @@ template <> struct Tr<__bf16> {
         const bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
+    // Two packed conversions (round to nearest even). Written per pair and
+    // reassembled through 32-bit words: element-wise conversion that feeds a
+    // matrix-core operand is otherwise emitted as four single conversions
+    // plus two permutes.
     __device__ static inline F cvt(f32x4 x) {
-        F r;
-        r[0] = (__bf16)x[0];
-        r[1] = (__bf16)x[1];
-        r[2] = (__bf16)x[2];
-        r[3] = (__bf16)x[3];
-        return r;
+        const bf16x2 lo = __builtin_convertvector(__builtin_shufflevector(x, x, 0, 1), bf16x2);
+        const bf16x2 hi = __builtin_convertvector(__builtin_shufflevector(x, x, 2, 3), bf16x2);
+        const u32x2 u = {__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+        return __builtin_bit_cast(F, u);
     }
     __device__ static inline float tof(__bf16 x) { return (float)x; }
     __device__ static inline __bf16 fromf(float x) { return (__bf16)x; }
@@ -1439,7 +1443,6 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
         // operands. Thread (channel pair, sub-chunk j) reads its 16 tokens'
         // decays, keys and queries at once, then walks them.
         {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             typedef float f32x2 __attribute__((ext_vector_type(2)));
             constexpr int NP = DK / 2; // channel pairs
             for (int item = tid; item < 4 * NP; item += kThreads) {
@@ -1459,21 +1462,21 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
                     acc += gl[l] * 1.44269504088896340736f;
                     gam[l] = acc;
                 }
+                const f32x2 e16 = {__builtin_amdgcn_exp2f(acc[0]), __builtin_amdgcn_exp2f(acc[1])};
 #pragma unroll
                 for (int l = 0; l < 16; ++l) {
                     const int row = 16 * j + l;
                     const f32x2 kv = {(float)kl[l][0], (float)kl[l][1]}, qv = {(float)ql[l][0], (float)ql[l][1]};
                     const f32x2 el = {__builtin_amdgcn_exp2f(gam[l][0]), __builtin_amdgcn_exp2f(gam[l][1])};
                     const f32x2 er = {__builtin_amdgcn_exp2f(-gam[l][0]), __builtin_amdgcn_exp2f(-gam[l][1])};
-                    const f32x2 ef = {__builtin_amdgcn_exp2f(acc[0] - gam[l][0]), __builtin_amdgcn_exp2f(acc[1] - gam[l][1])};
+                    const f32x2 ef = e16 * er; // exp(gamma_16 - gamma), <= 1
                     const f32x2 a1 = kv * el, a2 = qv * el, a3 = kv * er, a4 = kv * ef;
                     *reinterpret_cast<bf16x2 *>(Ks + row * L::K + d) = bf16x2{(__bf16)a1[0], (__bf16)a1[1]};
                     *reinterpret_cast<bf16x2 *>(Qs + row * L::K + d) = bf16x2{(__bf16)a2[0], (__bf16)a2[1]};
                     *reinterpret_cast<bf16x2 *>(Kr + row * L::K + d) = bf16x2{(__bf16)a3[0], (__bf16)a3[1]};
                     *reinterpret_cast<bf16x2 *>(Kf + row * L::K + d) = bf16x2{(__bf16)a4[0], (__bf16)a4[1]};
                 }
-                *reinterpret_cast<f32x2 *>(E16 + j * DK + d) =
-                    f32x2{__builtin_amdgcn_exp2f(acc[0]), __builtin_amdgcn_exp2f(acc[1])};
+                *reinterpret_cast<f32x2 *>(E16 + j * DK + d) = e16;
             }
         }
         __syncthreads();
