@@ -1318,7 +1318,9 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
 // them. The kernel therefore runs that algorithm on sub-chunks of 16 tokens
 // (the page's exactness holds for every chunk size): with gamma the
 // per-channel prefix sums of ln a inside a sub-chunk,
-//   Kl = K * exp(gamma),  Ql = Q * exp(gamma)          (<-K, <-Q; factors <= 1)
+//   Kl = K * exp(gamma),  Ql = Q * exp(gamma)          (-Kl <-K, Ql <-Q; factors <= 1;
+//                                                        Kl is kept negated so that Y
+//                                                        needs no negated copy of S)
 //   Kr = K * exp(-gamma)                               (factors >= 1, bounded
 //                                                        by 16 tokens of decay)
 //   Kf = K * exp(gamma_16 - gamma)                     (->K; factors <= 1)
@@ -1334,8 +1336,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
 template <int DK> struct KdaLds {
     using L = Ld<__bf16, DK>;
     static constexpr size_t oK = 0, oQ = oK + L::szK, oKr = oQ + L::szK, oKf = oKr + L::szK;
-    static constexpr size_t oG = oKf + L::szK;                       // g tile, fp32 [64][DK]
-    static constexpr size_t oE = oG + sizeof(float) * 64 * DK;       // exp(gamma_16), fp32 [4][DK]
+    static constexpr size_t oE = oKf + L::szK;                       // exp(gamma_16), fp32 [4][DK]
     static constexpr size_t oV = oE + sizeof(float) * 4 * DK, oB = oV + L::szV, oA = oB + 256;
     static constexpr size_t oT = oA + L::szA, oN = oT + L::szT, oP = oN + L::szN, total = oP + L::szT;
 };
@@ -1353,7 +1354,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
     E *Ks = reinterpret_cast<E *>(smem + LY::oK), *Qs = reinterpret_cast<E *>(smem + LY::oQ);
     E *Kr = reinterpret_cast<E *>(smem + LY::oKr), *Kf = reinterpret_cast<E *>(smem + LY::oKf);
-    float *Gt = reinterpret_cast<float *>(smem + LY::oG), *E16 = reinterpret_cast<float *>(smem + LY::oE);
+    float *E16 = reinterpret_cast<float *>(smem + LY::oE);
     E *Vs = reinterpret_cast<E *>(smem + LY::oV);
     float *Bs = reinterpret_cast<float *>(smem + LY::oB), *As = reinterpret_cast<float *>(smem + LY::oA);
     E *TsT = reinterpret_cast<E *>(smem + LY::oT), *NsT = reinterpret_cast<E *>(smem + LY::oN);
@@ -1395,18 +1396,23 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
         Sacc[m] = a.S0 ? *reinterpret_cast<const f32x4 *>(a.S0 + ((int64_t)u * DV + row0 + 16 * w + c16) * DK +
                                                            16 * m + 4 * g)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int NG = 64 * DK / 4 / kThreads; // f32x4 pieces of the g tile per thread
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    constexpr int NP = DK / 2; // channel pairs; the scaling pass has one thread per (pair, sub-chunk)
+    static_assert(4 * NP <= kThreads, "one scaling item per thread");
+    const int sj = tid / NP, sd = 2 * (tid % NP); // this thread's sub-chunk and channel pair
+    const bool scaler = tid < 4 * NP;
 
     // Loads of chunk c into registers; issued one chunk ahead so that they
-    // overlap the previous chunk's products.
-    f32x4 gv[NG];
+    // overlap the previous chunk's products. The log decays go straight into
+    // the layout of the scaling pass: 16 tokens of one channel pair.
+    f32x2 gq[16];
     auto load_chunk = [&](int c) {
         sg.load(c);
         const int n = min(kChunk, a.T - c * kChunk);
+        if (scaler) {
 #pragma unroll
-        for (int p = 0; p < NG; ++p) {
-            const int vi = p * kThreads + tid, row = vi / (DK / 4), c4 = vi % (DK / 4);
-            gv[p] = *reinterpret_cast<const f32x4 *>(gg + ((int64_t)c * kChunk + min(row, n - 1)) * sqk + 4 * c4);
+            for (int l = 0; l < 16; ++l)
+                gq[l] = *reinterpret_cast<const f32x2 *>(gg + ((int64_t)c * kChunk + min(16 * sj + l, n - 1)) * sqk + sd);
         }
     };
     // The output tile of a chunk ([64 tokens][64 values], bf16) is assembled in
@@ -1432,34 +1438,25 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
         if (r > 0) flush_o(r - 1);
         sg.store_kqb(Ks, Qs, Bs, nullptr);
         sg.store_v(Vs);
-#pragma unroll
-        for (int p = 0; p < NG; ++p) {
-            const int vi = p * kThreads + tid, row = vi / (DK / 4), c4 = vi % (DK / 4);
-            *reinterpret_cast<f32x4 *>(Gt + row * DK + 4 * c4) = row < nval ? gv[p] : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
         __syncthreads();
-        if (r + 1 < NC) load_chunk(r + 1);
         // Per-channel prefix sums inside each sub-chunk (base 2) and the scaled
-        // operands. Thread (channel pair, sub-chunk j) reads its 16 tokens'
-        // decays, keys and queries at once, then walks them.
-        {
-            typedef float f32x2 __attribute__((ext_vector_type(2)));
-            constexpr int NP = DK / 2; // channel pairs
-            for (int item = tid; item < 4 * NP; item += kThreads) {
-                const int j = item / NP, d = 2 * (item % NP);
-                f32x2 gl[16];
+        // operands. Thread (channel pair, sub-chunk j) holds its 16 tokens'
+        // decays, reads their keys and queries at once, then walks them.
+        // Tokens past the end of the sequence have zero log decay.
+        if (scaler) {
+            const int j = sj, d = sd;
+            {
                 bf16x2 kl[16], ql[16];
 #pragma unroll
                 for (int l = 0; l < 16; ++l) {
                     const int row = 16 * j + l;
-                    gl[l] = *reinterpret_cast<const f32x2 *>(Gt + row * DK + d);
                     kl[l] = *reinterpret_cast<const bf16x2 *>(Ks + row * L::K + d);
                     ql[l] = *reinterpret_cast<const bf16x2 *>(Qs + row * L::K + d);
                 }
                 f32x2 gam[16], acc = {0.f, 0.f};
 #pragma unroll
                 for (int l = 0; l < 16; ++l) {
-                    acc += gl[l] * 1.44269504088896340736f;
+                    if (16 * j + l < nval) acc += gq[l] * 1.44269504088896340736f;
                     gam[l] = acc;
                 }
                 const f32x2 e16 = {__builtin_amdgcn_exp2f(acc[0]), __builtin_amdgcn_exp2f(acc[1])};
@@ -1470,7 +1467,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
                     const f32x2 el = {__builtin_amdgcn_exp2f(gam[l][0]), __builtin_amdgcn_exp2f(gam[l][1])};
                     const f32x2 er = {__builtin_amdgcn_exp2f(-gam[l][0]), __builtin_amdgcn_exp2f(-gam[l][1])};
                     const f32x2 ef = e16 * er; // exp(gamma_16 - gamma), <= 1
-                    const f32x2 a1 = kv * el, a2 = qv * el, a3 = kv * er, a4 = kv * ef;
+                    const f32x2 a1 = -(kv * el), a2 = qv * el, a3 = kv * er, a4 = kv * ef;
                     *reinterpret_cast<bf16x2 *>(Ks + row * L::K + d) = bf16x2{(__bf16)a1[0], (__bf16)a1[1]};
                     *reinterpret_cast<bf16x2 *>(Qs + row * L::K + d) = bf16x2{(__bf16)a2[0], (__bf16)a2[1]};
                     *reinterpret_cast<bf16x2 *>(Kr + row * L::K + d) = bf16x2{(__bf16)a3[0], (__bf16)a3[1]};
@@ -1479,8 +1476,10 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
                 *reinterpret_cast<f32x2 *>(E16 + j * DK + d) = e16;
             }
         }
+        if (r + 1 < NC) load_chunk(r + 1);
         __syncthreads();
-        // Sub-chunk w: L = Kl Kr^T (strictly lower, times beta of the row) and A = Ql Kr^T.
+        // Sub-chunk w: L = Kl Kr^T (strictly lower, times beta of the row) and
+        // A = Ql Kr^T. Ks holds -Kl, so the products give -L.
         {
             f32x4 lt = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1492,7 +1491,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * w + 4 * g + i;
-                As[row * L::A + 16 * w + c16] = c16 < 4 * g + i ? Bs[row] * lt[i] : 0.f;
+                As[row * L::A + 16 * w + c16] = c16 < 4 * g + i ? -Bs[row] * lt[i] : 0.f;
                 Ps[row * L::T + 16 * w + c16] = TR::fromf(c16 <= 4 * g + i ? at[i] : 0.f);
             }
         }
@@ -1521,17 +1520,14 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
             const F tf = TR::ldcol(TsT, L::T, 16 * j, 16 * j, g, c16);
             const F pf = ldrow(Ps, L::T, 16 * j + c16, 16 * j, g);
             sched_fence();
-            F SB[NMT], SBn[NMT];
+            F SB[NMT];
 #pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                SB[m] = TR::cvt(Sacc[m]);
-                SBn[m] = TR::cvt(-Sacc[m]);
-            }
+            for (int m = 0; m < NMT; ++m) SB[m] = TR::cvt(Sacc[m]);
             f32x4 y = widen_bf16(vf);
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NMT; ++m) {
-                y = TR::mma16(y, kl[m], SBn[m]);
+                y = TR::mma16(y, kl[m], SB[m]); // Ks holds -Kl
                 o = TR::mma16(o, ql[m], SB[m]);
             }
             const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
