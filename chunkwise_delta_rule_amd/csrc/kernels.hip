@@ -1064,15 +1064,21 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) Zs[(16 * t + 4 * g + i) * LT + 16 * w + c16] = zb[i];
         }
-        // dZ = P^T dO + K dS'^T
+        // dZ = P^T dO + K dS'^T. The two parts use different product shapes and
+        // so accumulate separately: a chain that feeds one shape's result to
+        // the other as accumulator is not kept apart by the compiler's wait
+        // states and gives wrong sums.
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 zp = {0.f, 0.f, 0.f, 0.f}, zk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s2 = t; s2 < 4; ++s2)
-                z = TR::mma16(z, TR::ldcol(Ps, L::T, 16 * s2, 16 * t, g, c16), TR::ldcol(Ds, L::V, 16 * s2, 16 * w, g, c16));
+                zp = TR::mma16(zp, TR::ldcol(Ps, L::T, 16 * s2, 16 * t, g, c16), TR::ldcol(Ds, L::V, 16 * s2, 16 * w, g, c16));
 #pragma unroll
-            for (int m = 0; m < NMT; ++m) z = TR::mma16(z, ldrow(Ks, L::K, 16 * t + c16, 16 * m, g), dSB[m]);
+            for (int m = 0; m < NMT; m += 2)
+                zk = TR::mma32(zk, ldrow(Ks, L::K, 16 * t + c16, 16 * m, g), ldrow(Ks, L::K, 16 * t + c16, 16 * m + 16, g),
+                               dSB[m], dSB[m + 1]);
+            const f32x4 z = zp + zk;
             dZB[t] = TR::cvt(z);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dZs[(16 * t + 4 * g + i) * LT + 16 * w + c16] = dZB[t][i];
@@ -1096,10 +1102,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < NMT; ++m)
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                dSacc[m] = TR::mma16(dSacc[m], TR::ldcol(Qs, L::K, 16 * s2, 16 * m, g, c16),
-                                     TR::ldcol(Ds, L::V, 16 * s2, 16 * w, g, c16));
-                dSacc[m] = TR::mma16(dSacc[m], TR::ldcol(Ks, L::K, 16 * s2, 16 * m, g, c16), dYBn[s2]);
+            for (int s2 = 0; s2 < 4; s2 += 2) { // 16x16x32 products over token blocks s2, s2 + 1
+                dSacc[m] = TR::mma32(dSacc[m], TR::ldcol(Qs, L::K, 16 * s2, 16 * m, g, c16),
+                                     TR::ldcol(Qs, L::K, 16 * s2 + 16, 16 * m, g, c16),
+                                     TR::ldcol(Ds, L::V, 16 * s2, 16 * w, g, c16),
+                                     TR::ldcol(Ds, L::V, 16 * s2 + 16, 16 * w, g, c16));
+                dSacc[m] = TR::mma32(dSacc[m], TR::ldcol(Ks, L::K, 16 * s2, 16 * m, g, c16),
+                                     TR::ldcol(Ks, L::K, 16 * s2 + 16, 16 * m, g, c16), dYBn[s2], dYBn[s2 + 1]);
             }
         __syncthreads(); // Y, Z, dZ, dY tiles complete
 
@@ -1112,9 +1121,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         for (int s2 = 0; s2 < 4; ++s2) {
             f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kv = 0; kv < 4; ++kv) {
-                dp = TR::mma16(dp, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), ldrow(Zs, LT, 16 * s2 + c16, 16 * kv, g));
-                dt = TR::mma16(dt, ldrow(dZs, LT, 16 * w + c16, 16 * kv, g), ldrow(Ys, LT, 16 * s2 + c16, 16 * kv, g));
+            for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
+                dp = TR::mma32(dp, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), ldrow(Ds, L::V, 16 * w + c16, 16 * kv + 16, g),
+                               ldrow(Zs, LT, 16 * s2 + c16, 16 * kv, g), ldrow(Zs, LT, 16 * s2 + c16, 16 * kv + 16, g));
+                dt = TR::mma32(dt, ldrow(dZs, LT, 16 * w + c16, 16 * kv, g), ldrow(dZs, LT, 16 * w + c16, 16 * kv + 16, g),
+                               ldrow(Ys, LT, 16 * s2 + c16, 16 * kv, g), ldrow(Ys, LT, 16 * s2 + c16, 16 * kv + 16, g));
             }
             *reinterpret_cast<f32x4 *>(pb + ((w * 4 + s2) * 64 + lane) * 4) = dp;
             *reinterpret_cast<f32x4 *>(pb + 4096 + ((w * 4 + s2) * 64 + lane) * 4) = dt;
@@ -1123,10 +1134,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         for (int m = 0; m < NMT; ++m) {
             f32x4 dq = {0.f, 0.f, 0.f, 0.f}, dk1 = {0.f, 0.f, 0.f, 0.f}, dk2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kv = 0; kv < 4; ++kv) {
-                dq = TR::mma16(dq, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16));
-                dk1 = TR::mma16(dk1, ldrow(Zs, LT, 16 * w + c16, 16 * kv, g), TR::ldcol(Rs, L::K, 16 * kv, 16 * m, g, c16));
-                dk2 = TR::mma16(dk2, ldrow(dYs, LT, 16 * w + c16, 16 * kv, g), TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16));
+            for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
+                const F s0 = TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16), s1 = TR::ldcol(Ss, L::K, 16 * kv + 16, 16 * m, g, c16);
+                dq = TR::mma32(dq, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), ldrow(Ds, L::V, 16 * w + c16, 16 * kv + 16, g),
+                               s0, s1);
+                dk1 = TR::mma32(dk1, ldrow(Zs, LT, 16 * w + c16, 16 * kv, g), ldrow(Zs, LT, 16 * w + c16, 16 * kv + 16, g),
+                                TR::ldcol(Rs, L::K, 16 * kv, 16 * m, g, c16), TR::ldcol(Rs, L::K, 16 * kv + 16, 16 * m, g, c16));
+                dk2 = TR::mma32(dk2, ldrow(dYs, LT, 16 * w + c16, 16 * kv, g), ldrow(dYs, LT, 16 * w + c16, 16 * kv + 16, g),
+                                s0, s1);
             }
             *reinterpret_cast<f32x4 *>(pb + 8192 + ((w * NMT + m) * 64 + lane) * 4) = dq;
             *reinterpret_cast<f32x4 *>(pb + 8192 + 64 * DK + ((w * NMT + m) * 64 + lane) * 4) = dk1 - dk2;
@@ -1245,8 +1260,9 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     for (int j = 0; j < 4; ++j) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            x = TR::mma16(x, ldrow(TsT, L::T, 16 * w + c16, 16 * rb, g), TR::ldcol(dTs, LT, 16 * rb, 16 * j, g, c16));
+        for (int rb = 0; rb < 4; rb += 2)
+            x = TR::mma32(x, ldrow(TsT, L::T, 16 * w + c16, 16 * rb, g), ldrow(TsT, L::T, 16 * w + c16, 16 * rb + 16, g),
+                          TR::ldcol(dTs, LT, 16 * rb, 16 * j, g, c16), TR::ldcol(dTs, LT, 16 * rb + 16, 16 * j, g, c16));
         const float bc = Bt[16 * j + c16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1261,11 +1277,13 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     for (int j = 0; j < 4; ++j) {
         f32x4 da = {0.f, 0.f, 0.f, 0.f}, gm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            da = TR::mma16(da, ldrow(Xs, LT, 16 * w + c16, 16 * rb, g), TR::ldcol(TsT, L::T, 16 * rb, 16 * j, g, c16));
+        for (int rb = 0; rb < 4; rb += 2)
+            da = TR::mma32(da, ldrow(Xs, LT, 16 * w + c16, 16 * rb, g), ldrow(Xs, LT, 16 * w + c16, 16 * rb + 16, g),
+                           TR::ldcol(TsT, L::T, 16 * rb, 16 * j, g, c16), TR::ldcol(TsT, L::T, 16 * rb + 16, 16 * j, g, c16));
 #pragma unroll
-        for (int kd = 0; kd < NMT; ++kd)
-            gm = TR::mma16(gm, ldrow(Ks, L::K, 16 * w + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g));
+        for (int kd = 0; kd < NMT; kd += 2)
+            gm = TR::mma32(gm, ldrow(Ks, L::K, 16 * w + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * w + c16, 16 * kd + 16, g),
+                           ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd + 16, g));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
@@ -1283,12 +1301,17 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
 #pragma unroll
     for (int m = 0; m < NMT; ++m)
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            const F kc = TR::ldcol(Ks, L::K, 16 * sb, 16 * m, g, c16);
-            dQa[m] = TR::mma16(dQa[m], ldrow(dPs, LT, 16 * w + c16, 16 * sb, g), kc);
-            dKa[m] = TR::mma16(dKa[m], TR::ldcol(dPs, LT, 16 * sb, 16 * w, g, c16), TR::ldcol(Qs, L::K, 16 * sb, 16 * m, g, c16));
-            dKa[m] = TR::mma16(dKa[m], ldrow(dLs, LT, 16 * w + c16, 16 * sb, g), kc);
-            dKa[m] = TR::mma16(dKa[m], TR::ldcol(dLs, LT, 16 * sb, 16 * w, g, c16), kc);
+        for (int sb = 0; sb < 4; sb += 2) { // 16x16x32 products over token blocks sb, sb + 1
+            const F kc0 = TR::ldcol(Ks, L::K, 16 * sb, 16 * m, g, c16), kc1 = TR::ldcol(Ks, L::K, 16 * sb + 16, 16 * m, g, c16);
+            dQa[m] = TR::mma32(dQa[m], ldrow(dPs, LT, 16 * w + c16, 16 * sb, g), ldrow(dPs, LT, 16 * w + c16, 16 * sb + 16, g),
+                               kc0, kc1);
+            dKa[m] = TR::mma32(dKa[m], TR::ldcol(dPs, LT, 16 * sb, 16 * w, g, c16),
+                               TR::ldcol(dPs, LT, 16 * sb + 16, 16 * w, g, c16), TR::ldcol(Qs, L::K, 16 * sb, 16 * m, g, c16),
+                               TR::ldcol(Qs, L::K, 16 * sb + 16, 16 * m, g, c16));
+            dKa[m] = TR::mma32(dKa[m], ldrow(dLs, LT, 16 * w + c16, 16 * sb, g), ldrow(dLs, LT, 16 * w + c16, 16 * sb + 16, g),
+                               kc0, kc1);
+            dKa[m] = TR::mma32(dKa[m], TR::ldcol(dLs, LT, 16 * sb, 16 * w, g, c16),
+                               TR::ldcol(dLs, LT, 16 * sb + 16, 16 * w, g, c16), kc0, kc1);
         }
     E *dqg = reinterpret_cast<E *>(a.dq) + (tok0 + (int64_t)r * kChunk) * sqk + (int64_t)h * DK;
     E *dkg = reinterpret_cast<E *>(a.dk) + (tok0 + (int64_t)r * kChunk) * sqk + (int64_t)h * DK;
@@ -1483,10 +1506,12 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
         {
             f32x4 lt = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                const F kr = ldrow(Kr, L::K, 16 * w + c16, 16 * m, g);
-                lt = TR::mma16(lt, ldrow(Ks, L::K, 16 * w + c16, 16 * m, g), kr);
-                at = TR::mma16(at, ldrow(Qs, L::K, 16 * w + c16, 16 * m, g), kr);
+            for (int m = 0; m < NMT; m += 2) { // 16x16x32 products over dk blocks m, m + 1
+                const F kr0 = ldrow(Kr, L::K, 16 * w + c16, 16 * m, g), kr1 = ldrow(Kr, L::K, 16 * w + c16, 16 * m + 16, g);
+                lt = TR::mma32(lt, ldrow(Ks, L::K, 16 * w + c16, 16 * m, g), ldrow(Ks, L::K, 16 * w + c16, 16 * m + 16, g),
+                               kr0, kr1);
+                at = TR::mma32(at, ldrow(Qs, L::K, 16 * w + c16, 16 * m, g), ldrow(Qs, L::K, 16 * w + c16, 16 * m + 16, g),
+                               kr0, kr1);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1526,13 +1551,13 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
             f32x4 y = widen_bf16(vf);
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                y = TR::mma16(y, kl[m], SB[m]); // Ks holds -Kl
-                o = TR::mma16(o, ql[m], SB[m]);
+            for (int m = 0; m < NMT; m += 2) { // 16x16x32 products over dk blocks m, m + 1; Ks holds -Kl
+                y = TR::mma32(y, kl[m], kl[m + 1], SB[m], SB[m + 1]);
+                o = TR::mma32(o, ql[m], ql[m + 1], SB[m], SB[m + 1]);
             }
             const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
             const F zb = TR::cvt(TR::mma16(z0, tf, TR::cvt(y)));
-            o = TR::mma16(o, pf, zb);
+            o += TR::mma16(z0, pf, zb); // its own accumulator: o comes from 16x16x32 products
 #pragma unroll
             for (int i = 0; i < 4; ++i) Os[(16 * j + 4 * g + i) * LO + 16 * w + c16] = TR::fromf(o[i]);
 #pragma unroll

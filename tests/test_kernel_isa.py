@@ -13,6 +13,13 @@ instance of chain_kernel_ws must:
   a VGPR needs two wait states before a DPP instruction reads that VGPR as
   its (broadcast) first source. The DPP FMAs are inline assembly, so the
   compiler does not insert these wait states; the source guarantees them.
+
+Every kernel of the library (chain_bf16.hip and kernels.hip) must also keep
+matrix-core accumulation chains to one product shape: no 16x16x16 product
+may take the result of a 16x16x32 product (or the other way round) as its
+accumulator. The compiler emitted such a pair back to back without the wait
+states the hardware needs between the two shapes, and the sums came out
+wrong; the kernels therefore accumulate each shape separately and add.
 """
 
 import os
@@ -25,18 +32,28 @@ import pytest
 from chunkwise_delta_rule_amd import build
 
 SRC = os.path.join(build.PKG, "csrc", "chain_bf16.hip")
+SRC_OTHER = os.path.join(build.PKG, "csrc", "kernels.hip")
+
+
+def _compile(src):
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        cmd = [build.hipcc(), f"--offload-arch={build.ARCH}", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-I", os.path.join(build.ROOT, "include"), src, "-o", out]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-3000:]
+        return open(out).read()
 
 
 @pytest.fixture(scope="module")
 def asm():
-    with tempfile.TemporaryDirectory() as d:
-        out = os.path.join(d, "chain_bf16.s")
-        cmd = [build.hipcc(), f"--offload-arch={build.ARCH}", "-O3", "-std=c++17", "--cuda-device-only", "-S",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-               "-I", os.path.join(build.ROOT, "include"), SRC, "-o", out]
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        assert res.returncode == 0, res.stderr[-3000:]
-        return open(out).read()
+    return _compile(SRC)
+
+
+@pytest.fixture(scope="module")
+def asm_other():
+    return _compile(SRC_OTHER)
 
 
 def kernels(asm_text):
@@ -115,3 +132,60 @@ def test_dpp_check_catches_a_planted_hazard():
         test_dpp_broadcast_sources_have_two_wait_states(body)
     ok = body.replace("\tv_fmac", "\ts_nop 1\n\tv_fmac")
     test_dpp_broadcast_sources_have_two_wait_states(ok)
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def mixed_shape_chains(asm_text):
+    """(kernel, first opcode, second opcode, instructions between) for every
+    MFMA whose accumulator input is the result of an MFMA of another opcode,
+    with no other write of those registers in between."""
+    found = []
+    for m in re.finditer(r"^(_Z\S+):", asm_text, flags=re.M):
+        end = asm_text.index(".Lfunc_end", m.end())
+        insts = [l.strip() for l in asm_text[m.end():end].split("\n")]
+        insts = [l for l in insts if l and not l.startswith((";", ".")) and not l.endswith(":")]
+        parsed = []
+        for l in insts:
+            t = l.split(None, 1)
+            parsed.append((t[0], [x.strip() for x in t[1].split(",")] if len(t) > 1 else []))
+        for i, (op, ops) in enumerate(parsed):
+            if not op.startswith("v_mfma"):
+                continue
+            dst = _regs(ops[0])
+            for k in range(i + 1, min(i + 60, len(parsed))):
+                op2, ops2 = parsed[k]
+                if op2.startswith("v_mfma") and len(ops2) >= 4 and _regs(ops2[3]) & dst:
+                    if op2 != op:
+                        found.append((m.group(1), op, op2, k - i - 1))
+                    break
+                if ops2 and not op2.startswith(("s_", "ds_write", "global_store", "buffer_store")) and \
+                        _regs(ops2[0]) & dst:
+                    break
+    return found
+
+
+def test_no_mixed_shape_accumulation(asm, asm_other):
+    n_mfma = asm.count("v_mfma") + asm_other.count("v_mfma")
+    assert n_mfma > 1000
+    bad = mixed_shape_chains(asm) + mixed_shape_chains(asm_other)
+    assert not bad, "\n".join(f"{k}: {a} -> {b} ({gap} between)" for k, a, b, gap in bad[:10])
+
+
+def test_mixed_shape_check_catches_a_planted_chain():
+    body = ("_Zk:\n"
+            "\tv_mfma_f32_16x16x16_bf16 a[0:3], v[56:57], v[58:59], a[0:3]\n"
+            "\tds_read_b64 v[56:57], v241\n"
+            "\tv_mfma_f32_16x16x32_bf16 a[0:3], v[56:59], v[88:91], a[0:3]\n"
+            ".Lfunc_end0:\n")
+    assert len(mixed_shape_chains(body)) == 1
+    same = body.replace("16x16x32_bf16 a[0:3], v[56:59]", "16x16x16_bf16 a[0:3], v[56:57]")
+    assert mixed_shape_chains(same) == []
+    rewritten = body.replace("\tds_read_b64", "\tv_accvgpr_write_b32 a0, 0\n\tds_read_b64")
+    assert mixed_shape_chains(rewritten) == []
