@@ -296,7 +296,9 @@ int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *be
 size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     if (B <= 0 || H <= 0 || T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
     const size_t units = (size_t)B * H, nc = (size_t)(T + dn::kChunk - 1) / dn::kChunk;
-    return units * nc * ((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_floats(dk)) * sizeof(float);
+    // per (unit, chunk): the entering state and the partial sums (fp32), then T^T (bf16)
+    return units * nc * (((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_floats(dk)) * sizeof(float) +
+                         (size_t)dn::kChunk * dn::kChunk * sizeof(__bf16));
 }
 
 int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, const float *S0, const void *dO,
@@ -336,6 +338,9 @@ int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, 
     a.beta = beta;
     a.S0 = S0;
     a.S_chunks = Sck;
+    float *part = Sck + (size_t)B * H * NC * dv * dk;
+    __bf16 *Tck = reinterpret_cast<__bf16 *>(part + (size_t)B * H * NC * (dv / dn::kRows) * dn::bwd_part_floats(dk));
+    a.T_chunks = Tck;
     a.B = B;
     a.H = H;
     a.T = T;
@@ -353,7 +358,8 @@ int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, 
     b.dO = dO;
     b.dS_final = dS_final;
     b.S_chunks = Sck;
-    b.part = Sck + (size_t)B * H * NC * dv * dk;
+    b.T_chunks = Tck;
+    b.part = part;
     b.dS0 = dS0;
     b.dq = dq;
     b.dk = dk_;

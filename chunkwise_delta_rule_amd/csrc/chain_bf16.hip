@@ -909,7 +909,22 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
             if constexpr (GATED) vs.template write_gate<S>(bf.G(r + 3));
             if (has_v) vs.template load_v<S>(min(max(r + 3, 0), last));
             vs.template load_beta<S>(min(r + 5, last));
-            if (r + 1 >= 0 && r + 1 < NC) off_solve<DK>(bf, r + 1, lane, g, c16);
+            if (r + 1 >= 0 && r + 1 < NC) {
+                off_solve<DK>(bf, r + 1, lane, g, c16);
+                if constexpr (!WO && !GATED) {
+                    // for the backward pass: T^T of the chunk, row-major, from this
+                    // wave's own LDS writes (its blocks are complete here)
+                    if (wk.Tchunks) {
+                        const __bf16 *Tt = bf.Tt(r + 1);
+                        __bf16 *dst = wk.Tchunks + (int64_t)(r + 1) * kChunk * kChunk;
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) {
+                            const int piece = 64 * p + lane, row = piece >> 3, c8 = piece & 7;
+                            st8(dst + row * kChunk + 8 * c8, ld8(Tt + s64off(row, 8 * c8)));
+                        }
+                    }
+                }
+            }
         } else {
             ks.template write<S>(bf.K(r + 3));
             ks.template load<S>(min(r + 5, last));

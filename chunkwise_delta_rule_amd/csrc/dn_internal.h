@@ -28,6 +28,8 @@ struct ChainArgs {
     float *S_final;
     float *S_chunks; // dense kind only, or nullptr: the state entering every chunk,
                      // [B*H][chunks][dv][dk] fp32 (kept for the backward pass)
+    __bf16 *T_chunks; // with S_chunks (bf16 DeltaNet without output), or nullptr: T^T of
+                      // every chunk, [B*H][chunks][64][64] bf16 row-major (backward pass)
     const int32_t *cu_seqlens;
     const int32_t *seq_order;
     // Context-parallel workspace, per (b*H + h) and group g:
@@ -74,6 +76,7 @@ struct BwdArgs {
     const void *q, *k, *v, *beta, *dO;
     const float *dS_final; // [B*H][dv][dk] or nullptr (zero)
     const float *S_chunks; // [B*H][NC][dv][dk]: the state entering each chunk
+    const __bf16 *T_chunks; // [B*H][NC][64][64]: T^T of each chunk (the forward's), row-major
     float *part;           // [n_tiles][B*H][NC] blocks of per-tile partial sums
     float *dS0;            // [B*H][dv][dk] or nullptr
     void *dq, *dk, *dv, *dbeta;

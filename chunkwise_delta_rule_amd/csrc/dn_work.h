@@ -34,13 +34,14 @@ struct Work {
     const float *Sin; // initial rows, or nullptr (zero / identity)
     float *Sout;      // final rows, or nullptr
     bool identity, transposed_out, has_v;
+    __bf16 *Tchunks;  // T^T of chunk 0 of this unit (dense kind, first tile only), or nullptr
 };
 
 template <int DK, int DV> __device__ inline Work decode_work(const ChainArgs &a) {
     int u, tau;
     map_block(blockIdx.x, a.n_units, a.n_tiles, u, tau);
     const int H = a.H;
-    Work wk = {0, 0, 0, tau * kRows, u, nullptr, nullptr, nullptr, false, false, true};
+    Work wk = {0, 0, 0, tau * kRows, u, nullptr, nullptr, nullptr, false, false, true, nullptr};
     if (a.kind == kDense) {
         const int b = u / H;
         wk.h = u - b * H;
@@ -48,6 +49,8 @@ template <int DK, int DV> __device__ inline Work decode_work(const ChainArgs &a)
         wk.len = a.T;
         if (a.S_chunks)
             wk.Schunks = a.S_chunks + ((int64_t)u * ((a.T + kChunk - 1) / kChunk) * DV + wk.row0) * DK;
+        if (a.T_chunks && tau == 0)
+            wk.Tchunks = a.T_chunks + (int64_t)u * ((a.T + kChunk - 1) / kChunk) * kChunk * kChunk;
         if (a.S0) wk.Sin = a.S0 + ((int64_t)u * DV + wk.row0) * DK;
         if (a.S_final) wk.Sout = a.S_final + ((int64_t)u * DV + wk.row0) * DK;
     } else if (a.kind == kVarlen) {

@@ -877,69 +877,24 @@ template <bool WO> hipError_t launch_dims_f32(int dk, int dv, const ChainArgs &a
 //   X = N^T dT,  dbeta_i = X_ii + sum_j dA_ij L_ij,  dA = -(X diag(beta)) N^T
 //   (strictly lower),  dL = diag(beta) dA.
 // Pass 1 is the forward chain kernel without output, keeping the state that
-// enters every chunk. Pass 2 (bwd_chain_kernel) walks the chunks backwards
-// per (unit, 64 value rows), carrying dS in registers; it writes dV and,
-// per chunk, the sums over its 64 value rows of dP, dT, dO S and Z dS' - dY S.
-// Pass 3 (bwd_finish_kernel, one workgroup per chunk) adds those partial
-// sums over the value tiles and finishes dQ, dK and dbeta.
+// enters every chunk and the chunk's T^T (as the forward formed it). Pass 2
+// (bwd_chain_kernel) walks the chunks backwards per (unit, 64 value rows),
+// carrying dS in registers; it takes T^T from pass 1, forms P, and writes dV
+// and, per chunk, the sums over its 64 value rows of dP, dT, dO S and
+// Z dS' - dY S. Pass 3 (bwd_finish_kernel, one workgroup per chunk) adds those
+// partial sums over the value tiles, forms N^T = I - L^T T^T (from
+// N (I + diag(beta) L) = I, so no triangular solve) and finishes dQ, dK and
+// dbeta.
 // ---------------------------------------------------------------------------
 __device__ inline f32x4 widen_bf16(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
-
-// T^T (and, WITH_P, the masked scores P) of the staged chunk by the forward's
-// phases. ONES_AFTER_A: beta is replaced by ones after the Gram phase, so the
-// solve yields N^T instead of T^T.
-template <int DK, bool WITH_P, bool ONES_AFTER_A>
-__device__ __attribute__((always_inline)) inline void bwd_solve(const __bf16 *Ks, const __bf16 *Qs, float *Bs, float *As, __bf16 *Ps, __bf16 *TsT,
-                                 __bf16 *NsT, int w, int lane, int g, int c16) {
-    using PH = Phases<__bf16, DK>;
-    using F = typename Tr<__bf16>::F;
-    switch (w) {
-#define DN_BA(W)                                                                                               \
-    case W: {                                                                                                  \
-        typename PH::template GramFrags<W> f;                                                                  \
-        PH::template gram_fetch<W>(f, Ks, Qs, g, c16);                                                         \
-        sched_fence();                                                                                         \
-        if constexpr (WITH_P || !(W & 1)) PH::template gram_compute<W, false>(f, Bs, nullptr, As, Ps, g, c16); \
-    } break;
-        DN_BA(0) DN_BA(1) DN_BA(2) DN_BA(3)
-#undef DN_BA
-    }
-    __syncthreads();
-    if constexpr (ONES_AFTER_A) {
-        if (w == 0) Bs[lane] = 1.f;
-        __syncthreads();
-    }
-    F nfrag;
-    {
-        typename PH::DiagFrags df;
-        PH::diag_fetch(df, As, Bs, w, c16);
-        sched_fence();
-        nfrag = PH::diag_compute(df, NsT, TsT, w, g, c16);
-    }
-    __syncthreads();
-    switch (w) {
-#define DN_BC(B)                                                                                               \
-    case B: {                                                                                                  \
-        typename PH::template OffFrags<B> f;                                                                   \
-        PH::template off_fetch<B>(f, As, NsT, Bs, g, c16);                                                     \
-        sched_fence();                                                                                         \
-        PH::template off_compute<B>(f, nfrag, TsT, g, c16);                                                    \
-    } break;
-        DN_BC(0) DN_BC(1) DN_BC(2)
-#undef DN_BC
-    default: break;
-    }
-    __syncthreads();
-}
 
 template <int DK> struct BwdLds {
     using L = Ld<__bf16, DK>;
     static constexpr int LT = L::T; // stride of the 64-wide bf16 tiles
     static constexpr size_t oK = 0, oQ = oK + L::szK, oV = oQ + L::szK, oD = oV + L::szV, oB = oD + L::szV;
-    static constexpr size_t oT = oB + 256, oP = oT + L::szT, oN = oP + L::szT;
-    static constexpr size_t oX = oN + L::szN; // Y, Z, dZ, dY tiles; the Gram rows (fp32) alias them
+    static constexpr size_t oT = oB + 256, oP = oT + L::szT;
+    static constexpr size_t oX = oP + L::szT; // Y, Z, dZ, dY tiles
     static constexpr size_t oS = oX + 4 * L::szT, oR = oS + L::szK, total = oR + L::szK;
-    static_assert(L::szA <= 4 * L::szT, "Gram rows fit in the tile region");
 };
 
 template <int DK, int DV>
@@ -956,8 +911,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     E *Vs = reinterpret_cast<E *>(smem + LY::oV), *Ds = reinterpret_cast<E *>(smem + LY::oD);
     float *Bs = reinterpret_cast<float *>(smem + LY::oB);
     E *TsT = reinterpret_cast<E *>(smem + LY::oT), *Ps = reinterpret_cast<E *>(smem + LY::oP);
-    E *NsT = reinterpret_cast<E *>(smem + LY::oN);
-    float *As = reinterpret_cast<float *>(smem + LY::oX);
     E *Ys = reinterpret_cast<E *>(smem + LY::oX), *Zs = Ys + 64 * LT, *dZs = Zs + 64 * LT, *dYs = dZs + 64 * LT;
     E *Ss = reinterpret_cast<E *>(smem + LY::oS), *Rs = reinterpret_cast<E *>(smem + LY::oR);
 
@@ -996,18 +949,19 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         dSacc[m] = a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + ((int64_t)u * DV + row0 + 16 * w + c16) *
                                                                                   DK + 16 * m + 4 * g)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i = tid; i < kChunk * LT; i += kThreads) {
-        TsT[i] = TR::fromf(0.f);
-        Ps[i] = TR::fromf(0.f);
-    }
+    for (int i = tid; i < kChunk * LT; i += kThreads) Ps[i] = TR::fromf(0.f); // only P's lower blocks are written
 
     // HBM loads of chunk c (K, Q, V, beta, dO and the state entering it) into
     // registers; issued one chunk ahead so their latency hides under the
     // previous chunk's products.
-    typename TR::V dov[2];
+    typename TR::V dov[2], tv[2];
+    const E *Tg = a.T_chunks + (int64_t)u * a.NC * kChunk * kChunk;
     auto load_chunk = [&](int c) {
         const int n = min(kChunk, a.T - c * kChunk);
         sg.load(c);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) // T^T of the chunk, as the forward pass formed it
+            tv[p] = *reinterpret_cast<const typename TR::V *>(Tg + (int64_t)c * kChunk * kChunk + 8 * (p * kThreads + tid));
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
@@ -1028,6 +982,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         for (int p = 0; p < 2; ++p) {
             const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
             *reinterpret_cast<typename TR::V *>(Ds + row * L::V + 8 * cv) = row < nval ? dov[p] : typename TR::V{};
+            *reinterpret_cast<typename TR::V *>(TsT + row * L::T + 8 * cv) = tv[p];
         }
         // This wave's 16 value rows (column c16 of the accumulators).
         F SBn[NMT], dSB[NMT], YB[4], dZB[4], dYBn[4];
@@ -1041,7 +996,39 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         }
         __syncthreads();
         if (r > 0) load_chunk(r - 1);
-        bwd_solve<DK, true, false>(Ks, Qs, Bs, As, Ps, TsT, NsT, w, lane, g, c16);
+        // the masked scores P = (Q K^T) lower-inclusive (T^T came with the
+        // chunk): the ten 16x16 tiles (a, c <= a), three or two per wave
+        {
+            constexpr int NKB = DK / 32;
+            const int nt = w < 2 ? 3 : 2;
+#pragma unroll
+            for (int it = 0; it < 3; ++it) {
+                if (it >= nt) break;
+                // wave 0: (0,0) (3,0) (3,1); 1: (1,0) (1,1) (3,2); 2: (2,0) (2,1); 3: (2,2) (3,3)
+                const int code = w == 0 ? (it == 0 ? 0x00 : it == 1 ? 0x30 : 0x31)
+                               : w == 1 ? (it == 0 ? 0x10 : it == 1 ? 0x11 : 0x32)
+                               : w == 2 ? (it == 0 ? 0x20 : 0x21)
+                                        : (it == 0 ? 0x22 : 0x33);
+                const int ab = code >> 4, cb = code & 15;
+                F kf[NKB][2], qf[NKB][2];
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        kf[kb][h2] = ldrow(Ks, L::K, 16 * cb + c16, 32 * kb + 16 * h2, g);
+                        qf[kb][h2] = ldrow(Qs, L::K, 16 * ab + c16, 32 * kb + 16 * h2, g);
+                    }
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) acc = TR::mma32(acc, kf[kb][0], kf[kb][1], qf[kb][0], qf[kb][1]);
+                // acc[e] = k_{16cb + 4g + e} . q_{16ab + c16}
+                const int row = 16 * ab + c16, col = 16 * cb + 4 * g;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = (col + e > row) ? 0.f : acc[e];
+                stf(Ps + row * L::T + col, TR::cvt(acc));
+            }
+        }
+        __syncthreads();
         // Y = V - K S^T
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -1159,7 +1146,7 @@ template <int DK> struct FinLds {
     static constexpr int LT = L::T;
     static constexpr size_t szX = sizeof(__bf16) * 64 * LT;
     static constexpr size_t oK = 0, oQ = oK + L::szK, oB = oQ + L::szK, oBt = oB + 256, oDa = oBt + 256;
-    static constexpr size_t oA = oDa + 256, oT = oA + L::szA, oN = oT + L::szT, oP = oN + L::szN;
+    static constexpr size_t oT = oDa + 256, oP = oT + L::szT;
     static constexpr size_t oDT = oP + szX, oXs = oDT + szX, oL = oXs + szX, total = oL + szX;
 };
 
@@ -1175,8 +1162,8 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
     E *Ks = reinterpret_cast<E *>(smem + LY::oK), *Qs = reinterpret_cast<E *>(smem + LY::oQ);
     float *Bs = reinterpret_cast<float *>(smem + LY::oB), *Bt = reinterpret_cast<float *>(smem + LY::oBt);
-    float *dba = reinterpret_cast<float *>(smem + LY::oDa), *As = reinterpret_cast<float *>(smem + LY::oA);
-    E *TsT = reinterpret_cast<E *>(smem + LY::oT), *NsT = reinterpret_cast<E *>(smem + LY::oN);
+    float *dba = reinterpret_cast<float *>(smem + LY::oDa);
+    E *TsT = reinterpret_cast<E *>(smem + LY::oT); // N^T once formed
     E *dPs = reinterpret_cast<E *>(smem + LY::oP), *dTs = reinterpret_cast<E *>(smem + LY::oDT);
     E *Xs = reinterpret_cast<E *>(smem + LY::oXs), *dLs = reinterpret_cast<E *>(smem + LY::oL);
 
@@ -1205,6 +1192,11 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     sg.rg = 0.f;
     sg.nval = 0;
     sg.load(r);
+    typename TR::V tv[2]; // T^T of the chunk, as the forward pass formed it
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+        tv[p] = *reinterpret_cast<const typename TR::V *>(a.T_chunks + ((int64_t)u * a.NC + r) * kChunk * kChunk +
+                                                          8 * (p * kThreads + tid));
     // Partial sums over the value tiles (the chain kernel's accumulator
     // order): dP, dT (lower-inclusive, to LDS) and dQ, dK (this wave's token
     // rows, in registers). Every load is issued before the first use.
@@ -1238,7 +1230,12 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
             dKa[m] += ld4(tau, 8192 + 64 * DK + (w * NMT + m) * 256);
         }
     }
-    for (int i = tid; i < kChunk * LT; i += kThreads) TsT[i] = TR::fromf(0.f);
+    E *TtS = Xs, *Ls = dLs; // T^T and L until N^T is formed (X and dL come later)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
+        *reinterpret_cast<typename TR::V *>(TtS + row * LT + 8 * cv) = tv[p];
+    }
     sg.store_kqb(Ks, Qs, Bs, nullptr);
     if (w == 0) Bt[lane] = lane < nval ? TR::tof(sg.rbeta) : 0.f;
 #pragma unroll
@@ -1250,8 +1247,41 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
             dTs[row * LT + col] = TR::fromf(col <= row ? tt[s2][i] : 0.f);
         }
     __syncthreads();
-    // As = diag(beta) L (Gram phase), then N^T into TsT (solve with beta = 1)
-    bwd_solve<DK, false, true>(Ks, Qs, Bs, As, nullptr, TsT, NsT, w, lane, g, c16);
+    // Gram rows of this wave, gm[j][i] = k_t . k_{16j + c16} (t = 16w + 4g + i),
+    // and L = their strictly lower part
+    f32x4 gm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        gm[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kd = 0; kd < NMT; kd += 2)
+            gm[j] = TR::mma32(gm[j], ldrow(Ks, L::K, 16 * w + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * w + c16, 16 * kd + 16, g),
+                              ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd + 16, g));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
+            Ls[t * LT + col] = TR::fromf(col < t ? gm[j][i] : 0.f);
+        }
+    }
+    __syncthreads();
+    // N = (I + diag(beta) L)^-1 satisfies N = I - T L (T = N diag(beta)), so
+    // N^T = I - L^T T^T, an upper triangular product: row block w of it here.
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (b >= w) {
+#pragma unroll
+            for (int k0 = 0; k0 < 64; k0 += 32)
+                acc = TR::mma32(acc, TR::ldcol(Ls, LT, k0, 16 * w, g, c16), TR::ldcol(Ls, LT, k0 + 16, 16 * w, g, c16),
+                                TR::ldcol(TtS, LT, k0, 16 * b, g, c16), TR::ldcol(TtS, LT, k0 + 16, 16 * b, g, c16));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i, col = 16 * b + c16;
+            TsT[row * L::T + col] = TR::fromf((row == col ? 1.f : 0.f) - acc[i]);
+        }
+    }
+    __syncthreads();
 
     // This wave's token rows t = 16w + 4g + i:
     //   X = N^T dT -> dbeta_a = diag X, Xs = X diag(beta)
@@ -1275,20 +1305,16 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     float dbb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        f32x4 da = {0.f, 0.f, 0.f, 0.f}, gm = {0.f, 0.f, 0.f, 0.f};
+        f32x4 da = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rb = 0; rb < 4; rb += 2)
             da = TR::mma32(da, ldrow(Xs, LT, 16 * w + c16, 16 * rb, g), ldrow(Xs, LT, 16 * w + c16, 16 * rb + 16, g),
                            TR::ldcol(TsT, L::T, 16 * rb, 16 * j, g, c16), TR::ldcol(TsT, L::T, 16 * rb + 16, 16 * j, g, c16));
 #pragma unroll
-        for (int kd = 0; kd < NMT; kd += 2)
-            gm = TR::mma32(gm, ldrow(Ks, L::K, 16 * w + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * w + c16, 16 * kd + 16, g),
-                           ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd + 16, g));
-#pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
             const float dai = col < t ? -da[i] : 0.f;
-            dbb[i] += dai * gm[i];
+            dbb[i] += dai * gm[j][i];
             dLs[t * LT + col] = TR::fromf(Bt[t] * dai);
         }
     }

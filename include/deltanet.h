@@ -225,7 +225,8 @@ int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *be
  *   dq, dk, dv, dbeta : outputs, layouts of q, k, v, beta (dtype)
  *   dS0     : [B,H,dv,dk] fp32 output, or NULL to skip
  *   workspace : at least deltanet_bwd_workspace_bytes(...) bytes, 16-byte
- *             aligned: the state entering each chunk and per-chunk partial sums
+ *             aligned: the state entering each chunk, per-chunk partial sums
+ *             and each chunk's T (as the forward pass forms it)
  * Three launches: the forward chain keeping the per-chunk states, the reverse
  * chain of the state gradient, and a chunk-parallel pass for dq, dk, dbeta.
  * Errors as in deltanet_fwd (DN_ERR_UNSUPPORTED for DN_F32).
