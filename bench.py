@@ -233,8 +233,9 @@ def gdp_variant(dev, w, flops_per_head_step, peak_flops, nh=2, steps=20, warmup=
 
 
 def decode_variant(dev, B=256, H=16, d=128, steps=50, warmup=10):
-    """Time deltanet_decode_step (with and without decay) on a B x H state of
-    d x d fp32 in place; bytes = the state read and written plus the token's
+    """Time deltanet_decode_step (with and without decay) and
+    deltanet_kda_decode_step (per-channel decay) on a B x H state of d x d
+    fp32 in place; bytes = the state read and written plus the token's
     vectors (q, k, v, o, beta, g)."""
     import torch
     import chunkwise_delta_rule_amd as dn
@@ -247,9 +248,15 @@ def decode_variant(dev, B=256, H=16, d=128, steps=50, warmup=10):
     o = torch.empty_like(v)
     out = {"call": "deltanet_decode_step", "config": {"B": B, "H": H, "dk": d, "dv": d, "dtype": "bf16"},
            "steps": steps, "warmup": warmup}
-    for name, gg in (("plain", None), ("gated", g)):
-        ms, launch_ms, _ = time_steps(lambda: dn.deltanet_decode_step(q, k, v, beta, S, gg, o=o), warmup, steps)
-        nbytes = B * H * (2 * d * d * 4 + 2 * (2 * d + 2 * d + 1) + (4 if gg is not None else 0))
+    from chunkwise_delta_rule_amd.synth import make_channel_gates
+    gk = make_channel_gates((B, 1, H, d), seed=5, device=str(dev))[:, 0].contiguous()
+    for name, gg in (("plain", None), ("gated", g), ("kda", gk)):
+        if name == "kda":
+            step = lambda: dn.deltanet_kda_decode_step(q, k, v, beta, S, gk, o=o)
+        else:
+            step = lambda: dn.deltanet_decode_step(q, k, v, beta, S, gg, o=o)
+        ms, launch_ms, _ = time_steps(step, warmup, steps)
+        nbytes = B * H * (2 * d * d * 4 + 2 * (2 * d + 2 * d + 1) + (0 if gg is None else 4 * gg[0, 0].numel()))
         out[name] = {"ms_per_step": round(ms, 5), "avg_launch_us": round(launch_ms * 1e3, 2),
                      "tokens_per_s": round(B / (ms / 1e3), 1), "algorithmic_bytes": nbytes,
                      "achieved_GBps": round(nbytes / (launch_ms / 1e3) / 1e9, 1),

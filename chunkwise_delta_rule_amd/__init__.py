@@ -25,7 +25,7 @@ import os
 import torch
 
 __all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
-           "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
+           "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_decode_step", "deltanet_kda_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
            "deltanet_workspace_bytes",
            "deltanet_pick_cp_groups", "deltanet_status_string", "longest_first_order",
            "library_path", "load_library", "DeltaNetError", "DN_F32", "DN_BF16"]
@@ -79,6 +79,8 @@ def load_library(path: str | None = None):
     lib.deltanet_bwd_workspace_bytes.restype = sz
     lib.deltanet_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.deltanet_decode_step.restype = i
+    lib.deltanet_kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.deltanet_kda_decode_step.restype = i
     lib.deltanet_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.deltanet_workspace_bytes.restype = sz
     lib.deltanet_pick_cp_groups.argtypes = [i, i, i, i, i, i]
@@ -353,6 +355,40 @@ def deltanet_decode_step(q, k, v, beta, S, g=None, *, o=None, stream=None):
                                       _stream_handle(stream))
     if st != 0:
         raise DeltaNetError(st, "deltanet_decode_step")
+    return o
+
+
+def deltanet_kda_decode_step(q, k, v, beta, S, g, *, o=None, stream=None):
+    """One Kimi Delta Attention decode step in place (C-ABI
+    ``deltanet_kda_decode_step``).
+
+    q, k: [B,H,dk]; v: [B,H,dv]; beta: [B,H] (same dtype, fp32 or bf16);
+    S: [B,H,dv,dk] fp32, updated in place; g: [B,H,dk] fp32 per-channel log
+    decays. Returns o [B,H,dv].
+    """
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError("k must be [B, H, dk]")
+    B, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check(q, "q", dt, dev, (B, H, dk))
+    _check(k, "k", dt, dev, (B, H, dk))
+    _check(v, "v", dt, dev, (B, H, dv))
+    _check(beta, "beta", dt, dev, (B, H))
+    _check(S, "S", torch.float32, dev, (B, H, dv, dk))
+    _check(g, "g", torch.float32, dev, (B, H, dk))
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _check(o, "o", dt, dev, (B, H, dv))
+    with torch.cuda.device(dev):
+        st = lib.deltanet_kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S),
+                                          _ptr(o), B, H, dk, dv, _DTYPE_CODE[dt],
+                                          _stream_handle(stream))
+    if st != 0:
+        raise DeltaNetError(st, "deltanet_kda_decode_step")
     return o
 
 

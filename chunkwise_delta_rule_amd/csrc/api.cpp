@@ -182,6 +182,36 @@ int fwd_varlen(const void *q, const void *k, const void *v, const void *beta, co
 
 } // namespace
 
+namespace {
+// One decode step for every (sequence, head): g is a scalar log decay per
+// unit (Gated DeltaNet), gk a per-channel one (Kimi Delta Attention); at most
+// one of them is given.
+int decode_common(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *gk,
+                  float *S, void *o, int B, int H, int dk, int dv, int dtype, hipStream_t stream) {
+    if (dtype != DN_F32 && dtype != DN_BF16) return DN_ERR_INVALID;
+    if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0) return DN_ERR_INVALID;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return DN_ERR_UNSUPPORTED;
+    if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
+    const size_t esz = dtype == DN_BF16 ? 2 : 4;
+    if (!q || !k || !v || !beta || !S || !o) return DN_ERR_INVALID;
+    if (!aligned_to(q, 4 * esz) || !aligned_to(k, 4 * esz) || !aligned_to(v, esz) || !aligned_to(beta, esz) ||
+        !aligned_to(o, esz) || !aligned16(S) || (g && !aligned_to(g, 4)) || (gk && !aligned16(gk)))
+        return DN_ERR_INVALID;
+    dn::DecodeArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.g = g;
+    a.gk = gk;
+    a.S = S;
+    a.o = o;
+    a.n_units = B * H;
+    a.dv = dv;
+    return dn::launch_decode(dtype, dk, a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+} // namespace
+
 extern "C" {
 
 const char *deltanet_status_string(int status) {
@@ -375,26 +405,13 @@ int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, 
 
 int deltanet_decode_step(const void *q, const void *k, const void *v, const void *beta, const float *g,
                          float *S, void *o, int B, int H, int dk, int dv, int dtype, hipStream_t stream) {
-    if (dtype != DN_F32 && dtype != DN_BF16) return DN_ERR_INVALID;
-    if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0) return DN_ERR_INVALID;
-    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return DN_ERR_UNSUPPORTED;
-    if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
-    const size_t esz = dtype == DN_BF16 ? 2 : 4;
-    if (!q || !k || !v || !beta || !S || !o) return DN_ERR_INVALID;
-    if (!aligned_to(q, 4 * esz) || !aligned_to(k, 4 * esz) || !aligned_to(v, esz) || !aligned_to(beta, esz) ||
-        !aligned_to(o, esz) || !aligned16(S) || (g && !aligned_to(g, 4)))
-        return DN_ERR_INVALID;
-    dn::DecodeArgs a = {};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.beta = beta;
-    a.g = g;
-    a.S = S;
-    a.o = o;
-    a.n_units = B * H;
-    a.dv = dv;
-    return dn::launch_decode(dtype, dk, a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+    return decode_common(q, k, v, beta, g, nullptr, S, o, B, H, dk, dv, dtype, stream);
+}
+
+int deltanet_kda_decode_step(const void *q, const void *k, const void *v, const void *beta, const float *g,
+                             float *S, void *o, int B, int H, int dk, int dv, int dtype, hipStream_t stream) {
+    if (!g || !aligned16(g)) return DN_ERR_INVALID;
+    return decode_common(q, k, v, beta, nullptr, g, S, o, B, H, dk, dv, dtype, stream);
 }
 
 } // extern "C"

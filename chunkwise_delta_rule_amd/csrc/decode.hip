@@ -2,12 +2,13 @@
 // token per (sequence, head) applied to a state kept in HBM.
 //
 // The token recurrence of "Linear Attention, Visualized" (Haoran Zhang),
-// DeltaNet > "Recurrent form" and "Gated DeltaNet (GDN)", with the state S
-// (dv x dk, fp32) acting on column vectors:
-//   S <- a S (I - beta k k^T) + beta v k^T,   o = S q   (a = exp(g); a = 1 ungated)
-// evaluated per state row r as
-//   h_k = S[r] . k,  h_q = S[r] . q,  u = beta (v_r - a h_k),
-//   S[r] <- a S[r] + u k,  o_r = a h_q + u (k . q)
+// DeltaNet > "Recurrent form", "Gated DeltaNet (GDN)" and "Kimi Delta
+// Attention (KDA)", with the state S (dv x dk, fp32) acting on column vectors:
+//   S <- S D (I - beta k k^T) + beta v k^T,   o = S q
+// with D = a I (a = exp(g); a = 1 ungated) or, for KDA, D = Diag(exp(g_j))
+// over the key channels j. Per state row r, with w = S[r] D (the decayed row):
+//   h_k = w . k,  h_q = w . q,  u = beta (v_r - h_k),
+//   S[r] <- w + u k,  o_r = h_q + u (k . q)
 // so each row of S is read once and written once, in place.
 //
 // This is a streaming kernel: 2 dv dk 4 bytes of state per (sequence, head)
@@ -41,7 +42,8 @@ __device__ inline float quad_sum(float x) {
     return x;
 }
 
-template <typename E, int DK, bool GATED>
+// MODE 0: no decay, 1: scalar decay per unit, 2: per-channel decay (KDA).
+template <typename E, int DK, int MODE>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeArgs a) {
     constexpr int NJ = DK / 16; // column groups of 4 per lane
     const int tiles = a.dv / 64;
@@ -51,13 +53,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeArgs a)
     const E *k = reinterpret_cast<const E *>(a.k) + (int64_t)u * DK;
     const float beta = (float)reinterpret_cast<const E *>(a.beta)[u];
     const float v = (float)reinterpret_cast<const E *>(a.v)[(int64_t)u * a.dv + row];
-    const float decay = GATED ? expf(a.g[u]) : 1.f;
+    const float decay = MODE == 1 ? expf(a.g[u]) : 1.f;
     float *Srow = a.S + ((int64_t)u * a.dv + row) * DK + 4 * p;
 
     f32x4 s[NJ], kv[NJ];
     float hk = 0.f, hq = 0.f, kq = 0.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) s[j] = *reinterpret_cast<const f32x4 *>(Srow + 16 * j);
+    if constexpr (MODE == 2) { // the decayed row w = S[r] Diag(exp(g)) replaces S[r] below
+        const float *gk = a.gk + (int64_t)u * DK;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const f32x4 gv = *reinterpret_cast<const f32x4 *>(gk + 16 * j + 4 * p);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[j][e] *= __builtin_amdgcn_exp2f(gv[e] * 1.44269504088896340736f);
+        }
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         kv[j] = load4<E>(k + 16 * j + 4 * p);
@@ -85,10 +96,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeArgs a)
 template <typename E, int DK> hipError_t launch_dec(const DecodeArgs &a, hipStream_t s) {
     const int grid = a.n_units * (a.dv / 64);
     if (grid <= 0) return hipSuccess;
-    if (a.g)
-        hipLaunchKernelGGL((decode_kernel<E, DK, true>), dim3(grid), dim3(kDecThreads), 0, s, a);
+    if (a.gk)
+        hipLaunchKernelGGL((decode_kernel<E, DK, 2>), dim3(grid), dim3(kDecThreads), 0, s, a);
+    else if (a.g)
+        hipLaunchKernelGGL((decode_kernel<E, DK, 1>), dim3(grid), dim3(kDecThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_kernel<E, DK, false>), dim3(grid), dim3(kDecThreads), 0, s, a);
+        hipLaunchKernelGGL((decode_kernel<E, DK, 0>), dim3(grid), dim3(kDecThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -52,7 +52,8 @@ struct ChainArgs {
 // q, k: [n_units, dk]; v, o: [n_units, dv]; beta, g: [n_units]; S: [n_units, dv, dk].
 struct DecodeArgs {
     const void *q, *k, *v, *beta;
-    const float *g; // log decays, or nullptr (no decay)
+    const float *g;  // log decays, or nullptr (no decay)
+    const float *gk; // per-channel log decays [n_units][dk] (Kimi Delta Attention), or nullptr
     float *S;
     void *o;
     int n_units;

@@ -215,6 +215,18 @@ int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *be
                      int T, int dk, int dv, int chunk, int dtype, hipStream_t stream);
 
 /*
+ * One Kimi Delta Attention decode step (the recurrence above for a single
+ * token), in place, for every unit u = (b, h):
+ *     S[u] <- S[u] Diag(exp(g)) (I - beta k k^T) + beta v k^T,   o = S[u] q
+ *   g : [B, H, dk] float32 per-channel log decays, 16-byte aligned (required)
+ * Other arguments, dtypes, shapes and errors as in deltanet_decode_step; the
+ * state continues exactly from deltanet_kda_fwd's S_final.
+ */
+int deltanet_kda_decode_step(const void *q, const void *k, const void *v, const void *beta,
+                             const float *g, float *S, void *o, int B, int H, int dk, int dv,
+                             int dtype, hipStream_t stream);
+
+/*
  * Backward pass of deltanet_fwd (DN_BF16 only): gradients for upstream dO of
  * the output and dS_final of the final state. The pages give no backward
  * pass; this is the chain rule applied to the per-chunk algorithm above (see

@@ -31,6 +31,7 @@ def test_library_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd",
                           "deltanet_gated_fwd_varlen", "deltanet_gdp_fwd", "deltanet_decode_step",
+                          "deltanet_kda_fwd", "deltanet_kda_decode_step", "deltanet_bwd",
                           "deltanet_workspace_bytes",
                           "deltanet_pick_cp_groups", "deltanet_status_string"}
     raw = ctypes.CDLL(dn.library_path())
@@ -178,6 +179,24 @@ def test_decode_step_rejects_bad_arguments(lib, kw, status):
     st = lib.deltanet_decode_step(vp(a["q"]), vp(FAKE), vp(FAKE), vp(FAKE), vp(a["g"]) if a["g"] else None,
                                   vp(a["S"]) if a["S"] else None, vp(a["o"]) if a["o"] else None,
                                   a["B"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+    assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None), DN_ERR_INVALID),        # the per-channel decays are required
+    (dict(g=FAKE + 8), DN_ERR_INVALID),    # and 16-byte aligned
+    (dict(B=0), DN_ERR_INVALID),
+    (dict(dk=96), DN_ERR_UNSUPPORTED),
+    (dict(S=FAKE + 8), DN_ERR_INVALID),
+    (dict(o=None), DN_ERR_INVALID),
+])
+def test_kda_decode_step_rejects_bad_arguments(lib, kw, status):
+    a = dict(g=FAKE, S=FAKE, o=FAKE, B=2, H=2, dk=128, dv=128)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    st = lib.deltanet_kda_decode_step(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(a["g"]) if a["g"] else None,
+                                      vp(a["S"]) if a["S"] else None, vp(a["o"]) if a["o"] else None,
+                                      a["B"], a["H"], a["dk"], a["dv"], 1, None)
     assert st == status
 
 
