@@ -25,7 +25,7 @@ import os
 import torch
 
 __all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
-           "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_decode_step", "deltanet_kda_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
+           "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_kda_fwd_varlen", "deltanet_decode_step", "deltanet_kda_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
            "deltanet_workspace_bytes",
            "deltanet_pick_cp_groups", "deltanet_status_string", "longest_first_order",
            "library_path", "load_library", "DeltaNetError", "DN_F32", "DN_BF16"]
@@ -73,6 +73,8 @@ def load_library(path: str | None = None):
     lib.deltanet_gdp_fwd.restype = i
     lib.deltanet_kda_fwd.argtypes = [vp] * 8 + [i, i, i, i, i, i, i, vp]
     lib.deltanet_kda_fwd.restype = i
+    lib.deltanet_kda_fwd_varlen.argtypes = [vp] * 10 + [i, i, i, i, i, i, i, vp]
+    lib.deltanet_kda_fwd_varlen.restype = i
     lib.deltanet_bwd.argtypes = [vp] * 12 + [i, i, i, i, i, i, i, vp, sz, vp]
     lib.deltanet_bwd.restype = i
     lib.deltanet_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -356,6 +358,48 @@ def deltanet_decode_step(q, k, v, beta, S, g=None, *, o=None, stream=None):
     if st != 0:
         raise DeltaNetError(st, "deltanet_decode_step")
     return o
+
+
+def deltanet_kda_fwd_varlen(q, k, v, beta, g, cu_seqlens, S0=None, *, seq_order=None, chunk: int = 64,
+                            o=None, S_final=None, output_final_state: bool = True, stream=None):
+    """Kimi Delta Attention over packed sequences (C-ABI ``deltanet_kda_fwd_varlen``).
+
+    As ``deltanet_fwd_varlen`` (bf16), plus g: [T,H,dk] float32 per-channel
+    log decays.
+    """
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError("k must be [T, H, dk]")
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    if dt != torch.bfloat16:
+        raise TypeError("deltanet_kda_fwd_varlen takes bfloat16 inputs")
+    N = cu_seqlens.numel() - 1
+    _check(q, "q", dt, dev, (T, H, dk))
+    _check(k, "k", dt, dev, (T, H, dk))
+    _check(v, "v", dt, dev, (T, H, dv))
+    _check(beta, "beta", dt, dev, (T, H))
+    _check(g, "g", torch.float32, dev, (T, H, dk))
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev, (N + 1,))
+    if seq_order is not None:
+        _check(seq_order, "seq_order", torch.int32, dev, (N,))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev, (N, H, dv, dk))
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=dt, device=dev)
+    _check(o, "o", dt, dev, (T, H, dv))
+    if output_final_state and S_final is None:
+        S_final = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _check(S_final, "S_final", torch.float32, dev, (N, H, dv, dk))
+    with torch.cuda.device(dev):
+        st = lib.deltanet_kda_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o),
+                                         _ptr(S_final), _ptr(cu_seqlens), _ptr(seq_order), N, T, H, dk, dv,
+                                         chunk, _DTYPE_CODE[dt], _stream_handle(stream))
+    if st != 0:
+        raise DeltaNetError(st, "deltanet_kda_fwd_varlen")
+    return o, S_final
 
 
 def deltanet_kda_decode_step(q, k, v, beta, S, g, *, o=None, stream=None):

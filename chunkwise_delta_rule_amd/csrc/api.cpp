@@ -323,6 +323,39 @@ int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *be
     return dn::launch_kda(dk, dv, a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 
+int deltanet_kda_fwd_varlen(const void *q, const void *k, const void *v, const void *beta, const float *g,
+                            const float *S0, void *o, float *S_final, const int32_t *cu_seqlens,
+                            const int32_t *seq_order, int N, int total_T, int H, int dk, int dv, int chunk,
+                            int dtype, hipStream_t stream) {
+    int st = check_shape(dk, dv, chunk, dtype);
+    if (st != DN_OK) return st;
+    if (dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
+    if (N <= 0 || H <= 0 || total_T < 0 || !cu_seqlens) return DN_ERR_INVALID;
+    if ((int64_t)N * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
+    if (total_T > 0) {
+        if (!q || !k || !v || !beta || !g || !o) return DN_ERR_INVALID;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(g) || !aligned_to(beta, 2))
+            return DN_ERR_INVALID;
+    }
+    if (!aligned_to(cu_seqlens, 4) || (seq_order && !aligned_to(seq_order, 4))) return DN_ERR_INVALID;
+    if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return DN_ERR_INVALID;
+    dn::KdaArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.g = g;
+    a.S0 = S0;
+    a.o = o;
+    a.S_final = S_final;
+    a.cu_seqlens = cu_seqlens;
+    a.seq_order = seq_order;
+    a.B = N;
+    a.H = H;
+    a.T = total_T;
+    return dn::launch_kda(dk, dv, a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+
 size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     if (B <= 0 || H <= 0 || T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
     const size_t units = (size_t)B * H, nc = (size_t)(T + dn::kChunk - 1) / dn::kChunk;

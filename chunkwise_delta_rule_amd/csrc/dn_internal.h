@@ -67,7 +67,9 @@ struct KdaArgs {
     const float *S0;
     void *o;
     float *S_final;
-    int B, H, T;
+    const int32_t *cu_seqlens; // varlen: [B + 1] token offsets of B packed sequences, else nullptr
+    const int32_t *seq_order;  // varlen: processing order of the sequences, or nullptr
+    int B, H, T;               // varlen: B sequences, T the total token count
 };
 hipError_t launch_kda(int dk, int dv, const KdaArgs &a, hipStream_t stream);
 

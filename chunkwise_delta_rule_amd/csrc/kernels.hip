@@ -1413,9 +1413,22 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     const int ntile = DV / 64;
     int u, tau;
     map_block(blockIdx.x, a.B * a.H, ntile, u, tau); // the tiles of a unit share an XCD
-    const int b = u / a.H, h = u - b * a.H, row0 = 64 * tau;
-    const int64_t tok0 = (int64_t)b * a.T, sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
-    const int NC = (a.T + kChunk - 1) / kChunk;
+    const int rank = u / a.H, h = u - rank * a.H, row0 = 64 * tau;
+    // dense: sequence rank, T tokens each; varlen: sequence seq_order[rank] of the packed batch
+    int64_t tok0, su;
+    int len;
+    if (a.cu_seqlens) {
+        const int n = a.seq_order ? a.seq_order[rank] : rank;
+        tok0 = a.cu_seqlens[n];
+        len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+        su = (int64_t)n * a.H + h;
+    } else {
+        tok0 = (int64_t)rank * a.T;
+        len = a.T;
+        su = u;
+    }
+    const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
+    const int NC = (len + kChunk - 1) / kChunk;
 
     Stager<E, DK> sg;
     sg.sqk = sqk;
@@ -1429,7 +1442,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     sg.gh = nullptr;
     sg.sb = SubstepBase{0, 0u, 1u};
     sg.H = a.H;
-    sg.len = a.T;
+    sg.len = len;
     sg.tid = tid;
     sg.has_v = true;
     sg.rbeta = TR::fromf(0.f);
@@ -1442,8 +1455,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     f32x4 Sacc[NMT];
 #pragma unroll
     for (int m = 0; m < NMT; ++m)
-        Sacc[m] = a.S0 ? *reinterpret_cast<const f32x4 *>(a.S0 + ((int64_t)u * DV + row0 + 16 * w + c16) * DK +
-                                                           16 * m + 4 * g)
+        Sacc[m] = a.S0 ? *reinterpret_cast<const f32x4 *>(a.S0 + (su * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     constexpr int NP = DK / 2; // channel pairs; the scaling pass has one thread per (pair, sub-chunk)
@@ -1457,7 +1469,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     f32x2 gq[16];
     auto load_chunk = [&](int c) {
         sg.load(c);
-        const int n = min(kChunk, a.T - c * kChunk);
+        const int n = min(kChunk, len - c * kChunk);
         if (scaler) {
 #pragma unroll
             for (int l = 0; l < 16; ++l)
@@ -1471,7 +1483,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     constexpr int LO = 64 + 8;
     static_assert(sizeof(E) * 64 * LO <= L::szA, "output tile fits over the Gram rows");
     auto flush_o = [&](int c) {
-        const int n = min(kChunk, a.T - c * kChunk);
+        const int n = min(kChunk, len - c * kChunk);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
@@ -1482,7 +1494,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     };
     if (NC > 0) load_chunk(0);
     for (int r = 0; r < NC; ++r) {
-        const int nval = min(kChunk, a.T - r * kChunk);
+        const int nval = min(kChunk, len - r * kChunk);
         __syncthreads(); // the previous chunk's reads are done
         if (r > 0) flush_o(r - 1);
         sg.store_kqb(Ks, Qs, Bs, nullptr);
@@ -1597,7 +1609,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     if (a.S_final) {
 #pragma unroll
         for (int m = 0; m < NMT; ++m)
-            *reinterpret_cast<f32x4 *>(a.S_final + ((int64_t)u * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g) =
+            *reinterpret_cast<f32x4 *>(a.S_final + (su * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g) =
                 Sacc[m];
     }
 }
@@ -1634,7 +1646,7 @@ hipError_t launch_fill(float *p, size_t n, float value, hipStream_t stream) {
 
 template <int DK, int DV> hipError_t launch_kda_dims(const KdaArgs &a, hipStream_t s) {
     const int grid = a.B * a.H * (DV / 64);
-    if (grid <= 0 || a.T <= 0) return hipSuccess;
+    if (grid <= 0 || (a.T <= 0 && !a.cu_seqlens)) return hipSuccess; // varlen: empty sequences still copy S0
     hipLaunchKernelGGL((kda_chain_kernel<DK, DV>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

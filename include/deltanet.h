@@ -215,6 +215,18 @@ int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *be
                      int T, int dk, int dv, int chunk, int dtype, hipStream_t stream);
 
 /*
+ * deltanet_kda_fwd over a packed batch of N sequences (layouts as in
+ * deltanet_fwd_varlen: tokens [total_T, H, *], g [total_T, H, dk] float32,
+ * cu_seqlens [N + 1], optional seq_order, S0 / S_final [N, H, dv, dk]); the
+ * state starts afresh at each sequence. DN_BF16 only.
+ */
+int deltanet_kda_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                            const float *g, const float *S0, void *o, float *S_final,
+                            const int32_t *cu_seqlens, const int32_t *seq_order, int N,
+                            int total_T, int H, int dk, int dv, int chunk, int dtype,
+                            hipStream_t stream);
+
+/*
  * One Kimi Delta Attention decode step (the recurrence above for a single
  * token), in place, for every unit u = (b, h):
  *     S[u] <- S[u] Diag(exp(g)) (I - beta k k^T) + beta v k^T,   o = S[u] q

@@ -4,8 +4,9 @@ The oracle runs the KDA token recurrence of "Linear Attention, Visualized"
 ("Kimi Delta Attention (KDA)": per-channel decay, then the delta rule) token
 by token; the library runs that section's per-chunk algorithm on 16-token
 sub-chunks. Cases: every (dk, dv), ragged lengths around chunk and sub-chunk
-boundaries, initial state, weak, strong and absent decay, and decay equal
-across channels against the Gated DeltaNet kernel. Bar: max|gpu - oracle| /
+boundaries, initial state, weak, strong and absent decay, decay equal
+across channels against the Gated DeltaNet kernel, and packed sequences
+(varlen) against the oracle per sequence. Bar: max|gpu - oracle| /
 max|oracle| within 2e-2 (bf16 operands), for o and for the final state.
 """
 
@@ -13,8 +14,9 @@ import pytest
 import torch
 
 import oracle
-from chunkwise_delta_rule_amd import deltanet_gated_fwd, deltanet_kda_fwd
-from chunkwise_delta_rule_amd.synth import make_channel_gates, make_inputs
+from chunkwise_delta_rule_amd import (deltanet_gated_fwd, deltanet_kda_fwd, deltanet_kda_fwd_varlen,
+                                      longest_first_order)
+from chunkwise_delta_rule_amd.synth import make_channel_gates, make_inputs, make_varlen_inputs
 from helpers import TOL, f64, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -61,3 +63,30 @@ def test_kda_equal_channels_matches_gated_deltanet():
     o2, s2 = deltanet_gated_fwd(*d, gs[..., 0].contiguous().to(DEV), S0.to(DEV))
     torch.cuda.synchronize()
     assert rel_err(f64(o1), f64(o2)) < 2e-2 and rel_err(f64(s1), f64(s2)) < 2e-2
+
+
+@pytest.mark.parametrize("order", ["given", "longest_first"])
+def test_kda_varlen(order):
+    # packed sequences, the state starting afresh at each one: every sequence
+    # against the oracle's KDA recurrence over that sequence alone
+    lengths = [0, 1, 15, 16, 17, 64, 65, 200, 130, 7]
+    H, dk, dv = 3, 128, 128
+    print(f"[case] kda varlen {lengths} order={order}", flush=True)
+    q, k, v, beta, cu, S0 = make_varlen_inputs(lengths, H, dk, dv, seed=330, s0_std=0.3)
+    g = make_channel_gates((1, sum(lengths), H, dk), seed=330)[0]
+    d = [x.to(DEV) for x in (q, k, v, beta, g)]
+    cud = cu.to(DEV)
+    so = longest_first_order(cud) if order == "longest_first" else None
+    o, Sf = deltanet_kda_fwd_varlen(*d, cud, S0.to(DEV), seq_order=so)
+    torch.cuda.synchronize()
+    o64, s64 = f64(o), f64(Sf)
+    worst = 0.0
+    for n, L in enumerate(lengths):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = [f64(x)[None, a:b] for x in (q, k, v, beta, g)]
+        ro, rs = oracle.kda_fwd(*sl, f64(S0)[n:n + 1])
+        es = rel_err(s64[n:n + 1], rs)
+        eo = rel_err(o64[None, a:b], ro) if L > 0 else 0.0
+        worst = max(worst, eo, es)
+        assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16], (n, L, eo, es)
+    print(f"  worst err {worst:.3e}", flush=True)
