@@ -183,6 +183,108 @@ int fwd_varlen(const void *q, const void *k, const void *v, const void *beta, co
 } // namespace
 
 namespace {
+size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+// Workspace bytes per chunk slot of the backward pass: the state entering the
+// chunk and the per-value-tile partial sums (fp32), then T^T of the chunk (bf16).
+size_t bwd_slot_bytes(int dk, int dv) {
+    return ((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_floats(dk)) * sizeof(float) +
+           (size_t)dn::kChunk * dn::kChunk * sizeof(__bf16);
+}
+
+// Chunk slots of a packed batch, bounded without reading the lengths:
+// sum_n ceil(L_n / 64) <= total_T / 64 + N.
+size_t varlen_max_slots(int N, int total_T, int H) {
+    return ((size_t)total_T / dn::kChunk + (size_t)N) * (size_t)H;
+}
+
+// The backward pass, dense (cu_seqlens NULL: B sequences of T tokens) or
+// packed (B = N sequences, T = total tokens). Workspace: [S entering each
+// chunk | partial sums | T^T of each chunk | chunk offsets (varlen)].
+int bwd_common(const void *q, const void *k, const void *v, const void *beta, const float *S0, const void *dO,
+               const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dS0,
+               const int32_t *cu_seqlens, const int32_t *seq_order, int B, int H, int T, int dk, int dv, int chunk,
+               int dtype, void *workspace, size_t workspace_bytes, size_t need, hipStream_t stream) {
+    int st = check_shape(dk, dv, chunk, dtype);
+    if (st != DN_OK) return st;
+    if (dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
+    if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !dO || !dq || !dk_ || !dv_ || !dbeta) return DN_ERR_INVALID;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned_to(beta, 2) ||
+            !aligned_to(dq, 2) || !aligned_to(dk_, 2) || !aligned_to(dv_, 2) || !aligned_to(dbeta, 2))
+            return DN_ERR_INVALID;
+    }
+    if ((S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
+        return DN_ERR_INVALID;
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return DN_ERR_WORKSPACE;
+    const bool varlen = cu_seqlens != nullptr;
+    const int NC = varlen ? 0 : (T + dn::kChunk - 1) / dn::kChunk;
+    if (!varlen && NC == 0) { // no tokens: the gradient of S0 is the gradient of the final state
+        if (dS0) {
+            const size_t n = (size_t)B * H * dv * dk * sizeof(float);
+            const hipError_t e = dS_final ? hipMemcpyAsync(dS0, dS_final, n, hipMemcpyDeviceToDevice, stream)
+                                          : dn::launch_fill(dS0, n / sizeof(float), 0.f, stream);
+            if (e != hipSuccess) return DN_ERR_HIP;
+        }
+        return DN_OK;
+    }
+    const size_t slots = varlen ? varlen_max_slots(B, T, H) : (size_t)B * H * NC;
+    float *Sck = static_cast<float *>(workspace);
+    float *part = Sck + slots * dv * dk;
+    __bf16 *Tck = reinterpret_cast<__bf16 *>(part + slots * (dv / dn::kRows) * dn::bwd_part_floats(dk));
+    int32_t *cb = varlen ? reinterpret_cast<int32_t *>(Tck + slots * dn::kChunk * dn::kChunk) : nullptr;
+    if (varlen && dn::launch_chunk_base(cu_seqlens, B, cb, stream) != hipSuccess) return DN_ERR_HIP;
+    // pass 1: the forward chain, keeping the state entering every chunk and its T
+    dn::ChainArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.S0 = S0;
+    a.S_chunks = Sck;
+    a.T_chunks = Tck;
+    a.chunk_base = cb;
+    a.cu_seqlens = cu_seqlens;
+    a.seq_order = seq_order;
+    a.B = B;
+    a.H = H;
+    a.T = T;
+    a.nh = 1;
+    a.kind = varlen ? dn::kVarlen : dn::kDense;
+    a.n_units = B * H;
+    a.n_tiles = dv / dn::kRows;
+    if (dn::launch_chain(dtype, dk, dv, false, a, stream) != hipSuccess) return DN_ERR_HIP;
+    // passes 2 and 3
+    dn::BwdArgs b = {};
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.beta = beta;
+    b.dO = dO;
+    b.dS_final = dS_final;
+    b.S_chunks = Sck;
+    b.T_chunks = Tck;
+    b.part = part;
+    b.dS0 = dS0;
+    b.dq = dq;
+    b.dk = dk_;
+    b.dv = dv_;
+    b.dbeta = dbeta;
+    b.cu_seqlens = cu_seqlens;
+    b.seq_order = seq_order;
+    b.chunk_base = cb;
+    b.B = B;
+    b.H = H;
+    b.T = T;
+    b.NC = NC;
+    b.n_tiles = dv / dn::kRows;
+    b.max_slots = (int64_t)slots;
+    return dn::launch_bwd(dk, dv, b, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+}
+} // namespace
+
+namespace {
 // One decode step for every (sequence, head): g is a scalar log decay per
 // unit (Gated DeltaNet), gk a per-channel one (Kimi Delta Attention); at most
 // one of them is given.
@@ -358,82 +460,33 @@ int deltanet_kda_fwd_varlen(const void *q, const void *k, const void *v, const v
 
 size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     if (B <= 0 || H <= 0 || T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
-    const size_t units = (size_t)B * H, nc = (size_t)(T + dn::kChunk - 1) / dn::kChunk;
-    // per (unit, chunk): the entering state and the partial sums (fp32), then T^T (bf16)
-    return units * nc * (((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_floats(dk)) * sizeof(float) +
-                         (size_t)dn::kChunk * dn::kChunk * sizeof(__bf16));
+    const size_t slots = (size_t)B * H * ((T + dn::kChunk - 1) / dn::kChunk);
+    return bwd_slot_bytes(dk, dv) * slots;
+}
+
+size_t deltanet_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, int dv, int chunk) {
+    if (N <= 0 || H <= 0 || total_T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
+    return bwd_slot_bytes(dk, dv) * varlen_max_slots(N, total_T, H) + align16((size_t)(N + 1) * sizeof(int32_t));
 }
 
 int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, const float *S0, const void *dO,
                  const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dS0, int B, int H, int T,
                  int dk, int dv, int chunk, int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    int st = check_shape(dk, dv, chunk, dtype);
-    if (st != DN_OK) return st;
-    if (dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
     if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
-    if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
-    if (T > 0) {
-        if (!q || !k || !v || !beta || !dO || !dq || !dk_ || !dv_ || !dbeta) return DN_ERR_INVALID;
-        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned_to(beta, 2) ||
-            !aligned_to(dq, 2) || !aligned_to(dk_, 2) || !aligned_to(dv_, 2) || !aligned_to(dbeta, 2))
-            return DN_ERR_INVALID;
-    }
-    if ((S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
-        return DN_ERR_INVALID;
     const size_t need = deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk);
-    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return DN_ERR_WORKSPACE;
-    const int NC = (T + dn::kChunk - 1) / dn::kChunk;
-    float *Sck = static_cast<float *>(workspace);
-    if (NC == 0) { // no tokens: the gradient of S0 is the gradient of the final state
-        if (dS0) {
-            const size_t n = (size_t)B * H * dv * dk * sizeof(float);
-            const hipError_t e = dS_final ? hipMemcpyAsync(dS0, dS_final, n, hipMemcpyDeviceToDevice, stream)
-                                          : dn::launch_fill(dS0, n / sizeof(float), 0.f, stream);
-            if (e != hipSuccess) return DN_ERR_HIP;
-        }
-        return DN_OK;
-    }
-    // pass 1: the forward chain, keeping the state that enters every chunk
-    dn::ChainArgs a = {};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.beta = beta;
-    a.S0 = S0;
-    a.S_chunks = Sck;
-    float *part = Sck + (size_t)B * H * NC * dv * dk;
-    __bf16 *Tck = reinterpret_cast<__bf16 *>(part + (size_t)B * H * NC * (dv / dn::kRows) * dn::bwd_part_floats(dk));
-    a.T_chunks = Tck;
-    a.B = B;
-    a.H = H;
-    a.T = T;
-    a.nh = 1;
-    a.kind = dn::kDense;
-    a.n_units = B * H;
-    a.n_tiles = dv / dn::kRows;
-    if (dn::launch_chain(dtype, dk, dv, false, a, stream) != hipSuccess) return DN_ERR_HIP;
-    // passes 2 and 3
-    dn::BwdArgs b = {};
-    b.q = q;
-    b.k = k;
-    b.v = v;
-    b.beta = beta;
-    b.dO = dO;
-    b.dS_final = dS_final;
-    b.S_chunks = Sck;
-    b.T_chunks = Tck;
-    b.part = part;
-    b.dS0 = dS0;
-    b.dq = dq;
-    b.dk = dk_;
-    b.dv = dv_;
-    b.dbeta = dbeta;
-    b.B = B;
-    b.H = H;
-    b.T = T;
-    b.NC = NC;
-    b.n_tiles = dv / dn::kRows;
-    return dn::launch_bwd(dk, dv, b, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+    return bwd_common(q, k, v, beta, S0, dO, dS_final, dq, dk_, dv_, dbeta, dS0, nullptr, nullptr, B, H, T, dk, dv,
+                      chunk, dtype, workspace, workspace_bytes, need, stream);
+}
+
+int deltanet_bwd_varlen(const void *q, const void *k, const void *v, const void *beta, const float *S0,
+                        const void *dO, const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dS0,
+                        const int32_t *cu_seqlens, const int32_t *seq_order, int N, int total_T, int H, int dk,
+                        int dv, int chunk, int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (N <= 0 || H <= 0 || total_T < 0 || !cu_seqlens) return DN_ERR_INVALID;
+    if (!aligned_to(cu_seqlens, 4) || (seq_order && !aligned_to(seq_order, 4))) return DN_ERR_INVALID;
+    const size_t need = deltanet_bwd_varlen_workspace_bytes(N, total_T, H, dk, dv, chunk);
+    return bwd_common(q, k, v, beta, S0, dO, dS_final, dq, dk_, dv_, dbeta, dS0, cu_seqlens, seq_order, N, H,
+                      total_T, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
 }
 
 int deltanet_decode_step(const void *q, const void *k, const void *v, const void *beta, const float *g,

@@ -30,6 +30,8 @@ struct ChainArgs {
                      // [B*H][chunks][dv][dk] fp32 (kept for the backward pass)
     __bf16 *T_chunks; // with S_chunks (bf16 DeltaNet without output), or nullptr: T^T of
                       // every chunk, [B*H][chunks][64][64] bf16 row-major (backward pass)
+    const int32_t *chunk_base; // varlen with S_chunks: chunks before each sequence, [N + 1];
+                               // unit (n, h) owns chunk slots chunk_base[n] H + h NC_n + c
     const int32_t *cu_seqlens;
     const int32_t *seq_order;
     // Context-parallel workspace, per (b*H + h) and group g:
@@ -80,11 +82,17 @@ struct BwdArgs {
     const float *dS_final; // [B*H][dv][dk] or nullptr (zero)
     const float *S_chunks; // [B*H][NC][dv][dk]: the state entering each chunk
     const __bf16 *T_chunks; // [B*H][NC][64][64]: T^T of each chunk (the forward's), row-major
-    float *part;           // [n_tiles][B*H][NC] blocks of per-tile partial sums
+    float *part;           // [n_tiles][max_slots] blocks of per-tile partial sums
     float *dS0;            // [B*H][dv][dk] or nullptr
     void *dq, *dk, *dv, *dbeta;
+    // varlen: B sequences packed along T (cu_seqlens [B + 1], optional order),
+    // chunk slots as in ChainArgs::chunk_base; dense: slot of (unit u, chunk c) = u NC + c
+    const int32_t *cu_seqlens, *seq_order, *chunk_base;
     int B, H, T, NC, n_tiles;
+    int64_t max_slots; // chunk slots the workspace holds (dense: B H NC); the finishing grid
 };
+// Chunk slots before each packed sequence: cb[n] = sum_{m < n} ceil(L_m / 64), cb[N] the total.
+hipError_t launch_chunk_base(const int32_t *cu_seqlens, int N, int32_t *cb, hipStream_t stream);
 // Floats of one partial block: dP, dT (64 x 64 each), dQ, dK (64 x dk each).
 constexpr size_t bwd_part_floats(int dk) { return 2 * 64 * 64 + 2 * 64 * (size_t)dk; }
 hipError_t launch_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream);

@@ -62,6 +62,11 @@ template <int DK, int DV> __device__ inline Work decode_work(const ChainArgs &a)
         const int64_t su = (int64_t)n * H + wk.h;
         if (a.S0) wk.Sin = a.S0 + (su * DV + wk.row0) * DK;
         if (a.S_final) wk.Sout = a.S_final + (su * DV + wk.row0) * DK;
+        if (a.S_chunks) { // the chunk slots of this unit, contiguous
+            const int64_t slot0 = (int64_t)a.chunk_base[n] * H + (int64_t)wk.h * ((wk.len + kChunk - 1) / kChunk);
+            wk.Schunks = a.S_chunks + (slot0 * DV + wk.row0) * DK;
+            if (a.T_chunks && tau == 0) wk.Tchunks = a.T_chunks + slot0 * kChunk * kChunk;
+        }
     } else {
         const int groups = (a.kind == kCpOutput) ? a.G : a.G - 1;
         const int bh = u / groups;

@@ -917,9 +917,24 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     int u, tau;
     map_block(blockIdx.x, a.B * a.H, a.n_tiles, u, tau); // the tiles of a unit share an XCD
-    const int b = u / a.H, h = u - b * a.H, row0 = 64 * tau;
-    const int64_t tok0 = (int64_t)b * a.T, sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
-    const int units = a.B * a.H;
+    const int rank = u / a.H, h = u - rank * a.H, row0 = 64 * tau;
+    // token range, state slot su and first chunk slot of this unit
+    int64_t tok0, su, slot0;
+    int len;
+    if (a.cu_seqlens) {
+        const int n = a.seq_order ? a.seq_order[rank] : rank;
+        tok0 = a.cu_seqlens[n];
+        len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+        su = (int64_t)n * a.H + h;
+        slot0 = (int64_t)a.chunk_base[n] * a.H + (int64_t)h * ((len + kChunk - 1) / kChunk);
+    } else {
+        tok0 = (int64_t)rank * a.T;
+        len = a.T;
+        su = u;
+        slot0 = (int64_t)u * a.NC;
+    }
+    const int NC = (len + kChunk - 1) / kChunk;
+    const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
 
     Stager<E, DK> sg;
     sg.sqk = sqk;
@@ -933,7 +948,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     sg.gh = nullptr;
     sg.sb = SubstepBase{0, 0u, 1u};
     sg.H = a.H;
-    sg.len = a.T;
+    sg.len = len;
     sg.tid = tid;
     sg.has_v = true;
     sg.rbeta = TR::fromf(0.f);
@@ -946,8 +961,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     f32x4 dSacc[NMT], Sacc[NMT];
 #pragma unroll
     for (int m = 0; m < NMT; ++m)
-        dSacc[m] = a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + ((int64_t)u * DV + row0 + 16 * w + c16) *
-                                                                                  DK + 16 * m + 4 * g)
+        dSacc[m] = a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + (su * DV + row0 + 16 * w + c16) * DK +
+                                                                 16 * m + 4 * g)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i = tid; i < kChunk * LT; i += kThreads) Ps[i] = TR::fromf(0.f); // only P's lower blocks are written
 
@@ -955,9 +970,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     // registers; issued one chunk ahead so their latency hides under the
     // previous chunk's products.
     typename TR::V dov[2], tv[2];
-    const E *Tg = a.T_chunks + (int64_t)u * a.NC * kChunk * kChunk;
+    const E *Tg = a.T_chunks + slot0 * kChunk * kChunk;
     auto load_chunk = [&](int c) {
-        const int n = min(kChunk, a.T - c * kChunk);
+        const int n = min(kChunk, len - c * kChunk);
         sg.load(c);
 #pragma unroll
         for (int p = 0; p < 2; ++p) // T^T of the chunk, as the forward pass formed it
@@ -968,13 +983,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
             dov[p] = *reinterpret_cast<const typename TR::V *>(dOg + ((int64_t)c * kChunk + min(row, n - 1)) * sv +
                                                                8 * cv);
         }
-        const float *Sr = a.S_chunks + (((int64_t)u * a.NC + c) * DV + row0 + 16 * w + c16) * DK + 4 * g;
+        const float *Sr = a.S_chunks + ((slot0 + c) * DV + row0 + 16 * w + c16) * DK + 4 * g;
 #pragma unroll
         for (int m = 0; m < NMT; ++m) Sacc[m] = *reinterpret_cast<const f32x4 *>(Sr + 16 * m);
     };
-    if (a.NC > 0) load_chunk(a.NC - 1);
-    for (int r = a.NC - 1; r >= 0; --r) {
-        const int nval = min(kChunk, a.T - r * kChunk);
+    if (NC > 0) load_chunk(NC - 1);
+    for (int r = NC - 1; r >= 0; --r) {
+        const int nval = min(kChunk, len - r * kChunk);
         __syncthreads(); // the previous chunk's reads of the staging buffers are done
         sg.store_kqb(Ks, Qs, Bs, nullptr);
         sg.store_v(Vs);
@@ -1103,7 +1118,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         // stored in accumulator order: one 16-byte piece per (wave, column
         // block, lane), so every store (and the finishing kernel's load) of a
         // wave moves 1 KB of contiguous memory.
-        float *pb = a.part + (((int64_t)tau * units + u) * a.NC + r) * bwd_part_floats(DK);
+        float *pb = a.part + ((int64_t)tau * a.max_slots + slot0 + r) * bwd_part_floats(DK);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
             f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dt = {0.f, 0.f, 0.f, 0.f};
@@ -1137,7 +1152,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     if (a.dS0) {
 #pragma unroll
         for (int m = 0; m < NMT; ++m)
-            *reinterpret_cast<f32x4 *>(a.dS0 + ((int64_t)u * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g) = dSacc[m];
+            *reinterpret_cast<f32x4 *>(a.dS0 + (su * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g) = dSacc[m];
     }
 }
 
@@ -1168,10 +1183,35 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     E *Xs = reinterpret_cast<E *>(smem + LY::oXs), *dLs = reinterpret_cast<E *>(smem + LY::oL);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    const int u = blockIdx.x / a.NC, r = blockIdx.x - u * a.NC;
-    const int b = u / a.H, h = u - b * a.H;
-    const int64_t tok0 = (int64_t)b * a.T, sqk = (int64_t)a.H * DK;
-    const int units = a.B * a.H, nval = min(kChunk, a.T - r * kChunk);
+    // chunk slot s = blockIdx.x -> sequence, head h and chunk r
+    const int64_t s = blockIdx.x;
+    int64_t tok0;
+    int len, h, r;
+    if (a.cu_seqlens) {
+        // slots of sequence n: [cb[n] H, cb[n + 1] H), head-major; the grid covers
+        // the workspace's slot count, an upper bound, so trailing workgroups idle
+        const int32_t *cb = a.chunk_base;
+        if (s >= (int64_t)cb[a.B] * a.H) return;
+        int lo = 0, hi = a.B - 1; // largest n with cb[n] H <= s
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)cb[mid] * a.H <= s) lo = mid; else hi = mid - 1;
+        }
+        const int n = lo, ncn = cb[n + 1] - cb[n];
+        const int64_t off = s - (int64_t)cb[n] * a.H;
+        h = (int)(off / ncn);
+        r = (int)(off - (int64_t)h * ncn);
+        tok0 = a.cu_seqlens[n];
+        len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+    } else {
+        const int u = (int)(s / a.NC), b = u / a.H;
+        r = (int)(s - (int64_t)u * a.NC);
+        h = u - b * a.H;
+        tok0 = (int64_t)b * a.T;
+        len = a.T;
+    }
+    const int64_t sqk = (int64_t)a.H * DK;
+    const int nval = min(kChunk, len - r * kChunk);
 
     Stager<E, DK> sg;
     sg.sqk = sqk;
@@ -1185,7 +1225,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     sg.gh = nullptr;
     sg.sb = SubstepBase{0, 0u, 1u};
     sg.H = a.H;
-    sg.len = a.T;
+    sg.len = len;
     sg.tid = tid;
     sg.has_v = false;
     sg.rbeta = TR::fromf(0.f);
@@ -1195,7 +1235,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     typename TR::V tv[2]; // T^T of the chunk, as the forward pass formed it
 #pragma unroll
     for (int p = 0; p < 2; ++p)
-        tv[p] = *reinterpret_cast<const typename TR::V *>(a.T_chunks + ((int64_t)u * a.NC + r) * kChunk * kChunk +
+        tv[p] = *reinterpret_cast<const typename TR::V *>(a.T_chunks + s * kChunk * kChunk +
                                                           8 * (p * kThreads + tid));
     // Partial sums over the value tiles (the chain kernel's accumulator
     // order): dP, dT (lower-inclusive, to LDS) and dQ, dK (this wave's token
@@ -1204,7 +1244,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     const size_t PB = bwd_part_floats(DK);
     const float *pbt[NT];
 #pragma unroll
-    for (int tau = 0; tau < NT; ++tau) pbt[tau] = a.part + (((int64_t)tau * units + u) * a.NC + r) * PB;
+    for (int tau = 0; tau < NT; ++tau) pbt[tau] = a.part + ((int64_t)tau * a.max_slots + s) * PB;
     auto ld4 = [&](int tau, int off) { return *reinterpret_cast<const f32x4 *>(pbt[tau] + off + lane * 4); };
     f32x4 pp[4], tt[4], dQa[NMT], dKa[NMT];
 #pragma unroll
@@ -1614,6 +1654,31 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     }
 }
 
+// One workgroup of 1024 threads: thread t sums the chunk counts of its block
+// of sequences, a workgroup scan turns the sums into offsets, and each thread
+// then writes the offsets of its block.
+__global__ __launch_bounds__(1024) void chunk_base_kernel(const int32_t *cu, int N, int32_t *cb) {
+    __shared__ int part[1024];
+    const int t = threadIdx.x, per = (N + 1023) / 1024;
+    const int b = min(N, t * per), e = min(N, b + per);
+    int sum = 0;
+    for (int n = b; n < e; ++n) sum += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    part[t] = sum;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) { // inclusive scan
+        const int x = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += x;
+        __syncthreads();
+    }
+    int base = t ? part[t - 1] : 0;
+    for (int n = b; n < e; ++n) {
+        cb[n] = base;
+        base += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    }
+    if (t == 1023) cb[N] = part[1023];
+}
+
 __global__ void fill_kernel(float *p, size_t n, float value) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = value;
@@ -1621,11 +1686,12 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 
 template <int DK, int DV> hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t s) {
     const int units = a.B * a.H;
-    if (units <= 0 || a.NC <= 0) return hipSuccess;
+    if (units <= 0 || (!a.cu_seqlens && a.NC <= 0)) return hipSuccess; // varlen: empty sequences still set dS0
     hipLaunchKernelGGL((bwd_chain_kernel<DK, DV>), dim3(units * a.n_tiles), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_finish_kernel<DK, DV>), dim3(units * a.NC), dim3(kThreads), 0, s, a);
+    if (a.max_slots <= 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_finish_kernel<DK, DV>), dim3((unsigned)a.max_slots), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1635,6 +1701,12 @@ hipError_t launch_chain(int dtype, int dk, int dv, bool write_o, const ChainArgs
                         hipStream_t stream) {
     if (dtype == 1) return launch_chain_bf16(dk, dv, write_o, a, stream);
     return write_o ? launch_dims_f32<true>(dk, dv, a, stream) : launch_dims_f32<false>(dk, dv, a, stream);
+}
+
+hipError_t launch_chunk_base(const int32_t *cu_seqlens, int N, int32_t *cb, hipStream_t stream) {
+    if (N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(chunk_base_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, N, cb);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill(float *p, size_t n, float value, hipStream_t stream) {

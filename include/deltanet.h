@@ -265,6 +265,25 @@ int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta,
 size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 
 /*
+ * deltanet_bwd over a packed batch of N sequences (layouts as in
+ * deltanet_fwd_varlen: tokens [total_T, H, *], cu_seqlens [N + 1] int32,
+ * optional seq_order [N]; S0, dS_final, dS0 [N, H, dv, dk]); the state and
+ * its gradient restart at each sequence. Workspace: at least
+ * deltanet_bwd_varlen_workspace_bytes(...) bytes, 16-byte aligned, which
+ * bounds the chunk count by total_T / 64 + N so the lengths need not be read
+ * on the host. Errors as in deltanet_bwd.
+ */
+int deltanet_bwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                        const float *S0, const void *dO, const float *dS_final, void *dq,
+                        void *dk, void *dv, void *dbeta, float *dS0, const int32_t *cu_seqlens,
+                        const int32_t *seq_order, int N, int total_T, int H, int dk_,
+                        int dv_, int chunk, int dtype, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Bytes of workspace deltanet_bwd_varlen needs (0 for invalid shapes). */
+size_t deltanet_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, int dv, int chunk);
+
+/*
  * Bytes of workspace deltanet_fwd (or deltanet_gated_fwd) needs for this
  * shape and cp_groups (0 means the library's choice on the current device).
  * Returns 0 when the resolved group count is 1, and also for invalid shapes.

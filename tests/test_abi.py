@@ -31,7 +31,8 @@ def test_library_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd",
                           "deltanet_gated_fwd_varlen", "deltanet_gdp_fwd", "deltanet_decode_step",
-                          "deltanet_kda_fwd", "deltanet_kda_decode_step", "deltanet_bwd",
+                          "deltanet_kda_fwd", "deltanet_kda_fwd_varlen", "deltanet_kda_decode_step",
+                          "deltanet_bwd", "deltanet_bwd_varlen", "deltanet_bwd_varlen_workspace_bytes",
                           "deltanet_workspace_bytes",
                           "deltanet_pick_cp_groups", "deltanet_status_string"}
     raw = ctypes.CDLL(dn.library_path())
@@ -180,6 +181,34 @@ def test_decode_step_rejects_bad_arguments(lib, kw, status):
                                   vp(a["S"]) if a["S"] else None, vp(a["o"]) if a["o"] else None,
                                   a["B"], a["H"], a["dk"], a["dv"], a["dtype"], None)
     assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), DN_ERR_INVALID),
+    (dict(N=0), DN_ERR_INVALID),
+    (dict(cu=FAKE + 2), DN_ERR_INVALID),
+    (dict(dtype=0), DN_ERR_UNSUPPORTED),
+    (dict(dk=96), DN_ERR_UNSUPPORTED),
+    (dict(ws_bytes=0), DN_ERR_WORKSPACE),
+])
+def test_bwd_varlen_rejects_bad_arguments(lib, kw, status):
+    a = dict(cu=FAKE, N=3, T=200, dk=128, dtype=1, ws_bytes=1 << 40)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    ptrs = [vp(FAKE)] * 12
+    st = lib.deltanet_bwd_varlen(*ptrs, vp(a["cu"]) if a["cu"] else None, None, a["N"], a["T"], 2, a["dk"], 128,
+                                 64, a["dtype"], vp(FAKE) if a["ws_bytes"] else None, a["ws_bytes"], None)
+    if kw.get("ws_bytes", 1) == 0 or status != DN_ERR_WORKSPACE:
+        assert st == status
+
+
+def test_bwd_varlen_workspace_bound(lib):
+    # chunk slots are bounded by total_T / 64 + N per head, whatever the lengths
+    one = lib.deltanet_bwd_varlen_workspace_bytes(1, 64, 1, 128, 128, 64)  # 2 slots + the offsets
+    slot = (one - 16) // 2
+    assert slot == lib.deltanet_bwd_workspace_bytes(1, 1, 64, 128, 128, 64)
+    assert lib.deltanet_bwd_varlen_workspace_bytes(3, 200, 2, 128, 128, 64) == (200 // 64 + 3) * 2 * slot + 16
+    assert lib.deltanet_bwd_varlen_workspace_bytes(0, 200, 2, 128, 128, 64) == 0
 
 
 @pytest.mark.parametrize("kw,status", [

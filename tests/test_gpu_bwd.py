@@ -4,8 +4,8 @@ The oracle (``oracle.deltanet_bwd``) applies the chain rule to the
 token-serial recurrence and is pinned by finite differences; the library runs
 three passes (forward chain keeping per-chunk states, reverse state-gradient
 chain, chunk-parallel finish). Cases: every (dk, dv), ragged lengths, chunk
-boundaries, initial state and final-state gradient present or absent, and the
-empty sequence. Metric: max|gpu - oracle| / max|oracle| per gradient tensor.
+boundaries, initial state and final-state gradient present or absent, the
+empty sequence, and packed sequences (varlen) against the oracle per sequence. Metric: max|gpu - oracle| / max|oracle| per gradient tensor.
 """
 
 import numpy as np
@@ -13,8 +13,8 @@ import pytest
 import torch
 
 import oracle
-from chunkwise_delta_rule_amd import deltanet_bwd
-from chunkwise_delta_rule_amd.synth import make_inputs
+from chunkwise_delta_rule_amd import deltanet_bwd, deltanet_bwd_varlen, longest_first_order
+from chunkwise_delta_rule_amd.synth import make_inputs, make_varlen_inputs
 from helpers import f64, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -64,3 +64,32 @@ def test_bwd_empty_sequence():
     out0 = deltanet_bwd(z, z, z, b, z, S0, None)
     torch.cuda.synchronize()
     assert torch.equal(out[4], dSf) and bool((out0[4] == 0).all())
+
+
+@pytest.mark.parametrize("order", ["given", "longest_first"])
+def test_bwd_varlen(order):
+    # packed sequences (the state and its gradient restart at each one): every
+    # sequence's gradients against the oracle's reverse mode over that sequence
+    lengths = [0, 1, 63, 64, 65, 200, 130, 7]
+    H, dk, dv = 2, 128, 128
+    print(f"[case] bwd varlen {lengths} order={order}", flush=True)
+    q, k, v, beta, cu, S0 = make_varlen_inputs(lengths, H, dk, dv, seed=430, s0_std=0.3)
+    g = torch.Generator().manual_seed(431)
+    dO = torch.randn(v.shape, generator=g).to(torch.bfloat16)
+    dSf = torch.randn((len(lengths), H, dv, dk), generator=g) * 0.1
+    d = [x.to(DEV) for x in (q, k, v, beta, dO)]
+    cud = cu.to(DEV)
+    so = longest_first_order(cud) if order == "longest_first" else None
+    out = deltanet_bwd_varlen(d[0], d[1], d[2], d[3], d[4], cud, S0.to(DEV), dSf.to(DEV), seq_order=so)
+    torch.cuda.synchronize()
+    got = [f64(x) for x in out]
+    worst = 0.0
+    for n, L in enumerate(lengths):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = [f64(x)[None, a:b] for x in (q, k, v, beta, dO)]
+        ref = oracle.deltanet_bwd(*sl[:4], sl[4], f64(S0)[n:n + 1], f64(dSf)[n:n + 1])
+        mine = [got[0][None, a:b], got[1][None, a:b], got[2][None, a:b], got[3][None, a:b], got[4][n:n + 1]]
+        errs = [rel_err(x, r) for x, r in zip(mine, ref)] if L > 0 else [rel_err(mine[4], ref[4])]
+        worst = max(worst, max(errs))
+        assert max(errs) <= TOL_BWD, (n, L, errs)
+    print(f"  worst err {worst:.3e}", flush=True)
