@@ -204,6 +204,34 @@ def kda_variant(dev, w, inputs, fwd_ms, steps=20, warmup=5):
             "hbm_frac": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4)}
 
 
+def kda_long_variant(dev, B=1, H=16, T=131072, d=128, steps=5, warmup=2):
+    """Time deltanet_kda_fwd on one long sequence per head (the long-context
+    shape), serial chain against context parallelism at the library's group
+    count; bytes as in kda_variant."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import make_channel_gates, make_inputs
+
+    print(f"[bench] kda long-context variant B={B} H={H} T={T}", file=sys.stderr, flush=True)
+    q, k, v, beta, S0 = make_inputs(B, H, T, d, d, seed=11, device=str(dev))
+    g = make_channel_gates((B, T, H, d), seed=11, device=str(dev))
+    o = torch.empty_like(v)
+    Sf = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    G = dn.deltanet_pick_cp_groups(B, H, T, d, d, 64)
+    ws = torch.empty(max(dn.deltanet_workspace_bytes(B, H, T, d, d, 64, G), 1), dtype=torch.uint8, device=dev)
+    out = {"call": "deltanet_kda_fwd", "config": {"B": B, "H": H, "T": T, "dk": d, "dv": d}, "steps": steps,
+           "warmup": warmup}
+    nbytes = B * T * H * (2 * (4 * d + 1) + 4 * d) + B * H * d * d * 4
+    for name, groups in (("serial", 1), ("context_parallel", G)):
+        ms, _, _ = time_steps(lambda: dn.deltanet_kda_fwd(q, k, v, beta, g, S0, o=o, S_final=Sf,
+                                                          cp_groups=groups, workspace=ws), warmup, steps)
+        out[name] = {"cp_groups": groups, "ms_per_step": round(ms, 4),
+                     "tokens_per_s": round(B * T / (ms / 1e3), 1),
+                     "hbm_frac": round(nbytes / (ms / 1e3) / PEAK_HBM_BPS, 4)}
+    out["speedup"] = round(out["serial"]["ms_per_step"] / out["context_parallel"]["ms_per_step"], 3)
+    return out
+
+
 def gdp_variant(dev, w, flops_per_head_step, peak_flops, nh=2, steps=20, warmup=5):
     """Time deltanet_gdp_fwd with nh substeps per token on the workload's B, H,
     T (real tokens) and widths: the chunkwise path runs over T nh virtual
@@ -421,6 +449,7 @@ def main():
         result.setdefault("variants", {})["bwd"] = bwd_variant(dev, w, inputs, avg_launch_ms)
         result["variants"]["gdp"] = gdp_variant(dev, w, flops / n_tokens / w.H, peak_flops)
         result["variants"]["kda"] = kda_variant(dev, w, inputs, avg_launch_ms)
+        result["variants"]["kda_long"] = kda_long_variant(dev)
     if not args.gated and not args.no_variants:
         result.setdefault("variants", {})["decode"] = decode_variant(dev)
     if not args.no_cpu_baseline:

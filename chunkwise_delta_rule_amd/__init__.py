@@ -72,7 +72,7 @@ def load_library(path: str | None = None):
     lib.deltanet_gated_fwd_varlen.restype = i
     lib.deltanet_gdp_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.deltanet_gdp_fwd.restype = i
-    lib.deltanet_kda_fwd.argtypes = [vp] * 8 + [i, i, i, i, i, i, i, vp]
+    lib.deltanet_kda_fwd.argtypes = [vp] * 8 + [i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.deltanet_kda_fwd.restype = i
     lib.deltanet_kda_fwd_varlen.argtypes = [vp] * 10 + [i, i, i, i, i, i, i, vp]
     lib.deltanet_kda_fwd_varlen.restype = i
@@ -533,12 +533,13 @@ def deltanet_bwd_varlen(q, k, v, beta, dO, cu_seqlens, S0=None, dS_final=None, *
     return dq, dkk, dvv, db, dS0
 
 
-def deltanet_kda_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64, o=None, S_final=None,
-                     output_final_state: bool = True, stream=None):
+def deltanet_kda_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64, cp_groups: int = 1, o=None,
+                     S_final=None, output_final_state: bool = True, workspace=None, stream=None):
     """Kimi Delta Attention forward (C-ABI ``deltanet_kda_fwd``, bf16 only).
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H]; g: [B,T,H,dk] float32
-    per-channel log decays; S0: [B,H,dv,dk] fp32 or None. Returns (o, S_final).
+    per-channel log decays; S0: [B,H,dv,dk] fp32 or None. ``cp_groups`` as in
+    ``deltanet_fwd`` (context parallelism). Returns (o, S_final).
     """
     lib = load_library()
     if k.dim() != 4:
@@ -562,9 +563,14 @@ def deltanet_kda_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64, o=None, S_fi
         S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     if S_final is not None:
         _check(S_final, "S_final", torch.float32, dev, (B, H, dv, dk))
+    need = int(lib.deltanet_workspace_bytes(B, H, T, dk, dv, chunk, cp_groups))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
         st = lib.deltanet_kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o),
-                                  _ptr(S_final), B, H, T, dk, dv, chunk, DN_BF16, _stream_handle(stream))
+                                  _ptr(S_final), B, H, T, dk, dv, chunk, DN_BF16, cp_groups, _ptr(workspace),
+                                  ws_bytes, _stream_handle(stream))
     if st != 0:
         raise DeltaNetError(st, "deltanet_kda_fwd")
     return o, S_final

@@ -390,12 +390,12 @@ int deltanet_gated_fwd_varlen(const void *q, const void *k, const void *v, const
 }
 
 int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
-                     void *o, float *S_final, int B, int H, int T, int dk, int dv, int chunk, int dtype,
-                     hipStream_t stream) {
+                     void *o, float *S_final, int B, int H, int T, int dk, int dv, int chunk, int dtype, int cp_groups,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
     int st = check_shape(dk, dv, chunk, dtype);
     if (st != DN_OK) return st;
     if (dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
-    if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
+    if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return DN_ERR_INVALID;
     if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
     if (T > 0) {
         if (!q || !k || !v || !beta || !g || !o) return DN_ERR_INVALID;
@@ -403,6 +403,10 @@ int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *be
             return DN_ERR_INVALID;
     }
     if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return DN_ERR_INVALID;
+    int G, cpg;
+    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    const size_t need = ws_bytes_for(B, H, dk, dv, G);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return DN_ERR_WORKSPACE;
     if (T == 0) { // no tokens: the final state is the initial one
         if (!S_final) return DN_OK;
         const size_t n = (size_t)B * H * dv * dk;
@@ -410,19 +414,49 @@ int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *be
                                 : dn::launch_fill(S_final, n, 0.f, stream);
         return e == hipSuccess ? DN_OK : DN_ERR_HIP;
     }
-    dn::KdaArgs a = {};
+    dn::ChainArgs a = {};
     a.q = q;
     a.k = k;
     a.v = v;
     a.beta = beta;
-    a.g = g;
-    a.S0 = S0;
+    a.gk = g;
     a.o = o;
+    a.S0 = S0;
     a.S_final = S_final;
     a.B = B;
     a.H = H;
     a.T = T;
-    return dn::launch_kda(dk, dv, a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+    a.nh = 1;
+    hipError_t err;
+    if (G <= 1) {
+        a.kind = dn::kDense;
+        a.n_units = B * H;
+        a.n_tiles = dv / dn::kRows;
+        err = dn::launch_kda(dk, dv, true, a, stream);
+        return err == hipSuccess ? DN_OK : DN_ERR_HIP;
+    }
+    // Context parallelism, as for deltanet_fwd: (i) each group's transition
+    // (P_g from the identity with no values, Q_g from a zero state), (ii) the
+    // prefix composition of the group maps, (iii) every group from its start.
+    float *ws = static_cast<float *>(workspace);
+    const size_t per = (size_t)B * H * G;
+    a.ws_P = ws;
+    a.ws_Q = a.ws_P + per * dk * dk;
+    a.ws_S = a.ws_Q + per * dv * dk;
+    a.G = G;
+    a.chunks_per_group = cpg;
+    a.kind = dn::kCpTransition;
+    a.n_units = B * H * (G - 1);
+    a.n_tiles = dv / dn::kRows + dk / dn::kRows;
+    err = dn::launch_kda(dk, dv, false, a, stream);
+    if (err != hipSuccess) return DN_ERR_HIP;
+    err = dn::launch_compose(dk, dv, a, stream);
+    if (err != hipSuccess) return DN_ERR_HIP;
+    a.kind = dn::kCpOutput;
+    a.n_units = B * H * G;
+    a.n_tiles = dv / dn::kRows;
+    err = dn::launch_kda(dk, dv, true, a, stream);
+    return err == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 
 int deltanet_kda_fwd_varlen(const void *q, const void *k, const void *v, const void *beta, const float *g,
@@ -441,21 +475,25 @@ int deltanet_kda_fwd_varlen(const void *q, const void *k, const void *v, const v
     }
     if (!aligned_to(cu_seqlens, 4) || (seq_order && !aligned_to(seq_order, 4))) return DN_ERR_INVALID;
     if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return DN_ERR_INVALID;
-    dn::KdaArgs a = {};
+    dn::ChainArgs a = {};
     a.q = q;
     a.k = k;
     a.v = v;
     a.beta = beta;
-    a.g = g;
-    a.S0 = S0;
+    a.gk = g;
     a.o = o;
+    a.S0 = S0;
     a.S_final = S_final;
     a.cu_seqlens = cu_seqlens;
     a.seq_order = seq_order;
+    a.kind = dn::kVarlen;
+    a.nh = 1;
     a.B = N;
     a.H = H;
     a.T = total_T;
-    return dn::launch_kda(dk, dv, a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+    a.n_units = N * H;
+    a.n_tiles = dv / dn::kRows;
+    return dn::launch_kda(dk, dv, true, a, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
 
 size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {

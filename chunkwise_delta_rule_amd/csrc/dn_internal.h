@@ -23,6 +23,7 @@ enum WorkKind : int {
 struct ChainArgs {
     const void *q, *k, *v, *beta;
     const float *g; // log decay per token, layout of beta; nullptr: no decay (DeltaNet)
+    const float *gk; // Kimi Delta Attention: per-channel log decays, layout of k (fp32)
     void *o;
     const float *S0;
     float *S_final;
@@ -62,18 +63,10 @@ struct DecodeArgs {
     int dv;
 };
 
-// Kimi Delta Attention forward (bf16): per-channel log decays g [B,T,H,dk] fp32.
-struct KdaArgs {
-    const void *q, *k, *v, *beta;
-    const float *g;
-    const float *S0;
-    void *o;
-    float *S_final;
-    const int32_t *cu_seqlens; // varlen: [B + 1] token offsets of B packed sequences, else nullptr
-    const int32_t *seq_order;  // varlen: processing order of the sequences, or nullptr
-    int B, H, T;               // varlen: B sequences, T the total token count
-};
-hipError_t launch_kda(int dk, int dv, const KdaArgs &a, hipStream_t stream);
+// Kimi Delta Attention chain (bf16, per-channel log decays a.gk): the work
+// kinds of the chain kernels (dense, varlen, context-parallel transitions and
+// outputs), grid = n_units * n_tiles workgroups of kThreads threads.
+hipError_t launch_kda(int dk, int dv, bool write_o, const ChainArgs &a, hipStream_t stream);
 
 // Backward pass (bf16): gradients of q, k, v, beta and S0 for upstream dO and
 // dS_final, from the per-chunk states S_chunks of a forward pass.

@@ -1430,8 +1430,8 @@ template <int DK> struct KdaLds {
     static constexpr size_t oT = oA + L::szA, oN = oT + L::szT, oP = oN + L::szN, total = oP + L::szT;
 };
 
-template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
+template <int DK, int DV, bool WO>
+__global__ __launch_bounds__(kThreads) void kda_chain_kernel(const ChainArgs a) {
     using E = __bf16;
     using TR = Tr<E>;
     using F = typename TR::F;
@@ -1450,53 +1450,20 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     E *Ps = reinterpret_cast<E *>(smem + LY::oP);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    const int ntile = DV / 64;
-    int u, tau;
-    map_block(blockIdx.x, a.B * a.H, ntile, u, tau); // the tiles of a unit share an XCD
-    const int rank = u / a.H, h = u - rank * a.H, row0 = 64 * tau;
-    // dense: sequence rank, T tokens each; varlen: sequence seq_order[rank] of the packed batch
-    int64_t tok0, su;
-    int len;
-    if (a.cu_seqlens) {
-        const int n = a.seq_order ? a.seq_order[rank] : rank;
-        tok0 = a.cu_seqlens[n];
-        len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
-        su = (int64_t)n * a.H + h;
-    } else {
-        tok0 = (int64_t)rank * a.T;
-        len = a.T;
-        su = u;
-    }
-    const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
+    // the work item: a token range of one (sequence, head), 64 state rows,
+    // where they start and end (dense, packed, or a group of a split sequence)
+    const Work wk = decode_work<DK, DV>(a);
+    const int h = wk.h, row0 = wk.row0, len = wk.len;
+    const int64_t tok0 = wk.tok0, sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
     const int NC = (len + kChunk - 1) / kChunk;
-
-    Stager<E, DK> sg;
-    sg.sqk = sqk;
-    sg.sv = sv;
-    sg.kg = reinterpret_cast<const E *>(a.k) + tok0 * sqk + (int64_t)h * DK;
-    sg.qg = reinterpret_cast<const E *>(a.q) + tok0 * sqk + (int64_t)h * DK;
-    sg.vg = reinterpret_cast<const E *>(a.v) + tok0 * sv + (int64_t)h * DV + row0;
-    sg.bg = reinterpret_cast<const E *>(a.beta) + tok0 * a.H + h;
-    sg.gg = nullptr;
-    sg.qh = nullptr;
-    sg.gh = nullptr;
-    sg.sb = SubstepBase{0, 0u, 1u};
-    sg.H = a.H;
-    sg.len = len;
-    sg.tid = tid;
-    sg.has_v = true;
-    sg.rbeta = TR::fromf(0.f);
-    sg.rg = 0.f;
-    sg.nval = 0;
-    const float *gg = a.g + tok0 * sqk + (int64_t)h * DK;
-    E *og = reinterpret_cast<E *>(a.o) + tok0 * sv + (int64_t)h * DV + row0;
+    Stager<E, DK> sg = make_stager<E, DK, DV, false>(a, wk, tid); // a.g is unused here: no scalar decay
+    const bool has_v = wk.has_v;
+    const float *gg = a.gk + tok0 * sqk + (int64_t)h * DK;
+    E *og = WO ? reinterpret_cast<E *>(a.o) + tok0 * sv + (int64_t)h * DV + row0 : nullptr;
 
     // state rows 16w + c16 of this tile: Sacc[m][i] = S[row0 + 16w + c16][16m + 4g + i]
     f32x4 Sacc[NMT];
-#pragma unroll
-    for (int m = 0; m < NMT; ++m)
-        Sacc[m] = a.S0 ? *reinterpret_cast<const f32x4 *>(a.S0 + (su * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    state_in<DK>(Sacc, wk, w, g, c16);
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     constexpr int NP = DK / 2; // channel pairs; the scaling pass has one thread per (pair, sub-chunk)
     static_assert(4 * NP <= kThreads, "one scaling item per thread");
@@ -1536,7 +1503,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
     for (int r = 0; r < NC; ++r) {
         const int nval = min(kChunk, len - r * kChunk);
         __syncthreads(); // the previous chunk's reads are done
-        if (r > 0) flush_o(r - 1);
+        if (WO && r > 0) flush_o(r - 1);
         sg.store_kqb(Ks, Qs, Bs, nullptr);
         sg.store_v(Vs);
         __syncthreads();
@@ -1619,7 +1586,7 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
                 kf[m] = TR::ldcol(Kf, L::K, 16 * j, 16 * m, g, c16);
                 ef[m] = *reinterpret_cast<const f32x4 *>(E16 + j * DK + 16 * m + 4 * g);
             }
-            const F vf = TR::ldcol(Vs, L::V, 16 * j, 16 * w, g, c16);
+            const F vf = has_v ? TR::ldcol(Vs, L::V, 16 * j, 16 * w, g, c16) : F{}; // no V: state transitions
             const F tf = TR::ldcol(TsT, L::T, 16 * j, 16 * j, g, c16);
             const F pf = ldrow(Ps, L::T, 16 * j + c16, 16 * j, g);
             sched_fence();
@@ -1642,16 +1609,11 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const KdaArgs a) {
             for (int m = 0; m < NMT; ++m) Sacc[m] = TR::mma16(Sacc[m] * ef[m], kf[m], zb);
         }
     }
-    if (NC > 0) {
+    if (WO && NC > 0) {
         __syncthreads();
         flush_o(NC - 1);
     }
-    if (a.S_final) {
-#pragma unroll
-        for (int m = 0; m < NMT; ++m)
-            *reinterpret_cast<f32x4 *>(a.S_final + (su * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g) =
-                Sacc[m];
-    }
+    state_out<DK>(Sacc, wk, w, g, c16);
 }
 
 // One workgroup of 1024 threads: thread t sums the chunk counts of its block
@@ -1716,18 +1678,21 @@ hipError_t launch_fill(float *p, size_t n, float value, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int DK, int DV> hipError_t launch_kda_dims(const KdaArgs &a, hipStream_t s) {
-    const int grid = a.B * a.H * (DV / 64);
-    if (grid <= 0 || (a.T <= 0 && !a.cu_seqlens)) return hipSuccess; // varlen: empty sequences still copy S0
-    hipLaunchKernelGGL((kda_chain_kernel<DK, DV>), dim3(grid), dim3(kThreads), 0, s, a);
+template <int DK, int DV> hipError_t launch_kda_dims(bool write_o, const ChainArgs &a, hipStream_t s) {
+    const int grid = a.n_units * a.n_tiles;
+    if (grid <= 0) return hipSuccess;
+    if (write_o)
+        hipLaunchKernelGGL((kda_chain_kernel<DK, DV, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((kda_chain_kernel<DK, DV, false>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_kda(int dk, int dv, const KdaArgs &a, hipStream_t stream) {
-    if (dk == 128 && dv == 128) return launch_kda_dims<128, 128>(a, stream);
-    if (dk == 128 && dv == 64) return launch_kda_dims<128, 64>(a, stream);
-    if (dk == 64 && dv == 128) return launch_kda_dims<64, 128>(a, stream);
-    if (dk == 64 && dv == 64) return launch_kda_dims<64, 64>(a, stream);
+hipError_t launch_kda(int dk, int dv, bool write_o, const ChainArgs &a, hipStream_t stream) {
+    if (dk == 128 && dv == 128) return launch_kda_dims<128, 128>(write_o, a, stream);
+    if (dk == 128 && dv == 64) return launch_kda_dims<128, 64>(write_o, a, stream);
+    if (dk == 64 && dv == 128) return launch_kda_dims<64, 128>(write_o, a, stream);
+    if (dk == 64 && dv == 64) return launch_kda_dims<64, 64>(write_o, a, stream);
     return hipErrorInvalidValue;
 }
 

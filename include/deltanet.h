@@ -207,12 +207,15 @@ int deltanet_decode_step(const void *q, const void *k, const void *v, const void
  * Evaluated with that section's complete per-chunk algorithm on sub-chunks of
  * 16 tokens (exact for any chunk size); the in-sub-chunk growth factor
  * exp(-sum of g over up to 16 tokens) must stay finite in fp32, which holds
- * for g >= -5.4. Other arguments as in deltanet_fwd (serial chain only, no
- * workspace).
+ * for g >= -5.4. Other arguments as in deltanet_fwd, including context
+ * parallelism (cp_groups, with deltanet_workspace_bytes of workspace): each
+ * group's transition is the same kernel run from the identity with no values,
+ * which the per-channel decay leaves a linear map of the entering state.
  */
 int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *beta,
                      const float *g, const float *S0, void *o, float *S_final, int B, int H,
-                     int T, int dk, int dv, int chunk, int dtype, hipStream_t stream);
+                     int T, int dk, int dv, int chunk, int dtype, int cp_groups, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 /*
  * deltanet_kda_fwd over a packed batch of N sequences (layouts as in

@@ -5,8 +5,9 @@ The oracle runs the KDA token recurrence of "Linear Attention, Visualized"
 by token; the library runs that section's per-chunk algorithm on 16-token
 sub-chunks. Cases: every (dk, dv), ragged lengths around chunk and sub-chunk
 boundaries, initial state, weak, strong and absent decay, decay equal
-across channels against the Gated DeltaNet kernel, and packed sequences
-(varlen) against the oracle per sequence. Bar: max|gpu - oracle| /
+across channels against the Gated DeltaNet kernel, packed sequences
+(varlen) against the oracle per sequence, and context parallelism (group
+transitions, composition, per-group outputs). Bar: max|gpu - oracle| /
 max|oracle| within 2e-2 (bf16 operands), for o and for the final state.
 """
 
@@ -90,3 +91,35 @@ def test_kda_varlen(order):
         worst = max(worst, eo, es)
         assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16], (n, L, eo, es)
     print(f"  worst err {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("G", [2, 5, 0])
+def test_kda_context_parallel(G):
+    # one long sequence per head split into G groups (0: the library's choice):
+    # transitions from the identity, composition, then every group from its start
+    B, H, T, dk, dv = 1, 2, 1000, 128, 128
+    print(f"[case] kda context parallel T={T} G={G}", flush=True)
+    q, k, v, beta, S0 = make_inputs(B, H, T, dk, dv, seed=340 + G, s0_std=0.3)
+    g = make_channel_gates((B, T, H, dk), seed=340 + G)
+    d = [x.to(DEV) for x in (q, k, v, beta, g)]
+    o, Sf = deltanet_kda_fwd(*d, S0.to(DEV), cp_groups=G)
+    os_, Ss = deltanet_kda_fwd(*d, S0.to(DEV), cp_groups=1)
+    torch.cuda.synchronize()
+    ro, rs = oracle.kda_fwd(f64(q), f64(k), f64(v), f64(beta), f64(g), f64(S0))
+    eo, es = rel_err(f64(o), ro), rel_err(f64(Sf), rs)
+    print(f"  err o={eo:.3e} S={es:.3e}; vs serial o={rel_err(f64(o), f64(os_)):.3e}", flush=True)
+    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+    assert rel_err(f64(o), f64(os_)) <= TOL[torch.bfloat16]
+
+
+def test_kda_context_parallel_shapes():
+    for dk, dv in [(64, 64), (64, 128), (128, 64)]:
+        q, k, v, beta, S0 = make_inputs(2, 1, 300, dk, dv, seed=350 + dk + dv, s0_std=0.3)
+        g = make_channel_gates((2, 300, 1, dk), seed=350 + dk + dv)
+        d = [x.to(DEV) for x in (q, k, v, beta, g)]
+        o, Sf = deltanet_kda_fwd(*d, S0.to(DEV), cp_groups=3)
+        torch.cuda.synchronize()
+        ro, rs = oracle.kda_fwd(f64(q), f64(k), f64(v), f64(beta), f64(g), f64(S0))
+        eo, es = rel_err(f64(o), ro), rel_err(f64(Sf), rs)
+        print(f"[case] kda cp dk={dk} dv={dv}: err o={eo:.3e} S={es:.3e}", flush=True)
+        assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
