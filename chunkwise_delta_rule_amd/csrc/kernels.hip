@@ -1121,6 +1121,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         float *pb = a.part + ((int64_t)tau * a.max_slots + slot0 + r) * bwd_part_floats(DK);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
+            if (s2 > w) break; // dP and dT are lower-inclusive: tiles right of the diagonal are zero
             f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
@@ -1248,9 +1249,9 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     auto ld4 = [&](int tau, int off) { return *reinterpret_cast<const f32x4 *>(pbt[tau] + off + lane * 4); };
     f32x4 pp[4], tt[4], dQa[NMT], dKa[NMT];
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-        pp[s2] = ld4(0, (w * 4 + s2) * 256);
-        tt[s2] = ld4(0, 4096 + (w * 4 + s2) * 256);
+    for (int s2 = 0; s2 < 4; ++s2) { // tiles right of the diagonal are neither stored nor loaded
+        pp[s2] = s2 <= w ? ld4(0, (w * 4 + s2) * 256) : f32x4{0.f, 0.f, 0.f, 0.f};
+        tt[s2] = s2 <= w ? ld4(0, 4096 + (w * 4 + s2) * 256) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int m = 0; m < NMT; ++m) {
@@ -1261,8 +1262,10 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     for (int tau = 1; tau < NT; ++tau) {
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-            pp[s2] += ld4(tau, (w * 4 + s2) * 256);
-            tt[s2] += ld4(tau, 4096 + (w * 4 + s2) * 256);
+            if (s2 <= w) {
+                pp[s2] += ld4(tau, (w * 4 + s2) * 256);
+                tt[s2] += ld4(tau, 4096 + (w * 4 + s2) * 256);
+            }
         }
 #pragma unroll
         for (int m = 0; m < NMT; ++m) {
