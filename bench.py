@@ -317,7 +317,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(sharding across GPUs is described in DESIGN.md, not implemented).", file=sys.stderr)
+              "(how the path would shard across GPUs is described in the design notes, not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import torch
