@@ -230,6 +230,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
         return DN_OK;
     }
     const size_t slots = varlen ? varlen_max_slots(B, T, H) : (size_t)B * H * NC;
+    if (slots > (size_t)INT32_MAX) return DN_ERR_UNSUPPORTED; // one finishing workgroup per chunk slot
     float *Sck = static_cast<float *>(workspace);
     float *part = Sck + slots * dv * dk;
     __bf16 *Tck = reinterpret_cast<__bf16 *>(part + slots * (dv / dn::kRows) * dn::bwd_part_floats(dk));

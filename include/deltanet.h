@@ -287,7 +287,8 @@ int deltanet_bwd_varlen(const void *q, const void *k, const void *v, const void 
 size_t deltanet_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, int dv, int chunk);
 
 /*
- * Bytes of workspace deltanet_fwd (or deltanet_gated_fwd) needs for this
+ * Bytes of workspace deltanet_fwd (or deltanet_gated_fwd, deltanet_gdp_fwd,
+ * deltanet_kda_fwd) needs for this
  * shape and cp_groups (0 means the library's choice on the current device).
  * Returns 0 when the resolved group count is 1, and also for invalid shapes.
  */
