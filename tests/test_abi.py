@@ -202,6 +202,22 @@ def test_bwd_varlen_rejects_bad_arguments(lib, kw, status):
         assert st == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(cp=-1), DN_ERR_INVALID),
+    (dict(cp=2), DN_ERR_WORKSPACE),        # context parallelism needs a workspace
+    (dict(g=None), DN_ERR_INVALID),
+    (dict(g=FAKE + 8), DN_ERR_INVALID),
+    (dict(dtype=0), DN_ERR_UNSUPPORTED),
+])
+def test_kda_fwd_rejects_bad_arguments(lib, kw, status):
+    a = dict(cp=1, g=FAKE, dtype=1)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    st = lib.deltanet_kda_fwd(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(a["g"]) if a["g"] else None, None,
+                              vp(FAKE), None, 1, 2, 4096, 128, 128, 64, a["dtype"], a["cp"], None, 0, None)
+    assert st == status
+
+
 def test_bwd_varlen_workspace_bound(lib):
     # chunk slots are bounded by total_T / 64 + N per head, whatever the lengths
     one = lib.deltanet_bwd_varlen_workspace_bytes(1, 64, 1, 128, 128, 64)  # 2 slots + the offsets

@@ -93,3 +93,24 @@ def test_bwd_varlen(order):
         worst = max(worst, max(errs))
         assert max(errs) <= TOL_BWD, (n, L, errs)
     print(f"  worst err {worst:.3e}", flush=True)
+
+
+def test_bwd_varlen_d64_no_state():
+    # dk = dv = 64, no initial state and no final-state gradient
+    lengths = [100, 1, 64]
+    H = 3
+    q, k, v, beta, cu, _ = make_varlen_inputs(lengths, H, 64, 64, seed=440)
+    g = torch.Generator().manual_seed(441)
+    dO = torch.randn(v.shape, generator=g).to(torch.bfloat16)
+    d = [x.to(DEV) for x in (q, k, v, beta, dO)]
+    out = deltanet_bwd_varlen(*d, cu.to(DEV))
+    torch.cuda.synchronize()
+    got = [f64(x) for x in out]
+    for n in range(len(lengths)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = [f64(x)[None, a:b] for x in (q, k, v, beta, dO)]
+        ref = oracle.deltanet_bwd(*sl[:4], sl[4], None, None)
+        mine = [got[0][None, a:b], got[1][None, a:b], got[2][None, a:b], got[3][None, a:b], got[4][n:n + 1]]
+        errs = [rel_err(x, r) for x, r in zip(mine, ref)]
+        print(f"[case] bwd varlen d64 seq {n}: " + " ".join(f"{e:.2e}" for e in errs), flush=True)
+        assert max(errs) <= TOL_BWD, (n, errs)

@@ -123,3 +123,19 @@ def test_kda_context_parallel_shapes():
         eo, es = rel_err(f64(o), ro), rel_err(f64(Sf), rs)
         print(f"[case] kda cp dk={dk} dv={dv}: err o={eo:.3e} S={es:.3e}", flush=True)
         assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+
+
+def test_kda_varlen_small_heads():
+    # dk = dv = 64, one head per sequence, a single very short and a long one
+    lengths = [3, 130, 64]
+    q, k, v, beta, cu, S0 = make_varlen_inputs(lengths, 1, 64, 64, seed=360, s0_std=0.3)
+    g = make_channel_gates((1, sum(lengths), 1, 64), seed=360)[0]
+    d = [x.to(DEV) for x in (q, k, v, beta, g)]
+    o, Sf = deltanet_kda_fwd_varlen(*d, cu.to(DEV), S0.to(DEV))
+    torch.cuda.synchronize()
+    for n in range(len(lengths)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        ro, rs = oracle.kda_fwd(*[f64(x)[None, a:b] for x in (q, k, v, beta, g)], f64(S0)[n:n + 1])
+        eo, es = rel_err(f64(o)[None, a:b], ro), rel_err(f64(Sf)[n:n + 1], rs)
+        print(f"[case] kda varlen d64 seq {n}: err o={eo:.3e} S={es:.3e}", flush=True)
+        assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
