@@ -109,6 +109,9 @@ def load(path: str = _LIB_PATH):
     lib.oracle_deltanet_bwd.argtypes = [dp] * 12 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                                     ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.oracle_deltanet_bwd.restype = ctypes.c_int
+    lib.oracle_gated_deltanet_bwd.argtypes = [dp] * 14 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                                          ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_gated_deltanet_bwd.restype = ctypes.c_int
     lib.oracle_kda_fwd.argtypes = [dp] * 8 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int]
     lib.oracle_kda_fwd.restype = ctypes.c_int
@@ -339,6 +342,33 @@ def deltanet_bwd(q, k, v, beta, dO, S0=None, dS_final=None, nthreads: int = 0, l
     if rc != 0:
         raise RuntimeError(f"oracle_deltanet_bwd failed with {rc}")
     return dq, dkk, dvv, db, dS0
+
+
+def gated_deltanet_bwd(q, k, v, beta, g, dO, S0=None, dS_final=None, nthreads: int = 0, lib=None):
+    """Token-serial fp64 backward of Gated DeltaNet (reverse mode of the gated recurrence).
+
+    Inputs as ``gated_deltanet_fwd`` (g [B,T,H]: log decays) plus the upstream
+    gradients dO [B,T,H,dv] and dS_final [B,H,dv,dk] (None: zero). Returns
+    (dq, dk, dv, dbeta, dg, dS0). The pages give no backward pass; this is the
+    chain rule on p3 "Gated DeltaNet (GDN)" (transposed state), written out in
+    ``deltanet_oracle.c``.
+    """
+    q, k, v, beta, g, dO = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g), _f64(dO)
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    assert g.shape == beta.shape
+    S0 = None if S0 is None else _f64(S0)
+    dS_final = None if dS_final is None else _f64(dS_final)
+    dq, dkk, dvv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    db, dg = np.empty_like(beta), np.empty_like(g)
+    dS0 = np.empty((B, H, dv, dk))
+    lib = lib or load()
+    rc = lib.oracle_gated_deltanet_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO),
+                                       _ptr(dS_final), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg),
+                                       _ptr(dS0), B, H, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gated_deltanet_bwd failed with {rc}")
+    return dq, dkk, dvv, db, dg, dS0
 
 
 def gdp_fwd(q, k, v, beta, g, n_h, S0=None):

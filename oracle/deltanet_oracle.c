@@ -429,6 +429,154 @@ int oracle_deltanet_bwd(const double *q, const double *k, const double *v, const
     return failed ? -2 : 0;
 }
 
+/*
+ * Reverse mode of the Gated DeltaNet recurrence ("Linear Attention,
+ * Visualized", "Gated DeltaNet (GDN)", transposed state), token by token:
+ *     P_t = a_t S_{t-1}   (a_t = exp(g_t)),   S_t = P_t + beta_t (v_t - P_t k_t) k_t^T,
+ *     o_t = S_t q_t.
+ * With G the gradient of S_t (after adding dO_t q_t^T), the step from P_t is
+ * the DeltaNet step, so its gradients follow with P_t in place of S_{t-1};
+ * the gradient of P_t is H = G - beta_t (G k_t) k_t^T, and then
+ *     dg_t = <H, P_t>  (= a_t <H, S_{t-1}>),   gradient of S_{t-1} = a_t H.
+ * The pages derive no backward pass; this is the chain rule on that
+ * recurrence. States are recomputed from checkpoints every kSeg tokens.
+ */
+static void unit_backward_decay(const double *q, const double *k, const double *v, const double *beta,
+                                const double *g, const double *dO, double *dq, double *dk, double *dv,
+                                double *dbeta, double *dg, ptrdiff_t qk_stride, ptrdiff_t vo_stride,
+                                ptrdiff_t beta_stride, int64_t L, int dk_, int dv_, double *S, double *G,
+                                double *seg, double *tmp)
+{
+    const size_t sz = (size_t)dv_ * dk_;
+    const int64_t nseg = (L + kSeg - 1) / kSeg;
+    double *ck = (double *)malloc(sizeof(double) * sz * (size_t)(nseg > 0 ? nseg : 1));
+    double *Pt = (double *)malloc(sizeof(double) * sz);
+    if (!ck || !Pt) {
+        free(ck);
+        free(Pt);
+        return;
+    }
+    for (int64_t s0 = 0; s0 < nseg; ++s0) { /* checkpoints */
+        memcpy(ck + (size_t)s0 * sz, S, sizeof(double) * sz);
+        const int64_t e0 = (s0 + 1) * kSeg < L ? (s0 + 1) * kSeg : L;
+        unit_forward(q + s0 * kSeg * qk_stride, k + s0 * kSeg * qk_stride, v + s0 * kSeg * vo_stride,
+                     beta + s0 * kSeg * beta_stride, g + s0 * kSeg * beta_stride, NULL, qk_stride, vo_stride,
+                     beta_stride, e0 - s0 * kSeg, dk_, dv_, S, tmp);
+    }
+    double *res = tmp, *gk = tmp + dv_, *scratch = tmp + 2 * dv_;
+    for (int64_t s0 = nseg - 1; s0 >= 0; --s0) {
+        const int64_t b0 = s0 * kSeg, e0 = (s0 + 1) * kSeg < L ? (s0 + 1) * kSeg : L;
+        memcpy(seg, ck + (size_t)s0 * sz, sizeof(double) * sz); /* seg[j]: state before token b0 + j */
+        for (int64_t t = b0; t < e0; ++t) {
+            double *nxt = seg + (size_t)(t - b0 + 1) * sz;
+            memcpy(nxt, seg + (size_t)(t - b0) * sz, sizeof(double) * sz);
+            unit_forward(q + t * qk_stride, k + t * qk_stride, v + t * vo_stride, beta + t * beta_stride,
+                         g + t * beta_stride, NULL, qk_stride, vo_stride, beta_stride, 1, dk_, dv_, nxt, scratch);
+        }
+        for (int64_t t = e0 - 1; t >= b0; --t) {
+            const double *Snew = seg + (size_t)(t - b0 + 1) * sz, *Sold = seg + (size_t)(t - b0) * sz;
+            const double *kv = k + t * qk_stride, *qv = q + t * qk_stride, *vv = v + t * vo_stride;
+            const double *ov = dO + t * vo_stride;
+            const double bb = beta[t * beta_stride], at = exp(g[t * beta_stride]);
+            for (size_t e = 0; e < sz; ++e) Pt[e] = at * Sold[e];
+            /* o_t = S_t q_t: dq_t = S_t^T dO_t and G += dO_t q_t^T */
+            for (int c = 0; c < dk_; ++c) {
+                double s = 0.0;
+                for (int r = 0; r < dv_; ++r) s += Snew[(size_t)r * dk_ + c] * ov[r];
+                dq[t * qk_stride + c] = s;
+            }
+            for (int r = 0; r < dv_; ++r)
+                for (int c = 0; c < dk_; ++c) G[(size_t)r * dk_ + c] += ov[r] * qv[c];
+            /* the write from P_t: res = v - P_t k, gk = G k */
+            for (int r = 0; r < dv_; ++r) {
+                double pk = 0.0, gkr = 0.0;
+                for (int c = 0; c < dk_; ++c) {
+                    pk += Pt[(size_t)r * dk_ + c] * kv[c];
+                    gkr += G[(size_t)r * dk_ + c] * kv[c];
+                }
+                res[r] = vv[r] - pk;
+                gk[r] = gkr;
+            }
+            double sb = 0.0;
+            for (int r = 0; r < dv_; ++r) {
+                sb += gk[r] * res[r];
+                dv[t * vo_stride + r] = bb * gk[r];
+            }
+            dbeta[t * beta_stride] = sb;
+            for (int c = 0; c < dk_; ++c) {
+                double x = 0.0, y = 0.0;
+                for (int r = 0; r < dv_; ++r) {
+                    x += G[(size_t)r * dk_ + c] * res[r];
+                    y += Pt[(size_t)r * dk_ + c] * gk[r];
+                }
+                dk[t * qk_stride + c] = bb * (x - y);
+            }
+            /* H = G - beta (G k) k^T is the gradient of P_t; dg_t = <H, P_t>; G <- a_t H */
+            double sg = 0.0;
+            for (int r = 0; r < dv_; ++r)
+                for (int c = 0; c < dk_; ++c) {
+                    const double hv = G[(size_t)r * dk_ + c] - bb * gk[r] * kv[c];
+                    sg += hv * Pt[(size_t)r * dk_ + c];
+                    G[(size_t)r * dk_ + c] = at * hv;
+                }
+            dg[t * beta_stride] = sg;
+        }
+    }
+    free(Pt);
+    free(ck);
+}
+
+/*
+ * Gated DeltaNet backward: as oracle_deltanet_bwd, with the log decays g
+ * [B,T,H] (layout of beta) as an input and their gradient dg [B,T,H] as an
+ * output.
+ */
+int oracle_gated_deltanet_bwd(const double *q, const double *k, const double *v, const double *beta,
+                              const double *g, const double *S0, const double *dO, const double *dS_final,
+                              double *dq, double *dk, double *dv, double *dbeta, double *dg, double *dS0, int B,
+                              int H, int64_t T, int dk_, int dv_, int nthreads)
+{
+    if (!q || !k || !v || !beta || !g || !dO || !dq || !dk || !dv || !dbeta || !dg || B <= 0 || H <= 0 ||
+        T < 0 || dk_ <= 0 || dv_ <= 0)
+        return -1;
+    const ptrdiff_t qs = (ptrdiff_t)H * dk_, vs = (ptrdiff_t)H * dv_;
+    const size_t sz = (size_t)dv_ * dk_;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (sz * (kSeg + 3) + 3 * (size_t)(dv_ + dk_)));
+        if (!w) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            double *S = w, *G = w + sz, *seg = w + 2 * sz, *tmp = seg + sz * (kSeg + 1);
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t unit = 0; unit < (int64_t)B * H; ++unit) {
+                const int64_t bi = unit / H, tok = bi * T;
+                const int hi = (int)(unit % H);
+                if (S0) memcpy(S, S0 + (size_t)unit * sz, sizeof(double) * sz);
+                else memset(S, 0, sizeof(double) * sz);
+                if (dS_final) memcpy(G, dS_final + (size_t)unit * sz, sizeof(double) * sz);
+                else memset(G, 0, sizeof(double) * sz);
+                unit_backward_decay(q + tok * qs + (ptrdiff_t)hi * dk_, k + tok * qs + (ptrdiff_t)hi * dk_,
+                                    v + tok * vs + (ptrdiff_t)hi * dv_, beta + tok * H + hi, g + tok * H + hi,
+                                    dO + tok * vs + (ptrdiff_t)hi * dv_, dq + tok * qs + (ptrdiff_t)hi * dk_,
+                                    dk + tok * qs + (ptrdiff_t)hi * dk_, dv + tok * vs + (ptrdiff_t)hi * dv_,
+                                    dbeta + tok * H + hi, dg + tok * H + hi, qs, vs, H, T, dk_, dv_, S, G, seg,
+                                    tmp);
+                if (dS0) memcpy(dS0 + (size_t)unit * sz, G, sizeof(double) * sz);
+            }
+            free(w);
+        }
+    }
+    return bad ? -2 : 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

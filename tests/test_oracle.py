@@ -510,6 +510,80 @@ def pin_bwd_state_gradient_closed_form(lib):
     return _rel(dS0[0, 0], ref) < 1e-12
 
 
+# ---- Gated backward (chain rule on the gated recurrence)
+
+def _gbwd_case(seed, B=1, T=70, H=2, dk=4, dv=3):
+    rng, args, dO, dSf = _bwd_case(seed, B=B, T=T, H=H, dk=dk, dv=dv)
+    g = _gates(rng, (B, T, H), lo=0.3)
+    q, k, v, beta, S0 = args
+    return rng, (q, k, v, beta, g, S0), dO, dSf
+
+
+def _gloss(lib, args, dO, dSf):
+    o, S = oracle.gated_deltanet_fwd(*args, lib=lib)
+    return float((o * dO).sum() + (S * dSf).sum())
+
+
+def pin_gated_bwd_finite_differences(lib):
+    # central differences of L = <dO, o> + <dS_final, S_T> for sampled entries of
+    # q, k, v, beta, g and S0; T = 70 crosses the 64-token checkpoint segment
+    rng, args, dO, dSf = _gbwd_case(90)
+    q, k, v, beta, g, S0 = args
+    dq, dk, dv, db, dg, dS0 = oracle.gated_deltanet_bwd(q, k, v, beta, g, dO, S0, dSf, lib=lib)
+    grads = (dq, dk, dv, db, dg, dS0)
+    ok = True
+    for ai in range(6):
+        a = args[ai]
+        for _ in range(10):
+            idx = tuple(int(rng.integers(0, n)) for n in a.shape)
+            h = 1e-5
+            ap = [x.copy() for x in args]
+            am = [x.copy() for x in args]
+            ap[ai][idx] += h
+            am[ai][idx] -= h
+            fd = (_gloss(lib, ap, dO, dSf) - _gloss(lib, am, dO, dSf)) / (2 * h)
+            ok &= abs(fd - grads[ai][idx]) <= 1e-6 * max(1.0, abs(fd))
+    return bool(ok)
+
+
+def pin_gated_bwd_no_decay_is_deltanet(lib):
+    # g = 0 means a_t = 1: every gradient but dg is the ungated one
+    rng, args, dO, dSf = _bwd_case(91, T=40)
+    q, k, v, beta, S0 = args
+    z = np.zeros(beta.shape)
+    gg = oracle.gated_deltanet_bwd(q, k, v, beta, z, dO, S0, dSf, lib=lib)
+    ug = oracle.deltanet_bwd(q, k, v, beta, dO, S0, dSf, lib=lib)
+    pairs = [(gg[0], ug[0]), (gg[1], ug[1]), (gg[2], ug[2]), (gg[3], ug[3]), (gg[5], ug[4])]
+    return all(_rel(x, y) < 1e-12 for x, y in pairs)
+
+
+def pin_gated_bwd_decay_closed_form(lib):
+    # with beta = 0 the state only decays, S_t = exp(G_t) S0 with G_t = g_1 + .. + g_t,
+    # so L = sum_t exp(G_t) <dO_t, S0 q_t> + exp(G_T) <dS_final, S0> and
+    # dL/dg_s = sum_{t >= s} exp(G_t) <dO_t, S0 q_t> + exp(G_T) <dS_final, S0>
+    rng, args, dO, dSf = _gbwd_case(92, T=12, H=1)
+    q, k, v, beta, g, S0 = args
+    beta = np.zeros_like(beta)
+    _, _, dv, _, dg, dS0 = oracle.gated_deltanet_bwd(q, k, v, beta, g, dO, S0, dSf, lib=lib)
+    Gc = np.cumsum(g[0, :, 0])
+    terms = np.array([np.exp(Gc[t]) * dO[0, t, 0] @ S0[0, 0] @ q[0, t, 0] for t in range(12)])
+    last = np.exp(Gc[-1]) * (dSf[0, 0] * S0[0, 0]).sum()
+    ref = np.cumsum(terms[::-1])[::-1] + last
+    # and dS0 = sum_t exp(G_t) dO_t q_t^T + exp(G_T) dS_final; dv = 0
+    ref_s = sum(np.exp(Gc[t]) * np.outer(dO[0, t, 0], q[0, t, 0]) for t in range(12)) + np.exp(Gc[-1]) * dSf[0, 0]
+    return _rel(dg[0, :, 0], ref) < 1e-12 and _rel(dS0[0, 0], ref_s) < 1e-12 and np.abs(dv).max() == 0
+
+
+def pin_gated_bwd_zero_upstream_and_empty(lib):
+    rng, args, dO, dSf = _gbwd_case(93, T=20)
+    q, k, v, beta, g, S0 = args
+    out = oracle.gated_deltanet_bwd(q, k, v, beta, g, np.zeros_like(dO), S0, None, lib=lib)
+    ok = all(np.abs(x).max() == 0 for x in out)
+    e = lambda x: x[:, :0]
+    o0 = oracle.gated_deltanet_bwd(e(q), e(k), e(v), e(beta), e(g), e(dO), S0, dSf, lib=lib)
+    return bool(ok and np.array_equal(o0[5], dSf))
+
+
 # ---- Kimi Delta Attention (p3 "Kimi Delta Attention (KDA)"): per-channel decay
 
 def _kda_case(seed, B=1, T=23, H=2, dk=6, dv=4):
@@ -604,7 +678,9 @@ PINS = [pin_golden_three_tokens, pin_golden_three_tokens_lambda, pin_golden_alic
         pin_gated_resume_and_varlen, pin_bwd_finite_differences, pin_bwd_linear_inputs_exact,
         pin_bwd_zero_upstream_and_empty, pin_bwd_state_gradient_closed_form,
         pin_kda_scalar_decay_is_gdn, pin_kda_beta_zero, pin_kda_single_token, pin_kda_one_hot_keys,
-        pin_kda_read_back, pin_kda_chunked_agreement]
+        pin_kda_read_back, pin_kda_chunked_agreement, pin_gated_bwd_finite_differences,
+        pin_gated_bwd_no_decay_is_deltanet, pin_gated_bwd_decay_closed_form,
+        pin_gated_bwd_zero_upstream_and_empty]
 
 
 def failed_pins(lib):
@@ -661,6 +737,15 @@ MUTANTS = {
     "bwd_state_gradient_sign": ("G[(size_t)i * dk_ + j] -= bt * du[i] * kt[j];",
                                 "G[(size_t)i * dk_ + j] += bt * du[i] * kt[j];"),
     "bwd_beta_gradient_scaled": ("dbeta[t * beta_stride] = db;", "dbeta[t * beta_stride] = bt * db;"),
+    "gbwd_dg_from_new_state": ("sg += hv * Pt[(size_t)r * dk_ + c];",
+                               "sg += hv * Snew[(size_t)r * dk_ + c];"),
+    "gbwd_dg_before_correction": ("sg += hv * Pt[(size_t)r * dk_ + c];",
+                                  "sg += G[(size_t)r * dk_ + c] * Pt[(size_t)r * dk_ + c];"),
+    "gbwd_gradient_not_decayed": ("G[(size_t)r * dk_ + c] = at * hv;", "G[(size_t)r * dk_ + c] = hv;"),
+    "gbwd_residual_of_undecayed_state": ("pk += Pt[(size_t)r * dk_ + c] * kv[c];",
+                                         "pk += Sold[(size_t)r * dk_ + c] * kv[c];"),
+    "gbwd_dk_of_undecayed_state": ("y += Pt[(size_t)r * dk_ + c] * gk[r];",
+                                   "y += Sold[(size_t)r * dk_ + c] * gk[r];"),
     "kda_decay_of_channel0": ("for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= exp(gt[j]);",
                               "for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= exp(gt[0]);"),
     "kda_decay_by_value_row": ("for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] *= exp(gt[j]);",
