@@ -26,7 +26,9 @@ import torch
 
 __all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
            "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_kda_fwd_varlen", "deltanet_decode_step", "deltanet_kda_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
-           "deltanet_bwd_varlen", "deltanet_bwd_varlen_workspace_bytes",
+           "deltanet_bwd_varlen", "deltanet_bwd_varlen_workspace_bytes", "deltanet_gated_bwd",
+           "deltanet_gated_bwd_workspace_bytes", "deltanet_gated_bwd_varlen",
+           "deltanet_gated_bwd_varlen_workspace_bytes",
            "deltanet_workspace_bytes",
            "deltanet_pick_cp_groups", "deltanet_status_string", "longest_first_order",
            "library_path", "load_library", "DeltaNetError", "DN_F32", "DN_BF16"]
@@ -84,6 +86,14 @@ def load_library(path: str | None = None):
     lib.deltanet_bwd_varlen.restype = i
     lib.deltanet_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.deltanet_bwd_varlen_workspace_bytes.restype = sz
+    lib.deltanet_gated_bwd.argtypes = [vp] * 14 + [i, i, i, i, i, i, i, vp, sz, vp]
+    lib.deltanet_gated_bwd.restype = i
+    lib.deltanet_gated_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.deltanet_gated_bwd_workspace_bytes.restype = sz
+    lib.deltanet_gated_bwd_varlen.argtypes = [vp] * 16 + [i, i, i, i, i, i, i, vp, sz, vp]
+    lib.deltanet_gated_bwd_varlen.restype = i
+    lib.deltanet_gated_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.deltanet_gated_bwd_varlen_workspace_bytes.restype = sz
     lib.deltanet_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.deltanet_decode_step.restype = i
     lib.deltanet_kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
@@ -531,6 +541,104 @@ def deltanet_bwd_varlen(q, k, v, beta, dO, cu_seqlens, S0=None, dS_final=None, *
     if st != 0:
         raise DeltaNetError(st, "deltanet_bwd_varlen")
     return dq, dkk, dvv, db, dS0
+
+
+def deltanet_gated_bwd_workspace_bytes(B, H, T, dk, dv, chunk=64) -> int:
+    return int(load_library().deltanet_gated_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def deltanet_gated_bwd_varlen_workspace_bytes(N, total_T, H, dk, dv, chunk=64) -> int:
+    return int(load_library().deltanet_gated_bwd_varlen_workspace_bytes(N, total_T, H, dk, dv, chunk))
+
+
+def deltanet_gated_bwd(q, k, v, beta, g, dO, S0=None, dS_final=None, *, chunk: int = 64, workspace=None,
+                       want_dS0: bool = True, stream=None):
+    """Backward of ``deltanet_gated_fwd`` (C-ABI ``deltanet_gated_bwd``, bf16 only).
+
+    q, k: [B,T,H,dk]; v, dO: [B,T,H,dv]; beta: [B,T,H] (bf16); g: [B,T,H]
+    fp32 log decays; S0, dS_final: [B,H,dv,dk] fp32 or None. Returns (dq, dk,
+    dv, dbeta, dg, dS0 or None).
+    """
+    lib = load_library()
+    if k.dim() != 4:
+        raise ValueError("k must be [B, T, H, dk]")
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    if dt != torch.bfloat16:
+        raise TypeError("deltanet_gated_bwd supports bfloat16 inputs only")
+    _check(q, "q", dt, dev, (B, T, H, dk))
+    _check(k, "k", dt, dev, (B, T, H, dk))
+    _check(v, "v", dt, dev, (B, T, H, dv))
+    _check(beta, "beta", dt, dev, (B, T, H))
+    _check(g, "g", torch.float32, dev, (B, T, H))
+    _check(dO, "dO", dt, dev, (B, T, H, dv))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if dS_final is not None:
+        _check(dS_final, "dS_final", torch.float32, dev, (B, H, dv, dk))
+    dq, dkk, dvv, db = (torch.empty_like(x) for x in (q, k, v, beta))
+    dg = torch.empty_like(g)
+    dS0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None
+    need = int(lib.deltanet_gated_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.deltanet_gated_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO),
+                                    _ptr(dS_final), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg), _ptr(dS0),
+                                    B, H, T, dk, dv, chunk, DN_BF16, _ptr(workspace), ws_bytes,
+                                    _stream_handle(stream))
+    if st != 0:
+        raise DeltaNetError(st, "deltanet_gated_bwd")
+    return dq, dkk, dvv, db, dg, dS0
+
+
+def deltanet_gated_bwd_varlen(q, k, v, beta, g, dO, cu_seqlens, S0=None, dS_final=None, *, seq_order=None,
+                              chunk: int = 64, workspace=None, want_dS0: bool = True, stream=None):
+    """Backward of ``deltanet_gated_fwd_varlen`` (C-ABI ``deltanet_gated_bwd_varlen``, bf16 only).
+
+    q, k: [T,H,dk]; v, dO: [T,H,dv]; beta: [T,H] (bf16); g: [T,H] fp32;
+    cu_seqlens: [N+1] int32; S0, dS_final: [N,H,dv,dk] fp32 or None. Returns
+    (dq, dk, dv, dbeta, dg, dS0 or None).
+    """
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError("k must be [T, H, dk]")
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    if dt != torch.bfloat16:
+        raise TypeError("deltanet_gated_bwd_varlen supports bfloat16 inputs only")
+    N = cu_seqlens.numel() - 1
+    _check(q, "q", dt, dev, (T, H, dk))
+    _check(k, "k", dt, dev, (T, H, dk))
+    _check(v, "v", dt, dev, (T, H, dv))
+    _check(beta, "beta", dt, dev, (T, H))
+    _check(g, "g", torch.float32, dev, (T, H))
+    _check(dO, "dO", dt, dev, (T, H, dv))
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev, (N + 1,))
+    if seq_order is not None:
+        _check(seq_order, "seq_order", torch.int32, dev, (N,))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev, (N, H, dv, dk))
+    if dS_final is not None:
+        _check(dS_final, "dS_final", torch.float32, dev, (N, H, dv, dk))
+    dq, dkk, dvv, db = (torch.empty_like(x) for x in (q, k, v, beta))
+    dg = torch.empty_like(g)
+    dS0 = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None
+    need = int(lib.deltanet_gated_bwd_varlen_workspace_bytes(N, T, H, dk, dv, chunk))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.deltanet_gated_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO),
+                                           _ptr(dS_final), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg),
+                                           _ptr(dS0), _ptr(cu_seqlens), _ptr(seq_order), N, T, H, dk, dv, chunk,
+                                           DN_BF16, _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if st != 0:
+        raise DeltaNetError(st, "deltanet_gated_bwd_varlen")
+    return dq, dkk, dvv, db, dg, dS0
 
 
 def deltanet_kda_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64, cp_groups: int = 1, o=None,

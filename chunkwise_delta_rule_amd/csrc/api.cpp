@@ -187,8 +187,8 @@ size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
 
 // Workspace bytes per chunk slot of the backward pass: the state entering the
 // chunk and the per-value-tile partial sums (fp32), then T^T of the chunk (bf16).
-size_t bwd_slot_bytes(int dk, int dv) {
-    return ((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_floats(dk)) * sizeof(float) +
+size_t bwd_slot_bytes(int dk, int dv, bool gated) {
+    return ((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_stride(dk, gated)) * sizeof(float) +
            (size_t)dn::kChunk * dn::kChunk * sizeof(__bf16);
 }
 
@@ -201,10 +201,10 @@ size_t varlen_max_slots(int N, int total_T, int H) {
 // The backward pass, dense (cu_seqlens NULL: B sequences of T tokens) or
 // packed (B = N sequences, T = total tokens). Workspace: [S entering each
 // chunk | partial sums | T^T of each chunk | chunk offsets (varlen)].
-int bwd_common(const void *q, const void *k, const void *v, const void *beta, const float *S0, const void *dO,
-               const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dS0,
-               const int32_t *cu_seqlens, const int32_t *seq_order, int B, int H, int T, int dk, int dv, int chunk,
-               int dtype, void *workspace, size_t workspace_bytes, size_t need, hipStream_t stream) {
+int bwd_common(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
+               const void *dO, const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dg,
+               float *dS0, const int32_t *cu_seqlens, const int32_t *seq_order, int B, int H, int T, int dk, int dv,
+               int chunk, int dtype, void *workspace, size_t workspace_bytes, size_t need, hipStream_t stream) {
     int st = check_shape(dk, dv, chunk, dtype);
     if (st != DN_OK) return st;
     if (dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
@@ -214,6 +214,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned_to(beta, 2) ||
             !aligned_to(dq, 2) || !aligned_to(dk_, 2) || !aligned_to(dv_, 2) || !aligned_to(dbeta, 2))
             return DN_ERR_INVALID;
+        if (g && (!dg || !aligned_to(g, 4) || !aligned_to(dg, 4))) return DN_ERR_INVALID;
     }
     if ((S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
         return DN_ERR_INVALID;
@@ -233,7 +234,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     if (slots > (size_t)INT32_MAX) return DN_ERR_UNSUPPORTED; // one finishing workgroup per chunk slot
     float *Sck = static_cast<float *>(workspace);
     float *part = Sck + slots * dv * dk;
-    __bf16 *Tck = reinterpret_cast<__bf16 *>(part + slots * (dv / dn::kRows) * dn::bwd_part_floats(dk));
+    __bf16 *Tck = reinterpret_cast<__bf16 *>(part + slots * (dv / dn::kRows) * dn::bwd_part_stride(dk, g != nullptr));
     int32_t *cb = varlen ? reinterpret_cast<int32_t *>(Tck + slots * dn::kChunk * dn::kChunk) : nullptr;
     if (varlen && dn::launch_chunk_base(cu_seqlens, B, cb, stream) != hipSuccess) return DN_ERR_HIP;
     // pass 1: the forward chain, keeping the state entering every chunk and its T
@@ -242,6 +243,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     a.k = k;
     a.v = v;
     a.beta = beta;
+    a.g = g;
     a.S0 = S0;
     a.S_chunks = Sck;
     a.T_chunks = Tck;
@@ -272,6 +274,8 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     b.dk = dk_;
     b.dv = dv_;
     b.dbeta = dbeta;
+    b.g = g;
+    b.dg = dg;
     b.cu_seqlens = cu_seqlens;
     b.seq_order = seq_order;
     b.chunk_base = cb;
@@ -500,12 +504,23 @@ int deltanet_kda_fwd_varlen(const void *q, const void *k, const void *v, const v
 size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
     if (B <= 0 || H <= 0 || T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
     const size_t slots = (size_t)B * H * ((T + dn::kChunk - 1) / dn::kChunk);
-    return bwd_slot_bytes(dk, dv) * slots;
+    return bwd_slot_bytes(dk, dv, false) * slots;
 }
 
 size_t deltanet_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, int dv, int chunk) {
     if (N <= 0 || H <= 0 || total_T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
-    return bwd_slot_bytes(dk, dv) * varlen_max_slots(N, total_T, H) + align16((size_t)(N + 1) * sizeof(int32_t));
+    return bwd_slot_bytes(dk, dv, false) * varlen_max_slots(N, total_T, H) + align16((size_t)(N + 1) * sizeof(int32_t));
+}
+
+size_t deltanet_gated_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+    if (B <= 0 || H <= 0 || T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
+    const size_t slots = (size_t)B * H * ((T + dn::kChunk - 1) / dn::kChunk);
+    return bwd_slot_bytes(dk, dv, true) * slots;
+}
+
+size_t deltanet_gated_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, int dv, int chunk) {
+    if (N <= 0 || H <= 0 || total_T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
+    return bwd_slot_bytes(dk, dv, true) * varlen_max_slots(N, total_T, H) + align16((size_t)(N + 1) * sizeof(int32_t));
 }
 
 int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, const float *S0, const void *dO,
@@ -513,8 +528,32 @@ int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, 
                  int dk, int dv, int chunk, int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
     const size_t need = deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk);
-    return bwd_common(q, k, v, beta, S0, dO, dS_final, dq, dk_, dv_, dbeta, dS0, nullptr, nullptr, B, H, T, dk, dv,
-                      chunk, dtype, workspace, workspace_bytes, need, stream);
+    return bwd_common(q, k, v, beta, nullptr, S0, dO, dS_final, dq, dk_, dv_, dbeta, nullptr, dS0, nullptr, nullptr, B,
+                      H, T, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+}
+
+int deltanet_gated_bwd(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
+                       const void *dO, const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dg,
+                       float *dS0, int B, int H, int T, int dk, int dv, int chunk, int dtype, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
+    if (T > 0 && (!g || !dg)) return DN_ERR_INVALID;
+    const size_t need = deltanet_gated_bwd_workspace_bytes(B, H, T, dk, dv, chunk);
+    return bwd_common(q, k, v, beta, g, S0, dO, dS_final, dq, dk_, dv_, dbeta, dg, dS0, nullptr, nullptr, B, H, T, dk,
+                      dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+}
+
+int deltanet_gated_bwd_varlen(const void *q, const void *k, const void *v, const void *beta, const float *g,
+                              const float *S0, const void *dO, const float *dS_final, void *dq, void *dk_, void *dv_,
+                              void *dbeta, float *dg, float *dS0, const int32_t *cu_seqlens, const int32_t *seq_order,
+                              int N, int total_T, int H, int dk, int dv, int chunk, int dtype, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    if (N <= 0 || H <= 0 || total_T < 0 || !cu_seqlens) return DN_ERR_INVALID;
+    if (total_T > 0 && (!g || !dg)) return DN_ERR_INVALID;
+    if (!aligned_to(cu_seqlens, 4) || (seq_order && !aligned_to(seq_order, 4))) return DN_ERR_INVALID;
+    const size_t need = deltanet_gated_bwd_varlen_workspace_bytes(N, total_T, H, dk, dv, chunk);
+    return bwd_common(q, k, v, beta, g, S0, dO, dS_final, dq, dk_, dv_, dbeta, dg, dS0, cu_seqlens, seq_order, N, H,
+                      total_T, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
 }
 
 int deltanet_bwd_varlen(const void *q, const void *k, const void *v, const void *beta, const float *S0,
@@ -524,8 +563,8 @@ int deltanet_bwd_varlen(const void *q, const void *k, const void *v, const void 
     if (N <= 0 || H <= 0 || total_T < 0 || !cu_seqlens) return DN_ERR_INVALID;
     if (!aligned_to(cu_seqlens, 4) || (seq_order && !aligned_to(seq_order, 4))) return DN_ERR_INVALID;
     const size_t need = deltanet_bwd_varlen_workspace_bytes(N, total_T, H, dk, dv, chunk);
-    return bwd_common(q, k, v, beta, S0, dO, dS_final, dq, dk_, dv_, dbeta, dS0, cu_seqlens, seq_order, N, H,
-                      total_T, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+    return bwd_common(q, k, v, beta, nullptr, S0, dO, dS_final, dq, dk_, dv_, dbeta, nullptr, dS0, cu_seqlens,
+                      seq_order, N, H, total_T, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
 }
 
 int deltanet_decode_step(const void *q, const void *k, const void *v, const void *beta, const float *g,

@@ -911,7 +911,7 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
             vs.template load_beta<S>(min(r + 5, last));
             if (r + 1 >= 0 && r + 1 < NC) {
                 off_solve<DK>(bf, r + 1, lane, g, c16);
-                if constexpr (!WO && !GATED) {
+                if constexpr (!WO) {
                     // for the backward pass: T^T of the chunk, row-major, from this
                     // wave's own LDS writes (its blocks are complete here)
                     if (wk.Tchunks) {

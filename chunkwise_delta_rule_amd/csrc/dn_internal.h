@@ -78,6 +78,8 @@ struct BwdArgs {
     float *part;           // [n_tiles][max_slots] blocks of per-tile partial sums
     float *dS0;            // [B*H][dv][dk] or nullptr
     void *dq, *dk, *dv, *dbeta;
+    const float *g; // Gated DeltaNet: log decays [tokens][H] (layout of beta), or nullptr
+    float *dg;      // their gradient (gated only)
     // varlen: B sequences packed along T (cu_seqlens [B + 1], optional order),
     // chunk slots as in ChainArgs::chunk_base; dense: slot of (unit u, chunk c) = u NC + c
     const int32_t *cu_seqlens, *seq_order, *chunk_base;
@@ -88,6 +90,9 @@ struct BwdArgs {
 hipError_t launch_chunk_base(const int32_t *cu_seqlens, int N, int32_t *cb, hipStream_t stream);
 // Floats of one partial block: dP, dT (64 x 64 each), dQ, dK (64 x dk each).
 constexpr size_t bwd_part_floats(int dk) { return 2 * 64 * 64 + 2 * 64 * (size_t)dk; }
+// Gated: per token k . (row-scaled Z dS') and k . (row-scaled dY S), and per
+// wave exp(gamma_C) <dS', S>, after those blocks (padded to 256 floats).
+constexpr size_t bwd_part_stride(int dk, bool gated) { return bwd_part_floats(dk) + (gated ? 256 : 0); }
 hipError_t launch_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream);
 // Fill n floats with value (a kernel, not a memset, so it can sit in a captured graph).
 hipError_t launch_fill(float *p, size_t n, float value, hipStream_t stream);

@@ -553,7 +553,8 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
             rg = st.j == 0 ? x : 0.f;
         }
     }
-    __device__ inline void store_kqb(E *Ks, E *Qs, float *Bs, float *Gs) const {
+    // Returns lane l's decay prefix sum (gated), else 0.
+    __device__ inline float store_kqb(E *Ks, E *Qs, float *Bs, float *Gs) const {
         const V zero = {};
 #pragma unroll
         for (int p = 0; p < NKQ; ++p) {
@@ -565,11 +566,14 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
         // the four waves write identical values: no branch needed
         const int l = tid & (kChunk - 1);
         Bs[l] = l < nval ? TR::tof(rbeta) : 0.f;
+        float gl = 0.f;
         if (gg) {
             // inclusive prefix sum over the chunk's tokens (lane l = token l), in
             // base-2 units; tokens past the end add nothing
-            Gs[l] = wave_inclusive_sum(l < nval ? rg * 1.44269504088896340736f : 0.f, l);
+            gl = wave_inclusive_sum(l < nval ? rg * 1.44269504088896340736f : 0.f, l);
+            if (Gs) Gs[l] = gl;
         }
+        return gl;
     }
     __device__ inline void store_v(E *Vs) const {
         if (!has_v) return;
@@ -888,22 +892,33 @@ template <bool WO> hipError_t launch_dims_f32(int dk, int dv, const ChainArgs &a
 // ---------------------------------------------------------------------------
 __device__ inline f32x4 widen_bf16(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
 
-template <int DK> struct BwdLds {
+template <int DK, bool GATED> struct BwdLds {
     using L = Ld<__bf16, DK>;
     static constexpr int LT = L::T; // stride of the 64-wide bf16 tiles
     static constexpr size_t oK = 0, oQ = oK + L::szK, oV = oQ + L::szK, oD = oV + L::szV, oB = oD + L::szV;
     static constexpr size_t oT = oB + 256, oP = oT + L::szT;
     static constexpr size_t oX = oP + L::szT; // Y, Z, dZ, dY tiles
-    static constexpr size_t oS = oX + 4 * L::szT, oR = oS + L::szK, total = oR + L::szK;
+    static constexpr size_t oS = oX + 4 * L::szT, oR = oS + L::szK;
+    // gated: decay prefix sums (the row-scaled dO tile replaces V once Y is formed)
+    static constexpr size_t oG = oR + L::szK;
+    static constexpr size_t total = GATED ? oG + 256 : oR + L::szK;
 };
 
-template <int DK, int DV>
+// A bf16 vector with every element times f.
+__device__ inline bf16x8 scale8(bf16x8 x, float f) {
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * f);
+    return y;
+}
+
+template <int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     using E = __bf16;
     using TR = Tr<E>;
     using F = typename TR::F;
     using L = Ld<E, DK>;
-    using LY = BwdLds<DK>;
+    using LY = BwdLds<DK, GATED>;
     constexpr int NMT = DK / 16, LT = LY::LT;
     static_assert(LY::total <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
@@ -913,6 +928,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     E *TsT = reinterpret_cast<E *>(smem + LY::oT), *Ps = reinterpret_cast<E *>(smem + LY::oP);
     E *Ys = reinterpret_cast<E *>(smem + LY::oX), *Zs = Ys + 64 * LT, *dZs = Zs + 64 * LT, *dYs = dZs + 64 * LT;
     E *Ss = reinterpret_cast<E *>(smem + LY::oS), *Rs = reinterpret_cast<E *>(smem + LY::oR);
+    // gated: prefix sums gamma (base 2), and diag(exp(gamma)) dO over V after Y;
+    // ungated: dO itself
+    float *Gs = GATED ? reinterpret_cast<float *>(smem + LY::oG) : nullptr;
+    E *Dgs = GATED ? Vs : Ds;
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     int u, tau;
@@ -954,6 +973,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     sg.rbeta = TR::fromf(0.f);
     sg.rg = 0.f;
     sg.nval = 0;
+    if constexpr (GATED) { // decays (and so queries) addressed by absolute token
+        sg.gg = a.g;
+        sg.gh = a.g + h;
+        sg.qh = reinterpret_cast<const E *>(a.q) + (int64_t)h * DK;
+        sg.sb = SubstepBase{tok0, 0u, 1u};
+    }
     const E *dOg = reinterpret_cast<const E *>(a.dO) + tok0 * sv + (int64_t)h * DV + row0;
     E *dVg = reinterpret_cast<E *>(a.dv) + tok0 * sv + (int64_t)h * DV + row0;
 
@@ -991,8 +1016,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     for (int r = NC - 1; r >= 0; --r) {
         const int nval = min(kChunk, len - r * kChunk);
         __syncthreads(); // the previous chunk's reads of the staging buffers are done
-        sg.store_kqb(Ks, Qs, Bs, nullptr);
+        const float gl = sg.store_kqb(Ks, Qs, Bs, Gs); // gated: gamma of token `lane`
         sg.store_v(Vs);
+        // gated: gamma_C (the chunk's last prefix sum; tokens past the end add nothing)
+        const float gC = GATED ? __shfl(gl, 63) : 0.f, eC = GATED ? __builtin_amdgcn_exp2f(gC) : 1.f;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
@@ -1002,12 +1029,16 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         // This wave's 16 value rows (column c16 of the accumulators).
         F SBn[NMT], dSB[NMT], YB[4], dZB[4], dYBn[4];
         f32x4 acc[4];
+        float sdot = 0.f; // gated: this lane's share of <dS', S>
 #pragma unroll
         for (int m = 0; m < NMT; ++m) {
             stf(Ss + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(Sacc[m]));
             stf(Rs + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(dSacc[m])); // dS after the chunk
             SBn[m] = TR::cvt(-Sacc[m]);
             dSB[m] = TR::cvt(dSacc[m]);
+            if constexpr (GATED)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sdot += dSacc[m][i] * Sacc[m][i];
         }
         __syncthreads();
         if (r > 0) load_chunk(r - 1);
@@ -1038,23 +1069,51 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
                 for (int kb = 0; kb < NKB; ++kb) acc = TR::mma32(acc, kf[kb][0], kf[kb][1], qf[kb][0], qf[kb][1]);
                 // acc[e] = k_{16cb + 4g + e} . q_{16ab + c16}
                 const int row = 16 * ab + c16, col = 16 * cb + 4 * g;
+                if constexpr (GATED) { // times exp(gamma_row - gamma_col)
+                    const float gr = Gs[row];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = (col + e > row) ? 0.f : acc[e];
+                    for (int e = 0; e < 4; ++e)
+                        acc[e] = (col + e > row) ? 0.f : acc[e] * __builtin_amdgcn_exp2f(gr - Gs[col + e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = (col + e > row) ? 0.f : acc[e];
+                }
                 stf(Ps + row * L::T + col, TR::cvt(acc));
             }
         }
         __syncthreads();
-        // Y = V - K S^T
+        // Y = V - K S^T (gated: V - diag(exp(gamma)) K S^T). eg[t][i] = exp(gamma)
+        // and ez[t][i] = exp(gamma_C - gamma) of token 16t + 4g + i (gated).
+        f32x4 eg[4], ez[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            acc[t] = widen_bf16(TR::ldcol(Vs, L::V, 16 * t, 16 * w, g, c16));
+            if constexpr (GATED) {
+                const f32x4 gq = *reinterpret_cast<const f32x4 *>(Gs + 16 * t + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    eg[t][i] = __builtin_amdgcn_exp2f(gq[i]);
+                    ez[t][i] = __builtin_amdgcn_exp2f(gC - gq[i]);
+                }
+            }
+            acc[t] = GATED ? f32x4{0.f, 0.f, 0.f, 0.f} : widen_bf16(TR::ldcol(Vs, L::V, 16 * t, 16 * w, g, c16));
 #pragma unroll
             for (int kb = 0; kb < NMT / 2; ++kb)
                 acc[t] = TR::mma32(acc[t], ldrow(Ks, L::K, 16 * t + c16, 32 * kb, g),
                                    ldrow(Ks, L::K, 16 * t + c16, 32 * kb + 16, g), SBn[2 * kb], SBn[2 * kb + 1]);
+            if constexpr (GATED) acc[t] = widen_bf16(TR::ldcol(Vs, L::V, 16 * t, 16 * w, g, c16)) + eg[t] * acc[t];
             YB[t] = TR::cvt(acc[t]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) Ys[(16 * t + 4 * g + i) * LT + 16 * w + c16] = YB[t][i];
+        }
+        if constexpr (GATED) {
+            // diag(exp(gamma)) dO into this wave's value columns of V, which only
+            // this wave's Y products above read (token `lane`)
+            const float f = __builtin_amdgcn_exp2f(gl);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(Ds + lane * L::V + 16 * w + 8 * h2);
+                *reinterpret_cast<bf16x8 *>(Vs + lane * L::V + 16 * w + 8 * h2) = scale8(x, f);
+            }
         }
         // Z = T Y
 #pragma unroll
@@ -1080,7 +1139,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
             for (int m = 0; m < NMT; m += 2)
                 zk = TR::mma32(zk, ldrow(Ks, L::K, 16 * t + c16, 16 * m, g), ldrow(Ks, L::K, 16 * t + c16, 16 * m + 16, g),
                                dSB[m], dSB[m + 1]);
-            const f32x4 z = zp + zk;
+            const f32x4 z = GATED ? zp + ez[t] * zk : zp + zk; // gated: K rows scaled by exp(gamma_C - gamma)
             dZB[t] = TR::cvt(z);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dZs[(16 * t + 4 * g + i) * LT + 16 * w + c16] = dZB[t][i];
@@ -1091,34 +1150,40 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s2 = t; s2 < 4; ++s2) z = TR::mma16(z, ldrow(TsT, L::T, 16 * t + c16, 16 * s2, g), dZB[s2]);
-            dYBn[t] = TR::cvt(-z);
             const F yb = TR::cvt(z);
+            // gated: the state-side uses of dY take the row factor exp(gamma)
+            const f32x4 zs = GATED ? eg[t] * z : z;
+            dYBn[t] = TR::cvt(-zs);
+            const F ysb = GATED ? TR::cvt(zs) : yb;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = 16 * t + 4 * g + i;
-                dYs[tok * LT + 16 * w + c16] = yb[i];
+                dYs[tok * LT + 16 * w + c16] = ysb[i];
                 if (tok < nval) dVg[((int64_t)r * kChunk + tok) * sv + 16 * w + c16] = yb[i];
             }
         }
-        // dS <- dS' + dO^T Q - dY^T K
+        // dS <- dS' + dO^T Q - dY^T K (gated: exp(gamma_C) dS' + (diag(exp(gamma)) dO)^T Q
+        // - (diag(exp(gamma)) dY)^T K)
 #pragma unroll
-        for (int m = 0; m < NMT; ++m)
+        for (int m = 0; m < NMT; ++m) {
+            if constexpr (GATED) dSacc[m] *= eC;
 #pragma unroll
             for (int s2 = 0; s2 < 4; s2 += 2) { // 16x16x32 products over token blocks s2, s2 + 1
                 dSacc[m] = TR::mma32(dSacc[m], TR::ldcol(Qs, L::K, 16 * s2, 16 * m, g, c16),
                                      TR::ldcol(Qs, L::K, 16 * s2 + 16, 16 * m, g, c16),
-                                     TR::ldcol(Ds, L::V, 16 * s2, 16 * w, g, c16),
-                                     TR::ldcol(Ds, L::V, 16 * s2 + 16, 16 * w, g, c16));
+                                     TR::ldcol(Dgs, L::V, 16 * s2, 16 * w, g, c16),
+                                     TR::ldcol(Dgs, L::V, 16 * s2 + 16, 16 * w, g, c16));
                 dSacc[m] = TR::mma32(dSacc[m], TR::ldcol(Ks, L::K, 16 * s2, 16 * m, g, c16),
                                      TR::ldcol(Ks, L::K, 16 * s2 + 16, 16 * m, g, c16), dYBn[s2], dYBn[s2 + 1]);
             }
+        }
         __syncthreads(); // Y, Z, dZ, dY tiles complete
 
         // Sums over this tile's 64 value rows, token rows 16w .. 16w + 15 per wave,
         // stored in accumulator order: one 16-byte piece per (wave, column
         // block, lane), so every store (and the finishing kernel's load) of a
         // wave moves 1 KB of contiguous memory.
-        float *pb = a.part + ((int64_t)tau * a.max_slots + slot0 + r) * bwd_part_floats(DK);
+        float *pb = a.part + ((int64_t)tau * a.max_slots + slot0 + r) * bwd_part_stride(DK, GATED);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
             if (s2 > w) break; // dP and dT are lower-inclusive: tiles right of the diagonal are zero
@@ -1133,21 +1198,56 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
             *reinterpret_cast<f32x4 *>(pb + ((w * 4 + s2) * 64 + lane) * 4) = dp;
             *reinterpret_cast<f32x4 *>(pb + 4096 + ((w * 4 + s2) * 64 + lane) * 4) = dt;
         }
+        // gated: k . a and k . b per token (a = the Z dS' rows scaled by
+        // exp(gamma_C - gamma), b = the dY S rows scaled by exp(gamma))
+        f32x4 ska = {0.f, 0.f, 0.f, 0.f}, skb = {0.f, 0.f, 0.f, 0.f};
+        f32x4 ezw = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (GATED) {
+            const f32x4 gq = *reinterpret_cast<const f32x4 *>(Gs + 16 * w + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ezw[i] = __builtin_amdgcn_exp2f(gC - gq[i]);
+        }
 #pragma unroll
         for (int m = 0; m < NMT; ++m) {
             f32x4 dq = {0.f, 0.f, 0.f, 0.f}, dk1 = {0.f, 0.f, 0.f, 0.f}, dk2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
                 const F s0 = TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16), s1 = TR::ldcol(Ss, L::K, 16 * kv + 16, 16 * m, g, c16);
-                dq = TR::mma32(dq, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), ldrow(Ds, L::V, 16 * w + c16, 16 * kv + 16, g),
+                dq = TR::mma32(dq, ldrow(Dgs, L::V, 16 * w + c16, 16 * kv, g), ldrow(Dgs, L::V, 16 * w + c16, 16 * kv + 16, g),
                                s0, s1);
                 dk1 = TR::mma32(dk1, ldrow(Zs, LT, 16 * w + c16, 16 * kv, g), ldrow(Zs, LT, 16 * w + c16, 16 * kv + 16, g),
                                 TR::ldcol(Rs, L::K, 16 * kv, 16 * m, g, c16), TR::ldcol(Rs, L::K, 16 * kv + 16, 16 * m, g, c16));
                 dk2 = TR::mma32(dk2, ldrow(dYs, LT, 16 * w + c16, 16 * kv, g), ldrow(dYs, LT, 16 * w + c16, 16 * kv + 16, g),
                                 s0, s1);
             }
+            if constexpr (GATED) {
+                dk1 *= ezw;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float kk = (float)Ks[(16 * w + 4 * g + i) * L::K + 16 * m + c16];
+                    ska[i] += kk * dk1[i];
+                    skb[i] += kk * dk2[i];
+                }
+            }
             *reinterpret_cast<f32x4 *>(pb + 8192 + ((w * NMT + m) * 64 + lane) * 4) = dq;
             *reinterpret_cast<f32x4 *>(pb + 8192 + 64 * DK + ((w * NMT + m) * 64 + lane) * 4) = dk1 - dk2;
+        }
+        if constexpr (GATED) {
+            float *px = pb + bwd_part_floats(DK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    ska[i] += __shfl_xor(ska[i], o, 16);
+                    skb[i] += __shfl_xor(skb[i], o, 16);
+                }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) sdot += __shfl_xor(sdot, o, 64);
+            if (c16 == 0) {
+                *reinterpret_cast<f32x4 *>(px + 16 * w + 4 * g) = ska;
+                *reinterpret_cast<f32x4 *>(px + 64 + 16 * w + 4 * g) = skb;
+            }
+            if (lane == 0) px[128 + w] = eC * sdot;
         }
     }
     if (a.dS0) {
@@ -1157,22 +1257,25 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     }
 }
 
-template <int DK> struct FinLds {
+template <int DK, bool GATED> struct FinLds {
     using L = Ld<__bf16, DK>;
     static constexpr int LT = L::T;
     static constexpr size_t szX = sizeof(__bf16) * 64 * LT;
     static constexpr size_t oK = 0, oQ = oK + L::szK, oB = oQ + L::szK, oBt = oB + 256, oDa = oBt + 256;
     static constexpr size_t oT = oDa + 256, oP = oT + L::szT;
-    static constexpr size_t oDT = oP + szX, oXs = oDT + szX, oL = oXs + szX, total = oL + szX;
+    static constexpr size_t oDT = oP + szX, oXs = oDT + szX, oL = oXs + szX;
+    // gated: the decay-weighted score gradients F (fp32, rows padded to 65) and q . dQ per token
+    static constexpr size_t oF = oL + szX, oQd = oF + sizeof(float) * 64 * 65;
+    static constexpr size_t total = GATED ? oQd + 256 : oL + szX;
 };
 
-template <int DK, int DV>
+template <int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     using E = __bf16;
     using TR = Tr<E>;
     using F = typename TR::F;
     using L = Ld<E, DK>;
-    using LY = FinLds<DK>;
+    using LY = FinLds<DK, GATED>;
     constexpr int NMT = DK / 16, LT = LY::LT;
     static_assert(LY::total <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
@@ -1182,6 +1285,8 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     E *TsT = reinterpret_cast<E *>(smem + LY::oT); // N^T once formed
     E *dPs = reinterpret_cast<E *>(smem + LY::oP), *dTs = reinterpret_cast<E *>(smem + LY::oDT);
     E *Xs = reinterpret_cast<E *>(smem + LY::oXs), *dLs = reinterpret_cast<E *>(smem + LY::oL);
+    float *Fs = GATED ? reinterpret_cast<float *>(smem + LY::oF) : nullptr;
+    float *Qd = GATED ? reinterpret_cast<float *>(smem + LY::oQd) : nullptr;
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     // chunk slot s = blockIdx.x -> sequence, head h and chunk r
@@ -1232,6 +1337,12 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     sg.rbeta = TR::fromf(0.f);
     sg.rg = 0.f;
     sg.nval = 0;
+    if constexpr (GATED) { // decays (and so queries) addressed by absolute token
+        sg.gg = a.g;
+        sg.gh = a.g + h;
+        sg.qh = reinterpret_cast<const E *>(a.q) + (int64_t)h * DK;
+        sg.sb = SubstepBase{tok0, 0u, 1u};
+    }
     sg.load(r);
     typename TR::V tv[2]; // T^T of the chunk, as the forward pass formed it
 #pragma unroll
@@ -1242,7 +1353,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     // order): dP, dT (lower-inclusive, to LDS) and dQ, dK (this wave's token
     // rows, in registers). Every load is issued before the first use.
     constexpr int NT = DV / 64;
-    const size_t PB = bwd_part_floats(DK);
+    const size_t PB = bwd_part_stride(DK, GATED);
     const float *pbt[NT];
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) pbt[tau] = a.part + ((int64_t)tau * a.max_slots + s) * PB;
@@ -1273,26 +1384,52 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
             dKa[m] += ld4(tau, 8192 + 64 * DK + (w * NMT + m) * 256);
         }
     }
+    // gated: per token k . a, k . b (summed over the value tiles, wave 0's lanes)
+    // and the tiles' exp(gamma_C) <dS', S> shares
+    float xa = 0.f, xb = 0.f, xs = 0.f;
+    if constexpr (GATED) {
+        if (w == 0) {
+#pragma unroll
+            for (int tau = 0; tau < NT; ++tau) {
+                const float *px = pbt[tau] + bwd_part_floats(DK);
+                xa += px[lane];
+                xb += px[64 + lane];
+                xs += lane < 4 ? px[128 + lane] : 0.f;
+            }
+        }
+    }
     E *TtS = Xs, *Ls = dLs; // T^T and L until N^T is formed (X and dL come later)
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
         *reinterpret_cast<typename TR::V *>(TtS + row * LT + 8 * cv) = tv[p];
     }
-    sg.store_kqb(Ks, Qs, Bs, nullptr);
+    const float gl = sg.store_kqb(Ks, Qs, Bs, nullptr); // gated: gamma (base 2) of token `lane`
+    // gated: decay factor exp(gamma_t - gamma_s) of entry (t, s) of this lane's
+    // tiles, t = 16w + 4g + i, s = 16j + c16 (s <= t; other entries unused)
+    float grow[4] = {0.f, 0.f, 0.f, 0.f}, gcol[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (GATED) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) grow[i] = __shfl(gl, 16 * w + 4 * g + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gcol[j] = __shfl(gl, 16 * j + c16);
+    }
+    auto decay = [&](int i, int j) { return GATED ? __builtin_amdgcn_exp2f(grow[i] - gcol[j]) : 1.f; };
     if (w == 0) Bt[lane] = lane < nval ? TR::tof(sg.rbeta) : 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * w + 4 * g + i, col = 16 * s2 + c16;
-            dPs[row * LT + col] = TR::fromf(col <= row ? pp[s2][i] : 0.f);
+            dPs[row * LT + col] = TR::fromf(col <= row ? pp[s2][i] * decay(i, s2) : 0.f);
             dTs[row * LT + col] = TR::fromf(col <= row ? tt[s2][i] : 0.f);
         }
     __syncthreads();
     // Gram rows of this wave, gm[j][i] = k_t . k_{16j + c16} (t = 16w + 4g + i),
     // and L = their strictly lower part
-    f32x4 gm[4];
+    // (gated: L takes the decay factors, and F starts as dP * (decayed Q K^T),
+    // lower-inclusive)
+    f32x4 gm[4], fp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         gm[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1300,10 +1437,24 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
         for (int kd = 0; kd < NMT; kd += 2)
             gm[j] = TR::mma32(gm[j], ldrow(Ks, L::K, 16 * w + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * w + c16, 16 * kd + 16, g),
                               ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd + 16, g));
+        if constexpr (GATED) {
+            f32x4 qk = {0.f, 0.f, 0.f, 0.f};
+            if (j <= w) {
+#pragma unroll
+                for (int kd = 0; kd < NMT; kd += 2)
+                    qk = TR::mma32(qk, ldrow(Qs, L::K, 16 * w + c16, 16 * kd, g), ldrow(Qs, L::K, 16 * w + c16, 16 * kd + 16, g),
+                                   ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd + 16, g));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
+                fp[j][i] = col <= t ? pp[j][i] * decay(i, j) * qk[i] : 0.f;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
-            Ls[t * LT + col] = TR::fromf(col < t ? gm[j][i] : 0.f);
+            Ls[t * LT + col] = TR::fromf(col < t ? gm[j][i] * decay(i, j) : 0.f);
         }
     }
     __syncthreads();
@@ -1356,10 +1507,26 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
-            const float dai = col < t ? -da[i] : 0.f;
-            dbb[i] += dai * gm[j][i];
+            const float dai = col < t ? -da[i] * decay(i, j) : 0.f; // gated: dA times the decay
+            const float m = dai * gm[j][i];
+            dbb[i] += m;
             dLs[t * LT + col] = TR::fromf(Bt[t] * dai);
+            if constexpr (GATED) Fs[t * 65 + col] = fp[j][i] + Bt[t] * m;
         }
+    }
+    if constexpr (GATED) { // q . dQ per token, dQ = diag(exp(gamma)) dO S so far
+        float qd[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qd[i] += (float)Qs[(16 * w + 4 * g + i) * L::K + 16 * m + c16] * dQa[m][i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) qd[i] += __shfl_xor(qd[i], o, 16);
+        if (c16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Qd[16 * w + 4 * g + i] = qd[i];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) // sum over the 16 lanes of the row group
@@ -1395,6 +1562,33 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
             }
             if (c16 == 0)
                 reinterpret_cast<E *>(a.dbeta)[(tok0 + (int64_t)r * kChunk + t) * a.H + h] = TR::fromf(dba[t] + dbb[i]);
+        }
+    }
+    if constexpr (GATED) {
+        // d gamma_t = (row t of F) - (column t of F) + q_t . dQ_t - k_t . (a_t + b_t),
+        // plus, on the chunk's last prefix sum, sum_t k_t . a_t + exp(gamma_C) <dS', S>
+        // (the two make <dS', S'>); dg_t sums d gamma over the chunk's tokens from t on.
+        if (w == 0) {
+            const int t = lane;
+            float rf = 0.f, cf = 0.f;
+            for (int j = 0; j < 64; ++j) {
+                rf += Fs[t * 65 + j];
+                cf += Fs[j * 65 + t];
+            }
+            float dgam = rf - cf + Qd[t] - xa - xb;
+            float sa = xa;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                sa += __shfl_xor(sa, o, 64);
+                xs += __shfl_xor(xs, o, 64);
+            }
+            if (t == 63) dgam += sa + xs;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) { // suffix sum over the lanes
+                const float y = __shfl_down(dgam, o, 64);
+                dgam += t + o < 64 ? y : 0.f;
+            }
+            if (t < nval) a.dg[(tok0 + (int64_t)r * kChunk + t) * a.H + h] = dgam;
         }
     }
 }
@@ -1652,11 +1846,17 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 template <int DK, int DV> hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t s) {
     const int units = a.B * a.H;
     if (units <= 0 || (!a.cu_seqlens && a.NC <= 0)) return hipSuccess; // varlen: empty sequences still set dS0
-    hipLaunchKernelGGL((bwd_chain_kernel<DK, DV>), dim3(units * a.n_tiles), dim3(kThreads), 0, s, a);
+    if (a.g)
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, true>), dim3(units * a.n_tiles), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, false>), dim3(units * a.n_tiles), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.max_slots <= 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_finish_kernel<DK, DV>), dim3((unsigned)a.max_slots), dim3(kThreads), 0, s, a);
+    if (a.g)
+        hipLaunchKernelGGL((bwd_finish_kernel<DK, DV, true>), dim3((unsigned)a.max_slots), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_finish_kernel<DK, DV, false>), dim3((unsigned)a.max_slots), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -287,6 +287,47 @@ int deltanet_bwd_varlen(const void *q, const void *k, const void *v, const void 
 size_t deltanet_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, int dv, int chunk);
 
 /*
+ * Backward pass of deltanet_gated_fwd (nh = 1, DN_BF16 only): the chain rule
+ * on "Linear Attention, Visualized", "Gated DeltaNet (GDN)" > "Complete
+ * per-chunk algorithm" (the pages give no backward pass), exact up to rounding.
+ * Arguments as deltanet_bwd, plus
+ *   g  : [B,T,H] fp32 log decays (the forward's), 4-byte aligned
+ *   dg : [B,T,H] fp32 output, their gradient
+ * Inside a chunk the decays enter through the row factors exp(gamma_t) and
+ * exp(gamma_C - gamma_t) and the pairwise factors exp(gamma_t - gamma_s)
+ * (gamma: in-chunk prefix sums of g), so g should be <= 0 (decay) as in the
+ * forward; dg is the in-chunk suffix sum of the gradients of those prefix
+ * sums. Workspace: at least deltanet_gated_bwd_workspace_bytes(...) bytes,
+ * 16-byte aligned. Errors as in deltanet_bwd; g or dg NULL with tokens
+ * present: DN_ERR_INVALID.
+ */
+int deltanet_gated_bwd(const void *q, const void *k, const void *v, const void *beta,
+                       const float *g, const float *S0, const void *dO, const float *dS_final,
+                       void *dq, void *dk, void *dv, void *dbeta, float *dg, float *dS0, int B,
+                       int H, int T, int dk_, int dv_, int chunk, int dtype, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace deltanet_gated_bwd needs (0 for invalid shapes). */
+size_t deltanet_gated_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+
+/*
+ * deltanet_gated_bwd over a packed batch (layouts as in deltanet_bwd_varlen;
+ * g, dg [total_T, H] fp32). Workspace: at least
+ * deltanet_gated_bwd_varlen_workspace_bytes(...) bytes, 16-byte aligned.
+ */
+int deltanet_gated_bwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                              const float *g, const float *S0, const void *dO,
+                              const float *dS_final, void *dq, void *dk, void *dv, void *dbeta,
+                              float *dg, float *dS0, const int32_t *cu_seqlens,
+                              const int32_t *seq_order, int N, int total_T, int H, int dk_,
+                              int dv_, int chunk, int dtype, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace deltanet_gated_bwd_varlen needs (0 for invalid shapes). */
+size_t deltanet_gated_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, int dv,
+                                                 int chunk);
+
+/*
  * Bytes of workspace deltanet_fwd (or deltanet_gated_fwd, deltanet_gdp_fwd,
  * deltanet_kda_fwd) needs for this
  * shape and cp_groups (0 means the library's choice on the current device).
