@@ -183,6 +183,30 @@ def bwd_variant(dev, w, inputs, fwd_ms, steps=10, warmup=3):
             "workspace_bytes": need, "hbm_frac_algorithmic": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4)}
 
 
+def gated_bwd_variant(dev, w, inputs, fwd_ms, steps=10, warmup=3):
+    """Time deltanet_gated_bwd on the workload with the gated variant's log
+    decays (synth.make_gates). Bytes: as bwd_variant plus g read and dg
+    written (fp32, one per head-token)."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import make_gates
+
+    print("[bench] gated backward variant", file=sys.stderr, flush=True)
+    q, k, v, beta, S0 = inputs
+    gl = make_gates((w.B, w.T, w.H), seed=7, device=str(dev))
+    g = torch.Generator(device=dev).manual_seed(9)
+    dO = torch.randn(v.shape, generator=g, device=dev, dtype=torch.float32).to(v.dtype)
+    need = dn.deltanet_gated_bwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ms, launch_ms, _ = time_steps(lambda: dn.deltanet_gated_bwd(q, k, v, beta, gl, dO, S0, workspace=ws),
+                                  warmup, steps)
+    nbytes = w.B * w.T * w.H * (2 * (2 * (2 * w.dk + 2 * w.dv + 1)) + 2 * 4)
+    return {"call": "deltanet_gated_bwd", "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1), "avg_launch_us": round(launch_ms * 1e3, 2),
+            "vs_forward_time": round(launch_ms / fwd_ms, 3), "algorithmic_bytes": nbytes,
+            "workspace_bytes": need, "hbm_frac_algorithmic": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4)}
+
+
 def kda_variant(dev, w, inputs, fwd_ms, steps=20, warmup=5):
     """Time deltanet_kda_fwd on the workload with per-channel log decays
     (synth.make_channel_gates). Bytes: q, k, v, beta, o plus g (fp32, dk per
@@ -447,6 +471,7 @@ def main():
             "vs_ungated_time": round(g_launch_ms / avg_launch_ms, 4)}}
     if not args.gated and not args.no_variants and not w.varlen and w.dtype == "bf16":
         result.setdefault("variants", {})["bwd"] = bwd_variant(dev, w, inputs, avg_launch_ms)
+        result["variants"]["gated_bwd"] = gated_bwd_variant(dev, w, inputs, avg_launch_ms)
         result["variants"]["gdp"] = gdp_variant(dev, w, flops / n_tokens / w.H, peak_flops)
         result["variants"]["kda"] = kda_variant(dev, w, inputs, avg_launch_ms)
         result["variants"]["kda_long"] = kda_long_variant(dev)

@@ -218,6 +218,39 @@ def test_kda_fwd_rejects_bad_arguments(lib, kw, status):
     assert st == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None), DN_ERR_INVALID),        # the decays are required when tokens are present
+    (dict(dg=None), DN_ERR_INVALID),       # and so is their gradient
+    (dict(g=FAKE + 2), DN_ERR_INVALID),    # fp32, 4-byte aligned
+    (dict(B=0), DN_ERR_INVALID),
+    (dict(dtype=0), DN_ERR_UNSUPPORTED),
+    (dict(dk=96), DN_ERR_UNSUPPORTED),
+    (dict(ws_bytes=0), DN_ERR_WORKSPACE),
+])
+def test_gated_bwd_rejects_bad_arguments(lib, kw, status):
+    a = dict(g=FAKE, dg=FAKE, B=2, dk=128, dtype=1, ws_bytes=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    opt = lambda x: vp(x) if x else None
+    st = lib.deltanet_gated_bwd(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), opt(a["g"]), None, vp(FAKE), None,
+                                vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), opt(a["dg"]), None, a["B"], 2, 200, a["dk"],
+                                128, 64, a["dtype"], None, a["ws_bytes"], None)
+    assert st == status
+
+
+def test_gated_bwd_workspace_sizes(lib):
+    # the gated partial blocks carry 256 more floats per value tile than the ungated ones
+    for dk, dv in [(128, 128), (64, 64), (64, 128), (128, 64)]:
+        slots = 2 * 3 * 4  # B = 2, H = 3, T = 200 -> 4 chunks
+        extra = slots * (dv // 64) * 256 * 4
+        assert (lib.deltanet_gated_bwd_workspace_bytes(2, 3, 200, dk, dv, 64)
+                == lib.deltanet_bwd_workspace_bytes(2, 3, 200, dk, dv, 64) + extra)
+        vslots = (200 // 64 + 3) * 2
+        assert (lib.deltanet_gated_bwd_varlen_workspace_bytes(3, 200, 2, dk, dv, 64)
+                == lib.deltanet_bwd_varlen_workspace_bytes(3, 200, 2, dk, dv, 64) + vslots * (dv // 64) * 256 * 4)
+    assert lib.deltanet_gated_bwd_workspace_bytes(2, 3, 200, 96, 128, 64) == 0
+
+
 def test_bwd_varlen_workspace_bound(lib):
     # chunk slots are bounded by total_T / 64 + N per head, whatever the lengths
     one = lib.deltanet_bwd_varlen_workspace_bytes(1, 64, 1, 128, 128, 64)  # 2 slots + the offsets
