@@ -194,6 +194,31 @@ def test_bwd_layer_b8_h16_t4096_sampled():
     assert eb <= 2e-2 and es <= 2e-2
 
 
+def test_gated_bwd_layer_b8_h16_t4096_sampled():
+    # the Gated DeltaNet backward at the benchmark's full shape, in the launch
+    # configuration bench.py times, sampled units against the oracle
+    w = WORKLOADS["layer_b8_h16_t4096"]
+    print(f"[case] {w.name} full size, gated backward", flush=True)
+    q, k, v, beta, S0 = workload_inputs(w, seed=3, device=DEV)
+    gl = make_gates((w.B, w.T, w.H), seed=7, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(9)
+    dO = torch.randn(v.shape, generator=g, device=DEV, dtype=torch.float32).to(v.dtype)
+    out = dn.deltanet_gated_bwd(q, k, v, beta, gl, dO, S0)
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(x).all()) for x in out)
+    units = [(0, 3), (7, 15)]
+    sel = lambda x, b, h: f64(x[b:b + 1, :, h:h + 1])
+    cat = lambda xs: np.concatenate(xs, axis=0)
+    ref = oracle.gated_deltanet_bwd(*(cat([sel(x, b, h) for b, h in units]) for x in (q, k, v, beta, gl, dO)))
+    for name, i in (("dq", 0), ("dk", 1), ("dv", 2), ("dbeta", 3), ("dg", 4)):
+        e = rel_err(np.stack([f64(out[i][b, :, h]) for b, h in units]), ref[i][:, :, 0])
+        print(f"  {name} err {e:.3e}", flush=True)
+        assert e <= 2e-2
+    es = rel_err(np.stack([f64(out[5][b, h]) for b, h in units]), ref[5][:, 0])
+    print(f"  dS0 err {es:.3e}", flush=True)
+    assert es <= 2e-2
+
+
 def test_kda_layer_b8_h16_t4096_sampled():
     # KDA at the benchmark's full shape, sampled units against the oracle
     w = WORKLOADS["layer_b8_h16_t4096"]
