@@ -561,7 +561,7 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
             const int vi = p * NT + tid, row = vi / KQV, cv = vi % KQV;
             const bool ok = row < nval;
             *reinterpret_cast<V *>(Ks + row * L::K + cv * TR::kVec) = ok ? rk[p] : zero;
-            *reinterpret_cast<V *>(Qs + row * L::K + cv * TR::kVec) = ok ? rq[p] : zero;
+            if (Qs) *reinterpret_cast<V *>(Qs + row * L::K + cv * TR::kVec) = ok ? rq[p] : zero;
         }
         // the four waves write identical values: no branch needed
         const int l = tid & (kChunk - 1);
@@ -574,6 +574,14 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
             if (Gs) Gs[l] = gl;
         }
         return gl;
+    }
+    __device__ inline void store_q(E *Qs) const {
+        const V zero = {};
+#pragma unroll
+        for (int p = 0; p < NKQ; ++p) {
+            const int vi = p * NT + tid, row = vi / KQV, cv = vi % KQV;
+            *reinterpret_cast<V *>(Qs + row * L::K + cv * TR::kVec) = row < nval ? rq[p] : zero;
+        }
     }
     __device__ inline void store_v(E *Vs) const {
         if (!has_v) return;
@@ -1261,9 +1269,12 @@ template <int DK, bool GATED> struct FinLds {
     using L = Ld<__bf16, DK>;
     static constexpr int LT = L::T;
     static constexpr size_t szX = sizeof(__bf16) * 64 * LT;
-    static constexpr size_t oK = 0, oQ = oK + L::szK, oB = oQ + L::szK, oBt = oB + 256, oDa = oBt + 256;
-    static constexpr size_t oT = oDa + 256, oP = oT + L::szT;
-    static constexpr size_t oDT = oP + szX, oXs = oDT + szX, oL = oXs + szX;
+    // Ungated, Q is staged only for the last products, over the T and X tiles
+    // (adjacent, both dead by then), so that two workgroups fit in a CU's LDS.
+    static constexpr size_t oK = 0, oQ = oK + L::szK, oB = (GATED ? oQ + L::szK : oQ), oBt = oB + 256, oDa = oBt + 256;
+    static constexpr size_t oT = oDa + 256, oXs = oT + L::szT;
+    static constexpr size_t oP = oXs + szX, oDT = oP + szX, oL = oDT + szX;
+    static_assert(GATED || L::szT + szX >= L::szK, "Q fits over the T and X tiles");
     // gated: the decay-weighted score gradients F (fp32, rows padded to 65) and q . dQ per token
     static constexpr size_t oF = oL + szX, oQd = oF + sizeof(float) * 64 * 65;
     static constexpr size_t total = GATED ? oQd + 256 : oL + szX;
@@ -1279,7 +1290,8 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     constexpr int NMT = DK / 16, LT = LY::LT;
     static_assert(LY::total <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
-    E *Ks = reinterpret_cast<E *>(smem + LY::oK), *Qs = reinterpret_cast<E *>(smem + LY::oQ);
+    E *Ks = reinterpret_cast<E *>(smem + LY::oK);
+    E *Qs = reinterpret_cast<E *>(smem + (GATED ? LY::oQ : LY::oT)); // ungated: staged late
     float *Bs = reinterpret_cast<float *>(smem + LY::oB), *Bt = reinterpret_cast<float *>(smem + LY::oBt);
     float *dba = reinterpret_cast<float *>(smem + LY::oDa);
     E *TsT = reinterpret_cast<E *>(smem + LY::oT); // N^T once formed
@@ -1404,7 +1416,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
         const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
         *reinterpret_cast<typename TR::V *>(TtS + row * LT + 8 * cv) = tv[p];
     }
-    const float gl = sg.store_kqb(Ks, Qs, Bs, nullptr); // gated: gamma (base 2) of token `lane`
+    const float gl = sg.store_kqb(Ks, GATED ? Qs : nullptr, Bs, nullptr); // gated: gamma (base 2) of token `lane`
     // gated: decay factor exp(gamma_t - gamma_s) of entry (t, s) of this lane's
     // tiles, t = 16w + 4g + i, s = 16j + c16 (s <= t; other entries unused)
     float grow[4] = {0.f, 0.f, 0.f, 0.f}, gcol[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1533,6 +1545,10 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) dbb[i] += __shfl_xor(dbb[i], o, 16);
     __syncthreads();
+    if constexpr (!GATED) { // N^T and X are no longer read: Q goes over them
+        sg.store_q(Qs);
+        __syncthreads();
+    }
     // dQ += dP K;  dK += dP^T Q + (dL + dL^T) K
 #pragma unroll
     for (int m = 0; m < NMT; ++m)
