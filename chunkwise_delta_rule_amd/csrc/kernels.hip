@@ -1269,15 +1269,15 @@ template <int DK, bool GATED> struct FinLds {
     using L = Ld<__bf16, DK>;
     static constexpr int LT = L::T;
     static constexpr size_t szX = sizeof(__bf16) * 64 * LT;
-    // Ungated, Q is staged only for the last products, over the T and X tiles
-    // (adjacent, both dead by then), so that two workgroups fit in a CU's LDS.
-    static constexpr size_t oK = 0, oQ = oK + L::szK, oB = (GATED ? oQ + L::szK : oQ), oBt = oB + 256, oDa = oBt + 256;
+    // Q is staged only for the last products, over the T and X tiles (adjacent,
+    // both dead by then), so that two workgroups fit in a CU's LDS.
+    static constexpr size_t oK = 0, oB = oK + L::szK, oBt = oB + 256, oDa = oBt + 256;
     static constexpr size_t oT = oDa + 256, oXs = oT + L::szT;
     static constexpr size_t oP = oXs + szX, oDT = oP + szX, oL = oDT + szX;
-    static_assert(GATED || L::szT + szX >= L::szK, "Q fits over the T and X tiles");
-    // gated: the decay-weighted score gradients F (fp32, rows padded to 65) and q . dQ per token
-    static constexpr size_t oF = oL + szX, oQd = oF + sizeof(float) * 64 * 65;
-    static constexpr size_t total = GATED ? oQd + 256 : oL + szX;
+    static_assert(L::szT + szX >= L::szK, "Q fits over the T and X tiles");
+    // gated: per token (row sum of F) + q . dQ, and per wave the column sums of F
+    static constexpr size_t oRq = oL + szX, oCs = oRq + 256;
+    static constexpr size_t total = GATED ? oCs + 4 * 256 : oL + szX;
 };
 
 template <int DK, int DV, bool GATED>
@@ -1291,14 +1291,14 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     static_assert(LY::total <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
     E *Ks = reinterpret_cast<E *>(smem + LY::oK);
-    E *Qs = reinterpret_cast<E *>(smem + (GATED ? LY::oQ : LY::oT)); // ungated: staged late
+    E *Qs = reinterpret_cast<E *>(smem + LY::oT); // staged late
     float *Bs = reinterpret_cast<float *>(smem + LY::oB), *Bt = reinterpret_cast<float *>(smem + LY::oBt);
     float *dba = reinterpret_cast<float *>(smem + LY::oDa);
     E *TsT = reinterpret_cast<E *>(smem + LY::oT); // N^T once formed
     E *dPs = reinterpret_cast<E *>(smem + LY::oP), *dTs = reinterpret_cast<E *>(smem + LY::oDT);
     E *Xs = reinterpret_cast<E *>(smem + LY::oXs), *dLs = reinterpret_cast<E *>(smem + LY::oL);
-    float *Fs = GATED ? reinterpret_cast<float *>(smem + LY::oF) : nullptr;
-    float *Qd = GATED ? reinterpret_cast<float *>(smem + LY::oQd) : nullptr;
+    float *Rq = GATED ? reinterpret_cast<float *>(smem + LY::oRq) : nullptr;
+    float *Cs = GATED ? reinterpret_cast<float *>(smem + LY::oCs) : nullptr;
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     // chunk slot s = blockIdx.x -> sequence, head h and chunk r
@@ -1416,7 +1416,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
         const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
         *reinterpret_cast<typename TR::V *>(TtS + row * LT + 8 * cv) = tv[p];
     }
-    const float gl = sg.store_kqb(Ks, GATED ? Qs : nullptr, Bs, nullptr); // gated: gamma (base 2) of token `lane`
+    const float gl = sg.store_kqb(Ks, nullptr, Bs, nullptr); // gated: gamma (base 2) of token `lane`
     // gated: decay factor exp(gamma_t - gamma_s) of entry (t, s) of this lane's
     // tiles, t = 16w + 4g + i, s = 16j + c16 (s <= t; other entries unused)
     float grow[4] = {0.f, 0.f, 0.f, 0.f}, gcol[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1438,10 +1438,11 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
         }
     __syncthreads();
     // Gram rows of this wave, gm[j][i] = k_t . k_{16j + c16} (t = 16w + 4g + i),
-    // and L = their strictly lower part
-    // (gated: L takes the decay factors, and F starts as dP * (decayed Q K^T),
-    // lower-inclusive)
-    f32x4 gm[4], fp[4];
+    // and L = their strictly lower part (gated: times the decay factors)
+    f32x4 gm[4];
+    // gated: this lane's shares of the row sums (rows t) and column sums
+    // (columns 16j + c16) of F = dP * P + dL * L, P and L with their decays
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         gm[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1449,20 +1450,6 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
         for (int kd = 0; kd < NMT; kd += 2)
             gm[j] = TR::mma32(gm[j], ldrow(Ks, L::K, 16 * w + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * w + c16, 16 * kd + 16, g),
                               ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd + 16, g));
-        if constexpr (GATED) {
-            f32x4 qk = {0.f, 0.f, 0.f, 0.f};
-            if (j <= w) {
-#pragma unroll
-                for (int kd = 0; kd < NMT; kd += 2)
-                    qk = TR::mma32(qk, ldrow(Qs, L::K, 16 * w + c16, 16 * kd, g), ldrow(Qs, L::K, 16 * w + c16, 16 * kd + 16, g),
-                                   ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd + 16, g));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
-                fp[j][i] = col <= t ? pp[j][i] * decay(i, j) * qk[i] : 0.f;
-            }
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
@@ -1523,31 +1510,57 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
             const float m = dai * gm[j][i];
             dbb[i] += m;
             dLs[t * LT + col] = TR::fromf(Bt[t] * dai);
-            if constexpr (GATED) Fs[t * 65 + col] = fp[j][i] + Bt[t] * m;
+            if constexpr (GATED) {
+                const float f = Bt[t] * m; // dL * L
+                rsum[i] += f;
+                csum[j] += f;
+            }
         }
-    }
-    if constexpr (GATED) { // q . dQ per token, dQ = diag(exp(gamma)) dO S so far
-        float qd[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < NMT; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qd[i] += (float)Qs[(16 * w + 4 * g + i) * L::K + 16 * m + c16] * dQa[m][i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) qd[i] += __shfl_xor(qd[i], o, 16);
-        if (c16 == 0)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Qd[16 * w + 4 * g + i] = qd[i];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) // sum over the 16 lanes of the row group
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) dbb[i] += __shfl_xor(dbb[i], o, 16);
     __syncthreads();
-    if constexpr (!GATED) { // N^T and X are no longer read: Q goes over them
-        sg.store_q(Qs);
-        __syncthreads();
+    sg.store_q(Qs); // N^T and X are no longer read: Q goes over them
+    __syncthreads();
+    if constexpr (GATED) {
+        // F's score part dP * (decayed Q K^T) for this wave's rows (dPs holds dP
+        // with the decays), then per token q . dQ (dQ = diag(exp(gamma)) dO S so far)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j > w) break;
+            f32x4 qk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kd = 0; kd < NMT; kd += 2)
+                qk = TR::mma32(qk, ldrow(Qs, L::K, 16 * w + c16, 16 * kd, g), ldrow(Qs, L::K, 16 * w + c16, 16 * kd + 16, g),
+                               ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd + 16, g));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
+                const float f = col <= t ? TR::tof(dPs[t * LT + col]) * qk[i] : 0.f;
+                rsum[i] += f;
+                csum[j] += f;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rsum[i] += TR::tof(Qs[(16 * w + 4 * g + i) * L::K + 16 * m + c16]) * dQa[m][i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) // over the 16 lanes of the row group
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) rsum[i] += __shfl_xor(rsum[i], o, 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) // over the four row groups
+#pragma unroll
+            for (int o = 16; o < 64; o <<= 1) csum[j] += __shfl_xor(csum[j], o, 64);
+        if (c16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Rq[16 * w + 4 * g + i] = rsum[i];
+        if (g == 0)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Cs[64 * w + 16 * j + c16] = csum[j];
     }
     // dQ += dP K;  dK += dP^T Q + (dL + dL^T) K
 #pragma unroll
@@ -1584,14 +1597,11 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
         // d gamma_t = (row t of F) - (column t of F) + q_t . dQ_t - k_t . (a_t + b_t),
         // plus, on the chunk's last prefix sum, sum_t k_t . a_t + exp(gamma_C) <dS', S>
         // (the two make <dS', S'>); dg_t sums d gamma over the chunk's tokens from t on.
+        __syncthreads(); // row and column sums complete
         if (w == 0) {
             const int t = lane;
-            float rf = 0.f, cf = 0.f;
-            for (int j = 0; j < 64; ++j) {
-                rf += Fs[t * 65 + j];
-                cf += Fs[j * 65 + t];
-            }
-            float dgam = rf - cf + Qd[t] - xa - xb;
+            const float cf = Cs[t] + Cs[64 + t] + Cs[128 + t] + Cs[192 + t];
+            float dgam = Rq[t] - cf - xa - xb;
             float sa = xa;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
