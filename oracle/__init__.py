@@ -371,6 +371,33 @@ def gated_deltanet_bwd(q, k, v, beta, g, dO, S0=None, dS_final=None, nthreads: i
     return dq, dkk, dvv, db, dg, dS0
 
 
+def gdp_bwd(q, k, v, beta, g, n_h, dO, S0=None, dS_final=None, lib=None):
+    """Gated Delta Product backward, fp64: the reverse mode of the gated
+    recurrence over the virtual sequence that p3 "GDP as GDN over a virtual
+    sequence" defines (n_h substeps per real token; the decay sits on the first
+    substep, the query and the output on the last).
+
+    Shapes as ``gdp_fwd`` plus dO [B,T,H,dv] and dS_final [B,H,dv,dk] (None:
+    zero). Returns (dq [B,T,H,dk], dk [B,T,n_h,H,dk], dv [B,T,n_h,H,dv],
+    dbeta [B,T,n_h,H], dg [B,T,H], dS0).
+    """
+    q, k, v, beta, g, dO = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(g), _f64(dO)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    TV = T * n_h
+    qv = np.zeros((B, T, n_h, H, dk))
+    qv[:, :, n_h - 1] = q
+    gv = np.zeros((B, T, n_h, H))
+    gv[:, :, 0] = g
+    dOv = np.zeros((B, T, n_h, H, dv))
+    dOv[:, :, n_h - 1] = dO
+    flat = lambda x: x.reshape((B, TV) + x.shape[3:])
+    dqv, dkv, dvv, dbv, dgv, dS0 = gated_deltanet_bwd(flat(qv), flat(k), flat(v), flat(beta), flat(gv), flat(dOv),
+                                                      S0, dS_final, lib=lib)
+    unflat = lambda x: x.reshape((B, T, n_h) + x.shape[2:])
+    return (unflat(dqv)[:, :, n_h - 1], unflat(dkv), unflat(dvv), unflat(dbv), unflat(dgv)[:, :, 0], dS0)
+
+
 def gdp_fwd(q, k, v, beta, g, n_h, S0=None):
     """Gated Delta Product forward, fp64, token by token (numpy; small cases).
 

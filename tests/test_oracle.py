@@ -584,6 +584,39 @@ def pin_gated_bwd_zero_upstream_and_empty(lib):
     return bool(ok and np.array_equal(o0[5], dSf))
 
 
+def pin_gdp_bwd_finite_differences(lib):
+    # the GDP backward (gated reverse mode over the virtual sequence) against
+    # central differences of the numpy token-by-token GDP forward, n_h = 3
+    rng = np.random.default_rng(95)
+    B, T, H, dk, dv, nh = 1, 9, 2, 4, 3, 3
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, nh, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, nh, H, dv))
+    beta = rng.uniform(0.1, 1.2, (B, T, nh, H))
+    g = _gates(rng, (B, T, H), lo=0.3)
+    S0 = rng.standard_normal((B, H, dv, dk)) * 0.5
+    dO = rng.standard_normal((B, T, H, dv))
+    dSf = rng.standard_normal((B, H, dv, dk))
+    args = [q, k, v, beta, g, S0]
+
+    def loss(a):
+        o, S = oracle.gdp_fwd(a[0], a[1], a[2], a[3], a[4], nh, a[5])
+        return float((o * dO).sum() + (S * dSf).sum())
+    grads = oracle.gdp_bwd(q, k, v, beta, g, nh, dO, S0, dSf, lib=lib)
+    ok = True
+    for ai in range(6):
+        for _ in range(8):
+            idx = tuple(int(rng.integers(0, n)) for n in args[ai].shape)
+            ap = [x.copy() for x in args]
+            am = [x.copy() for x in args]
+            ap[ai][idx] += 1e-5
+            am[ai][idx] -= 1e-5
+            fd = (loss(ap) - loss(am)) / 2e-5
+            ok &= abs(fd - grads[ai][idx]) <= 1e-6 * max(1.0, abs(fd))
+    return bool(ok)
+
+
 # ---- Kimi Delta Attention (p3 "Kimi Delta Attention (KDA)"): per-channel decay
 
 def _kda_case(seed, B=1, T=23, H=2, dk=6, dv=4):
@@ -680,7 +713,7 @@ PINS = [pin_golden_three_tokens, pin_golden_three_tokens_lambda, pin_golden_alic
         pin_kda_scalar_decay_is_gdn, pin_kda_beta_zero, pin_kda_single_token, pin_kda_one_hot_keys,
         pin_kda_read_back, pin_kda_chunked_agreement, pin_gated_bwd_finite_differences,
         pin_gated_bwd_no_decay_is_deltanet, pin_gated_bwd_decay_closed_form,
-        pin_gated_bwd_zero_upstream_and_empty]
+        pin_gated_bwd_zero_upstream_and_empty, pin_gdp_bwd_finite_differences]
 
 
 def failed_pins(lib):
