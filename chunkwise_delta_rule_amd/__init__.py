@@ -28,7 +28,7 @@ __all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltane
            "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_kda_fwd_varlen", "deltanet_decode_step", "deltanet_kda_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
            "deltanet_bwd_varlen", "deltanet_bwd_varlen_workspace_bytes", "deltanet_gated_bwd",
            "deltanet_gated_bwd_workspace_bytes", "deltanet_gated_bwd_varlen",
-           "deltanet_gated_bwd_varlen_workspace_bytes",
+           "deltanet_gated_bwd_varlen_workspace_bytes", "deltanet_gdp_bwd", "deltanet_gdp_bwd_workspace_bytes",
            "deltanet_workspace_bytes",
            "deltanet_pick_cp_groups", "deltanet_status_string", "longest_first_order",
            "library_path", "load_library", "DeltaNetError", "DN_F32", "DN_BF16"]
@@ -94,6 +94,10 @@ def load_library(path: str | None = None):
     lib.deltanet_gated_bwd_varlen.restype = i
     lib.deltanet_gated_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.deltanet_gated_bwd_varlen_workspace_bytes.restype = sz
+    lib.deltanet_gdp_bwd.argtypes = [vp] * 14 + [i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.deltanet_gdp_bwd.restype = i
+    lib.deltanet_gdp_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.deltanet_gdp_bwd_workspace_bytes.restype = sz
     lib.deltanet_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.deltanet_decode_step.restype = i
     lib.deltanet_kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
@@ -638,6 +642,54 @@ def deltanet_gated_bwd_varlen(q, k, v, beta, g, dO, cu_seqlens, S0=None, dS_fina
                                            DN_BF16, _ptr(workspace), ws_bytes, _stream_handle(stream))
     if st != 0:
         raise DeltaNetError(st, "deltanet_gated_bwd_varlen")
+    return dq, dkk, dvv, db, dg, dS0
+
+
+def deltanet_gdp_bwd_workspace_bytes(B, H, T, n_h, dk, dv, chunk=64) -> int:
+    return int(load_library().deltanet_gdp_bwd_workspace_bytes(B, H, T, n_h, dk, dv, chunk))
+
+
+def deltanet_gdp_bwd(q, k, v, beta, g, dO, S0=None, dS_final=None, *, chunk: int = 64, workspace=None,
+                     want_dS0: bool = True, stream=None):
+    """Backward of ``deltanet_gdp_fwd`` (C-ABI ``deltanet_gdp_bwd``, bf16 only).
+
+    q: [B,T,H,dk]; k: [B,T,n_h,H,dk]; v: [B,T,n_h,H,dv]; beta: [B,T,n_h,H]
+    (bf16); g: [B,T,H] fp32; dO: [B,T,H,dv]; S0, dS_final: [B,H,dv,dk] fp32
+    or None. Returns (dq, dk, dv, dbeta, dg, dS0 or None) in the layouts of
+    the inputs.
+    """
+    lib = load_library()
+    if k.dim() != 5:
+        raise ValueError("k must be [B, T, n_h, H, dk]")
+    B, T, n_h, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    if dt != torch.bfloat16:
+        raise TypeError("deltanet_gdp_bwd supports bfloat16 inputs only")
+    _check(q, "q", dt, dev, (B, T, H, dk))
+    _check(k, "k", dt, dev, (B, T, n_h, H, dk))
+    _check(v, "v", dt, dev, (B, T, n_h, H, dv))
+    _check(beta, "beta", dt, dev, (B, T, n_h, H))
+    _check(g, "g", torch.float32, dev, (B, T, H))
+    _check(dO, "dO", dt, dev, (B, T, H, dv))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if dS_final is not None:
+        _check(dS_final, "dS_final", torch.float32, dev, (B, H, dv, dk))
+    dq, dkk, dvv, db = (torch.empty_like(x) for x in (q, k, v, beta))
+    dg = torch.empty_like(g)
+    dS0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None
+    need = int(lib.deltanet_gdp_bwd_workspace_bytes(B, H, T, n_h, dk, dv, chunk))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.deltanet_gdp_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO),
+                                  _ptr(dS_final), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg), _ptr(dS0),
+                                  B, H, T, n_h, dk, dv, chunk, DN_BF16, _ptr(workspace), ws_bytes,
+                                  _stream_handle(stream))
+    if st != 0:
+        raise DeltaNetError(st, "deltanet_gdp_bwd")
     return dq, dkk, dvv, db, dg, dS0
 
 

@@ -203,8 +203,9 @@ size_t varlen_max_slots(int N, int total_T, int H) {
 // chunk | partial sums | T^T of each chunk | chunk offsets (varlen)].
 int bwd_common(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
                const void *dO, const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dg,
-               float *dS0, const int32_t *cu_seqlens, const int32_t *seq_order, int B, int H, int T, int dk, int dv,
-               int chunk, int dtype, void *workspace, size_t workspace_bytes, size_t need, hipStream_t stream) {
+               float *dS0, const int32_t *cu_seqlens, const int32_t *seq_order, int B, int H, int T, int nh, int dk,
+               int dv, int chunk, int dtype, void *workspace, size_t workspace_bytes, size_t need,
+               hipStream_t stream) {
     int st = check_shape(dk, dv, chunk, dtype);
     if (st != DN_OK) return st;
     if (dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
@@ -253,7 +254,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     a.B = B;
     a.H = H;
     a.T = T;
-    a.nh = 1;
+    a.nh = nh;
     a.kind = varlen ? dn::kVarlen : dn::kDense;
     a.n_units = B * H;
     a.n_tiles = dv / dn::kRows;
@@ -282,6 +283,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     b.B = B;
     b.H = H;
     b.T = T;
+    b.nh = nh;
     b.NC = NC;
     b.n_tiles = dv / dn::kRows;
     b.max_slots = (int64_t)slots;
@@ -529,7 +531,7 @@ int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, 
     if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
     const size_t need = deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk);
     return bwd_common(q, k, v, beta, nullptr, S0, dO, dS_final, dq, dk_, dv_, dbeta, nullptr, dS0, nullptr, nullptr, B,
-                      H, T, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+                      H, T, 1, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
 }
 
 int deltanet_gated_bwd(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
@@ -539,8 +541,25 @@ int deltanet_gated_bwd(const void *q, const void *k, const void *v, const void *
     if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
     if (T > 0 && (!g || !dg)) return DN_ERR_INVALID;
     const size_t need = deltanet_gated_bwd_workspace_bytes(B, H, T, dk, dv, chunk);
-    return bwd_common(q, k, v, beta, g, S0, dO, dS_final, dq, dk_, dv_, dbeta, dg, dS0, nullptr, nullptr, B, H, T, dk,
-                      dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+    return bwd_common(q, k, v, beta, g, S0, dO, dS_final, dq, dk_, dv_, dbeta, dg, dS0, nullptr, nullptr, B, H, T, 1,
+                      dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+}
+
+size_t deltanet_gdp_bwd_workspace_bytes(int B, int H, int T, int n_h, int dk, int dv, int chunk) {
+    if (n_h <= 0 || T < 0 || (int64_t)T * n_h > INT32_MAX / 2) return 0;
+    return deltanet_gated_bwd_workspace_bytes(B, H, T * n_h, dk, dv, chunk);
+}
+
+int deltanet_gdp_bwd(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
+                     const void *dO, const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dg,
+                     float *dS0, int B, int H, int T, int n_h, int dk, int dv, int chunk, int dtype, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    if (B <= 0 || H <= 0 || T < 0 || n_h <= 0) return DN_ERR_INVALID;
+    if ((int64_t)T * n_h > INT32_MAX / 2) return DN_ERR_UNSUPPORTED;
+    if (T > 0 && (!g || !dg)) return DN_ERR_INVALID;
+    const size_t need = deltanet_gdp_bwd_workspace_bytes(B, H, T, n_h, dk, dv, chunk);
+    return bwd_common(q, k, v, beta, g, S0, dO, dS_final, dq, dk_, dv_, dbeta, dg, dS0, nullptr, nullptr, B, H, T * n_h,
+                      n_h, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
 }
 
 int deltanet_gated_bwd_varlen(const void *q, const void *k, const void *v, const void *beta, const float *g,
@@ -553,7 +572,7 @@ int deltanet_gated_bwd_varlen(const void *q, const void *k, const void *v, const
     if (!aligned_to(cu_seqlens, 4) || (seq_order && !aligned_to(seq_order, 4))) return DN_ERR_INVALID;
     const size_t need = deltanet_gated_bwd_varlen_workspace_bytes(N, total_T, H, dk, dv, chunk);
     return bwd_common(q, k, v, beta, g, S0, dO, dS_final, dq, dk_, dv_, dbeta, dg, dS0, cu_seqlens, seq_order, N, H,
-                      total_T, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+                      total_T, 1, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
 }
 
 int deltanet_bwd_varlen(const void *q, const void *k, const void *v, const void *beta, const float *S0,
@@ -564,7 +583,7 @@ int deltanet_bwd_varlen(const void *q, const void *k, const void *v, const void 
     if (!aligned_to(cu_seqlens, 4) || (seq_order && !aligned_to(seq_order, 4))) return DN_ERR_INVALID;
     const size_t need = deltanet_bwd_varlen_workspace_bytes(N, total_T, H, dk, dv, chunk);
     return bwd_common(q, k, v, beta, nullptr, S0, dO, dS_final, dq, dk_, dv_, dbeta, nullptr, dS0, cu_seqlens,
-                      seq_order, N, H, total_T, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+                      seq_order, N, H, total_T, 1, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
 }
 
 int deltanet_decode_step(const void *q, const void *k, const void *v, const void *beta, const float *g,

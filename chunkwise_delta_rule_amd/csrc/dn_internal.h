@@ -84,6 +84,10 @@ struct BwdArgs {
     // chunk slots as in ChainArgs::chunk_base; dense: slot of (unit u, chunk c) = u NC + c
     const int32_t *cu_seqlens, *seq_order, *chunk_base;
     int B, H, T, NC, n_tiles;
+    // Gated Delta Product: nh substeps per real token; T, k, v, beta, dk, dv,
+    // dbeta are over the virtual sequence, q, g, dO, dq, dg per real token (the
+    // query on the last substep, the decay on the first); 1 otherwise
+    int nh;
     int64_t max_slots; // chunk slots the workspace holds (dense: B H NC); the finishing grid
 };
 // Chunk slots before each packed sequence: cb[n] = sum_{m < n} ceil(L_m / 64), cb[N] the total.

@@ -981,13 +981,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     sg.rbeta = TR::fromf(0.f);
     sg.rg = 0.f;
     sg.nval = 0;
-    if constexpr (GATED) { // decays (and so queries) addressed by absolute token
+    if constexpr (GATED) { // decays (and so queries) addressed by real token
         sg.gg = a.g;
         sg.gh = a.g + h;
         sg.qh = reinterpret_cast<const E *>(a.q) + (int64_t)h * DK;
-        sg.sb = SubstepBase{tok0, 0u, 1u};
+        sg.sb = substep_base(tok0, a.nh);
     }
     const E *dOg = reinterpret_cast<const E *>(a.dO) + tok0 * sv + (int64_t)h * DV + row0;
+    const E *dOh = reinterpret_cast<const E *>(a.dO) + (int64_t)h * DV + row0; // real token 0 (substeps)
     E *dVg = reinterpret_cast<E *>(a.dv) + tok0 * sv + (int64_t)h * DV + row0;
 
     // dS rows 16w + c16 of this tile: dSacc[m][i] = dS[row0 + 16w + c16][16m + 4g + i]
@@ -1013,8 +1014,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
-            dov[p] = *reinterpret_cast<const typename TR::V *>(dOg + ((int64_t)c * kChunk + min(row, n - 1)) * sv +
-                                                               8 * cv);
+            const int64_t x = (int64_t)c * kChunk + min(row, n - 1);
+            if (GATED && a.nh > 1) { // the output gradient of the real token, on its last substep only
+                const Substep st = substep_at(sg.sb, (uint32_t)x);
+                const typename TR::V y = *reinterpret_cast<const typename TR::V *>(dOh + st.t * sv + 8 * cv);
+                dov[p] = st.j == a.nh - 1 ? y : typename TR::V{};
+            } else {
+                dov[p] = *reinterpret_cast<const typename TR::V *>(dOg + x * sv + 8 * cv);
+            }
         }
         const float *Sr = a.S_chunks + ((slot0 + c) * DV + row0 + 16 * w + c16) * DK + 4 * g;
 #pragma unroll
@@ -1349,11 +1356,11 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     sg.rbeta = TR::fromf(0.f);
     sg.rg = 0.f;
     sg.nval = 0;
-    if constexpr (GATED) { // decays (and so queries) addressed by absolute token
+    if constexpr (GATED) { // decays (and so queries) addressed by real token
         sg.gg = a.g;
         sg.gh = a.g + h;
         sg.qh = reinterpret_cast<const E *>(a.q) + (int64_t)h * DK;
-        sg.sb = SubstepBase{tok0, 0u, 1u};
+        sg.sb = substep_base(tok0, a.nh);
     }
     sg.load(r);
     typename TR::V tv[2]; // T^T of the chunk, as the forward pass formed it
@@ -1578,15 +1585,23 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
             dKa[m] = TR::mma32(dKa[m], TR::ldcol(dLs, LT, 16 * sb, 16 * w, g, c16),
                                TR::ldcol(dLs, LT, 16 * sb + 16, 16 * w, g, c16), kc0, kc1);
         }
-    E *dqg = reinterpret_cast<E *>(a.dq) + (tok0 + (int64_t)r * kChunk) * sqk + (int64_t)h * DK;
     E *dkg = reinterpret_cast<E *>(a.dk) + (tok0 + (int64_t)r * kChunk) * sqk + (int64_t)h * DK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = 16 * w + 4 * g + i;
         if (t < nval) {
+            // dq row: the token itself, or (substeps) the real token, on its last substep only
+            int64_t qt = tok0 + (int64_t)r * kChunk + t;
+            bool wq = true;
+            if (GATED && a.nh > 1) {
+                const Substep st = substep_at(sg.sb, (uint32_t)(r * kChunk + t));
+                qt = st.t;
+                wq = st.j == a.nh - 1;
+            }
+            E *dqg = reinterpret_cast<E *>(a.dq) + qt * sqk + (int64_t)h * DK;
 #pragma unroll
             for (int m = 0; m < NMT; ++m) {
-                dqg[(int64_t)t * sqk + 16 * m + c16] = TR::fromf(dQa[m][i]);
+                if (wq) dqg[16 * m + c16] = TR::fromf(dQa[m][i]);
                 dkg[(int64_t)t * sqk + 16 * m + c16] = TR::fromf(dKa[m][i]);
             }
             if (c16 == 0)
@@ -1614,7 +1629,10 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
                 const float y = __shfl_down(dgam, o, 64);
                 dgam += t + o < 64 ? y : 0.f;
             }
-            if (t < nval) a.dg[(tok0 + (int64_t)r * kChunk + t) * a.H + h] = dgam;
+            if (t < nval) { // substeps: the decay's gradient is the first substep's
+                const Substep st = substep_at(sg.sb, (uint32_t)(r * kChunk + t));
+                if (st.j == 0) a.dg[st.t * a.H + h] = dgam;
+            }
         }
     }
 }

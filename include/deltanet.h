@@ -328,6 +328,29 @@ size_t deltanet_gated_bwd_varlen_workspace_bytes(int N, int total_T, int H, int 
                                                  int chunk);
 
 /*
+ * Backward pass of deltanet_gdp_fwd (DN_BF16 only): "Linear Attention,
+ * Visualized", "Gated Delta Product (GDP)" > "GDP as GDN over a virtual
+ * sequence" makes GDP Gated DeltaNet over n_h substeps per token, so this is
+ * the gated backward over that virtual sequence. Layouts as deltanet_gdp_fwd:
+ *   q, dO : [B,T,H,dk] / [B,T,H,dv] (dtype), per real token (the query and the
+ *           output sit on the last substep)
+ *   k, v, beta : [B,T,n_h,H,*] per substep;  g : [B,T,H] fp32 (on the first substep)
+ *   dq, dk, dv, dbeta, dg : outputs in the layouts of q, k, v, beta, g
+ *   S0, dS_final, dS0 : as deltanet_gated_bwd
+ * Workspace: at least deltanet_gdp_bwd_workspace_bytes(...) bytes, 16-byte
+ * aligned (that of deltanet_gated_bwd at T n_h tokens). Errors as in
+ * deltanet_gated_bwd; n_h <= 0: DN_ERR_INVALID; T n_h > 2^30: DN_ERR_UNSUPPORTED.
+ */
+int deltanet_gdp_bwd(const void *q, const void *k, const void *v, const void *beta,
+                     const float *g, const float *S0, const void *dO, const float *dS_final,
+                     void *dq, void *dk, void *dv, void *dbeta, float *dg, float *dS0, int B,
+                     int H, int T, int n_h, int dk_, int dv_, int chunk, int dtype,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace deltanet_gdp_bwd needs (0 for invalid shapes). */
+size_t deltanet_gdp_bwd_workspace_bytes(int B, int H, int T, int n_h, int dk, int dv, int chunk);
+
+/*
  * Bytes of workspace deltanet_fwd (or deltanet_gated_fwd, deltanet_gdp_fwd,
  * deltanet_kda_fwd) needs for this
  * shape and cp_groups (0 means the library's choice on the current device).
