@@ -284,6 +284,34 @@ def gdp_variant(dev, w, flops_per_head_step, peak_flops, nh=2, steps=20, warmup=
             "mfma_frac": round(flops / (launch_ms / 1e3) / peak_flops, 4)}
 
 
+def gdp_bwd_variant(dev, w, fwd_ms, nh=2, steps=10, warmup=3):
+    """Time deltanet_gdp_bwd with nh substeps per token on the workload's B, H,
+    T (real tokens), inputs drawn as in gdp_variant. Bytes: q, g, dO, dq, dg
+    per real token; k, v, beta, dk, dv, dbeta per substep."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import make_gates, make_inputs
+
+    print(f"[bench] gdp backward variant n_h={nh}", file=sys.stderr, flush=True)
+    B, H, T = w.B, w.H, w.T
+    q, _, _, _, _ = make_inputs(B, H, T, w.dk, w.dv, seed=6, device=str(dev))
+    _, k, v, beta, _ = make_inputs(B, H, T * nh, w.dk, w.dv, seed=7, device=str(dev))
+    k, v, beta = k.view(B, T, nh, H, w.dk), v.view(B, T, nh, H, w.dv), beta.view(B, T, nh, H)
+    g = make_gates((B, T, H), seed=6, device=str(dev))
+    gen = torch.Generator(device=dev).manual_seed(9)
+    dO = torch.randn((B, T, H, w.dv), generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
+    need = dn.deltanet_gdp_bwd_workspace_bytes(B, H, T, nh, w.dk, w.dv)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ms, launch_ms, _ = time_steps(lambda: dn.deltanet_gdp_bwd(q, k, v, beta, g, dO, workspace=ws), warmup, steps)
+    nbytes = B * T * H * 2 * (2 * (w.dk + w.dv) + 4 + nh * 2 * (w.dk + w.dv + 1))
+    return {"call": "deltanet_gdp_bwd", "n_h": nh, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(B * T / (ms / 1e3), 1),
+            "virtual_steps_per_s": round(B * T * nh / (ms / 1e3), 1),
+            "avg_launch_us": round(launch_ms * 1e3, 2), "vs_forward_time": round(launch_ms / fwd_ms, 3),
+            "algorithmic_bytes": nbytes, "workspace_bytes": need,
+            "hbm_frac_algorithmic": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4)}
+
+
 def decode_variant(dev, B=256, H=16, d=128, steps=50, warmup=10):
     """Time deltanet_decode_step (with and without decay) and
     deltanet_kda_decode_step (per-channel decay) on a B x H state of d x d
@@ -473,6 +501,7 @@ def main():
         result.setdefault("variants", {})["bwd"] = bwd_variant(dev, w, inputs, avg_launch_ms)
         result["variants"]["gated_bwd"] = gated_bwd_variant(dev, w, inputs, avg_launch_ms)
         result["variants"]["gdp"] = gdp_variant(dev, w, flops / n_tokens / w.H, peak_flops)
+        result["variants"]["gdp_bwd"] = gdp_bwd_variant(dev, w, result["variants"]["gdp"]["avg_launch_us"] / 1e3)
         result["variants"]["kda"] = kda_variant(dev, w, inputs, avg_launch_ms)
         result["variants"]["kda_long"] = kda_long_variant(dev)
     if not args.gated and not args.no_variants:

@@ -920,7 +920,9 @@ __device__ inline bf16x8 scale8(bf16x8 x, float f) {
     return y;
 }
 
-template <int DK, int DV, bool GATED>
+// SUB: several substeps per real token (Gated Delta Product), so queries,
+// decays and output gradients are addressed through the substep map.
+template <int DK, int DV, bool GATED, bool SUB>
 __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     using E = __bf16;
     using TR = Tr<E>;
@@ -985,7 +987,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         sg.gg = a.g;
         sg.gh = a.g + h;
         sg.qh = reinterpret_cast<const E *>(a.q) + (int64_t)h * DK;
-        sg.sb = substep_base(tok0, a.nh);
+        sg.sb = SUB ? substep_base(tok0, a.nh) : SubstepBase{tok0, 0u, 1u};
     }
     const E *dOg = reinterpret_cast<const E *>(a.dO) + tok0 * sv + (int64_t)h * DV + row0;
     const E *dOh = reinterpret_cast<const E *>(a.dO) + (int64_t)h * DV + row0; // real token 0 (substeps)
@@ -1015,7 +1017,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         for (int p = 0; p < 2; ++p) {
             const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
             const int64_t x = (int64_t)c * kChunk + min(row, n - 1);
-            if (GATED && a.nh > 1) { // the output gradient of the real token, on its last substep only
+            if constexpr (SUB) { // the output gradient of the real token, on its last substep only
                 const Substep st = substep_at(sg.sb, (uint32_t)x);
                 const typename TR::V y = *reinterpret_cast<const typename TR::V *>(dOh + st.t * sv + 8 * cv);
                 dov[p] = st.j == a.nh - 1 ? y : typename TR::V{};
@@ -1287,7 +1289,7 @@ template <int DK, bool GATED> struct FinLds {
     static constexpr size_t total = GATED ? oCs + 4 * 256 : oL + szX;
 };
 
-template <int DK, int DV, bool GATED>
+template <int DK, int DV, bool GATED, bool SUB>
 __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     using E = __bf16;
     using TR = Tr<E>;
@@ -1360,7 +1362,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
         sg.gg = a.g;
         sg.gh = a.g + h;
         sg.qh = reinterpret_cast<const E *>(a.q) + (int64_t)h * DK;
-        sg.sb = substep_base(tok0, a.nh);
+        sg.sb = SUB ? substep_base(tok0, a.nh) : SubstepBase{tok0, 0u, 1u};
     }
     sg.load(r);
     typename TR::V tv[2]; // T^T of the chunk, as the forward pass formed it
@@ -1593,7 +1595,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
             // dq row: the token itself, or (substeps) the real token, on its last substep only
             int64_t qt = tok0 + (int64_t)r * kChunk + t;
             bool wq = true;
-            if (GATED && a.nh > 1) {
+            if constexpr (SUB) {
                 const Substep st = substep_at(sg.sb, (uint32_t)(r * kChunk + t));
                 qt = st.t;
                 wq = st.j == a.nh - 1;
@@ -1629,9 +1631,13 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
                 const float y = __shfl_down(dgam, o, 64);
                 dgam += t + o < 64 ? y : 0.f;
             }
-            if (t < nval) { // substeps: the decay's gradient is the first substep's
-                const Substep st = substep_at(sg.sb, (uint32_t)(r * kChunk + t));
-                if (st.j == 0) a.dg[st.t * a.H + h] = dgam;
+            if (t < nval) {
+                if constexpr (SUB) { // the decay's gradient is the first substep's
+                    const Substep st = substep_at(sg.sb, (uint32_t)(r * kChunk + t));
+                    if (st.j == 0) a.dg[st.t * a.H + h] = dgam;
+                } else {
+                    a.dg[(tok0 + (int64_t)r * kChunk + t) * a.H + h] = dgam;
+                }
             }
         }
     }
@@ -1890,17 +1896,23 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 template <int DK, int DV> hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t s) {
     const int units = a.B * a.H;
     if (units <= 0 || (!a.cu_seqlens && a.NC <= 0)) return hipSuccess; // varlen: empty sequences still set dS0
-    if (a.g)
-        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, true>), dim3(units * a.n_tiles), dim3(kThreads), 0, s, a);
+    const dim3 cg(units * a.n_tiles);
+    if (a.g && a.nh > 1)
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, true, true>), cg, dim3(kThreads), 0, s, a);
+    else if (a.g)
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, true, false>), cg, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, false>), dim3(units * a.n_tiles), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, false, false>), cg, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.max_slots <= 0) return hipSuccess;
-    if (a.g)
-        hipLaunchKernelGGL((bwd_finish_kernel<DK, DV, true>), dim3((unsigned)a.max_slots), dim3(kThreads), 0, s, a);
+    const dim3 fg((unsigned)a.max_slots);
+    if (a.g && a.nh > 1)
+        hipLaunchKernelGGL((bwd_finish_kernel<DK, DV, true, true>), fg, dim3(kThreads), 0, s, a);
+    else if (a.g)
+        hipLaunchKernelGGL((bwd_finish_kernel<DK, DV, true, false>), fg, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((bwd_finish_kernel<DK, DV, false>), dim3((unsigned)a.max_slots), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((bwd_finish_kernel<DK, DV, false, false>), fg, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

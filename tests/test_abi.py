@@ -251,6 +251,29 @@ def test_gated_bwd_workspace_sizes(lib):
     assert lib.deltanet_gated_bwd_workspace_bytes(2, 3, 200, 96, 128, 64) == 0
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(nh=0), DN_ERR_INVALID),
+    (dict(g=None), DN_ERR_INVALID),
+    (dict(T=1 << 29, nh=4), DN_ERR_UNSUPPORTED),  # the virtual length must stay under 2^30
+    (dict(dtype=0), DN_ERR_UNSUPPORTED),
+    (dict(ws_bytes=0), DN_ERR_WORKSPACE),
+])
+def test_gdp_bwd_rejects_bad_arguments(lib, kw, status):
+    a = dict(g=FAKE, nh=2, T=100, dtype=1, ws_bytes=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    st = lib.deltanet_gdp_bwd(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(a["g"]) if a["g"] else None, None,
+                              vp(FAKE), None, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, 2, 2, a["T"],
+                              a["nh"], 128, 128, 64, a["dtype"], None, a["ws_bytes"], None)
+    assert st == status
+
+
+def test_gdp_bwd_workspace_is_gated_over_the_virtual_length(lib):
+    assert (lib.deltanet_gdp_bwd_workspace_bytes(2, 3, 100, 3, 128, 64, 64)
+            == lib.deltanet_gated_bwd_workspace_bytes(2, 3, 300, 128, 64, 64))
+    assert lib.deltanet_gdp_bwd_workspace_bytes(2, 3, 100, 0, 128, 64, 64) == 0
+
+
 def test_bwd_varlen_workspace_bound(lib):
     # chunk slots are bounded by total_T / 64 + N per head, whatever the lengths
     one = lib.deltanet_bwd_varlen_workspace_bytes(1, 64, 1, 128, 128, 64)  # 2 slots + the offsets
