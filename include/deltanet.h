@@ -86,7 +86,7 @@ typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype_t;
 enum {
     DN_OK = 0,
     DN_ERR_INVALID = -1,     /* NULL/misaligned pointer, negative or zero size, bad enum */
-    DN_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (chunk, dk, dv) */
+    DN_ERR_UNSUPPORTED = -2, /* valid request the library does not implement (chunk, dk, dv) */
     DN_ERR_WORKSPACE = -3,   /* workspace missing or smaller than deltanet_workspace_bytes */
     DN_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 };
