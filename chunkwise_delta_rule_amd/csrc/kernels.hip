@@ -521,6 +521,9 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
     V rk[NKQ], rq[NKQ], rv[NVV];
     E rbeta;
     float rg;
+    // gated: whether the loaded query (decay) belongs to this substep; applied
+    // at staging so that no select waits on a load in flight
+    bool qon[NKQ], gon;
     int nval;
 
     __device__ inline void load(int c) {
@@ -533,8 +536,8 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
             rk[p] = *reinterpret_cast<const V *>(kg + (base + row) * sqk + cv * TR::kVec);
             if (gg) { // the query of the real token, on its last substep only
                 const Substep st = substep_at(sb, (uint32_t)(base + row));
-                const V x = *reinterpret_cast<const V *>(qh + st.t * sqk + cv * TR::kVec);
-                rq[p] = st.j == (int)sb.nh - 1 ? x : V{};
+                rq[p] = *reinterpret_cast<const V *>(qh + st.t * sqk + cv * TR::kVec);
+                qon[p] = st.j == (int)sb.nh - 1;
             } else {
                 rq[p] = *reinterpret_cast<const V *>(qg + (base + row) * sqk + cv * TR::kVec);
             }
@@ -549,8 +552,8 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
         rbeta = bg[(base + min(tid & (kChunk - 1), last)) * H]; // every wave holds all 64
         if (gg) { // the decay of the real token, on its first substep only
             const Substep st = substep_at(sb, (uint32_t)(base + min(tid & (kChunk - 1), last)));
-            const float x = gh[st.t * H];
-            rg = st.j == 0 ? x : 0.f;
+            rg = gh[st.t * H];
+            gon = st.j == 0;
         }
     }
     // Returns lane l's decay prefix sum (gated), else 0.
@@ -561,7 +564,7 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
             const int vi = p * NT + tid, row = vi / KQV, cv = vi % KQV;
             const bool ok = row < nval;
             *reinterpret_cast<V *>(Ks + row * L::K + cv * TR::kVec) = ok ? rk[p] : zero;
-            if (Qs) *reinterpret_cast<V *>(Qs + row * L::K + cv * TR::kVec) = ok ? rq[p] : zero;
+            if (Qs) *reinterpret_cast<V *>(Qs + row * L::K + cv * TR::kVec) = ok && (!gg || qon[p]) ? rq[p] : zero;
         }
         // the four waves write identical values: no branch needed
         const int l = tid & (kChunk - 1);
@@ -570,7 +573,7 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
         if (gg) {
             // inclusive prefix sum over the chunk's tokens (lane l = token l), in
             // base-2 units; tokens past the end add nothing
-            gl = wave_inclusive_sum(l < nval ? rg * 1.44269504088896340736f : 0.f, l);
+            gl = wave_inclusive_sum(l < nval && gon ? rg * 1.44269504088896340736f : 0.f, l);
             if (Gs) Gs[l] = gl;
         }
         return gl;
@@ -580,7 +583,7 @@ template <typename E, int DK, int NT = kThreads> struct Stager {
 #pragma unroll
         for (int p = 0; p < NKQ; ++p) {
             const int vi = p * NT + tid, row = vi / KQV, cv = vi % KQV;
-            *reinterpret_cast<V *>(Qs + row * L::K + cv * TR::kVec) = row < nval ? rq[p] : zero;
+            *reinterpret_cast<V *>(Qs + row * L::K + cv * TR::kVec) = row < nval && (!gg || qon[p]) ? rq[p] : zero;
         }
     }
     __device__ inline void store_v(E *Vs) const {
@@ -1006,6 +1009,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     // registers; issued one chunk ahead so their latency hides under the
     // previous chunk's products.
     typename TR::V dov[2], tv[2];
+    bool don[2] = {true, true}; // substeps: the row is its real token's last substep (applied at staging)
     const E *Tg = a.T_chunks + slot0 * kChunk * kChunk;
     auto load_chunk = [&](int c) {
         const int n = min(kChunk, len - c * kChunk);
@@ -1019,8 +1023,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
             const int64_t x = (int64_t)c * kChunk + min(row, n - 1);
             if constexpr (SUB) { // the output gradient of the real token, on its last substep only
                 const Substep st = substep_at(sg.sb, (uint32_t)x);
-                const typename TR::V y = *reinterpret_cast<const typename TR::V *>(dOh + st.t * sv + 8 * cv);
-                dov[p] = st.j == a.nh - 1 ? y : typename TR::V{};
+                dov[p] = *reinterpret_cast<const typename TR::V *>(dOh + st.t * sv + 8 * cv);
+                don[p] = st.j == a.nh - 1;
             } else {
                 dov[p] = *reinterpret_cast<const typename TR::V *>(dOg + x * sv + 8 * cv);
             }
@@ -1040,7 +1044,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
-            *reinterpret_cast<typename TR::V *>(Ds + row * L::V + 8 * cv) = row < nval ? dov[p] : typename TR::V{};
+            *reinterpret_cast<typename TR::V *>(Ds + row * L::V + 8 * cv) =
+                row < nval && (!SUB || don[p]) ? dov[p] : typename TR::V{};
             *reinterpret_cast<typename TR::V *>(TsT + row * L::T + 8 * cv) = tv[p];
         }
         // This wave's 16 value rows (column c16 of the accumulators).
