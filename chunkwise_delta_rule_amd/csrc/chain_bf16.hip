@@ -282,6 +282,7 @@ struct VStager {
     bf16x8 r[2][NV];
     __bf16 rb[2];
     float rg[2];
+    bool gkeep[2]; // the decay sits on this substep (applied in write_gate, not at the load)
     int n[2], nb[2];
     __device__ inline void init(const __bf16 *vg, const __bf16 *bg, const float *gg, int64_t sv_, int H_, int len_,
                                 int lane_) {
@@ -299,6 +300,7 @@ struct VStager {
             n[b] = nb[b] = 0;
             rb[b] = (__bf16)0.f;
             rg[b] = 0.f;
+            gkeep[b] = false;
 #pragma unroll
             for (int p = 0; p < NV; ++p) r[b][p] = bf16x8{};
         }
@@ -323,7 +325,8 @@ struct VStager {
         if (gt) { // the decay sits on the first substep of its real token
             const Substep st = substep_at(sb, (uint32_t)(c * kChunk + min(lane, nb[B] - 1)));
             const float x = gt[st.t * H];
-            rg[B] = st.j == 0 ? x : 0.f;
+            rg[B] = x;
+            gkeep[B] = st.j == 0;
         }
     }
     template <int B> __device__ inline void write_v(__bf16 *Vs) const {
@@ -338,7 +341,7 @@ struct VStager {
     // Inclusive prefix sum of the chunk's decay logarithms over the lanes
     // (token l in lane l), in base-2 units; tokens past the end add nothing.
     template <int B> __device__ inline void write_gate(float *Gs) const {
-        Gs[lane] = wave_inclusive_sum(lane < nb[B] ? rg[B] * 1.44269504088896340736f : 0.f, lane);
+        Gs[lane] = wave_inclusive_sum(lane < nb[B] && gkeep[B] ? rg[B] * 1.44269504088896340736f : 0.f, lane);
     }
 };
 
@@ -385,19 +388,25 @@ template <int DK> struct QStage {
     // head's query at real token 0, dk 8 g).
     const __bf16 *qh;
     SubstepBase sb; // split of the work's first virtual step
+    // The substep test is kept in `keep` and applied by mask_virtual just
+    // before the registers are used: a select here would wait on the loads.
+    bool keep[2][2];
     template <int B> __device__ inline void load_virtual(int c) {
         const int n = min(kChunk, len - c * kChunk);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const Substep st = substep_at(sb, (uint32_t)(c * kChunk + min(row[i], n - 1)));
             const __bf16 *b = qh + st.t * sqk;
-            const bool keep = st.j == (int)sb.nh - 1;
+            keep[B][i] = st.j == (int)sb.nh - 1;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(b + 32 * kb);
-                f[B][i][kb] = keep ? x : bf16x8{};
-            }
+            for (int kb = 0; kb < NKB; ++kb) f[B][i][kb] = *reinterpret_cast<const bf16x8 *>(b + 32 * kb);
         }
+    }
+    template <int B> __device__ inline void mask_virtual() {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) f[B][i][kb] = keep[B][i] ? f[B][i][kb] : bf16x8{};
     }
 };
 
@@ -930,6 +939,7 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
             ks.template load<S>(min(r + 5, last));
             if constexpr (WO) {
                 if (r + 1 >= 0 && r + 1 < NC) {
+                    if constexpr (GATED) q.template mask_virtual<S>();
                     q.template write<S>(bf.Q(r + 1), g);
                     p_tiles<DK, S, GATED>(bf, q, r + 1, ROLE - 2, lane, g, c16);
                 }
