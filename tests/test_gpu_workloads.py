@@ -219,6 +219,36 @@ def test_gated_bwd_layer_b8_h16_t4096_sampled():
     assert es <= 2e-2
 
 
+def test_gdp_bwd_layer_b8_h16_t4096_sampled():
+    # the GDP backward (n_h = 2) at the benchmark's full shape, inputs drawn
+    # as bench.py's variant draws them, sampled units against the oracle
+    w = WORKLOADS["layer_b8_h16_t4096"]
+    nh = 2
+    print(f"[case] {w.name} full size, gdp backward n_h={nh}", flush=True)
+    from chunkwise_delta_rule_amd.synth import make_inputs
+    B, H, T = w.B, w.H, w.T
+    q, _, _, _, _ = make_inputs(B, H, T, w.dk, w.dv, seed=6, device=DEV)
+    _, k, v, beta, _ = make_inputs(B, H, T * nh, w.dk, w.dv, seed=7, device=DEV)
+    k, v, beta = k.view(B, T, nh, H, w.dk), v.view(B, T, nh, H, w.dv), beta.view(B, T, nh, H)
+    gl = make_gates((B, T, H), seed=6, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    dO = torch.randn((B, T, H, w.dv), generator=gen, device=DEV, dtype=torch.float32).to(q.dtype)
+    out = dn.deltanet_gdp_bwd(q, k, v, beta, gl, dO)
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(x).all()) for x in out)
+    units = [(2, 5)]
+    for b, h in units:
+        ref = oracle.gdp_bwd(f64(q[b:b + 1, :, h:h + 1]), f64(k[b:b + 1, :, :, h:h + 1]),
+                             f64(v[b:b + 1, :, :, h:h + 1]), f64(beta[b:b + 1, :, :, h:h + 1]),
+                             f64(gl[b:b + 1, :, h:h + 1]), nh, f64(dO[b:b + 1, :, h:h + 1]))
+        mine = [f64(out[0][b:b + 1, :, h:h + 1]), f64(out[1][b:b + 1, :, :, h:h + 1]),
+                f64(out[2][b:b + 1, :, :, h:h + 1]), f64(out[3][b:b + 1, :, :, h:h + 1]),
+                f64(out[4][b:b + 1, :, h:h + 1]), f64(out[5][b:b + 1, h:h + 1])]
+        errs = [rel_err(x, r) for x, r in zip(mine, ref)]
+        print("  unit ({}, {}) err ".format(b, h) + " ".join(f"{e:.3e}" for e in errs), flush=True)
+        assert max(errs) <= 2e-2
+
+
 def test_kda_layer_b8_h16_t4096_sampled():
     # KDA at the benchmark's full shape, sampled units against the oracle
     w = WORKLOADS["layer_b8_h16_t4096"]
