@@ -143,3 +143,25 @@ def test_gated_bwd_varlen_d64_no_state():
         errs = [rel_err(x, r) for x, r in zip(mine, ref)]
         print(f"[case] gated bwd varlen d64 seq {n}: " + " ".join(f"{e:.2e}" for e in errs), flush=True)
         assert max(errs) <= TOL_BWD, (n, errs)
+
+
+def test_gated_bwd_near_reset_decays():
+    # a few g = -80 (the state is all but erased there), as in the forward's reset test
+    B, H, T, dk, dv = 1, 2, 200, 128, 128
+    print("[case] gated bwd near-reset decays", flush=True)
+    q, k, v, beta, S0 = make_inputs(B, H, T, dk, dv, seed=670, s0_std=0.3)
+    gl = make_gates((B, T, H), seed=671)
+    gl[0, 30, 0] = -80.0
+    gl[0, 64, 1] = -80.0
+    gl[0, 150, :] = -80.0
+    gen = torch.Generator().manual_seed(672)
+    dO = torch.randn(v.shape, generator=gen).to(torch.bfloat16)
+    dSf = torch.randn((B, H, dv, dk), generator=gen) * 0.1
+    d = [x.to(DEV) for x in (q, k, v, beta, gl, dO)]
+    out = deltanet_gated_bwd(*d, S0.to(DEV), dSf.to(DEV))
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(x).all()) for x in out)
+    ref = oracle.gated_deltanet_bwd(f64(q), f64(k), f64(v), f64(beta), f64(gl), f64(dO), f64(S0), f64(dSf))
+    errs = [rel_err(f64(x), r) for x, r in zip(out, ref)]
+    print("  err " + " ".join(f"{n}={e:.3e}" for n, e in zip(NAMES, errs)), flush=True)
+    assert max(errs) <= TOL_BWD
