@@ -86,8 +86,23 @@ def load(path: str = _LIB_PATH):
     if path == _LIB_PATH and _lib is not None:
         return _lib
     if path == _LIB_PATH:
+        override = os.environ.get("DELTANET_ORACLE_LIB")
+        if override:
+            # a separately built copy of the same source (the sanitizer test's build)
+            lib = ctypes.CDLL(override)
+            _declare(lib)
+            _lib = lib
+            return lib
         build()
     lib = ctypes.CDLL(path)
+    _declare(lib)
+    if path == _LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _declare(lib):
+    """Argument and result types of the C oracle's exports."""
     dp = ctypes.POINTER(ctypes.c_double)
     lib.oracle_deltanet_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -117,9 +132,6 @@ def load(path: str = _LIB_PATH):
     lib.oracle_kda_fwd.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
-    if path == _LIB_PATH:
-        _lib = lib
-    return lib
 
 
 def _f64(x):
