@@ -18,6 +18,11 @@ same workload. ``variants.kda`` times ``deltanet_kda_fwd`` (per-channel decay) o
 workload. ``variants.gdp`` times ``deltanet_gdp_fwd`` (Gated Delta Product, n_h = 2 substeps
 per token) on the same B, H, T and widths. ``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
 head, state updated in place) on B=256 H=16 d=128 bf16, a 256 MiB state.
+The other four workloads of the forward pass are timed by the same clock under
+``variants.<workload>``: B=4 H=16 T=8192 (serial chain and the library's
+context-parallel choice), B=1 H=16 T=131072 (serial chain against context
+parallelism, with the speed-up), the packed batch of 64 sequences at H=32, and
+the tiny fp32 case.
 
 Accounting (per head-token, chunk C, key/value widths dk/dv):
   flops  F = 2C(3dk + 2dv) + 6 dk dv  -- the eight dense products of the
@@ -157,7 +162,8 @@ def cpu_baseline(inputs, w, varlen, budget_s, g=None):
         sample = f"{nb} of {B} sequences ({toks} tokens x {w.H} heads)"
         units = nb * w.H
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(min(threads, units)),
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3), "cpu_model": cpu_model(),
+            "host_threads": threads}
 
 
 def bwd_variant(dev, w, inputs, fwd_ms, steps=10, warmup=3):
@@ -310,6 +316,84 @@ def gdp_bwd_variant(dev, w, fwd_ms, nh=2, steps=10, warmup=3):
             "avg_launch_us": round(launch_ms * 1e3, 2), "vs_forward_time": round(launch_ms / fwd_ms, 3),
             "algorithmic_bytes": nbytes, "workspace_bytes": need,
             "hbm_frac_algorithmic": round(nbytes / (launch_ms / 1e3) / PEAK_HBM_BPS, 4)}
+
+
+def metric_for(w):
+    """The metric string with the workload's own shape in it."""
+    if w.varlen:
+        shape = f"N={w.N} packed L~U[{w.len_lo},{w.len_hi}] H={w.H} d={w.dk}"
+    else:
+        shape = f"B={w.B} H={w.H} T={w.T} d={w.dk}"
+    prec = "bf16" if w.dtype == "bf16" else "fp32"
+    return f"forward tokens/sec + % {prec} MFMA peak, {shape} chunk={w.chunk}"
+
+
+def workload_variant(dev, name, cp_list=(1,), steps=10, warmup=3, seed=2):
+    """Time deltanet_fwd (or deltanet_fwd_varlen) on another of the five
+    workloads, once per entry of ``cp_list`` (1 serial chunk chain, 0 the
+    library's group count, G > 1 forced). Bytes and flops as for the headline
+    line. With a serial and an automatic entry the ratio of their times is
+    reported as ``cp_speedup``."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[name]
+    print(f"[bench] workload variant {name}", file=sys.stderr, flush=True)
+    inputs = workload_inputs(w, seed=seed, device=str(dev))
+    esz = 2 if w.dtype == "bf16" else 4
+    peak = PEAK_BF16_FLOPS if w.dtype == "bf16" else PEAK_FP32_FLOPS
+    out = {"metric": metric_for(w), "steps": steps, "warmup": warmup}
+    if w.varlen:
+        q, k, v, beta, cu, S0, lengths = inputs
+        n_tokens, n_units = int(sum(lengths)), w.N * w.H
+        order = dn.longest_first_order(cu)
+        o = torch.empty_like(v)
+        Sf = torch.empty((w.N, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+        runs = [("serial", 1, lambda: dn.deltanet_fwd_varlen(q, k, v, beta, cu, S0, seq_order=order, o=o,
+                                                             S_final=Sf))]
+        out["config"] = {"N": w.N, "H": w.H, "total_T": n_tokens, "dk": w.dk, "dv": w.dv, "chunk": w.chunk}
+    else:
+        q, k, v, beta, S0 = inputs
+        n_tokens, n_units = w.B * w.T, w.B * w.H
+        o = torch.empty_like(v)
+        Sf = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+        runs = []
+        for cp in cp_list:
+            G = cp if cp > 0 else dn.deltanet_pick_cp_groups(w.B, w.H, w.T, w.dk, w.dv, w.chunk)
+            ws = torch.empty(max(dn.deltanet_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, G), 1),
+                             dtype=torch.uint8, device=dev)
+            label = "serial" if G == 1 and cp == 1 else ("context_parallel_auto" if cp == 0 else f"cp{G}")
+            runs.append((label, G, lambda G=G, ws=ws: dn.deltanet_fwd(q, k, v, beta, S0, o=o, S_final=Sf,
+                                                                      cp_groups=G, workspace=ws)))
+        out["config"] = {"B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk}
+    nbytes = algorithmic_bytes(w, esz, n_tokens, n_units, S0 is not None, True)
+    flops = n_tokens * w.H * flops_per_head_token(w.chunk, w.dk, w.dv)
+    out["algorithmic_bytes"] = nbytes
+    out["flops_per_step"] = flops
+    for label, G, fn in runs:
+        ms, launch_ms, _ = time_steps(fn, warmup, steps)
+        out[label] = {"cp_groups": G, "ms_per_step": round(ms, 5), "tokens_per_s": round(n_tokens / (ms / 1e3), 1),
+                      "hbm_frac": round(nbytes / (ms / 1e3) / PEAK_HBM_BPS, 4),
+                      "mfma_frac": round(flops / (ms / 1e3) / peak, 4)}
+    if "serial" in out and "context_parallel_auto" in out:
+        out["cp_speedup"] = round(out["serial"]["ms_per_step"] / out["context_parallel_auto"]["ms_per_step"], 3)
+    if not bool(torch.isfinite(o).all()) or not bool(torch.isfinite(Sf).all()):
+        print(f"bench.py: non-finite output in workload variant {name}", file=sys.stderr)
+        sys.exit(3)
+    del inputs, q, k, v, beta, o, Sf
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def decode_variant(dev, B=256, H=16, d=128, steps=50, warmup=10):
@@ -465,7 +549,7 @@ def main():
                 "mfma_tflops": round(flops / (avg_launch_ms / 1e3) / 1e12, 1),
                 "mfma_frac": round(flops / (avg_launch_ms / 1e3) / peak_flops, 4)}
 
-    metric = "forward tokens/sec + % bf16 MFMA peak, B=8 H=16 T=4096 d=128 chunk=64"
+    metric = metric_for(w)
     result = {
         "metric": ("Gated DeltaNet " + metric) if args.gated else metric,
         "value": round(tokens_per_s, 1),
@@ -504,6 +588,13 @@ def main():
         result["variants"]["gdp_bwd"] = gdp_bwd_variant(dev, w, result["variants"]["gdp"]["avg_launch_us"] / 1e3)
         result["variants"]["kda"] = kda_variant(dev, w, inputs, avg_launch_ms)
         result["variants"]["kda_long"] = kda_long_variant(dev)
+    if not args.gated and not args.no_variants and w.name == "layer_b8_h16_t4096":
+        # the other workloads of the forward pass, each timed by the same clock
+        result["variants"]["chunks128_b4_h16_t8192"] = workload_variant(dev, "chunks128_b4_h16_t8192", (1, 0))
+        result["variants"]["long_b1_h16_t131072"] = workload_variant(dev, "long_b1_h16_t131072", (1, 0),
+                                                                     steps=5, warmup=2)
+        result["variants"]["varlen_n64_h32"] = workload_variant(dev, "varlen_n64_h32", steps=5, warmup=2)
+        result["variants"]["tiny_f32"] = workload_variant(dev, "tiny_f32", steps=20, warmup=5)
     if not args.gated and not args.no_variants:
         result.setdefault("variants", {})["decode"] = decode_variant(dev)
     if not args.no_cpu_baseline:
