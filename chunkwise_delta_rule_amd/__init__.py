@@ -24,7 +24,7 @@ import os
 
 import torch
 
-__all__ = ["deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
+__all__ = ["deltanet_fwd", "deltanet_fwd_noalloc", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
            "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_kda_fwd_varlen", "deltanet_decode_step", "deltanet_kda_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
            "deltanet_bwd_varlen", "deltanet_bwd_varlen_workspace_bytes", "deltanet_gated_bwd",
            "deltanet_gated_bwd_workspace_bytes", "deltanet_gated_bwd_varlen",
@@ -102,6 +102,8 @@ def load_library(path: str | None = None):
     lib.deltanet_decode_step.restype = i
     lib.deltanet_kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.deltanet_kda_decode_step.restype = i
+    lib.deltanet_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    lib.deltanet_fwd_noalloc.restype = i
     lib.deltanet_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.deltanet_workspace_bytes.restype = sz
     lib.deltanet_pick_cp_groups.argtypes = [i, i, i, i, i, i]
@@ -206,6 +208,36 @@ def deltanet_fwd(q, k, v, beta, S0=None, *, chunk: int = 64, cp_groups: int = 1,
     """
     return _fwd(q, k, v, beta, None, S0, chunk, cp_groups, o, S_final, output_final_state,
                 workspace, stream)
+
+
+def deltanet_fwd_noalloc(q, k, v, beta, S0=None, *, o, S_final=None, chunk: int = 64, cp_groups: int = 1,
+                         stream=None):
+    """``deltanet_fwd`` through the C-ABI ``deltanet_fwd_noalloc``: the
+    context-parallel workspace is the library's fixed per-device array, and
+    neither the library nor this wrapper allocates (o, and S_final when
+    wanted, are the caller's). Returns (o, S_final)."""
+    lib = load_library()
+    if k.dim() != 4:
+        raise ValueError("k must be [B, T, H, dk]")
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check(q, "q", dt, dev, (B, T, H, dk))
+    _check(v, "v", dt, dev, (B, T, H, dv))
+    _check(beta, "beta", dt, dev, (B, T, H))
+    _check(o, "o", dt, dev, (B, T, H, dv))
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev, (B, H, dv, dk))
+    if S_final is not None:
+        _check(S_final, "S_final", torch.float32, dev, (B, H, dv, dk))
+    with torch.cuda.device(dev):
+        st = lib.deltanet_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final),
+                                      B, H, T, dk, dv, chunk, _DTYPE_CODE[dt], cp_groups, _stream_handle(stream))
+    if st != 0:
+        raise DeltaNetError(st, "deltanet_fwd_noalloc")
+    return o, S_final
 
 
 def deltanet_gated_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64, cp_groups: int = 1, o=None,

@@ -4,7 +4,8 @@
 
 The library is the C-ABI declared in ``include/deltanet.h``: the host layer
 (``csrc/api.cpp``) and the kernels (``csrc/kernels.hip``, ``csrc/chain_bf16.hip``,
-``csrc/decode.hip``), compiled for gfx950
+``csrc/decode.hip``) and the no-allocation entry point (``csrc/noalloc.hip``),
+compiled for gfx950
 only. Packed-fp32 VALU instructions are switched off for all device code.
 """
 
@@ -18,7 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libdeltanet.so")
 SOURCES = [os.path.join(PKG, "csrc", "kernels.hip"), os.path.join(PKG, "csrc", "chain_bf16.hip"),
-           os.path.join(PKG, "csrc", "decode.hip"), os.path.join(PKG, "csrc", "api.cpp")]
+           os.path.join(PKG, "csrc", "decode.hip"), os.path.join(PKG, "csrc", "noalloc.hip"),
+           os.path.join(PKG, "csrc", "api.cpp")]
 HEADERS = [os.path.join(PKG, "csrc", "dn_internal.h"), os.path.join(PKG, "csrc", "dn_work.h"),
            os.path.join(ROOT, "include", "deltanet.h")]
 ARCH = "gfx950"

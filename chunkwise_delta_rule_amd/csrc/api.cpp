@@ -71,6 +71,10 @@ size_t ws_bytes_for(int B, int H, int dk, int dv, int G) {
     return (size_t)B * H * G * ((size_t)dk * dk + 2 * (size_t)dv * dk) * sizeof(float);
 }
 
+} // namespace
+
+namespace dn {
+
 // Dense forward, with (g != nullptr) or without the per-token decay. T counts
 // virtual steps: nh substeps per real token (Gated Delta Product; nh = 1
 // otherwise), so q, g and o hold T / nh real tokens per sequence.
@@ -140,6 +144,11 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
     err = dn::launch_chain(dtype, dk, dv, true, a, stream);
     return err == hipSuccess ? DN_OK : DN_ERR_HIP;
 }
+
+} // namespace dn
+
+namespace {
+using dn::fwd_dense;
 
 int fwd_varlen(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
                void *o, float *S_final, const int32_t *cu_seqlens, const int32_t *seq_order, int N, int total_T,

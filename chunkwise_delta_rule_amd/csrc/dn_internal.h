@@ -114,6 +114,14 @@ hipError_t launch_chain(int dtype, int dk, int dv, bool write_o, const ChainArgs
 // contract as launch_chain, 512 threads per workgroup.
 hipError_t launch_chain_bf16(int dk, int dv, bool write_o, const ChainArgs &a, hipStream_t stream);
 
+// The dense forward behind deltanet_fwd, deltanet_gated_fwd (g != nullptr)
+// and deltanet_gdp_fwd (nh > 1; T counts virtual steps): argument checks,
+// group resolution and the launches, with the caller's workspace. Returns a
+// DN_* status of include/deltanet.h.
+int fwd_dense(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
+              void *o, float *S_final, int B, int H, int T, int nh, int dk, int dv, int chunk, int dtype,
+              int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 // Enqueue the prefix composition S_{g+1} = S_g P_g + Q_g for g = 0..G-2,
 // writing start states of groups 1..G-1 into ws_S.
 hipError_t launch_compose(int dk, int dv, const ChainArgs &a, hipStream_t stream);

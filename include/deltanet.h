@@ -351,6 +351,24 @@ int deltanet_gdp_bwd(const void *q, const void *k, const void *v, const void *be
 size_t deltanet_gdp_bwd_workspace_bytes(int B, int H, int T, int n_h, int dk, int dv, int chunk);
 
 /*
+ * deltanet_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation). The context-parallel workspace lives in a fixed
+ * device array of the library, DN_NOALLOC_SCRATCH_BYTES (32 MiB) per device,
+ * held from the first call on a device until the process ends; the call
+ * itself allocates nothing. Semantics, layouts and errors as deltanet_fwd;
+ * a shape and cp_groups whose deltanet_workspace_bytes exceeds
+ * DN_NOALLOC_SCRATCH_BYTES returns DN_ERR_WORKSPACE before anything is
+ * enqueued (cp_groups = 1 needs no workspace at any size). Every call on one
+ * device shares that array: calls that overlap in time on one device (other
+ * streams, other threads) race and must be serialised by the caller.
+ */
+#define DN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int deltanet_fwd_noalloc(const void *q, const void *k, const void *v, const void *beta,
+                         const float *S0, void *o, float *S_final, int B, int H, int T,
+                         int dk, int dv, int chunk, int dtype, int cp_groups, hipStream_t stream);
+
+/*
  * Bytes of workspace deltanet_fwd (or deltanet_gated_fwd, deltanet_gdp_fwd,
  * deltanet_kda_fwd) needs for this
  * shape and cp_groups (0 means the library's choice on the current device).

@@ -323,3 +323,21 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises((ValueError, TypeError)):
         dn.deltanet_fwd(x, x, x, torch.zeros(1, 4, 1))
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_array(lib):
+    # 8 x 16 heads of T = 131072 in 16 groups need 403 MB of workspace, more than
+    # the fixed 32 MiB array: refused before anything touches the device
+    vp = ctypes.c_void_p
+    need = dn.deltanet_workspace_bytes(8, 16, 131072, 128, 128, 64, 16)
+    assert need > 32 << 20
+    st = lib.deltanet_fwd_noalloc(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE), None, 8, 16, 131072,
+                                  128, 128, 64, 1, 16, None)
+    assert st == DN_ERR_WORKSPACE
+    # invalid shapes keep the forward's own status
+    st = lib.deltanet_fwd_noalloc(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE), None, 1, 1, 128,
+                                  96, 128, 64, 1, 1, None)
+    assert st == DN_ERR_UNSUPPORTED
+    st = lib.deltanet_fwd_noalloc(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE), None, 1, 1, 128,
+                                  128, 128, 32, 1, 1, None)
+    assert st == DN_ERR_UNSUPPORTED
