@@ -166,16 +166,33 @@ __device__ inline void fwd_subst(float (&x)[16], float (&arow)[16]) {
 
 // Element offsets inside the LDS buffers. K, Q: [64][DK]; T^T, V tile:
 // [64][64]. The 8-element (16-byte) unit u of row r is stored at unit
-// u ^ swz(r).
+// u ^ swz(r). LDS reads are served over 64 banks (16 lanes per pass for
+// 16-byte reads, 32 for 8-byte and transposing reads) but writes over 32
+// banks (8 lanes per pass for 16-byte writes, 16 for 8-byte ones); every
+// layout below keeps both free of bank conflicts.
 template <int DK> __device__ inline int kswz(int r) {
-    if constexpr (DK == 128) // row bits 0,1,2,3 -> unit bits 0,2,3,1
-        return (r & 1) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 1);
-    else // 8 units per row: row bits 1,2,3 -> unit bits 0,2,1
-        return ((r >> 1) & 1) | (((r >> 2) & 1) << 2) | (((r >> 3) & 1) << 1);
+    // DK = 128: unit bits 0-2 = row bits 0-2 (eight consecutive rows written
+    // at one unit hit eight different 32-bank positions) and unit bit 3 =
+    // row bit 1 ^ row bit 3 (rows two apart never share a unit pair, which
+    // keeps the transposing reads of K^T apart; all 16 rows stay distinct)
+    if constexpr (DK == 128)
+        return (r & 7) | ((((r >> 1) ^ (r >> 3)) & 1) << 3);
+    else // 8 units per row: unit = (b0 ^ b3) ^ 3 b2 ^ 4 b1 for row bits b0..b3
+        return ((r ^ (r >> 3)) & 1) ^ (((r >> 2) & 1) * 3) ^ (((r >> 1) & 1) << 2);
 }
 template <int DK> __device__ inline int koff(int r, int c) { return r * DK + (((c >> 3) ^ kswz<DK>(r)) << 3) + (c & 7); }
 __device__ inline int s64swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 __device__ inline int s64off(int r, int c) { return r * 64 + (((c >> 3) ^ s64swz(r)) << 3) + (c & 7); }
+// T^T: as the 64 x 64 layout, with the two 8-byte halves of every unit
+// swapped in odd rows (so that the 8-byte writes of 16 rows at one column
+// group fill all 32 write banks).
+__device__ inline int ttoff(int r, int c) { return s64off(r, c) ^ (4 * (r & 1)); }
+// X ([64][16] fp32, four 16-byte units per row) and N^T ([64][16] bf16, two
+// units per row): unit u of row r at u ^ xswz(r) (resp. u ^ nswz(r)).
+__device__ inline int xswz(int r) { return ((r >> 2) & 3) ^ (((r >> 1) & 1) << 1); }
+__device__ inline int xoff(int r, int u) { return 16 * r + 4 * (u ^ xswz(r)); }
+__device__ inline int nswz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+__device__ inline int noff(int r, int c) { return 16 * r + ((((c >> 3) ^ nswz(r)) << 3) | (c & 7)); }
 // First dk of the 4-run held by lane group g of state tile m (delta above).
 __device__ inline int dk_of(int m, int g) { return 32 * (m >> 1) + 8 * g + 4 * ((m + g) & 1); }
 // P operand fragment of token tile t and 32-token block s <= t / 2 (0..5).
@@ -500,7 +517,7 @@ __device__ inline bf16x8 chain_fetch(int i, const ChainSrc<DK, WO> &src, int lan
     if (k == CS::kZ) {
         // T row 16t + c16 = column of T^T, over tokens 32s + {4g + e, 16 + 4g + e}
         const int t = CS::tT(j), row = 32 * CS::tS(j) + 4 * g + (c16 >> 2), col = 16 * t + 4 * (c16 & 3);
-        return cat8(tr4(src.T + s64off(row, col)), tr4(src.T + s64off(row + 16, col)));
+        return cat8(tr4(src.T + ttoff(row, col)), tr4(src.T + ttoff(row + 16, col)));
     }
     if (k == CS::kOp) return ld8(src.P + 512 * j + 8 * lane);
     return k_trfrag<DK>(src.K, j / 2, j % 2, g, c16);
@@ -691,7 +708,7 @@ template <int DK, bool GATED> __device__ inline void gram_tiles(const WsBufs<DK>
     float *X = bf.X(c);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-        *reinterpret_cast<f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g) = dot_tile<DK>(k.f[b], k.f[b]);
+        *reinterpret_cast<f32x4 *>(X + xoff(16 * b + c16, g)) = dot_tile<DK>(k.f[b], k.f[b]);
     const float *Bs = bf.B(c);
     const float b1 = Bs[16 + c16], b2 = Bs[32 + c16], b3 = Bs[48 + c16];
     // row factors of A_ac: beta of row token 16a + j, times the decay when gated
@@ -731,12 +748,13 @@ template <int DK, bool GATED> __device__ inline void gram_tiles(const WsBufs<DK>
 // Gated: entry (j, i) of A_bb also takes the decay exp(gamma_j - gamma_i).
 template <int DK, bool GATED> __device__ inline void diag_solve(const WsBufs<DK> &bf, int c, int g, int c16) {
     using LY = WsLds<DK>;
-    float *Xr = bf.X(c) + (16 * g + c16) * LY::LX;
+    float *X = bf.X(c);
+    const int xr = 16 * g + c16;
     const float br = bf.B(c)[16 * g + c16];
     float arow[16];
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
-        f32x4 t = *reinterpret_cast<const f32x4 *>(Xr + 4 * j4);
+        f32x4 t = *reinterpret_cast<const f32x4 *>(X + xoff(xr, j4));
         if constexpr (GATED) {
             const float *Gs = bf.G(c) + 16 * g;
             t *= exp2v(Gs[c16] - *reinterpret_cast<const f32x4 *>(Gs + 4 * j4)); // masked entries unused
@@ -749,15 +767,15 @@ template <int DK, bool GATED> __device__ inline void diag_solve(const WsBufs<DK>
     for (int i = 0; i < 16; ++i) x[i] = (i == c16) ? 1.f : 0.f;
     fwd_subst(x, arow);
     // x[i] = N_gg[i][c]
-    __bf16 *Nr = bf.N(c) + (16 * g + c16) * LY::LN;
+    __bf16 *N = bf.N(c);
     const f32x4 x0 = {x[0], x[1], x[2], x[3]}, x1 = {x[4], x[5], x[6], x[7]};
     const f32x4 x2 = {x[8], x[9], x[10], x[11]}, x3 = {x[12], x[13], x[14], x[15]};
-    st8(Nr, cvt8(x0, x1));
-    st8(Nr + 8, cvt8(x2, x3));
-    *reinterpret_cast<f32x4 *>(Xr + 0) = x0 * br;
-    *reinterpret_cast<f32x4 *>(Xr + 4) = x1 * br;
-    *reinterpret_cast<f32x4 *>(Xr + 8) = x2 * br;
-    *reinterpret_cast<f32x4 *>(Xr + 12) = x3 * br;
+    st8(N + noff(xr, 0), cvt8(x0, x1));
+    st8(N + noff(xr, 8), cvt8(x2, x3));
+    *reinterpret_cast<f32x4 *>(X + xoff(xr, 0)) = x0 * br;
+    *reinterpret_cast<f32x4 *>(X + xoff(xr, 1)) = x1 * br;
+    *reinterpret_cast<f32x4 *>(X + xoff(xr, 2)) = x2 * br;
+    *reinterpret_cast<f32x4 *>(X + xoff(xr, 3)) = x3 * br;
 }
 
 // Wave 5: T^T of chunk c. Off-diagonal blocks N_ab = -N_aa sum_{c=b}^{a-1}
@@ -771,21 +789,21 @@ template <int DK> __device__ inline void off_solve(const WsBufs<DK> &bf, int c, 
     const bf16x4 A10 = ld4(As + 0 * 256), A20 = ld4(As + 1 * 256), A21 = ld4(As + 2 * 256);
     const bf16x4 A30 = ld4(As + 3 * 256), A31 = ld4(As + 4 * 256), A32 = ld4(As + 5 * 256);
     // B fragments of the diagonal blocks: N_bb[4g + e][c16] = N^T[16b + c16][4g + e]
-    const bf16x4 n00 = ld4(Ns + (c16)*LY::LN + 4 * g);
-    const bf16x4 n11 = ld4(Ns + (16 + c16) * LY::LN + 4 * g);
-    const bf16x4 n22 = ld4(Ns + (32 + c16) * LY::LN + 4 * g);
+    const bf16x4 n00 = ld4(Ns + noff(c16, 4 * g));
+    const bf16x4 n11 = ld4(Ns + noff(16 + c16, 4 * g));
+    const bf16x4 n22 = ld4(Ns + noff(32 + c16, 4 * g));
     // A fragments (rows) of the diagonal blocks: N_aa[c16][4g + e] = N^T[16a + 4g + e][c16]
     const int kq = c16 >> 2, kr = c16 & 3;
-    const bf16x4 r11 = tr4(Ns + (16 + 4 * g + kq) * LY::LN + 4 * kr);
-    const bf16x4 r22 = tr4(Ns + (32 + 4 * g + kq) * LY::LN + 4 * kr);
-    const bf16x4 r33 = tr4(Ns + (48 + 4 * g + kq) * LY::LN + 4 * kr);
+    const bf16x4 r11 = tr4(Ns + noff(16 + 4 * g + kq, 4 * kr));
+    const bf16x4 r22 = tr4(Ns + noff(32 + 4 * g + kq, 4 * kr));
+    const bf16x4 r33 = tr4(Ns + noff(48 + 4 * g + kq, 4 * kr));
     const float be0 = Bs[c16], be1 = Bs[16 + c16], be2 = Bs[32 + c16];
     // T^T[16b + c16][16b + 4g + e] = T_bb[4g + e][c16], from row 16b + c16 of X
     f32x4 td[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) td[b] = *reinterpret_cast<const f32x4 *>(X + (16 * b + c16) * LY::LX + 4 * g);
+    for (int b = 0; b < 4; ++b) td[b] = *reinterpret_cast<const f32x4 *>(X + xoff(16 * b + c16, g));
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    auto put = [&](int b, int a, f32x4 tab) { st4(Tt + s64off(16 * b + c16, 16 * a + 4 * g), cvt4(tab)); };
+    auto put = [&](int b, int a, f32x4 tab) { st4(Tt + ttoff(16 * b + c16, 16 * a + 4 * g), cvt4(tab)); };
     // column block 0
     const f32x4 n10 = -mfma16(r11, cvt4(mfma16(A10, n00, z)), z);
     const bf16x4 f10 = cvt4(n10);
@@ -843,11 +861,18 @@ __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c,
         }
         p[i] = cvt4(-acc);
     }
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const int pa = kPA[half][i], pc = kPC[half][i];
-        // token 16pc + 4g + e is slot 4 (pc % 2) + e of fragment (pa, pc / 2), lane 16g + c
-        st4(Pb + 512 * pfrag(pa, pc >> 1) + 4 * (pc & 1), p[i]);
+    // token 16pc + 4g + e is slot 4 (pc % 2) + e of fragment (pa, pc / 2),
+    // lane 16g + c: each fragment is written whole (16 bytes per lane), the
+    // tiles right of the diagonal block as zeros
+    const bf16x4 z4 = {};
+    if (half == 0) {
+        st8(Pb + 512 * pfrag(0, 0), cat8(p[0], z4));
+        st8(Pb + 512 * pfrag(3, 0), cat8(p[1], p[2]));
+        st8(Pb + 512 * pfrag(3, 1), cat8(p[3], p[4]));
+    } else {
+        st8(Pb + 512 * pfrag(1, 0), cat8(p[0], p[1]));
+        st8(Pb + 512 * pfrag(2, 0), cat8(p[2], p[3]));
+        st8(Pb + 512 * pfrag(2, 1), cat8(p[4], z4));
     }
 }
 
@@ -929,7 +954,9 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
 #pragma unroll
                         for (int p = 0; p < 8; ++p) {
                             const int piece = 64 * p + lane, row = piece >> 3, c8 = piece & 7;
-                            st8(dst + row * kChunk + 8 * c8, ld8(Tt + s64off(row, 8 * c8)));
+                            bf16x8 x = ld8(Tt + s64off(row, 8 * c8));
+                            if (row & 1) x = __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3);
+                            st8(dst + row * kChunk + 8 * c8, x);
                         }
                     }
                 }
