@@ -341,3 +341,24 @@ def test_noalloc_rejects_a_workspace_beyond_its_array(lib):
     st = lib.deltanet_fwd_noalloc(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE), None, 1, 1, 128,
                                   128, 128, 32, 1, 1, None)
     assert st == DN_ERR_UNSUPPORTED
+
+
+def prototype(name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    return [" ".join(p.split()) for p in m.group(1).split(",")]
+
+
+def test_boundary_signatures_as_documented():
+    # the departures from the proposed boundary that the design notes list
+    fwd = prototype("deltanet_fwd")
+    assert fwd[:7] == ["const void *q", "const void *k", "const void *v", "const void *beta", "const float *S0",
+                       "void *o", "float *S_final"]
+    assert "int dtype" in fwd and "int cp_groups" in fwd and "void *workspace" in fwd
+    var = prototype("deltanet_fwd_varlen")
+    assert "const int32_t *cu_seqlens" in var and "const int32_t *seq_order" in var
+    assert not any("workspace" in p for p in var)
+    assert "int dtype" in var
+    assert not any("dn_dtype_t" in p for name in ("deltanet_fwd", "deltanet_fwd_varlen", "deltanet_gated_fwd")
+                   for p in prototype(name))
