@@ -1671,16 +1671,55 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
 // Staging still moves 64-token chunks. Four waves; each wave holds 16 state
 // rows, computes the Gram/score tiles and the solve of one sub-chunk, then
 // runs the four sub-chunks' products for its rows in order.
-// Limit: exp(-gamma) must stay finite, i.e. every sum of 16 consecutive
-// log decays of one channel must exceed about -87 (g >= -5.4 suffices).
+// Strong decay: Kr's factor exp(-gamma) is only safe while |gamma| stays
+// moderate. A sub-chunk in which some channel's prefix sum leaves
+// [-kKdaLim, kKdaLim] (base 2) takes L and A from an exact path instead:
+// every entry k_l . (exp(gamma_l - gamma_m) * k_m) (or q_l . ...) is formed
+// with the decay factor of the pair itself, which lies in (0, 1] for
+// decays, each scaling thread adding its own channels and a 16-lane row
+// reduction adding the threads. Kl, Ql, Kf and exp(gamma_16) only ever carry
+// later-minus-earlier differences, so the chain is exact for any decay.
 // ---------------------------------------------------------------------------
 template <int DK> struct KdaLds {
     using L = Ld<__bf16, DK>;
     static constexpr size_t oK = 0, oQ = oK + L::szK, oKr = oQ + L::szK, oKf = oKr + L::szK;
     static constexpr size_t oE = oKf + L::szK;                       // exp(gamma_16), fp32 [4][DK]
     static constexpr size_t oV = oE + sizeof(float) * 4 * DK, oB = oV + L::szV, oA = oB + 256;
-    static constexpr size_t oT = oA + L::szA, oN = oT + L::szT, oP = oN + L::szN, total = oP + L::szT;
+    static constexpr size_t oT = oA + L::szA, oN = oT + L::szT, oP = oN + L::szN;
+    // exact path: per sub-chunk, row partial sums of the 120 entries of L and
+    // the 136 entries of A ([4][256][4] fp32), and the per-sub-chunk flags
+    static constexpr size_t oX = oP + L::szT, oF = oX + sizeof(float) * 4 * 256 * 4, total = oF + 16;
 };
+
+// Compile-time loop: f(Int<I>{}) for I = B..E-1 (step indices stay constants).
+template <int I> struct Int {
+    static constexpr int value = I;
+};
+template <int B, int E, typename Fn> __device__ inline void static_for(Fn &&f) {
+    if constexpr (B < E) {
+        f(Int<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Prefix-sum bound of the factored path (base 2): Kr = K 2^-gamma and
+// Kl = K 2^gamma stay normal and finite in bf16 while |gamma| <= kKdaLim.
+constexpr float kKdaLim = 96.f;
+
+// Inclusive sum within each 16-lane row (lanes shifted in from outside the
+// row add 0); lane 15 of a row holds the row's total.
+__device__ inline float row_scan16(float x) {
+    const int zero = 0;
+#define DN_ROW_SHR(N)                                                                                          \
+    x += __builtin_bit_cast(                                                                                   \
+        float, __builtin_amdgcn_update_dpp(zero, __builtin_bit_cast(int, x), 0x110 + (N), 0xF, 0xF, false))
+    DN_ROW_SHR(1);
+    DN_ROW_SHR(2);
+    DN_ROW_SHR(4);
+    DN_ROW_SHR(8);
+#undef DN_ROW_SHR
+    return x;
+}
 
 template <int DK, int DV, bool WO>
 __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const ChainArgs a) {
@@ -1700,6 +1739,8 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const ChainArgs a) 
     float *Bs = reinterpret_cast<float *>(smem + LY::oB), *As = reinterpret_cast<float *>(smem + LY::oA);
     E *TsT = reinterpret_cast<E *>(smem + LY::oT), *NsT = reinterpret_cast<E *>(smem + LY::oN);
     E *Ps = reinterpret_cast<E *>(smem + LY::oP);
+    float *Xp = reinterpret_cast<float *>(smem + LY::oX); // exact path: [j][entry][row] partial sums
+    int *exact = reinterpret_cast<int *>(smem + LY::oF);  // exact path taken by sub-chunk j
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     // the work item: a token range of one (sequence, head), 64 state rows,
@@ -1774,10 +1815,12 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const ChainArgs a) 
                     ql[l] = *reinterpret_cast<const bf16x2 *>(Qs + row * L::K + d);
                 }
                 f32x2 gam[16], acc = {0.f, 0.f};
+                bool wide = false; // a prefix sum outside the factored path's range
 #pragma unroll
                 for (int l = 0; l < 16; ++l) {
                     if (16 * j + l < nval) acc += gq[l] * 1.44269504088896340736f;
                     gam[l] = acc;
+                    wide |= !(fabsf(acc[0]) <= kKdaLim && fabsf(acc[1]) <= kKdaLim);
                 }
                 const f32x2 e16 = {__builtin_amdgcn_exp2f(acc[0]), __builtin_amdgcn_exp2f(acc[1])};
 #pragma unroll
@@ -1786,7 +1829,8 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const ChainArgs a) 
                     const f32x2 kv = {(float)kl[l][0], (float)kl[l][1]}, qv = {(float)ql[l][0], (float)ql[l][1]};
                     const f32x2 el = {__builtin_amdgcn_exp2f(gam[l][0]), __builtin_amdgcn_exp2f(gam[l][1])};
                     const f32x2 er = {__builtin_amdgcn_exp2f(-gam[l][0]), __builtin_amdgcn_exp2f(-gam[l][1])};
-                    const f32x2 ef = e16 * er; // exp(gamma_16 - gamma), <= 1
+                    // exp(gamma_16 - gamma) <= 1, from the difference itself
+                    const f32x2 ef = {__builtin_amdgcn_exp2f(acc[0] - gam[l][0]), __builtin_amdgcn_exp2f(acc[1] - gam[l][1])};
                     const f32x2 a1 = -(kv * el), a2 = qv * el, a3 = kv * er, a4 = kv * ef;
                     *reinterpret_cast<bf16x2 *>(Ks + row * L::K + d) = bf16x2{(__bf16)a1[0], (__bf16)a1[1]};
                     *reinterpret_cast<bf16x2 *>(Qs + row * L::K + d) = bf16x2{(__bf16)a2[0], (__bf16)a2[1]};
@@ -1794,13 +1838,59 @@ __global__ __launch_bounds__(kThreads) void kda_chain_kernel(const ChainArgs a) 
                     *reinterpret_cast<bf16x2 *>(Kf + row * L::K + d) = bf16x2{(__bf16)a4[0], (__bf16)a4[1]};
                 }
                 *reinterpret_cast<f32x2 *>(E16 + j * DK + d) = e16;
+                // Exact path, wave-uniform: taken by every sub-chunk of this
+                // wave when any of them needs it (all lanes of the wave are
+                // scaling threads). Lane (row rw, c) of sub-chunk j adds its
+                // two channels of every entry; the 16-lane row scan leaves the
+                // row's sum in its lane 15, which stores it.
+                const bool wave_exact = __builtin_amdgcn_ballot_w64(wide) != 0;
+                constexpr int RPS = NP / 16; // 16-lane rows per sub-chunk
+                if (lane == 0 || lane == 32) exact[j] = wave_exact ? 1 : 0;
+                if (wave_exact) {
+                    float *xp = Xp + j * 256 * 4 + ((lane >> 4) % RPS);
+                    const bool last = c16 == 15;
+                    static_for<0, 16>([&](auto lc) {
+                        constexpr int l = decltype(lc)::value;
+                        const f32x2 kv = {(float)kl[l][0], (float)kl[l][1]}, qv = {(float)ql[l][0], (float)ql[l][1]};
+                        static_for<0, l + 1>([&](auto mc) {
+                            constexpr int m = decltype(mc)::value;
+                            const f32x2 km = {(float)kl[m][0], (float)kl[m][1]};
+                            const f32x2 t = km * f32x2{__builtin_amdgcn_exp2f(gam[l][0] - gam[m][0]),
+                                                       __builtin_amdgcn_exp2f(gam[l][1] - gam[m][1])};
+                            const float sa = row_scan16(qv[0] * t[0] + qv[1] * t[1]);
+                            if (last) xp[4 * (120 + l * (l + 1) / 2 + m)] = sa; // A entry (l, m)
+                            if constexpr (m < l) {
+                                const float sl = row_scan16(kv[0] * t[0] + kv[1] * t[1]);
+                                if (last) xp[4 * (l * (l - 1) / 2 + m)] = sl; // L entry (l, m)
+                            }
+                        });
+                    });
+                }
             }
         }
         if (r + 1 < NC) load_chunk(r + 1);
         __syncthreads();
         // Sub-chunk w: L = Kl Kr^T (strictly lower, times beta of the row) and
-        // A = Ql Kr^T. Ks holds -Kl, so the products give -L.
-        {
+        // A = Ql Kr^T. Ks holds -Kl, so the products give -L. On the exact
+        // path the entries are the row sums of the scaling threads instead.
+        if (exact[w]) {
+            constexpr int RPS = (DK / 2) / 16;
+            const float *xp = Xp + w * 256 * 4;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int idx = 64 * p + lane, l = idx >> 4, m = idx & 15, row = 16 * w + l;
+                float sl = 0.f, sa = 0.f;
+                if (m <= l) {
+#pragma unroll
+                    for (int q = 0; q < RPS; ++q) {
+                        sa += xp[4 * (120 + l * (l + 1) / 2 + m) + q];
+                        if (m < l) sl += xp[4 * (l * (l - 1) / 2 + m) + q];
+                    }
+                }
+                As[row * L::A + 16 * w + m] = m < l ? Bs[row] * sl : 0.f;
+                Ps[row * L::T + 16 * w + m] = TR::fromf(m <= l ? sa : 0.f);
+            }
+        } else {
             f32x4 lt = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NMT; m += 2) { // 16x16x32 products over dk blocks m, m + 1

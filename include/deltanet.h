@@ -205,9 +205,11 @@ int deltanet_decode_step(const void *q, const void *k, const void *v, const void
  * with a_t = exp(g_t) elementwise (state transposed as above).
  *   g : [B, T, H, dk] float32 log decays, 16-byte aligned, required when T > 0.
  * Evaluated with that section's complete per-chunk algorithm on sub-chunks of
- * 16 tokens (exact for any chunk size); the in-sub-chunk growth factor
- * exp(-sum of g over up to 16 tokens) must stay finite in fp32, which holds
- * for g >= -5.4. Other arguments as in deltanet_fwd, including context
+ * 16 tokens (exact for any chunk size). Any decay a in (0, 1] per channel is
+ * supported: where a channel decays by more than 2^96 within a sub-chunk, the
+ * in-sub-chunk products take each pair's own decay factor instead of the
+ * factored form (exact, slower; decays below fp32's range act as a reset).
+ * Other arguments as in deltanet_fwd, including context
  * parallelism (cp_groups, with deltanet_workspace_bytes of workspace): each
  * group's transition is the same kernel run from the identity with no values,
  * which the per-channel decay leaves a linear map of the entering state.
