@@ -194,11 +194,14 @@ int fwd_varlen(const void *q, const void *k, const void *v, const void *beta, co
 namespace {
 size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
 
-// Workspace bytes per chunk slot of the backward pass: the state entering the
-// chunk and the per-value-tile partial sums (fp32), then T^T of the chunk (bf16).
+// Workspace bytes per chunk slot of the backward pass. DeltaNet: the state
+// entering the chunk and the gradient of the state leaving it (bf16), then
+// T^T of the chunk (bf16). The gated passes: the state entering the chunk and
+// the per-value-tile partial sums (fp32), then T^T of the chunk (bf16).
 size_t bwd_slot_bytes(int dk, int dv, bool gated) {
-    return ((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_stride(dk, gated)) * sizeof(float) +
-           (size_t)dn::kChunk * dn::kChunk * sizeof(__bf16);
+    const size_t tt = (size_t)dn::kChunk * dn::kChunk * sizeof(__bf16);
+    if (!gated) return 2 * (size_t)dv * dk * sizeof(__bf16) + tt;
+    return ((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_stride(dk, true)) * sizeof(float) + tt;
 }
 
 // Chunk slots of a packed batch, bounded without reading the lengths:
@@ -208,8 +211,10 @@ size_t varlen_max_slots(int N, int total_T, int H) {
 }
 
 // The backward pass, dense (cu_seqlens NULL: B sequences of T tokens) or
-// packed (B = N sequences, T = total tokens). Workspace: [S entering each
-// chunk | partial sums | T^T of each chunk | chunk offsets (varlen)].
+// packed (B = N sequences, T = total tokens). Workspace, DeltaNet: [S entering
+// each chunk (bf16) | dS leaving each chunk (bf16) | T^T of each chunk | chunk
+// offsets (varlen)]; gated: [S entering each chunk (fp32) | partial sums |
+// T^T of each chunk | chunk offsets (varlen)].
 int bwd_common(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
                const void *dO, const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dg,
                float *dS0, const int32_t *cu_seqlens, const int32_t *seq_order, int B, int H, int T, int nh, int dk,
@@ -242,9 +247,18 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     }
     const size_t slots = varlen ? varlen_max_slots(B, T, H) : (size_t)B * H * NC;
     if (slots > (size_t)INT32_MAX) return DN_ERR_UNSUPPORTED; // one finishing workgroup per chunk slot
-    float *Sck = static_cast<float *>(workspace);
-    float *part = Sck + slots * dv * dk;
-    __bf16 *Tck = reinterpret_cast<__bf16 *>(part + slots * (dv / dn::kRows) * dn::bwd_part_stride(dk, g != nullptr));
+    const bool gated = g != nullptr;
+    float *Sck = nullptr, *part = nullptr;
+    __bf16 *S16 = nullptr, *G16 = nullptr, *Tck;
+    if (gated) {
+        Sck = static_cast<float *>(workspace);
+        part = Sck + slots * dv * dk;
+        Tck = reinterpret_cast<__bf16 *>(part + slots * (dv / dn::kRows) * dn::bwd_part_stride(dk, true));
+    } else {
+        S16 = static_cast<__bf16 *>(workspace);
+        G16 = S16 + slots * dv * dk;
+        Tck = G16 + slots * dv * dk;
+    }
     int32_t *cb = varlen ? reinterpret_cast<int32_t *>(Tck + slots * dn::kChunk * dn::kChunk) : nullptr;
     if (varlen && dn::launch_chunk_base(cu_seqlens, B, cb, stream) != hipSuccess) return DN_ERR_HIP;
     // pass 1: the forward chain, keeping the state entering every chunk and its T
@@ -256,6 +270,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     a.g = g;
     a.S0 = S0;
     a.S_chunks = Sck;
+    a.S_chunks16 = S16;
     a.T_chunks = Tck;
     a.chunk_base = cb;
     a.cu_seqlens = cu_seqlens;
@@ -268,7 +283,9 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     a.n_units = B * H;
     a.n_tiles = dv / dn::kRows;
     if (dn::launch_chain(dtype, dk, dv, false, a, stream) != hipSuccess) return DN_ERR_HIP;
-    // passes 2 and 3
+    // DeltaNet: the reverse chain of the state gradients (with dv and dS0),
+    // then every chunk's dq, dk, dbeta in parallel. Gated: the backward chain
+    // with per-tile partial sums, then the finishing pass.
     dn::BwdArgs b = {};
     b.q = q;
     b.k = k;
@@ -277,6 +294,8 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     b.dO = dO;
     b.dS_final = dS_final;
     b.S_chunks = Sck;
+    b.S_chunks16 = S16;
+    b.G_chunks = G16;
     b.T_chunks = Tck;
     b.part = part;
     b.dS0 = dS0;
@@ -296,7 +315,13 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     b.NC = NC;
     b.n_tiles = dv / dn::kRows;
     b.max_slots = (int64_t)slots;
-    return dn::launch_bwd(dk, dv, b, stream) == hipSuccess ? DN_OK : DN_ERR_HIP;
+    if (gated) {
+        if (dn::launch_bwd(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+    } else {
+        if (dn::launch_bwd_rev(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+        if (dn::launch_bwd_grad(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+    }
+    return DN_OK;
 }
 } // namespace
 

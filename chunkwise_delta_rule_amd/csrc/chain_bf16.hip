@@ -663,6 +663,11 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
             ck.transposed_out = false;
             ws_state_out<DK>(Sacc, ck, cw, g, c16);
         }
+        if (!WO && r >= 0 && wk.Schunks16) { // the same in bf16 ([dv][dk] rows)
+            __bf16 *so = wk.Schunks16 + (int64_t)r * DV * DK + (16 * cw + c16) * DK;
+#pragma unroll
+            for (int m = 0; m < DK / 16; ++m) st4(so + dk_of(m, g), cvt4(Sacc[m]));
+        }
         if (r >= 0)
             consumer_chain<DK, WO, GATED>(bf, r, Sacc, WO ? og + (GATED ? 0 : (int64_t)r * kChunk * sv) : nullptr,
                                           sv, min(kChunk, wk.len - r * kChunk), sb, has_v, cw, lane, g, c16);
@@ -1022,6 +1027,402 @@ __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Reverse chain of the DeltaNet backward pass.
+//
+// The pages give no backward pass; this is the chain rule on the per-chunk
+// algorithm above. For a chunk with upstream dO and dS' (the gradient of the
+// state after the chunk):
+//   dZ = P^T dO + K dS'^T,  dY = T^T dZ,  dV = dY,
+//   dS = dS' + dO^T Q - dY^T K.
+// The state gradient enters only through K dS'^T, so this is the forward's
+// chain run backwards with T^T for T, P^T dO for V and one more product
+// (dO^T Q) in the update. Rows of dS (value index) are independent, so 64-row
+// tiles split it as in the forward. T^T of each chunk comes from the forward
+// pass; P is formed here. The kernel writes dV, the dS' of every chunk
+// (bf16, for the chunk-parallel gradient kernel) and dS0.
+//
+// Waves: 0-3 carry 16 rows of dS each in fp32 registers (accumulator layout
+// of the forward's state, G[m][i] = dS[row][delta(m, g, i)]); wave 4 stages
+// T^T, wave 5 the dO tile, waves 6-7 stage K and Q and form P^T as ready-made
+// operand fragments. Step i of the loop is chunk NC - 1 - i; one barrier per
+// step; producers work one step (T^T, dO, Q, P^T) or two (K) ahead.
+// ---------------------------------------------------------------------------
+template <int DK> struct RevLds {
+    static constexpr size_t szK = sizeof(__bf16) * 64 * DK;
+    static constexpr size_t sz64 = sizeof(__bf16) * 64 * 64;
+    static constexpr size_t szP = sizeof(__bf16) * 6 * 64 * 8;
+    static constexpr size_t oK = 0;             // K x3, step i in buffer (i + 3) % 3
+    static constexpr size_t oQ = oK + 3 * szK;  // Q x2 (step parity)
+    static constexpr size_t oT = oQ + 2 * szK;  // T^T x2, row-major (64 x 64 layout)
+    static constexpr size_t oP = oT + 2 * sz64; // P^T operand fragments x2
+    static constexpr size_t oD = oP + 2 * szP;  // dO tile x2 (64 tokens x 64 values)
+    static constexpr size_t total = oD + 2 * sz64;
+};
+template <int DK> struct RevBufs {
+    using LY = RevLds<DK>;
+    unsigned char *base;
+    __device__ inline __bf16 *K(int i) const { return (__bf16 *)(base + LY::oK + ((i + 3) % 3) * LY::szK); }
+    __device__ inline __bf16 *Q(int i) const { return (__bf16 *)(base + LY::oQ + (i & 1) * LY::szK); }
+    __device__ inline __bf16 *Tt(int i) const { return (__bf16 *)(base + LY::oT + (i & 1) * LY::sz64); }
+    __device__ inline __bf16 *P(int i) const { return (__bf16 *)(base + LY::oP + (i & 1) * LY::szP); }
+    __device__ inline __bf16 *D(int i) const { return (__bf16 *)(base + LY::oD + (i & 1) * LY::sz64); }
+};
+
+// What one reverse-chain workgroup works on: a (sequence, head) unit and 64
+// value rows, its token range and its chunk slots.
+struct RevWork {
+    int64_t tok0, slot0, su;
+    int len, h, row0;
+};
+__device__ inline RevWork rev_work(const BwdArgs &a) {
+    int u, tau;
+    map_block(blockIdx.x, a.B * a.H, a.n_tiles, u, tau); // the tiles of a unit share an XCD
+    const int rank = u / a.H;
+    RevWork wk;
+    wk.h = u - rank * a.H;
+    wk.row0 = 64 * tau;
+    if (a.cu_seqlens) {
+        const int n = a.seq_order ? a.seq_order[rank] : rank;
+        wk.tok0 = a.cu_seqlens[n];
+        wk.len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+        wk.su = (int64_t)n * a.H + wk.h;
+        wk.slot0 = (int64_t)a.chunk_base[n] * a.H + (int64_t)wk.h * ((wk.len + kChunk - 1) / kChunk);
+    } else {
+        wk.tok0 = (int64_t)rank * a.T;
+        wk.len = a.T;
+        wk.su = u;
+        wk.slot0 = (int64_t)u * a.NC;
+    }
+    return wk;
+}
+
+// Chunk of step j (clamped into the sequence: loads past either end re-read
+// a valid chunk whose ring slot is never consumed).
+__device__ inline int rev_chunk(int NC, int j) { return min(max(NC - 1 - j, 0), NC - 1); }
+
+// T^T of a chunk (64 x 64 bf16 row-major in the workspace) by the 64 lanes of
+// wave 4: lane l owns the 16-byte piece l % 8 of rows l / 8 + 8 p.
+struct TStager {
+    const __bf16 *tg; // T^T of chunk 0 of this unit
+    int lane;
+    bf16x8 r[2][8];
+    __device__ inline void init(const __bf16 *tg_, int lane_) {
+        tg = tg_;
+        lane = lane_;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int p = 0; p < 8; ++p) r[b][p] = bf16x8{};
+    }
+    template <int B> __device__ inline void load(int c) {
+        const __bf16 *t = tg + (int64_t)c * kChunk * kChunk + (lane / 8) * kChunk + 8 * (lane % 8);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) r[B][p] = ld8(t + 8 * p * kChunk);
+    }
+    template <int B> __device__ inline void write(__bf16 *Ts) const {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) st8(Ts + s64off(lane / 8 + 8 * p, 8 * (lane % 8)), r[B][p]);
+    }
+};
+
+// The dO tile (64 tokens x this workgroup's 64 values) by the 64 lanes of
+// wave 5, as the forward stages V: rows past the end are written as zeros.
+struct DStager {
+    const __bf16 *dt; // row rv0 of chunk 0, value column col
+    int64_t sv;
+    int len, rv0, col;
+    bf16x8 r[2][8];
+    int n[2];
+    __device__ inline void init(const __bf16 *dg, int64_t sv_, int len_, int lane) {
+        sv = sv_;
+        len = len_;
+        rv0 = lane / 8;
+        col = 8 * (lane % 8);
+        dt = dg + rv0 * sv + col;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            n[b] = 0;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) r[b][p] = bf16x8{};
+        }
+    }
+    template <int B> __device__ inline void load(int c) {
+        n[B] = rows_of(len, c);
+        const __bf16 *b = dt + (int64_t)c * kChunk * sv;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int row = min(rv0 + 8 * p, n[B] - 1);
+            r[B][p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(row - rv0) * sv);
+        }
+    }
+    template <int B> __device__ inline void write(__bf16 *Ds) const {
+        const bf16x8 z = {};
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int row = rv0 + 8 * p;
+            st8(Ds + s64off(row, col), row < n[B] ? r[B][p] : z);
+        }
+    }
+};
+
+// Waves 6-7: P^T of a chunk as A-operand fragments of the consumer's
+// dZ = P^T dO products. Fragment (t, s) holds, in lane (g, c), row 16t + c
+// of P^T (column 16t + c of P) over the tokens 32s + {4g + e, 16 + 4g + e}
+// (the token order of the dO fragments), i.e. the tiles P[16pa + 4g + e][16pc + c]
+// for pc = t and pa = 2s, 2s + 1 in its two halves. The fragments are
+// (t, s) = (0,0) (0,1) (1,0) (1,1) (2,1) (3,1); blocks above the diagonal
+// (half 0 of (1,0) and of (3,1)) are zero and never written.
+__device__ constexpr int rev_frag(int t, int s) { return t < 2 ? 2 * t + s : t + 2; }
+template <int DK, int B>
+__device__ inline void pt_tiles(const RevBufs<DK> &bf, const QStage<DK> &q, int i, int half, int lane, int g, int c16) {
+    KRows<DK> k;
+    k_rows<DK>(k, bf.K(i), g, c16);
+    __bf16 *Pb = bf.P(i) + 8 * lane;
+#pragma unroll
+    for (int x = 0; x < 5; ++x) {
+        const int pa = kPA[half][x], pc = kPC[half][x];
+        const int qi = half ? pa - 1 : (pa == 3 ? 1 : 0);
+        // acc[e] = q_{16pa+4g+e} . k_{16pc+c} = P[16pa + 4g + e][16pc + c]
+        f32x4 acc = dot_tile<DK>(q.f[B][qi], k.f[pc]);
+        if (pa == pc) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e < c16) ? 0.f : acc[e];
+        }
+        st4(Pb + 512 * rev_frag(pc, pa >> 1) + 4 * (pa & 1), cvt4(acc));
+    }
+}
+
+// The consumer's products of one step, each with one LDS operand fragment:
+//   V  (j):     Y_t += PT_{t,s} DB_s                  6 steps (Y = dZ, from zero)
+//   Y  (t, kb): Y_t += K_{t,kb} GB_kb                 4 * DK/32 steps (GB = bf16(dS'))
+//   Q  (m, s):  G^T_m += Q^T_{m,s} DB_s               2 * DK/16 steps, split around Z
+//   Z  (j):     Z_t += TT_{t,s} YB_s                  6 steps (Z = dY; TT = rows of T^T)
+//   K  (m, s):  G^T_m += K^T_{m,s} ZN_s               2 * DK/16 steps (ZN = bf16(-dY))
+template <int DK> struct RevSteps {
+    static constexpr int NKB = DK / 32, NMT = DK / 16;
+    static constexpr int nV = 6, nY = 4 * NKB, nQ = 2 * NMT, nZ = 6, nK = 2 * NMT;
+    static constexpr int bY = nV, bQ1 = bY + nY, bZ = bQ1 + nQ / 2, bQ2 = bZ + nZ, bK = bQ2 + nQ - nQ / 2;
+    static constexpr int n = bK + nK;
+    static constexpr int depth = 8;
+    enum { kV, kY, kQ, kZ, kK };
+    static constexpr int kind(int i) {
+        return i < bY ? kV : i < bQ1 ? kY : i < bZ ? kQ : i < bQ2 ? kZ : i < bK ? kQ : kK;
+    }
+    static constexpr int idx(int i) {
+        return i < bY ? i : i < bQ1 ? i - bY : i < bZ ? i - bQ1 : i < bQ2 ? i - bZ : i < bK ? i - bQ2 + nQ / 2 : i - bK;
+    }
+    // V / Z step j -> token tile t and 32-token block s (rev_frag(tT(j), tS(j)) == j)
+    static constexpr int tT(int j) { return j < 4 ? j / 2 : j - 2; }
+    static constexpr int tS(int j) { return j < 4 ? j % 2 : 1; }
+};
+
+template <int DK>
+__device__ inline bf16x8 rev_fetch(int i, const __bf16 *K, const __bf16 *Q, const __bf16 *T, const __bf16 *P, int lane,
+                                   int g, int c16) {
+    using RS = RevSteps<DK>;
+    const int k = RS::kind(i), j = RS::idx(i);
+    if (k == RS::kV) return ld8(P + 512 * j + 8 * lane);
+    if (k == RS::kY) return ld8(K + koff<DK>(16 * (j / RS::NKB) + c16, 32 * (j % RS::NKB) + 8 * g));
+    if (k == RS::kQ) return k_trfrag<DK>(Q, j / 2, j % 2, g, c16);
+    if (k == RS::kZ) {
+        // row 16t + c of T^T over the tokens 32s + {4g + e, 16 + 4g + e}
+        const int row = 16 * RS::tT(j) + c16, col = 32 * RS::tS(j) + 4 * g;
+        return cat8(ld4(T + s64off(row, col)), ld4(T + s64off(row, col + 16)));
+    }
+    return k_trfrag<DK>(K, j / 2, j % 2, g, c16);
+}
+
+template <int DK, int DV>
+__device__ void rev_consumer_loop(const BwdArgs &a, const RevWork &wk, const RevBufs<DK> &bf, int NC, int cw, int lane,
+                                  int g, int c16) {
+    using RS = RevSteps<DK>;
+    constexpr int NMT = DK / 16, D = RS::depth;
+    const int lrow = 16 * cw + c16;
+    f32x4 G[NMT];
+#pragma unroll
+    for (int m = 0; m < NMT; ++m)
+        G[m] = a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + (wk.su * DV + wk.row0 + lrow) * DK + dk_of(m, g))
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t sv = (int64_t)a.H * DV;
+    __bf16 *dvg = reinterpret_cast<__bf16 *>(a.dv) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 + lrow;
+    __bf16 *gout = a.G_chunks + (wk.slot0 * DV + wk.row0 + lrow) * DK;
+    __syncthreads(); // matches the producers' prologue
+    for (int i = -2; i < NC; ++i) {
+        if (i >= 0) {
+            const int r = NC - 1 - i, nval = min(kChunk, wk.len - r * kChunk);
+            // dS' of chunk r (the gradient of the state after it), for the gradient kernel
+#pragma unroll
+            for (int m = 0; m < NMT; ++m) st4(gout + (int64_t)r * DV * DK + dk_of(m, g), cvt4(G[m]));
+            const __bf16 *Kb = bf.K(i), *Qb = bf.Q(i), *Tb = bf.Tt(i), *Pb = bf.P(i), *Db = bf.D(i);
+            // dO fragments over the tokens 32s + {4g + e, 16 + 4g + e}, this lane's value column
+            bf16x8 DB[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int row = 32 * s + 4 * g + (c16 >> 2), col = 16 * cw + 4 * (c16 & 3);
+                DB[s] = cat8(tr4(Db + s64off(row, col)), tr4(Db + s64off(row + 16, col)));
+            }
+            bf16x8 buf[D], GB[RS::NKB], YB[2], ZN[2];
+            static_for<0, D>([&](auto ic) { buf[ic.value] = rev_fetch<DK>(ic.value, Kb, Qb, Tb, Pb, lane, g, c16); });
+            const bool odd = g & 1;
+#pragma unroll
+            for (int s = 0; s < RS::NKB; ++s) {
+                const bf16x4 lo = cvt4(G[2 * s]), hi = cvt4(G[2 * s + 1]);
+                GB[s] = odd ? cat8(hi, lo) : cat8(lo, hi);
+            }
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            f32x4 Y[4], Z[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                Y[t] = zero;
+                Z[t] = zero;
+            }
+            fence();
+            static_for<0, RS::n>([&](auto ic) {
+                constexpr int i2 = decltype(ic)::value;
+                const bf16x8 f = buf[i2 % D];
+                if constexpr (i2 + D < RS::n) buf[i2 % D] = rev_fetch<DK>(i2 + D, Kb, Qb, Tb, Pb, lane, g, c16);
+                if constexpr (i2 == RS::bZ) {
+                    YB[0] = cvt8(Y[0], Y[1]);
+                    YB[1] = cvt8(Y[2], Y[3]);
+                }
+                if constexpr (i2 == RS::bK) {
+                    ZN[0] = cvt8(-Z[0], -Z[1]);
+                    ZN[1] = cvt8(-Z[2], -Z[3]);
+                }
+                fence();
+                constexpr int k = RS::kind(i2), j = RS::idx(i2);
+                if constexpr (k == RS::kV) Y[RS::tT(j)] = mfma32(f, DB[RS::tS(j)], Y[RS::tT(j)]);
+                if constexpr (k == RS::kY) Y[j / RS::NKB] = mfma32(f, GB[j % RS::NKB], Y[j / RS::NKB]);
+                if constexpr (k == RS::kQ) G[j / 2] = mfma32(f, DB[j % 2], G[j / 2]);
+                if constexpr (k == RS::kZ) Z[RS::tT(j)] = mfma32(f, YB[RS::tS(j)], Z[RS::tT(j)]);
+                if constexpr (k == RS::kK) G[j / 2] = mfma32(f, ZN[j % 2], G[j / 2]);
+                fence();
+            });
+            // dV = dY: Z[t][e] = dY[16t + 4g + e][lrow]
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = 16 * t + 4 * g + e;
+                    if (tok < nval) dvg[((int64_t)r * kChunk + tok) * sv] = (__bf16)Z[t][e];
+                }
+        }
+        __syncthreads();
+    }
+    if (a.dS0) {
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+            *reinterpret_cast<f32x4 *>(a.dS0 + (wk.su * DV + wk.row0 + lrow) * DK + dk_of(m, g)) = G[m];
+    }
+}
+
+template <int DK, int DV, int ROLE>
+__device__ void rev_producer_loop(const BwdArgs &a, const RevWork &wk, const RevBufs<DK> &bf, int NC, int g, int c16) {
+    const int lane = 16 * g + c16;
+    const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
+    KStager<DK> ks;
+    QStage<DK> q;
+    TStager ts;
+    DStager ds;
+    if constexpr (ROLE == 0) {
+        ts.init(a.T_chunks + wk.slot0 * kChunk * kChunk, lane);
+        ts.template load<0>(rev_chunk(NC, 0));
+    }
+    if constexpr (ROLE == 1) {
+        ds.init(reinterpret_cast<const __bf16 *>(a.dO) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0, sv, wk.len, lane);
+        ds.template load<0>(rev_chunk(NC, 0));
+    }
+    if constexpr (ROLE >= 2) {
+        ks.init(reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len,
+                64 * (ROLE - 2) + lane);
+        q.init(reinterpret_cast<const __bf16 *>(a.q) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len, ROLE - 2, g,
+               c16);
+        ks.template load<0>(rev_chunk(NC, 0));
+        ks.template load<1>(rev_chunk(NC, 1));
+        q.template load<0>(rev_chunk(NC, 0));
+    }
+    __syncthreads();
+    // Iteration i (consumers on step i):
+    //   wave 4:    T^T of step i+1 into LDS, loads of step i+3
+    //   wave 5:    dO of step i+1 into LDS, loads of step i+3
+    //   waves 6-7: K of step i+2 into LDS (loads of step i+4); Q of step i+1
+    //              into LDS and P^T of step i+1 (loads of step i+3)
+    // Register sets by step parity; staging is unconditional (clamped chunks
+    // land in ring slots that are rewritten before they are read).
+    auto iteration = [&](int i, auto ipar) {
+        constexpr int PK = decltype(ipar)::value, PS = 1 - PK; // sets of steps i+2 (K) and i+1 (the rest)
+        if constexpr (ROLE == 0) {
+            ts.template write<PS>(bf.Tt(i + 1));
+            ts.template load<PS>(rev_chunk(NC, i + 3));
+        } else if constexpr (ROLE == 1) {
+            ds.template write<PS>(bf.D(i + 1));
+            ds.template load<PS>(rev_chunk(NC, i + 3));
+        } else {
+            ks.template write<PK>(bf.K(i + 2));
+            ks.template load<PK>(rev_chunk(NC, i + 4));
+            if (i + 1 >= 0 && i + 1 < NC) {
+                q.template write<PS>(bf.Q(i + 1), g);
+                pt_tiles<DK, PS>(bf, q, i + 1, ROLE - 2, lane, g, c16);
+            }
+            q.template load<PS>(rev_chunk(NC, i + 3));
+        }
+        __syncthreads();
+    };
+    for (int i = -2; i < NC; i += 2) { // i even
+        iteration(i, Int<0>{});
+        if (i + 1 < NC) iteration(i + 1, Int<1>{});
+    }
+}
+
+template <int DK, int DV> __global__ __launch_bounds__(kWsThreads) void rev_chain_kernel(const BwdArgs a) {
+    using LY = RevLds<DK>;
+    static_assert(LY::total <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const RevWork wk = rev_work(a);
+    const int NC = (wk.len + kChunk - 1) / kChunk;
+    const RevBufs<DK> bf{smem};
+    if (NC == 0) { // no tokens: dS0 = dS'
+        if (wave < 4 && a.dS0) {
+            const int lrow = 16 * wave + c16;
+#pragma unroll
+            for (int m = 0; m < DK / 16; ++m) {
+                const int64_t off = (wk.su * DV + wk.row0 + lrow) * DK + dk_of(m, g);
+                *reinterpret_cast<f32x4 *>(a.dS0 + off) =
+                    a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        return;
+    }
+    { // P^T: the blocks above the diagonal are never written; zero both rings once
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 *zp = reinterpret_cast<f32x4 *>(smem + LY::oP);
+        for (int x = tid; x < (int)(2 * LY::szP / 16); x += kWsThreads) zp[x] = zero;
+    }
+    __syncthreads();
+    if (wave < 4) {
+        rev_consumer_loop<DK, DV>(a, wk, bf, NC, wave, lane, g, c16);
+    } else if (wave == 4) {
+        rev_producer_loop<DK, DV, 0>(a, wk, bf, NC, g, c16);
+    } else if (wave == 5) {
+        rev_producer_loop<DK, DV, 1>(a, wk, bf, NC, g, c16);
+    } else if (wave == 6) {
+        rev_producer_loop<DK, DV, 2>(a, wk, bf, NC, g, c16);
+    } else {
+        rev_producer_loop<DK, DV, 3>(a, wk, bf, NC, g, c16);
+    }
+}
+
+template <int DK, int DV> hipError_t launch_rev(const BwdArgs &a, hipStream_t s) {
+    const int grid = a.B * a.H * a.n_tiles;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((rev_chain_kernel<DK, DV>), dim3(grid), dim3(kWsThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int DK, int DV, bool WO> hipError_t launch_ws(const ChainArgs &a, hipStream_t s) {
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
@@ -1044,6 +1445,14 @@ template <bool WO> hipError_t launch_ws_dims(int dk, int dv, const ChainArgs &a,
 
 hipError_t launch_chain_bf16(int dk, int dv, bool write_o, const ChainArgs &a, hipStream_t stream) {
     return write_o ? launch_ws_dims<true>(dk, dv, a, stream) : launch_ws_dims<false>(dk, dv, a, stream);
+}
+
+hipError_t launch_bwd_rev(int dk, int dv, const BwdArgs &a, hipStream_t stream) {
+    if (dk == 128 && dv == 128) return launch_rev<128, 128>(a, stream);
+    if (dk == 128 && dv == 64) return launch_rev<128, 64>(a, stream);
+    if (dk == 64 && dv == 128) return launch_rev<64, 128>(a, stream);
+    if (dk == 64 && dv == 64) return launch_rev<64, 64>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 } // namespace dn

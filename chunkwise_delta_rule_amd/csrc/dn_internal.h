@@ -29,6 +29,8 @@ struct ChainArgs {
     float *S_final;
     float *S_chunks; // dense kind only, or nullptr: the state entering every chunk,
                      // [B*H][chunks][dv][dk] fp32 (kept for the backward pass)
+    __bf16 *S_chunks16; // bf16 DeltaNet without output, or nullptr: the same in bf16,
+                        // at the chunk slots of S_chunks (dense: u NC + c; varlen: chunk_base)
     __bf16 *T_chunks; // with S_chunks (bf16 DeltaNet without output), or nullptr: T^T of
                       // every chunk, [B*H][chunks][64][64] bf16 row-major (backward pass)
     const int32_t *chunk_base; // varlen with S_chunks: chunks before each sequence, [N + 1];
@@ -75,6 +77,9 @@ struct BwdArgs {
     const float *dS_final; // [B*H][dv][dk] or nullptr (zero)
     const float *S_chunks; // [B*H][NC][dv][dk]: the state entering each chunk
     const __bf16 *T_chunks; // [B*H][NC][64][64]: T^T of each chunk (the forward's), row-major
+    const __bf16 *S_chunks16; // reverse-chain pipeline: the entering states in bf16 [slot][dv][dk]
+    __bf16 *G_chunks;         // reverse-chain pipeline: dS' of each chunk (the gradient of the
+                              // state after it) in bf16 [slot][dv][dk]
     float *part;           // [n_tiles][max_slots] blocks of per-tile partial sums
     float *dS0;            // [B*H][dv][dk] or nullptr
     void *dq, *dk, *dv, *dbeta;
@@ -97,7 +102,12 @@ constexpr size_t bwd_part_floats(int dk) { return 2 * 64 * 64 + 2 * 64 * (size_t
 // Gated: per token k . (row-scaled Z dS') and k . (row-scaled dY S), and per
 // wave exp(gamma_C) <dS', S>, after those blocks (padded to 256 floats).
 constexpr size_t bwd_part_stride(int dk, bool gated) { return bwd_part_floats(dk) + (gated ? 256 : 0); }
+// The gated backward passes (a.g set): the reverse chain with per-value-tile
+// partial sums into a.part, then one finishing workgroup per chunk slot.
 hipError_t launch_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream);
+// Chunk-parallel gradients of the reverse-chain pipeline (DeltaNet): dq, dk,
+// dbeta from a.S_chunks16 and a.G_chunks. grid = a.max_slots workgroups.
+hipError_t launch_bwd_grad(int dk, int dv, const BwdArgs &a, hipStream_t stream);
 // Fill n floats with value (a kernel, not a memset, so it can sit in a captured graph).
 hipError_t launch_fill(float *p, size_t n, float value, hipStream_t stream);
 
@@ -109,6 +119,12 @@ hipError_t launch_decode(int dtype, int dk, const DecodeArgs &a, hipStream_t str
 // grid = n_units * n_tiles workgroups of kThreads threads.
 hipError_t launch_chain(int dtype, int dk, int dv, bool write_o, const ChainArgs &a,
                         hipStream_t stream);
+
+// Reverse chain of the DeltaNet backward pass (chain_bf16.hip): per (unit, 64
+// value rows), walks the chunks backwards carrying dS, writes dS' of every
+// chunk (a.G_chunks), dV and dS0. Needs a.T_chunks. grid = units * n_tiles
+// workgroups of 512 threads.
+hipError_t launch_bwd_rev(int dk, int dv, const BwdArgs &a, hipStream_t stream);
 
 // The bf16 chain kernel with specialised waves (chain_bf16.hip); same
 // contract as launch_chain, 512 threads per workgroup.

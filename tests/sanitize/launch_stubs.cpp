@@ -66,11 +66,29 @@ void chain_common(int dtype, int dk, int dv, bool write_o, const dn::ChainArgs &
     rd(a.S0, a.S0 ? units * dv * dk * 4 : 0);
     if (write_o) wr(a.o, real * a.H * dv * e);
     wr(a.S_final, a.S_final ? units * dv * dk * 4 : 0);
-    if (a.S_chunks) {
+    if (a.S_chunks || a.S_chunks16) {
         const size_t slots = a.kind == dn::kVarlen ? varlen_slots(a)
                                                    : units * (((size_t)a.T + dn::kChunk - 1) / dn::kChunk);
-        wr(a.S_chunks, slots * dv * dk * 4);
+        wr(a.S_chunks, a.S_chunks ? slots * dv * dk * 4 : 0);
+        wr(a.S_chunks16, a.S_chunks16 ? slots * dv * dk * 2 : 0);
         wr(a.T_chunks, a.T_chunks ? slots * dn::kChunk * dn::kChunk * 2 : 0);
+    }
+}
+
+// The inputs every backward launch reads: token tensors and, packed, the
+// sequence offsets; returns the token steps and the real tokens.
+void bwd_inputs(int dk, int dv, const dn::BwdArgs &b, size_t &steps, size_t &real) {
+    const size_t nh = b.nh > 0 ? b.nh : 1;
+    const bool varlen = b.cu_seqlens != nullptr;
+    steps = varlen ? (size_t)b.T : (size_t)b.B * b.T;
+    real = varlen ? steps : steps / nh;
+    rd(b.q, real * b.H * dk * 2);
+    rd(b.k, steps * b.H * dk * 2);
+    rd(b.beta, steps * b.H * 2);
+    rd(b.dO, real * b.H * dv * 2);
+    if (varlen) {
+        rd(b.cu_seqlens, (size_t)(b.B + 1) * 4);
+        rd(b.chunk_base, (size_t)(b.B + 1) * 4);
     }
 }
 
@@ -104,6 +122,36 @@ hipError_t launch_chunk_base(const int32_t *cu_seqlens, int N, int32_t *cb, hipS
     ++launches;
     cb[0] = 0;
     for (int n = 0; n < N; ++n) cb[n + 1] = cb[n] + (cu_seqlens[n + 1] - cu_seqlens[n] + kChunk - 1) / kChunk;
+    return hipSuccess;
+}
+
+
+hipError_t launch_bwd_rev(int dk, int dv, const BwdArgs &b, hipStream_t) {
+    ++launches;
+    size_t steps, real;
+    bwd_inputs(dk, dv, b, steps, real);
+    const size_t units = (size_t)b.B * b.H, slots = (size_t)b.max_slots;
+    rd(b.seq_order, b.cu_seqlens && b.seq_order ? (size_t)b.B * 4 : 0);
+    rd(b.dS_final, b.dS_final ? units * dv * dk * 4 : 0);
+    rd(b.T_chunks, slots * kChunk * kChunk * 2);
+    wr(b.G_chunks, slots * dv * dk * 2);
+    wr(b.dv, steps * b.H * dv * 2);
+    wr(b.dS0, b.dS0 ? units * dv * dk * 4 : 0);
+    return hipSuccess;
+}
+
+hipError_t launch_bwd_grad(int dk, int dv, const BwdArgs &b, hipStream_t) {
+    ++launches;
+    size_t steps, real;
+    bwd_inputs(dk, dv, b, steps, real);
+    const size_t slots = (size_t)b.max_slots;
+    rd(b.v, steps * b.H * dv * 2);
+    rd(b.S_chunks16, slots * dv * dk * 2);
+    rd(b.G_chunks, slots * dv * dk * 2);
+    rd(b.T_chunks, slots * kChunk * kChunk * 2);
+    wr(b.dq, real * b.H * dk * 2);
+    wr(b.dk, steps * b.H * dk * 2);
+    wr(b.dbeta, steps * b.H * 2);
     return hipSuccess;
 }
 

@@ -238,17 +238,22 @@ def test_gated_bwd_rejects_bad_arguments(lib, kw, status):
     assert st == status
 
 
-def test_gated_bwd_workspace_sizes(lib):
-    # the gated partial blocks carry 256 more floats per value tile than the ungated ones
+def test_bwd_workspace_sizes(lib):
+    # per chunk slot, DeltaNet: the state entering the chunk and the gradient of
+    # the state leaving it (bf16 each), then T^T (64 x 64 bf16); gated: the state
+    # entering the chunk (fp32), per value tile dP, dT (64 x 64), dQ, dK (64 x dk)
+    # and 256 floats of decay terms (fp32), then T^T
     for dk, dv in [(128, 128), (64, 64), (64, 128), (128, 64)]:
+        plain = 2 * dv * dk * 2 + 64 * 64 * 2
+        gated = (dv * dk + (dv // 64) * (2 * 64 * 64 + 2 * 64 * dk + 256)) * 4 + 64 * 64 * 2
         slots = 2 * 3 * 4  # B = 2, H = 3, T = 200 -> 4 chunks
-        extra = slots * (dv // 64) * 256 * 4
-        assert (lib.deltanet_gated_bwd_workspace_bytes(2, 3, 200, dk, dv, 64)
-                == lib.deltanet_bwd_workspace_bytes(2, 3, 200, dk, dv, 64) + extra)
-        vslots = (200 // 64 + 3) * 2
-        assert (lib.deltanet_gated_bwd_varlen_workspace_bytes(3, 200, 2, dk, dv, 64)
-                == lib.deltanet_bwd_varlen_workspace_bytes(3, 200, 2, dk, dv, 64) + vslots * (dv // 64) * 256 * 4)
+        assert lib.deltanet_bwd_workspace_bytes(2, 3, 200, dk, dv, 64) == slots * plain
+        assert lib.deltanet_gated_bwd_workspace_bytes(2, 3, 200, dk, dv, 64) == slots * gated
+        vslots = (200 // 64 + 3) * 2  # N = 3, total 200 tokens, H = 2; + 4 offsets, padded to 16 bytes
+        assert lib.deltanet_bwd_varlen_workspace_bytes(3, 200, 2, dk, dv, 64) == vslots * plain + 16
+        assert lib.deltanet_gated_bwd_varlen_workspace_bytes(3, 200, 2, dk, dv, 64) == vslots * gated + 16
     assert lib.deltanet_gated_bwd_workspace_bytes(2, 3, 200, 96, 128, 64) == 0
+    assert lib.deltanet_bwd_workspace_bytes(2, 3, 200, 96, 128, 64) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
