@@ -19,8 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libdeltanet.so")
 SOURCES = [os.path.join(PKG, "csrc", "kernels.hip"), os.path.join(PKG, "csrc", "chain_bf16.hip"),
-           os.path.join(PKG, "csrc", "decode.hip"), os.path.join(PKG, "csrc", "noalloc.hip"),
-           os.path.join(PKG, "csrc", "api.cpp")]
+           os.path.join(PKG, "csrc", "bwd_grad.hip"), os.path.join(PKG, "csrc", "decode.hip"),
+           os.path.join(PKG, "csrc", "noalloc.hip"), os.path.join(PKG, "csrc", "api.cpp")]
 HEADERS = [os.path.join(PKG, "csrc", "dn_internal.h"), os.path.join(PKG, "csrc", "dn_work.h"),
            os.path.join(ROOT, "include", "deltanet.h")]
 ARCH = "gfx950"

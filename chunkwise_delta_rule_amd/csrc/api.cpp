@@ -224,6 +224,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     if (st != DN_OK) return st;
     if (dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
     if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
+    if (H > 65536) return DN_ERR_UNSUPPORTED; // the gradient kernel's in-chunk offsets stay within 32 bits
     if (T > 0) {
         if (!q || !k || !v || !beta || !dO || !dq || !dk_ || !dv_ || !dbeta) return DN_ERR_INVALID;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned_to(beta, 2) ||

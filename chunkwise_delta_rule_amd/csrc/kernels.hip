@@ -1649,418 +1649,6 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Chunk-parallel gradients of the DeltaNet backward pass (reverse-chain
-// pipeline): one workgroup per chunk slot. With the state entering the chunk
-// (S, from the forward chain) and the gradient of the state after it (dS',
-// from the reverse chain), everything else of the chunk is local:
-//   Y = V - K S^T, Z = T Y, dZ = P^T dO + K dS'^T, dY = T^T dZ,
-//   dP = dO Z^T, dT = dZ Y^T (lower-inclusive), dQ = dO S + dP K,
-//   dK = dP^T Q + Z dS' - dY S + (dL + dL^T) K, dbeta through T.
-// The value dimension is walked in 64-row halves (the per-half products are
-// those of bwd_chain_kernel's chunk body); the sums over it (dP, dT, dO S,
-// Z dS' - dY S) stay in registers in the layout of bwd_finish_kernel, whose
-// finishing products follow unchanged. dV comes from the reverse chain.
-// ---------------------------------------------------------------------------
-template <int DK> struct GradLds {
-    using L = Ld<__bf16, DK>;
-    static constexpr int LT = L::T;
-    static constexpr size_t szX = sizeof(__bf16) * 64 * LT;
-    // the finish (FinLds<DK, false>); Q is staged over oT + oXs at its end
-    static constexpr size_t oK = 0, oB = oK + L::szK, oBt = oB + 256, oDa = oBt + 256;
-    static constexpr size_t oT = oDa + 256, oXs = oT + L::szT;
-    static constexpr size_t oP = oXs + szX, oDT = oP + szX, oL = oDT + szX;
-    // the value halves, over the finish's later tiles (dead until the halves are done)
-    static constexpr size_t hTT = oT, hQ = hTT + L::szT, hP = hQ + L::szK, hV = hP + L::szT;
-    static constexpr size_t hD = hV + L::szV, hS = hD + L::szV, hR = hS + L::szK, hY = hR + L::szK;
-    static constexpr size_t total = hY + 4 * szX;
-};
-
-__device__ inline bf16x4 neg_bf16(bf16x4 x) { // sign flip, exact
-    const u32x2 u = __builtin_bit_cast(u32x2, x);
-    return __builtin_bit_cast(bf16x4, u32x2{u[0] ^ 0x80008000u, u[1] ^ 0x80008000u});
-}
-
-template <int DK, int DV> __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(const BwdArgs a) {
-    using E = __bf16;
-    using TR = Tr<E>;
-    using F = typename TR::F;
-    using V = typename TR::V;
-    using L = Ld<E, DK>;
-    using LY = GradLds<DK>;
-    constexpr int NMT = DK / 16, LT = LY::LT, NH = DV / 64;
-    static_assert(LY::total <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
-    E *Ks = reinterpret_cast<E *>(smem + LY::oK);
-    float *Bs = reinterpret_cast<float *>(smem + LY::oB), *Bt = reinterpret_cast<float *>(smem + LY::oBt);
-    float *dba = reinterpret_cast<float *>(smem + LY::oDa);
-    E *TsT = reinterpret_cast<E *>(smem + LY::oT); // N^T once formed; Q at the end
-    E *dPs = reinterpret_cast<E *>(smem + LY::oP), *dTs = reinterpret_cast<E *>(smem + LY::oDT);
-    E *Xs = reinterpret_cast<E *>(smem + LY::oXs), *dLs = reinterpret_cast<E *>(smem + LY::oL);
-    // value halves
-    E *hTs = reinterpret_cast<E *>(smem + LY::hTT), *hQs = reinterpret_cast<E *>(smem + LY::hQ);
-    E *Ps = reinterpret_cast<E *>(smem + LY::hP), *Vs = reinterpret_cast<E *>(smem + LY::hV);
-    E *Ds = reinterpret_cast<E *>(smem + LY::hD), *Ss = reinterpret_cast<E *>(smem + LY::hS);
-    E *Rs = reinterpret_cast<E *>(smem + LY::hR);
-    E *Ys = reinterpret_cast<E *>(smem + LY::hY), *Zs = Ys + 64 * LT, *dZs = Zs + 64 * LT, *dYs = dZs + 64 * LT;
-
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    // chunk slot s = blockIdx.x -> sequence, head h and chunk r (as bwd_finish_kernel)
-    const int64_t s = blockIdx.x;
-    int64_t tok0;
-    int len, h, r;
-    if (a.cu_seqlens) {
-        const int32_t *cb = a.chunk_base;
-        if (s >= (int64_t)cb[a.B] * a.H) return;
-        int lo = 0, hi = a.B - 1; // largest n with cb[n] H <= s
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)cb[mid] * a.H <= s) lo = mid; else hi = mid - 1;
-        }
-        const int n = lo, ncn = cb[n + 1] - cb[n];
-        const int64_t off = s - (int64_t)cb[n] * a.H;
-        h = (int)(off / ncn);
-        r = (int)(off - (int64_t)h * ncn);
-        tok0 = a.cu_seqlens[n];
-        len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
-    } else {
-        const int u = (int)(s / a.NC), b = u / a.H;
-        r = (int)(s - (int64_t)u * a.NC);
-        h = u - b * a.H;
-        tok0 = (int64_t)b * a.T;
-        len = a.T;
-    }
-    const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
-    const int nval = min(kChunk, len - r * kChunk);
-
-    Stager<E, DK> sg;
-    sg.sqk = sqk;
-    sg.sv = 0;
-    sg.kg = reinterpret_cast<const E *>(a.k) + tok0 * sqk + (int64_t)h * DK;
-    sg.qg = reinterpret_cast<const E *>(a.q) + tok0 * sqk + (int64_t)h * DK;
-    sg.vg = nullptr;
-    sg.bg = reinterpret_cast<const E *>(a.beta) + tok0 * a.H + h;
-    sg.gg = nullptr;
-    sg.qh = nullptr;
-    sg.gh = nullptr;
-    sg.sb = SubstepBase{0, 0u, 1u};
-    sg.H = a.H;
-    sg.len = len;
-    sg.tid = tid;
-    sg.has_v = false;
-    sg.rbeta = TR::fromf(0.f);
-    sg.rg = 0.f;
-    sg.nval = 0;
-    sg.load(r);
-    V tv[2]; // T^T of the chunk, as the forward pass formed it
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-        tv[p] = *reinterpret_cast<const V *>(a.T_chunks + s * kChunk * kChunk + 8 * (p * kThreads + tid));
-    // value half loads: S and dS' rows (64 x DK), V and dO (64 tokens x 64 values)
-    constexpr int NS = 64 * DK / 8 / kThreads; // 16-byte vectors of S (and dS') per thread
-    const E *Sg = a.S_chunks16 + s * DV * DK, *Gg = a.G_chunks + s * DV * DK;
-    const E *Vg = reinterpret_cast<const E *>(a.v) + (tok0 + (int64_t)r * kChunk) * sv + (int64_t)h * DV;
-    const E *Dg = reinterpret_cast<const E *>(a.dO) + (tok0 + (int64_t)r * kChunk) * sv + (int64_t)h * DV;
-    V hs[NS], hg[NS], hv[2], hd[2];
-    auto load_half = [&](int tau) {
-#pragma unroll
-        for (int p = 0; p < NS; ++p) {
-            const int vi = p * kThreads + tid;
-            hs[p] = *reinterpret_cast<const V *>(Sg + (int64_t)tau * 64 * DK + 8 * vi);
-            hg[p] = *reinterpret_cast<const V *>(Gg + (int64_t)tau * 64 * DK + 8 * vi);
-        }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int vi = p * kThreads + tid, row = min(vi / 8, nval - 1), cv = vi % 8;
-            hv[p] = *reinterpret_cast<const V *>(Vg + (int64_t)row * sv + 64 * tau + 8 * cv);
-            hd[p] = *reinterpret_cast<const V *>(Dg + (int64_t)row * sv + 64 * tau + 8 * cv);
-        }
-    };
-    load_half(0);
-
-    sg.store_kqb(Ks, hQs, Bs, nullptr);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
-        *reinterpret_cast<V *>(hTs + row * L::T + 8 * cv) = tv[p];
-    }
-    __syncthreads();
-    // the masked scores P = (Q K^T) lower-inclusive: the ten 16x16 tiles (a, c <= a)
-    {
-        constexpr int NKB = DK / 32;
-        const int nt = w < 2 ? 3 : 2;
-#pragma unroll
-        for (int it = 0; it < 3; ++it) {
-            if (it >= nt) break;
-            // wave 0: (0,0) (3,0) (3,1); 1: (1,0) (1,1) (3,2); 2: (2,0) (2,1); 3: (2,2) (3,3)
-            const int code = w == 0 ? (it == 0 ? 0x00 : it == 1 ? 0x30 : 0x31)
-                           : w == 1 ? (it == 0 ? 0x10 : it == 1 ? 0x11 : 0x32)
-                           : w == 2 ? (it == 0 ? 0x20 : 0x21)
-                                    : (it == 0 ? 0x22 : 0x33);
-            const int ab = code >> 4, cb = code & 15;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-                acc = TR::mma32(acc, ldrow(Ks, L::K, 16 * cb + c16, 32 * kb, g), ldrow(Ks, L::K, 16 * cb + c16, 32 * kb + 16, g),
-                                ldrow(hQs, L::K, 16 * ab + c16, 32 * kb, g), ldrow(hQs, L::K, 16 * ab + c16, 32 * kb + 16, g));
-            // acc[e] = k_{16cb + 4g + e} . q_{16ab + c16}
-            const int row = 16 * ab + c16, col = 16 * cb + 4 * g;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = (col + e > row) ? 0.f : acc[e];
-            stf(Ps + row * L::T + col, TR::cvt(acc));
-        }
-    }
-
-    // sums over the value dimension, token rows 16w + 4g + i of this wave:
-    // pp / tt = dP / dT tiles (w, s2), dQa = dO S, dKa = Z dS' - dY S
-    f32x4 pp[4], tt[4], dQa[NMT], dKa[NMT];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-        pp[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
-        tt[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int m = 0; m < NMT; ++m) {
-        dQa[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dKa[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int tau = 0; tau < NH; ++tau) {
-        // stage this half (its loads were issued before the previous half's products)
-#pragma unroll
-        for (int p = 0; p < NS; ++p) {
-            const int vi = p * kThreads + tid, row = vi / (DK / 8), cv = vi % (DK / 8);
-            *reinterpret_cast<V *>(Ss + row * L::K + 8 * cv) = hs[p];
-            *reinterpret_cast<V *>(Rs + row * L::K + 8 * cv) = hg[p];
-        }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
-            *reinterpret_cast<V *>(Vs + row * L::V + 8 * cv) = row < nval ? hv[p] : V{};
-            *reinterpret_cast<V *>(Ds + row * L::V + 8 * cv) = row < nval ? hd[p] : V{};
-        }
-        __syncthreads();
-        if (tau + 1 < NH) load_half(tau + 1);
-        // This wave's 16 value rows of the half (column c16 of the accumulators).
-        F SBn[NMT], dSB[NMT], YB[4], dZB[4];
-        f32x4 acc[4];
-#pragma unroll
-        for (int m = 0; m < NMT; ++m) {
-            SBn[m] = neg_bf16(ldrow(Ss, L::K, 16 * w + c16, 16 * m, g));
-            dSB[m] = ldrow(Rs, L::K, 16 * w + c16, 16 * m, g);
-        }
-        // Y = V - K S^T
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            acc[t] = widen_bf16(TR::ldcol(Vs, L::V, 16 * t, 16 * w, g, c16));
-#pragma unroll
-            for (int kb = 0; kb < NMT / 2; ++kb)
-                acc[t] = TR::mma32(acc[t], ldrow(Ks, L::K, 16 * t + c16, 32 * kb, g),
-                                   ldrow(Ks, L::K, 16 * t + c16, 32 * kb + 16, g), SBn[2 * kb], SBn[2 * kb + 1]);
-            YB[t] = TR::cvt(acc[t]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ys[(16 * t + 4 * g + i) * LT + 16 * w + c16] = YB[t][i];
-        }
-        // Z = T Y
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s2 = 0; s2 <= t; ++s2) z = TR::mma16(z, TR::ldcol(hTs, L::T, 16 * s2, 16 * t, g, c16), YB[s2]);
-            const F zb = TR::cvt(z);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Zs[(16 * t + 4 * g + i) * LT + 16 * w + c16] = zb[i];
-        }
-        // dZ = P^T dO + K dS'^T (the two product shapes in separate accumulators)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 zp = {0.f, 0.f, 0.f, 0.f}, zk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s2 = t; s2 < 4; ++s2)
-                zp = TR::mma16(zp, TR::ldcol(Ps, L::T, 16 * s2, 16 * t, g, c16), TR::ldcol(Ds, L::V, 16 * s2, 16 * w, g, c16));
-#pragma unroll
-            for (int m = 0; m < NMT; m += 2)
-                zk = TR::mma32(zk, ldrow(Ks, L::K, 16 * t + c16, 16 * m, g), ldrow(Ks, L::K, 16 * t + c16, 16 * m + 16, g),
-                               dSB[m], dSB[m + 1]);
-            dZB[t] = TR::cvt(zp + zk);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dZs[(16 * t + 4 * g + i) * LT + 16 * w + c16] = dZB[t][i];
-        }
-        // dY = T^T dZ
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s2 = t; s2 < 4; ++s2) z = TR::mma16(z, ldrow(hTs, L::T, 16 * t + c16, 16 * s2, g), dZB[s2]);
-            const F yb = TR::cvt(z);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dYs[(16 * t + 4 * g + i) * LT + 16 * w + c16] = yb[i];
-        }
-        __syncthreads(); // Y, Z, dZ, dY tiles of the half complete
-        // sums over the half's 64 value rows, token rows 16w .. 16w + 15
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-            if (s2 > w) break; // dP and dT are lower-inclusive
-#pragma unroll
-            for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
-                pp[s2] = TR::mma32(pp[s2], ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g),
-                                   ldrow(Ds, L::V, 16 * w + c16, 16 * kv + 16, g), ldrow(Zs, LT, 16 * s2 + c16, 16 * kv, g),
-                                   ldrow(Zs, LT, 16 * s2 + c16, 16 * kv + 16, g));
-                tt[s2] = TR::mma32(tt[s2], ldrow(dZs, LT, 16 * w + c16, 16 * kv, g),
-                                   ldrow(dZs, LT, 16 * w + c16, 16 * kv + 16, g), ldrow(Ys, LT, 16 * s2 + c16, 16 * kv, g),
-                                   ldrow(Ys, LT, 16 * s2 + c16, 16 * kv + 16, g));
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < NMT; ++m) {
-            f32x4 dk1 = {0.f, 0.f, 0.f, 0.f}, dk2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
-                const F s0 = TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16), s1 = TR::ldcol(Ss, L::K, 16 * kv + 16, 16 * m, g, c16);
-                dQa[m] = TR::mma32(dQa[m], ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g),
-                                   ldrow(Ds, L::V, 16 * w + c16, 16 * kv + 16, g), s0, s1);
-                dk1 = TR::mma32(dk1, ldrow(Zs, LT, 16 * w + c16, 16 * kv, g), ldrow(Zs, LT, 16 * w + c16, 16 * kv + 16, g),
-                                TR::ldcol(Rs, L::K, 16 * kv, 16 * m, g, c16), TR::ldcol(Rs, L::K, 16 * kv + 16, 16 * m, g, c16));
-                dk2 = TR::mma32(dk2, ldrow(dYs, LT, 16 * w + c16, 16 * kv, g), ldrow(dYs, LT, 16 * w + c16, 16 * kv + 16, g),
-                                s0, s1);
-            }
-            dKa[m] += dk1 - dk2;
-        }
-        __syncthreads(); // the half's tiles are no longer read
-    }
-
-    // ---- the finish, as bwd_finish_kernel (ungated) ----
-    E *TtS = Xs, *Ls = dLs; // T^T and L until N^T is formed (X and dL come later)
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
-        *reinterpret_cast<V *>(TtS + row * LT + 8 * cv) = tv[p];
-    }
-    if (w == 0) Bt[lane] = lane < nval ? TR::tof(sg.rbeta) : 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * s2 + c16;
-            dPs[row * LT + col] = TR::fromf(col <= row ? pp[s2][i] : 0.f);
-            dTs[row * LT + col] = TR::fromf(col <= row ? tt[s2][i] : 0.f);
-        }
-    __syncthreads();
-    // Gram rows of this wave, gm[j][i] = k_t . k_{16j + c16} (t = 16w + 4g + i),
-    // and L = their strictly lower part
-    f32x4 gm[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        gm[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kd = 0; kd < NMT; kd += 2)
-            gm[j] = TR::mma32(gm[j], ldrow(Ks, L::K, 16 * w + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * w + c16, 16 * kd + 16, g),
-                              ldrow(Ks, L::K, 16 * j + c16, 16 * kd, g), ldrow(Ks, L::K, 16 * j + c16, 16 * kd + 16, g));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
-            Ls[t * LT + col] = TR::fromf(col < t ? gm[j][i] : 0.f);
-        }
-    }
-    __syncthreads();
-    // N = (I + diag(beta) L)^-1 satisfies N = I - T L (T = N diag(beta)), so
-    // N^T = I - L^T T^T, an upper triangular product: row block w of it here.
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (b >= w) {
-#pragma unroll
-            for (int k0 = 0; k0 < 64; k0 += 32)
-                acc = TR::mma32(acc, TR::ldcol(Ls, LT, k0, 16 * w, g, c16), TR::ldcol(Ls, LT, k0 + 16, 16 * w, g, c16),
-                                TR::ldcol(TtS, LT, k0, 16 * b, g, c16), TR::ldcol(TtS, LT, k0 + 16, 16 * b, g, c16));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * w + 4 * g + i, col = 16 * b + c16;
-            TsT[row * L::T + col] = TR::fromf((row == col ? 1.f : 0.f) - acc[i]);
-        }
-    }
-    __syncthreads();
-    // X = N^T dT -> dbeta_a = diag X, Xs = X diag(beta)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int rb = 0; rb < 4; rb += 2)
-            x = TR::mma32(x, ldrow(TsT, L::T, 16 * w + c16, 16 * rb, g), ldrow(TsT, L::T, 16 * w + c16, 16 * rb + 16, g),
-                          TR::ldcol(dTs, LT, 16 * rb, 16 * j, g, c16), TR::ldcol(dTs, LT, 16 * rb + 16, 16 * j, g, c16));
-        const float bc = Bt[16 * j + c16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (j == w && c16 == 4 * g + i) dba[16 * w + 4 * g + i] = x[i];
-            Xs[(16 * w + 4 * g + i) * LT + 16 * j + c16] = TR::fromf(x[i] * bc);
-        }
-    }
-    __syncthreads();
-    // dA = -(X diag(beta)) N^T, strictly lower; dbeta_b = sum_j dA_tj G_tj; dL = diag(beta) dA
-    float dbb[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f32x4 da = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int rb = 0; rb < 4; rb += 2)
-            da = TR::mma32(da, ldrow(Xs, LT, 16 * w + c16, 16 * rb, g), ldrow(Xs, LT, 16 * w + c16, 16 * rb + 16, g),
-                           TR::ldcol(TsT, L::T, 16 * rb, 16 * j, g, c16), TR::ldcol(TsT, L::T, 16 * rb + 16, 16 * j, g, c16));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * w + 4 * g + i, col = 16 * j + c16;
-            const float dai = col < t ? -da[i] : 0.f;
-            dbb[i] += dai * gm[j][i];
-            dLs[t * LT + col] = TR::fromf(Bt[t] * dai);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) // sum over the 16 lanes of the row group
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) dbb[i] += __shfl_xor(dbb[i], o, 16);
-    __syncthreads();
-    E *Qs = TsT;
-    sg.store_q(Qs); // N^T and X are no longer read: Q goes over them
-    __syncthreads();
-    // dQ += dP K;  dK += dP^T Q + (dL + dL^T) K
-#pragma unroll
-    for (int m = 0; m < NMT; ++m)
-#pragma unroll
-        for (int sb = 0; sb < 4; sb += 2) { // 16x16x32 products over token blocks sb, sb + 1
-            const F kc0 = TR::ldcol(Ks, L::K, 16 * sb, 16 * m, g, c16), kc1 = TR::ldcol(Ks, L::K, 16 * sb + 16, 16 * m, g, c16);
-            dQa[m] = TR::mma32(dQa[m], ldrow(dPs, LT, 16 * w + c16, 16 * sb, g), ldrow(dPs, LT, 16 * w + c16, 16 * sb + 16, g),
-                               kc0, kc1);
-            dKa[m] = TR::mma32(dKa[m], TR::ldcol(dPs, LT, 16 * sb, 16 * w, g, c16),
-                               TR::ldcol(dPs, LT, 16 * sb + 16, 16 * w, g, c16), TR::ldcol(Qs, L::K, 16 * sb, 16 * m, g, c16),
-                               TR::ldcol(Qs, L::K, 16 * sb + 16, 16 * m, g, c16));
-            dKa[m] = TR::mma32(dKa[m], ldrow(dLs, LT, 16 * w + c16, 16 * sb, g), ldrow(dLs, LT, 16 * w + c16, 16 * sb + 16, g),
-                               kc0, kc1);
-            dKa[m] = TR::mma32(dKa[m], TR::ldcol(dLs, LT, 16 * sb, 16 * w, g, c16),
-                               TR::ldcol(dLs, LT, 16 * sb + 16, 16 * w, g, c16), kc0, kc1);
-        }
-    E *dkg = reinterpret_cast<E *>(a.dk) + (tok0 + (int64_t)r * kChunk) * sqk + (int64_t)h * DK;
-    E *dqg = reinterpret_cast<E *>(a.dq) + (tok0 + (int64_t)r * kChunk) * sqk + (int64_t)h * DK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = 16 * w + 4 * g + i;
-        if (t < nval) {
-#pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                dqg[(int64_t)t * sqk + 16 * m + c16] = TR::fromf(dQa[m][i]);
-                dkg[(int64_t)t * sqk + 16 * m + c16] = TR::fromf(dKa[m][i]);
-            }
-            if (c16 == 0)
-                reinterpret_cast<E *>(a.dbeta)[(tok0 + (int64_t)r * kChunk + t) * a.H + h] = TR::fromf(dba[t] + dbb[i]);
-        }
-    }
-}
-
-template <int DK, int DV> hipError_t launch_grad_dims(const BwdArgs &a, hipStream_t s) {
-    if (a.max_slots <= 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_grad_kernel<DK, DV>), dim3((unsigned)a.max_slots), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // Kimi Delta Attention (KDA) forward, bf16 operands.
 //
 // "Linear Attention, Visualized", "Kimi Delta Attention (KDA)": the state
@@ -2425,14 +2013,6 @@ hipError_t launch_chain(int dtype, int dk, int dv, bool write_o, const ChainArgs
                         hipStream_t stream) {
     if (dtype == 1) return launch_chain_bf16(dk, dv, write_o, a, stream);
     return write_o ? launch_dims_f32<true>(dk, dv, a, stream) : launch_dims_f32<false>(dk, dv, a, stream);
-}
-
-hipError_t launch_bwd_grad(int dk, int dv, const BwdArgs &a, hipStream_t stream) {
-    if (dk == 128 && dv == 128) return launch_grad_dims<128, 128>(a, stream);
-    if (dk == 128 && dv == 64) return launch_grad_dims<128, 64>(a, stream);
-    if (dk == 64 && dv == 128) return launch_grad_dims<64, 128>(a, stream);
-    if (dk == 64 && dv == 64) return launch_grad_dims<64, 64>(a, stream);
-    return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_base(const int32_t *cu_seqlens, int N, int32_t *cb, hipStream_t stream) {

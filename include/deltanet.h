@@ -254,11 +254,13 @@ int deltanet_kda_decode_step(const void *q, const void *k, const void *v, const 
  *   dq, dk, dv, dbeta : outputs, layouts of q, k, v, beta (dtype)
  *   dS0     : [B,H,dv,dk] fp32 output, or NULL to skip
  *   workspace : at least deltanet_bwd_workspace_bytes(...) bytes, 16-byte
- *             aligned: the state entering each chunk, per-chunk partial sums
- *             and each chunk's T (as the forward pass forms it)
+ *             aligned: per chunk, the state entering it and the gradient of
+ *             the state leaving it (bf16 each) and its T (as the forward pass
+ *             forms it)
  * Three launches: the forward chain keeping the per-chunk states, the reverse
- * chain of the state gradient, and a chunk-parallel pass for dq, dk, dbeta.
- * Errors as in deltanet_fwd (DN_ERR_UNSUPPORTED for DN_F32).
+ * chain of the state gradient (dv, dS0), and a chunk-parallel pass for dq,
+ * dk, dbeta. Errors as in deltanet_fwd (DN_ERR_UNSUPPORTED for DN_F32, and
+ * for H > 65536).
  */
 int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta,
                  const float *S0, const void *dO, const float *dS_final, void *dq, void *dk,

@@ -14,7 +14,7 @@ instance of chain_kernel_ws must:
   its (broadcast) first source. The DPP FMAs are inline assembly, so the
   compiler does not insert these wait states; the source guarantees them.
 
-Every kernel of the library (chain_bf16.hip and kernels.hip) must also keep
+Every kernel of the library (chain_bf16.hip, bwd_grad.hip and kernels.hip) must also keep
 matrix-core accumulation chains to one product shape: no 16x16x16 product
 may take the result of a 16x16x32 product (or the other way round) as its
 accumulator. The compiler emitted such a pair back to back without the wait
@@ -33,6 +33,7 @@ from chunkwise_delta_rule_amd import build
 
 SRC = os.path.join(build.PKG, "csrc", "chain_bf16.hip")
 SRC_OTHER = os.path.join(build.PKG, "csrc", "kernels.hip")
+SRC_GRAD = os.path.join(build.PKG, "csrc", "bwd_grad.hip")
 
 
 def _compile(src):
@@ -54,6 +55,11 @@ def asm():
 @pytest.fixture(scope="module")
 def asm_other():
     return _compile(SRC_OTHER)
+
+
+@pytest.fixture(scope="module")
+def asm_grad():
+    return _compile(SRC_GRAD)
 
 
 def kernels(asm_text):
@@ -171,10 +177,10 @@ def mixed_shape_chains(asm_text):
     return found
 
 
-def test_no_mixed_shape_accumulation(asm, asm_other):
-    n_mfma = asm.count("v_mfma") + asm_other.count("v_mfma")
+def test_no_mixed_shape_accumulation(asm, asm_other, asm_grad):
+    n_mfma = asm.count("v_mfma") + asm_other.count("v_mfma") + asm_grad.count("v_mfma")
     assert n_mfma > 1000
-    bad = mixed_shape_chains(asm) + mixed_shape_chains(asm_other)
+    bad = mixed_shape_chains(asm) + mixed_shape_chains(asm_other) + mixed_shape_chains(asm_grad)
     assert not bad, "\n".join(f"{k}: {a} -> {b} ({gap} between)" for k, a, b, gap in bad[:10])
 
 
@@ -189,3 +195,19 @@ def test_mixed_shape_check_catches_a_planted_chain():
     assert mixed_shape_chains(same) == []
     rewritten = body.replace("\tds_read_b64", "\tv_accvgpr_write_b32 a0, 0\n\tds_read_b64")
     assert mixed_shape_chains(rewritten) == []
+
+
+def test_gradient_kernel_two_workgroups_per_cu(asm_grad):
+    # the chunk-parallel gradient kernel is sized for two workgroups of 4
+    # waves per CU: at most 256 registers per lane, no scratch, at most 80 KB
+    # of LDS
+    found = 0
+    for m in re.finditer(r"^(_Z\S*bwd_grad_kernel\S*):", asm_grad, flags=re.M):
+        found += 1
+        end = asm_grad.index(".Lfunc_end", m.end())
+        tail = asm_grad[end:end + 4000]
+        name = m.group(1)
+        assert int(re.search(r"ScratchSize:\s*(\d+)", tail).group(1)) == 0, name
+        assert int(re.search(r"TotalNumVgprs:\s*(\d+)", tail).group(1)) <= 256, name
+        assert int(re.search(r"LDSByteSize:\s*(\d+)", tail).group(1)) <= 80 * 1024, name
+    assert found == 4
