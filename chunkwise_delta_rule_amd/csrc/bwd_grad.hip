@@ -44,19 +44,24 @@
 // transposed, so that its accumulator layout becomes one 8-byte write per
 // lane (D^T[col][4 g .. 4 g + 3]); its readers swap row and column reads.
 //
-// LDS rows are unpadded. Each layout XORs a few row bits into the column
-// unit so that every access above is free of bank conflicts (64 banks for
-// reads: 16 lanes per pass for 16-byte reads, 32 for 8-byte and transposing
-// ones; 32 banks for writes: 8 lanes per pass for 16-byte writes, 16 for
-// 8-byte ones):
-//   o64   64-column tiles (T^T, P, the Y/Z/dZ/dY^T quarter tiles, dP^T, dT^T,
-//         L^T and dL^T, N, (X diag(beta))^T): 8-byte units, row bits
-//         (1, 2) -> unit bits (2, 3), row bit 3 -> bit 1, row bit 0 -> bit 0;
-//   okk   dk-column tiles (K, Q, S, dS'): 16-byte units, for dk = 128 row
-//         bits 0-2 -> unit bits 1-3 and row bit 3 -> bit 0; for dk = 64 row
-//         bits 1-2 -> unit bits 1-2 and row bit 3 -> bit 0;
-//   ov    32-column quarter tiles of V and dO: 16-byte units, row bit 2 ->
-//         unit bit 1, row bit 3 -> bit 0.
+// LDS layouts: rows padded and a few row bits XORed into the low bits of the
+// column unit, so that the accesses above are free of bank conflicts (64 banks
+// for reads: 16 lanes per pass for 16-byte reads, 32 for 8-byte and
+// transposing ones; 32 banks for writes: 8 lanes per pass for 16-byte writes,
+// 16 for 8-byte ones) while an address stays affine in the 16-row and
+// 16-column block indices, so that one register plus immediate offsets
+// serves a loop over blocks:
+//   o64   64-column tiles (T^T, the Y/Z/dZ/dY^T quarter tiles, dP^T, dT^T,
+//         L^T and dL^T, N, (X diag(beta))^T): rows of 80, 8-byte units,
+//         row bit 2 -> unit bit 0, row bit 3 -> unit bit 1;
+//   o64p  P: rows of 72, row bit 3 -> unit bit 0 (two-way conflicts on the
+//         transposing reads, which only the first phase makes);
+//   okk   dk-column tiles (K, Q, S, dS'): rows of dk + 16, 16-byte units,
+//         row bit 3 -> unit bit 0;
+//   ov    32-column quarter tiles of dO: unpadded 16-byte units, row bit 2 ->
+//         unit bit 1, row bit 3 -> unit bit 0.
+// V enters only as the starting value of the Y accumulators and is read from
+// HBM straight into their layout.
 #include "dn_internal.h"
 
 namespace dn {
@@ -87,10 +92,7 @@ __device__ inline bf16x4 cvt4(f32x4 x) {
     const u32x2 u = {__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
     return __builtin_bit_cast(bf16x4, u);
 }
-__device__ inline f32x4 widen4(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
 __device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
-__device__ inline bf16x4 lo4(bf16x8 x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
-__device__ inline bf16x4 hi4(bf16x8 x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
 __device__ inline bf16x8 neg8(bf16x8 x) { // sign flip, exact
     const u32x4 u = __builtin_bit_cast(u32x4, x);
     const unsigned m = 0x80008000u;
@@ -106,10 +108,12 @@ __device__ inline bf16x4 tr4(const __bf16 *p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
 }
 
-// Element offsets of the swizzled layouts (see the file header).
-__device__ inline int o64(int r, int c) {
-    const int s = (((r >> 1) & 3) << 2) | (((r >> 3) & 1) << 1) | (r & 1);
-    return r * 64 + 4 * ((c >> 2) ^ s) + (c & 3);
+// Element offsets of the LDS layouts (see the file header).
+__device__ inline int o64(int r, int c) { // 64 columns, rows of 80
+    return r * 80 + 4 * ((c >> 2) ^ (((r >> 2) & 1) | (((r >> 3) & 1) << 1))) + (c & 3);
+}
+__device__ inline int o64p(int r, int c) { // 64 columns, rows of 72 (P)
+    return r * 72 + 4 * ((c >> 2) ^ ((r >> 3) & 1)) + (c & 3);
 }
 template <int DK> __device__ inline int okk(int r, int c) {
     return r * (DK + 16) + 8 * ((c >> 3) ^ ((r >> 3) & 1)) + (c & 7);
@@ -118,35 +122,52 @@ __device__ inline int ov(int r, int c) {
     const int s = (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
     return r * 32 + 8 * ((c >> 3) ^ s) + (c & 7);
 }
-// The lane coordinates again, opaque to the compiler. Each phase derives its
-// LDS addresses from fresh copies, so that the compiler forms them where the
-// phase uses them instead of keeping (or spilling) every address of the
-// kernel live from the phase that first formed it.
-__device__ inline void renew(int lane, int &g, int &c) {
+// Per-lane element offsets of the access patterns, for the blocks at (0, 0);
+// a block 16 x rows and 16 y columns away adds 16 x times the row length
+// plus 16 y (every layout above keeps that affine), so one register and
+// immediate offsets serve a loop over blocks.
+struct Offs {
+    int g, c;
+    int t64, r64;     // o64: transposing-read provider (4 g + c / 4, 4 (c % 4)); 8-byte piece (c, 4 g)
+    int t64p, r64p;   // o64p: the same
+    int tkk, r8kk;    // okk: transposing-read provider; 16-byte piece (c, 8 g)
+    int tv, rv0, rv1; // ov: provider (4 g + c / 4, 16 vt + 4 (c % 4)); pieces (c, 4 g), (c, 16 + 4 g)
+};
+// Formed from an opaque copy of the lane index: each phase forms its own
+// offsets where it uses them, instead of the compiler keeping (or spilling)
+// the offsets of every phase live from the first one.
+template <int DK> __device__ inline Offs offs(int lane, int vt) {
     int l = lane;
     asm volatile("" : "+v"(l));
-    g = l >> 4;
-    c = l & 15;
+    Offs o;
+    o.g = l >> 4;
+    o.c = l & 15;
+    const int tr = 4 * o.g + (o.c >> 2), tc = 4 * (o.c & 3);
+    o.t64 = o64(tr, tc);
+    o.r64 = o64(o.c, 4 * o.g);
+    o.t64p = o64p(tr, tc);
+    o.r64p = o64p(o.c, 4 * o.g);
+    o.tkk = okk<DK>(tr, tc);
+    o.r8kk = okk<DK>(o.c, 8 * o.g);
+    o.tv = ov(tr, 16 * vt + tc);
+    o.rv0 = ov(o.c, 4 * o.g);
+    o.rv1 = ov(o.c, 16 + 4 * o.g);
+    return o;
 }
-// Provider address of a transposing read of the 16 x 16 block at (k0, n0):
-// the receiving lane (g, c) gets rows k0 + 4 g .. k0 + 4 g + 3 of column n0 + c.
-__device__ inline int tr_row(int k0, int g, int c) { return k0 + 4 * g + (c >> 2); }
-__device__ inline int tr_col(int n0, int c) { return n0 + 4 * (c & 3); }
 
 template <int DK> struct GradLds {
     static constexpr size_t szK = (size_t)64 * (DK + 16) * 2; // K (Q at the start and at the end)
     static constexpr size_t szQt = (size_t)32 * (DK + 16) * 2; // a quarter of S or dS'
-    static constexpr size_t sz64 = 64 * 64 * 2, sz32 = 32 * 64 * 2, szV = 64 * 32 * 2;
+    static constexpr size_t sz64 = 64 * 80 * 2, sz32 = 32 * 80 * 2, szP = 64 * 72 * 2, szD = 64 * 32 * 2;
     static constexpr size_t oK = 0, oTT = oK + szK, oB = oTT + sz64, oDa = oB + 256, oR = oDa + 256;
-    // quarter phase: P, S, dS', V, dO, Y^T, Z^T, dZ^T, dY^T (Q over the last four, and past
-    // them, at the start)
-    static constexpr size_t oP = oR, oS = oP + sz64, oG = oS + szQt, oV = oG + szQt, oD = oV + szV;
-    static constexpr size_t oY = oD + szV, oZ = oY + sz32, odZ = oZ + sz32, odY = odZ + sz32;
-    static constexpr size_t end = (odY + sz32 > oY + szK) ? odY + sz32 : oY + szK;
-    // finish: dP^T, dT^T, L^T (then dL^T), N, (X diag(beta))^T (Q over the last, and past it)
-    static constexpr size_t fdP = oR, fdT = fdP + sz64, fL = fdT + sz64, fN = fL + sz64, fX = fN + sz64;
-    static constexpr size_t fend = fX + (sz64 > szK ? sz64 : szK);
+    // quarter phase: P, S, dS', dO, Y^T, Z^T, dZ^T, dY^T (Q over the last four at the start)
+    static constexpr size_t oP = oR, oS = oP + szP, oG = oS + szQt, oD = oG + szQt;
+    static constexpr size_t oY = oD + szD, oZ = oY + sz32, odZ = oZ + sz32, odY = odZ + sz32, end = odY + sz32;
+    // finish: dP^T, L^T (then dL^T), dT^T, N, (X diag(beta))^T (Q over dT^T and N at the end)
+    static constexpr size_t fdP = oR, fL = fdP + sz64, fdT = fL + sz64, fN = fdT + sz64, fX = fN + sz64;
+    static constexpr size_t fend = fX + sz64;
     static constexpr size_t total = end > fend ? end : fend;
+    static_assert(4 * sz32 >= szK && 2 * sz64 >= szK, "Q fits over the tiles it shares");
 };
 
 // Two waves per SIMD (two workgroups per CU): at most 256 registers per lane.
@@ -158,12 +179,13 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int KU = DK / 8;              // 16-byte units per dk row
     constexpr int NKV = 64 * KU / kGT;      // K (and Q) units per thread
     constexpr int NSV = 32 * KU / kGT;      // units of a quarter of S (and dS') per thread
+    constexpr int RK = DK + 16;             // row length of the dk-column tiles
     static_assert(LY::total <= 80 * 1024, "two workgroups per CU");
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
     E *Ks = reinterpret_cast<E *>(smem + LY::oK), *TT = reinterpret_cast<E *>(smem + LY::oTT);
     float *Bt = reinterpret_cast<float *>(smem + LY::oB), *dba = reinterpret_cast<float *>(smem + LY::oDa);
     E *Ps = reinterpret_cast<E *>(smem + LY::oP), *Ss = reinterpret_cast<E *>(smem + LY::oS);
-    E *Gs = reinterpret_cast<E *>(smem + LY::oG), *Vs = reinterpret_cast<E *>(smem + LY::oV);
+    E *Gs = reinterpret_cast<E *>(smem + LY::oG);
     E *Ds = reinterpret_cast<E *>(smem + LY::oD), *YT = reinterpret_cast<E *>(smem + LY::oY);
     E *ZT = reinterpret_cast<E *>(smem + LY::oZ), *dZT = reinterpret_cast<E *>(smem + LY::odZ);
     E *dYT = reinterpret_cast<E *>(smem + LY::odY);
@@ -171,7 +193,7 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     E *dPT = reinterpret_cast<E *>(smem + LY::fdP), *dTT = reinterpret_cast<E *>(smem + LY::fdT);
     E *LT = reinterpret_cast<E *>(smem + LY::fL), *Ns = reinterpret_cast<E *>(smem + LY::fN);
     E *XT = reinterpret_cast<E *>(smem + LY::fX);
-    E *Q1 = XT; // Q for the last products
+    E *Q1 = dTT; // Q for the last products (over dT^T and N)
 
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     int g = lane >> 4, c = lane & 15;
@@ -212,7 +234,8 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const E *Tg = a.T_chunks + s * kChunk * kChunk;
 
     // ---- HBM loads: K, Q, T^T, beta, the first quarter ----
-    bf16x8 kv[NKV], qv[NKV], tv[2];
+    bf16x8 kv[NKV], qv[NKV];
+    bf16x4 tv[4];
 #pragma unroll
     for (int p = 0; p < NKV; ++p) {
         const int vi = p * kGT + tid, row = vi / KU, u = vi % KU;
@@ -221,9 +244,14 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         qv[p] = ld8(qg + off);
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) tv[p] = ld8(Tg + (uint32_t)(8 * (p * kGT + tid)));
+    for (int p = 0; p < 4; ++p) tv[p] = ld4(Tg + (uint32_t)(4 * (p * kGT + tid)));
     const float bt = (w == 0 && lane < nval) ? (float)reinterpret_cast<const E *>(a.beta)[(t0 + lane) * a.H + h] : 0.f;
-    bf16x8 sq[NSV], gq[NSV], vq, dq;
+    // per quarter: S, dS' and dO for LDS, and the V entries this lane's Y tiles
+    // start from (token 16 (2 tg + j) + 4 g + i, value 16 vt + c of the quarter),
+    // rows past the chunk's end masked to zero when used
+    const int vt = w & 1, tg = w >> 1;
+    bf16x8 sq[NSV], gq[NSV], dq;
+    E vy[2][4], vcur[2][4];
     auto load_quarter = [&](int tau) {
 #pragma unroll
         for (int p = 0; p < NSV; ++p) {
@@ -233,8 +261,14 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             gq[p] = ld8(Gg + off);
         }
         const uint32_t off = (uint32_t)(min(tid >> 2, nval - 1) * sv + 32 * tau + 8 * (tid & 3));
-        vq = ld8(vg + off);
         dq = ld8(dg + off);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * (2 * tg + j) + 4 * (lane >> 4) + i;
+                vy[j][i] = vg[(uint32_t)(min(row, nval - 1) * sv + 32 * tau + 16 * vt + (lane & 15))];
+            }
     };
     auto stage_quarter = [&]() {
 #pragma unroll
@@ -244,9 +278,11 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             st8(Gs + okk<DK>(row, 8 * u), gq[p]);
         }
         const int row = tid >> 2, u = tid & 3;
-        const bool on = row < nval;
-        st8(Vs + ov(row, 8 * u), on ? vq : bf16x8{});
-        st8(Ds + ov(row, 8 * u), on ? dq : bf16x8{});
+        st8(Ds + ov(row, 8 * u), row < nval ? dq : bf16x8{});
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vcur[j][i] = vy[j][i];
     };
     load_quarter(0);
 #pragma unroll
@@ -257,17 +293,18 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         st8(Q0 + okk<DK>(row, 8 * u), on ? qv[p] : bf16x8{});
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int vi = p * kGT + tid, row = vi >> 3, u = vi & 7;
-        st4(TT + o64(row, 8 * u), lo4(tv[p]));
-        st4(TT + o64(row, 8 * u + 4), hi4(tv[p]));
+    for (int p = 0; p < 4; ++p) {
+        const int vi = p * kGT + tid;
+        st4(TT + o64(vi >> 4, 4 * (vi & 15)), tv[p]);
     }
     if (w == 0) Bt[lane] = bt;
     stage_quarter();
     __syncthreads();
     if (NQ > 1) load_quarter(1);
 
-    renew(lane, g, c);
+    Offs o = offs<DK>(lane, vt);
+    g = o.g;
+    c = o.c;
     // ---- P = lower-inclusive(Q K^T): the ten 16 x 16 tiles (a, b <= a) ----
     {
         const int nt = w < 2 ? 3 : 2;
@@ -283,13 +320,13 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
-                acc = mfma32(ld8(Ks + okk<DK>(16 * tb + c, 32 * kb + 8 * g)), ld8(Q0 + okk<DK>(16 * ta + c, 32 * kb + 8 * g)),
+                acc = mfma32(ld8(Ks + o.r8kk + RK * 16 * tb + 32 * kb), ld8(Q0 + o.r8kk + RK * 16 * ta + 32 * kb),
                              acc);
             // acc[e] = k_{16 tb + 4 g + e} . q_{16 ta + c} = P[16 ta + c][16 tb + 4 g + e]
             const int row = 16 * ta + c, col = 16 * tb + 4 * g;
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = col + e > row ? 0.f : acc[e];
-            st4(Ps + o64(row, col), cvt4(acc));
+            st4(Ps + o.r64p + 72 * 16 * ta + 16 * tb, cvt4(acc));
         }
     }
     __syncthreads(); // P complete; Q's tiles free for Y^T ..
@@ -307,7 +344,6 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dQa[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         dKa[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int vt = w & 1, tg = w >> 1;
 #pragma unroll
     for (int tau = 0; tau < NQ; ++tau) {
         if (tau > 0) {
@@ -315,7 +351,9 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
             if (tau + 1 < NQ) load_quarter(tau + 1);
         }
-        renew(lane, g, c);
+        o = offs<DK>(lane, vt);
+        g = o.g;
+        c = o.c;
         // A1: Y = V - K S^T and dZ = P^T dO + K dS'^T for token tiles 2 tg, 2 tg + 1
         // and the 16 values 16 vt + c of the quarter
         bf16x4 yb[2], zb[2];
@@ -323,17 +361,19 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             bf16x8 sr[NKB], gr[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                sr[kb] = neg8(ld8(Ss + okk<DK>(16 * vt + c, 32 * kb + 8 * g)));
-                gr[kb] = ld8(Gs + okk<DK>(16 * vt + c, 32 * kb + 8 * g));
+                sr[kb] = neg8(ld8(Ss + o.r8kk + RK * 16 * vt + 32 * kb));
+                gr[kb] = ld8(Gs + o.r8kk + RK * 16 * vt + 32 * kb);
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int t = 2 * tg + j;
-                f32x4 ay = widen4(tr4(Vs + ov(tr_row(16 * t, g, c), tr_col(16 * vt, c))));
+                f32x4 ay;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ay[i] = 16 * t + 4 * g + i < nval ? (float)vcur[j][i] : 0.f;
                 f32x4 zk = {0.f, 0.f, 0.f, 0.f}, zp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    const bf16x8 kr = ld8(Ks + okk<DK>(16 * t + c, 32 * kb + 8 * g));
+                    const bf16x8 kr = ld8(Ks + o.r8kk + RK * 16 * t + 32 * kb);
                     ay = mfma32(kr, sr[kb], ay);
                     zk = mfma32(kr, gr[kb], zk);
                 }
@@ -341,16 +381,18 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2)
                     if (s2 >= t)
-                        zp = mfma16(tr4(Ps + o64(tr_row(16 * s2, g, c), tr_col(16 * t, c))),
-                                    tr4(Ds + ov(tr_row(16 * s2, g, c), tr_col(16 * vt, c))), zp);
+                        zp = mfma16(tr4(Ps + o.t64p + 72 * 16 * s2 + 16 * t),
+                                    tr4(Ds + o.tv + 32 * 16 * s2), zp);
                 yb[j] = cvt4(ay);
                 zb[j] = cvt4(zp + zk);
-                st4(YT + o64(16 * vt + c, 16 * t + 4 * g), yb[j]);
-                st4(dZT + o64(16 * vt + c, 16 * t + 4 * g), zb[j]);
+                st4(YT + o.r64 + 80 * 16 * vt + 16 * t, yb[j]);
+                st4(dZT + o.r64 + 80 * 16 * vt + 16 * t, zb[j]);
             }
         }
         __syncthreads();
-        renew(lane, g, c);
+        o = offs<DK>(lane, vt);
+        g = o.g;
+        c = o.c;
         // A2: Z = T Y and dY = T^T dZ for the same tiles
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -359,44 +401,46 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
                 if (s2 <= t) {
-                    const bf16x4 yf = (s2 >> 1) == tg ? yb[s2 & 1] : ld4(YT + o64(16 * vt + c, 16 * s2 + 4 * g));
-                    z = mfma16(tr4(TT + o64(tr_row(16 * s2, g, c), tr_col(16 * t, c))), yf, z);
+                    const bf16x4 yf = (s2 >> 1) == tg ? yb[s2 & 1] : ld4(YT + o.r64 + 80 * 16 * vt + 16 * s2);
+                    z = mfma16(tr4(TT + o.t64 + 80 * (16 * s2) + 16 * t), yf, z);
                 }
                 if (s2 >= t) {
-                    const bf16x4 zf = (s2 >> 1) == tg ? zb[s2 & 1] : ld4(dZT + o64(16 * vt + c, 16 * s2 + 4 * g));
-                    dy = mfma16(ld4(TT + o64(16 * t + c, 16 * s2 + 4 * g)), zf, dy);
+                    const bf16x4 zf = (s2 >> 1) == tg ? zb[s2 & 1] : ld4(dZT + o.r64 + 80 * 16 * vt + 16 * s2);
+                    dy = mfma16(ld4(TT + o.r64 + 80 * 16 * t + 16 * s2), zf, dy);
                 }
             }
-            st4(ZT + o64(16 * vt + c, 16 * t + 4 * g), cvt4(z));
-            st4(dYT + o64(16 * vt + c, 16 * t + 4 * g), cvt4(dy));
+            st4(ZT + o.r64 + 80 * 16 * vt + 16 * t, cvt4(z));
+            st4(dYT + o.r64 + 80 * 16 * vt + 16 * t, cvt4(dy));
         }
         __syncthreads();
-        renew(lane, g, c);
+        o = offs<DK>(lane, vt);
+        g = o.g;
+        c = o.c;
         // B: the quarter's share of the sums, token rows 16 w .. 16 w + 15
         {
-            const bf16x8 aO = cat8(ld4(Ds + ov(16 * w + c, 4 * g)), ld4(Ds + ov(16 * w + c, 16 + 4 * g)));
-            const bf16x8 aZ = cat8(tr4(ZT + o64(tr_row(0, g, c), tr_col(16 * w, c))),
-                                   tr4(ZT + o64(tr_row(16, g, c), tr_col(16 * w, c))));
-            const bf16x8 adZ = cat8(tr4(dZT + o64(tr_row(0, g, c), tr_col(16 * w, c))),
-                                    tr4(dZT + o64(tr_row(16, g, c), tr_col(16 * w, c))));
-            const bf16x8 adYn = neg8(cat8(tr4(dYT + o64(tr_row(0, g, c), tr_col(16 * w, c))),
-                                          tr4(dYT + o64(tr_row(16, g, c), tr_col(16 * w, c)))));
+            const bf16x8 aO = cat8(ld4(Ds + o.rv0 + 32 * 16 * w), ld4(Ds + o.rv1 + 32 * 16 * w));
+            const bf16x8 aZ = cat8(tr4(ZT + o.t64 + 80 * (0) + 16 * w),
+                                   tr4(ZT + o.t64 + 80 * (16) + 16 * w));
+            const bf16x8 adZ = cat8(tr4(dZT + o.t64 + 80 * (0) + 16 * w),
+                                    tr4(dZT + o.t64 + 80 * (16) + 16 * w));
+            const bf16x8 adYn = neg8(cat8(tr4(dYT + o.t64 + 80 * (0) + 16 * w),
+                                          tr4(dYT + o.t64 + 80 * (16) + 16 * w)));
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
                 if (s2 > w) break; // dP and dT are lower-inclusive
-                const bf16x8 bZ = cat8(tr4(ZT + o64(tr_row(0, g, c), tr_col(16 * s2, c))),
-                                       tr4(ZT + o64(tr_row(16, g, c), tr_col(16 * s2, c))));
-                const bf16x8 bY = cat8(tr4(YT + o64(tr_row(0, g, c), tr_col(16 * s2, c))),
-                                       tr4(YT + o64(tr_row(16, g, c), tr_col(16 * s2, c))));
+                const bf16x8 bZ = cat8(tr4(ZT + o.t64 + 80 * (0) + 16 * s2),
+                                       tr4(ZT + o.t64 + 80 * (16) + 16 * s2));
+                const bf16x8 bY = cat8(tr4(YT + o.t64 + 80 * (0) + 16 * s2),
+                                       tr4(YT + o.t64 + 80 * (16) + 16 * s2));
                 pp[s2] = mfma32(aO, bZ, pp[s2]);
                 tt[s2] = mfma32(adZ, bY, tt[s2]);
             }
 #pragma unroll
             for (int m = 0; m < NMT; ++m) {
-                const bf16x8 bS = cat8(tr4(Ss + okk<DK>(tr_row(0, g, c), tr_col(16 * m, c))),
-                                       tr4(Ss + okk<DK>(tr_row(16, g, c), tr_col(16 * m, c))));
-                const bf16x8 bG = cat8(tr4(Gs + okk<DK>(tr_row(0, g, c), tr_col(16 * m, c))),
-                                       tr4(Gs + okk<DK>(tr_row(16, g, c), tr_col(16 * m, c))));
+                const bf16x8 bS = cat8(tr4(Ss + o.tkk + RK * (0) + 16 * m),
+                                       tr4(Ss + o.tkk + RK * (16) + 16 * m));
+                const bf16x8 bG = cat8(tr4(Gs + o.tkk + RK * (0) + 16 * m),
+                                       tr4(Gs + o.tkk + RK * (16) + 16 * m));
                 dQa[m] = mfma32(aO, bS, dQa[m]);
                 dKa[m] = mfma32(aZ, bG, dKa[m]);
                 dKa[m] = mfma32(adYn, bS, dKa[m]);
@@ -406,7 +450,9 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 
     // ---- finish ----
-    renew(lane, g, c);
+    o = offs<DK>(lane, vt);
+    g = o.g;
+    c = o.c;
     // dP^T and dT^T (lower-inclusive), and L^T from this wave's Gram rows
     // gm[j][i] = k_t . k_{16 j + c}, t = 16 w + 4 g + i
 #pragma unroll
@@ -418,8 +464,8 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             x[i] = on ? x[i] : 0.f;
             y[i] = on ? y[i] : 0.f;
         }
-        st4(dPT + o64(16 * s2 + c, 16 * w + 4 * g), cvt4(x));
-        st4(dTT + o64(16 * s2 + c, 16 * w + 4 * g), cvt4(y));
+        st4(dPT + o.r64 + 80 * 16 * s2 + 16 * w, cvt4(x));
+        st4(dTT + o.r64 + 80 * 16 * s2 + 16 * w, cvt4(y));
     }
     f32x4 gm[4];
 #pragma unroll
@@ -427,15 +473,17 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         gm[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-            gm[j] = mfma32(ld8(Ks + okk<DK>(16 * w + c, 32 * kb + 8 * g)), ld8(Ks + okk<DK>(16 * j + c, 32 * kb + 8 * g)),
+            gm[j] = mfma32(ld8(Ks + o.r8kk + RK * 16 * w + 32 * kb), ld8(Ks + o.r8kk + RK * 16 * j + 32 * kb),
                            gm[j]);
         f32x4 l = gm[j];
 #pragma unroll
         for (int i = 0; i < 4; ++i) l[i] = 16 * j + c < 16 * w + 4 * g + i ? l[i] : 0.f;
-        st4(LT + o64(16 * j + c, 16 * w + 4 * g), cvt4(l));
+        st4(LT + o.r64 + 80 * 16 * j + 16 * w, cvt4(l));
     }
     __syncthreads();
-    renew(lane, g, c);
+    o = offs<DK>(lane, vt);
+    g = o.g;
+    c = o.c;
     // N^T = I - L^T T^T, row block w (upper triangular: blocks b >= w), stored as N
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -443,34 +491,38 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (b >= w) {
 #pragma unroll
             for (int k0 = 0; k0 < 64; k0 += 32)
-                acc = mfma32(cat8(ld4(LT + o64(16 * w + c, k0 + 4 * g)), ld4(LT + o64(16 * w + c, k0 + 16 + 4 * g))),
-                             cat8(tr4(TT + o64(tr_row(k0, g, c), tr_col(16 * b, c))),
-                                  tr4(TT + o64(tr_row(k0 + 16, g, c), tr_col(16 * b, c)))),
+                acc = mfma32(cat8(ld4(LT + o.r64 + 80 * 16 * w + k0), ld4(LT + o.r64 + 80 * 16 * w + k0 + 16)),
+                             cat8(tr4(TT + o.t64 + 80 * (k0) + 16 * b),
+                                  tr4(TT + o.t64 + 80 * (k0 + 16) + 16 * b)),
                              acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = (16 * w + 4 * g + i == 16 * b + c ? 1.f : 0.f) - acc[i];
-        st4(Ns + o64(16 * b + c, 16 * w + 4 * g), cvt4(acc));
+        st4(Ns + o.r64 + 80 * 16 * b + 16 * w, cvt4(acc));
     }
     __syncthreads();
-    renew(lane, g, c);
+    o = offs<DK>(lane, vt);
+    g = o.g;
+    c = o.c;
     // X = N^T dT: dbeta_a = diag X; (X diag(beta))^T to LDS
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k0 = 0; k0 < 64; k0 += 32)
-            x = mfma32(cat8(tr4(Ns + o64(tr_row(k0, g, c), tr_col(16 * w, c))),
-                            tr4(Ns + o64(tr_row(k0 + 16, g, c), tr_col(16 * w, c)))),
-                       cat8(ld4(dTT + o64(16 * j + c, k0 + 4 * g)), ld4(dTT + o64(16 * j + c, k0 + 16 + 4 * g))), x);
+            x = mfma32(cat8(tr4(Ns + o.t64 + 80 * (k0) + 16 * w),
+                            tr4(Ns + o.t64 + 80 * (k0 + 16) + 16 * w)),
+                       cat8(ld4(dTT + o.r64 + 80 * 16 * j + k0), ld4(dTT + o.r64 + 80 * 16 * j + k0 + 16)), x);
         const float bc = Bt[16 * j + c];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (j == w && c == 4 * g + i) dba[16 * w + 4 * g + i] = x[i];
-        st4(XT + o64(16 * j + c, 16 * w + 4 * g), cvt4(x * bc));
+        st4(XT + o.r64 + 80 * 16 * j + 16 * w, cvt4(x * bc));
     }
     __syncthreads();
-    renew(lane, g, c);
+    o = offs<DK>(lane, vt);
+    g = o.g;
+    c = o.c;
     // dA = strict-lower(-(X diag(beta)) N^T); dbeta_b = sum_j dA_tj gm_tj; dL = diag(beta) dA,
     // stored as dL^T over L^T
     float dbb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -479,9 +531,9 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         f32x4 da = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k0 = 0; k0 < 64; k0 += 32)
-            da = mfma32(cat8(tr4(XT + o64(tr_row(k0, g, c), tr_col(16 * w, c))),
-                             tr4(XT + o64(tr_row(k0 + 16, g, c), tr_col(16 * w, c)))),
-                        cat8(ld4(Ns + o64(16 * j + c, k0 + 4 * g)), ld4(Ns + o64(16 * j + c, k0 + 16 + 4 * g))), da);
+            da = mfma32(cat8(tr4(XT + o.t64 + 80 * (k0) + 16 * w),
+                             tr4(XT + o.t64 + 80 * (k0 + 16) + 16 * w)),
+                        cat8(ld4(Ns + o.r64 + 80 * 16 * j + k0), ld4(Ns + o.r64 + 80 * 16 * j + k0 + 16)), da);
         f32x4 dl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -490,7 +542,7 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             dbb[i] += dai * gm[j][i];
             dl[i] = Bt[t] * dai;
         }
-        st4(LT + o64(16 * j + c, 16 * w + 4 * g), cvt4(dl));
+        st4(LT + o.r64 + 80 * 16 * j + 16 * w, cvt4(dl));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) // sum over the 16 lanes of the row group
@@ -503,28 +555,30 @@ __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         st8(Q1 + okk<DK>(row, 8 * u), row < nval ? qv[p] : bf16x8{});
     }
     __syncthreads();
-    renew(lane, g, c);
+    o = offs<DK>(lane, vt);
+    g = o.g;
+    c = o.c;
     // dQ += dP K;  dK += dP^T Q + dL K + dL^T K
     bf16x8 aPc[2], aPr[2], aLc[2], aLr[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
         const int k0 = 32 * h2;
-        aPc[h2] = cat8(tr4(dPT + o64(tr_row(k0, g, c), tr_col(16 * w, c))),
-                       tr4(dPT + o64(tr_row(k0 + 16, g, c), tr_col(16 * w, c))));
-        aPr[h2] = cat8(ld4(dPT + o64(16 * w + c, k0 + 4 * g)), ld4(dPT + o64(16 * w + c, k0 + 16 + 4 * g)));
-        aLc[h2] = cat8(tr4(LT + o64(tr_row(k0, g, c), tr_col(16 * w, c))),
-                       tr4(LT + o64(tr_row(k0 + 16, g, c), tr_col(16 * w, c))));
-        aLr[h2] = cat8(ld4(LT + o64(16 * w + c, k0 + 4 * g)), ld4(LT + o64(16 * w + c, k0 + 16 + 4 * g)));
+        aPc[h2] = cat8(tr4(dPT + o.t64 + 80 * (k0) + 16 * w),
+                       tr4(dPT + o.t64 + 80 * (k0 + 16) + 16 * w));
+        aPr[h2] = cat8(ld4(dPT + o.r64 + 80 * 16 * w + k0), ld4(dPT + o.r64 + 80 * 16 * w + k0 + 16));
+        aLc[h2] = cat8(tr4(LT + o.t64 + 80 * (k0) + 16 * w),
+                       tr4(LT + o.t64 + 80 * (k0 + 16) + 16 * w));
+        aLr[h2] = cat8(ld4(LT + o.r64 + 80 * 16 * w + k0), ld4(LT + o.r64 + 80 * 16 * w + k0 + 16));
     }
 #pragma unroll
     for (int m = 0; m < NMT; ++m)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const int k0 = 32 * h2;
-            const bf16x8 kc = cat8(tr4(Ks + okk<DK>(tr_row(k0, g, c), tr_col(16 * m, c))),
-                                   tr4(Ks + okk<DK>(tr_row(k0 + 16, g, c), tr_col(16 * m, c))));
-            const bf16x8 qc = cat8(tr4(Q1 + okk<DK>(tr_row(k0, g, c), tr_col(16 * m, c))),
-                                   tr4(Q1 + okk<DK>(tr_row(k0 + 16, g, c), tr_col(16 * m, c))));
+            const bf16x8 kc = cat8(tr4(Ks + o.tkk + RK * (k0) + 16 * m),
+                                   tr4(Ks + o.tkk + RK * (k0 + 16) + 16 * m));
+            const bf16x8 qc = cat8(tr4(Q1 + o.tkk + RK * (k0) + 16 * m),
+                                   tr4(Q1 + o.tkk + RK * (k0 + 16) + 16 * m));
             dQa[m] = mfma32(aPc[h2], kc, dQa[m]);
             dKa[m] = mfma32(aPr[h2], qc, dKa[m]);
             dKa[m] = mfma32(aLc[h2], kc, dKa[m]);
