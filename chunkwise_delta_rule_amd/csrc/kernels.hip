@@ -1659,36 +1659,51 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
 // them. The kernel therefore runs that algorithm on sub-chunks of 16 tokens
 // (the page's exactness holds for every chunk size): with gamma the
 // per-channel prefix sums of ln a inside a sub-chunk,
-//   Kl = K * exp(gamma),  Ql = Q * exp(gamma)          (-Kl <-K, Ql <-Q; factors <= 1;
-//                                                        Kl is kept negated so that Y
-//                                                        needs no negated copy of S)
+//   Kl = K * exp(gamma),  Ql = Q * exp(gamma)          (factors <= 1; -Kl is
+//                                                        stored, so that Y needs
+//                                                        no negated copy of S)
 //   Kr = K * exp(-gamma)                               (factors >= 1, bounded
 //                                                        by 16 tokens of decay)
-//   Kf = K * exp(gamma_16 - gamma)                     (->K; factors <= 1)
+//   Kf = K * exp(gamma_16 - gamma)                     (factors <= 1)
 //   L = Kl Kr^T (strictly lower),  A = Ql Kr^T (lower-inclusive),
-//   T = (I + diag(beta) L)^-1 diag(beta)               (the DPP diagonal solve)
+//   T = (I + diag(beta) L)^-1 diag(beta)               (DPP forward substitution)
 //   Y = V - Kl S^T,  Z = T Y,  O = Ql S^T + A Z,  S <- S Diag(exp(gamma_16)) + Z^T Kf.
-// Staging still moves 64-token chunks. Four waves; each wave holds 16 state
-// rows, computes the Gram/score tiles and the solve of one sub-chunk, then
-// runs the four sub-chunks' products for its rows in order.
 // Strong decay: Kr's factor exp(-gamma) is only safe while |gamma| stays
 // moderate. A sub-chunk in which some channel's prefix sum leaves
 // [-kKdaLim, kKdaLim] (base 2) takes L and A from an exact path instead:
 // every entry k_l . (exp(gamma_l - gamma_m) * k_m) (or q_l . ...) is formed
 // with the decay factor of the pair itself, which lies in (0, 1] for
-// decays, each scaling thread adding its own channels and a 16-lane row
-// reduction adding the threads. Kl, Ql, Kf and exp(gamma_16) only ever carry
+// decays, each lane adding its own channels and a 16-lane row reduction
+// adding the lanes. Kl, Ql, Kf and exp(gamma_16) only ever carry
 // later-minus-earlier differences, so the chain is exact for any decay.
+//
+// One workgroup of 8 waves per (work item, 64 state rows), in two stages:
+//   waves 0-3  (chain) hold 16 state rows each in fp32 registers and run the
+//              four sub-chunks of chunk r in order;
+//   waves 4-7  (prep) wave 4 + j owns sub-chunk j of chunk r + 1: from its
+//              16 tokens' keys, queries and log decays (loaded into registers
+//              a chunk ahead, two channels per lane at dk = 128) it forms the
+//              prefix sums, the scaled copies, the 16 x 16 blocks L and A
+//              (or their exact form) and T, all in its own rows of LDS, so
+//              the prep stages need no barrier among themselves.
+// One barrier per chunk; the chain reads one half of a double buffer while
+// the prep waves fill the other. Wave w and w + 4 share a SIMD.
 // ---------------------------------------------------------------------------
 template <int DK> struct KdaLds {
     using L = Ld<__bf16, DK>;
-    static constexpr size_t oK = 0, oQ = oK + L::szK, oKr = oQ + L::szK, oKf = oKr + L::szK;
-    static constexpr size_t oE = oKf + L::szK;                       // exp(gamma_16), fp32 [4][DK]
-    static constexpr size_t oV = oE + sizeof(float) * 4 * DK, oB = oV + L::szV, oA = oB + 256;
-    static constexpr size_t oT = oA + L::szA, oN = oT + L::szT, oP = oN + L::szN;
-    // exact path: per sub-chunk, row partial sums of the 120 entries of L and
-    // the 136 entries of A ([4][256][4] fp32), and the per-sub-chunk flags
-    static constexpr size_t oX = oP + L::szT, oF = oX + sizeof(float) * 4 * 256 * 4, total = oF + 16;
+    static constexpr int kBL = 24;                                    // row length of a 16 x 16 bf16 block
+    static constexpr size_t szBlk = 16 * kBL * 2;
+    // buffer b: -Kl, Ql, Kf [64][L::K]; exp(gamma_16) fp32 [4][DK]; T^T and A diagonal blocks [4][16][kBL]
+    static constexpr size_t oKL = 0, oQL = L::szK, oKF = 2 * L::szK, oE = 3 * L::szK;
+    static constexpr size_t oTB = oE + sizeof(float) * 4 * DK, oPB = oTB + 4 * szBlk, szBuf = oPB + 4 * szBlk;
+    // prep only: Kr [64][L::K]; the exact path's row partial sums of one
+    // sub-chunk (256 entries x 4 rows of lanes, fp32), over that sub-chunk's
+    // own Kr rows where they fit; the fp32 blocks of diag(beta) L [4][16][20]
+    static constexpr size_t oKr = 2 * szBuf, szX = sizeof(float) * 256 * 4;
+    static constexpr bool kXoverKr = (size_t)16 * L::K * 2 >= szX;
+    static constexpr size_t oX = kXoverKr ? oKr : oKr + L::szK;
+    static constexpr size_t oAs = kXoverKr ? oKr + L::szK : oX + 4 * szX;
+    static constexpr size_t total = oAs + sizeof(float) * 4 * 16 * 20;
 };
 
 // Compile-time loop: f(Int<I>{}) for I = B..E-1 (step indices stay constants).
@@ -1721,241 +1736,296 @@ __device__ inline float row_scan16(float x) {
     return x;
 }
 
+constexpr int kKdaThreads = 512;
+
+// Compiler-level ordering of LDS accesses within one wave (no instruction).
+__device__ inline void lds_order() { asm volatile("" ::: "memory"); }
+
 template <int DK, int DV, bool WO>
-__global__ __launch_bounds__(kThreads) void kda_chain_kernel(const ChainArgs a) {
+__global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs a) {
     using E = __bf16;
     using TR = Tr<E>;
     using F = typename TR::F;
     using L = Ld<E, DK>;
     using LY = KdaLds<DK>;
-    using PH = Phases<E, DK>;
-    constexpr int NMT = DK / 16;
+    constexpr int NMT = DK / 16, CPL = DK / 64, BL = LY::kBL;
     static_assert(LY::total <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
-    E *Ks = reinterpret_cast<E *>(smem + LY::oK), *Qs = reinterpret_cast<E *>(smem + LY::oQ);
-    E *Kr = reinterpret_cast<E *>(smem + LY::oKr), *Kf = reinterpret_cast<E *>(smem + LY::oKf);
-    float *E16 = reinterpret_cast<float *>(smem + LY::oE);
-    E *Vs = reinterpret_cast<E *>(smem + LY::oV);
-    float *Bs = reinterpret_cast<float *>(smem + LY::oB), *As = reinterpret_cast<float *>(smem + LY::oA);
-    E *TsT = reinterpret_cast<E *>(smem + LY::oT), *NsT = reinterpret_cast<E *>(smem + LY::oN);
-    E *Ps = reinterpret_cast<E *>(smem + LY::oP);
-    float *Xp = reinterpret_cast<float *>(smem + LY::oX); // exact path: [j][entry][row] partial sums
-    int *exact = reinterpret_cast<int *>(smem + LY::oF);  // exact path taken by sub-chunk j
-
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = lane >> 4, c16 = lane & 15;
     // the work item: a token range of one (sequence, head), 64 state rows,
     // where they start and end (dense, packed, or a group of a split sequence)
     const Work wk = decode_work<DK, DV>(a);
-    const int h = wk.h, row0 = wk.row0, len = wk.len;
+    const int h = wk.h, len = wk.len;
     const int64_t tok0 = wk.tok0, sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
     const int NC = (len + kChunk - 1) / kChunk;
-    Stager<E, DK> sg = make_stager<E, DK, DV, false>(a, wk, tid); // a.g is unused here: no scalar decay
-    const bool has_v = wk.has_v;
-    const float *gg = a.gk + tok0 * sqk + (int64_t)h * DK;
-    E *og = WO ? reinterpret_cast<E *>(a.o) + tok0 * sv + (int64_t)h * DV + row0 : nullptr;
+    auto rows_of = [&](int c) { return min(kChunk, len - c * kChunk); };
 
-    // state rows 16w + c16 of this tile: Sacc[m][i] = S[row0 + 16w + c16][16m + 4g + i]
-    f32x4 Sacc[NMT];
-    state_in<DK>(Sacc, wk, w, g, c16);
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    constexpr int NP = DK / 2; // channel pairs; the scaling pass has one thread per (pair, sub-chunk)
-    static_assert(4 * NP <= kThreads, "one scaling item per thread");
-    const int sj = tid / NP, sd = 2 * (tid % NP); // this thread's sub-chunk and channel pair
-    const bool scaler = tid < 4 * NP;
-
-    // Loads of chunk c into registers; issued one chunk ahead so that they
-    // overlap the previous chunk's products. The log decays go straight into
-    // the layout of the scaling pass: 16 tokens of one channel pair.
-    f32x2 gq[16];
-    auto load_chunk = [&](int c) {
-        sg.load(c);
-        const int n = min(kChunk, len - c * kChunk);
-        if (scaler) {
+    if (wave < 4) {
+        // ---- chain: state rows 16 w + c16, Sacc[m][i] = S[row0 + 16w + c16][16m + 4g + i] ----
+        const int w = wave;
+        f32x4 Sacc[NMT];
+        state_in<DK>(Sacc, wk, w, g, c16);
+        const bool has_v = wk.has_v;
+        const E *vg = reinterpret_cast<const E *>(a.v) + tok0 * sv + (int64_t)h * DV + wk.row0 + 16 * w + c16;
+        E *og = WO ? reinterpret_cast<E *>(a.o) + tok0 * sv + (int64_t)h * DV + wk.row0 + 16 * w + c16 : nullptr;
+        // V[64 c + 16 j + 4 g + i][this lane's row], entry 4 j + i, a chunk ahead
+        E vn[16], vc[16];
+        auto load_v = [&](int c) {
+            const int n = rows_of(c);
 #pragma unroll
-            for (int l = 0; l < 16; ++l)
-                gq[l] = *reinterpret_cast<const f32x2 *>(gg + ((int64_t)c * kChunk + min(16 * sj + l, n - 1)) * sqk + sd);
-        }
-    };
-    // The output tile of a chunk ([64 tokens][64 values], bf16) is assembled in
-    // LDS over the Gram rows (free once the solve is done) and written as
-    // whole 128-byte rows after the next barrier.
-    E *Os = reinterpret_cast<E *>(As);
-    constexpr int LO = 64 + 8;
-    static_assert(sizeof(E) * 64 * LO <= L::szA, "output tile fits over the Gram rows");
-    auto flush_o = [&](int c) {
-        const int n = min(kChunk, len - c * kChunk);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int vi = p * kThreads + tid, row = vi / 8, cv = vi % 8;
-            if (row < n)
-                *reinterpret_cast<typename TR::V *>(og + ((int64_t)c * kChunk + row) * sv + 8 * cv) =
-                    *reinterpret_cast<const typename TR::V *>(Os + row * LO + 8 * cv);
-        }
-    };
-    if (NC > 0) load_chunk(0);
-    for (int r = 0; r < NC; ++r) {
-        const int nval = min(kChunk, len - r * kChunk);
-        __syncthreads(); // the previous chunk's reads are done
-        if (WO && r > 0) flush_o(r - 1);
-        sg.store_kqb(Ks, Qs, Bs, nullptr);
-        sg.store_v(Vs);
-        __syncthreads();
-        // Per-channel prefix sums inside each sub-chunk (base 2) and the scaled
-        // operands. Thread (channel pair, sub-chunk j) holds its 16 tokens'
-        // decays, reads their keys and queries at once, then walks them.
-        // Tokens past the end of the sequence have zero log decay.
-        if (scaler) {
-            const int j = sj, d = sd;
-            {
-                bf16x2 kl[16], ql[16];
-#pragma unroll
-                for (int l = 0; l < 16; ++l) {
-                    const int row = 16 * j + l;
-                    kl[l] = *reinterpret_cast<const bf16x2 *>(Ks + row * L::K + d);
-                    ql[l] = *reinterpret_cast<const bf16x2 *>(Qs + row * L::K + d);
-                }
-                f32x2 gam[16], acc = {0.f, 0.f};
-                bool wide = false; // a prefix sum outside the factored path's range
-#pragma unroll
-                for (int l = 0; l < 16; ++l) {
-                    if (16 * j + l < nval) acc += gq[l] * 1.44269504088896340736f;
-                    gam[l] = acc;
-                    wide |= !(fabsf(acc[0]) <= kKdaLim && fabsf(acc[1]) <= kKdaLim);
-                }
-                const f32x2 e16 = {__builtin_amdgcn_exp2f(acc[0]), __builtin_amdgcn_exp2f(acc[1])};
-#pragma unroll
-                for (int l = 0; l < 16; ++l) {
-                    const int row = 16 * j + l;
-                    const f32x2 kv = {(float)kl[l][0], (float)kl[l][1]}, qv = {(float)ql[l][0], (float)ql[l][1]};
-                    const f32x2 el = {__builtin_amdgcn_exp2f(gam[l][0]), __builtin_amdgcn_exp2f(gam[l][1])};
-                    const f32x2 er = {__builtin_amdgcn_exp2f(-gam[l][0]), __builtin_amdgcn_exp2f(-gam[l][1])};
-                    // exp(gamma_16 - gamma) <= 1, from the difference itself
-                    const f32x2 ef = {__builtin_amdgcn_exp2f(acc[0] - gam[l][0]), __builtin_amdgcn_exp2f(acc[1] - gam[l][1])};
-                    const f32x2 a1 = -(kv * el), a2 = qv * el, a3 = kv * er, a4 = kv * ef;
-                    *reinterpret_cast<bf16x2 *>(Ks + row * L::K + d) = bf16x2{(__bf16)a1[0], (__bf16)a1[1]};
-                    *reinterpret_cast<bf16x2 *>(Qs + row * L::K + d) = bf16x2{(__bf16)a2[0], (__bf16)a2[1]};
-                    *reinterpret_cast<bf16x2 *>(Kr + row * L::K + d) = bf16x2{(__bf16)a3[0], (__bf16)a3[1]};
-                    *reinterpret_cast<bf16x2 *>(Kf + row * L::K + d) = bf16x2{(__bf16)a4[0], (__bf16)a4[1]};
-                }
-                *reinterpret_cast<f32x2 *>(E16 + j * DK + d) = e16;
-                // Exact path, wave-uniform: taken by every sub-chunk of this
-                // wave when any of them needs it (all lanes of the wave are
-                // scaling threads). Lane (row rw, c) of sub-chunk j adds its
-                // two channels of every entry; the 16-lane row scan leaves the
-                // row's sum in its lane 15, which stores it.
-                const bool wave_exact = __builtin_amdgcn_ballot_w64(wide) != 0;
-                constexpr int RPS = NP / 16; // 16-lane rows per sub-chunk
-                if (lane == 0 || lane == 32) exact[j] = wave_exact ? 1 : 0;
-                if (wave_exact) {
-                    float *xp = Xp + j * 256 * 4 + ((lane >> 4) % RPS);
-                    const bool last = c16 == 15;
-                    static_for<0, 16>([&](auto lc) {
-                        constexpr int l = decltype(lc)::value;
-                        const f32x2 kv = {(float)kl[l][0], (float)kl[l][1]}, qv = {(float)ql[l][0], (float)ql[l][1]};
-                        static_for<0, l + 1>([&](auto mc) {
-                            constexpr int m = decltype(mc)::value;
-                            const f32x2 km = {(float)kl[m][0], (float)kl[m][1]};
-                            const f32x2 t = km * f32x2{__builtin_amdgcn_exp2f(gam[l][0] - gam[m][0]),
-                                                       __builtin_amdgcn_exp2f(gam[l][1] - gam[m][1])};
-                            const float sa = row_scan16(qv[0] * t[0] + qv[1] * t[1]);
-                            if (last) xp[4 * (120 + l * (l + 1) / 2 + m)] = sa; // A entry (l, m)
-                            if constexpr (m < l) {
-                                const float sl = row_scan16(kv[0] * t[0] + kv[1] * t[1]);
-                                if (last) xp[4 * (l * (l - 1) / 2 + m)] = sl; // L entry (l, m)
-                            }
-                        });
-                    });
-                }
+            for (int x = 0; x < 16; ++x) {
+                const int row = 16 * (x >> 2) + 4 * g + (x & 3);
+                vn[x] = has_v ? vg[((int64_t)c * kChunk + min(row, n - 1)) * sv] : TR::fromf(0.f);
             }
-        }
-        if (r + 1 < NC) load_chunk(r + 1);
-        __syncthreads();
-        // Sub-chunk w: L = Kl Kr^T (strictly lower, times beta of the row) and
-        // A = Ql Kr^T. Ks holds -Kl, so the products give -L. On the exact
-        // path the entries are the row sums of the scaling threads instead.
-        if (exact[w]) {
-            constexpr int RPS = (DK / 2) / 16;
-            const float *xp = Xp + w * 256 * 4;
+        };
+        if (NC > 0) load_v(0);
+        __syncthreads(); // chunk 0 prepared
+        for (int r = 0; r < NC; ++r) {
+            const int n = rows_of(r);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int idx = 64 * p + lane, l = idx >> 4, m = idx & 15, row = 16 * w + l;
-                float sl = 0.f, sa = 0.f;
-                if (m <= l) {
+            for (int x = 0; x < 16; ++x) vc[x] = vn[x];
+            if (r + 1 < NC) load_v(r + 1);
+            const unsigned char *B = smem + (r & 1) * LY::szBuf;
+            const E *KLb = reinterpret_cast<const E *>(B + LY::oKL), *QLb = reinterpret_cast<const E *>(B + LY::oQL);
+            const E *KFb = reinterpret_cast<const E *>(B + LY::oKF);
+            const E *TBb = reinterpret_cast<const E *>(B + LY::oTB), *PBb = reinterpret_cast<const E *>(B + LY::oPB);
+            const float *Eb = reinterpret_cast<const float *>(B + LY::oE);
 #pragma unroll
-                    for (int q = 0; q < RPS; ++q) {
-                        sa += xp[4 * (120 + l * (l + 1) / 2 + m) + q];
-                        if (m < l) sl += xp[4 * (l * (l - 1) / 2 + m) + q];
+            for (int j = 0; j < 4; ++j) {
+                // every LDS operand of the sub-chunk first, so their latency is paid once
+                F kl[NMT], ql[NMT], kf[NMT];
+                f32x4 ef[NMT];
+#pragma unroll
+                for (int m = 0; m < NMT; ++m) {
+                    kl[m] = ldrow(KLb, L::K, 16 * j + c16, 16 * m, g);
+                    ql[m] = ldrow(QLb, L::K, 16 * j + c16, 16 * m, g);
+                    kf[m] = TR::ldcol(KFb, L::K, 16 * j, 16 * m, g, c16);
+                    ef[m] = *reinterpret_cast<const f32x4 *>(Eb + j * DK + 16 * m + 4 * g);
+                }
+                const F tf = TR::ldcol(TBb + j * 16 * BL, BL, 0, 0, g, c16); // row c16 of T_jj
+                const F pf = ldrow(PBb + j * 16 * BL, BL, c16, 0, g);         // row c16 of A_jj
+                sched_fence();
+                F SB[NMT];
+#pragma unroll
+                for (int m = 0; m < NMT; ++m) SB[m] = TR::cvt(Sacc[m]);
+                f32x4 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = 16 * j + 4 * g + i < n ? (float)vc[4 * j + i] : 0.f;
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < NMT; m += 2) { // 16x16x32 products over dk blocks m, m + 1; KL holds -Kl
+                    y = TR::mma32(y, kl[m], kl[m + 1], SB[m], SB[m + 1]);
+                    o = TR::mma32(o, ql[m], ql[m + 1], SB[m], SB[m + 1]);
+                }
+                const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+                const F zb = TR::cvt(TR::mma16(z0, tf, TR::cvt(y)));
+                o += TR::mma16(z0, pf, zb); // its own accumulator: o comes from 16x16x32 products
+                if (WO && has_v) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tok = 16 * j + 4 * g + i;
+                        if (tok < n) og[((int64_t)r * kChunk + tok) * sv] = TR::fromf(o[i]);
                     }
                 }
-                As[row * L::A + 16 * w + m] = m < l ? Bs[row] * sl : 0.f;
-                Ps[row * L::T + 16 * w + m] = TR::fromf(m <= l ? sa : 0.f);
-            }
-        } else {
-            f32x4 lt = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < NMT; m += 2) { // 16x16x32 products over dk blocks m, m + 1
-                const F kr0 = ldrow(Kr, L::K, 16 * w + c16, 16 * m, g), kr1 = ldrow(Kr, L::K, 16 * w + c16, 16 * m + 16, g);
-                lt = TR::mma32(lt, ldrow(Ks, L::K, 16 * w + c16, 16 * m, g), ldrow(Ks, L::K, 16 * w + c16, 16 * m + 16, g),
-                               kr0, kr1);
-                at = TR::mma32(at, ldrow(Qs, L::K, 16 * w + c16, 16 * m, g), ldrow(Qs, L::K, 16 * w + c16, 16 * m + 16, g),
-                               kr0, kr1);
+                for (int m = 0; m < NMT; ++m) Sacc[m] = TR::mma16(Sacc[m] * ef[m], kf[m], zb);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * w + 4 * g + i;
-                As[row * L::A + 16 * w + c16] = c16 < 4 * g + i ? -Bs[row] * lt[i] : 0.f;
-                Ps[row * L::T + 16 * w + c16] = TR::fromf(c16 <= 4 * g + i ? at[i] : 0.f);
-            }
+            __syncthreads();
         }
-        __syncthreads();
-        {
-            typename PH::DiagFrags df;
-            PH::diag_fetch(df, As, Bs, w, c16);
-            sched_fence();
-            (void)PH::diag_compute(df, NsT, TsT, w, g, c16);
-        }
-        __syncthreads();
-        // The four sub-chunks in order, for this wave's 16 state rows.
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // every LDS operand of the sub-chunk first, so their latency is paid once
-            F kl[NMT], ql[NMT], kf[NMT];
-            f32x4 ef[NMT];
-#pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                kl[m] = ldrow(Ks, L::K, 16 * j + c16, 16 * m, g);
-                ql[m] = ldrow(Qs, L::K, 16 * j + c16, 16 * m, g);
-                kf[m] = TR::ldcol(Kf, L::K, 16 * j, 16 * m, g, c16);
-                ef[m] = *reinterpret_cast<const f32x4 *>(E16 + j * DK + 16 * m + 4 * g);
-            }
-            const F vf = has_v ? TR::ldcol(Vs, L::V, 16 * j, 16 * w, g, c16) : F{}; // no V: state transitions
-            const F tf = TR::ldcol(TsT, L::T, 16 * j, 16 * j, g, c16);
-            const F pf = ldrow(Ps, L::T, 16 * j + c16, 16 * j, g);
-            sched_fence();
-            F SB[NMT];
-#pragma unroll
-            for (int m = 0; m < NMT; ++m) SB[m] = TR::cvt(Sacc[m]);
-            f32x4 y = widen_bf16(vf);
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < NMT; m += 2) { // 16x16x32 products over dk blocks m, m + 1; Ks holds -Kl
-                y = TR::mma32(y, kl[m], kl[m + 1], SB[m], SB[m + 1]);
-                o = TR::mma32(o, ql[m], ql[m + 1], SB[m], SB[m + 1]);
-            }
-            const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
-            const F zb = TR::cvt(TR::mma16(z0, tf, TR::cvt(y)));
-            o += TR::mma16(z0, pf, zb); // its own accumulator: o comes from 16x16x32 products
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Os[(16 * j + 4 * g + i) * LO + 16 * w + c16] = TR::fromf(o[i]);
-#pragma unroll
-            for (int m = 0; m < NMT; ++m) Sacc[m] = TR::mma16(Sacc[m] * ef[m], kf[m], zb);
-        }
+        state_out<DK>(Sacc, wk, w, g, c16);
+        return;
     }
-    if (WO && NC > 0) {
+
+    // ---- prep: wave 4 + j prepares sub-chunk j, lane l owns channels CPL l .. CPL l + CPL - 1 ----
+    const int j = wave - 4, d0 = CPL * lane;
+    const E *kg = reinterpret_cast<const E *>(a.k) + tok0 * sqk + (int64_t)h * DK + d0;
+    const E *qg = reinterpret_cast<const E *>(a.q) + tok0 * sqk + (int64_t)h * DK + d0;
+    const float *gg = a.gk + tok0 * sqk + (int64_t)h * DK + d0;
+    const E *bg = reinterpret_cast<const E *>(a.beta) + tok0 * a.H + h;
+    E *Kr = reinterpret_cast<E *>(smem + LY::oKr);
+    float *Ab = reinterpret_cast<float *>(smem + LY::oAs) + j * 16 * 20; // diag(beta) L of the sub-chunk
+    float *Xp = reinterpret_cast<float *>(smem + LY::oX + (LY::kXoverKr ? (size_t)j * 16 * L::K * 2 : j * LY::szX));
+    // keys, queries and log decays of the sub-chunk's 16 tokens, a chunk ahead;
+    // beta of token 16 j + c16
+    E kx[16][CPL], qx[16][CPL];
+    float gx[16][CPL], bx = 0.f;
+    auto load = [&](int c) {
+        const int n = rows_of(c);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int64_t off = ((int64_t)c * kChunk + min(16 * j + t, n - 1)) * sqk;
+            if constexpr (CPL == 2) {
+                const bf16x2 kk = *reinterpret_cast<const bf16x2 *>(kg + off);
+                const bf16x2 qq = *reinterpret_cast<const bf16x2 *>(qg + off);
+                typedef float f32x2 __attribute__((ext_vector_type(2)));
+                const f32x2 gv = *reinterpret_cast<const f32x2 *>(gg + off);
+                kx[t][0] = kk[0];
+                kx[t][1] = kk[1];
+                qx[t][0] = qq[0];
+                qx[t][1] = qq[1];
+                gx[t][0] = gv[0];
+                gx[t][1] = gv[1];
+            } else {
+                kx[t][0] = kg[off];
+                qx[t][0] = qg[off];
+                gx[t][0] = gg[off];
+            }
+        }
+        bx = (float)bg[((int64_t)c * kChunk + min(16 * j + c16, n - 1)) * a.H];
+    };
+    if (NC > 0) load(0);
+    // iteration r prepares chunk r + 1 into buffer (r + 1) & 1
+    for (int r = -1; r < NC; ++r) {
+        const int c = r + 1;
+        if (c < NC) {
+            const int n = rows_of(c);
+            unsigned char *B = smem + (c & 1) * LY::szBuf;
+            E *KLb = reinterpret_cast<E *>(B + LY::oKL), *QLb = reinterpret_cast<E *>(B + LY::oQL);
+            E *KFb = reinterpret_cast<E *>(B + LY::oKF);
+            E *TBj = reinterpret_cast<E *>(B + LY::oTB) + j * 16 * BL, *PBj = reinterpret_cast<E *>(B + LY::oPB) + j * 16 * BL;
+            float *Eb = reinterpret_cast<float *>(B + LY::oE);
+            // per-channel prefix sums (base 2); tokens past the end have no decay
+            float acc[CPL], gam[16][CPL];
+            bool wide = false; // a prefix sum outside the factored path's range
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) acc[q] = 0.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+#pragma unroll
+                for (int q = 0; q < CPL; ++q) {
+                    if (16 * j + t < n) acc[q] += gx[t][q] * 1.44269504088896340736f;
+                    gam[t][q] = acc[q];
+                    wide |= !(fabsf(acc[q]) <= kKdaLim);
+                }
+            }
+            // exact path for the whole sub-chunk when any of its channels needs it
+            const bool exact = __builtin_amdgcn_ballot_w64(wide) != 0;
+            float e16[CPL];
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) e16[q] = __builtin_amdgcn_exp2f(acc[q]);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int row = 16 * j + t;
+                const bool on = row < n;
+                E a1[CPL], a2[CPL], a3[CPL], a4[CPL];
+#pragma unroll
+                for (int q = 0; q < CPL; ++q) {
+                    const float kv = on ? (float)kx[t][q] : 0.f, qv = on ? (float)qx[t][q] : 0.f;
+                    const float el = __builtin_amdgcn_exp2f(gam[t][q]), er = __builtin_amdgcn_exp2f(-gam[t][q]);
+                    // exp(gamma_16 - gamma) <= 1: within the factored range the
+                    // product of the two factors; beyond it, from the difference itself
+                    const float ef = exact ? __builtin_amdgcn_exp2f(acc[q] - gam[t][q]) : e16[q] * er;
+                    a1[q] = TR::fromf(-(kv * el));
+                    a2[q] = TR::fromf(qv * el);
+                    a3[q] = TR::fromf(on ? kv * er : 0.f);
+                    a4[q] = TR::fromf(kv * ef);
+                }
+                if constexpr (CPL == 2) {
+                    *reinterpret_cast<bf16x2 *>(KLb + row * L::K + d0) = bf16x2{a1[0], a1[1]};
+                    *reinterpret_cast<bf16x2 *>(QLb + row * L::K + d0) = bf16x2{a2[0], a2[1]};
+                    *reinterpret_cast<bf16x2 *>(Kr + row * L::K + d0) = bf16x2{a3[0], a3[1]};
+                    *reinterpret_cast<bf16x2 *>(KFb + row * L::K + d0) = bf16x2{a4[0], a4[1]};
+                } else {
+                    KLb[row * L::K + d0] = a1[0];
+                    QLb[row * L::K + d0] = a2[0];
+                    Kr[row * L::K + d0] = a3[0];
+                    KFb[row * L::K + d0] = a4[0];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) Eb[j * DK + d0 + q] = e16[q];
+            if (exact) {
+                // lane (row rw of 16 lanes, c16) adds its channels of every
+                // entry; the 16-lane row scan leaves the row's sum in its lane
+                // 15, which stores it: Xp[4 entry + rw]
+                float *xp = Xp + (lane >> 4);
+                const bool last = c16 == 15;
+                static_for<0, 16>([&](auto lc) {
+                    constexpr int l = decltype(lc)::value;
+                    const bool onl = 16 * j + l < n;
+                    static_for<0, l + 1>([&](auto mc) {
+                        constexpr int m = decltype(mc)::value;
+                        float sa = 0.f, sl = 0.f;
+#pragma unroll
+                        for (int q = 0; q < CPL; ++q) {
+                            const float km = 16 * j + m < n ? (float)kx[m][q] : 0.f;
+                            const float t = km * __builtin_amdgcn_exp2f(gam[l][q] - gam[m][q]);
+                            sa += (onl ? (float)qx[l][q] : 0.f) * t;
+                            sl += (onl ? (float)kx[l][q] : 0.f) * t;
+                        }
+                        sa = row_scan16(sa);
+                        if (last) xp[4 * (120 + l * (l + 1) / 2 + m)] = sa; // A entry (l, m)
+                        if constexpr (m < l) {
+                            sl = row_scan16(sl);
+                            if (last) xp[4 * (l * (l - 1) / 2 + m)] = sl; // L entry (l, m)
+                        }
+                    });
+                });
+            }
+            const float bt = 16 * j + c16 < n ? bx : 0.f; // beta of row 16 j + c16
+            // this sub-chunk's registers are consumed: the next chunk's loads go out
+            if (c + 1 < NC) load(c + 1);
+            // The rows written above are read back by this wave only: LDS keeps
+            // a wave's accesses in order, and this keeps the compiler from
+            // moving a read of them above the writes (their pointer types differ).
+            lds_order();
+            if (exact) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int idx = 64 * p + lane, l = idx >> 4, m = idx & 15;
+                    float sl = 0.f, sa = 0.f;
+                    if (m <= l) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            sa += Xp[4 * (120 + l * (l + 1) / 2 + m) + q];
+                            if (m < l) sl += Xp[4 * (l * (l - 1) / 2 + m) + q];
+                        }
+                    }
+                    const float bl = __shfl(bt, l);
+                    Ab[l * 20 + m] = m < l ? bl * sl : 0.f;
+                    PBj[l * BL + m] = TR::fromf(m <= l ? sa : 0.f);
+                }
+            } else {
+                // -L = (-Kl) Kr^T and A = Ql Kr^T over dk, rows 16 j + 4 g + i, columns 16 j + c16
+                f32x4 lt = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < NMT; m += 2) {
+                    const F kr0 = ldrow(Kr, L::K, 16 * j + c16, 16 * m, g), kr1 = ldrow(Kr, L::K, 16 * j + c16, 16 * m + 16, g);
+                    lt = TR::mma32(lt, ldrow(KLb, L::K, 16 * j + c16, 16 * m, g),
+                                   ldrow(KLb, L::K, 16 * j + c16, 16 * m + 16, g), kr0, kr1);
+                    at = TR::mma32(at, ldrow(QLb, L::K, 16 * j + c16, 16 * m, g),
+                                   ldrow(QLb, L::K, 16 * j + c16, 16 * m + 16, g), kr0, kr1);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * g + i;
+                    const float bl = __shfl(bt, row);
+                    Ab[row * 20 + c16] = c16 < row ? -bl * lt[i] : 0.f;
+                    PBj[row * BL + c16] = TR::fromf(c16 <= row ? at[i] : 0.f);
+                }
+            }
+            lds_order();
+            // T = (I + diag(beta) L)^-1 diag(beta): lane c16 solves column c16
+            // (every lane group the same) and writes row c16 of T^T
+            float arow[16], x[16];
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(Ab + c16 * 20 + 4 * j4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) arow[4 * j4 + e] = t[e];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = i == c16 ? 1.f : 0.f;
+            solve_step<0>(x, arow);
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 xv = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
+                stf(TBj + c16 * BL + 4 * i4, TR::cvt(xv * bt));
+            }
+        }
         __syncthreads();
-        flush_o(NC - 1);
     }
-    state_out<DK>(Sacc, wk, w, g, c16);
 }
 
 // One workgroup of 1024 threads: thread t sums the chunk counts of its block
@@ -2032,9 +2102,9 @@ template <int DK, int DV> hipError_t launch_kda_dims(bool write_o, const ChainAr
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
     if (write_o)
-        hipLaunchKernelGGL((kda_chain_kernel<DK, DV, true>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((kda_chain_kernel<DK, DV, true>), dim3(grid), dim3(kKdaThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((kda_chain_kernel<DK, DV, false>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((kda_chain_kernel<DK, DV, false>), dim3(grid), dim3(kKdaThreads), 0, s, a);
     return hipGetLastError();
 }
 
