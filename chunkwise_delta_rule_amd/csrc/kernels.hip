@@ -1689,11 +1689,19 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
 // One barrier per chunk; the chain reads one half of a double buffer while
 // the prep waves fill the other. Wave w and w + 4 share a SIMD.
 // ---------------------------------------------------------------------------
+// LDS layouts of the KDA kernel. Rows of dk + 16 elements with the 16-byte
+// unit index XORed by row bit 3 (okda) keep the 8-byte row reads (16 rows of
+// a 16 x 16 block, two lane groups per pass), the transposing reads (8 rows
+// x 32 bytes per pass) and the 4-byte writes of the prep waves free of bank
+// conflicts; the 16 x 16 blocks use rows of 16 with the same XOR (oblk).
+template <int DK> __device__ inline int okda(int r, int c) {
+    return r * (DK + 16) + 8 * ((c >> 3) ^ ((r >> 3) & 1)) + (c & 7);
+}
+__device__ inline int oblk(int r, int c) { return r * 16 + 8 * ((c >> 3) ^ ((r >> 3) & 1)) + (c & 7); }
 template <int DK> struct KdaLds {
     using L = Ld<__bf16, DK>;
-    static constexpr int kBL = 24;                                    // row length of a 16 x 16 bf16 block
-    static constexpr size_t szBlk = 16 * kBL * 2;
-    // buffer b: -Kl, Ql, Kf [64][L::K]; exp(gamma_16) fp32 [4][DK]; T^T and A diagonal blocks [4][16][kBL]
+    static constexpr size_t szBlk = 16 * 16 * 2;
+    // buffer b: -Kl, Ql, Kf [64][L::K]; exp(gamma_16) fp32 [4][DK]; T^T and A diagonal blocks [4][16][16]
     static constexpr size_t oKL = 0, oQL = L::szK, oKF = 2 * L::szK, oE = 3 * L::szK;
     static constexpr size_t oTB = oE + sizeof(float) * 4 * DK, oPB = oTB + 4 * szBlk, szBuf = oPB + 4 * szBlk;
     // prep only: Kr [64][L::K]; the exact path's row partial sums of one
@@ -1736,6 +1744,22 @@ __device__ inline float row_scan16(float x) {
     return x;
 }
 
+// CPL consecutive channels of one token: a bf16 pair (dk = 128) or one bf16,
+// and their log decays; kdv reads channel q as float.
+template <int CPL> struct KdaPack;
+template <> struct KdaPack<1> {
+    using B = __bf16;
+    using F = float;
+};
+template <> struct KdaPack<2> {
+    using B = bf16x2;
+    using F = float __attribute__((ext_vector_type(2)));
+};
+__device__ inline float kdv(__bf16 x, int) { return (float)x; }
+__device__ inline float kdv(float x, int) { return x; }
+__device__ inline float kdv(bf16x2 x, int q) { return (float)x[q]; }
+__device__ inline float kdv(float __attribute__((ext_vector_type(2))) x, int q) { return x[q]; }
+
 constexpr int kKdaThreads = 512;
 
 // Compiler-level ordering of LDS accesses within one wave (no instruction).
@@ -1748,11 +1772,20 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
     using F = typename TR::F;
     using L = Ld<E, DK>;
     using LY = KdaLds<DK>;
-    constexpr int NMT = DK / 16, CPL = DK / 64, BL = LY::kBL;
+    constexpr int NMT = DK / 16, CPL = DK / 64, RK = DK + 16;
     static_assert(LY::total <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::total];
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, c16 = lane & 15;
+    // per-lane offsets of the row pieces (c16, 4 g) and of the transposing-read
+    // providers (4 g + c16 / 4, 4 (c16 % 4)); a block 16 rows and 16 columns
+    // away adds 16 rows of the layout plus 16 (the swizzles keep that affine)
+    const int orow = okda<DK>(c16, 4 * g), otr = okda<DK>(4 * g + (c16 >> 2), 4 * (c16 & 3));
+    const int brow = oblk(c16, 4 * g), btr = oblk(4 * g + (c16 >> 2), 4 * (c16 & 3));
+    auto ld4 = [](const E *p) { return *reinterpret_cast<const bf16x4 *>(p); };
+    auto tr4 = [](const E *p) {
+        return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
+    };
     // the work item: a token range of one (sequence, head), 64 state rows,
     // where they start and end (dense, packed, or a group of a split sequence)
     const Work wk = decode_work<DK, DV>(a);
@@ -1769,14 +1802,14 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
         const bool has_v = wk.has_v;
         const E *vg = reinterpret_cast<const E *>(a.v) + tok0 * sv + (int64_t)h * DV + wk.row0 + 16 * w + c16;
         E *og = WO ? reinterpret_cast<E *>(a.o) + tok0 * sv + (int64_t)h * DV + wk.row0 + 16 * w + c16 : nullptr;
-        // V[64 c + 16 j + 4 g + i][this lane's row], entry 4 j + i, a chunk ahead
-        E vn[16], vc[16];
+        // V[64 c + 16 j + 4 g + i][this lane's row], entry 4 j + i (in pairs), a chunk ahead
+        bf16x2 vn[8], vc[8];
         auto load_v = [&](int c) {
             const int n = rows_of(c);
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
                 const int row = 16 * (x >> 2) + 4 * g + (x & 3);
-                vn[x] = has_v ? vg[((int64_t)c * kChunk + min(row, n - 1)) * sv] : TR::fromf(0.f);
+                vn[x >> 1][x & 1] = has_v ? vg[((int64_t)c * kChunk + min(row, n - 1)) * sv] : TR::fromf(0.f);
             }
         };
         if (NC > 0) load_v(0);
@@ -1784,7 +1817,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
         for (int r = 0; r < NC; ++r) {
             const int n = rows_of(r);
 #pragma unroll
-            for (int x = 0; x < 16; ++x) vc[x] = vn[x];
+            for (int x = 0; x < 8; ++x) vc[x] = vn[x];
             if (r + 1 < NC) load_v(r + 1);
             const unsigned char *B = smem + (r & 1) * LY::szBuf;
             const E *KLb = reinterpret_cast<const E *>(B + LY::oKL), *QLb = reinterpret_cast<const E *>(B + LY::oQL);
@@ -1798,20 +1831,20 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
                 f32x4 ef[NMT];
 #pragma unroll
                 for (int m = 0; m < NMT; ++m) {
-                    kl[m] = ldrow(KLb, L::K, 16 * j + c16, 16 * m, g);
-                    ql[m] = ldrow(QLb, L::K, 16 * j + c16, 16 * m, g);
-                    kf[m] = TR::ldcol(KFb, L::K, 16 * j, 16 * m, g, c16);
+                    kl[m] = ld4(KLb + orow + 16 * j * RK + 16 * m);
+                    ql[m] = ld4(QLb + orow + 16 * j * RK + 16 * m);
+                    kf[m] = tr4(KFb + otr + 16 * j * RK + 16 * m);
                     ef[m] = *reinterpret_cast<const f32x4 *>(Eb + j * DK + 16 * m + 4 * g);
                 }
-                const F tf = TR::ldcol(TBb + j * 16 * BL, BL, 0, 0, g, c16); // row c16 of T_jj
-                const F pf = ldrow(PBb + j * 16 * BL, BL, c16, 0, g);         // row c16 of A_jj
+                const F tf = tr4(TBb + j * 256 + btr); // row c16 of T_jj
+                const F pf = ld4(PBb + j * 256 + brow); // row c16 of A_jj
                 sched_fence();
                 F SB[NMT];
 #pragma unroll
                 for (int m = 0; m < NMT; ++m) SB[m] = TR::cvt(Sacc[m]);
                 f32x4 y;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] = 16 * j + 4 * g + i < n ? (float)vc[4 * j + i] : 0.f;
+                for (int i = 0; i < 4; ++i) y[i] = 16 * j + 4 * g + i < n ? (float)vc[2 * j + (i >> 1)][i & 1] : 0.f;
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int m = 0; m < NMT; m += 2) { // 16x16x32 products over dk blocks m, m + 1; KL holds -Kl
@@ -1839,51 +1872,48 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
 
     // ---- prep: wave 4 + j prepares sub-chunk j, lane l owns channels CPL l .. CPL l + CPL - 1 ----
     const int j = wave - 4, d0 = CPL * lane;
-    const E *kg = reinterpret_cast<const E *>(a.k) + tok0 * sqk + (int64_t)h * DK + d0;
-    const E *qg = reinterpret_cast<const E *>(a.q) + tok0 * sqk + (int64_t)h * DK + d0;
-    const float *gg = a.gk + tok0 * sqk + (int64_t)h * DK + d0;
+    const E *kg = reinterpret_cast<const E *>(a.k) + tok0 * sqk + (int64_t)h * DK;
+    const E *qg = reinterpret_cast<const E *>(a.q) + tok0 * sqk + (int64_t)h * DK;
+    const float *gg = a.gk + tok0 * sqk + (int64_t)h * DK;
     const E *bg = reinterpret_cast<const E *>(a.beta) + tok0 * a.H + h;
     E *Kr = reinterpret_cast<E *>(smem + LY::oKr);
     float *Ab = reinterpret_cast<float *>(smem + LY::oAs) + j * 16 * 20; // diag(beta) L of the sub-chunk
     float *Xp = reinterpret_cast<float *>(smem + LY::oX + (LY::kXoverKr ? (size_t)j * 16 * L::K * 2 : j * LY::szX));
-    // keys, queries and log decays of the sub-chunk's 16 tokens, a chunk ahead;
-    // beta of token 16 j + c16
-    E kx[16][CPL], qx[16][CPL];
-    float gx[16][CPL], bx = 0.f;
-    auto load = [&](int c) {
+    // keys, queries and log decays of the sub-chunk's 16 tokens (this lane's
+    // channels, packed), a chunk ahead; beta of token 16 j + c16
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    using KP = typename KdaPack<CPL>::B;
+    using GP = typename KdaPack<CPL>::F;
+    KP kx[16], qx[16];
+    GP gx[16];
+    float bx = 0.f;
+    auto load = [&](int c, int dd, int cc) {
         const int n = rows_of(c);
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const int64_t off = ((int64_t)c * kChunk + min(16 * j + t, n - 1)) * sqk;
-            if constexpr (CPL == 2) {
-                const bf16x2 kk = *reinterpret_cast<const bf16x2 *>(kg + off);
-                const bf16x2 qq = *reinterpret_cast<const bf16x2 *>(qg + off);
-                typedef float f32x2 __attribute__((ext_vector_type(2)));
-                const f32x2 gv = *reinterpret_cast<const f32x2 *>(gg + off);
-                kx[t][0] = kk[0];
-                kx[t][1] = kk[1];
-                qx[t][0] = qq[0];
-                qx[t][1] = qq[1];
-                gx[t][0] = gv[0];
-                gx[t][1] = gv[1];
-            } else {
-                kx[t][0] = kg[off];
-                qx[t][0] = qg[off];
-                gx[t][0] = gg[off];
-            }
+            const uint32_t off = (uint32_t)(((int64_t)c * kChunk + min(16 * j + t, n - 1)) * sqk + dd);
+            kx[t] = *reinterpret_cast<const KP *>(kg + off);
+            qx[t] = *reinterpret_cast<const KP *>(qg + off);
+            gx[t] = *reinterpret_cast<const GP *>(gg + off);
         }
-        bx = (float)bg[((int64_t)c * kChunk + min(16 * j + c16, n - 1)) * a.H];
+        bx = (float)bg[(uint32_t)(((int64_t)c * kChunk + min(16 * j + cc, n - 1)) * a.H)];
     };
-    if (NC > 0) load(0);
+    if (NC > 0) load(0, d0, c16);
     // iteration r prepares chunk r + 1 into buffer (r + 1) & 1
     for (int r = -1; r < NC; ++r) {
         const int c = r + 1;
         if (c < NC) {
+            // lane coordinates again, opaque to the compiler, so that the
+            // offsets derived from them are formed here rather than hoisted out
+            // of the loop and kept live (or spilled) across it
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int pg = ln >> 4, pc = ln & 15, pd = CPL * ln;
             const int n = rows_of(c);
             unsigned char *B = smem + (c & 1) * LY::szBuf;
             E *KLb = reinterpret_cast<E *>(B + LY::oKL), *QLb = reinterpret_cast<E *>(B + LY::oQL);
             E *KFb = reinterpret_cast<E *>(B + LY::oKF);
-            E *TBj = reinterpret_cast<E *>(B + LY::oTB) + j * 16 * BL, *PBj = reinterpret_cast<E *>(B + LY::oPB) + j * 16 * BL;
+            E *TBj = reinterpret_cast<E *>(B + LY::oTB) + j * 256, *PBj = reinterpret_cast<E *>(B + LY::oPB) + j * 256;
             float *Eb = reinterpret_cast<float *>(B + LY::oE);
             // per-channel prefix sums (base 2); tokens past the end have no decay
             float acc[CPL], gam[16][CPL];
@@ -1894,7 +1924,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
             for (int t = 0; t < 16; ++t) {
 #pragma unroll
                 for (int q = 0; q < CPL; ++q) {
-                    if (16 * j + t < n) acc[q] += gx[t][q] * 1.44269504088896340736f;
+                    if (16 * j + t < n) acc[q] += kdv(gx[t], q) * 1.44269504088896340736f;
                     gam[t][q] = acc[q];
                     wide |= !(fabsf(acc[q]) <= kKdaLim);
                 }
@@ -1911,7 +1941,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
                 E a1[CPL], a2[CPL], a3[CPL], a4[CPL];
 #pragma unroll
                 for (int q = 0; q < CPL; ++q) {
-                    const float kv = on ? (float)kx[t][q] : 0.f, qv = on ? (float)qx[t][q] : 0.f;
+                    const float kv = on ? kdv(kx[t], q) : 0.f, qv = on ? kdv(qx[t], q) : 0.f;
                     const float el = __builtin_amdgcn_exp2f(gam[t][q]), er = __builtin_amdgcn_exp2f(-gam[t][q]);
                     // exp(gamma_16 - gamma) <= 1: within the factored range the
                     // product of the two factors; beyond it, from the difference itself
@@ -1922,25 +1952,27 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
                     a4[q] = TR::fromf(kv * ef);
                 }
                 if constexpr (CPL == 2) {
-                    *reinterpret_cast<bf16x2 *>(KLb + row * L::K + d0) = bf16x2{a1[0], a1[1]};
-                    *reinterpret_cast<bf16x2 *>(QLb + row * L::K + d0) = bf16x2{a2[0], a2[1]};
-                    *reinterpret_cast<bf16x2 *>(Kr + row * L::K + d0) = bf16x2{a3[0], a3[1]};
-                    *reinterpret_cast<bf16x2 *>(KFb + row * L::K + d0) = bf16x2{a4[0], a4[1]};
+                    const int o = okda<DK>(t, pd) + 16 * j * RK; // t, and so the swizzle, is a constant here
+                    *reinterpret_cast<bf16x2 *>(KLb + o) = bf16x2{a1[0], a1[1]};
+                    *reinterpret_cast<bf16x2 *>(QLb + o) = bf16x2{a2[0], a2[1]};
+                    *reinterpret_cast<bf16x2 *>(Kr + o) = bf16x2{a3[0], a3[1]};
+                    *reinterpret_cast<bf16x2 *>(KFb + o) = bf16x2{a4[0], a4[1]};
                 } else {
-                    KLb[row * L::K + d0] = a1[0];
-                    QLb[row * L::K + d0] = a2[0];
-                    Kr[row * L::K + d0] = a3[0];
-                    KFb[row * L::K + d0] = a4[0];
+                    const int o = okda<DK>(t, pd) + 16 * j * RK;
+                    KLb[o] = a1[0];
+                    QLb[o] = a2[0];
+                    Kr[o] = a3[0];
+                    KFb[o] = a4[0];
                 }
             }
 #pragma unroll
-            for (int q = 0; q < CPL; ++q) Eb[j * DK + d0 + q] = e16[q];
+            for (int q = 0; q < CPL; ++q) Eb[j * DK + pd + q] = e16[q];
             if (exact) {
-                // lane (row rw of 16 lanes, c16) adds its channels of every
-                // entry; the 16-lane row scan leaves the row's sum in its lane
+                // ln (row rw of 16 lanes, pc) adds its channels of every
+                // entry; the 16-ln row scan leaves the row's sum in its ln
                 // 15, which stores it: Xp[4 entry + rw]
-                float *xp = Xp + (lane >> 4);
-                const bool last = c16 == 15;
+                float *xp = Xp + (ln >> 4);
+                const bool last = pc == 15;
                 static_for<0, 16>([&](auto lc) {
                     constexpr int l = decltype(lc)::value;
                     const bool onl = 16 * j + l < n;
@@ -1949,10 +1981,10 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
                         float sa = 0.f, sl = 0.f;
 #pragma unroll
                         for (int q = 0; q < CPL; ++q) {
-                            const float km = 16 * j + m < n ? (float)kx[m][q] : 0.f;
+                            const float km = 16 * j + m < n ? kdv(kx[m], q) : 0.f;
                             const float t = km * __builtin_amdgcn_exp2f(gam[l][q] - gam[m][q]);
-                            sa += (onl ? (float)qx[l][q] : 0.f) * t;
-                            sl += (onl ? (float)kx[l][q] : 0.f) * t;
+                            sa += (onl ? kdv(qx[l], q) : 0.f) * t;
+                            sl += (onl ? kdv(kx[l], q) : 0.f) * t;
                         }
                         sa = row_scan16(sa);
                         if (last) xp[4 * (120 + l * (l + 1) / 2 + m)] = sa; // A entry (l, m)
@@ -1960,12 +1992,13 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
                             sl = row_scan16(sl);
                             if (last) xp[4 * (l * (l - 1) / 2 + m)] = sl; // L entry (l, m)
                         }
+                        sched_fence(); // one entry at a time: few registers live
                     });
                 });
             }
-            const float bt = 16 * j + c16 < n ? bx : 0.f; // beta of row 16 j + c16
+            const float bt = 16 * j + pc < n ? bx : 0.f; // beta of row 16 j + pc
             // this sub-chunk's registers are consumed: the next chunk's loads go out
-            if (c + 1 < NC) load(c + 1);
+            if (c + 1 < NC) load(c + 1, pd, pc);
             // The rows written above are read back by this wave only: LDS keeps
             // a wave's accesses in order, and this keeps the compiler from
             // moving a read of them above the writes (their pointer types differ).
@@ -1973,7 +2006,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
             if (exact) {
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const int idx = 64 * p + lane, l = idx >> 4, m = idx & 15;
+                    const int idx = 64 * p + ln, l = idx >> 4, m = idx & 15;
                     float sl = 0.f, sa = 0.f;
                     if (m <= l) {
 #pragma unroll
@@ -1984,44 +2017,43 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
                     }
                     const float bl = __shfl(bt, l);
                     Ab[l * 20 + m] = m < l ? bl * sl : 0.f;
-                    PBj[l * BL + m] = TR::fromf(m <= l ? sa : 0.f);
+                    PBj[oblk(l, m)] = TR::fromf(m <= l ? sa : 0.f);
                 }
             } else {
-                // -L = (-Kl) Kr^T and A = Ql Kr^T over dk, rows 16 j + 4 g + i, columns 16 j + c16
+                // -L = (-Kl) Kr^T and A = Ql Kr^T over dk, rows 16 j + 4 g + i, columns 16 j + pc
                 f32x4 lt = {0.f, 0.f, 0.f, 0.f}, at = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int m = 0; m < NMT; m += 2) {
-                    const F kr0 = ldrow(Kr, L::K, 16 * j + c16, 16 * m, g), kr1 = ldrow(Kr, L::K, 16 * j + c16, 16 * m + 16, g);
-                    lt = TR::mma32(lt, ldrow(KLb, L::K, 16 * j + c16, 16 * m, g),
-                                   ldrow(KLb, L::K, 16 * j + c16, 16 * m + 16, g), kr0, kr1);
-                    at = TR::mma32(at, ldrow(QLb, L::K, 16 * j + c16, 16 * m, g),
-                                   ldrow(QLb, L::K, 16 * j + c16, 16 * m + 16, g), kr0, kr1);
+                    const int o = okda<DK>(pc, 4 * pg) + 16 * j * RK + 16 * m;
+                    const F kr0 = ld4(Kr + o), kr1 = ld4(Kr + o + 16);
+                    lt = TR::mma32(lt, ld4(KLb + o), ld4(KLb + o + 16), kr0, kr1);
+                    at = TR::mma32(at, ld4(QLb + o), ld4(QLb + o + 16), kr0, kr1);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = 4 * g + i;
+                    const int row = 4 * pg + i;
                     const float bl = __shfl(bt, row);
-                    Ab[row * 20 + c16] = c16 < row ? -bl * lt[i] : 0.f;
-                    PBj[row * BL + c16] = TR::fromf(c16 <= row ? at[i] : 0.f);
+                    Ab[row * 20 + pc] = pc < row ? -bl * lt[i] : 0.f;
+                    PBj[oblk(row, pc)] = TR::fromf(pc <= row ? at[i] : 0.f);
                 }
             }
             lds_order();
-            // T = (I + diag(beta) L)^-1 diag(beta): lane c16 solves column c16
-            // (every lane group the same) and writes row c16 of T^T
+            // T = (I + diag(beta) L)^-1 diag(beta): ln pc solves column pc
+            // (every ln group the same) and writes row pc of T^T
             float arow[16], x[16];
 #pragma unroll
             for (int j4 = 0; j4 < 4; ++j4) {
-                const f32x4 t = *reinterpret_cast<const f32x4 *>(Ab + c16 * 20 + 4 * j4);
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(Ab + pc * 20 + 4 * j4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) arow[4 * j4 + e] = t[e];
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = i == c16 ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = i == pc ? 1.f : 0.f;
             solve_step<0>(x, arow);
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const f32x4 xv = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
-                stf(TBj + c16 * BL + 4 * i4, TR::cvt(xv * bt));
+                stf(TBj + oblk(pc, 4 * i4), TR::cvt(xv * bt));
             }
         }
         __syncthreads();
