@@ -1711,8 +1711,18 @@ template <int DK> struct KdaLds {
     static constexpr bool kXoverKr = (size_t)16 * L::K * 2 >= szX;
     static constexpr size_t oX = kXoverKr ? oKr : oKr + L::szK;
     static constexpr size_t oAs = kXoverKr ? oKr + L::szK : oX + 4 * szX;
-    static constexpr size_t total = oAs + sizeof(float) * 4 * 16 * 20;
+    // chain wave w: its V tile [64 tokens][16 rows] and O^T tile [16 rows][64 tokens]
+    // (o64 layout), staging 16-byte loads and 8-byte stores to HBM
+    static constexpr size_t oVO = oAs + sizeof(float) * 4 * 16 * 20, szVO = 2 * 64 * 16 * 2;
+    static constexpr size_t total = oVO + 4 * szVO;
 };
+// 64-column bf16 tile with its 8-byte units XORed by row bits 0-3: the
+// 8-byte writes of 16 rows at one column and the transposing reads of 8 rows
+// at 4 consecutive units are free of bank conflicts.
+__device__ inline int okda64(int r, int c) {
+    const int s = (((r >> 1) & 3) << 2) | (((r >> 3) & 1) << 1) | (r & 1);
+    return r * 64 + 4 * ((c >> 2) ^ s) + (c & 3);
+}
 
 // Compile-time loop: f(Int<I>{}) for I = B..E-1 (step indices stay constants).
 template <int I> struct Int {
@@ -1800,16 +1810,20 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
         f32x4 Sacc[NMT];
         state_in<DK>(Sacc, wk, w, g, c16);
         const bool has_v = wk.has_v;
-        const E *vg = reinterpret_cast<const E *>(a.v) + tok0 * sv + (int64_t)h * DV + wk.row0 + 16 * w + c16;
-        E *og = WO ? reinterpret_cast<E *>(a.o) + tok0 * sv + (int64_t)h * DV + wk.row0 + 16 * w + c16 : nullptr;
-        // V[64 c + 16 j + 4 g + i][this lane's row], entry 4 j + i (in pairs), a chunk ahead
-        bf16x2 vn[8], vc[8];
+        // this wave's 16 value rows: V loads of 16 bytes (two per lane: token
+        // p / 2, half p % 2 of the 32 bytes), O stores of 8 bytes
+        const E *vg = reinterpret_cast<const E *>(a.v) + tok0 * sv + (int64_t)h * DV + wk.row0 + 16 * w;
+        E *og = WO ? reinterpret_cast<E *>(a.o) + tok0 * sv + (int64_t)h * DV + wk.row0 + 16 * w : nullptr;
+        E *Vw = reinterpret_cast<E *>(smem + LY::oVO + w * LY::szVO), *Ow = Vw + 64 * 16;
+        bf16x8 vreg[2];
         auto load_v = [&](int c) {
             const int n = rows_of(c);
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const int row = 16 * (x >> 2) + 4 * g + (x & 3);
-                vn[x >> 1][x & 1] = has_v ? vg[((int64_t)c * kChunk + min(row, n - 1)) * sv] : TR::fromf(0.f);
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int p = lane + 64 * s2;
+                vreg[s2] = has_v ? *reinterpret_cast<const bf16x8 *>(
+                                       vg + (uint32_t)(((int64_t)c * kChunk + min(p >> 1, n - 1)) * sv + 8 * (p & 1)))
+                                 : bf16x8{};
             }
         };
         if (NC > 0) load_v(0);
@@ -1817,7 +1831,11 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
         for (int r = 0; r < NC; ++r) {
             const int n = rows_of(r);
 #pragma unroll
-            for (int x = 0; x < 8; ++x) vc[x] = vn[x];
+            for (int s2 = 0; s2 < 2; ++s2) { // V tile of chunk r, rows past the end zero
+                const int p = lane + 64 * s2;
+                *reinterpret_cast<bf16x8 *>(Vw + 16 * (p >> 1) + 8 * (p & 1)) = (p >> 1) < n ? vreg[s2] : bf16x8{};
+            }
+            lds_order();
             if (r + 1 < NC) load_v(r + 1);
             const unsigned char *B = smem + (r & 1) * LY::szBuf;
             const E *KLb = reinterpret_cast<const E *>(B + LY::oKL), *QLb = reinterpret_cast<const E *>(B + LY::oQL);
@@ -1838,13 +1856,12 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
                 }
                 const F tf = tr4(TBb + j * 256 + btr); // row c16 of T_jj
                 const F pf = ld4(PBb + j * 256 + brow); // row c16 of A_jj
+                const F vf = tr4(Vw + 16 * (16 * j + 4 * g + (c16 >> 2)) + 4 * (c16 & 3)); // V[16j + 4g + e][c16]
                 sched_fence();
                 F SB[NMT];
 #pragma unroll
                 for (int m = 0; m < NMT; ++m) SB[m] = TR::cvt(Sacc[m]);
-                f32x4 y;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] = 16 * j + 4 * g + i < n ? (float)vc[2 * j + (i >> 1)][i & 1] : 0.f;
+                f32x4 y = widen_bf16(vf);
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int m = 0; m < NMT; m += 2) { // 16x16x32 products over dk blocks m, m + 1; KL holds -Kl
@@ -1854,16 +1871,20 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
                 const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
                 const F zb = TR::cvt(TR::mma16(z0, tf, TR::cvt(y)));
                 o += TR::mma16(z0, pf, zb); // its own accumulator: o comes from 16x16x32 products
-                if (WO && has_v) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int tok = 16 * j + 4 * g + i;
-                        if (tok < n) og[((int64_t)r * kChunk + tok) * sv] = TR::fromf(o[i]);
-                    }
-                }
+                if (WO && has_v) stf(Ow + okda64(c16, 16 * j + 4 * g), TR::cvt(o)); // O^T[c16][16j + 4g + i]
 #pragma unroll
                 for (int m = 0; m < NMT; ++m) Sacc[m] = TR::mma16(Sacc[m] * ef[m], kf[m], zb);
             }
+            if (WO && has_v) { // O rows: lane (g, c16) stores token 16 b + c16, rows 4 g .. 4 g + 3
+                lds_order();
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const F x = tr4(Ow + okda64(4 * g + (c16 >> 2), 16 * b + 4 * (c16 & 3)));
+                    const int tok = 16 * b + c16;
+                    if (tok < n) stf(og + (uint32_t)(((int64_t)r * kChunk + tok) * sv + 4 * g), x);
+                }
+            }
+            lds_order();
             __syncthreads();
         }
         state_out<DK>(Sacc, wk, w, g, c16);
