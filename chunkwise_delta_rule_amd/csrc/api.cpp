@@ -56,6 +56,15 @@ int pick_groups(int B, int H, int T, int dv) {
     return G < 1 ? 1 : G;
 }
 
+// State rows per workgroup tile of the bf16 forward with output on the
+// serial chain: 32 when 64-row tiles would leave compute units idle (twice
+// the workgroups, each with half the consumer work and its producer work
+// spread over six waves, so the per-chunk latency drops), else 64.
+int pick_rows(int dtype, int n_units, int dv) {
+    if (dtype != DN_BF16) return dn::kRows;
+    return (int64_t)n_units * (dv / dn::kRows) < device_cus() ? 32 : dn::kRows;
+}
+
 // Resolve the requested group count into (G, chunks per group) with no empty group.
 void resolve_groups(int requested, int B, int H, int T, int dv, int &G, int &cpg) {
     const int nc = (T + dn::kChunk - 1) / dn::kChunk;
@@ -117,7 +126,8 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
     if (G <= 1) {
         a.kind = dn::kDense;
         a.n_units = B * H;
-        a.n_tiles = dv / dn::kRows;
+        a.rows = pick_rows(dtype, a.n_units, dv);
+        a.n_tiles = dv / a.rows;
         err = dn::launch_chain(dtype, dk, dv, true, a, stream);
         return err == hipSuccess ? DN_OK : DN_ERR_HIP;
     }
@@ -184,7 +194,8 @@ int fwd_varlen(const void *q, const void *k, const void *v, const void *beta, co
     a.H = H;
     a.T = total_T;
     a.n_units = N * H;
-    a.n_tiles = dv / dn::kRows;
+    a.rows = pick_rows(dtype, a.n_units, dv);
+    a.n_tiles = dv / a.rows;
     hipError_t err = dn::launch_chain(dtype, dk, dv, true, a, stream);
     return err == hipSuccess ? DN_OK : DN_ERR_HIP;
 }

@@ -242,6 +242,12 @@ template <int DK> struct WsBufs {
 // valid row for the missing rows and writes them as zeros. Two register sets
 // (chunk parity) keep two chunks in flight.
 __device__ inline int rows_of(int len, int c) { return min(kChunk, len - c * kChunk); }
+// End of the chain kernel's iteration range r = -3 .. NC - 1, rounded up so
+// that the count is even: the producers run two iterations per loop trip
+// with no conditional one inside, so the compiler's wait counts see the loads
+// of both register sets in flight and wait only for the older set (the spare
+// iteration stages into ring slots that nobody reads again).
+__device__ inline int ws_rend(int NC) { return NC + ((NC + 3) & 1); }
 
 // K by the 128 threads of waves 6-7 (pt = 0..127): thread pt owns the 16-byte
 // column piece 8 (pt % KV) of rows pt / KV + RPS p, p = 0..NK-1.
@@ -286,11 +292,15 @@ template <int DK> struct KStager {
     }
 };
 
-// V tile (64 x 64) and beta by the 64 lanes of wave 5: lane l owns the
-// 16-byte piece 8 (l % 8) of rows l / 8 + 8 p, p = 0..7, and beta (and the
-// decay logarithm, when gated) of row l.
-struct VStager {
-    static constexpr int NV = 8;
+// V tile (64 tokens x NCOL value columns) and beta by the 64 lanes of one
+// wave, and beta (and the decay logarithm, when gated) of row l in lane l.
+// NCOL = 64: lane l owns the 16-byte piece l % 8 of rows l / 8 + 8 p,
+// p = 0..7. NCOL = 32: lane l = 8 a + 4 h + u owns piece u of rows
+// (a % 4) + 4 h + 8 (a / 4) + 16 p, p = 0..3, so that each group of 8 lanes
+// writes two rows whose swizzles differ in bit 2 (all 32 write banks).
+template <int NCOL> struct VStager {
+    static constexpr int PPR = NCOL / 8, NV = PPR, RSTEP = 64 / PPR;
+    static_assert(NCOL == 64 || NCOL == 32, "tile width");
     const __bf16 *vt, *bt;
     const float *gt; // this head's log decays at real token 0, or nullptr
     SubstepBase sb;  // split of the work's first virtual step
@@ -307,8 +317,14 @@ struct VStager {
         H = H_;
         len = len_;
         lane = lane_;
-        rv0 = lane / 8;
-        col = 8 * (lane % 8);
+        if constexpr (NCOL == 64) {
+            rv0 = lane / 8;
+            col = 8 * (lane % 8);
+        } else {
+            const int a8 = lane >> 3;
+            rv0 = (a8 & 3) + 4 * ((lane >> 2) & 1) + 8 * (a8 >> 2);
+            col = 8 * (lane & 3);
+        }
         vt = vg + rv0 * sv + col;
         bt = bg;
         gt = gg;
@@ -327,11 +343,11 @@ struct VStager {
         const __bf16 *b = vt + (int64_t)c * kChunk * sv;
         if (n[B] == kChunk) {
 #pragma unroll
-            for (int p = 0; p < NV; ++p) r[B][p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(8 * p) * sv);
+            for (int p = 0; p < NV; ++p) r[B][p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(RSTEP * p) * sv);
         } else {
 #pragma unroll
             for (int p = 0; p < NV; ++p) {
-                const int row = min(rv0 + 8 * p, n[B] - 1);
+                const int row = min(rv0 + RSTEP * p, n[B] - 1);
                 r[B][p] = *reinterpret_cast<const bf16x8 *>(b + (int64_t)(row - rv0) * sv);
             }
         }
@@ -350,7 +366,7 @@ struct VStager {
         const bf16x8 z = {};
 #pragma unroll
         for (int p = 0; p < NV; ++p) {
-            const int row = rv0 + 8 * p;
+            const int row = rv0 + RSTEP * p;
             st8(Vs + s64off(row, col), (n[B] == kChunk || row < n[B]) ? r[B][p] : z);
         }
     }
@@ -656,19 +672,19 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
 
     const SubstepBase sb = GATED ? substep_base(wk.tok0, a.nh) : SubstepBase{0, 0u, 1u};
     __syncthreads(); // matches the producers' prologue
-    for (int r = -3; r < NC; ++r) {
-        if (!WO && r >= 0 && wk.Schunks) { // the state entering chunk r, for the backward pass
+    for (int r = -3; r < ws_rend(NC); ++r) {
+        if (!WO && r >= 0 && r < NC && wk.Schunks) { // the state entering chunk r, for the backward pass
             Work ck = wk;
             ck.Sout = wk.Schunks + (int64_t)r * DV * DK;
             ck.transposed_out = false;
             ws_state_out<DK>(Sacc, ck, cw, g, c16);
         }
-        if (!WO && r >= 0 && wk.Schunks16) { // the same in bf16 ([dv][dk] rows)
+        if (!WO && r >= 0 && r < NC && wk.Schunks16) { // the same in bf16 ([dv][dk] rows)
             __bf16 *so = wk.Schunks16 + (int64_t)r * DV * DK + (16 * cw + c16) * DK;
 #pragma unroll
             for (int m = 0; m < DK / 16; ++m) st4(so + dk_of(m, g), cvt4(Sacc[m]));
         }
-        if (r >= 0)
+        if (r >= 0 && r < NC)
             consumer_chain<DK, WO, GATED>(bf, r, Sacc, WO ? og + (GATED ? 0 : (int64_t)r * kChunk * sv) : nullptr,
                                           sv, min(kChunk, wk.len - r * kChunk), sb, has_v, cw, lane, g, c16);
         __syncthreads();
@@ -699,21 +715,22 @@ template <int DK> __device__ inline f32x4 dot_tile(const bf16x8 (&x)[DK / 32], c
     return acc;
 }
 
-// Wave 4: the Gram tiles of chunk c from one set of K row fragments. The four
+// The Gram tiles of chunk c from K row fragments. gram_diag: the four
 // diagonal tiles G_bb go to X(c) (row 16b + j holds G_bb[j][0..15]; G_bb is
-// symmetric), then the off-diagonal tiles A_ac = diag(beta_a) G_ac (a > c)
-// go to A(c) as bf16 k16 operands: lane (g, j) holds A[16a + j][16c + 4g ..
-// +3], per lane in the order A10, A20, A21, A30, A31, A32. The off-diagonal
-// products cover the LDS round trip of X before the solve reads it back.
-// Gated: entry (l, i) of A_ac also takes the decay exp(gamma_l - gamma_i).
-template <int DK, bool GATED> __device__ inline void gram_tiles(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
-    using LY = WsLds<DK>;
-    KRows<DK> k;
-    k_rows<DK>(k, bf.K(c), g, c16);
+// symmetric). gram_off: the off-diagonal tiles A_ac = diag(beta_a) G_ac
+// (a > c) go to A(c) as bf16 k16 operands: lane (g, j) holds A[16a + j][16c +
+// 4g .. +3], per lane in the order A10, A20, A21, A30, A31, A32. Gated: entry
+// (l, i) of A_ac also takes the decay exp(gamma_l - gamma_i). gram_tiles
+// (one wave doing both from one set of fragments): the off-diagonal products
+// cover the LDS round trip of X before the solve reads it back.
+template <int DK> __device__ inline void gram_diag(const KRows<DK> &k, const WsBufs<DK> &bf, int c, int g, int c16) {
     float *X = bf.X(c);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
         *reinterpret_cast<f32x4 *>(X + xoff(16 * b + c16, g)) = dot_tile<DK>(k.f[b], k.f[b]);
+}
+template <int DK, bool GATED>
+__device__ inline void gram_off(const KRows<DK> &k, const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
     const float *Bs = bf.B(c);
     const float b1 = Bs[16 + c16], b2 = Bs[32 + c16], b3 = Bs[48 + c16];
     // row factors of A_ac: beta of row token 16a + j, times the decay when gated
@@ -744,6 +761,12 @@ template <int DK, bool GATED> __device__ inline void gram_tiles(const WsBufs<DK>
     st4(As + 3 * 256, cvt4(dot_tile<DK>(k.f[0], k.f[3]) * s30));
     st4(As + 4 * 256, cvt4(dot_tile<DK>(k.f[1], k.f[3]) * s31));
     st4(As + 5 * 256, cvt4(dot_tile<DK>(k.f[2], k.f[3]) * s32));
+}
+template <int DK, bool GATED> __device__ inline void gram_tiles(const WsBufs<DK> &bf, int c, int lane, int g, int c16) {
+    KRows<DK> k;
+    k_rows<DK>(k, bf.K(c), g, c16);
+    gram_diag<DK>(k, bf, c, g, c16);
+    gram_off<DK, GATED>(k, bf, c, lane, g, c16);
 }
 
 // Wave 4, after gram_tiles on the same chunk: lane group b solves diagonal
@@ -881,21 +904,49 @@ __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c,
     }
 }
 
-template <int DK, int DV, bool WO, bool GATED, int ROLE>
+// Producer roles. A 64-row workgroup has four producer waves:
+//   kRoleGram     all Gram tiles of chunk r+2 and the inverses of its diagonal
+//                 blocks
+//   kRoleVT       V(r+1), beta(r+3) (and the decays) into LDS; T of chunk r+1
+//   kRoleKQP0/1   K(r+3) into LDS; Q and half of P of chunk r+1
+// A 32-row workgroup has two consumer waves and splits the first two roles
+// over four waves, so that each of its six producer waves has less on its
+// critical path and the matrix products spread over the SIMDs:
+//   kRoleGramDiag diagonal Gram tiles of chunk r+2 and their inverses
+//   kRoleGramOff  off-diagonal Gram tiles of chunk r+2
+//   kRoleOffSolve T of chunk r+1
+//   kRoleV        V(r+1), beta(r+3) (and the decays) into LDS
+enum {
+    kRoleGram = 0,
+    kRoleVT = 1,
+    kRoleKQP0 = 2,
+    kRoleKQP1 = 3,
+    kRoleGramDiag = 4,
+    kRoleGramOff = 5,
+    kRoleOffSolve = 6,
+    kRoleV = 7
+};
+
+template <int DK, int DV, bool WO, bool GATED, int ROLE, int ROWS>
 __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int g, int c16) {
+    constexpr bool kGramDiag = ROLE == kRoleGram || ROLE == kRoleGramDiag;
+    constexpr bool kGramOff = ROLE == kRoleGram || ROLE == kRoleGramOff;
+    constexpr bool kStageV = ROLE == kRoleVT || ROLE == kRoleV;
+    constexpr bool kOffSolve = ROLE == kRoleVT || ROLE == kRoleOffSolve;
+    constexpr bool kKQP = ROLE == kRoleKQP0 || ROLE == kRoleKQP1;
     const bool has_v = WO || wk.has_v;
     const int lane = 16 * g + c16;
     const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
     KStager<DK> ks;
-    VStager vs;
+    VStager<ROWS> vs;
     QStage<DK> q;
-    if constexpr (ROLE == 1) {
+    if constexpr (kStageV) {
         vs.init(reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0,
                 reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h,
                 GATED ? a.g + wk.h : nullptr, sv, a.H, wk.len, lane);
         if constexpr (GATED) vs.sb = substep_base(wk.tok0, a.nh);
     }
-    if constexpr (ROLE >= 2) {
+    if constexpr (kKQP) {
         ks.init(reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len,
                 64 * (ROLE - 2) + lane);
         if constexpr (WO)
@@ -907,26 +958,22 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
         }
     }
     if (NC > 0) { // K(0), K(1), beta(0), beta(1) are written in the first two iterations
-        if constexpr (ROLE >= 2) {
+        if constexpr (kKQP) {
             ks.template load<0>(0);
             ks.template load<1>(min(1, NC - 1));
         }
-        if constexpr (ROLE == 1) {
+        if constexpr (kStageV) {
             vs.template load_beta<0>(0);
             vs.template load_beta<1>(min(1, NC - 1));
         }
     }
     __syncthreads();
-    if (NC == 0) { // no chunks: the same barriers as the consumers' three iterations
-#pragma unroll
-        for (int i = 0; i < 3; ++i) __syncthreads();
+    if (NC == 0) { // no chunks: the same barriers as the consumers' iterations
+        for (int r = -3; r < ws_rend(NC); ++r) __syncthreads();
         return;
     }
 
-    // Iteration r:
-    //   wave 4:    Gram tiles of chunk r+2, inverses of its diagonal blocks
-    //   wave 5:    V(r+1) and beta(r+3) into LDS; T of chunk r+1
-    //   waves 6-7: K(r+3) into LDS; Q and P of chunk r+1
+    // Iteration r: chunks as in the role list above.
     // Every staging copy comes from registers loaded two iterations before
     // (register set = chunk parity; R = r & 1 is a template argument, so the
     // loop runs two iterations per trip) and is replaced by the loads of the
@@ -937,17 +984,31 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     const int last = NC - 1;
     auto iteration = [&](int r, auto rpar) {
         constexpr int S = 1 - decltype(rpar)::value; // set of chunks r+1, r+3, r+5
-        if constexpr (ROLE == 0) {
+        if constexpr (ROLE == kRoleGram) {
             if (r + 2 >= 0 && r + 2 < NC) {
                 gram_tiles<DK, GATED>(bf, r + 2, lane, g, c16);
                 diag_solve<DK, GATED>(bf, r + 2, g, c16);
             }
-        } else if constexpr (ROLE == 1) {
+        } else if constexpr (kGramDiag || kGramOff) {
+            if (r + 2 >= 0 && r + 2 < NC) {
+                KRows<DK> k;
+                k_rows<DK>(k, bf.K(r + 2), g, c16);
+                if constexpr (kGramDiag) {
+                    gram_diag<DK>(k, bf, r + 2, g, c16);
+                    diag_solve<DK, GATED>(bf, r + 2, g, c16);
+                } else {
+                    gram_off<DK, GATED>(k, bf, r + 2, lane, g, c16);
+                }
+            }
+        }
+        if constexpr (kStageV) {
             if (has_v) vs.template write_v<S>(bf.V(r + 1));
             vs.template write_beta<S>(bf.B(r + 3));
             if constexpr (GATED) vs.template write_gate<S>(bf.G(r + 3));
             if (has_v) vs.template load_v<S>(min(max(r + 3, 0), last));
             vs.template load_beta<S>(min(r + 5, last));
+        }
+        if constexpr (kOffSolve) {
             if (r + 1 >= 0 && r + 1 < NC) {
                 off_solve<DK>(bf, r + 1, lane, g, c16);
                 if constexpr (!WO) {
@@ -966,7 +1027,8 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
                     }
                 }
             }
-        } else {
+        }
+        if constexpr (kKQP) {
             ks.template write<S>(bf.K(r + 3));
             ks.template load<S>(min(r + 5, last));
             if constexpr (WO) {
@@ -985,13 +1047,18 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
         }
         __syncthreads();
     };
-    for (int r = -3; r < NC; r += 2) { // r odd
+    for (int r = -3; r < ws_rend(NC); r += 2) { // r odd
         iteration(r, Int<1>{});
-        if (r + 1 < NC) iteration(r + 1, Int<0>{});
+        iteration(r + 1, Int<0>{});
     }
 }
 
-template <int DK, int DV, bool WO, bool GATED>
+// ROWS = 64: waves 0-3 consumers, waves 4-7 the roles kRoleGram, kRoleVT,
+// kRoleKQP0, kRoleKQP1. ROWS = 32: waves 0-1 consumers, waves 2-7 the roles
+// kRoleGramDiag, kRoleGramOff, kRoleOffSolve, kRoleV, kRoleKQP0, kRoleKQP1;
+// wave w runs on SIMD w % 4, so the two consumers share their SIMDs with the
+// lightest producers (T and the V staging).
+template <int DK, int DV, bool WO, bool GATED, int ROWS>
 __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a) {
     using LY = WsLds<DK>;
     constexpr size_t kLds = GATED ? LY::total_gated : LY::total;
@@ -1000,7 +1067,7 @@ __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    const Work wk = decode_work<DK, DV>(a);
+    const Work wk = decode_work<DK, DV, ROWS>(a);
     const int NC = (wk.len + kChunk - 1) / kChunk;
     const WsBufs<DK> bf{smem};
 
@@ -1014,16 +1081,35 @@ __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a)
     }
     __syncthreads();
 
-    if (wave < 4) {
-        consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
-    } else if (wave == 4) {
-        producer_loop<DK, DV, WO, GATED, 0>(a, wk, bf, NC, g, c16);
-    } else if (wave == 5) {
-        producer_loop<DK, DV, WO, GATED, 1>(a, wk, bf, NC, g, c16);
-    } else if (wave == 6) {
-        producer_loop<DK, DV, WO, GATED, 2>(a, wk, bf, NC, g, c16);
+    if constexpr (ROWS == 64) {
+        if (wave < 4) {
+            consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
+        } else if (wave == 4) {
+            producer_loop<DK, DV, WO, GATED, kRoleGram, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 5) {
+            producer_loop<DK, DV, WO, GATED, kRoleVT, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 6) {
+            producer_loop<DK, DV, WO, GATED, kRoleKQP0, ROWS>(a, wk, bf, NC, g, c16);
+        } else {
+            producer_loop<DK, DV, WO, GATED, kRoleKQP1, ROWS>(a, wk, bf, NC, g, c16);
+        }
     } else {
-        producer_loop<DK, DV, WO, GATED, 3>(a, wk, bf, NC, g, c16);
+        static_assert(ROWS == 32, "tile rows");
+        if (wave < 2) {
+            consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
+        } else if (wave == 2) {
+            producer_loop<DK, DV, WO, GATED, kRoleGramDiag, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 3) {
+            producer_loop<DK, DV, WO, GATED, kRoleGramOff, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 4) {
+            producer_loop<DK, DV, WO, GATED, kRoleOffSolve, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 5) {
+            producer_loop<DK, DV, WO, GATED, kRoleV, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 6) {
+            producer_loop<DK, DV, WO, GATED, kRoleKQP0, ROWS>(a, wk, bf, NC, g, c16);
+        } else {
+            producer_loop<DK, DV, WO, GATED, kRoleKQP1, ROWS>(a, wk, bf, NC, g, c16);
+        }
     }
 }
 
@@ -1248,8 +1334,8 @@ __device__ void rev_consumer_loop(const BwdArgs &a, const RevWork &wk, const Rev
     __bf16 *dvg = reinterpret_cast<__bf16 *>(a.dv) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 + lrow;
     __bf16 *gout = a.G_chunks + (wk.slot0 * DV + wk.row0 + lrow) * DK;
     __syncthreads(); // matches the producers' prologue
-    for (int i = -2; i < NC; ++i) {
-        if (i >= 0) {
+    for (int i = -2; i < NC + (NC & 1); ++i) { // an even count, as the producers' loop
+        if (i >= 0 && i < NC) {
             const int r = NC - 1 - i, nval = min(kChunk, wk.len - r * kChunk);
             // dS' of chunk r (the gradient of the state after it), for the gradient kernel
 #pragma unroll
@@ -1369,9 +1455,14 @@ __device__ void rev_producer_loop(const BwdArgs &a, const RevWork &wk, const Rev
         }
         __syncthreads();
     };
-    for (int i = -2; i < NC; i += 2) { // i even
+    // an even number of iterations (one spare when NC is odd, which only
+    // stages into ring slots nobody reads again), two per trip: with no
+    // conditional iteration in the loop body the compiler's wait counts see
+    // the loads of both register sets in flight and wait only for the older
+    // set
+    for (int i = -2; i < NC + (NC & 1); i += 2) { // i even
         iteration(i, Int<0>{});
-        if (i + 1 < NC) iteration(i + 1, Int<1>{});
+        iteration(i + 1, Int<1>{});
     }
 }
 
@@ -1426,10 +1517,21 @@ template <int DK, int DV> hipError_t launch_rev(const BwdArgs &a, hipStream_t s)
 template <int DK, int DV, bool WO> hipError_t launch_ws(const ChainArgs &a, hipStream_t s) {
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
+    if (a.rows == 32) { // narrow tiles: forward with output, dense and packed kinds
+        if constexpr (WO) {
+            if ((a.kind != kDense && a.kind != kVarlen) || a.n_tiles != DV / 32) return hipErrorInvalidValue;
+            if (a.g)
+                hipLaunchKernelGGL((chain_kernel_ws<DK, DV, true, true, 32>), dim3(grid), dim3(kWsThreads), 0, s, a);
+            else
+                hipLaunchKernelGGL((chain_kernel_ws<DK, DV, true, false, 32>), dim3(grid), dim3(kWsThreads), 0, s, a);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     if (a.g)
-        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, true>), dim3(grid), dim3(kWsThreads), 0, s, a);
+        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, true, 64>), dim3(grid), dim3(kWsThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, false>), dim3(grid), dim3(kWsThreads), 0, s, a);
+        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, false, 64>), dim3(grid), dim3(kWsThreads), 0, s, a);
     return hipGetLastError();
 }
 

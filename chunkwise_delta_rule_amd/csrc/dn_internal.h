@@ -50,7 +50,10 @@ struct ChainArgs {
     int chunks_per_group;
     int nh;      // substeps per real token (Gated Delta Product; 1 otherwise, gated kernels only)
     int n_units; // units covered by the grid
-    int n_tiles; // 64-row state tiles per unit
+    int n_tiles; // state tiles per unit
+    int rows;    // state rows per tile of the bf16 chain kernel: 64, or 32 (forward with
+                 // output, dense and packed kinds, when 64-row tiles would leave compute
+                 // units idle); 0 reads as 64
 };
 
 // One decode step: a single token per unit applied to the state in place.

@@ -38,11 +38,13 @@ struct Work {
     __bf16 *Tchunks;  // T^T of chunk 0 of this unit (dense kind, first tile only), or nullptr
 };
 
-template <int DK, int DV> __device__ inline Work decode_work(const ChainArgs &a) {
+// ROWS: state rows per workgroup tile (64; 32 for the narrow forward tiles,
+// dense and packed kinds only).
+template <int DK, int DV, int ROWS = kRows> __device__ inline Work decode_work(const ChainArgs &a) {
     int u, tau;
     map_block(blockIdx.x, a.n_units, a.n_tiles, u, tau);
     const int H = a.H;
-    Work wk = {0, 0, 0, tau * kRows, u, nullptr, nullptr, nullptr, nullptr, false, false, true, nullptr};
+    Work wk = {0, 0, 0, tau * ROWS, u, nullptr, nullptr, nullptr, nullptr, false, false, true, nullptr};
     if (a.kind == kDense) {
         const int b = u / H;
         wk.h = u - b * H;

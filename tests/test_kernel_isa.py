@@ -75,8 +75,10 @@ def kernels(asm_text):
 
 
 def test_instances_present(asm):
-    # dk, dv in {64, 128}, with and without output, with and without decay
-    assert len(kernels(asm)) == 16
+    # dk, dv in {64, 128}, with and without decay: 64-row tiles with and
+    # without output, 32-row tiles with output
+    assert len(kernels(asm)) == 24
+    assert sum("ELi32EEEv" in name for name, _, _ in kernels(asm)) == 8
 
 
 def test_no_scratch_and_register_budget(asm):
