@@ -106,6 +106,13 @@ __device__ inline bf16x4 tr4(const __bf16 *p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
 }
 __device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
+// This lane's index in the wave, formed by two VALU instructions where it is
+// used (an asm block the compiler neither hoists nor keeps live).
+__device__ inline int lane_id() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 // Lane I of each group of four lanes, broadcast to the four (DPP quad_perm).
 template <int I> __device__ inline float quad_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x55 * I, 0xF, 0xF, true));
@@ -643,10 +650,12 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
         // O[t][i] = -O[16t + c][row 4g + i] (rows relative to this wave's 16).
         // Gated kernels: og is the output at real token 0; virtual row
         // 64 r + tok of the work is stored at its real token on the last
-        // substep only.
+        // substep only. The column index comes from the lane id formed here,
+        // so that no register holds it across the chain.
+        const int cl = lane_id() & 15;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int tok = 16 * t + c16;
+            const int tok = 16 * t + cl;
             if constexpr (GATED) {
                 const Substep st = substep_at(sb, (uint32_t)(r * kChunk + tok));
                 if (tok < nval && st.j == (int)sb.nh - 1) st4(og + st.t * sv, cvt4(-O[t]));
@@ -916,6 +925,11 @@ __device__ inline void p_tiles(const WsBufs<DK> &bf, const QStage<DK> &q, int c,
 //   kRoleGramOff  off-diagonal Gram tiles of chunk r+2
 //   kRoleOffSolve T of chunk r+1
 //   kRoleV        V(r+1), beta(r+3) (and the decays) into LDS
+// A 64-row workgroup of 12 waves (DeltaNet without decay) has four consumers
+// and eight producers: the four roles above and the two halves of kRoleKQP
+// split into K staging and Q plus P:
+//   kRoleK0/1     K(r+3) into LDS (half of the rows each)
+//   kRoleQP0/1    Q and half of P of chunk r+1
 enum {
     kRoleGram = 0,
     kRoleVT = 1,
@@ -924,7 +938,11 @@ enum {
     kRoleGramDiag = 4,
     kRoleGramOff = 5,
     kRoleOffSolve = 6,
-    kRoleV = 7
+    kRoleV = 7,
+    kRoleK0 = 8,
+    kRoleK1 = 9,
+    kRoleQP0 = 10,
+    kRoleQP1 = 11
 };
 
 template <int DK, int DV, bool WO, bool GATED, int ROLE, int ROWS>
@@ -933,7 +951,9 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     constexpr bool kGramOff = ROLE == kRoleGram || ROLE == kRoleGramOff;
     constexpr bool kStageV = ROLE == kRoleVT || ROLE == kRoleV;
     constexpr bool kOffSolve = ROLE == kRoleVT || ROLE == kRoleOffSolve;
-    constexpr bool kKQP = ROLE == kRoleKQP0 || ROLE == kRoleKQP1;
+    constexpr bool kStageK = ROLE == kRoleKQP0 || ROLE == kRoleKQP1 || ROLE == kRoleK0 || ROLE == kRoleK1;
+    constexpr bool kQP = ROLE == kRoleKQP0 || ROLE == kRoleKQP1 || ROLE == kRoleQP0 || ROLE == kRoleQP1;
+    constexpr int half = (ROLE == kRoleKQP1 || ROLE == kRoleK1 || ROLE == kRoleQP1) ? 1 : 0;
     const bool has_v = WO || wk.has_v;
     const int lane = 16 * g + c16;
     const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
@@ -946,19 +966,20 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
                 GATED ? a.g + wk.h : nullptr, sv, a.H, wk.len, lane);
         if constexpr (GATED) vs.sb = substep_base(wk.tok0, a.nh);
     }
-    if constexpr (kKQP) {
+    if constexpr (kStageK)
         ks.init(reinterpret_cast<const __bf16 *>(a.k) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len,
-                64 * (ROLE - 2) + lane);
+                64 * half + lane);
+    if constexpr (kQP) {
         if constexpr (WO)
-            q.init(reinterpret_cast<const __bf16 *>(a.q) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len, ROLE - 2,
-                   g, c16);
+            q.init(reinterpret_cast<const __bf16 *>(a.q) + wk.tok0 * sqk + (int64_t)wk.h * DK, sqk, wk.len, half, g,
+                   c16);
         if constexpr (WO && GATED) {
             q.qh = reinterpret_cast<const __bf16 *>(a.q) + (int64_t)wk.h * DK + 8 * g;
             q.sb = substep_base(wk.tok0, a.nh);
         }
     }
     if (NC > 0) { // K(0), K(1), beta(0), beta(1) are written in the first two iterations
-        if constexpr (kKQP) {
+        if constexpr (kStageK) {
             ks.template load<0>(0);
             ks.template load<1>(min(1, NC - 1));
         }
@@ -1028,14 +1049,16 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
                 }
             }
         }
-        if constexpr (kKQP) {
+        if constexpr (kStageK) {
             ks.template write<S>(bf.K(r + 3));
             ks.template load<S>(min(r + 5, last));
+        }
+        if constexpr (kQP) {
             if constexpr (WO) {
                 if (r + 1 >= 0 && r + 1 < NC) {
                     if constexpr (GATED) q.template mask_virtual<S>();
                     q.template write<S>(bf.Q(r + 1), g);
-                    p_tiles<DK, S, GATED>(bf, q, r + 1, ROLE - 2, lane, g, c16);
+                    p_tiles<DK, S, GATED>(bf, q, r + 1, half, lane, g, c16);
                 }
             }
             if constexpr (WO) {
@@ -1053,13 +1076,20 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     }
 }
 
-// ROWS = 64: waves 0-3 consumers, waves 4-7 the roles kRoleGram, kRoleVT,
-// kRoleKQP0, kRoleKQP1. ROWS = 32: waves 0-1 consumers, waves 2-7 the roles
-// kRoleGramDiag, kRoleGramOff, kRoleOffSolve, kRoleV, kRoleKQP0, kRoleKQP1;
-// wave w runs on SIMD w % 4, so the two consumers share their SIMDs with the
-// lightest producers (T and the V staging).
-template <int DK, int DV, bool WO, bool GATED, int ROWS>
-__global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a) {
+// Wave w runs on SIMD w % 4. Layouts (NW waves, ROWS state rows):
+//   NW = 8,  ROWS = 64: waves 0-3 consumers; 4-7 kRoleGram, kRoleVT,
+//            kRoleKQP0, kRoleKQP1
+//   NW = 12, ROWS = 64 (forward with output, no decay): waves 0-3
+//            consumers; 4-11 kRoleOffSolve, kRoleGramOff, kRoleK0, kRoleV,
+//            kRoleGramDiag, kRoleK1, kRoleQP0, kRoleQP1 (matrix products of
+//            about 2.6-2.7k cycles per chunk on every SIMD)
+//   NW = 8,  ROWS = 32: waves 0-1 consumers; 2-7 kRoleGramDiag,
+//            kRoleGramOff, kRoleOffSolve, kRoleV, kRoleKQP0, kRoleKQP1 (the
+//            consumers share their SIMDs with the lightest producers)
+// Twelve waves leave 168 registers per lane, too few for the consumers of
+// the decayed kernels, which keep the 8-wave layout.
+template <int DK, int DV, bool WO, bool GATED, int ROWS, int NW>
+__global__ __launch_bounds__(NW * 64) void chain_kernel_ws(const ChainArgs a) {
     using LY = WsLds<DK>;
     constexpr size_t kLds = GATED ? LY::total_gated : LY::total;
     static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -1077,11 +1107,33 @@ __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a)
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 *zt = reinterpret_cast<f32x4 *>(smem + LY::oT);
         constexpr int nvec = (int)((2 * LY::sz64 + 2 * LY::szP) / 16); // T^T x2 and P x2 are contiguous
-        for (int i = tid; i < nvec; i += kWsThreads) zt[i] = zero;
+        for (int i = tid; i < nvec; i += NW * 64) zt[i] = zero;
     }
     __syncthreads();
 
-    if constexpr (ROWS == 64) {
+    if constexpr (NW == 12) {
+        static_assert(ROWS == 64, "tile rows");
+        if (wave < 4) {
+            consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
+        } else if (wave == 4) {
+            producer_loop<DK, DV, WO, GATED, kRoleOffSolve, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 5) {
+            producer_loop<DK, DV, WO, GATED, kRoleGramOff, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 6) {
+            producer_loop<DK, DV, WO, GATED, kRoleK0, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 7) {
+            producer_loop<DK, DV, WO, GATED, kRoleV, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 8) {
+            producer_loop<DK, DV, WO, GATED, kRoleGramDiag, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 9) {
+            producer_loop<DK, DV, WO, GATED, kRoleK1, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 10) {
+            producer_loop<DK, DV, WO, GATED, kRoleQP0, ROWS>(a, wk, bf, NC, g, c16);
+        } else {
+            producer_loop<DK, DV, WO, GATED, kRoleQP1, ROWS>(a, wk, bf, NC, g, c16);
+        }
+    } else if constexpr (ROWS == 64) {
+        static_assert(NW == 8, "waves");
         if (wave < 4) {
             consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
         } else if (wave == 4) {
@@ -1094,7 +1146,7 @@ __global__ __launch_bounds__(kWsThreads) void chain_kernel_ws(const ChainArgs a)
             producer_loop<DK, DV, WO, GATED, kRoleKQP1, ROWS>(a, wk, bf, NC, g, c16);
         }
     } else {
-        static_assert(ROWS == 32, "tile rows");
+        static_assert(ROWS == 32 && NW == 8, "tile rows");
         if (wave < 2) {
             consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
         } else if (wave == 2) {
@@ -1521,17 +1573,19 @@ template <int DK, int DV, bool WO> hipError_t launch_ws(const ChainArgs &a, hipS
         if constexpr (WO) {
             if ((a.kind != kDense && a.kind != kVarlen) || a.n_tiles != DV / 32) return hipErrorInvalidValue;
             if (a.g)
-                hipLaunchKernelGGL((chain_kernel_ws<DK, DV, true, true, 32>), dim3(grid), dim3(kWsThreads), 0, s, a);
+                hipLaunchKernelGGL((chain_kernel_ws<DK, DV, true, true, 32, 8>), dim3(grid), dim3(512), 0, s, a);
             else
-                hipLaunchKernelGGL((chain_kernel_ws<DK, DV, true, false, 32>), dim3(grid), dim3(kWsThreads), 0, s, a);
+                hipLaunchKernelGGL((chain_kernel_ws<DK, DV, true, false, 32, 8>), dim3(grid), dim3(512), 0, s, a);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
     }
     if (a.g)
-        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, true, 64>), dim3(grid), dim3(kWsThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, false, 64>), dim3(grid), dim3(kWsThreads), 0, s, a);
+        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, true, 64, 8>), dim3(grid), dim3(512), 0, s, a);
+    else if constexpr (WO)
+        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, true, false, 64, 12>), dim3(grid), dim3(768), 0, s, a);
+    else // the backward's forward pass and the context-parallel transitions: 8 waves measured faster
+        hipLaunchKernelGGL((chain_kernel_ws<DK, DV, false, false, 64, 8>), dim3(grid), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -76,9 +76,12 @@ def kernels(asm_text):
 
 def test_instances_present(asm):
     # dk, dv in {64, 128}, with and without decay: 64-row tiles with and
-    # without output, 32-row tiles with output
-    assert len(kernels(asm)) == 24
-    assert sum("ELi32EEEv" in name for name, _, _ in kernels(asm)) == 8
+    # without output (12 waves for the output without decay, else 8), 32-row
+    # tiles with output
+    names = [name for name, _, _ in kernels(asm)]
+    assert len(names) == 24
+    assert sum("ELi32ELi8E" in n for n in names) == 8
+    assert sum("ELi64ELi12E" in n for n in names) == 4 and sum("ELi64ELi8E" in n for n in names) == 12
 
 
 def test_no_scratch_and_register_budget(asm):
