@@ -249,12 +249,6 @@ template <int DK> struct WsBufs {
 // valid row for the missing rows and writes them as zeros. Two register sets
 // (chunk parity) keep two chunks in flight.
 __device__ inline int rows_of(int len, int c) { return min(kChunk, len - c * kChunk); }
-// End of the chain kernel's iteration range r = -3 .. NC - 1, rounded up so
-// that the count is even: the producers run two iterations per loop trip
-// with no conditional one inside, so the compiler's wait counts see the loads
-// of both register sets in flight and wait only for the older set (the spare
-// iteration stages into ring slots that nobody reads again).
-__device__ inline int ws_rend(int NC) { return NC + ((NC + 3) & 1); }
 
 // K by the 128 threads of waves 6-7 (pt = 0..127): thread pt owns the 16-byte
 // column piece 8 (pt % KV) of rows pt / KV + RPS p, p = 0..NK-1.
@@ -681,19 +675,19 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
 
     const SubstepBase sb = GATED ? substep_base(wk.tok0, a.nh) : SubstepBase{0, 0u, 1u};
     __syncthreads(); // matches the producers' prologue
-    for (int r = -3; r < ws_rend(NC); ++r) {
-        if (!WO && r >= 0 && r < NC && wk.Schunks) { // the state entering chunk r, for the backward pass
+    for (int r = -3; r < NC; ++r) {
+        if (!WO && r >= 0 && wk.Schunks) { // the state entering chunk r, for the backward pass
             Work ck = wk;
             ck.Sout = wk.Schunks + (int64_t)r * DV * DK;
             ck.transposed_out = false;
             ws_state_out<DK>(Sacc, ck, cw, g, c16);
         }
-        if (!WO && r >= 0 && r < NC && wk.Schunks16) { // the same in bf16 ([dv][dk] rows)
+        if (!WO && r >= 0 && wk.Schunks16) { // the same in bf16 ([dv][dk] rows)
             __bf16 *so = wk.Schunks16 + (int64_t)r * DV * DK + (16 * cw + c16) * DK;
 #pragma unroll
             for (int m = 0; m < DK / 16; ++m) st4(so + dk_of(m, g), cvt4(Sacc[m]));
         }
-        if (r >= 0 && r < NC)
+        if (r >= 0)
             consumer_chain<DK, WO, GATED>(bf, r, Sacc, WO ? og + (GATED ? 0 : (int64_t)r * kChunk * sv) : nullptr,
                                           sv, min(kChunk, wk.len - r * kChunk), sb, has_v, cw, lane, g, c16);
         __syncthreads();
@@ -989,8 +983,9 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
         }
     }
     __syncthreads();
-    if (NC == 0) { // no chunks: the same barriers as the consumers' iterations
-        for (int r = -3; r < ws_rend(NC); ++r) __syncthreads();
+    if (NC == 0) { // no chunks: the same barriers as the consumers' three iterations
+#pragma unroll
+        for (int i = 0; i < 3; ++i) __syncthreads();
         return;
     }
 
@@ -1070,9 +1065,9 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
         }
         __syncthreads();
     };
-    for (int r = -3; r < ws_rend(NC); r += 2) { // r odd
+    for (int r = -3; r < NC; r += 2) { // r odd
         iteration(r, Int<1>{});
-        iteration(r + 1, Int<0>{});
+        if (r + 1 < NC) iteration(r + 1, Int<0>{});
     }
 }
 
@@ -1386,8 +1381,8 @@ __device__ void rev_consumer_loop(const BwdArgs &a, const RevWork &wk, const Rev
     __bf16 *dvg = reinterpret_cast<__bf16 *>(a.dv) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 + lrow;
     __bf16 *gout = a.G_chunks + (wk.slot0 * DV + wk.row0 + lrow) * DK;
     __syncthreads(); // matches the producers' prologue
-    for (int i = -2; i < NC + (NC & 1); ++i) { // an even count, as the producers' loop
-        if (i >= 0 && i < NC) {
+    for (int i = -2; i < NC; ++i) {
+        if (i >= 0) {
             const int r = NC - 1 - i, nval = min(kChunk, wk.len - r * kChunk);
             // dS' of chunk r (the gradient of the state after it), for the gradient kernel
 #pragma unroll
@@ -1507,14 +1502,9 @@ __device__ void rev_producer_loop(const BwdArgs &a, const RevWork &wk, const Rev
         }
         __syncthreads();
     };
-    // an even number of iterations (one spare when NC is odd, which only
-    // stages into ring slots nobody reads again), two per trip: with no
-    // conditional iteration in the loop body the compiler's wait counts see
-    // the loads of both register sets in flight and wait only for the older
-    // set
-    for (int i = -2; i < NC + (NC & 1); i += 2) { // i even
+    for (int i = -2; i < NC; i += 2) { // i even
         iteration(i, Int<0>{});
-        iteration(i + 1, Int<1>{});
+        if (i + 1 < NC) iteration(i + 1, Int<1>{});
     }
 }
 
