@@ -477,6 +477,9 @@ def main():
                     help="target seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--gated", action="store_true",
                     help="measure Gated DeltaNet (per-token log decays) instead of DeltaNet")
+    ap.add_argument("--variants", default="all",
+                    help="comma-separated variants to run after the main line (gated, bwd, gated_bwd, gdp, gdp_bwd, "
+                         "kda, kda_long, workloads, decode), or all")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the short gated and decode runs reported under variants")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -602,33 +605,44 @@ def main():
         "settle_s_untimed": SETTLE_S,
         "roofline": roofline,
     }
-    if not args.gated and not args.no_variants:
+    def want(name):
+        return not args.gated and not args.no_variants and (args.variants == "all" or name in args.variants.split(","))
+
+    if want("gated"):
         # the same workload through deltanet_gated_fwd (log decays drawn as in synth.make_gates)
         print("[bench] gated variant: warmup 5, timing 20 steps", file=sys.stderr, flush=True)
         g_ms, g_launch_ms, _ = time_steps(lambda: step(gated=True), 5, 20)
         g_bytes = algorithmic_bytes(w, esz, n_tokens, n_units, S0 is not None, True, True)
-        result["variants"] = {"gated": {
+        result.setdefault("variants", {})["gated"] = {
             "call": "deltanet_gated_fwd", "steps": 20, "warmup": 5,
             "ms_per_step": round(g_ms, 5), "tokens_per_s": round(n_tokens / (g_ms / 1e3), 1),
             "avg_launch_us": round(g_launch_ms * 1e3, 2), "algorithmic_bytes": g_bytes,
             "hbm_frac": round(g_bytes / (g_launch_ms / 1e3) / PEAK_HBM_BPS, 4),
             "mfma_frac": round(flops / (g_launch_ms / 1e3) / peak_flops, 4),
-            "vs_ungated_time": round(g_launch_ms / avg_launch_ms, 4)}}
-    if not args.gated and not args.no_variants and not w.varlen and w.dtype == "bf16":
-        result.setdefault("variants", {})["bwd"] = bwd_variant(dev, w, inputs, avg_launch_ms)
-        result["variants"]["gated_bwd"] = gated_bwd_variant(dev, w, inputs, avg_launch_ms)
-        result["variants"]["gdp"] = gdp_variant(dev, w, flops / n_tokens / w.H, peak_flops)
-        result["variants"]["gdp_bwd"] = gdp_bwd_variant(dev, w, result["variants"]["gdp"]["avg_launch_us"] / 1e3)
-        result["variants"]["kda"] = kda_variant(dev, w, inputs, avg_launch_ms)
-        result["variants"]["kda_long"] = kda_long_variant(dev)
-    if not args.gated and not args.no_variants and w.name == "layer_b8_h16_t4096":
+            "vs_ungated_time": round(g_launch_ms / avg_launch_ms, 4)}
+    if not w.varlen and w.dtype == "bf16" and any(map(want, ("bwd", "gated_bwd", "gdp", "gdp_bwd", "kda", "kda_long"))):
+        var = result.setdefault("variants", {})
+        if want("bwd"):
+            var["bwd"] = bwd_variant(dev, w, inputs, avg_launch_ms)
+        if want("gated_bwd"):
+            var["gated_bwd"] = gated_bwd_variant(dev, w, inputs, avg_launch_ms)
+        if want("gdp") or want("gdp_bwd"):
+            var["gdp"] = gdp_variant(dev, w, flops / n_tokens / w.H, peak_flops)
+        if want("gdp_bwd"):
+            var["gdp_bwd"] = gdp_bwd_variant(dev, w, var["gdp"]["avg_launch_us"] / 1e3)
+        if want("kda"):
+            var["kda"] = kda_variant(dev, w, inputs, avg_launch_ms)
+        if want("kda_long"):
+            var["kda_long"] = kda_long_variant(dev)
+    if want("workloads") and w.name == "layer_b8_h16_t4096":
         # the other workloads of the forward pass, each timed by the same clock
+        result.setdefault("variants", {})
         result["variants"]["chunks128_b4_h16_t8192"] = workload_variant(dev, "chunks128_b4_h16_t8192", (1, 0))
         result["variants"]["long_b1_h16_t131072"] = workload_variant(dev, "long_b1_h16_t131072", (1, 0),
                                                                      steps=5, warmup=2)
         result["variants"]["varlen_n64_h32"] = workload_variant(dev, "varlen_n64_h32", steps=5, warmup=2)
         result["variants"]["tiny_f32"] = workload_variant(dev, "tiny_f32", steps=20, warmup=5)
-    if not args.gated and not args.no_variants:
+    if want("decode"):
         result.setdefault("variants", {})["decode"] = decode_variant(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
