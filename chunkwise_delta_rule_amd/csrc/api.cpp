@@ -57,12 +57,13 @@ int pick_groups(int B, int H, int T, int dv) {
 }
 
 // State rows per workgroup tile of the bf16 forward with output on the
-// serial chain: 32 when 64-row tiles would leave compute units idle (twice
-// the workgroups, each with half the consumer work and its producer work
-// spread over six waves, so the per-chunk latency drops), else 64.
+// serial chain: 32 when the 32-row grid still fits on the compute units in
+// one round (twice the workgroups of the 64-row grid, each with half the
+// consumer work and its producer work spread over six waves, so a chunk takes
+// about a fifth less time), else 64 (a second round would cost more).
 int pick_rows(int dtype, int n_units, int dv) {
     if (dtype != DN_BF16) return dn::kRows;
-    return (int64_t)n_units * (dv / dn::kRows) < device_cus() ? 32 : dn::kRows;
+    return (int64_t)n_units * (dv / 32) <= device_cus() ? 32 : dn::kRows;
 }
 
 // Resolve the requested group count into (G, chunks per group) with no empty group.

@@ -52,8 +52,8 @@ struct ChainArgs {
     int n_units; // units covered by the grid
     int n_tiles; // state tiles per unit
     int rows;    // state rows per tile of the bf16 chain kernel: 64, or 32 (forward with
-                 // output, dense and packed kinds, when 64-row tiles would leave compute
-                 // units idle); 0 reads as 64
+                 // output, dense and packed kinds, when the 32-row grid fits on the compute
+                 // units in one round); 0 reads as 64
 };
 
 // One decode step: a single token per unit applied to the state in place.
