@@ -600,7 +600,7 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        Y[t] = GATED ? zero : widen4(vf[t]); // gated: -K S^T first, V added with the row factors
+        Y[t] = zero; // -K S^T first; V joins before the conversion, so its reads are waited for only there
         Z[t] = zero;
         O[t] = zero;
     }
@@ -610,10 +610,8 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
         const bf16x8 f = buf[i % D];
         if constexpr (i + D < CS::n) buf[i % D] = chain_fetch<DK, WO>(i + D, src, lane, g, c16);
         if constexpr (i == CS::bZ) {
-            if constexpr (GATED) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) Y[t] = widen4(vf[t]) + eg[t] * Y[t];
-            }
+            for (int t = 0; t < 4; ++t) Y[t] = GATED ? widen4(vf[t]) + eg[t] * Y[t] : widen4(vf[t]) + Y[t];
             YB[0] = cvt8(Y[0], Y[1]);
             YB[1] = cvt8(Y[2], Y[3]);
         }
