@@ -1955,36 +1955,50 @@ __global__ __launch_bounds__(kKdaThreads) void kda_chain_kernel(const ChainArgs 
             float e16[CPL];
 #pragma unroll
             for (int q = 0; q < CPL; ++q) e16[q] = __builtin_amdgcn_exp2f(acc[q]);
+            // the scaled rows; EXACT and FULL (every token of the sub-chunk
+            // inside the sequence) are wave-uniform, so each combination runs
+            // without the selects (and, in the factored path, without the
+            // third exponential) of the others
+            auto scale = [&](auto exact_c, auto full_c) {
+                constexpr bool EXACT = decltype(exact_c)::value != 0, FULL = decltype(full_c)::value != 0;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int row = 16 * j + t;
-                const bool on = row < n;
-                E a1[CPL], a2[CPL], a3[CPL], a4[CPL];
+                for (int t = 0; t < 16; ++t) {
+                    const bool on = FULL || 16 * j + t < n;
+                    E a1[CPL], a2[CPL], a3[CPL], a4[CPL];
 #pragma unroll
-                for (int q = 0; q < CPL; ++q) {
-                    const float kv = on ? kdv(kx[t], q) : 0.f, qv = on ? kdv(qx[t], q) : 0.f;
-                    const float el = __builtin_amdgcn_exp2f(gam[t][q]), er = __builtin_amdgcn_exp2f(-gam[t][q]);
-                    // exp(gamma_16 - gamma) <= 1: within the factored range the
-                    // product of the two factors; beyond it, from the difference itself
-                    const float ef = exact ? __builtin_amdgcn_exp2f(acc[q] - gam[t][q]) : e16[q] * er;
-                    a1[q] = TR::fromf(-(kv * el));
-                    a2[q] = TR::fromf(qv * el);
-                    a3[q] = TR::fromf(on ? kv * er : 0.f);
-                    a4[q] = TR::fromf(kv * ef);
+                    for (int q = 0; q < CPL; ++q) {
+                        const float kv = on ? kdv(kx[t], q) : 0.f, qv = on ? kdv(qx[t], q) : 0.f;
+                        const float el = __builtin_amdgcn_exp2f(gam[t][q]), er = __builtin_amdgcn_exp2f(-gam[t][q]);
+                        // exp(gamma_16 - gamma) <= 1: within the factored range the
+                        // product of the two factors; beyond it, from the difference itself
+                        const float ef = EXACT ? __builtin_amdgcn_exp2f(acc[q] - gam[t][q]) : e16[q] * er;
+                        a1[q] = TR::fromf(-(kv * el));
+                        a2[q] = TR::fromf(qv * el);
+                        a3[q] = TR::fromf(on ? kv * er : 0.f); // er may be infinite past the end (exact path)
+                        a4[q] = TR::fromf(kv * ef);
+                    }
+                    if constexpr (CPL == 2) {
+                        const int o = okda<DK>(t, pd) + 16 * j * RK; // t, and so the swizzle, is a constant here
+                        *reinterpret_cast<bf16x2 *>(KLb + o) = bf16x2{a1[0], a1[1]};
+                        *reinterpret_cast<bf16x2 *>(QLb + o) = bf16x2{a2[0], a2[1]};
+                        *reinterpret_cast<bf16x2 *>(Kr + o) = bf16x2{a3[0], a3[1]};
+                        *reinterpret_cast<bf16x2 *>(KFb + o) = bf16x2{a4[0], a4[1]};
+                    } else {
+                        const int o = okda<DK>(t, pd) + 16 * j * RK;
+                        KLb[o] = a1[0];
+                        QLb[o] = a2[0];
+                        Kr[o] = a3[0];
+                        KFb[o] = a4[0];
+                    }
                 }
-                if constexpr (CPL == 2) {
-                    const int o = okda<DK>(t, pd) + 16 * j * RK; // t, and so the swizzle, is a constant here
-                    *reinterpret_cast<bf16x2 *>(KLb + o) = bf16x2{a1[0], a1[1]};
-                    *reinterpret_cast<bf16x2 *>(QLb + o) = bf16x2{a2[0], a2[1]};
-                    *reinterpret_cast<bf16x2 *>(Kr + o) = bf16x2{a3[0], a3[1]};
-                    *reinterpret_cast<bf16x2 *>(KFb + o) = bf16x2{a4[0], a4[1]};
-                } else {
-                    const int o = okda<DK>(t, pd) + 16 * j * RK;
-                    KLb[o] = a1[0];
-                    QLb[o] = a2[0];
-                    Kr[o] = a3[0];
-                    KFb[o] = a4[0];
-                }
+            };
+            const bool full = 16 * j + 15 < n;
+            if (exact) {
+                if (full) scale(Int<1>{}, Int<1>{});
+                else scale(Int<1>{}, Int<0>{});
+            } else {
+                if (full) scale(Int<0>{}, Int<1>{});
+                else scale(Int<0>{}, Int<0>{});
             }
 #pragma unroll
             for (int q = 0; q < CPL; ++q) Eb[j * DK + pd + q] = e16[q];
