@@ -139,10 +139,13 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
     a.ws_S = a.ws_Q + per * dv * dk;
     a.G = G;
     a.chunks_per_group = cpg;
-    // (i) group transitions for groups 0..G-2
+    // (i) group transitions for groups 0..G-2: at dk = dv = 128 without decay,
+    // one 128-row tile for Q_g and one for P_g (the chunk's Gram tiles,
+    // inverses and T formed once per 128 state rows); else 64-row tiles
     a.kind = dn::kCpTransition;
     a.n_units = B * H * (G - 1);
-    a.n_tiles = dv / dn::kRows + dk / dn::kRows;
+    a.rows = (dtype == DN_BF16 && !g && dk == 128 && dv == 128) ? 128 : dn::kRows;
+    a.n_tiles = dv / a.rows + dk / a.rows;
     err = dn::launch_chain(dtype, dk, dv, false, a, stream);
     if (err != hipSuccess) return DN_ERR_HIP;
     // (ii) prefix composition of the maps -> start states of groups 1..G-1
@@ -150,6 +153,7 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
     if (err != hipSuccess) return DN_ERR_HIP;
     // (iii) every group from its start state, writing o (and S_final from the last group)
     a.kind = dn::kCpOutput;
+    a.rows = dn::kRows;
     a.n_units = B * H * G;
     a.n_tiles = dv / dn::kRows;
     err = dn::launch_chain(dtype, dk, dv, true, a, stream);

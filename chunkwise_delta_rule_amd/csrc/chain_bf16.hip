@@ -238,6 +238,9 @@ template <int DK> struct WsBufs {
     __device__ inline __bf16 *Tt(int c) const { return (__bf16 *)(base + LY::oT + (c & 1) * LY::sz64); }
     __device__ inline __bf16 *P(int c) const { return (__bf16 *)(base + LY::oP + (c & 1) * LY::szP); }
     __device__ inline __bf16 *V(int c) const { return (__bf16 *)(base + LY::oV + (c & 1) * LY::sz64); }
+    // 128-row tiles (no output, so the Q ring is free): V of all 128 value
+    // columns as two 64-column halves, half h at Vw(c) + 4096 h
+    __device__ inline __bf16 *Vw(int c) const { return (__bf16 *)(base + LY::oQ + (c & 1) * LY::szK); }
     __device__ inline __bf16 *N(int c) const { return (__bf16 *)(base + LY::oN + (c & 1) * LY::szN); }
     __device__ inline float *X(int c) const { return (float *)(base + LY::oX + (c & 1) * LY::szX); }
     __device__ inline __bf16 *A(int c) const { return (__bf16 *)(base + LY::oA + (c & 1) * LY::szA); }
@@ -542,22 +545,24 @@ __device__ inline bf16x8 chain_fetch(int i, const ChainSrc<DK, WO> &src, int lan
 
 __device__ inline f32x4 widen4(bf16x4 v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
 
-template <int DK, bool WO, bool GATED>
+template <int DK, bool WO, bool GATED, int ROWS>
 __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)[DK / 16], __bf16 *og, int64_t sv,
                                       int nval, const SubstepBase &sb, bool has_v, int cw, int lane, int g,
                                       int c16) {
     using CS = ChainSteps<DK, WO>;
-    constexpr int D = CS::depth;
+    constexpr int D = ROWS == 128 ? 4 : CS::depth; // 128-row tiles: 128 registers per lane
     const ChainSrc<DK, WO> src{bf.K(r), WO ? bf.Q(r) : nullptr, bf.Tt(r), WO ? bf.P(r) : nullptr};
     bf16x8 SB[CS::NKB], YB[2], ZB[2], ZS[2], buf[D];
     f32x4 Y[4], Z[4], O[4];
     // V_t in the accumulator layout: lane (g, c) gets V[16t + 4g + e][16cw + c]
     bf16x4 vf[4];
     if (has_v) {
-        const __bf16 *Vb = bf.V(r);
+        // 128-row tiles: consumers 4-7 read the second 64-column half
+        const __bf16 *Vb = ROWS == 128 ? bf.Vw(r) + 4096 * (cw >> 2) : bf.V(r);
+        const int vc = ROWS == 128 ? (cw & 3) : cw;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int row = 32 * s + 4 * g + (c16 >> 2), col = 16 * cw + 4 * (c16 & 3);
+            const int row = 32 * s + 4 * g + (c16 >> 2), col = 16 * vc + 4 * (c16 & 3);
             vf[2 * s] = tr4(Vb + s64off(row, col));
             vf[2 * s + 1] = tr4(Vb + s64off(row + 16, col));
         }
@@ -658,7 +663,7 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
     }
 }
 
-template <int DK, int DV, bool WO, bool GATED>
+template <int DK, int DV, bool WO, bool GATED, int ROWS>
 __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int cw, int lane,
                               int g, int c16) {
     constexpr int NMT = DK / 16;
@@ -674,19 +679,20 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     const SubstepBase sb = GATED ? substep_base(wk.tok0, a.nh) : SubstepBase{0, 0u, 1u};
     __syncthreads(); // matches the producers' prologue
     for (int r = -3; r < NC; ++r) {
-        if (!WO && r >= 0 && wk.Schunks) { // the state entering chunk r, for the backward pass
+        // the state entering chunk r, for the backward pass (never for 128-row tiles)
+        if (!WO && ROWS != 128 && r >= 0 && wk.Schunks) {
             Work ck = wk;
             ck.Sout = wk.Schunks + (int64_t)r * DV * DK;
             ck.transposed_out = false;
             ws_state_out<DK>(Sacc, ck, cw, g, c16);
         }
-        if (!WO && r >= 0 && wk.Schunks16) { // the same in bf16 ([dv][dk] rows)
+        if (!WO && ROWS != 128 && r >= 0 && wk.Schunks16) { // the same in bf16 ([dv][dk] rows)
             __bf16 *so = wk.Schunks16 + (int64_t)r * DV * DK + (16 * cw + c16) * DK;
 #pragma unroll
             for (int m = 0; m < DK / 16; ++m) st4(so + dk_of(m, g), cvt4(Sacc[m]));
         }
         if (r >= 0)
-            consumer_chain<DK, WO, GATED>(bf, r, Sacc, WO ? og + (GATED ? 0 : (int64_t)r * kChunk * sv) : nullptr,
+            consumer_chain<DK, WO, GATED, ROWS>(bf, r, Sacc, WO ? og + (GATED ? 0 : (int64_t)r * kChunk * sv) : nullptr,
                                           sv, min(kChunk, wk.len - r * kChunk), sb, has_v, cw, lane, g, c16);
         __syncthreads();
     }
@@ -934,14 +940,18 @@ enum {
     kRoleK0 = 8,
     kRoleK1 = 9,
     kRoleQP0 = 10,
-    kRoleQP1 = 11
+    kRoleQP1 = 11,
+    kRoleV1 = 12 // 128-row tiles: the second 64-column half of V (kRoleV stages the first and beta)
 };
 
 template <int DK, int DV, bool WO, bool GATED, int ROLE, int ROWS>
 __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<DK> &bf, int NC, int g, int c16) {
     constexpr bool kGramDiag = ROLE == kRoleGram || ROLE == kRoleGramDiag;
     constexpr bool kGramOff = ROLE == kRoleGram || ROLE == kRoleGramOff;
-    constexpr bool kStageV = ROLE == kRoleVT || ROLE == kRoleV;
+    constexpr bool kStageV = ROLE == kRoleVT || ROLE == kRoleV || ROLE == kRoleV1;
+    constexpr bool kStageBeta = ROLE == kRoleVT || ROLE == kRoleV;
+    constexpr int kVHalf = ROLE == kRoleV1 ? 1 : 0;
+    static_assert(ROWS == 128 || ROLE != kRoleV1, "second V half: 128-row tiles only");
     constexpr bool kOffSolve = ROLE == kRoleVT || ROLE == kRoleOffSolve;
     constexpr bool kStageK = ROLE == kRoleKQP0 || ROLE == kRoleKQP1 || ROLE == kRoleK0 || ROLE == kRoleK1;
     constexpr bool kQP = ROLE == kRoleKQP0 || ROLE == kRoleKQP1 || ROLE == kRoleQP0 || ROLE == kRoleQP1;
@@ -950,10 +960,10 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     const int lane = 16 * g + c16;
     const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
     KStager<DK> ks;
-    VStager<ROWS> vs;
+    VStager<(ROWS == 128 ? 64 : ROWS)> vs;
     QStage<DK> q;
     if constexpr (kStageV) {
-        vs.init(reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0,
+        vs.init(reinterpret_cast<const __bf16 *>(a.v) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 + 64 * kVHalf,
                 reinterpret_cast<const __bf16 *>(a.beta) + wk.tok0 * a.H + wk.h,
                 GATED ? a.g + wk.h : nullptr, sv, a.H, wk.len, lane);
         if constexpr (GATED) vs.sb = substep_base(wk.tok0, a.nh);
@@ -975,7 +985,7 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
             ks.template load<0>(0);
             ks.template load<1>(min(1, NC - 1));
         }
-        if constexpr (kStageV) {
+        if constexpr (kStageBeta) {
             vs.template load_beta<0>(0);
             vs.template load_beta<1>(min(1, NC - 1));
         }
@@ -1016,11 +1026,13 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
             }
         }
         if constexpr (kStageV) {
-            if (has_v) vs.template write_v<S>(bf.V(r + 1));
-            vs.template write_beta<S>(bf.B(r + 3));
-            if constexpr (GATED) vs.template write_gate<S>(bf.G(r + 3));
+            if (has_v) vs.template write_v<S>(ROWS == 128 ? bf.Vw(r + 1) + 4096 * kVHalf : bf.V(r + 1));
+            if constexpr (kStageBeta) {
+                vs.template write_beta<S>(bf.B(r + 3));
+                if constexpr (GATED) vs.template write_gate<S>(bf.G(r + 3));
+            }
             if (has_v) vs.template load_v<S>(min(max(r + 3, 0), last));
-            vs.template load_beta<S>(min(r + 5, last));
+            if constexpr (kStageBeta) vs.template load_beta<S>(min(r + 5, last));
         }
         if constexpr (kOffSolve) {
             if (r + 1 >= 0 && r + 1 < NC) {
@@ -1079,8 +1091,14 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
 //   NW = 8,  ROWS = 32: waves 0-1 consumers; 2-7 kRoleGramDiag,
 //            kRoleGramOff, kRoleOffSolve, kRoleV, kRoleKQP0, kRoleKQP1 (the
 //            consumers share their SIMDs with the lightest producers)
+//   NW = 15, ROWS = 128 (context-parallel transitions, no output, no decay,
+//            dk = dv = 128): waves 0-7 consumers; 8-14 kRoleGramOff,
+//            kRoleGramDiag, kRoleOffSolve, kRoleV, kRoleK0, kRoleK1, kRoleV1.
+//            One tile covers all value rows of Q_g or all key rows of P_g,
+//            so the chunk's Gram tiles, inverses and T are formed once for
+//            128 state rows instead of once per 64
 // Twelve waves leave 168 registers per lane, too few for the consumers of
-// the decayed kernels, which keep the 8-wave layout.
+// the decayed kernels, which keep the 8-wave layout; fifteen leave 128.
 template <int DK, int DV, bool WO, bool GATED, int ROWS, int NW>
 __global__ __launch_bounds__(NW * 64) void chain_kernel_ws(const ChainArgs a) {
     using LY = WsLds<DK>;
@@ -1104,10 +1122,29 @@ __global__ __launch_bounds__(NW * 64) void chain_kernel_ws(const ChainArgs a) {
     }
     __syncthreads();
 
-    if constexpr (NW == 12) {
+    if constexpr (ROWS == 128) {
+        static_assert(NW == 15 && !WO && !GATED && DK == 128 && DV == 128, "128-row tiles");
+        if (wave < 8) {
+            consumer_loop<DK, DV, WO, GATED, ROWS>(a, wk, bf, NC, wave, lane, g, c16);
+        } else if (wave == 8) {
+            producer_loop<DK, DV, WO, GATED, kRoleGramOff, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 9) {
+            producer_loop<DK, DV, WO, GATED, kRoleGramDiag, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 10) {
+            producer_loop<DK, DV, WO, GATED, kRoleOffSolve, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 11) {
+            producer_loop<DK, DV, WO, GATED, kRoleV, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 12) {
+            producer_loop<DK, DV, WO, GATED, kRoleK0, ROWS>(a, wk, bf, NC, g, c16);
+        } else if (wave == 13) {
+            producer_loop<DK, DV, WO, GATED, kRoleK1, ROWS>(a, wk, bf, NC, g, c16);
+        } else {
+            producer_loop<DK, DV, WO, GATED, kRoleV1, ROWS>(a, wk, bf, NC, g, c16);
+        }
+    } else if constexpr (NW == 12) {
         static_assert(ROWS == 64, "tile rows");
         if (wave < 4) {
-            consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
+            consumer_loop<DK, DV, WO, GATED, ROWS>(a, wk, bf, NC, wave, lane, g, c16);
         } else if (wave == 4) {
             producer_loop<DK, DV, WO, GATED, kRoleOffSolve, ROWS>(a, wk, bf, NC, g, c16);
         } else if (wave == 5) {
@@ -1128,7 +1165,7 @@ __global__ __launch_bounds__(NW * 64) void chain_kernel_ws(const ChainArgs a) {
     } else if constexpr (ROWS == 64) {
         static_assert(NW == 8, "waves");
         if (wave < 4) {
-            consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
+            consumer_loop<DK, DV, WO, GATED, ROWS>(a, wk, bf, NC, wave, lane, g, c16);
         } else if (wave == 4) {
             producer_loop<DK, DV, WO, GATED, kRoleGram, ROWS>(a, wk, bf, NC, g, c16);
         } else if (wave == 5) {
@@ -1141,7 +1178,7 @@ __global__ __launch_bounds__(NW * 64) void chain_kernel_ws(const ChainArgs a) {
     } else {
         static_assert(ROWS == 32 && NW == 8, "tile rows");
         if (wave < 2) {
-            consumer_loop<DK, DV, WO, GATED>(a, wk, bf, NC, wave, lane, g, c16);
+            consumer_loop<DK, DV, WO, GATED, ROWS>(a, wk, bf, NC, wave, lane, g, c16);
         } else if (wave == 2) {
             producer_loop<DK, DV, WO, GATED, kRoleGramDiag, ROWS>(a, wk, bf, NC, g, c16);
         } else if (wave == 3) {
@@ -1557,6 +1594,14 @@ template <int DK, int DV> hipError_t launch_rev(const BwdArgs &a, hipStream_t s)
 template <int DK, int DV, bool WO> hipError_t launch_ws(const ChainArgs &a, hipStream_t s) {
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
+    if (a.rows == 128) { // context-parallel transitions, dk = dv = 128, no decay
+        if constexpr (!WO && DK == 128 && DV == 128) {
+            if (a.kind != kCpTransition || a.g || a.n_tiles != 2) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((chain_kernel_ws<DK, DV, false, false, 128, 15>), dim3(grid), dim3(960), 0, s, a);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     if (a.rows == 32) { // narrow tiles: forward with output, dense and packed kinds
         if constexpr (WO) {
             if ((a.kind != kDense && a.kind != kVarlen) || a.n_tiles != DV / 32) return hipErrorInvalidValue;

@@ -39,7 +39,8 @@ struct Work {
 };
 
 // ROWS: state rows per workgroup tile (64; 32 for the narrow forward tiles,
-// dense and packed kinds only).
+// dense and packed kinds only; 128 for context-parallel transitions at
+// dk = dv = 128).
 template <int DK, int DV, int ROWS = kRows> __device__ inline Work decode_work(const ChainArgs &a) {
     int u, tau;
     map_block(blockIdx.x, a.n_units, a.n_tiles, u, tau);
@@ -91,10 +92,10 @@ template <int DK, int DV, int ROWS = kRows> __device__ inline Work decode_work(c
                 wk.Sin = a.ws_S + (slot * DV + wk.row0) * DK;
             }
             if (gi == a.G - 1 && a.S_final) wk.Sout = a.S_final + ((int64_t)bh * DV + wk.row0) * DK;
-        } else if (tau < DV / kRows) {
+        } else if (tau < DV / ROWS) {
             wk.Sout = a.ws_Q + (slot * DV + wk.row0) * DK; // Q_g rows, from a zero start
         } else {
-            wk.row0 = (tau - DV / kRows) * kRows; // rows of P_g (dk index), from identity
+            wk.row0 = (tau - DV / ROWS) * ROWS; // rows of P_g (dk index), from identity
             wk.identity = true;
             wk.has_v = false;
             wk.transposed_out = true;
