@@ -817,11 +817,13 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
 //   S_{g+1} = S_g P_g + Q_g,  g = 0..G-2,  S_0 = S0 (or zero);
 // writes S_1..S_{G-1} to ws_S. fp32 throughout (fp32 matrix cores). Each
 // wave computes DK/64 of the DK/16 output column tiles; the 16 rows of S are
-// exchanged through LDS between steps.
+// exchanged through LDS between steps. The operands of step g + 1 (P_{g+1}
+// and Q_{g+1} do not depend on the chain) are loaded while step g computes.
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void compose_kernel(const ChainArgs a) {
     constexpr int LDS_ = DK + 4;
     constexpr int TPW = DK / 64;
+    constexpr int NK = DK / 16;
     __shared__ __attribute__((aligned(16))) float Sl[16 * LDS_];
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -831,25 +833,44 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(const ChainArgs a) {
         const int r = idx / DK, col = idx - r * DK;
         Sl[r * LDS_ + col] = a.S0 ? a.S0[((int64_t)bh * DV + 16 * rb + r) * DK + col] : 0.f;
     }
-    __syncthreads();
-    for (int gi = 0; gi + 1 < a.G; ++gi) {
+    // pa[t][kk] = P_g^T[16 mt + c16][16 kk + 4 g ..], qa[t] = Q_g[16 rb + c16][16 mt + 4 g ..]
+    f32x4 pa[TPW][NK], qa[TPW], pn[TPW][NK], qn[TPW];
+    auto load = [&](int gi, f32x4 (&p)[TPW][NK], f32x4 (&q)[TPW]) {
         const int64_t slot = (int64_t)bh * a.G + gi;
         const float *Pt = a.ws_P + slot * DK * DK;
         const float *Qg = a.ws_Q + (slot * DV + 16 * rb) * DK;
-        f32x4 acc[TPW];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int mt = w * TPW + t;
-            acc[t] = *reinterpret_cast<const f32x4 *>(Qg + c16 * DK + 16 * mt + 4 * g);
+            q[t] = *reinterpret_cast<const f32x4 *>(Qg + c16 * DK + 16 * mt + 4 * g);
 #pragma unroll
-            for (int kk = 0; kk < DK / 16; ++kk) {
-                const f32x4 pa = *reinterpret_cast<const f32x4 *>(Pt + (16 * mt + c16) * DK + 16 * kk + 4 * g);
+            for (int kk = 0; kk < NK; ++kk)
+                p[t][kk] = *reinterpret_cast<const f32x4 *>(Pt + (16 * mt + c16) * DK + 16 * kk + 4 * g);
+        }
+    };
+    if (a.G > 1) load(0, pn, qn);
+    __syncthreads();
+    for (int gi = 0; gi + 1 < a.G; ++gi) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            qa[t] = qn[t];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) pa[t][kk] = pn[t][kk];
+        }
+        if (gi + 2 < a.G) load(gi + 1, pn, qn);
+        f32x4 acc[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            acc[t] = qa[t];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
                 const f32x4 sb = *reinterpret_cast<const f32x4 *>(Sl + c16 * LDS_ + 16 * kk + 4 * g);
-                acc[t] = Tr<float>::mma16(acc[t], pa, sb);
+                acc[t] = Tr<float>::mma16(acc[t], pa[t][kk], sb);
             }
         }
         // acc[t][i] = S_{g+1}[row 16rb + c16][16mt + 4g + i]
         __syncthreads();
+        const int64_t slot = (int64_t)bh * a.G + gi;
         float *Sn = a.ws_S + ((slot + 1) * DV + 16 * rb) * DK;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
