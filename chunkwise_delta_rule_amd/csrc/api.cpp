@@ -212,12 +212,13 @@ size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
 
 // Workspace bytes per chunk slot of the backward pass. DeltaNet: the state
 // entering the chunk and the gradient of the state leaving it (bf16), then
-// T^T of the chunk (bf16). The gated passes: the state entering the chunk and
-// the per-value-tile partial sums (fp32), then T^T of the chunk (bf16).
+// T^T of the chunk (bf16). The gated passes: the state entering the chunk
+// (bf16) and the per-value-tile partial sums (bf16 sums, fp32 per-token
+// extras), then T^T of the chunk (bf16).
 size_t bwd_slot_bytes(int dk, int dv, bool gated) {
     const size_t tt = (size_t)dn::kChunk * dn::kChunk * sizeof(__bf16);
     if (!gated) return 2 * (size_t)dv * dk * sizeof(__bf16) + tt;
-    return ((size_t)dv * dk + (size_t)(dv / dn::kRows) * dn::bwd_part_stride(dk, true)) * sizeof(float) + tt;
+    return (size_t)dv * dk * sizeof(__bf16) + (size_t)(dv / dn::kRows) * dn::bwd_part_bytes(dk) + tt;
 }
 
 // Chunk slots of a packed batch, bounded without reading the lengths:
@@ -265,12 +266,12 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     const size_t slots = varlen ? varlen_max_slots(B, T, H) : (size_t)B * H * NC;
     if (slots > (size_t)INT32_MAX) return DN_ERR_UNSUPPORTED; // one finishing workgroup per chunk slot
     const bool gated = g != nullptr;
-    float *Sck = nullptr, *part = nullptr;
+    unsigned char *part = nullptr;
     __bf16 *S16 = nullptr, *G16 = nullptr, *Tck;
     if (gated) {
-        Sck = static_cast<float *>(workspace);
-        part = Sck + slots * dv * dk;
-        Tck = reinterpret_cast<__bf16 *>(part + slots * (dv / dn::kRows) * dn::bwd_part_stride(dk, true));
+        S16 = static_cast<__bf16 *>(workspace);
+        part = reinterpret_cast<unsigned char *>(S16 + slots * dv * dk);
+        Tck = reinterpret_cast<__bf16 *>(part + slots * (dv / dn::kRows) * dn::bwd_part_bytes(dk));
     } else {
         S16 = static_cast<__bf16 *>(workspace);
         G16 = S16 + slots * dv * dk;
@@ -286,7 +287,6 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     a.beta = beta;
     a.g = g;
     a.S0 = S0;
-    a.S_chunks = Sck;
     a.S_chunks16 = S16;
     a.T_chunks = Tck;
     a.chunk_base = cb;
@@ -310,7 +310,6 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     b.beta = beta;
     b.dO = dO;
     b.dS_final = dS_final;
-    b.S_chunks = Sck;
     b.S_chunks16 = S16;
     b.G_chunks = G16;
     b.T_chunks = Tck;

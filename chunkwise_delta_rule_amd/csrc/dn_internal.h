@@ -74,16 +74,16 @@ struct DecodeArgs {
 hipError_t launch_kda(int dk, int dv, bool write_o, const ChainArgs &a, hipStream_t stream);
 
 // Backward pass (bf16): gradients of q, k, v, beta and S0 for upstream dO and
-// dS_final, from the per-chunk states S_chunks of a forward pass.
+// dS_final, from the per-chunk states S_chunks16 of a forward pass.
 struct BwdArgs {
     const void *q, *k, *v, *beta, *dO;
     const float *dS_final; // [B*H][dv][dk] or nullptr (zero)
-    const float *S_chunks; // [B*H][NC][dv][dk]: the state entering each chunk
     const __bf16 *T_chunks; // [B*H][NC][64][64]: T^T of each chunk (the forward's), row-major
-    const __bf16 *S_chunks16; // reverse-chain pipeline: the entering states in bf16 [slot][dv][dk]
+    const __bf16 *S_chunks16; // the state entering each chunk in bf16 [slot][dv][dk]
     __bf16 *G_chunks;         // reverse-chain pipeline: dS' of each chunk (the gradient of the
                               // state after it) in bf16 [slot][dv][dk]
-    float *part;           // [n_tiles][max_slots] blocks of per-tile partial sums
+    unsigned char *part;   // gated: [n_tiles][max_slots] blocks of per-tile partial sums
+                           // (bwd_part_bytes each)
     float *dS0;            // [B*H][dv][dk] or nullptr
     void *dq, *dk, *dv, *dbeta;
     const float *g; // Gated DeltaNet: log decays [tokens][H] (layout of beta), or nullptr
@@ -100,11 +100,14 @@ struct BwdArgs {
 };
 // Chunk slots before each packed sequence: cb[n] = sum_{m < n} ceil(L_m / 64), cb[N] the total.
 hipError_t launch_chunk_base(const int32_t *cu_seqlens, int N, int32_t *cb, hipStream_t stream);
-// Floats of one partial block: dP, dT (64 x 64 each), dQ, dK (64 x dk each).
-constexpr size_t bwd_part_floats(int dk) { return 2 * 64 * 64 + 2 * 64 * (size_t)dk; }
-// Gated: per token k . (row-scaled Z dS') and k . (row-scaled dY S), and per
-// wave exp(gamma_C) <dS', S>, after those blocks (padded to 256 floats).
-constexpr size_t bwd_part_stride(int dk, bool gated) { return bwd_part_floats(dk) + (gated ? 256 : 0); }
+// Elements of the bf16 sums of one partial block: dP, dT (64 x 64 each), dQ,
+// dK (64 x dk each), each summed in fp32 over the tile's 64 values and
+// rounded once.
+constexpr size_t bwd_part_elems(int dk) { return 2 * 64 * 64 + 2 * 64 * (size_t)dk; }
+// Bytes of one partial block: those sums, then in fp32 per token
+// k . (row-scaled Z dS') and k . (row-scaled dY S), and per wave
+// exp(gamma_C) <dS', S> (padded to 256 floats).
+constexpr size_t bwd_part_bytes(int dk) { return bwd_part_elems(dk) * 2 + 256 * 4; }
 // The gated backward passes (a.g set): the reverse chain with per-value-tile
 // partial sums into a.part, then one finishing workgroup per chunk slot.
 hipError_t launch_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream);

@@ -1021,7 +1021,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     E *dVg = reinterpret_cast<E *>(a.dv) + tok0 * sv + (int64_t)h * DV + row0;
 
     // dS rows 16w + c16 of this tile: dSacc[m][i] = dS[row0 + 16w + c16][16m + 4g + i]
-    f32x4 dSacc[NMT], Sacc[NMT];
+    // Sraw: the bf16 state entering the chunk, kept as loaded (the load is not
+    // waited for until the chunk's first use of it)
+    f32x4 dSacc[NMT];
+    bf16x4 Sraw[NMT];
 #pragma unroll
     for (int m = 0; m < NMT; ++m)
         dSacc[m] = a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + (su * DV + row0 + 16 * w + c16) * DK +
@@ -1053,9 +1056,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
                 dov[p] = *reinterpret_cast<const typename TR::V *>(dOg + x * sv + 8 * cv);
             }
         }
-        const float *Sr = a.S_chunks + ((slot0 + c) * DV + row0 + 16 * w + c16) * DK + 4 * g;
+        const E *Sr = a.S_chunks16 + ((slot0 + c) * DV + row0 + 16 * w + c16) * DK + 4 * g;
 #pragma unroll
-        for (int m = 0; m < NMT; ++m) Sacc[m] = *reinterpret_cast<const f32x4 *>(Sr + 16 * m);
+        for (int m = 0; m < NMT; ++m) Sraw[m] = *reinterpret_cast<const bf16x4 *>(Sr + 16 * m);
     };
     if (NC > 0) load_chunk(NC - 1);
     for (int r = NC - 1; r >= 0; --r) {
@@ -1078,13 +1081,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         float sdot = 0.f; // gated: this lane's share of <dS', S>
 #pragma unroll
         for (int m = 0; m < NMT; ++m) {
-            stf(Ss + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(Sacc[m]));
+            const f32x4 Sm = widen_bf16(Sraw[m]);
+            stf(Ss + (16 * w + c16) * L::K + 16 * m + 4 * g, Sraw[m]);
             stf(Rs + (16 * w + c16) * L::K + 16 * m + 4 * g, TR::cvt(dSacc[m])); // dS after the chunk
-            SBn[m] = TR::cvt(-Sacc[m]);
+            SBn[m] = -Sraw[m];
             dSB[m] = TR::cvt(dSacc[m]);
             if constexpr (GATED)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sdot += dSacc[m][i] * Sacc[m][i];
+                for (int i = 0; i < 4; ++i) sdot += dSacc[m][i] * Sm[i];
         }
         __syncthreads();
         if (r > 0) load_chunk(r - 1);
@@ -1229,7 +1233,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         // stored in accumulator order: one 16-byte piece per (wave, column
         // block, lane), so every store (and the finishing kernel's load) of a
         // wave moves 1 KB of contiguous memory.
-        float *pb = a.part + ((int64_t)tau * a.max_slots + slot0 + r) * bwd_part_stride(DK, GATED);
+        E *pb = reinterpret_cast<E *>(a.part + ((int64_t)tau * a.max_slots + slot0 + r) * bwd_part_bytes(DK));
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
             if (s2 > w) break; // dP and dT are lower-inclusive: tiles right of the diagonal are zero
@@ -1241,8 +1245,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
                 dt = TR::mma32(dt, ldrow(dZs, LT, 16 * w + c16, 16 * kv, g), ldrow(dZs, LT, 16 * w + c16, 16 * kv + 16, g),
                                ldrow(Ys, LT, 16 * s2 + c16, 16 * kv, g), ldrow(Ys, LT, 16 * s2 + c16, 16 * kv + 16, g));
             }
-            *reinterpret_cast<f32x4 *>(pb + ((w * 4 + s2) * 64 + lane) * 4) = dp;
-            *reinterpret_cast<f32x4 *>(pb + 4096 + ((w * 4 + s2) * 64 + lane) * 4) = dt;
+            *reinterpret_cast<bf16x4 *>(pb + ((w * 4 + s2) * 64 + lane) * 4) = TR::cvt(dp);
+            *reinterpret_cast<bf16x4 *>(pb + 4096 + ((w * 4 + s2) * 64 + lane) * 4) = TR::cvt(dt);
         }
         // gated: k . a and k . b per token (a = the Z dS' rows scaled by
         // exp(gamma_C - gamma), b = the dY S rows scaled by exp(gamma))
@@ -1275,11 +1279,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
                     skb[i] += kk * dk2[i];
                 }
             }
-            *reinterpret_cast<f32x4 *>(pb + 8192 + ((w * NMT + m) * 64 + lane) * 4) = dq;
-            *reinterpret_cast<f32x4 *>(pb + 8192 + 64 * DK + ((w * NMT + m) * 64 + lane) * 4) = dk1 - dk2;
+            *reinterpret_cast<bf16x4 *>(pb + 8192 + ((w * NMT + m) * 64 + lane) * 4) = TR::cvt(dq);
+            *reinterpret_cast<bf16x4 *>(pb + 8192 + 64 * DK + ((w * NMT + m) * 64 + lane) * 4) = TR::cvt(dk1 - dk2);
         }
         if constexpr (GATED) {
-            float *px = pb + bwd_part_floats(DK);
+            float *px = reinterpret_cast<float *>(pb + bwd_part_elems(DK));
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1403,11 +1407,13 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
     // order): dP, dT (lower-inclusive, to LDS) and dQ, dK (this wave's token
     // rows, in registers). Every load is issued before the first use.
     constexpr int NT = DV / 64;
-    const size_t PB = bwd_part_stride(DK, GATED);
-    const float *pbt[NT];
+    const E *pbt[NT];
 #pragma unroll
-    for (int tau = 0; tau < NT; ++tau) pbt[tau] = a.part + ((int64_t)tau * a.max_slots + s) * PB;
-    auto ld4 = [&](int tau, int off) { return *reinterpret_cast<const f32x4 *>(pbt[tau] + off + lane * 4); };
+    for (int tau = 0; tau < NT; ++tau)
+        pbt[tau] = reinterpret_cast<const E *>(a.part + ((int64_t)tau * a.max_slots + s) * bwd_part_bytes(DK));
+    auto ld4 = [&](int tau, int off) {
+        return widen_bf16(*reinterpret_cast<const bf16x4 *>(pbt[tau] + off + lane * 4));
+    };
     f32x4 pp[4], tt[4], dQa[NMT], dKa[NMT];
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) { // tiles right of the diagonal are neither stored nor loaded
@@ -1441,7 +1447,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(const BwdArgs a) {
         if (w == 0) {
 #pragma unroll
             for (int tau = 0; tau < NT; ++tau) {
-                const float *px = pbt[tau] + bwd_part_floats(DK);
+                const float *px = reinterpret_cast<const float *>(pbt[tau] + bwd_part_elems(DK));
                 xa += px[lane];
                 xb += px[64 + lane];
                 xs += lane < 4 ? px[128 + lane] : 0.f;

@@ -302,8 +302,10 @@ size_t deltanet_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, in
  * (gamma: in-chunk prefix sums of g), so g should be <= 0 (decay) as in the
  * forward; dg is the in-chunk suffix sum of the gradients of those prefix
  * sums. Workspace: at least deltanet_gated_bwd_workspace_bytes(...) bytes,
- * 16-byte aligned. Errors as in deltanet_bwd; g or dg NULL with tokens
- * present: DN_ERR_INVALID.
+ * 16-byte aligned: per chunk, the state entering it (bf16), per 64 value rows
+ * the chunk's sums over those rows (bf16, with fp32 per-token decay terms),
+ * and its T. Errors as in deltanet_bwd; g or dg NULL with tokens present:
+ * DN_ERR_INVALID.
  */
 int deltanet_gated_bwd(const void *q, const void *k, const void *v, const void *beta,
                        const float *g, const float *S0, const void *dO, const float *dS_final,

@@ -175,9 +175,9 @@ hipError_t launch_bwd(int dk, int dv, const BwdArgs &b, hipStream_t) {
         rd(b.chunk_base, (size_t)(b.B + 1) * 4);
         rd(b.seq_order, b.seq_order ? (size_t)b.B * 4 : 0);
     }
-    rd(b.S_chunks, slots * dv * dk * 4);
+    rd(b.S_chunks16, slots * dv * dk * 2);
     rd(b.T_chunks, slots * kChunk * kChunk * 2);
-    wr(b.part, (size_t)b.n_tiles * slots * bwd_part_stride(dk, b.g != nullptr) * 4);
+    wr(b.part, (size_t)b.n_tiles * slots * bwd_part_bytes(dk));
     wr(b.dq, real * b.H * dk * 2);
     wr(b.dk, steps * b.H * dk * 2);
     wr(b.dv, steps * b.H * dv * 2);

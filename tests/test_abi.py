@@ -241,11 +241,11 @@ def test_gated_bwd_rejects_bad_arguments(lib, kw, status):
 def test_bwd_workspace_sizes(lib):
     # per chunk slot, DeltaNet: the state entering the chunk and the gradient of
     # the state leaving it (bf16 each), then T^T (64 x 64 bf16); gated: the state
-    # entering the chunk (fp32), per value tile dP, dT (64 x 64), dQ, dK (64 x dk)
-    # and 256 floats of decay terms (fp32), then T^T
+    # entering the chunk (bf16), per value tile dP, dT (64 x 64), dQ, dK (64 x dk)
+    # (bf16) and 256 floats of decay terms (fp32), then T^T
     for dk, dv in [(128, 128), (64, 64), (64, 128), (128, 64)]:
         plain = 2 * dv * dk * 2 + 64 * 64 * 2
-        gated = (dv * dk + (dv // 64) * (2 * 64 * 64 + 2 * 64 * dk + 256)) * 4 + 64 * 64 * 2
+        gated = dv * dk * 2 + (dv // 64) * ((2 * 64 * 64 + 2 * 64 * dk) * 2 + 256 * 4) + 64 * 64 * 2
         slots = 2 * 3 * 4  # B = 2, H = 3, T = 200 -> 4 chunks
         assert lib.deltanet_bwd_workspace_bytes(2, 3, 200, dk, dv, 64) == slots * plain
         assert lib.deltanet_gated_bwd_workspace_bytes(2, 3, 200, dk, dv, 64) == slots * gated
