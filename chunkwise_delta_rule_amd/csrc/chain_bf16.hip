@@ -679,14 +679,7 @@ __device__ void consumer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
     const SubstepBase sb = GATED ? substep_base(wk.tok0, a.nh) : SubstepBase{0, 0u, 1u};
     __syncthreads(); // matches the producers' prologue
     for (int r = -3; r < NC; ++r) {
-        // the state entering chunk r, for the backward pass (never for 128-row tiles)
-        if (!WO && ROWS != 128 && r >= 0 && wk.Schunks) {
-            Work ck = wk;
-            ck.Sout = wk.Schunks + (int64_t)r * DV * DK;
-            ck.transposed_out = false;
-            ws_state_out<DK>(Sacc, ck, cw, g, c16);
-        }
-        if (!WO && ROWS != 128 && r >= 0 && wk.Schunks16) { // the same in bf16 ([dv][dk] rows)
+        if (!WO && ROWS != 128 && r >= 0 && wk.Schunks16) { // the state entering chunk r, for the backward pass
             __bf16 *so = wk.Schunks16 + (int64_t)r * DV * DK + (16 * cw + c16) * DK;
 #pragma unroll
             for (int m = 0; m < DK / 16; ++m) st4(so + dk_of(m, g), cvt4(Sacc[m]));

@@ -27,13 +27,12 @@ struct ChainArgs {
     void *o;
     const float *S0;
     float *S_final;
-    float *S_chunks; // dense kind only, or nullptr: the state entering every chunk,
-                     // [B*H][chunks][dv][dk] fp32 (kept for the backward pass)
-    __bf16 *S_chunks16; // bf16 DeltaNet without output, or nullptr: the same in bf16,
-                        // at the chunk slots of S_chunks (dense: u NC + c; varlen: chunk_base)
-    __bf16 *T_chunks; // with S_chunks (bf16 DeltaNet without output), or nullptr: T^T of
+    __bf16 *S_chunks16; // forward without output for the backward pass, or nullptr: the
+                        // state entering every chunk, [slot][dv][dk] bf16 (dense: slot
+                        // u NC + c; varlen: chunk_base)
+    __bf16 *T_chunks; // with S_chunks16, or nullptr: T^T of
                       // every chunk, [B*H][chunks][64][64] bf16 row-major (backward pass)
-    const int32_t *chunk_base; // varlen with S_chunks: chunks before each sequence, [N + 1];
+    const int32_t *chunk_base; // varlen with S_chunks16: chunks before each sequence, [N + 1];
                                // unit (n, h) owns chunk slots chunk_base[n] H + h NC_n + c
     const int32_t *cu_seqlens;
     const int32_t *seq_order;

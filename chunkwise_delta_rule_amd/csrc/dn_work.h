@@ -30,8 +30,7 @@ struct Work {
     int64_t tok0;
     int len, h, row0;
     int unit;         // index of the (sequence, head) unit
-    float *Schunks;   // rows of the state entering chunk 0 of this unit (dense kind), or nullptr
-    __bf16 *Schunks16; // the same rows in bf16 (backward pass, reverse-chain pipeline), or nullptr
+    __bf16 *Schunks16; // rows of the state entering chunk 0 of this unit in bf16 (backward pass), or nullptr
     const float *Sin; // initial rows, or nullptr (zero / identity)
     float *Sout;      // final rows, or nullptr
     bool identity, transposed_out, has_v;
@@ -45,14 +44,12 @@ template <int DK, int DV, int ROWS = kRows> __device__ inline Work decode_work(c
     int u, tau;
     map_block(blockIdx.x, a.n_units, a.n_tiles, u, tau);
     const int H = a.H;
-    Work wk = {0, 0, 0, tau * ROWS, u, nullptr, nullptr, nullptr, nullptr, false, false, true, nullptr};
+    Work wk = {0, 0, 0, tau * ROWS, u, nullptr, nullptr, nullptr, false, false, true, nullptr};
     if (a.kind == kDense) {
         const int b = u / H;
         wk.h = u - b * H;
         wk.tok0 = (int64_t)b * a.T;
         wk.len = a.T;
-        if (a.S_chunks)
-            wk.Schunks = a.S_chunks + ((int64_t)u * ((a.T + kChunk - 1) / kChunk) * DV + wk.row0) * DK;
         if (a.S_chunks16)
             wk.Schunks16 = a.S_chunks16 + ((int64_t)u * ((a.T + kChunk - 1) / kChunk) * DV + wk.row0) * DK;
         if (a.T_chunks && tau == 0)
@@ -68,10 +65,9 @@ template <int DK, int DV, int ROWS = kRows> __device__ inline Work decode_work(c
         const int64_t su = (int64_t)n * H + wk.h;
         if (a.S0) wk.Sin = a.S0 + (su * DV + wk.row0) * DK;
         if (a.S_final) wk.Sout = a.S_final + (su * DV + wk.row0) * DK;
-        if (a.S_chunks || a.S_chunks16) { // the chunk slots of this unit, contiguous
+        if (a.S_chunks16) { // the chunk slots of this unit, contiguous
             const int64_t slot0 = (int64_t)a.chunk_base[n] * H + (int64_t)wk.h * ((wk.len + kChunk - 1) / kChunk);
-            if (a.S_chunks) wk.Schunks = a.S_chunks + (slot0 * DV + wk.row0) * DK;
-            if (a.S_chunks16) wk.Schunks16 = a.S_chunks16 + (slot0 * DV + wk.row0) * DK;
+            wk.Schunks16 = a.S_chunks16 + (slot0 * DV + wk.row0) * DK;
             if (a.T_chunks && tau == 0) wk.Tchunks = a.T_chunks + slot0 * kChunk * kChunk;
         }
     } else {

@@ -66,11 +66,10 @@ void chain_common(int dtype, int dk, int dv, bool write_o, const dn::ChainArgs &
     rd(a.S0, a.S0 ? units * dv * dk * 4 : 0);
     if (write_o) wr(a.o, real * a.H * dv * e);
     wr(a.S_final, a.S_final ? units * dv * dk * 4 : 0);
-    if (a.S_chunks || a.S_chunks16) {
+    if (a.S_chunks16) {
         const size_t slots = a.kind == dn::kVarlen ? varlen_slots(a)
                                                    : units * (((size_t)a.T + dn::kChunk - 1) / dn::kChunk);
-        wr(a.S_chunks, a.S_chunks ? slots * dv * dk * 4 : 0);
-        wr(a.S_chunks16, a.S_chunks16 ? slots * dv * dk * 2 : 0);
+        wr(a.S_chunks16, slots * dv * dk * 2);
         wr(a.T_chunks, a.T_chunks ? slots * dn::kChunk * dn::kChunk * 2 : 0);
     }
 }
