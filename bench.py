@@ -19,7 +19,9 @@ workload is reported under ``variants.gated`` next to the headline figures.
 per-chunk states, reverse state-gradient chain, chunk-parallel finish) on the
 same workload. ``variants.kda`` times ``deltanet_kda_fwd`` (per-channel decay) on the same
 workload. ``variants.gdp`` times ``deltanet_gdp_fwd`` (Gated Delta Product, n_h = 2 substeps
-per token) on the same B, H, T and widths. ``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
+per token) on the same B, H, T and widths. ``variants.kda_long`` and
+``variants.gated_long`` time KDA and Gated DeltaNet on B=1 H=16 T=131072,
+serial chain against context parallelism. ``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
 head, state updated in place) on B=256 H=16 d=128 bf16, a 256 MiB state.
 The other four workloads of the forward pass are timed by the same clock under
 ``variants.<workload>``: B=4 H=16 T=8192 (serial chain and the library's
@@ -294,6 +296,34 @@ def kda_long_variant(dev, B=1, H=16, T=131072, d=128, steps=5, warmup=2):
     return out
 
 
+def gated_long_variant(dev, B=1, H=16, T=131072, d=128, steps=5, warmup=2):
+    """Time deltanet_gated_fwd on one long sequence per head (the long-context
+    shape), serial chain against context parallelism at the library's group
+    count; bytes: q, k, v, beta, o in bf16 and g in fp32 per head-token."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import make_gates, make_inputs
+
+    print(f"[bench] gated long-context variant B={B} H={H} T={T}", file=sys.stderr, flush=True)
+    q, k, v, beta, S0 = make_inputs(B, H, T, d, d, seed=12, device=str(dev))
+    g = make_gates((B, T, H), seed=12, device=str(dev))
+    o = torch.empty_like(v)
+    Sf = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    G = dn.deltanet_pick_cp_groups(B, H, T, d, d, 64)
+    ws = torch.empty(max(dn.deltanet_workspace_bytes(B, H, T, d, d, 64, G), 1), dtype=torch.uint8, device=dev)
+    out = {"call": "deltanet_gated_fwd", "config": {"B": B, "H": H, "T": T, "dk": d, "dv": d}, "steps": steps,
+           "warmup": warmup}
+    nbytes = B * T * H * (2 * (4 * d + 1) + 4) + B * H * d * d * 4
+    for name, groups in (("serial", 1), ("context_parallel", G)):
+        ms, _, _ = time_steps(lambda: dn.deltanet_gated_fwd(q, k, v, beta, g, S0, o=o, S_final=Sf,
+                                                            cp_groups=groups, workspace=ws), warmup, steps)
+        out[name] = {"cp_groups": groups, "ms_per_step": round(ms, 4),
+                     "tokens_per_s": round(B * T / (ms / 1e3), 1),
+                     "hbm_frac": round(nbytes / (ms / 1e3) / PEAK_HBM_BPS, 4)}
+    out["speedup"] = round(out["serial"]["ms_per_step"] / out["context_parallel"]["ms_per_step"], 3)
+    return out
+
+
 def gdp_variant(dev, w, flops_per_head_step, peak_flops, nh=2, steps=20, warmup=5):
     """Time deltanet_gdp_fwd with nh substeps per token on the workload's B, H,
     T (real tokens) and widths: the chunkwise path runs over T nh virtual
@@ -479,7 +509,7 @@ def main():
                     help="measure Gated DeltaNet (per-token log decays) instead of DeltaNet")
     ap.add_argument("--variants", default="all",
                     help="comma-separated variants to run after the main line (gated, bwd, gated_bwd, gdp, gdp_bwd, "
-                         "kda, kda_long, workloads, decode), or all")
+                         "kda, kda_long, gated_long, workloads, decode), or all")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the short gated and decode runs reported under variants")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -620,7 +650,8 @@ def main():
             "hbm_frac": round(g_bytes / (g_launch_ms / 1e3) / PEAK_HBM_BPS, 4),
             "mfma_frac": round(flops / (g_launch_ms / 1e3) / peak_flops, 4),
             "vs_ungated_time": round(g_launch_ms / avg_launch_ms, 4)}
-    if not w.varlen and w.dtype == "bf16" and any(map(want, ("bwd", "gated_bwd", "gdp", "gdp_bwd", "kda", "kda_long"))):
+    if not w.varlen and w.dtype == "bf16" and any(map(want, ("bwd", "gated_bwd", "gdp", "gdp_bwd", "kda", "kda_long",
+                                                               "gated_long"))):
         var = result.setdefault("variants", {})
         if want("bwd"):
             var["bwd"] = bwd_variant(dev, w, inputs, avg_launch_ms)
@@ -634,6 +665,8 @@ def main():
             var["kda"] = kda_variant(dev, w, inputs, avg_launch_ms)
         if want("kda_long"):
             var["kda_long"] = kda_long_variant(dev)
+        if want("gated_long"):
+            var["gated_long"] = gated_long_variant(dev)
     if want("workloads") and w.name == "layer_b8_h16_t4096":
         # the other workloads of the forward pass, each timed by the same clock
         result.setdefault("variants", {})

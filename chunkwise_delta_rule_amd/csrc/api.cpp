@@ -144,7 +144,7 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
     // inverses and T formed once per 128 state rows); else 64-row tiles
     a.kind = dn::kCpTransition;
     a.n_units = B * H * (G - 1);
-    a.rows = (dtype == DN_BF16 && !g && dk == 128 && dv == 128) ? 128 : dn::kRows;
+    a.rows = (dtype == DN_BF16 && dk == 128 && dv == 128) ? 128 : dn::kRows;
     a.n_tiles = dv / a.rows + dk / a.rows;
     err = dn::launch_chain(dtype, dk, dv, false, a, stream);
     if (err != hipSuccess) return DN_ERR_HIP;

@@ -550,7 +550,7 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
                                       int nval, const SubstepBase &sb, bool has_v, int cw, int lane, int g,
                                       int c16) {
     using CS = ChainSteps<DK, WO>;
-    constexpr int D = ROWS == 128 ? 4 : CS::depth; // 128-row tiles: 128 registers per lane
+    constexpr int D = ROWS == 128 ? (GATED ? 3 : 4) : CS::depth; // 128-row tiles: 128 registers per lane
     const ChainSrc<DK, WO> src{bf.K(r), WO ? bf.Q(r) : nullptr, bf.Tt(r), WO ? bf.P(r) : nullptr};
     bf16x8 SB[CS::NKB], YB[2], ZB[2], ZS[2], buf[D];
     f32x4 Y[4], Z[4], O[4];
@@ -575,17 +575,23 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
     // eg[t][e] = exp(gamma) and ez[t][e] = exp(gamma_C - gamma) of token
     // 16t + 4g + e (rows of Y and Z), eq[t] = exp(gamma) of token 16t + c
     // (columns of O), eC = exp(gamma_C).
+    // 128-row tiles (128 registers per lane) keep only the prefix sums gq[t]
+    // and form eg and ez where they are used.
+    constexpr bool kLazy = ROWS == 128;
     f32x4 eg[4], ez[4];
-    float eq[4], eC = 1.f;
+    float eq[4], gqv[4], gC = 0.f, eC = 1.f;
     if constexpr (GATED) {
         const float *Gs = bf.G(r);
-        const float gC = Gs[kChunk - 1];
+        gC = Gs[kChunk - 1];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const float gq = Gs[16 * t + 4 * g + (c16 & 3)];
-            eg[t] = quad_spread(__builtin_amdgcn_exp2f(gq));
-            ez[t] = quad_spread(__builtin_amdgcn_exp2f(gC - gq));
-            eq[t] = __builtin_amdgcn_exp2f(Gs[16 * t + c16]);
+            gqv[t] = gq;
+            if constexpr (!kLazy) {
+                eg[t] = quad_spread(__builtin_amdgcn_exp2f(gq));
+                ez[t] = quad_spread(__builtin_amdgcn_exp2f(gC - gq));
+            }
+            if constexpr (WO) eq[t] = __builtin_amdgcn_exp2f(Gs[16 * t + c16]);
         }
         eC = __builtin_amdgcn_exp2f(gC);
     }
@@ -615,6 +621,10 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
         const bf16x8 f = buf[i % D];
         if constexpr (i + D < CS::n) buf[i % D] = chain_fetch<DK, WO>(i + D, src, lane, g, c16);
         if constexpr (i == CS::bZ) {
+            if constexpr (GATED && kLazy) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) eg[t] = quad_spread(__builtin_amdgcn_exp2f(gqv[t]));
+            }
 #pragma unroll
             for (int t = 0; t < 4; ++t) Y[t] = GATED ? widen4(vf[t]) + eg[t] * Y[t] : widen4(vf[t]) + Y[t];
             YB[0] = cvt8(Y[0], Y[1]);
@@ -624,6 +634,10 @@ __device__ inline void consumer_chain(const WsBufs<DK> &bf, int r, f32x4 (&Sacc)
             ZB[0] = cvt8(Z[0], Z[1]);
             ZB[1] = cvt8(Z[2], Z[3]);
             if constexpr (GATED) { // rows of Z scaled by exp(gamma_C - gamma_l) for the update
+                if constexpr (kLazy) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) ez[t] = quad_spread(__builtin_amdgcn_exp2f(gC - gqv[t]));
+                }
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     ZS[s] = cvt8(Z[2 * s] * ez[2 * s], Z[2 * s + 1] * ez[2 * s + 1]);
@@ -1084,7 +1098,7 @@ __device__ void producer_loop(const ChainArgs &a, const Work &wk, const WsBufs<D
 //   NW = 8,  ROWS = 32: waves 0-1 consumers; 2-7 kRoleGramDiag,
 //            kRoleGramOff, kRoleOffSolve, kRoleV, kRoleKQP0, kRoleKQP1 (the
 //            consumers share their SIMDs with the lightest producers)
-//   NW = 15, ROWS = 128 (context-parallel transitions, no output, no decay,
+//   NW = 15, ROWS = 128 (context-parallel transitions, no output,
 //            dk = dv = 128): waves 0-7 consumers; 8-14 kRoleGramOff,
 //            kRoleGramDiag, kRoleOffSolve, kRoleV, kRoleK0, kRoleK1, kRoleV1.
 //            One tile covers all value rows of Q_g or all key rows of P_g,
@@ -1116,7 +1130,7 @@ __global__ __launch_bounds__(NW * 64) void chain_kernel_ws(const ChainArgs a) {
     __syncthreads();
 
     if constexpr (ROWS == 128) {
-        static_assert(NW == 15 && !WO && !GATED && DK == 128 && DV == 128, "128-row tiles");
+        static_assert(NW == 15 && !WO && DK == 128 && DV == 128, "128-row tiles");
         if (wave < 8) {
             consumer_loop<DK, DV, WO, GATED, ROWS>(a, wk, bf, NC, wave, lane, g, c16);
         } else if (wave == 8) {
@@ -1589,8 +1603,11 @@ template <int DK, int DV, bool WO> hipError_t launch_ws(const ChainArgs &a, hipS
     if (grid <= 0) return hipSuccess;
     if (a.rows == 128) { // context-parallel transitions, dk = dv = 128, no decay
         if constexpr (!WO && DK == 128 && DV == 128) {
-            if (a.kind != kCpTransition || a.g || a.n_tiles != 2) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((chain_kernel_ws<DK, DV, false, false, 128, 15>), dim3(grid), dim3(960), 0, s, a);
+            if (a.kind != kCpTransition || a.n_tiles != 2) return hipErrorInvalidValue;
+            if (a.g)
+                hipLaunchKernelGGL((chain_kernel_ws<DK, DV, false, true, 128, 15>), dim3(grid), dim3(960), 0, s, a);
+            else
+                hipLaunchKernelGGL((chain_kernel_ws<DK, DV, false, false, 128, 15>), dim3(grid), dim3(960), 0, s, a);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;

@@ -102,6 +102,12 @@ def test_gated_context_parallel_groups(G):
     assert_close(*run_gated(1, 2, 7 * 64 + 20, 128, 128, seed=120 + G, s0_std=0.3, cp_groups=G))
 
 
+@pytest.mark.parametrize("mu", [-1.0, 5.0])
+def test_gated_context_parallel_decay_strength(mu):
+    # strong (mu = -1) and weak decay through the 128-row transitions, 3 units of 5 groups
+    assert_close(*run_gated(1, 3, 9 * 64 + 7, 128, 128, seed=130, s0_std=0.3, cp_groups=5, mu=mu))
+
+
 def test_gated_context_parallel_fp32():
     assert_close(*run_gated(1, 1, 6 * 64 + 9, 64, 64, dtype="f32", seed=125, s0_std=0.3, cp_groups=3))
 

@@ -36,6 +36,7 @@ def gdp_inputs(B, H, T, nh, dk, dv, dtype, seed, s0_std=0.0):
     ("bf16", 128, 128, 2, 150, 1),
     ("bf16", 64, 128, 3, 77, 1),
     ("bf16", 128, 64, 2, 200, 3),
+    ("bf16", 128, 128, 2, 300, 3),
     ("f32", 64, 64, 2, 90, 1),
     ("f32", 64, 128, 3, 70, 2),
 ])

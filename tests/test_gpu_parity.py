@@ -111,6 +111,15 @@ def test_context_parallel_groups(G):
     assert_close(*run_dense(1, 2, 7 * 64 + 20, 128, 128, seed=20 + G, s0_std=0.3, cp_groups=G))
 
 
+@pytest.mark.parametrize("B,H,T,G", [(2, 3, 9 * 64 + 5, 5), (1, 5, 5 * 64 + 1, 6), (3, 1, 2 * 64, 2), (2, 7, 1500, 0)])
+def test_context_parallel_128_row_transitions(B, H, T, G):
+    # dk = dv = 128: the transitions run as 128-row tiles. Unit counts
+    # B H (G - 1) off the block map's groups of 8; one chunk per group (T =
+    # 5 x 64 + 1 in 6 groups: the last group holds one token); two groups;
+    # the automatic count (3 groups of 8 chunks here)
+    assert_close(*run_dense(B, H, T, 128, 128, seed=40 + G, s0_std=0.3, cp_groups=G))
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
 def test_context_parallel_shapes(dk, dv):
     assert_close(*run_dense(2, 1, 5 * 64 + 1, dk, dv, seed=30, s0_std=0.3, cp_groups=3))

@@ -78,12 +78,13 @@ def test_instances_present(asm):
     # dk, dv in {64, 128}, with and without decay: 64-row tiles with and
     # without output (12 waves for the output without decay, else 8), 32-row
     # tiles with output; 128-row tiles (15 waves) for the context-parallel
-    # transitions at dk = dv = 128 without decay
+    # transitions at dk = dv = 128, with and without decay
     names = [name for name, _, _ in kernels(asm)]
-    assert len(names) == 25
+    assert len(names) == 26
     assert sum("ELi32ELi8E" in n for n in names) == 8
     assert sum("ELi64ELi12E" in n for n in names) == 4 and sum("ELi64ELi8E" in n for n in names) == 12
     assert sum("ILi128ELi128ELb0ELb0ELi128ELi15E" in n for n in names) == 1
+    assert sum("ILi128ELi128ELb0ELb1ELi128ELi15E" in n for n in names) == 1
 
 
 def test_no_scratch_and_register_budget(asm):
