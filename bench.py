@@ -61,6 +61,14 @@ def flops_per_head_token(C, dk, dv):
     return 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
 
 
+def flops_per_head_token_triangular(C, dk, dv):
+    """The same eight products counting only the entries the masks keep:
+    K K^T strictly lower ((C - 1) / 2C of the dense count), T K, T V, Q K^T
+    and the masked scores times Z lower-inclusive ((C + 1) / 2C each); the
+    three state products stay dense."""
+    return (C - 1) * dk + (C + 1) * (2 * dk + 2 * dv) + 6 * dk * dv
+
+
 def kernel_sha():
     """Hash of the sources of the dominant kernel (chain_kernel_ws); the
     committed counter summary is used only while it matches."""
@@ -630,6 +638,9 @@ def main():
         "data": "synthetic",
         "config": config,
         "mfma_frac_of_bf16_peak": round(mfma_frac, 4),
+        "mfma_frac_triangle_aware": round(head_tokens * flops_per_head_token_triangular(w.chunk, w.dk, w.dv)
+                                          / (ms_per_step / 1e3) / peak_flops, 4),
+        "head_tokens_per_s": round(head_tokens / (ms_per_step / 1e3), 1),
         "flops_per_step": flops,
         "wall_s_timed": round(wall, 4),
         "settle_s_untimed": SETTLE_S,
@@ -681,6 +692,8 @@ def main():
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inputs, w, w.varlen, args.cpu_budget,
                                               g if args.gated else None)
+        if result["cpu_baseline"].get("value"):
+            result["cpu_baseline"]["gpu_speedup"] = round(tokens_per_s / result["cpu_baseline"]["value"], 1)
     print(json.dumps(result), flush=True)
 
 

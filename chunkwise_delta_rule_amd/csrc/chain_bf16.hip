@@ -13,7 +13,9 @@
 // chain of products per 16 state rows, and everything else (Gram tiles, the
 // inverse, P) depends only on the chunk and runs ahead of that chain.
 //
-// Wave roles (two waves per SIMD; wave w and w+4 share a SIMD), iteration r:
+// Wave roles of the 8-wave, 64-row layout (two waves per SIMD; wave w and
+// w+4 share a SIMD; the 12-wave, 32-row and 128-row layouts listed at
+// chain_kernel_ws split the same roles differently), iteration r:
 //   waves 0-3  consumers: each holds 16 rows of S in fp32 registers and runs
 //              Y, Z, O and the state update of chunk r
 //   wave 4     all Gram tiles of chunk r+2 from one set of K fragments, and
@@ -1601,7 +1603,7 @@ template <int DK, int DV> hipError_t launch_rev(const BwdArgs &a, hipStream_t s)
 template <int DK, int DV, bool WO> hipError_t launch_ws(const ChainArgs &a, hipStream_t s) {
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
-    if (a.rows == 128) { // context-parallel transitions, dk = dv = 128, no decay
+    if (a.rows == 128) { // context-parallel transitions at dk = dv = 128, with or without decay
         if constexpr (!WO && DK == 128 && DV == 128) {
             if (a.kind != kCpTransition || a.n_tiles != 2) return hipErrorInvalidValue;
             if (a.g)
@@ -1627,7 +1629,7 @@ template <int DK, int DV, bool WO> hipError_t launch_ws(const ChainArgs &a, hipS
         hipLaunchKernelGGL((chain_kernel_ws<DK, DV, WO, true, 64, 8>), dim3(grid), dim3(512), 0, s, a);
     else if constexpr (WO)
         hipLaunchKernelGGL((chain_kernel_ws<DK, DV, true, false, 64, 12>), dim3(grid), dim3(768), 0, s, a);
-    else // the backward's forward pass and the context-parallel transitions: 8 waves measured faster
+    else // the backward's forward pass and the context-parallel transitions at other widths: 8 waves measured faster than 12
         hipLaunchKernelGGL((chain_kernel_ws<DK, DV, false, false, 64, 8>), dim3(grid), dim3(512), 0, s, a);
     return hipGetLastError();
 }

@@ -52,7 +52,8 @@ struct ChainArgs {
     int n_tiles; // state tiles per unit
     int rows;    // state rows per tile of the bf16 chain kernel: 64, or 32 (forward with
                  // output, dense and packed kinds, when the 32-row grid fits on the compute
-                 // units in one round); 0 reads as 64
+                 // units in one round), or 128 (context-parallel transitions at dk = dv =
+                 // 128: one tile for Q_g, one for P_g); 0 reads as 64
 };
 
 // One decode step: a single token per unit applied to the state in place.
