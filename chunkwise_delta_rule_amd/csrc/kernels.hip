@@ -815,70 +815,66 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
 
 // Prefix composition of the group maps for one (b, h) and 16 state rows:
 //   S_{g+1} = S_g P_g + Q_g,  g = 0..G-2,  S_0 = S0 (or zero);
-// writes S_1..S_{G-1} to ws_S. fp32 throughout (fp32 matrix cores). Each
-// wave computes DK/64 of the DK/16 output column tiles; the 16 rows of S are
-// exchanged through LDS between steps. The operands of step g + 1 (P_{g+1}
-// and Q_{g+1} do not depend on the chain) are loaded while step g computes.
+// writes S_1..S_{G-1} to ws_S. fp32 throughout (fp32 matrix cores). Wave w
+// of DK/16 computes output column tile w, with the contraction split over two
+// accumulators (even and odd 16-blocks) so that the dependent product chain
+// is half as long; the 16 rows of S are exchanged through LDS between steps.
+// The operands of steps g + 1 and g + 2 (P and Q do not depend on the chain)
+// are in flight while step g computes.
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void compose_kernel(const ChainArgs a) {
+__global__ __launch_bounds__(64 * (DK / 16)) void compose_kernel(const ChainArgs a) {
     constexpr int LDS_ = DK + 4;
-    constexpr int TPW = DK / 64;
-    constexpr int NK = DK / 16;
+    constexpr int NK = DK / 16, NT = 64 * (DK / 16);
     __shared__ __attribute__((aligned(16))) float Sl[16 * LDS_];
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     const int rb = blockIdx.x % (DV / 16);
     const int bh = blockIdx.x / (DV / 16);
-    for (int idx = tid; idx < 16 * DK; idx += kThreads) {
+    for (int idx = tid; idx < 16 * DK; idx += NT) {
         const int r = idx / DK, col = idx - r * DK;
         Sl[r * LDS_ + col] = a.S0 ? a.S0[((int64_t)bh * DV + 16 * rb + r) * DK + col] : 0.f;
     }
-    // pa[t][kk] = P_g^T[16 mt + c16][16 kk + 4 g ..], qa[t] = Q_g[16 rb + c16][16 mt + 4 g ..]
-    f32x4 pa[TPW][NK], qa[TPW], pn[TPW][NK], qn[TPW];
-    auto load = [&](int gi, f32x4 (&p)[TPW][NK], f32x4 (&q)[TPW]) {
+    // p[kk] = P_g^T[16 w + c16][16 kk + 4 g ..], q = Q_g[16 rb + c16][16 w + 4 g ..]; three
+    // register sets, step g in set g % 3, so the loads of step g + 2 go into the
+    // set step g - 1 has finished with
+    f32x4 P0[NK], P1[NK], P2[NK], Q0, Q1, Q2;
+    auto load = [&](int gi, f32x4 (&p)[NK], f32x4 &q) {
         const int64_t slot = (int64_t)bh * a.G + gi;
         const float *Pt = a.ws_P + slot * DK * DK;
         const float *Qg = a.ws_Q + (slot * DV + 16 * rb) * DK;
+        q = *reinterpret_cast<const f32x4 *>(Qg + c16 * DK + 16 * w + 4 * g);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int mt = w * TPW + t;
-            q[t] = *reinterpret_cast<const f32x4 *>(Qg + c16 * DK + 16 * mt + 4 * g);
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk)
-                p[t][kk] = *reinterpret_cast<const f32x4 *>(Pt + (16 * mt + c16) * DK + 16 * kk + 4 * g);
-        }
+        for (int kk = 0; kk < NK; ++kk)
+            p[kk] = *reinterpret_cast<const f32x4 *>(Pt + (16 * w + c16) * DK + 16 * kk + 4 * g);
     };
-    if (a.G > 1) load(0, pn, qn);
-    __syncthreads();
-    for (int gi = 0; gi + 1 < a.G; ++gi) {
+    auto step = [&](int gi, const f32x4 (&pc)[NK], const f32x4 &qc, f32x4 (&pl)[NK], f32x4 &ql) {
+        f32x4 acc0 = qc, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            qa[t] = qn[t];
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) pa[t][kk] = pn[t][kk];
+        for (int kk = 0; kk < NK; kk += 2) {
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(Sl + c16 * LDS_ + 16 * kk + 4 * g);
+            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(Sl + c16 * LDS_ + 16 * kk + 16 + 4 * g);
+            acc0 = Tr<float>::mma16(acc0, pc[kk], s0);
+            acc1 = Tr<float>::mma16(acc1, pc[kk + 1], s1);
         }
-        if (gi + 2 < a.G) load(gi + 1, pn, qn);
-        f32x4 acc[TPW];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            acc[t] = qa[t];
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const f32x4 sb = *reinterpret_cast<const f32x4 *>(Sl + c16 * LDS_ + 16 * kk + 4 * g);
-                acc[t] = Tr<float>::mma16(acc[t], pa[t][kk], sb);
-            }
-        }
-        // acc[t][i] = S_{g+1}[row 16rb + c16][16mt + 4g + i]
+        const f32x4 acc = acc0 + acc1;
+        // issued after this step's products, so that waiting for this step's
+        // operands never waits for them
+        if (gi + 2 < a.G - 1) load(gi + 2, pl, ql);
+        // acc[i] = S_{g+1}[row 16 rb + c16][16 w + 4 g + i]
         __syncthreads();
         const int64_t slot = (int64_t)bh * a.G + gi;
         float *Sn = a.ws_S + ((slot + 1) * DV + 16 * rb) * DK;
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int mt = w * TPW + t;
-            *reinterpret_cast<f32x4 *>(Sl + c16 * LDS_ + 16 * mt + 4 * g) = acc[t];
-            *reinterpret_cast<f32x4 *>(Sn + c16 * DK + 16 * mt + 4 * g) = acc[t];
-        }
+        *reinterpret_cast<f32x4 *>(Sl + c16 * LDS_ + 16 * w + 4 * g) = acc;
+        *reinterpret_cast<f32x4 *>(Sn + c16 * DK + 16 * w + 4 * g) = acc;
         __syncthreads();
+    };
+    if (a.G > 1) load(0, P0, Q0);
+    if (a.G > 2) load(1, P1, Q1);
+    __syncthreads();
+    for (int gi = 0; gi + 1 < a.G; gi += 3) {
+        step(gi, P0, Q0, P2, Q2);
+        if (gi + 2 < a.G) step(gi + 1, P1, Q1, P0, Q0);
+        if (gi + 3 < a.G) step(gi + 2, P2, Q2, P1, Q1);
     }
 }
 
@@ -2240,10 +2236,11 @@ hipError_t launch_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream) {
 hipError_t launch_compose(int dk, int dv, const ChainArgs &a, hipStream_t stream) {
     const int grid = a.B * a.H * (dv / 16);
     if (grid <= 0 || a.G < 2) return hipSuccess;
-    if (dk == 128 && dv == 128) hipLaunchKernelGGL((compose_kernel<128, 128>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else if (dk == 128 && dv == 64) hipLaunchKernelGGL((compose_kernel<128, 64>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else if (dk == 64 && dv == 128) hipLaunchKernelGGL((compose_kernel<64, 128>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else if (dk == 64 && dv == 64) hipLaunchKernelGGL((compose_kernel<64, 64>), dim3(grid), dim3(kThreads), 0, stream, a);
+    // one wave per output column tile of 16: 64 dk threads
+    if (dk == 128 && dv == 128) hipLaunchKernelGGL((compose_kernel<128, 128>), dim3(grid), dim3(512), 0, stream, a);
+    else if (dk == 128 && dv == 64) hipLaunchKernelGGL((compose_kernel<128, 64>), dim3(grid), dim3(512), 0, stream, a);
+    else if (dk == 64 && dv == 128) hipLaunchKernelGGL((compose_kernel<64, 128>), dim3(grid), dim3(256), 0, stream, a);
+    else if (dk == 64 && dv == 64) hipLaunchKernelGGL((compose_kernel<64, 64>), dim3(grid), dim3(256), 0, stream, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
