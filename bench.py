@@ -21,7 +21,8 @@ same workload. ``variants.kda`` times ``deltanet_kda_fwd`` (per-channel decay) o
 workload. ``variants.gdp`` times ``deltanet_gdp_fwd`` (Gated Delta Product, n_h = 2 substeps
 per token) on the same B, H, T and widths. ``variants.kda_long`` and
 ``variants.gated_long`` time KDA and Gated DeltaNet on B=1 H=16 T=131072,
-serial chain against context parallelism. ``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
+serial chain against context parallelism, and ``variants.bwd_long`` the
+DeltaNet backward there (deltanet_bwd against deltanet_bwd_cp). ``variants.decode`` times ``deltanet_decode_step`` (one token per sequence and
 head, state updated in place) on B=256 H=16 d=128 bf16, a 256 MiB state.
 The other four workloads of the forward pass are timed by the same clock under
 ``variants.<workload>``: B=4 H=16 T=8192 (serial chain and the library's
@@ -304,6 +305,36 @@ def kda_long_variant(dev, B=1, H=16, T=131072, d=128, steps=5, warmup=2):
     return out
 
 
+def bwd_long_variant(dev, B=1, H=16, T=131072, d=128, steps=3, warmup=1):
+    """Time deltanet_bwd on one long sequence per head (the long-context
+    shape), serial chains against context parallelism at the library's group
+    count (deltanet_bwd_cp); bytes as in bwd_variant."""
+    import torch
+    import chunkwise_delta_rule_amd as dn
+    from chunkwise_delta_rule_amd.synth import make_inputs
+
+    print(f"[bench] backward long-context variant B={B} H={H} T={T}", file=sys.stderr, flush=True)
+    q, k, v, beta, S0 = make_inputs(B, H, T, d, d, seed=13, device=str(dev))
+    g = torch.Generator(device=dev).manual_seed(14)
+    dO = torch.randn(v.shape, generator=g, device=dev, dtype=torch.float32).to(v.dtype)
+    G = dn.deltanet_pick_cp_groups(B, H, T, d, d, 64)
+    ws = torch.empty(max(dn.deltanet_bwd_cp_workspace_bytes(B, H, T, d, d, 64, G), 1), dtype=torch.uint8,
+                     device=dev)
+    out = {"call": "deltanet_bwd / deltanet_bwd_cp", "config": {"B": B, "H": H, "T": T, "dk": d, "dv": d},
+           "steps": steps, "warmup": warmup}
+    nbytes = B * T * H * 2 * (2 * (2 * d + 2 * d + 1))  # read q, k, v, beta, dO; write dq, dk, dv, dbeta
+    for name, groups in (("serial", 1), ("context_parallel", G)):
+        ms, _, _ = time_steps(lambda: dn.deltanet_bwd(q, k, v, beta, dO, S0, cp_groups=groups, workspace=ws),
+                              warmup, steps)
+        out[name] = {"cp_groups": groups, "ms_per_step": round(ms, 4),
+                     "tokens_per_s": round(B * T / (ms / 1e3), 1),
+                     "hbm_frac_algorithmic": round(nbytes / (ms / 1e3) / PEAK_HBM_BPS, 4)}
+    out["speedup"] = round(out["serial"]["ms_per_step"] / out["context_parallel"]["ms_per_step"], 3)
+    del q, k, v, beta, dO, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def gated_long_variant(dev, B=1, H=16, T=131072, d=128, steps=5, warmup=2):
     """Time deltanet_gated_fwd on one long sequence per head (the long-context
     shape), serial chain against context parallelism at the library's group
@@ -517,7 +548,7 @@ def main():
                     help="measure Gated DeltaNet (per-token log decays) instead of DeltaNet")
     ap.add_argument("--variants", default="all",
                     help="comma-separated variants to run after the main line (gated, bwd, gated_bwd, gdp, gdp_bwd, "
-                         "kda, kda_long, gated_long, workloads, decode), or all")
+                         "kda, kda_long, gated_long, bwd_long, workloads, decode), or all")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the short gated and decode runs reported under variants")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -662,7 +693,7 @@ def main():
             "mfma_frac": round(flops / (g_launch_ms / 1e3) / peak_flops, 4),
             "vs_ungated_time": round(g_launch_ms / avg_launch_ms, 4)}
     if not w.varlen and w.dtype == "bf16" and any(map(want, ("bwd", "gated_bwd", "gdp", "gdp_bwd", "kda", "kda_long",
-                                                               "gated_long"))):
+                                                               "gated_long", "bwd_long"))):
         var = result.setdefault("variants", {})
         if want("bwd"):
             var["bwd"] = bwd_variant(dev, w, inputs, avg_launch_ms)
@@ -678,6 +709,8 @@ def main():
             var["kda_long"] = kda_long_variant(dev)
         if want("gated_long"):
             var["gated_long"] = gated_long_variant(dev)
+        if want("bwd_long"):
+            var["bwd_long"] = bwd_long_variant(dev)
     if want("workloads") and w.name == "layer_b8_h16_t4096":
         # the other workloads of the forward pass, each timed by the same clock
         result.setdefault("variants", {})

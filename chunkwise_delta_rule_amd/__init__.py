@@ -26,6 +26,7 @@ import torch
 
 __all__ = ["deltanet_fwd", "deltanet_fwd_noalloc", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
            "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_kda_fwd_varlen", "deltanet_decode_step", "deltanet_kda_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
+           "deltanet_bwd_cp_workspace_bytes",
            "deltanet_bwd_varlen", "deltanet_bwd_varlen_workspace_bytes", "deltanet_gated_bwd",
            "deltanet_gated_bwd_workspace_bytes", "deltanet_gated_bwd_varlen",
            "deltanet_gated_bwd_varlen_workspace_bytes", "deltanet_gdp_bwd", "deltanet_gdp_bwd_workspace_bytes",
@@ -82,6 +83,10 @@ def load_library(path: str | None = None):
     lib.deltanet_bwd.restype = i
     lib.deltanet_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.deltanet_bwd_workspace_bytes.restype = sz
+    lib.deltanet_bwd_cp.argtypes = [vp] * 12 + [i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.deltanet_bwd_cp.restype = i
+    lib.deltanet_bwd_cp_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.deltanet_bwd_cp_workspace_bytes.restype = sz
     lib.deltanet_bwd_varlen.argtypes = [vp] * 14 + [i, i, i, i, i, i, i, vp, sz, vp]
     lib.deltanet_bwd_varlen.restype = i
     lib.deltanet_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -491,9 +496,15 @@ def deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk=64) -> int:
     return int(load_library().deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
 
 
-def deltanet_bwd(q, k, v, beta, dO, S0=None, dS_final=None, *, chunk: int = 64, workspace=None,
-                 want_dS0: bool = True, stream=None):
-    """Backward of ``deltanet_fwd`` (C-ABI ``deltanet_bwd``, bf16 only).
+def deltanet_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk=64, cp_groups=0) -> int:
+    return int(load_library().deltanet_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk, cp_groups))
+
+
+def deltanet_bwd(q, k, v, beta, dO, S0=None, dS_final=None, *, chunk: int = 64, cp_groups: int = 1,
+                 workspace=None, want_dS0: bool = True, stream=None):
+    """Backward of ``deltanet_fwd`` (C-ABI ``deltanet_bwd``, bf16 only; with
+    ``cp_groups`` other than 1, ``deltanet_bwd_cp``: 0 the library's group
+    count, G > 1 forced).
 
     q, k: [B,T,H,dk]; v, dO: [B,T,H,dv]; beta: [B,T,H] (bf16); S0, dS_final:
     [B,H,dv,dk] fp32 or None. Returns (dq, dk, dv, dbeta, dS0 or None).
@@ -517,16 +528,23 @@ def deltanet_bwd(q, k, v, beta, dO, S0=None, dS_final=None, *, chunk: int = 64, 
         _check(dS_final, "dS_final", torch.float32, dev, (B, H, dv, dk))
     dq, dkk, dvv, db = (torch.empty_like(x) for x in (q, k, v, beta))
     dS0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None
-    need = int(lib.deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
+    cp = cp_groups != 1
+    need = int(lib.deltanet_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk, cp_groups) if cp
+               else lib.deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
-        st = lib.deltanet_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_final),
-                              _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dS0), B, H, T, dk, dv, chunk,
-                              DN_BF16, _ptr(workspace), ws_bytes, _stream_handle(stream))
+        if cp:
+            st = lib.deltanet_bwd_cp(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_final),
+                                     _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dS0), B, H, T, dk, dv, chunk,
+                                     DN_BF16, cp_groups, _ptr(workspace), ws_bytes, _stream_handle(stream))
+        else:
+            st = lib.deltanet_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_final),
+                                  _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dS0), B, H, T, dk, dv, chunk,
+                                  DN_BF16, _ptr(workspace), ws_bytes, _stream_handle(stream))
     if st != 0:
-        raise DeltaNetError(st, "deltanet_bwd")
+        raise DeltaNetError(st, "deltanet_bwd_cp" if cp else "deltanet_bwd")
     return dq, dkk, dvv, db, dS0
 
 

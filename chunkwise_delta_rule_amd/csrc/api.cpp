@@ -236,7 +236,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
                const void *dO, const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dg,
                float *dS0, const int32_t *cu_seqlens, const int32_t *seq_order, int B, int H, int T, int nh, int dk,
                int dv, int chunk, int dtype, void *workspace, size_t workspace_bytes, size_t need,
-               hipStream_t stream) {
+               hipStream_t stream, int cp_groups = 1) {
     int st = check_shape(dk, dv, chunk, dtype);
     if (st != DN_OK) return st;
     if (dtype != DN_BF16) return DN_ERR_UNSUPPORTED;
@@ -299,6 +299,34 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     a.kind = varlen ? dn::kVarlen : dn::kDense;
     a.n_units = B * H;
     a.n_tiles = dv / dn::kRows;
+    // context parallelism (dense DeltaNet): G groups of cpg chunks
+    int G = 1, cpg = NC;
+    if (!varlen && !gated && cp_groups != 1) resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    float *cws = nullptr;
+    if (G > 1) {
+        // [P_g^T | Q_g, then C_g | S_g, then E_g] per (b*H + h, g), after the per-chunk slots
+        cws = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(workspace) + bwd_slot_bytes(dk, dv, false) * slots);
+        const size_t per = (size_t)B * H * G;
+        a.ws_P = cws;
+        a.ws_Q = a.ws_P + per * dk * dk;
+        a.ws_S = a.ws_Q + per * dv * dk;
+        a.G = G;
+        a.chunks_per_group = cpg;
+        // (i) the transitions of every group (the reverse chain needs P_g of groups 1..G-1)
+        a.kind = dn::kCpTransition;
+        a.cp_trans_groups = G;
+        a.n_units = B * H * G;
+        a.rows = (dk == 128 && dv == 128) ? 128 : dn::kRows;
+        a.n_tiles = dv / a.rows + dk / a.rows;
+        if (dn::launch_chain(dtype, dk, dv, false, a, stream) != hipSuccess) return DN_ERR_HIP;
+        // (ii) the start states of groups 1..G-1
+        if (dn::launch_compose(dk, dv, a, stream) != hipSuccess) return DN_ERR_HIP;
+        // (iii) every group from its start state, keeping the state entering each chunk and its T
+        a.kind = dn::kCpOutput;
+        a.n_units = B * H * G;
+        a.rows = dn::kRows;
+        a.n_tiles = dv / dn::kRows;
+    }
     if (dn::launch_chain(dtype, dk, dv, false, a, stream) != hipSuccess) return DN_ERR_HIP;
     // DeltaNet: the reverse chain of the state gradients (with dv and dS0),
     // then every chunk's dq, dk, dbeta in parallel. Gated: the backward chain
@@ -333,6 +361,22 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     b.max_slots = (int64_t)slots;
     if (gated) {
         if (dn::launch_bwd(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+    } else if (G > 1) {
+        // reverse chain over the groups: C_g of groups 1..G-1 from a zero end gradient,
+        // the composed end gradients E_g, then every group from E_g
+        const size_t per = (size_t)B * H * G;
+        b.G = G;
+        b.cpg = cpg;
+        b.ws_P = cws;
+        b.ws_C = cws + per * dk * dk;
+        b.ws_E = b.ws_C + per * dv * dk;
+        b.rev_kind = dn::kRevCpAffine;
+        if (dn::launch_bwd_rev(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+        if (dn::launch_compose_bwd(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+        b.rev_kind = dn::kRevCpRun;
+        if (dn::launch_bwd_rev(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+        b.rev_kind = dn::kRevChain;
+        if (dn::launch_bwd_grad(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
     } else {
         if (dn::launch_bwd_rev(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
         if (dn::launch_bwd_grad(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
@@ -559,6 +603,13 @@ size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chu
     return bwd_slot_bytes(dk, dv, false) * slots;
 }
 
+size_t deltanet_bwd_cp_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int cp_groups) {
+    if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
+    int G, cpg;
+    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    return deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk) + ws_bytes_for(B, H, dk, dv, G);
+}
+
 size_t deltanet_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, int dv, int chunk) {
     if (N <= 0 || H <= 0 || total_T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
     return bwd_slot_bytes(dk, dv, false) * varlen_max_slots(N, total_T, H) + align16((size_t)(N + 1) * sizeof(int32_t));
@@ -582,6 +633,16 @@ int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta, 
     const size_t need = deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk);
     return bwd_common(q, k, v, beta, nullptr, S0, dO, dS_final, dq, dk_, dv_, dbeta, nullptr, dS0, nullptr, nullptr, B,
                       H, T, 1, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+}
+
+int deltanet_bwd_cp(const void *q, const void *k, const void *v, const void *beta, const float *S0, const void *dO,
+                    const float *dS_final, void *dq, void *dk_, void *dv_, void *dbeta, float *dS0, int B, int H, int T,
+                    int dk, int dv, int chunk, int dtype, int cp_groups, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+    if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return DN_ERR_INVALID;
+    const size_t need = deltanet_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk, cp_groups);
+    return bwd_common(q, k, v, beta, nullptr, S0, dO, dS_final, dq, dk_, dv_, dbeta, nullptr, dS0, nullptr, nullptr, B,
+                      H, T, 1, dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream, cp_groups);
 }
 
 int deltanet_gated_bwd(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,

@@ -1251,14 +1251,47 @@ template <int DK> struct RevBufs {
 struct RevWork {
     int64_t tok0, slot0, su;
     int len, h, row0;
+    const float *gin; // rows of the gradient at the end of the token range, or nullptr (zero)
+    float *gout;      // rows of the gradient at its start, or nullptr
+    bool store;       // write dv and the dS' of every chunk
 };
-__device__ inline RevWork rev_work(const BwdArgs &a) {
+// Work units of the reverse chain: (sequence, head) units, or (b, h, group)
+// for the context-parallel kinds (groups 1..G-1 for kRevCpAffine, all G for
+// kRevCpRun).
+__device__ inline int rev_units(const BwdArgs &a) {
+    return a.rev_kind == kRevChain ? a.B * a.H : a.B * a.H * (a.rev_kind == kRevCpAffine ? a.G - 1 : a.G);
+}
+template <int DK, int DV> __device__ inline RevWork rev_work(const BwdArgs &a) {
     int u, tau;
-    map_block(blockIdx.x, a.B * a.H, a.n_tiles, u, tau); // the tiles of a unit share an XCD
-    const int rank = u / a.H;
+    map_block(blockIdx.x, rev_units(a), a.n_tiles, u, tau); // the tiles of a unit share an XCD
     RevWork wk;
-    wk.h = u - rank * a.H;
     wk.row0 = 64 * tau;
+    if (a.rev_kind != kRevChain) {
+        const int groups = a.rev_kind == kRevCpAffine ? a.G - 1 : a.G;
+        const int bh = u / groups;
+        const int gi = u - bh * groups + (a.rev_kind == kRevCpAffine ? 1 : 0);
+        const int b = bh / a.H;
+        wk.h = bh - b * a.H;
+        const int t_begin = gi * a.cpg * kChunk;
+        wk.tok0 = (int64_t)b * a.T + t_begin;
+        wk.len = min(a.T, (gi + 1) * a.cpg * kChunk) - t_begin;
+        wk.su = bh;
+        wk.slot0 = (int64_t)bh * a.NC + (int64_t)gi * a.cpg;
+        if (a.rev_kind == kRevCpAffine) {
+            wk.gin = nullptr;
+            wk.gout = a.ws_C + (((int64_t)bh * a.G + gi) * DV + wk.row0) * DK;
+            wk.store = false;
+        } else {
+            wk.gin = gi == a.G - 1 ? (a.dS_final ? a.dS_final + ((int64_t)bh * DV + wk.row0) * DK : nullptr)
+                                   : a.ws_E + (((int64_t)bh * a.G + gi) * DV + wk.row0) * DK;
+            wk.gout = gi == 0 && a.dS0 ? a.dS0 + ((int64_t)bh * DV + wk.row0) * DK : nullptr;
+            wk.store = true;
+        }
+        return wk;
+    }
+    const int rank = u / a.H;
+    wk.h = u - rank * a.H;
+    wk.store = true;
     if (a.cu_seqlens) {
         const int n = a.seq_order ? a.seq_order[rank] : rank;
         wk.tok0 = a.cu_seqlens[n];
@@ -1271,6 +1304,8 @@ __device__ inline RevWork rev_work(const BwdArgs &a) {
         wk.su = u;
         wk.slot0 = (int64_t)u * a.NC;
     }
+    wk.gin = a.dS_final ? a.dS_final + (wk.su * DV + wk.row0) * DK : nullptr;
+    wk.gout = a.dS0 ? a.dS0 + (wk.su * DV + wk.row0) * DK : nullptr;
     return wk;
 }
 
@@ -1419,8 +1454,7 @@ __device__ void rev_consumer_loop(const BwdArgs &a, const RevWork &wk, const Rev
     f32x4 G[NMT];
 #pragma unroll
     for (int m = 0; m < NMT; ++m)
-        G[m] = a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + (wk.su * DV + wk.row0 + lrow) * DK + dk_of(m, g))
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
+        G[m] = wk.gin ? *reinterpret_cast<const f32x4 *>(wk.gin + lrow * DK + dk_of(m, g)) : f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t sv = (int64_t)a.H * DV;
     __bf16 *dvg = reinterpret_cast<__bf16 *>(a.dv) + wk.tok0 * sv + (int64_t)wk.h * DV + wk.row0 + lrow;
     __bf16 *gout = a.G_chunks + (wk.slot0 * DV + wk.row0 + lrow) * DK;
@@ -1429,8 +1463,10 @@ __device__ void rev_consumer_loop(const BwdArgs &a, const RevWork &wk, const Rev
         if (i >= 0) {
             const int r = NC - 1 - i, nval = min(kChunk, wk.len - r * kChunk);
             // dS' of chunk r (the gradient of the state after it), for the gradient kernel
+            if (wk.store) {
 #pragma unroll
-            for (int m = 0; m < NMT; ++m) st4(gout + (int64_t)r * DV * DK + dk_of(m, g), cvt4(G[m]));
+                for (int m = 0; m < NMT; ++m) st4(gout + (int64_t)r * DV * DK + dk_of(m, g), cvt4(G[m]));
+            }
             const __bf16 *Kb = bf.K(i), *Qb = bf.Q(i), *Tb = bf.Tt(i), *Pb = bf.P(i), *Db = bf.D(i);
             // dO fragments over the tokens 32s + {4g + e, 16 + 4g + e}, this lane's value column
             bf16x8 DB[2];
@@ -1477,20 +1513,21 @@ __device__ void rev_consumer_loop(const BwdArgs &a, const RevWork &wk, const Rev
                 fence();
             });
             // dV = dY: Z[t][e] = dY[16t + 4g + e][lrow]
+            if (wk.store) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tok = 16 * t + 4 * g + e;
-                    if (tok < nval) dvg[((int64_t)r * kChunk + tok) * sv] = (__bf16)Z[t][e];
-                }
+                    for (int e = 0; e < 4; ++e) {
+                        const int tok = 16 * t + 4 * g + e;
+                        if (tok < nval) dvg[((int64_t)r * kChunk + tok) * sv] = (__bf16)Z[t][e];
+                    }
+            }
         }
         __syncthreads();
     }
-    if (a.dS0) {
+    if (wk.gout) {
 #pragma unroll
-        for (int m = 0; m < NMT; ++m)
-            *reinterpret_cast<f32x4 *>(a.dS0 + (wk.su * DV + wk.row0 + lrow) * DK + dk_of(m, g)) = G[m];
+        for (int m = 0; m < NMT; ++m) *reinterpret_cast<f32x4 *>(wk.gout + lrow * DK + dk_of(m, g)) = G[m];
     }
 }
 
@@ -1559,17 +1596,17 @@ template <int DK, int DV> __global__ __launch_bounds__(kWsThreads) void rev_chai
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    const RevWork wk = rev_work(a);
+    const RevWork wk = rev_work<DK, DV>(a);
     const int NC = (wk.len + kChunk - 1) / kChunk;
     const RevBufs<DK> bf{smem};
-    if (NC == 0) { // no tokens: dS0 = dS'
-        if (wave < 4 && a.dS0) {
+    if (NC == 0) { // no tokens: the gradient at the start is the one at the end
+        if (wave < 4 && wk.gout) {
             const int lrow = 16 * wave + c16;
 #pragma unroll
             for (int m = 0; m < DK / 16; ++m) {
-                const int64_t off = (wk.su * DV + wk.row0 + lrow) * DK + dk_of(m, g);
-                *reinterpret_cast<f32x4 *>(a.dS0 + off) =
-                    a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+                const int off = lrow * DK + dk_of(m, g);
+                *reinterpret_cast<f32x4 *>(wk.gout + off) =
+                    wk.gin ? *reinterpret_cast<const f32x4 *>(wk.gin + off) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
         return;
@@ -1594,7 +1631,8 @@ template <int DK, int DV> __global__ __launch_bounds__(kWsThreads) void rev_chai
 }
 
 template <int DK, int DV> hipError_t launch_rev(const BwdArgs &a, hipStream_t s) {
-    const int grid = a.B * a.H * a.n_tiles;
+    const int units = a.rev_kind == kRevChain ? a.B * a.H : a.B * a.H * (a.rev_kind == kRevCpAffine ? a.G - 1 : a.G);
+    const int grid = units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
     hipLaunchKernelGGL((rev_chain_kernel<DK, DV>), dim3(grid), dim3(kWsThreads), 0, s, a);
     return hipGetLastError();

@@ -50,6 +50,8 @@ struct ChainArgs {
     int nh;      // substeps per real token (Gated Delta Product; 1 otherwise, gated kernels only)
     int n_units; // units covered by the grid
     int n_tiles; // state tiles per unit
+    int cp_trans_groups; // groups 0..cp_trans_groups-1 get a transition (kCpTransition); 0 reads
+                         // as G - 1 (the forward pass; the backward's needs all G)
     int rows;    // state rows per tile of the bf16 chain kernel: 64, or 32 (forward with
                  // output, dense and packed kinds, when the 32-row grid fits on the compute
                  // units in one round), or 128 (context-parallel transitions at dk = dv =
@@ -97,7 +99,19 @@ struct BwdArgs {
     // query on the last substep, the decay on the first); 1 otherwise
     int nh;
     int64_t max_slots; // chunk slots the workspace holds (dense: B H NC); the finishing grid
+    // Reverse chain over context-parallel groups of cpg chunks (dense DeltaNet):
+    //   kRevCpAffine  groups 1..G-1 from a zero gradient at the group's end, writing only
+    //                 the gradient at its start, C_g, to ws_C ([B*H*G][dv][dk] fp32)
+    //   kRevCpRun     every group from its composed end gradient (ws_E, or dS_final for
+    //                 the last group), writing dv and dS' of its chunks (dS0 from group 0)
+    int rev_kind, G, cpg;
+    const float *ws_P; // P_g^T of the forward transitions, [B*H*G][dk][dk]
+    float *ws_C, *ws_E;
 };
+enum RevKind { kRevChain = 0, kRevCpAffine = 1, kRevCpRun = 2 };
+// Composition of the backward group maps for one (b, h) and 16 state rows:
+// E_{G-1} = dS_final (or zero), E_{g-1} = E_g P_g^T + C_g for g = G-1..1, into ws_E.
+hipError_t launch_compose_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream);
 // Chunk slots before each packed sequence: cb[n] = sum_{m < n} ceil(L_m / 64), cb[N] the total.
 hipError_t launch_chunk_base(const int32_t *cu_seqlens, int N, int32_t *cb, hipStream_t stream);
 // Elements of the bf16 sums of one partial block: dP, dT (64 x 64 each), dQ,

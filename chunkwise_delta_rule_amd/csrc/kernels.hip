@@ -878,6 +878,63 @@ __global__ __launch_bounds__(64 * (DK / 16)) void compose_kernel(const ChainArgs
     }
 }
 
+// Composition of the backward pass's group maps (context-parallel reverse
+// chain) for one (b, h) and 16 gradient rows. Over a group the reverse chain
+// is affine in the gradient at the group's end, dS_start = dS_end P_g^T + C_g,
+// with P_g the group's forward transition (the gradient of S P_g + Q_g with
+// respect to S) and C_g the reverse chain's result from a zero end gradient.
+//   E_{G-1} = dS_final (or zero),  E_{g-1} = E_g P_g^T + C_g,  g = G-1..1,
+// into ws_E (E_g: the gradient at the end of group g). ws_P holds P_g^T, so
+// E_g P_g^T is the product with the stored matrix itself: operand A of the
+// product reads it down its columns. Layout of the waves as in compose_kernel.
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * (DK / 16)) void compose_bwd_kernel(const BwdArgs a) {
+    constexpr int LDS_ = DK + 4;
+    constexpr int NK = DK / 16, NT = 64 * (DK / 16);
+    __shared__ __attribute__((aligned(16))) float El[16 * LDS_];
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int rb = blockIdx.x % (DV / 16);
+    const int bh = blockIdx.x / (DV / 16);
+    for (int idx = tid; idx < 16 * DK; idx += NT) {
+        const int r = idx / DK, col = idx - r * DK;
+        El[r * LDS_ + col] = a.dS_final ? a.dS_final[((int64_t)bh * DV + 16 * rb + r) * DK + col] : 0.f;
+    }
+    // p[kk][j] = (P_g^T)[16 kk + 4 g + j][16 w + c16], c = C_g[16 rb + c16][16 w + 4 g ..]
+    f32x4 pa[NK], ca, pn[NK], cn;
+    auto load = [&](int gi, f32x4 (&p)[NK], f32x4 &c) {
+        const int64_t slot = (int64_t)bh * a.G + gi;
+        const float *W = a.ws_P + slot * DK * DK;
+        c = *reinterpret_cast<const f32x4 *>(a.ws_C + (slot * DV + 16 * rb + c16) * DK + 16 * w + 4 * g);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[kk][j] = W[(16 * kk + 4 * g + j) * DK + 16 * w + c16];
+    };
+    if (a.G > 1) load(a.G - 1, pn, cn);
+    __syncthreads();
+    for (int gi = a.G - 1; gi >= 1; --gi) {
+        ca = cn;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) pa[kk] = pn[kk];
+        f32x4 acc0 = ca, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NK; kk += 2) {
+            const f32x4 e0 = *reinterpret_cast<const f32x4 *>(El + c16 * LDS_ + 16 * kk + 4 * g);
+            const f32x4 e1 = *reinterpret_cast<const f32x4 *>(El + c16 * LDS_ + 16 * kk + 16 + 4 * g);
+            acc0 = Tr<float>::mma16(acc0, pa[kk], e0);
+            acc1 = Tr<float>::mma16(acc1, pa[kk + 1], e1);
+        }
+        const f32x4 acc = acc0 + acc1; // acc[i] = E_{g-1}[16 rb + c16][16 w + 4 g + i]
+        if (gi >= 2) load(gi - 1, pn, cn);
+        __syncthreads();
+        float *En = a.ws_E + (((int64_t)bh * a.G + gi - 1) * DV + 16 * rb) * DK;
+        *reinterpret_cast<f32x4 *>(El + c16 * LDS_ + 16 * w + 4 * g) = acc;
+        *reinterpret_cast<f32x4 *>(En + c16 * DK + 16 * w + 4 * g) = acc;
+        __syncthreads();
+    }
+}
+
 template <int DK, int DV, bool WO> hipError_t launch_one(const ChainArgs &a, hipStream_t s) {
     const int grid = a.n_units * a.n_tiles;
     if (grid <= 0) return hipSuccess;
@@ -2231,6 +2288,17 @@ hipError_t launch_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream) {
     if (dk == 64 && dv == 128) return launch_bwd_dims<64, 128>(a, stream);
     if (dk == 64 && dv == 64) return launch_bwd_dims<64, 64>(a, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_compose_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stream) {
+    const int grid = a.B * a.H * (dv / 16);
+    if (grid <= 0 || a.G < 2) return hipSuccess;
+    if (dk == 128 && dv == 128) hipLaunchKernelGGL((compose_bwd_kernel<128, 128>), dim3(grid), dim3(512), 0, stream, a);
+    else if (dk == 128 && dv == 64) hipLaunchKernelGGL((compose_bwd_kernel<128, 64>), dim3(grid), dim3(512), 0, stream, a);
+    else if (dk == 64 && dv == 128) hipLaunchKernelGGL((compose_bwd_kernel<64, 128>), dim3(grid), dim3(256), 0, stream, a);
+    else if (dk == 64 && dv == 64) hipLaunchKernelGGL((compose_bwd_kernel<64, 64>), dim3(grid), dim3(256), 0, stream, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_compose(int dk, int dv, const ChainArgs &a, hipStream_t stream) {

@@ -272,6 +272,32 @@ int deltanet_bwd(const void *q, const void *k, const void *v, const void *beta,
 size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 
 /*
+ * deltanet_bwd with the chunk chains split into cp_groups contiguous groups
+ * of chunks per sequence (1: serial, as deltanet_bwd; 0: the library's choice,
+ * deltanet_pick_cp_groups), for long sequences with few (sequence, head)
+ * units. Over a group the reverse chain is affine in the gradient at the
+ * group's end, dS_start = dS_end P_g^T + C_g, with P_g the group's forward
+ * transition ("Context Parallelism for DeltaNet", section 2, the affine group
+ * map, taken in reverse mode; the pages give no backward pass). The forward
+ * states come from the context-parallel forward (transitions of every group,
+ * their composition, every group from its start state); the reverse chain
+ * then forms C_g of groups 1..G-1 from a zero end gradient, composes the end
+ * gradients of all groups from dS_final, and runs every group from its own.
+ * Results match deltanet_bwd up to rounding. Arguments as deltanet_bwd;
+ * workspace: at least deltanet_bwd_cp_workspace_bytes(...) bytes, 16-byte
+ * aligned (deltanet_bwd's, plus per (sequence, head, group) P_g^T, and two
+ * dv x dk fp32 matrices). cp_groups < 0: DN_ERR_INVALID.
+ */
+int deltanet_bwd_cp(const void *q, const void *k, const void *v, const void *beta,
+                    const float *S0, const void *dO, const float *dS_final, void *dq, void *dk,
+                    void *dv, void *dbeta, float *dS0, int B, int H, int T, int dk_, int dv_,
+                    int chunk, int dtype, int cp_groups, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Bytes of workspace deltanet_bwd_cp needs for cp_groups (0 for invalid shapes). */
+size_t deltanet_bwd_cp_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int cp_groups);
+
+/*
  * deltanet_bwd over a packed batch of N sequences (layouts as in
  * deltanet_fwd_varlen: tokens [total_T, H, *], cu_seqlens [N + 1] int32,
  * optional seq_order [N]; S0, dS_final, dS0 [N, H, dv, dk]); the state and

@@ -133,9 +133,24 @@ hipError_t launch_bwd_rev(int dk, int dv, const BwdArgs &b, hipStream_t) {
     rd(b.seq_order, b.cu_seqlens && b.seq_order ? (size_t)b.B * 4 : 0);
     rd(b.dS_final, b.dS_final ? units * dv * dk * 4 : 0);
     rd(b.T_chunks, slots * kChunk * kChunk * 2);
+    if (b.rev_kind == kRevCpAffine) { // only the group-start gradients C_g of groups 1..G-1
+        wr(b.ws_C + units * dv * dk, units * (b.G - 1) * dv * dk * 4);
+        return hipSuccess;
+    }
+    if (b.rev_kind == kRevCpRun) rd(b.ws_E, units * (b.G - 1) * dv * dk * 4);
     wr(b.G_chunks, slots * dv * dk * 2);
     wr(b.dv, steps * b.H * dv * 2);
     wr(b.dS0, b.dS0 ? units * dv * dk * 4 : 0);
+    return hipSuccess;
+}
+
+hipError_t launch_compose_bwd(int dk, int dv, const BwdArgs &b, hipStream_t) {
+    ++launches;
+    const size_t units = (size_t)b.B * b.H, per = units * b.G;
+    rd(b.ws_P, per * dk * dk * 4);
+    rd(b.ws_C, per * dv * dk * 4);
+    rd(b.dS_final, b.dS_final ? units * dv * dk * 4 : 0);
+    wr(b.ws_E, units * (b.G - 1) * dv * dk * 4);
     return hipSuccess;
 }
 

@@ -355,6 +355,23 @@ def prototype(name):
     return [" ".join(p.split()) for p in m.group(1).split(",")]
 
 
+def test_bwd_cp_workspace_sizes(lib):
+    # deltanet_bwd's workspace plus, per (sequence, head, group), P_g^T (dk^2)
+    # and two dv x dk matrices, fp32; one group needs nothing more
+    for dk, dv in [(128, 128), (64, 128), (128, 64)]:
+        serial = dn.deltanet_bwd_workspace_bytes(2, 3, 1000, dk, dv)
+        assert dn.deltanet_bwd_cp_workspace_bytes(2, 3, 1000, dk, dv, 64, 1) == serial
+        # 16 chunks in 4 groups of 4
+        assert dn.deltanet_bwd_cp_workspace_bytes(2, 3, 1000, dk, dv, 64, 4) == serial + 2 * 3 * 4 * (
+            dk * dk + 2 * dv * dk) * 4
+        G = dn.deltanet_pick_cp_groups(1, 2, 131072, dk, dv, 64)
+        assert G > 1
+        assert dn.deltanet_bwd_cp_workspace_bytes(1, 2, 131072, dk, dv, 64, 0) == \
+            dn.deltanet_bwd_workspace_bytes(1, 2, 131072, dk, dv) + 2 * G * (dk * dk + 2 * dv * dk) * 4
+    assert lib.deltanet_bwd_cp_workspace_bytes(2, 3, 1000, 128, 128, 64, -1) == 0
+    assert lib.deltanet_bwd_cp_workspace_bytes(2, 3, 1000, 96, 128, 64, 2) == 0
+
+
 def test_boundary_signatures_as_documented():
     # the departures from the proposed boundary that the design notes list
     fwd = prototype("deltanet_fwd")

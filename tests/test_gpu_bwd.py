@@ -5,7 +5,8 @@ token-serial recurrence and is pinned by finite differences; the library runs
 three passes (forward chain keeping per-chunk states, reverse state-gradient
 chain, chunk-parallel finish). Cases: every (dk, dv), ragged lengths, chunk
 boundaries, initial state and final-state gradient present or absent, the
-empty sequence, and packed sequences (varlen) against the oracle per sequence. Metric: max|gpu - oracle| / max|oracle| per gradient tensor.
+empty sequence, packed sequences (varlen) against the oracle per sequence, and
+the context-parallel backward (deltanet_bwd_cp) over several group counts. Metric: max|gpu - oracle| / max|oracle| per gradient tensor.
 """
 
 import numpy as np
@@ -22,15 +23,15 @@ DEV = "cuda:0"
 TOL_BWD = 2e-2  # as for the bf16 forward; measured errors are 1e-3 .. 7e-3
 
 
-def run_bwd(B, H, T, dk, dv, seed, s0=True, dsf=True):
-    print(f"[case] bwd B={B} H={H} T={T} dk={dk} dv={dv} s0={s0} dSf={dsf}", flush=True)
+def run_bwd(B, H, T, dk, dv, seed, s0=True, dsf=True, cp_groups=1):
+    print(f"[case] bwd B={B} H={H} T={T} dk={dk} dv={dv} s0={s0} dSf={dsf} cp={cp_groups}", flush=True)
     q, k, v, beta, S0 = make_inputs(B, H, T, dk, dv, seed=seed, s0_std=0.3 if s0 else 0.0)
     g = torch.Generator().manual_seed(seed + 1)
     dO = torch.randn(v.shape, generator=g).to(torch.bfloat16)
     dSf = torch.randn((B, H, dv, dk), generator=g) * 0.1 if dsf else None
     d = [x.to(DEV) for x in (q, k, v, beta, dO)]
     out = deltanet_bwd(d[0], d[1], d[2], d[3], d[4], None if S0 is None else S0.to(DEV),
-                       None if dSf is None else dSf.to(DEV))
+                       None if dSf is None else dSf.to(DEV), cp_groups=cp_groups)
     torch.cuda.synchronize()
     ref = oracle.deltanet_bwd(f64(q), f64(k), f64(v), f64(beta), f64(dO), f64(S0), f64(dSf))
     errs = [rel_err(f64(x), r) for x, r in zip(out, ref)]
@@ -48,6 +49,33 @@ def test_bwd_shapes_ragged(dk, dv):
 def test_bwd_lengths(T):
     errs = run_bwd(1, 2, T, 128, 128, seed=410 + T)
     assert max(errs) <= TOL_BWD
+
+
+@pytest.mark.parametrize("dk,dv,G", [(128, 128, 2), (128, 128, 3), (128, 128, 7), (64, 64, 4), (64, 128, 3),
+                                      (128, 64, 5)])
+def test_bwd_context_parallel(dk, dv, G):
+    # deltanet_bwd_cp: the chains split into G groups (ragged last group)
+    errs = run_bwd(2, 3, 7 * 64 + 21, dk, dv, seed=430 + G + dk, cp_groups=G)
+    assert max(errs) <= TOL_BWD
+
+
+@pytest.mark.parametrize("s0,dsf", [(False, False), (True, False), (False, True)])
+def test_bwd_context_parallel_optional_states(s0, dsf):
+    errs = run_bwd(1, 2, 6 * 64 + 1, 128, 128, seed=440, s0=s0, dsf=dsf, cp_groups=6)
+    assert max(errs) <= TOL_BWD
+
+
+def test_bwd_context_parallel_matches_serial_closely():
+    q, k, v, beta, S0 = make_inputs(1, 2, 2000, 128, 128, seed=450, s0_std=0.2)
+    g = torch.Generator().manual_seed(451)
+    dO = torch.randn(v.shape, generator=g).to(torch.bfloat16)
+    dSf = torch.randn((1, 2, 128, 128), generator=g) * 0.1
+    d = [x.to(DEV) for x in (q, k, v, beta, dO, S0, dSf)]
+    a = deltanet_bwd(*d)
+    b = deltanet_bwd(*d, cp_groups=4)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert rel_err(f64(y), f64(x)) < 2e-2
 
 
 def test_bwd_without_s0_and_final_gradient():

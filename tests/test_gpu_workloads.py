@@ -179,6 +179,24 @@ def test_bwd_layer_b8_h16_t4096_every_unit():
     report(f"bwd {w.name} all units", [(n, f64(x), r) for n, x, r in zip(names, out, ref)], 2e-2)
 
 
+def test_bwd_long_b1_h16_t131072_context_parallel_every_head():
+    # the backward at the long-context shape with the library's group count,
+    # every head against the oracle's reverse mode
+    w = WORKLOADS["long_b1_h16_t131072"]
+    G = dn.deltanet_pick_cp_groups(w.B, w.H, w.T, w.dk, w.dv)
+    print(f"[case] {w.name} full size, backward, cp_groups=0 ({G} groups)", flush=True)
+    assert G > 1
+    q, k, v, beta, S0 = workload_inputs(w, seed=5, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(11)
+    dO = torch.randn(v.shape, generator=g, device=DEV, dtype=torch.float32).to(v.dtype)
+    dSf = torch.randn((w.B, w.H, w.dv, w.dk), generator=g, device=DEV, dtype=torch.float32) * 0.1
+    out = dn.deltanet_bwd(q, k, v, beta, dO, S0, dSf, cp_groups=0)
+    torch.cuda.synchronize()
+    ref = oracle.deltanet_bwd(f64(q), f64(k), f64(v), f64(beta), f64(dO), f64(S0), f64(dSf))
+    names = ("dq", "dk", "dv", "dbeta", "dS0")
+    report(f"bwd {w.name} all heads, cp_groups=0", [(n, f64(x), r) for n, x, r in zip(names, out, ref)], 2e-2)
+
+
 def test_gated_bwd_layer_b8_h16_t4096_every_unit():
     # the Gated DeltaNet backward at the benchmark's full shape, in the launch
     # configuration bench.py times, every unit against the oracle
