@@ -306,9 +306,10 @@ def kda_long_variant(dev, B=1, H=16, T=131072, d=128, steps=5, warmup=2):
 
 
 def bwd_long_variant(dev, B=1, H=16, T=131072, d=128, steps=3, warmup=1):
-    """Time deltanet_bwd on one long sequence per head (the long-context
-    shape), serial chains against context parallelism at the library's group
-    count (deltanet_bwd_cp); bytes as in bwd_variant."""
+    """Time deltanet_bwd and deltanet_gated_bwd on one long sequence per head
+    (the long-context shape), serial chains against context parallelism at
+    the library's group count (deltanet_bwd_cp, deltanet_gated_bwd_cp); bytes
+    as in bwd_variant."""
     import torch
     import chunkwise_delta_rule_amd as dn
     from chunkwise_delta_rule_amd.synth import make_inputs
@@ -320,7 +321,7 @@ def bwd_long_variant(dev, B=1, H=16, T=131072, d=128, steps=3, warmup=1):
     G = dn.deltanet_pick_cp_groups(B, H, T, d, d, 64)
     ws = torch.empty(max(dn.deltanet_bwd_cp_workspace_bytes(B, H, T, d, d, 64, G), 1), dtype=torch.uint8,
                      device=dev)
-    out = {"call": "deltanet_bwd / deltanet_bwd_cp", "config": {"B": B, "H": H, "T": T, "dk": d, "dv": d},
+    out = {"call": "deltanet_bwd / deltanet_bwd_cp (gated_*: deltanet_gated_bwd / deltanet_gated_bwd_cp)", "config": {"B": B, "H": H, "T": T, "dk": d, "dv": d},
            "steps": steps, "warmup": warmup}
     nbytes = B * T * H * 2 * (2 * (2 * d + 2 * d + 1))  # read q, k, v, beta, dO; write dq, dk, dv, dbeta
     for name, groups in (("serial", 1), ("context_parallel", G)):
@@ -330,7 +331,21 @@ def bwd_long_variant(dev, B=1, H=16, T=131072, d=128, steps=3, warmup=1):
                      "tokens_per_s": round(B * T / (ms / 1e3), 1),
                      "hbm_frac_algorithmic": round(nbytes / (ms / 1e3) / PEAK_HBM_BPS, 4)}
     out["speedup"] = round(out["serial"]["ms_per_step"] / out["context_parallel"]["ms_per_step"], 3)
-    del q, k, v, beta, dO, ws
+    # the same for the Gated DeltaNet backward (deltanet_gated_bwd / deltanet_gated_bwd_cp)
+    from chunkwise_delta_rule_amd.synth import make_gates
+    gl = make_gates((B, T, H), seed=13, device=str(dev))
+    del ws
+    ws = torch.empty(max(dn.deltanet_gated_bwd_cp_workspace_bytes(B, H, T, d, d, 64, G), 1), dtype=torch.uint8,
+                     device=dev)
+    gbytes = nbytes + B * T * H * 8  # g read, dg written (fp32)
+    for name, groups in (("gated_serial", 1), ("gated_context_parallel", G)):
+        ms, _, _ = time_steps(lambda: dn.deltanet_gated_bwd(q, k, v, beta, gl, dO, S0, cp_groups=groups,
+                                                            workspace=ws), warmup, steps)
+        out[name] = {"cp_groups": groups, "ms_per_step": round(ms, 4),
+                     "tokens_per_s": round(B * T / (ms / 1e3), 1),
+                     "hbm_frac_algorithmic": round(gbytes / (ms / 1e3) / PEAK_HBM_BPS, 4)}
+    out["gated_speedup"] = round(out["gated_serial"]["ms_per_step"] / out["gated_context_parallel"]["ms_per_step"], 3)
+    del q, k, v, beta, dO, gl, ws
     torch.cuda.empty_cache()
     return out
 

@@ -26,7 +26,7 @@ import torch
 
 __all__ = ["deltanet_fwd", "deltanet_fwd_noalloc", "deltanet_fwd_varlen", "deltanet_gated_fwd", "deltanet_gated_fwd_varlen",
            "deltanet_gdp_fwd", "deltanet_kda_fwd", "deltanet_kda_fwd_varlen", "deltanet_decode_step", "deltanet_kda_decode_step", "deltanet_bwd", "deltanet_bwd_workspace_bytes",
-           "deltanet_bwd_cp_workspace_bytes",
+           "deltanet_bwd_cp_workspace_bytes", "deltanet_gated_bwd_cp_workspace_bytes",
            "deltanet_bwd_varlen", "deltanet_bwd_varlen_workspace_bytes", "deltanet_gated_bwd",
            "deltanet_gated_bwd_workspace_bytes", "deltanet_gated_bwd_varlen",
            "deltanet_gated_bwd_varlen_workspace_bytes", "deltanet_gdp_bwd", "deltanet_gdp_bwd_workspace_bytes",
@@ -93,6 +93,10 @@ def load_library(path: str | None = None):
     lib.deltanet_bwd_varlen_workspace_bytes.restype = sz
     lib.deltanet_gated_bwd.argtypes = [vp] * 14 + [i, i, i, i, i, i, i, vp, sz, vp]
     lib.deltanet_gated_bwd.restype = i
+    lib.deltanet_gated_bwd_cp.argtypes = [vp] * 14 + [i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.deltanet_gated_bwd_cp.restype = i
+    lib.deltanet_gated_bwd_cp_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.deltanet_gated_bwd_cp_workspace_bytes.restype = sz
     lib.deltanet_gated_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.deltanet_gated_bwd_workspace_bytes.restype = sz
     lib.deltanet_gated_bwd_varlen.argtypes = [vp] * 16 + [i, i, i, i, i, i, i, vp, sz, vp]
@@ -500,6 +504,10 @@ def deltanet_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk=64, cp_groups=0) -> i
     return int(load_library().deltanet_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk, cp_groups))
 
 
+def deltanet_gated_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk=64, cp_groups=0) -> int:
+    return int(load_library().deltanet_gated_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk, cp_groups))
+
+
 def deltanet_bwd(q, k, v, beta, dO, S0=None, dS_final=None, *, chunk: int = 64, cp_groups: int = 1,
                  workspace=None, want_dS0: bool = True, stream=None):
     """Backward of ``deltanet_fwd`` (C-ABI ``deltanet_bwd``, bf16 only; with
@@ -605,9 +613,10 @@ def deltanet_gated_bwd_varlen_workspace_bytes(N, total_T, H, dk, dv, chunk=64) -
     return int(load_library().deltanet_gated_bwd_varlen_workspace_bytes(N, total_T, H, dk, dv, chunk))
 
 
-def deltanet_gated_bwd(q, k, v, beta, g, dO, S0=None, dS_final=None, *, chunk: int = 64, workspace=None,
-                       want_dS0: bool = True, stream=None):
-    """Backward of ``deltanet_gated_fwd`` (C-ABI ``deltanet_gated_bwd``, bf16 only).
+def deltanet_gated_bwd(q, k, v, beta, g, dO, S0=None, dS_final=None, *, chunk: int = 64, cp_groups: int = 1,
+                       workspace=None, want_dS0: bool = True, stream=None):
+    """Backward of ``deltanet_gated_fwd`` (C-ABI ``deltanet_gated_bwd``, bf16 only;
+    with ``cp_groups`` other than 1, ``deltanet_gated_bwd_cp``).
 
     q, k: [B,T,H,dk]; v, dO: [B,T,H,dv]; beta: [B,T,H] (bf16); g: [B,T,H]
     fp32 log decays; S0, dS_final: [B,H,dv,dk] fp32 or None. Returns (dq, dk,
@@ -634,17 +643,25 @@ def deltanet_gated_bwd(q, k, v, beta, g, dO, S0=None, dS_final=None, *, chunk: i
     dq, dkk, dvv, db = (torch.empty_like(x) for x in (q, k, v, beta))
     dg = torch.empty_like(g)
     dS0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None
-    need = int(lib.deltanet_gated_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
+    cp = cp_groups != 1
+    need = int(lib.deltanet_gated_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk, cp_groups) if cp
+               else lib.deltanet_gated_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
-        st = lib.deltanet_gated_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO),
-                                    _ptr(dS_final), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg), _ptr(dS0),
-                                    B, H, T, dk, dv, chunk, DN_BF16, _ptr(workspace), ws_bytes,
-                                    _stream_handle(stream))
+        if cp:
+            st = lib.deltanet_gated_bwd_cp(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO),
+                                           _ptr(dS_final), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg),
+                                           _ptr(dS0), B, H, T, dk, dv, chunk, DN_BF16, cp_groups, _ptr(workspace),
+                                           ws_bytes, _stream_handle(stream))
+        else:
+            st = lib.deltanet_gated_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(dO),
+                                        _ptr(dS_final), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db), _ptr(dg), _ptr(dS0),
+                                        B, H, T, dk, dv, chunk, DN_BF16, _ptr(workspace), ws_bytes,
+                                        _stream_handle(stream))
     if st != 0:
-        raise DeltaNetError(st, "deltanet_gated_bwd")
+        raise DeltaNetError(st, "deltanet_gated_bwd_cp" if cp else "deltanet_gated_bwd")
     return dq, dkk, dvv, db, dg, dS0
 
 

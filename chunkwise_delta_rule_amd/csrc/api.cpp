@@ -301,11 +301,11 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     a.n_tiles = dv / dn::kRows;
     // context parallelism (dense DeltaNet): G groups of cpg chunks
     int G = 1, cpg = NC;
-    if (!varlen && !gated && cp_groups != 1) resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    if (!varlen && cp_groups != 1) resolve_groups(cp_groups, B, H, T, dv, G, cpg);
     float *cws = nullptr;
     if (G > 1) {
         // [P_g^T | Q_g, then C_g | S_g, then E_g] per (b*H + h, g), after the per-chunk slots
-        cws = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(workspace) + bwd_slot_bytes(dk, dv, false) * slots);
+        cws = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(workspace) + bwd_slot_bytes(dk, dv, gated) * slots);
         const size_t per = (size_t)B * H * G;
         a.ws_P = cws;
         a.ws_Q = a.ws_P + per * dk * dk;
@@ -319,6 +319,7 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
         a.rows = (dk == 128 && dv == 128) ? 128 : dn::kRows;
         a.n_tiles = dv / a.rows + dk / a.rows;
         if (dn::launch_chain(dtype, dk, dv, false, a, stream) != hipSuccess) return DN_ERR_HIP;
+        a.cp_trans_groups = 0;
         // (ii) the start states of groups 1..G-1
         if (dn::launch_compose(dk, dv, a, stream) != hipSuccess) return DN_ERR_HIP;
         // (iii) every group from its start state, keeping the state entering each chunk and its T
@@ -359,11 +360,10 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
     b.NC = NC;
     b.n_tiles = dv / dn::kRows;
     b.max_slots = (int64_t)slots;
-    if (gated) {
-        if (dn::launch_bwd(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
-    } else if (G > 1) {
+    if (G > 1) {
         // reverse chain over the groups: C_g of groups 1..G-1 from a zero end gradient,
-        // the composed end gradients E_g, then every group from E_g
+        // the composed end gradients E_g, then every group from E_g (gated: the
+        // backward chain with its partial sums, then the finishing pass)
         const size_t per = (size_t)B * H * G;
         b.G = G;
         b.cpg = cpg;
@@ -371,12 +371,16 @@ int bwd_common(const void *q, const void *k, const void *v, const void *beta, co
         b.ws_C = cws + per * dk * dk;
         b.ws_E = b.ws_C + per * dv * dk;
         b.rev_kind = dn::kRevCpAffine;
-        if (dn::launch_bwd_rev(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+        if ((gated ? dn::launch_bwd(dk, dv, b, stream) : dn::launch_bwd_rev(dk, dv, b, stream)) != hipSuccess)
+            return DN_ERR_HIP;
         if (dn::launch_compose_bwd(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
         b.rev_kind = dn::kRevCpRun;
-        if (dn::launch_bwd_rev(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+        if ((gated ? dn::launch_bwd(dk, dv, b, stream) : dn::launch_bwd_rev(dk, dv, b, stream)) != hipSuccess)
+            return DN_ERR_HIP;
         b.rev_kind = dn::kRevChain;
-        if (dn::launch_bwd_grad(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+        if (!gated && dn::launch_bwd_grad(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
+    } else if (gated) {
+        if (dn::launch_bwd(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
     } else {
         if (dn::launch_bwd_rev(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
         if (dn::launch_bwd_grad(dk, dv, b, stream) != hipSuccess) return DN_ERR_HIP;
@@ -610,6 +614,13 @@ size_t deltanet_bwd_cp_workspace_bytes(int B, int H, int T, int dk, int dv, int 
     return deltanet_bwd_workspace_bytes(B, H, T, dk, dv, chunk) + ws_bytes_for(B, H, dk, dv, G);
 }
 
+size_t deltanet_gated_bwd_cp_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int cp_groups) {
+    if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
+    int G, cpg;
+    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    return deltanet_gated_bwd_workspace_bytes(B, H, T, dk, dv, chunk) + ws_bytes_for(B, H, dk, dv, G);
+}
+
 size_t deltanet_bwd_varlen_workspace_bytes(int N, int total_T, int H, int dk, int dv, int chunk) {
     if (N <= 0 || H <= 0 || total_T < 0 || check_shape(dk, dv, chunk, DN_BF16) != DN_OK) return 0;
     return bwd_slot_bytes(dk, dv, false) * varlen_max_slots(N, total_T, H) + align16((size_t)(N + 1) * sizeof(int32_t));
@@ -654,6 +665,17 @@ int deltanet_gated_bwd(const void *q, const void *k, const void *v, const void *
     const size_t need = deltanet_gated_bwd_workspace_bytes(B, H, T, dk, dv, chunk);
     return bwd_common(q, k, v, beta, g, S0, dO, dS_final, dq, dk_, dv_, dbeta, dg, dS0, nullptr, nullptr, B, H, T, 1,
                       dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream);
+}
+
+int deltanet_gated_bwd_cp(const void *q, const void *k, const void *v, const void *beta, const float *g,
+                          const float *S0, const void *dO, const float *dS_final, void *dq, void *dk_, void *dv_,
+                          void *dbeta, float *dg, float *dS0, int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                          int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return DN_ERR_INVALID;
+    if (T > 0 && (!g || !dg)) return DN_ERR_INVALID;
+    const size_t need = deltanet_gated_bwd_cp_workspace_bytes(B, H, T, dk, dv, chunk, cp_groups);
+    return bwd_common(q, k, v, beta, g, S0, dO, dS_final, dq, dk_, dv_, dbeta, dg, dS0, nullptr, nullptr, B, H, T, 1,
+                      dk, dv, chunk, dtype, workspace, workspace_bytes, need, stream, cp_groups);
 }
 
 size_t deltanet_gdp_bwd_workspace_bytes(int B, int H, int T, int n_h, int dk, int dv, int chunk) {

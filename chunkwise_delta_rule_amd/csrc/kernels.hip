@@ -1025,22 +1025,56 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     int u, tau;
-    map_block(blockIdx.x, a.B * a.H, a.n_tiles, u, tau); // the tiles of a unit share an XCD
-    const int rank = u / a.H, h = u - rank * a.H, row0 = 64 * tau;
-    // token range, state slot su and first chunk slot of this unit
+    // units: (sequence, head), or (b, h, group) for the context-parallel kinds
+    // (groups 1..G-1 for kRevCpAffine, all G for kRevCpRun)
+    const int cp_groups = a.rev_kind == kRevChain ? 1 : (a.rev_kind == kRevCpAffine ? a.G - 1 : a.G);
+    map_block(blockIdx.x, a.B * a.H * cp_groups, a.n_tiles, u, tau); // the tiles of a unit share an XCD
+    const int row0 = 64 * tau;
+    // token range, state slot su and first chunk slot of this unit; the
+    // gradient at the end of the range (gin, nullptr: zero), where the one at
+    // its start goes (gout), and whether dv and the partial sums are written
+    int rank, h;
     int64_t tok0, su, slot0;
     int len;
-    if (a.cu_seqlens) {
-        const int n = a.seq_order ? a.seq_order[rank] : rank;
-        tok0 = a.cu_seqlens[n];
-        len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
-        su = (int64_t)n * a.H + h;
-        slot0 = (int64_t)a.chunk_base[n] * a.H + (int64_t)h * ((len + kChunk - 1) / kChunk);
+    const float *gin;
+    float *gout;
+    bool store = true;
+    if (a.rev_kind != kRevChain) {
+        const int bh = u / cp_groups;
+        const int gi = u - bh * cp_groups + (a.rev_kind == kRevCpAffine ? 1 : 0);
+        rank = bh / a.H;
+        h = bh - rank * a.H;
+        const int t_begin = gi * a.cpg * kChunk;
+        tok0 = (int64_t)rank * a.T + t_begin;
+        len = min(a.T, (gi + 1) * a.cpg * kChunk) - t_begin;
+        su = bh;
+        slot0 = (int64_t)bh * a.NC + (int64_t)gi * a.cpg;
+        if (a.rev_kind == kRevCpAffine) {
+            gin = nullptr;
+            gout = a.ws_C + (((int64_t)bh * a.G + gi) * DV + row0) * DK;
+            store = false;
+        } else {
+            gin = gi == a.G - 1 ? (a.dS_final ? a.dS_final + ((int64_t)bh * DV + row0) * DK : nullptr)
+                                : a.ws_E + (((int64_t)bh * a.G + gi) * DV + row0) * DK;
+            gout = gi == 0 && a.dS0 ? a.dS0 + ((int64_t)bh * DV + row0) * DK : nullptr;
+        }
     } else {
-        tok0 = (int64_t)rank * a.T;
-        len = a.T;
-        su = u;
-        slot0 = (int64_t)u * a.NC;
+        rank = u / a.H;
+        h = u - rank * a.H;
+        if (a.cu_seqlens) {
+            const int n = a.seq_order ? a.seq_order[rank] : rank;
+            tok0 = a.cu_seqlens[n];
+            len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+            su = (int64_t)n * a.H + h;
+            slot0 = (int64_t)a.chunk_base[n] * a.H + (int64_t)h * ((len + kChunk - 1) / kChunk);
+        } else {
+            tok0 = (int64_t)rank * a.T;
+            len = a.T;
+            su = u;
+            slot0 = (int64_t)u * a.NC;
+        }
+        gin = a.dS_final ? a.dS_final + (su * DV + row0) * DK : nullptr;
+        gout = a.dS0 ? a.dS0 + (su * DV + row0) * DK : nullptr;
     }
     const int NC = (len + kChunk - 1) / kChunk;
     const int64_t sqk = (int64_t)a.H * DK, sv = (int64_t)a.H * DV;
@@ -1080,9 +1114,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
     bf16x4 Sraw[NMT];
 #pragma unroll
     for (int m = 0; m < NMT; ++m)
-        dSacc[m] = a.dS_final ? *reinterpret_cast<const f32x4 *>(a.dS_final + (su * DV + row0 + 16 * w + c16) * DK +
-                                                                 16 * m + 4 * g)
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
+        dSacc[m] = gin ? *reinterpret_cast<const f32x4 *>(gin + (16 * w + c16) * DK + 16 * m + 4 * g)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i = tid; i < kChunk * LT; i += kThreads) Ps[i] = TR::fromf(0.f); // only P's lower blocks are written
 
     // HBM loads of chunk c (K, Q, V, beta, dO and the state entering it) into
@@ -1262,7 +1295,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int tok = 16 * t + 4 * g + i;
                 dYs[tok * LT + 16 * w + c16] = ysb[i];
-                if (tok < nval) dVg[((int64_t)r * kChunk + tok) * sv + 16 * w + c16] = yb[i];
+                if (store && tok < nval) dVg[((int64_t)r * kChunk + tok) * sv + 16 * w + c16] = yb[i];
             }
         }
         // dS <- dS' + dO^T Q - dY^T K (gated: exp(gamma_C) dS' + (diag(exp(gamma)) dO)^T Q
@@ -1282,81 +1315,83 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(const BwdArgs a) {
         }
         __syncthreads(); // Y, Z, dZ, dY tiles complete
 
-        // Sums over this tile's 64 value rows, token rows 16w .. 16w + 15 per wave,
-        // stored in accumulator order: one 16-byte piece per (wave, column
-        // block, lane), so every store (and the finishing kernel's load) of a
-        // wave moves 1 KB of contiguous memory.
-        E *pb = reinterpret_cast<E *>(a.part + ((int64_t)tau * a.max_slots + slot0 + r) * bwd_part_bytes(DK));
+        if (store) { // context-parallel affine runs need only the gradient at the group's start
+            // Sums over this tile's 64 value rows, token rows 16w .. 16w + 15 per wave,
+            // stored in accumulator order: one 16-byte piece per (wave, column
+            // block, lane), so every store (and the finishing kernel's load) of a
+            // wave moves 1 KB of contiguous memory.
+            E *pb = reinterpret_cast<E *>(a.part + ((int64_t)tau * a.max_slots + slot0 + r) * bwd_part_bytes(DK));
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-            if (s2 > w) break; // dP and dT are lower-inclusive: tiles right of the diagonal are zero
-            f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dt = {0.f, 0.f, 0.f, 0.f};
+            for (int s2 = 0; s2 < 4; ++s2) {
+                if (s2 > w) break; // dP and dT are lower-inclusive: tiles right of the diagonal are zero
+                f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
-                dp = TR::mma32(dp, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), ldrow(Ds, L::V, 16 * w + c16, 16 * kv + 16, g),
-                               ldrow(Zs, LT, 16 * s2 + c16, 16 * kv, g), ldrow(Zs, LT, 16 * s2 + c16, 16 * kv + 16, g));
-                dt = TR::mma32(dt, ldrow(dZs, LT, 16 * w + c16, 16 * kv, g), ldrow(dZs, LT, 16 * w + c16, 16 * kv + 16, g),
-                               ldrow(Ys, LT, 16 * s2 + c16, 16 * kv, g), ldrow(Ys, LT, 16 * s2 + c16, 16 * kv + 16, g));
+                for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
+                    dp = TR::mma32(dp, ldrow(Ds, L::V, 16 * w + c16, 16 * kv, g), ldrow(Ds, L::V, 16 * w + c16, 16 * kv + 16, g),
+                                   ldrow(Zs, LT, 16 * s2 + c16, 16 * kv, g), ldrow(Zs, LT, 16 * s2 + c16, 16 * kv + 16, g));
+                    dt = TR::mma32(dt, ldrow(dZs, LT, 16 * w + c16, 16 * kv, g), ldrow(dZs, LT, 16 * w + c16, 16 * kv + 16, g),
+                                   ldrow(Ys, LT, 16 * s2 + c16, 16 * kv, g), ldrow(Ys, LT, 16 * s2 + c16, 16 * kv + 16, g));
+                }
+                *reinterpret_cast<bf16x4 *>(pb + ((w * 4 + s2) * 64 + lane) * 4) = TR::cvt(dp);
+                *reinterpret_cast<bf16x4 *>(pb + 4096 + ((w * 4 + s2) * 64 + lane) * 4) = TR::cvt(dt);
             }
-            *reinterpret_cast<bf16x4 *>(pb + ((w * 4 + s2) * 64 + lane) * 4) = TR::cvt(dp);
-            *reinterpret_cast<bf16x4 *>(pb + 4096 + ((w * 4 + s2) * 64 + lane) * 4) = TR::cvt(dt);
-        }
-        // gated: k . a and k . b per token (a = the Z dS' rows scaled by
-        // exp(gamma_C - gamma), b = the dY S rows scaled by exp(gamma))
-        f32x4 ska = {0.f, 0.f, 0.f, 0.f}, skb = {0.f, 0.f, 0.f, 0.f};
-        f32x4 ezw = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (GATED) {
-            const f32x4 gq = *reinterpret_cast<const f32x4 *>(Gs + 16 * w + 4 * g);
+            // gated: k . a and k . b per token (a = the Z dS' rows scaled by
+            // exp(gamma_C - gamma), b = the dY S rows scaled by exp(gamma))
+            f32x4 ska = {0.f, 0.f, 0.f, 0.f}, skb = {0.f, 0.f, 0.f, 0.f};
+            f32x4 ezw = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (GATED) {
+                const f32x4 gq = *reinterpret_cast<const f32x4 *>(Gs + 16 * w + 4 * g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ezw[i] = __builtin_amdgcn_exp2f(gC - gq[i]);
-        }
+                for (int i = 0; i < 4; ++i) ezw[i] = __builtin_amdgcn_exp2f(gC - gq[i]);
+            }
 #pragma unroll
-        for (int m = 0; m < NMT; ++m) {
-            f32x4 dq = {0.f, 0.f, 0.f, 0.f}, dk1 = {0.f, 0.f, 0.f, 0.f}, dk2 = {0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < NMT; ++m) {
+                f32x4 dq = {0.f, 0.f, 0.f, 0.f}, dk1 = {0.f, 0.f, 0.f, 0.f}, dk2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
-                const F s0 = TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16), s1 = TR::ldcol(Ss, L::K, 16 * kv + 16, 16 * m, g, c16);
-                dq = TR::mma32(dq, ldrow(Dgs, L::V, 16 * w + c16, 16 * kv, g), ldrow(Dgs, L::V, 16 * w + c16, 16 * kv + 16, g),
-                               s0, s1);
-                dk1 = TR::mma32(dk1, ldrow(Zs, LT, 16 * w + c16, 16 * kv, g), ldrow(Zs, LT, 16 * w + c16, 16 * kv + 16, g),
-                                TR::ldcol(Rs, L::K, 16 * kv, 16 * m, g, c16), TR::ldcol(Rs, L::K, 16 * kv + 16, 16 * m, g, c16));
-                dk2 = TR::mma32(dk2, ldrow(dYs, LT, 16 * w + c16, 16 * kv, g), ldrow(dYs, LT, 16 * w + c16, 16 * kv + 16, g),
-                                s0, s1);
+                for (int kv = 0; kv < 4; kv += 2) { // 16x16x32 products over value blocks kv, kv + 1
+                    const F s0 = TR::ldcol(Ss, L::K, 16 * kv, 16 * m, g, c16), s1 = TR::ldcol(Ss, L::K, 16 * kv + 16, 16 * m, g, c16);
+                    dq = TR::mma32(dq, ldrow(Dgs, L::V, 16 * w + c16, 16 * kv, g), ldrow(Dgs, L::V, 16 * w + c16, 16 * kv + 16, g),
+                                   s0, s1);
+                    dk1 = TR::mma32(dk1, ldrow(Zs, LT, 16 * w + c16, 16 * kv, g), ldrow(Zs, LT, 16 * w + c16, 16 * kv + 16, g),
+                                    TR::ldcol(Rs, L::K, 16 * kv, 16 * m, g, c16), TR::ldcol(Rs, L::K, 16 * kv + 16, 16 * m, g, c16));
+                    dk2 = TR::mma32(dk2, ldrow(dYs, LT, 16 * w + c16, 16 * kv, g), ldrow(dYs, LT, 16 * w + c16, 16 * kv + 16, g),
+                                    s0, s1);
+                }
+                if constexpr (GATED) {
+                    dk1 *= ezw;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float kk = (float)Ks[(16 * w + 4 * g + i) * L::K + 16 * m + c16];
+                        ska[i] += kk * dk1[i];
+                        skb[i] += kk * dk2[i];
+                    }
+                }
+                *reinterpret_cast<bf16x4 *>(pb + 8192 + ((w * NMT + m) * 64 + lane) * 4) = TR::cvt(dq);
+                *reinterpret_cast<bf16x4 *>(pb + 8192 + 64 * DK + ((w * NMT + m) * 64 + lane) * 4) = TR::cvt(dk1 - dk2);
             }
             if constexpr (GATED) {
-                dk1 *= ezw;
+                float *px = reinterpret_cast<float *>(pb + bwd_part_elems(DK));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float kk = (float)Ks[(16 * w + 4 * g + i) * L::K + 16 * m + c16];
-                    ska[i] += kk * dk1[i];
-                    skb[i] += kk * dk2[i];
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) {
+                        ska[i] += __shfl_xor(ska[i], o, 16);
+                        skb[i] += __shfl_xor(skb[i], o, 16);
+                    }
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) sdot += __shfl_xor(sdot, o, 64);
+                if (c16 == 0) {
+                    *reinterpret_cast<f32x4 *>(px + 16 * w + 4 * g) = ska;
+                    *reinterpret_cast<f32x4 *>(px + 64 + 16 * w + 4 * g) = skb;
                 }
+                if (lane == 0) px[128 + w] = eC * sdot;
             }
-            *reinterpret_cast<bf16x4 *>(pb + 8192 + ((w * NMT + m) * 64 + lane) * 4) = TR::cvt(dq);
-            *reinterpret_cast<bf16x4 *>(pb + 8192 + 64 * DK + ((w * NMT + m) * 64 + lane) * 4) = TR::cvt(dk1 - dk2);
-        }
-        if constexpr (GATED) {
-            float *px = reinterpret_cast<float *>(pb + bwd_part_elems(DK));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    ska[i] += __shfl_xor(ska[i], o, 16);
-                    skb[i] += __shfl_xor(skb[i], o, 16);
-                }
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) sdot += __shfl_xor(sdot, o, 64);
-            if (c16 == 0) {
-                *reinterpret_cast<f32x4 *>(px + 16 * w + 4 * g) = ska;
-                *reinterpret_cast<f32x4 *>(px + 64 + 16 * w + 4 * g) = skb;
-            }
-            if (lane == 0) px[128 + w] = eC * sdot;
         }
     }
-    if (a.dS0) {
+    if (gout) {
 #pragma unroll
         for (int m = 0; m < NMT; ++m)
-            *reinterpret_cast<f32x4 *>(a.dS0 + (su * DV + row0 + 16 * w + c16) * DK + 16 * m + 4 * g) = dSacc[m];
+            *reinterpret_cast<f32x4 *>(gout + (16 * w + c16) * DK + 16 * m + 4 * g) = dSacc[m];
     }
 }
 
@@ -2224,7 +2259,7 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 }
 
 template <int DK, int DV> hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t s) {
-    const int units = a.B * a.H;
+    const int units = a.B * a.H * (a.rev_kind == kRevChain ? 1 : a.rev_kind == kRevCpAffine ? a.G - 1 : a.G);
     if (units <= 0 || (!a.cu_seqlens && a.NC <= 0)) return hipSuccess; // varlen: empty sequences still set dS0
     const dim3 cg(units * a.n_tiles);
     if (a.nh > 1)
@@ -2233,7 +2268,7 @@ template <int DK, int DV> hipError_t launch_bwd_dims(const BwdArgs &a, hipStream
         hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, true, false>), cg, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.max_slots <= 0) return hipSuccess;
+    if (a.max_slots <= 0 || a.rev_kind == kRevCpAffine) return hipSuccess; // affine runs write no partial sums
     const dim3 fg((unsigned)a.max_slots);
     if (a.nh > 1)
         hipLaunchKernelGGL((bwd_finish_kernel<DK, DV, true, true>), fg, dim3(kThreads), 0, s, a);

@@ -343,6 +343,22 @@ int deltanet_gated_bwd(const void *q, const void *k, const void *v, const void *
 size_t deltanet_gated_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
 
 /*
+ * deltanet_gated_bwd with context parallelism, as deltanet_bwd_cp is to
+ * deltanet_bwd: the decayed group map S -> S P_g + Q_g is still affine, so the
+ * reverse chain over a group is affine in the gradient at its end with the
+ * same P_g^T. Arguments as deltanet_gated_bwd plus cp_groups (1 serial, 0 the
+ * library's choice); workspace: at least deltanet_gated_bwd_cp_workspace_bytes.
+ */
+int deltanet_gated_bwd_cp(const void *q, const void *k, const void *v, const void *beta,
+                          const float *g, const float *S0, const void *dO, const float *dS_final,
+                          void *dq, void *dk, void *dv, void *dbeta, float *dg, float *dS0, int B,
+                          int H, int T, int dk_, int dv_, int chunk, int dtype, int cp_groups,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace deltanet_gated_bwd_cp needs for cp_groups (0 for invalid shapes). */
+size_t deltanet_gated_bwd_cp_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int cp_groups);
+
+/*
  * deltanet_gated_bwd over a packed batch (layouts as in deltanet_bwd_varlen;
  * g, dg [total_T, H] fp32). Workspace: at least
  * deltanet_gated_bwd_varlen_workspace_bytes(...) bytes, 16-byte aligned.

@@ -113,10 +113,10 @@ void fwd_varlen(const std::vector<int> &lens, int H, int dk, int dv, int dtype, 
     expect(st, DN_OK, what);
 }
 
-// mode 0 DeltaNet, 1 gated, 2 GDP (nh substeps), 3 DeltaNet with context
-// parallelism (nh: the group count, 0 automatic)
+// mode 0 DeltaNet, 1 gated, 2 GDP (nh substeps), 3 DeltaNet and 4 gated with
+// context parallelism (nh: the group count, 0 automatic)
 void bwd_dense(int B, int H, int T, int dk, int dv, int mode, int nh = 1) {
-    const size_t real = (size_t)B * T, steps = mode == 3 ? real : real * nh;
+    const size_t real = (size_t)B * T, steps = mode >= 3 ? real : real * nh;
     Buf q(real * H * dk * 2), k(steps * H * dk * 2), v(steps * H * dv * 2), beta(steps * H * 2), dO(real * H * dv * 2);
     Buf dq(real * H * dk * 2), dk_(steps * H * dk * 2), dv_(steps * H * dv * 2), db(steps * H * 2);
     Buf g(real * H * 4), dg(real * H * 4);
@@ -134,6 +134,12 @@ void bwd_dense(int B, int H, int T, int dk, int dv, int mode, int nh = 1) {
         st = deltanet_gated_bwd(q.p, k.p, v.p, beta.p, g.as<float>(), S0.as<float>(), dO.p, dSf.as<float>(), dq.p,
                                 dk_.p, dv_.p, db.p, dg.as<float>(), dS0.as<float>(), B, H, T, dk, dv, 64, DN_BF16,
                                 ws.p, need, nullptr);
+    } else if (mode == 4) {
+        need = deltanet_gated_bwd_cp_workspace_bytes(B, H, T, dk, dv, 64, nh);
+        Buf ws(need);
+        st = deltanet_gated_bwd_cp(q.p, k.p, v.p, beta.p, g.as<float>(), S0.as<float>(), dO.p, dSf.as<float>(), dq.p,
+                                   dk_.p, dv_.p, db.p, dg.as<float>(), dS0.as<float>(), B, H, T, dk, dv, 64, DN_BF16, nh,
+                                   ws.p, need, nullptr);
     } else if (mode == 3) {
         need = deltanet_bwd_cp_workspace_bytes(B, H, T, dk, dv, 64, nh);
         Buf ws(need);
@@ -243,6 +249,7 @@ int main() {
             bwd_dense(1, 2, 0, dk, dv, 0);
             bwd_dense(2, 3, 700, dk, dv, 3, 4);
             bwd_dense(1, 2, 1100, dk, dv, 3, 0);
+            bwd_dense(2, 3, 700, dk, dv, 4, 4);
             bwd_varlen({0, 1, 64, 65, 190}, 2, dk, dv, false);
             bwd_varlen({3, 128, 77}, 2, dk, dv, true);
             for (int mode = 0; mode < 3; ++mode) decode(3, 2, dk, dv, DN_BF16, mode);

@@ -191,6 +191,11 @@ hipError_t launch_bwd(int dk, int dv, const BwdArgs &b, hipStream_t) {
     }
     rd(b.S_chunks16, slots * dv * dk * 2);
     rd(b.T_chunks, slots * kChunk * kChunk * 2);
+    if (b.rev_kind == kRevCpAffine) { // the group-start gradients C_g of groups 1..G-1 only
+        wr(b.ws_C + units * dv * dk, units * (b.G - 1) * dv * dk * 4);
+        return hipSuccess;
+    }
+    if (b.rev_kind == kRevCpRun) rd(b.ws_E, units * (b.G - 1) * dv * dk * 4);
     wr(b.part, (size_t)b.n_tiles * slots * bwd_part_bytes(dk));
     wr(b.dq, real * b.H * dk * 2);
     wr(b.dk, steps * b.H * dk * 2);

@@ -368,7 +368,12 @@ def test_bwd_cp_workspace_sizes(lib):
         assert G > 1
         assert dn.deltanet_bwd_cp_workspace_bytes(1, 2, 131072, dk, dv, 64, 0) == \
             dn.deltanet_bwd_workspace_bytes(1, 2, 131072, dk, dv) + 2 * G * (dk * dk + 2 * dv * dk) * 4
+        gated = dn.deltanet_gated_bwd_workspace_bytes(2, 3, 1000, dk, dv)
+        assert dn.deltanet_gated_bwd_cp_workspace_bytes(2, 3, 1000, dk, dv, 64, 1) == gated
+        assert dn.deltanet_gated_bwd_cp_workspace_bytes(2, 3, 1000, dk, dv, 64, 4) == gated + 2 * 3 * 4 * (
+            dk * dk + 2 * dv * dk) * 4
     assert lib.deltanet_bwd_cp_workspace_bytes(2, 3, 1000, 128, 128, 64, -1) == 0
+    assert lib.deltanet_gated_bwd_cp_workspace_bytes(2, 3, 1000, 128, 128, 64, -1) == 0
     assert lib.deltanet_bwd_cp_workspace_bytes(2, 3, 1000, 96, 128, 64, 2) == 0
 
 

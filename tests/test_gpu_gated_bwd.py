@@ -6,7 +6,9 @@ no-decay reduction and the pure-decay closed form; the library runs the same
 three passes as the ungated backward with the decay factors applied. Cases:
 every (dk, dv), ragged lengths and chunk boundaries, strong and mild decay,
 initial state and final-state gradient present or absent, no decay against
-the ungated backward, the empty sequence, and packed sequences. Metric:
+the ungated backward, the empty sequence, packed sequences, and the
+context-parallel backward (deltanet_gated_bwd_cp) over several group counts
+and decay strengths. Metric:
 max|gpu - oracle| / max|oracle| per gradient tensor.
 """
 
@@ -26,15 +28,16 @@ TOL_BWD = 2e-2  # as for the ungated backward
 NAMES = ("dq", "dk", "dv", "dbeta", "dg", "dS0")
 
 
-def run_gbwd(B, H, T, dk, dv, seed, s0=True, dsf=True, mu=2.0):
-    print(f"[case] gated bwd B={B} H={H} T={T} dk={dk} dv={dv} s0={s0} dSf={dsf} mu={mu}", flush=True)
+def run_gbwd(B, H, T, dk, dv, seed, s0=True, dsf=True, mu=2.0, cp_groups=1):
+    print(f"[case] gated bwd B={B} H={H} T={T} dk={dk} dv={dv} s0={s0} dSf={dsf} mu={mu} cp={cp_groups}", flush=True)
     q, k, v, beta, S0 = make_inputs(B, H, T, dk, dv, seed=seed, s0_std=0.3 if s0 else 0.0)
     gl = make_gates((B, T, H), seed=seed + 2, mu=mu)
     gen = torch.Generator().manual_seed(seed + 1)
     dO = torch.randn(v.shape, generator=gen).to(torch.bfloat16)
     dSf = torch.randn((B, H, dv, dk), generator=gen) * 0.1 if dsf else None
     d = [x.to(DEV) for x in (q, k, v, beta, gl, dO)]
-    out = deltanet_gated_bwd(*d, None if S0 is None else S0.to(DEV), None if dSf is None else dSf.to(DEV))
+    out = deltanet_gated_bwd(*d, None if S0 is None else S0.to(DEV), None if dSf is None else dSf.to(DEV),
+                             cp_groups=cp_groups)
     torch.cuda.synchronize()
     ref = oracle.gated_deltanet_bwd(f64(q), f64(k), f64(v), f64(beta), f64(gl), f64(dO), f64(S0), f64(dSf))
     errs = [rel_err(f64(x), r) for x, r in zip(out, ref)]
@@ -59,6 +62,19 @@ def test_gated_bwd_decay_strength(mu):
     # mu = -1: a = sigmoid(N(-1, 1)), most tokens keep under half the state;
     # mu = 5: almost no decay
     errs = run_gbwd(1, 2, 256, 128, 128, seed=620, mu=mu)
+    assert max(errs) <= TOL_BWD
+
+
+@pytest.mark.parametrize("dk,dv,G,mu", [(128, 128, 2, 2.0), (128, 128, 5, -1.0), (128, 128, 7, 5.0),
+                                         (64, 64, 3, 2.0), (64, 128, 4, 0.0), (128, 64, 3, -1.0)])
+def test_gated_bwd_context_parallel(dk, dv, G, mu):
+    # deltanet_gated_bwd_cp: the chains split into G groups (ragged last group)
+    errs = run_gbwd(2, 3, 7 * 64 + 21, dk, dv, seed=640 + G + dk, mu=mu, cp_groups=G)
+    assert max(errs) <= TOL_BWD
+
+
+def test_gated_bwd_context_parallel_without_states():
+    errs = run_gbwd(1, 2, 6 * 64 + 1, 128, 128, seed=650, s0=False, dsf=False, cp_groups=6)
     assert max(errs) <= TOL_BWD
 
 
