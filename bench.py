@@ -290,7 +290,7 @@ def kda_long_variant(dev, B=1, H=16, T=131072, d=128, steps=5, warmup=2):
     g = make_channel_gates((B, T, H, d), seed=11, device=str(dev))
     o = torch.empty_like(v)
     Sf = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
-    G = dn.deltanet_pick_cp_groups(B, H, T, d, d, 64)
+    G = 0  # the KDA forward's own choice of group count (the workspace query's covers it)
     ws = torch.empty(max(dn.deltanet_workspace_bytes(B, H, T, d, d, 64, G), 1), dtype=torch.uint8, device=dev)
     out = {"call": "deltanet_kda_fwd", "config": {"B": B, "H": H, "T": T, "dk": d, "dv": d}, "steps": steps,
            "warmup": warmup}
@@ -318,7 +318,7 @@ def bwd_long_variant(dev, B=1, H=16, T=131072, d=128, steps=3, warmup=1):
     q, k, v, beta, S0 = make_inputs(B, H, T, d, d, seed=13, device=str(dev))
     g = torch.Generator(device=dev).manual_seed(14)
     dO = torch.randn(v.shape, generator=g, device=dev, dtype=torch.float32).to(v.dtype)
-    G = dn.deltanet_pick_cp_groups(B, H, T, d, d, 64)
+    G = 0  # the backward's own choice of group count
     ws = torch.empty(max(dn.deltanet_bwd_cp_workspace_bytes(B, H, T, d, d, 64, G), 1), dtype=torch.uint8,
                      device=dev)
     out = {"call": "deltanet_bwd / deltanet_bwd_cp (gated_*: deltanet_gated_bwd / deltanet_gated_bwd_cp)", "config": {"B": B, "H": H, "T": T, "dk": d, "dv": d},

@@ -45,16 +45,26 @@ int device_cus() {
 // those workgroups fill at least half of the compute units, splitting only
 // adds the transition work. Otherwise the chain is cut into enough groups to
 // give every compute unit an output workgroup, keeping at least 8 chunks per
-// group so the per-group transition cost stays amortised.
-int pick_groups(int B, int H, int T, int dv) {
+// group so the per-group transition cost stays amortised. With `lead` (the
+// forward at dk = dv = 128, whose group 0 runs its output chain beside the
+// transitions of the others), groups 1..G-1 take the compute units in the
+// output phase, so there is one group more.
+int pick_groups(int B, int H, int T, int dv, bool lead) {
     const int nc = (T + dn::kChunk - 1) / dn::kChunk;
     const int serial_wgs = B * H * (dv / dn::kRows);
     const int cus = device_cus();
     if (serial_wgs * 2 >= cus || nc < 16) return 1;
     int G = cus / serial_wgs;
+    if (lead && G >= 2) G += 1;
     if (G > nc / 8) G = nc / 8;
     return G < 1 ? 1 : G;
 }
+
+// Whether the dense forward runs group 0 ahead (see fwd_dense): the shapes
+// whose transitions take one 128-row tile each for Q_g and P_g, so that the
+// transitions of groups 1..G-2 and the output chain of group 0 together
+// occupy as many workgroups as the output phase of groups 1..G-1.
+bool fwd_lead_shape(int dk, int dv) { return dk == 128 && dv == 128; }
 
 // State rows per workgroup tile of the bf16 forward with output on the
 // serial chain: 32 when the 32-row grid still fits on the compute units in
@@ -67,9 +77,9 @@ int pick_rows(int dtype, int n_units, int dv) {
 }
 
 // Resolve the requested group count into (G, chunks per group) with no empty group.
-void resolve_groups(int requested, int B, int H, int T, int dv, int &G, int &cpg) {
+void resolve_groups(int requested, int B, int H, int T, int dv, int &G, int &cpg, bool lead = false) {
     const int nc = (T + dn::kChunk - 1) / dn::kChunk;
-    G = requested == 0 ? pick_groups(B, H, T, dv) : requested;
+    G = requested == 0 ? pick_groups(B, H, T, dv, lead) : requested;
     if (G > nc) G = nc;
     if (G < 1) G = 1;
     cpg = nc > 0 ? (nc + G - 1) / G : 1;
@@ -81,6 +91,40 @@ size_t ws_bytes_for(int B, int H, int dk, int dv, int G) {
     return (size_t)B * H * G * ((size_t)dk * dk + 2 * (size_t)dv * dk) * sizeof(float);
 }
 
+// A second stream per device for work that runs beside the caller's stream
+// inside one call, ordered by a fork event recorded on the caller's stream
+// and a join event the caller's stream waits for. Created on first use (at
+// the default priority) and kept until the process ends.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool failed = false;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex side_mu; // guards the table and every fork/join sequence (the events are shared)
+SideStream side_table[kMaxSideDevices];
+
+// The current device's side stream, or nullptr (creation failed, or the
+// caller's stream is being captured: then nothing is created or forked and
+// the work runs on the caller's stream). Called with side_mu held.
+SideStream *side_stream(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+    SideStream &e = side_table[dev];
+    if (e.failed) return nullptr;
+    if (!e.s) {
+        if (hipStreamCreateWithFlags(&e.s, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&e.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&e.join, hipEventDisableTiming) != hipSuccess) {
+            e.failed = true; // what was created stays; the caller's stream serves from now on
+            return nullptr;
+        }
+    }
+    return &e;
+}
+
 } // namespace
 
 namespace dn {
@@ -90,7 +134,7 @@ namespace dn {
 // otherwise), so q, g and o hold T / nh real tokens per sequence.
 int fwd_dense(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
               void *o, float *S_final, int B, int H, int T, int nh, int dk, int dv, int chunk, int dtype,
-              int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+              int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream, bool allow_side) {
     int st = check_shape(dk, dv, chunk, dtype);
     if (st != DN_OK) return st;
     if (B <= 0 || H <= 0 || T < 0 || cp_groups < 0) return DN_ERR_INVALID;
@@ -105,7 +149,7 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
     if ((int64_t)B * H > (int64_t)1 << 24) return DN_ERR_UNSUPPORTED;
 
     int G, cpg;
-    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    resolve_groups(cp_groups, B, H, T, dv, G, cpg, fwd_lead_shape(dk, dv));
     const size_t need = ws_bytes_for(B, H, dk, dv, G);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return DN_ERR_WORKSPACE;
@@ -139,22 +183,61 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
     a.ws_S = a.ws_Q + per * dv * dk;
     a.G = G;
     a.chunks_per_group = cpg;
-    // (i) group transitions for groups 0..G-2: at dk = dv = 128 without decay,
-    // one 128-row tile for Q_g and one for P_g (the chunk's Gram tiles,
-    // inverses and T formed once per 128 state rows); else 64-row tiles
+    // Group 0 starts from S0, which is known: at dk = dv = 128 with three or
+    // more groups it runs its output chain (writing the start state of group
+    // 1) beside the transitions of groups 1..G-2, on the compute units those
+    // leave free, and the output phase covers groups 1..G-1 only.
+    const bool lead = dtype == DN_BF16 && fwd_lead_shape(dk, dv) && G >= 3;
+    const int first = lead ? 1 : 0;
+    dn::ChainArgs a0 = a;
+    if (lead) {
+        a0.kind = dn::kCpOutput;
+        a0.cp_first = 0;
+        a0.cp_count = 1;
+        a0.cp_lead = 1;
+        a0.S_final = nullptr;
+        a0.rows = dn::kRows;
+        a0.n_units = B * H;
+        a0.n_tiles = dv / dn::kRows;
+    }
+    // (i) group transitions for groups first..G-2: at dk = dv = 128, one
+    // 128-row tile for Q_g and one for P_g (the chunk's Gram tiles, inverses
+    // and T formed once per 128 state rows); else 64-row tiles
     a.kind = dn::kCpTransition;
-    a.n_units = B * H * (G - 1);
+    a.cp_first = first;
+    a.n_units = B * H * (G - 1 - first);
     a.rows = (dtype == DN_BF16 && dk == 128 && dv == 128) ? 128 : dn::kRows;
     a.n_tiles = dv / a.rows + dk / a.rows;
-    err = dn::launch_chain(dtype, dk, dv, false, a, stream);
+    if (lead) {
+        std::lock_guard<std::mutex> lock(side_mu);
+        SideStream *sd = allow_side ? side_stream(stream) : nullptr;
+        if (sd) {
+            // the transitions (the shorter of the two) go to the second stream,
+            // whose start waits for the fork event: the output chain of group 0
+            // starts at once on the caller's stream, and the join event is
+            // usually complete by the time the caller's stream reaches it
+            if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
+                return DN_ERR_HIP;
+            const hipError_t e1 = dn::launch_chain(dtype, dk, dv, false, a, sd->s);
+            if (hipEventRecord(sd->join, sd->s) != hipSuccess) return DN_ERR_HIP;
+            err = dn::launch_chain(dtype, dk, dv, true, a0, stream);
+            if (hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess || e1 != hipSuccess) return DN_ERR_HIP;
+        } else {
+            err = dn::launch_chain(dtype, dk, dv, true, a0, stream);
+            if (err == hipSuccess) err = dn::launch_chain(dtype, dk, dv, false, a, stream);
+        }
+    } else {
+        err = dn::launch_chain(dtype, dk, dv, false, a, stream);
+    }
     if (err != hipSuccess) return DN_ERR_HIP;
-    // (ii) prefix composition of the maps -> start states of groups 1..G-1
+    // (ii) prefix composition of the maps -> start states of groups first+1..G-1
     err = dn::launch_compose(dk, dv, a, stream);
     if (err != hipSuccess) return DN_ERR_HIP;
-    // (iii) every group from its start state, writing o (and S_final from the last group)
+    // (iii) every group from first on from its start state, writing o (and
+    // S_final from the last group)
     a.kind = dn::kCpOutput;
     a.rows = dn::kRows;
-    a.n_units = B * H * G;
+    a.n_units = B * H * (G - first);
     a.n_tiles = dv / dn::kRows;
     err = dn::launch_chain(dtype, dk, dv, true, a, stream);
     return err == hipSuccess ? DN_OK : DN_ERR_HIP;
@@ -437,7 +520,7 @@ int deltanet_pick_cp_groups(int B, int H, int T, int dk, int dv, int chunk) {
     if (st != DN_OK && check_shape(dk, dv, chunk, DN_F32) != DN_OK) return st;
     if (B <= 0 || H <= 0 || T < 0) return DN_ERR_INVALID;
     int G, cpg;
-    resolve_groups(0, B, H, T, dv, G, cpg);
+    resolve_groups(0, B, H, T, dv, G, cpg, fwd_lead_shape(dk, dv));
     return G;
 }
 
@@ -446,7 +529,7 @@ size_t deltanet_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, 
     if (check_shape(dk, dv, chunk, DN_BF16) != DN_OK && check_shape(dk, dv, chunk, DN_F32) != DN_OK)
         return 0;
     int G, cpg;
-    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    resolve_groups(cp_groups, B, H, T, dv, G, cpg, fwd_lead_shape(dk, dv));
     return ws_bytes_for(B, H, dk, dv, G);
 }
 
@@ -454,7 +537,7 @@ int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta, 
                  void *o, float *S_final, int B, int H, int T, int dk, int dv, int chunk, int dtype,
                  int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return fwd_dense(q, k, v, beta, nullptr, S0, o, S_final, B, H, T, 1, dk, dv, chunk, dtype, cp_groups, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, stream, true);
 }
 
 int deltanet_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
@@ -471,7 +554,7 @@ int deltanet_gated_fwd(const void *q, const void *k, const void *v, const void *
                        hipStream_t stream) {
     if (T > 0 && !g) return DN_ERR_INVALID;
     return fwd_dense(q, k, v, beta, g, S0, o, S_final, B, H, T, 1, dk, dv, chunk, dtype, cp_groups, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, stream, true);
 }
 
 int deltanet_gdp_fwd(const void *q, const void *k, const void *v, const void *beta, const float *g,
@@ -482,7 +565,7 @@ int deltanet_gdp_fwd(const void *q, const void *k, const void *v, const void *be
     if ((int64_t)T * n_h > INT32_MAX / 2) return DN_ERR_UNSUPPORTED;
     if (T > 0 && !g) return DN_ERR_INVALID;
     return fwd_dense(q, k, v, beta, g, S0, o, S_final, B, H, T * n_h, n_h, dk, dv, chunk, dtype, cp_groups,
-                     workspace, workspace_bytes, stream);
+                     workspace, workspace_bytes, stream, true);
 }
 
 int deltanet_gated_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,

@@ -52,6 +52,13 @@ struct ChainArgs {
     int n_tiles; // state tiles per unit
     int cp_trans_groups; // groups 0..cp_trans_groups-1 get a transition (kCpTransition); 0 reads
                          // as G - 1 (the forward pass; the backward's needs all G)
+    int cp_first; // first group of a context-parallel launch (transitions, outputs and the
+                  // composition start there; the composition then reads the start state of
+                  // that group from ws_S); 0 otherwise
+    int cp_count; // kCpOutput: groups cp_first..cp_first+cp_count-1; 0 reads as the rest
+    int cp_lead;  // kCpOutput: every group but the last also writes its end state into the
+                  // start-state slot of the next group in ws_S (group 0 run ahead of the
+                  // transitions); 0 otherwise
     int rows;    // state rows per tile of the bf16 chain kernel: 64, or 32 (forward with
                  // output, dense and packed kinds, when the 32-row grid fits on the compute
                  // units in one round), or 128 (context-parallel transitions at dk = dv =
@@ -156,7 +163,7 @@ hipError_t launch_chain_bf16(int dk, int dv, bool write_o, const ChainArgs &a, h
 // DN_* status of include/deltanet.h.
 int fwd_dense(const void *q, const void *k, const void *v, const void *beta, const float *g, const float *S0,
               void *o, float *S_final, int B, int H, int T, int nh, int dk, int dv, int chunk, int dtype,
-              int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream);
+              int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream, bool allow_side);
 
 // Enqueue the prefix composition S_{g+1} = S_g P_g + Q_g for g = 0..G-2,
 // writing start states of groups 1..G-1 into ws_S.

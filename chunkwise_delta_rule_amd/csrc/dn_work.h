@@ -71,9 +71,10 @@ template <int DK, int DV, int ROWS = kRows> __device__ inline Work decode_work(c
             if (a.T_chunks && tau == 0) wk.Tchunks = a.T_chunks + slot0 * kChunk * kChunk;
         }
     } else {
-        const int groups = (a.kind == kCpOutput) ? a.G : (a.cp_trans_groups > 0 ? a.cp_trans_groups : a.G - 1);
+        const int groups = a.kind == kCpOutput ? (a.cp_count > 0 ? a.cp_count : a.G - a.cp_first)
+                                               : (a.cp_trans_groups > 0 ? a.cp_trans_groups : a.G - 1 - a.cp_first);
         const int bh = u / groups;
-        const int gi = u - bh * groups;
+        const int gi = u - bh * groups + a.cp_first;
         const int b = bh / H;
         wk.h = bh - b * H;
         const int t_begin = gi * a.chunks_per_group * kChunk;
@@ -87,7 +88,11 @@ template <int DK, int DV, int ROWS = kRows> __device__ inline Work decode_work(c
             } else {
                 wk.Sin = a.ws_S + (slot * DV + wk.row0) * DK;
             }
-            if (gi == a.G - 1 && a.S_final) wk.Sout = a.S_final + ((int64_t)bh * DV + wk.row0) * DK;
+            if (gi == a.G - 1) {
+                if (a.S_final) wk.Sout = a.S_final + ((int64_t)bh * DV + wk.row0) * DK;
+            } else if (a.cp_lead) {
+                wk.Sout = a.ws_S + ((slot + 1) * DV + wk.row0) * DK; // the next group's start
+            }
             if (a.S_chunks16) { // the backward's forward pass: the group's chunk slots of unit bh
                 const int64_t slot0 = (int64_t)bh * ((a.T + kChunk - 1) / kChunk) + (int64_t)gi * a.chunks_per_group;
                 wk.Schunks16 = a.S_chunks16 + (slot0 * DV + wk.row0) * DK;

@@ -814,8 +814,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel_serial(const ChainArgs 
 }
 
 // Prefix composition of the group maps for one (b, h) and 16 state rows:
-//   S_{g+1} = S_g P_g + Q_g,  g = 0..G-2,  S_0 = S0 (or zero);
-// writes S_1..S_{G-1} to ws_S. fp32 throughout (fp32 matrix cores). Wave w
+//   S_{g+1} = S_g P_g + Q_g,  g = f..G-2,  S_0 = S0 (or zero),
+// with f = cp_first (S_f read from ws_S when f > 0: the end state of a group
+// that ran its chain ahead of the transitions); writes S_{f+1}..S_{G-1} to ws_S. fp32 throughout (fp32 matrix cores). Wave w
 // of DK/16 computes output column tile w, with the contraction split over two
 // accumulators (even and odd 16-blocks) so that the dependent product chain
 // is half as long; the 16 rows of S are exchanged through LDS between steps.
@@ -830,9 +831,13 @@ __global__ __launch_bounds__(64 * (DK / 16)) void compose_kernel(const ChainArgs
     const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     const int rb = blockIdx.x % (DV / 16);
     const int bh = blockIdx.x / (DV / 16);
+    const int f = a.cp_first;
+    const float *Sf = f > 0  ? a.ws_S + ((int64_t)bh * a.G + f) * DV * DK
+                      : a.S0 ? a.S0 + (int64_t)bh * DV * DK
+                             : nullptr;
     for (int idx = tid; idx < 16 * DK; idx += NT) {
         const int r = idx / DK, col = idx - r * DK;
-        Sl[r * LDS_ + col] = a.S0 ? a.S0[((int64_t)bh * DV + 16 * rb + r) * DK + col] : 0.f;
+        Sl[r * LDS_ + col] = Sf ? Sf[(16 * rb + r) * DK + col] : 0.f;
     }
     // p[kk] = P_g^T[16 w + c16][16 kk + 4 g ..], q = Q_g[16 rb + c16][16 w + 4 g ..]; three
     // register sets, step g in set g % 3, so the loads of step g + 2 go into the
@@ -868,10 +873,10 @@ __global__ __launch_bounds__(64 * (DK / 16)) void compose_kernel(const ChainArgs
         *reinterpret_cast<f32x4 *>(Sn + c16 * DK + 16 * w + 4 * g) = acc;
         __syncthreads();
     };
-    if (a.G > 1) load(0, P0, Q0);
-    if (a.G > 2) load(1, P1, Q1);
+    if (a.G > f + 1) load(f, P0, Q0);
+    if (a.G > f + 2) load(f + 1, P1, Q1);
     __syncthreads();
-    for (int gi = 0; gi + 1 < a.G; gi += 3) {
+    for (int gi = f; gi + 1 < a.G; gi += 3) {
         step(gi, P0, Q0, P2, Q2);
         if (gi + 2 < a.G) step(gi + 1, P1, Q1, P0, Q0);
         if (gi + 3 < a.G) step(gi + 2, P2, Q2, P1, Q1);
@@ -2338,7 +2343,7 @@ hipError_t launch_compose_bwd(int dk, int dv, const BwdArgs &a, hipStream_t stre
 
 hipError_t launch_compose(int dk, int dv, const ChainArgs &a, hipStream_t stream) {
     const int grid = a.B * a.H * (dv / 16);
-    if (grid <= 0 || a.G < 2) return hipSuccess;
+    if (grid <= 0 || a.G - a.cp_first < 2) return hipSuccess;
     // one wave per output column tile of 16: 64 dk threads
     if (dk == 128 && dv == 128) hipLaunchKernelGGL((compose_kernel<128, 128>), dim3(grid), dim3(512), 0, stream, a);
     else if (dk == 128 && dv == 64) hipLaunchKernelGGL((compose_kernel<128, 64>), dim3(grid), dim3(512), 0, stream, a);

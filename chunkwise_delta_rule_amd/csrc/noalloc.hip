@@ -55,5 +55,5 @@ extern "C" int deltanet_fwd_noalloc(const void *q, const void *k, const void *v,
         if (!ws) return DN_ERR_HIP;
     }
     return dn::fwd_dense(q, k, v, beta, nullptr, S0, o, S_final, B, H, T, 1, dk, dv, chunk, dtype, cp_groups, ws,
-                         need > 0 ? kScratchBytes : 0, stream);
+                         need > 0 ? kScratchBytes : 0, stream, false);
 }

@@ -274,7 +274,8 @@ size_t deltanet_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chu
 /*
  * deltanet_bwd with the chunk chains split into cp_groups contiguous groups
  * of chunks per sequence (1: serial, as deltanet_bwd; 0: the library's choice,
- * deltanet_pick_cp_groups), for long sequences with few (sequence, head)
+ * deltanet_pick_cp_groups less the forward's extra group at dk = dv = 128),
+ * for long sequences with few (sequence, head)
  * units. Over a group the reverse chain is affine in the gradient at the
  * group's end, dS_start = dS_end P_g^T + C_g, with P_g the group's forward
  * transition ("Context Parallelism for DeltaNet", section 2, the affine group
@@ -426,9 +427,15 @@ size_t deltanet_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
                                 int cp_groups);
 
 /*
- * Group count deltanet_fwd uses when called with cp_groups = 0, for the
- * current HIP device. Returns 1 (serial) when splitting does not pay, or a
- * negative status for invalid shapes.
+ * Group count deltanet_fwd (and deltanet_gated_fwd, deltanet_gdp_fwd) uses
+ * when called with cp_groups = 0, for the current HIP device. Returns 1
+ * (serial) when splitting does not pay, or a negative status for invalid
+ * shapes. At dk = dv = 128 these forwards run group 0, whose start state is
+ * S0, beside the transitions of the other groups (on a second stream of the
+ * library, joined back into the caller's stream before the call's later
+ * work; on the caller's stream itself while it is being captured), so their
+ * choice there holds one group more than the choice of deltanet_kda_fwd and
+ * of the context-parallel backward passes with cp_groups = 0.
  */
 int deltanet_pick_cp_groups(int B, int H, int T, int dk, int dv, int chunk);
 

@@ -63,6 +63,7 @@ void chain_common(int dtype, int dk, int dv, bool write_o, const dn::ChainArgs &
         return;
     }
     if (a.kind == dn::kCpOutput) rd(a.ws_S, units * a.G * dv * dk * 4);
+    if (a.kind == dn::kCpOutput && a.cp_lead) wr(a.ws_S, units * a.G * dv * dk * 4);
     rd(a.S0, a.S0 ? units * dv * dk * 4 : 0);
     if (write_o) wr(a.o, real * a.H * dv * e);
     wr(a.S_final, a.S_final ? units * dv * dk * 4 : 0);
@@ -243,4 +244,23 @@ hipError_t hipMemcpyAsync(void *dst, const void *src, size_t sizeBytes, hipMemcp
     std::memcpy(dst, src, sizeBytes);
     return hipSuccess;
 }
+// the second stream of the context-parallel forward: handles that are never
+// dereferenced, no capture
+static int side_objects[3];
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus *s) {
+    *s = hipStreamCaptureStatusNone;
+    return hipSuccess;
+}
+hipError_t hipStreamCreateWithFlags(hipStream_t *s, unsigned int) {
+    *s = reinterpret_cast<hipStream_t>(&side_objects[0]);
+    return hipSuccess;
+}
+hipError_t hipEventCreateWithFlags(hipEvent_t *e, unsigned int) {
+    static int n = 1;
+    *e = reinterpret_cast<hipEvent_t>(&side_objects[n]);
+    n = n == 1 ? 2 : 1;
+    return hipSuccess;
+}
+hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned int) { return hipSuccess; }
 }
