@@ -56,6 +56,8 @@ struct ChainArgs {
                   // composition start there; the composition then reads the start state of
                   // that group from ws_S); 0 otherwise
     int cp_count; // kCpOutput: groups cp_first..cp_first+cp_count-1; 0 reads as the rest
+    int cp_c0;    // chunks of group 0 (the later groups hold chunks_per_group each, the
+                  // last one the rest); 0 reads as chunks_per_group
     int cp_lead;  // kCpOutput: every group but the last also writes its end state into the
                   // start-state slot of the next group in ws_S (group 0 run ahead of the
                   // transitions); 0 otherwise

@@ -77,8 +77,12 @@ template <int DK, int DV, int ROWS = kRows> __device__ inline Work decode_work(c
         const int gi = u - bh * groups + a.cp_first;
         const int b = bh / H;
         wk.h = bh - b * H;
-        const int t_begin = gi * a.chunks_per_group * kChunk;
-        const int t_end = min(a.T, (gi + 1) * a.chunks_per_group * kChunk);
+        // first chunk of group i: group 0 holds cp_c0 chunks (0: chunks_per_group),
+        // every later group chunks_per_group (the last one the rest)
+        const int c0 = a.cp_c0 > 0 ? a.cp_c0 : a.chunks_per_group;
+        const int gc0 = gi == 0 ? 0 : c0 + (gi - 1) * a.chunks_per_group;
+        const int t_begin = gc0 * kChunk;
+        const int t_end = min(a.T, (gi == 0 ? c0 : gc0 + a.chunks_per_group) * kChunk);
         wk.tok0 = (int64_t)b * a.T + t_begin;
         wk.len = t_end - t_begin;
         const int64_t slot = (int64_t)bh * a.G + gi;
@@ -94,7 +98,7 @@ template <int DK, int DV, int ROWS = kRows> __device__ inline Work decode_work(c
                 wk.Sout = a.ws_S + ((slot + 1) * DV + wk.row0) * DK; // the next group's start
             }
             if (a.S_chunks16) { // the backward's forward pass: the group's chunk slots of unit bh
-                const int64_t slot0 = (int64_t)bh * ((a.T + kChunk - 1) / kChunk) + (int64_t)gi * a.chunks_per_group;
+                const int64_t slot0 = (int64_t)bh * ((a.T + kChunk - 1) / kChunk) + gc0;
                 wk.Schunks16 = a.S_chunks16 + (slot0 * DV + wk.row0) * DK;
                 if (a.T_chunks && tau == 0) wk.Tchunks = a.T_chunks + slot0 * kChunk * kChunk;
             }
