@@ -16,8 +16,9 @@ constexpr int kThreads = 256; // 4 waves of 64; each wave owns 16 state rows
 enum WorkKind : int {
     kDense = 0,        // one unit per (b, h); whole sequence; writes o
     kVarlen = 1,       // one unit per (sequence, h); writes o
-    kCpTransition = 2, // one unit per (b, h, group < G-1); writes P_g^T, Q_g
-    kCpOutput = 3,     // one unit per (b, h, group); starts from the composed state; writes o
+    kCpTransition = 2, // one unit per (b, h, group of the launch's range); writes P_g^T, Q_g
+    kCpOutput = 3,     // one unit per (b, h, group of the launch's range); starts from the
+                       // group's start state; writes o
 };
 
 struct ChainArgs {
@@ -50,8 +51,9 @@ struct ChainArgs {
     int nh;      // substeps per real token (Gated Delta Product; 1 otherwise, gated kernels only)
     int n_units; // units covered by the grid
     int n_tiles; // state tiles per unit
-    int cp_trans_groups; // groups 0..cp_trans_groups-1 get a transition (kCpTransition); 0 reads
-                         // as G - 1 (the forward pass; the backward's needs all G)
+    int cp_trans_groups; // groups cp_first..cp_first+cp_trans_groups-1 get a transition
+                         // (kCpTransition); 0 reads as those up to G - 2 (the forward pass;
+                         // the backward's needs all G)
     int cp_first; // first group of a context-parallel launch (transitions, outputs and the
                   // composition start there; the composition then reads the start state of
                   // that group from ws_S); 0 otherwise
@@ -167,8 +169,9 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
               void *o, float *S_final, int B, int H, int T, int nh, int dk, int dv, int chunk, int dtype,
               int cp_groups, void *workspace, size_t workspace_bytes, hipStream_t stream, bool allow_side);
 
-// Enqueue the prefix composition S_{g+1} = S_g P_g + Q_g for g = 0..G-2,
-// writing start states of groups 1..G-1 into ws_S.
+// Enqueue the prefix composition S_{g+1} = S_g P_g + Q_g for g = f..G-2,
+// f = cp_first (S_0 = S0, or the start state of group f in ws_S when f > 0),
+// writing the start states of groups f+1..G-1 into ws_S.
 hipError_t launch_compose(int dk, int dv, const ChainArgs &a, hipStream_t stream);
 
 } // namespace dn

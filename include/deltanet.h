@@ -107,7 +107,12 @@ enum {
  *                   deltanet_workspace_bytes(...) bytes (may be NULL/0 when the
  *                   resolved group count is 1). Contents are scratch; they need
  *                   no initialisation and are clobbered.
- *   stream        : HIP stream to enqueue on.
+ *   stream        : HIP stream to enqueue on. With context parallelism at
+ *                   dk = dv = 128 (three or more groups) part of the call runs
+ *                   on a second stream the library keeps per device, forked
+ *                   from and joined back into `stream` with events, so the
+ *                   call is still ordered on `stream` alone; while `stream`
+ *                   is being captured everything runs on `stream`.
  * Returns DN_OK or a negative status.
  */
 int deltanet_fwd(const void *q, const void *k, const void *v, const void *beta,
