@@ -12,6 +12,7 @@
 #include <vector>
 
 int stub_launch_count();
+void stub_set_capturing(bool c);
 
 namespace {
 
@@ -227,6 +228,16 @@ void rejected() {
 } // namespace
 
 int main() {
+    // dk = dv = 128: group 0 ahead of the transitions, on two streams and (as
+    // under capture) on one; 18 chunks give group 0 fewer chunks than the
+    // later groups for 3 and 4 groups, and an even split for 9
+    for (bool cap : {false, true}) {
+        stub_set_capturing(cap);
+        for (int cp : {3, 4, 9}) fwd_dense(1, 2, 17 * 64 + 5, 128, 128, DN_BF16, cp, true, true, 0);
+        fwd_dense(1, 2, 17 * 64 + 5, 128, 128, DN_BF16, 4, false, true, 1);
+        fwd_dense(1, 2, 17 * 64 + 5, 128, 128, DN_BF16, 3, true, false, 1, 2);
+    }
+    stub_set_capturing(false);
     for (int dtype : {DN_BF16, DN_F32}) {
         const int dk = 64;
         for (int cp : {1, 0, 2, 3, 7}) fwd_dense(2, 3, 7 * 64 + 20, dk, 128, dtype, cp, true, true, 0);

@@ -95,6 +95,7 @@ void bwd_inputs(int dk, int dv, const dn::BwdArgs &b, size_t &steps, size_t &rea
 } // namespace
 
 int stub_launch_count() { return launches; }
+void stub_set_capturing(bool c);
 
 namespace dn {
 
@@ -245,10 +246,12 @@ hipError_t hipMemcpyAsync(void *dst, const void *src, size_t sizeBytes, hipMemcp
     return hipSuccess;
 }
 // the second stream of the context-parallel forward: handles that are never
-// dereferenced, no capture
+// dereferenced; the caller's stream reads as captured after
+// stub_set_capturing(true), which sends the forward down its one-stream path
 static int side_objects[3];
+static bool stub_capturing = false;
 hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus *s) {
-    *s = hipStreamCaptureStatusNone;
+    *s = stub_capturing ? hipStreamCaptureStatusActive : hipStreamCaptureStatusNone;
     return hipSuccess;
 }
 hipError_t hipStreamCreateWithFlags(hipStream_t *s, unsigned int) {
@@ -264,3 +267,5 @@ hipError_t hipEventCreateWithFlags(hipEvent_t *e, unsigned int) {
 hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned int) { return hipSuccess; }
 }
+
+void stub_set_capturing(bool c) { stub_capturing = c; }
