@@ -125,6 +125,33 @@ SideStream *side_stream(hipStream_t stream) {
     return &e;
 }
 
+// Enqueues launch_lead (group 0 ahead) on `stream` and launch_trans (the
+// transitions of the other groups) beside it: the transitions go to the
+// device's second stream, forked from `stream` by an event (so they follow
+// the caller's earlier work) and joined back into it by another (so the
+// caller's later work follows them). The second stream's start waits for the
+// fork event, a few microseconds, so the longer chain, group 0's, stays on
+// `stream`. Without a second stream (allow_side false, creation failed, or
+// `stream` being captured) both run one after the other on `stream`.
+template <class F0, class F1>
+hipError_t launch_beside(hipStream_t stream, bool allow_side, F0 &&launch_lead, F1 &&launch_trans) {
+    std::lock_guard<std::mutex> lock(side_mu);
+    SideStream *sd = allow_side ? side_stream(stream) : nullptr;
+    if (!sd) {
+        const hipError_t e = launch_lead(stream);
+        return e == hipSuccess ? launch_trans(stream) : e;
+    }
+    hipError_t e = hipEventRecord(sd->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->fork, 0);
+    if (e != hipSuccess) return e;
+    const hipError_t e1 = launch_trans(sd->s);
+    e = hipEventRecord(sd->join, sd->s);
+    if (e != hipSuccess) return e;
+    const hipError_t e0 = launch_lead(stream);
+    e = hipStreamWaitEvent(stream, sd->join, 0);
+    return e != hipSuccess ? e : e1 != hipSuccess ? e1 : e0;
+}
+
 } // namespace
 
 namespace dn {
@@ -223,23 +250,9 @@ int fwd_dense(const void *q, const void *k, const void *v, const void *beta, con
     a.rows = (dtype == DN_BF16 && dk == 128 && dv == 128) ? 128 : dn::kRows;
     a.n_tiles = dv / a.rows + dk / a.rows;
     if (lead) {
-        std::lock_guard<std::mutex> lock(side_mu);
-        SideStream *sd = allow_side ? side_stream(stream) : nullptr;
-        if (sd) {
-            // the transitions (the shorter of the two) go to the second stream,
-            // whose start waits for the fork event: the output chain of group 0
-            // starts at once on the caller's stream, and the join event is
-            // usually complete by the time the caller's stream reaches it
-            if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
-                return DN_ERR_HIP;
-            const hipError_t e1 = dn::launch_chain(dtype, dk, dv, false, a, sd->s);
-            if (hipEventRecord(sd->join, sd->s) != hipSuccess) return DN_ERR_HIP;
-            err = dn::launch_chain(dtype, dk, dv, true, a0, stream);
-            if (hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess || e1 != hipSuccess) return DN_ERR_HIP;
-        } else {
-            err = dn::launch_chain(dtype, dk, dv, true, a0, stream);
-            if (err == hipSuccess) err = dn::launch_chain(dtype, dk, dv, false, a, stream);
-        }
+        err = launch_beside(
+            stream, allow_side, [&](hipStream_t s) { return dn::launch_chain(dtype, dk, dv, true, a0, s); },
+            [&](hipStream_t s) { return dn::launch_chain(dtype, dk, dv, false, a, s); });
     } else {
         err = dn::launch_chain(dtype, dk, dv, false, a, stream);
     }
@@ -606,7 +619,7 @@ int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *be
     }
     if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return DN_ERR_INVALID;
     int G, cpg;
-    resolve_groups(cp_groups, B, H, T, dv, G, cpg);
+    resolve_groups(cp_groups, B, H, T, dv, G, cpg, fwd_lead_shape(dk, dv));
     const size_t need = ws_bytes_for(B, H, dk, dv, G);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return DN_ERR_WORKSPACE;
     if (T == 0) { // no tokens: the final state is the initial one
@@ -647,15 +660,36 @@ int deltanet_kda_fwd(const void *q, const void *k, const void *v, const void *be
     a.ws_S = a.ws_Q + per * dv * dk;
     a.G = G;
     a.chunks_per_group = cpg;
+    // At dk = dv = 128 with three or more groups, group 0 runs from S0 beside
+    // the transitions of groups 1..G-2, as in the dense forward (one workgroup
+    // per CU here: the transitions' 64-row tiles take two rounds of the CUs
+    // and group 0's workgroups fit in the second), and the output phase
+    // covers groups 1..G-1.
+    const bool lead = fwd_lead_shape(dk, dv) && G >= 3;
+    const int first = lead ? 1 : 0;
+    dn::ChainArgs a0 = a;
+    a0.kind = dn::kCpOutput;
+    a0.cp_count = 1;
+    a0.cp_lead = 1;
+    a0.S_final = nullptr;
+    a0.n_units = B * H;
+    a0.n_tiles = dv / dn::kRows;
     a.kind = dn::kCpTransition;
-    a.n_units = B * H * (G - 1);
+    a.cp_first = first;
+    a.n_units = B * H * (G - 1 - first);
     a.n_tiles = dv / dn::kRows + dk / dn::kRows;
-    err = dn::launch_kda(dk, dv, false, a, stream);
+    if (lead) {
+        err = launch_beside(
+            stream, true, [&](hipStream_t s) { return dn::launch_kda(dk, dv, true, a0, s); },
+            [&](hipStream_t s) { return dn::launch_kda(dk, dv, false, a, s); });
+    } else {
+        err = dn::launch_kda(dk, dv, false, a, stream);
+    }
     if (err != hipSuccess) return DN_ERR_HIP;
     err = dn::launch_compose(dk, dv, a, stream);
     if (err != hipSuccess) return DN_ERR_HIP;
     a.kind = dn::kCpOutput;
-    a.n_units = B * H * G;
+    a.n_units = B * H * (G - first);
     a.n_tiles = dv / dn::kRows;
     err = dn::launch_kda(dk, dv, true, a, stream);
     return err == hipSuccess ? DN_OK : DN_ERR_HIP;

@@ -432,15 +432,15 @@ size_t deltanet_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
                                 int cp_groups);
 
 /*
- * Group count deltanet_fwd (and deltanet_gated_fwd, deltanet_gdp_fwd) uses
- * when called with cp_groups = 0, for the current HIP device. Returns 1
- * (serial) when splitting does not pay, or a negative status for invalid
- * shapes. At dk = dv = 128 these forwards run group 0, whose start state is
- * S0, beside the transitions of the other groups (on a second stream of the
- * library, joined back into the caller's stream before the call's later
- * work; on the caller's stream itself while it is being captured), so their
- * choice there holds one group more than the choice of deltanet_kda_fwd and
- * of the context-parallel backward passes with cp_groups = 0.
+ * Group count deltanet_fwd (and deltanet_gated_fwd, deltanet_gdp_fwd,
+ * deltanet_kda_fwd) uses when called with cp_groups = 0, for the current HIP
+ * device. Returns 1 (serial) when splitting does not pay, or a negative
+ * status for invalid shapes. At dk = dv = 128 these forwards run group 0,
+ * whose start state is S0, beside the transitions of the other groups (on a
+ * second stream of the library, joined back into the caller's stream before
+ * the call's later work; on the caller's stream itself while it is being
+ * captured), so their choice there holds one group more than the choice of
+ * the context-parallel backward passes with cp_groups = 0.
  */
 int deltanet_pick_cp_groups(int B, int H, int T, int dk, int dv, int chunk);
 

@@ -93,7 +93,7 @@ def test_kda_varlen(order):
     print(f"  worst err {worst:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("G", [2, 5, 0])
+@pytest.mark.parametrize("G", [2, 5, 8, 0])
 def test_kda_context_parallel(G):
     # one long sequence per head split into G groups (0: the library's choice):
     # transitions from the identity, composition, then every group from its start
